@@ -1,0 +1,266 @@
+"""Benchmark of the packed W4A4 block-scaled linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama_prefill]
+
+A step is one pass of the hot path over one batch: for each of the four
+Llama-3.1-8B linears (QKV, O, gate+up, down) the activations are rescaled
+and quantized (w4a4_quantize_act) and multiplied with the packed weight
+(w4a4_linear, row-scale epilogue included).  Weights are quantized and
+packed once, before timing (the paper packs them offline).  Inputs are
+seeded synthetic tensors already resident in HBM.
+
+Printed: one JSON line with the workload's throughput (TFLOP/s, whole step),
+the GEMM kernel's roofline position (algorithmic flops per launch over its
+HIP-event-timed average duration, against the MI355X dense MXFP4 peak),
+decode weight-streaming bandwidth (M = 1, 4, 16, cycling 32 layer copies so
+that the 256 MB last-level cache cannot hold the weights), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import w4a4_block_scaled_amd as w4  # noqa: E402
+from w4a4_block_scaled_amd import inputs  # noqa: E402
+
+PEAK = {  # MI355X published dense peaks
+    "mxfp4": (10.1e15, "TFLOP/s", "mfma"),   # FP4 / FP6 MFMA
+    "mxint4": (5.0e15, "TFLOP/s", "mfma"),   # runs on the FP8 scaled MFMA
+    "nvfp4": (2.5e15, "TFLOP/s", "mfma"),    # runs on the fp16 MFMA
+}
+HBM_PEAK = 8.0e12
+DTYPE = {"mxfp4": "fp4", "nvfp4": "fp4xe4m3->fp16", "mxint4": "int4->fp8"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """Device tensors of one linear: inputs, packed weight, outputs."""
+
+    def __init__(self, case, dev):
+        self.case = case
+        self.N, self.K, self.M, self.fmt = case.N, case.K, case.M, case.fmt
+        if case.w_codes is not None:
+            wc = torch.from_numpy(case.w_codes).to(dev)
+            ws = torch.from_numpy(case.w_scales).to(dev)
+            tw = torch.tensor([case.t_w], dtype=torch.float32, device=dev)
+        else:
+            wc, ws, tw = w4.quantize_act(case.w_prescaled.to(dev), None, case.fmt)
+        self.blob = w4.pack_weight(wc, ws, tw, torch.from_numpy(case.r).to(dev), case.fmt)
+        del wc, ws
+        self.x = case.x.to(dev)
+        self.c = torch.from_numpy(case.c).to(dev)
+        G = w4.block_size(case.fmt)
+        self.codes = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((self.M, self.K // G), dtype=torch.uint8, device=dev)
+        self.t = torch.ones(1, dtype=torch.float32, device=dev)
+        self.ws = torch.empty(max(16, w4.lib().w4a4_quantize_workspace_bytes(
+            w4.FORMATS[case.fmt], self.M, self.K)), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
+
+    def quantize(self):
+        w4.quantize_act(self.x, self.c, self.fmt, out=(self.codes, self.scales, self.t),
+                        workspace=self.ws)
+
+    def gemm(self, blob=None):
+        w4.linear(self.codes, self.scales, self.t, self.blob if blob is None else blob, self.fmt,
+                  self.N, self.K, out=self.y)
+
+    @property
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    def gemm_bytes(self):
+        G = w4.block_size(self.fmt)
+        return (self.N * self.K / 2 + self.N * self.K / G + 4 * self.N + self.M * self.K / 2 +
+                self.M * self.K / G + 2 * self.M * self.N)
+
+
+def time_steps(layers, steps, warmup, with_events=True):
+    """Run warmup + timed steps; returns (ms per step, per-layer GEMM ms list)."""
+    for _ in range(warmup):
+        for L in layers:
+            L.quantize()
+            L.gemm()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in layers] for _ in range(steps)] if with_events else None
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(steps):
+        for i, L in enumerate(layers):
+            L.quantize()
+            if with_events:
+                ev[s][i][0].record()
+            L.gemm()
+            if with_events:
+                ev[s][i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    gemm_ms = None
+    if with_events:
+        gemm_ms = [float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]))
+                   for i in range(len(layers))]
+    return ms, gemm_ms
+
+
+def decode_bandwidth(dev, steps, copies=32):
+    """Weight-streaming rate of the GEMM at M = 1, 4, 16 (MXFP4 Llama shapes).
+
+    Each step runs the four linears of one "layer"; 32 distinct copies of the
+    packed weights (3.7 GB) are cycled so that no copy is still cached.
+    """
+    out = {}
+    base = [Layer(c, dev) for c in inputs.workload_cases("llama_decode", M=16)]
+    blobs = [[L.blob.clone() for L in base] for _ in range(copies)]
+    for M in (1, 4, 16):
+        cases = inputs.workload_cases("llama_decode", M=M, build_weights=False)
+        act = [(c.x.to(dev), torch.from_numpy(c.c).to(dev)) for c in cases]
+        # quantized activations for this M
+        q = [w4.quantize_act(x, c, "mxfp4") for x, c in act]
+        ys = [torch.empty((M, L.N), dtype=torch.bfloat16, device=dev) for L in base]
+        nbytes = sum(L.N * L.K / 2 + L.N * L.K / 32 + 4 * L.N + M * L.K / 2 + M * L.K / 32 +
+                     2 * M * L.N for L in base)
+
+        def run_layer(k):
+            for j, L in enumerate(base):
+                w4.linear(q[j][0], q[j][1], q[j][2], blobs[k % copies][j], "mxfp4", L.N, L.K, out=ys[j])
+
+        for k in range(copies):
+            run_layer(k)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(steps, copies)
+        e0.record()
+        for k in range(n):
+            run_layer(k)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        out[str(M)] = {"us_per_4_linears": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                       "frac_of_8TBps": round(nbytes / (us * 1e-6) / HBM_PEAK, 3)}
+    del blobs
+    return out
+
+
+def cpu_baseline(workload, M, rows=64, cols=1024):
+    """The oracle as it stands, on a bounded sample: `rows` activation rows and
+    `cols` weight rows of each linear (quantization of both plus the fp64
+    linear).  Reported in the workload's unit (TFLOP/s of the sampled GEMM)."""
+    import oracle
+    from oracle.quant import quantize_rows, rescale, nv_tensor_scale, pack_nibbles
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    flops, secs = 0.0, 0.0
+    for case in inputs.workload_cases(workload, M=M):
+        rr = np.arange(min(rows, case.M))
+        cc = np.arange(min(cols, case.N))
+        x = case.x.float().numpy()[rr]
+        t0 = time.perf_counter()
+        xt = rescale(x, case.c)
+        ta = nv_tensor_scale(xt) if case.fmt == "nvfp4" else None
+        ac, as_, _ = quantize_rows(xt, case.fmt, t=ta)
+        if case.w_codes is not None:
+            wc, ws, tw = case.w_codes[cc], case.w_scales[cc], case.t_w
+        else:
+            w = case.w_prescaled[cc].float().numpy()
+            tw = nv_tensor_scale(w) if case.fmt == "nvfp4" else 1.0
+            wq, ws, _ = quantize_rows(w, case.fmt, t=tw if case.fmt == "nvfp4" else None)
+            wc = pack_nibbles(wq)
+        oracle.linear_bf16(pack_nibbles(ac), as_, ta, wc, ws, tw, case.r[cc], case.fmt)
+        secs += time.perf_counter() - t0
+        flops += 2.0 * len(rr) * len(cc) * case.K
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} activation rows x {cols} weight rows of each of the 4 linears "
+                      f"(quantize both + fp64 linear), {secs:.1f} s"}
+
+
+def traffic_record(kernel):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "w4a4_block_scaled_amd", "csrc", "gemm.hip"), "rb").read()
+    if rec.get("gemm_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get(kernel)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama_prefill", choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--M", type=int, default=None)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the hot path would shard by tokens or output features; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    seed, fmt, Ms, lins = inputs.WORKLOADS[a.workload]
+    M = a.M or Ms[-1]
+    log(f"[bench] building {a.workload} M={M} ({fmt})")
+    layers = [Layer(c, dev) for c in inputs.workload_cases(a.workload, M=M)]
+    torch.cuda.synchronize()
+    log("[bench] timing")
+    ms, gemm_ms = time_steps(layers, a.steps, a.warmup)
+    flops = sum(L.flops for L in layers)
+    value = flops / (ms * 1e-3) / 1e12
+    peak, unit, bound = PEAK[fmt]
+    achieved = sum(L.flops for L in layers) / (sum(gemm_ms) * 1e-3)   # per-launch average
+    roof = {"bound": bound, "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12,
+            "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": traffic_record(f"gemm_{a.workload}_M{M}"),
+            "kernel": f"gemm_tile_kernel<{fmt}>" if M > 16 or fmt == "nvfp4" else f"gemm_decode_kernel<{fmt}>",
+            "per_linear": {L.case.name: {"us": round(t * 1e3, 2),
+                                         "TFLOP/s": round(L.flops / (t * 1e-3) / 1e12, 1),
+                                         "frac": round(L.flops / (t * 1e-3) / peak, 4)}
+                           for L, t in zip(layers, gemm_ms)}}
+    out = {"metric": "W4A4 linear TFLOPS & % MXFP4 MFMA peak (prefill); HBM GB/s (decode)",
+           "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps,
+           "warmup": a.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[fmt], "data": "synthetic",
+           "config": {"workload": a.workload, "format": fmt, "M": M,
+                      "linears": [[L.case.name, L.N, L.K] for L in layers],
+                      "step": "quantize_act + linear for each linear; weights packed once"},
+           "tokens_per_s": round(M / (ms * 1e-3), 1),
+           "roofline": roof}
+    del layers
+    torch.cuda.empty_cache()
+    if not a.no_decode:
+        log("[bench] decode bandwidth")
+        out["decode_hbm"] = decode_bandwidth(dev, a.steps)
+    if not a.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(a.workload, M)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * w4a4.h - C ABI of the MI355X (gfx950) packed W4A4 block-scaled linear.
+ *
+ * What the library computes (DualQuant, "Dual-scale Calibration-free
+ * Weight-and-Activation Quantization for LLMs"):
+ *
+ *   Section 4.2, eq. (2)-(3): a weight is stored as W ~ diag(r) . Q . diag(c)
+ *   with row scales r (the inverse alpha) and column scales c (the inverse
+ *   beta); the column scales become an activation rescaling X~ = X diag(c).
+ *   Section 4.4: at inference the layer computes Q(X~) . Q^T . diag(r), where
+ *   Q(X~) is the format-native row-wise block quantization of X~, c is
+ *   multiplied in inside the activation-quantization kernel and r is applied
+ *   to the GEMM output.  Section 3: block formats MXFP4 (E2M1, blocks of 32,
+ *   E8M0 scale), MXINT4 (int4, blocks of 32, E8M0 scale) and NVFP4 (E2M1,
+ *   blocks of 16, UE4M3 scale) plus an FP32 tensor scale for NVFP4.
+ *   Appendix I: weights are packed offline into the GEMM's storage layout
+ *   and stay packed; group scales are consumed inside the GEMM; the GEMM
+ *   entry allocates nothing, so a whole model can be captured in a graph.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument named as device memory must point to memory
+ *     of the device that owns `stream` (a hipStream_t; NULL = the null
+ *     stream of the current device).  The caller owns all buffers; the
+ *     library never allocates, frees or synchronizes, and keeps no pointer
+ *     after a call returns.  Work is enqueued on `stream`; buffers must stay
+ *     valid until the stream has executed it.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     non-OK status means nothing was enqueued.  w4a4_last_error() then
+ *     returns a message (thread-local).  Launch failures return
+ *     W4A4_ERR_HIP.  No entry point aborts the process.
+ *   - Row-major everywhere; K is the reduction (input-feature) dimension.
+ *   - Canonical code layout: [rows x K/2] bytes, element 2j of a row in the
+ *     low nibble of byte j and element 2j+1 in the high nibble.  FP4 codes
+ *     are E2M1 (sign bit 3), INT4 codes two's complement.  Canonical scale
+ *     layout: [rows x K/G] bytes (E8M0 for MX formats, UE4M3 for NVFP4).
+ *   - Calls are reentrant; the library has no mutable global state.
+ */
+#ifndef W4A4_H_
+#define W4A4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A4_MXFP4 = 0,   /* E2M1 elements, G = 32, E8M0 block scale             */
+  W4A4_NVFP4 = 1,   /* E2M1 elements, G = 16, UE4M3 block scale + fp32 t   */
+  W4A4_MXINT4 = 2   /* int4 elements, G = 32, E8M0 block scale             */
+} w4a4_format;
+
+typedef enum {
+  W4A4_OK = 0,
+  W4A4_ERR_NULL = 1,       /* a required pointer is NULL                        */
+  W4A4_ERR_SHAPE = 2,      /* M < 0, N or K out of range, K % G, N % 16, K % 128 */
+  W4A4_ERR_ALIGN = 3,      /* a pointer misses its documented alignment         */
+  W4A4_ERR_FORMAT = 4,     /* unknown format value                              */
+  W4A4_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required        */
+  W4A4_ERR_HIP = 6         /* a HIP call or kernel launch failed                */
+} w4a4_status;
+
+/* Block size G of a format (32, 16 or 32); 0 for an unknown format. */
+int w4a4_block_size(w4a4_format fmt);
+
+/* Byte sizes, so that callers allocate every buffer.  Return 0 for invalid
+ * arguments. */
+size_t w4a4_act_codes_bytes(w4a4_format fmt, int64_t M, int64_t K);   /* M*K/2 */
+size_t w4a4_act_scales_bytes(w4a4_format fmt, int64_t M, int64_t K);  /* M*K/G */
+size_t w4a4_quantize_workspace_bytes(w4a4_format fmt, int64_t M, int64_t K);
+size_t w4a4_packed_weight_bytes(w4a4_format fmt, int64_t N, int64_t K);
+size_t w4a4_linear_workspace_bytes(w4a4_format fmt, int64_t M, int64_t N, int64_t K);
+
+/*
+ * w4a4_quantize_act - fused rescale + block quantization of activations.
+ *
+ * DualQuant Section 4.4 (beta applied inside the activation-quantization
+ * kernel, no separate launch; the format-native per-row block scale is still
+ * computed on X~) with eq. (3) (X~ = X diag(beta)^-1 = X diag(c)), and the
+ * quantizer of Section 3 (nearest grid point, clipped).
+ *
+ *   X      device, bf16 [M x K], 16-byte aligned.
+ *   c      device, fp32 [K], 16-byte aligned; NULL means c = 1 (this is how
+ *          weights W / (r c^T) are quantized before packing).
+ *   codes  device, out, [M x K/2] canonical codes, 4-byte aligned.
+ *   scales device, out, [M x K/G] canonical scale bytes.
+ *   t_act  device, out, one fp32: the NVFP4 tensor scale
+ *          t = fp32(max|X~|) / 2688 (t = 1 for an all-zero tensor).  Ignored
+ *          (may be NULL) for MX formats.
+ *   workspace / ws_bytes: device scratch of at least
+ *          w4a4_quantize_workspace_bytes() bytes (0 for MX formats; NVFP4
+ *          uses it for the tensor-amax partial maxima), 4-byte aligned.
+ *
+ * Per row, per block of G along K, with x~ = fp32(x) * c[k] (one rounded
+ * fp32 multiply) and a = max |x~| over the block:
+ *   MX:    e = clamp(floor(log2 a) - 2, -127, 127), byte e + 127 (0 if a = 0);
+ *          MXFP4 code = RNE_E2M1(x~ * 2^-e) saturating at +-6;
+ *          MXINT4 code = clamp(RNE(x~ * 2^-e), -8, 7).
+ *          A block holding Inf/NaN gets byte 0xFF and zero codes.
+ *   NVFP4: byte s = RNE_E4M3(a / (6 t)) saturating at 448; code =
+ *          RNE_E2M1(x~ / (s t)); a block whose scale is 0 keeps sign-only
+ *          zero codes.  Inputs must be finite.
+ * All rounding decisions are exact (ties to even, decided against exact
+ * midpoints), so codes and scales are fully determined by X and c.
+ * Requires M >= 0, K > 0, K % G == 0.
+ */
+w4a4_status w4a4_quantize_act(w4a4_format fmt, int64_t M, int64_t K,
+                              const void* X, const float* c,
+                              void* codes, void* scales, float* t_act,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * w4a4_pack_weight - pack a quantized weight into the GEMM storage layout.
+ *
+ * DualQuant Appendix I: the per-layer artifacts (quantized weight Q, row
+ * scales, column scales; Section 4.4) are packed offline into the target
+ * storage layout and remain packed during inference.  Here Q arrives as
+ * canonical codes and block scales (for instance from w4a4_quantize_act with
+ * c = NULL on W / (r c^T)); the column scales c are not part of the blob,
+ * they are passed to w4a4_quantize_act at run time.
+ *
+ *   codes  device, [N x K/2] canonical codes, 16-byte aligned.
+ *   scales device, [N x K/G] canonical scale bytes.
+ *   t_w    device, one fp32 NVFP4 weight tensor scale; NULL means 1.
+ *   r      device, fp32 [N] row scales (multiplied into the output).
+ *   blob   device, out, w4a4_packed_weight_bytes() bytes, 256-byte aligned.
+ *
+ * Blob contents (opaque to callers apart from this description): a 256-byte
+ * header (magic "W4A4PK01", format, N, K, t_w), then the codes in MFMA
+ * fragment order (16 output rows x 128 K per 1 KiB tile), the block scales
+ * regrouped per lane and K-step, and r.  Requires N % 16 == 0, K % 128 == 0.
+ */
+w4a4_status w4a4_pack_weight(w4a4_format fmt, int64_t N, int64_t K,
+                             const void* codes, const void* scales,
+                             const float* t_w, const float* r,
+                             void* blob, void* stream);
+
+/*
+ * w4a4_unpack_weight - inverse of w4a4_pack_weight (round-trip checks,
+ * serialization).  Writes canonical codes, scales, r (each may be NULL to
+ * skip) and t_w (device fp32, may be NULL) from a blob packed with the same
+ * fmt, N and K.
+ */
+w4a4_status w4a4_unpack_weight(w4a4_format fmt, int64_t N, int64_t K,
+                               const void* blob, void* codes, void* scales,
+                               float* r, float* t_w, void* stream);
+
+/*
+ * w4a4_linear - block-scaled 4-bit x 4-bit GEMM with the row-scale epilogue.
+ *
+ * DualQuant Section 4.4: Y = Q(X~) . Q^T . diag(r); Appendix I: the block
+ * scales are applied inside the GEMM (no weight dequantization pass) and the
+ * entry point allocates nothing.
+ *
+ *   Y[m, n] = bf16_rne( r[n] * t * sum_k a^[m,k] w^[n,k] )
+ *
+ * where a^ / w^ are code times block scale and t = t_act * t_w for NVFP4
+ * (1 for MX formats).  Accumulation is fp32.
+ *
+ *   a_codes  device, [M x K/2] canonical activation codes, 16-byte aligned.
+ *   a_scales device, [M x K/G] canonical activation scales, 16-byte aligned.
+ *   t_act    device, one fp32 (NVFP4 only; may be NULL for MX formats).
+ *   blob     device, a blob packed for the same fmt, N, K, 256-byte aligned.
+ *   Y        device, out, bf16 [M x N], 16-byte aligned.
+ *   workspace/ws_bytes: device scratch of at least
+ *            w4a4_linear_workspace_bytes() bytes (may be 0).
+ *
+ * Requires M >= 0, N % 16 == 0, K % 128 == 0.  The blob's fmt, N and K are
+ * trusted, not re-read from device memory.
+ */
+w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K,
+                        const void* a_codes, const void* a_scales,
+                        const float* t_act, const void* blob, void* Y,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* w4a4_last_error(void);
+
+/* Library version string. */
+const char* w4a4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif  /* W4A4_H_ */

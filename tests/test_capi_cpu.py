@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/w4a4.h declares, answers size queries, and rejects invalid arguments
+on the host before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w4a4_block_scaled_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(w4.library_path()),
+                                reason="libw4a4.so not built (python -m w4a4_block_scaled_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("w4a4_quantize_act", "w4a4_pack_weight", "w4a4_linear"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    L = w4.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_version_and_block_sizes():
+    L = w4.lib()
+    assert L.w4a4_version().decode().startswith("w4a4")
+    assert [L.w4a4_block_size(f) for f in (0, 1, 2, 7)] == [32, 16, 32, 0]
+
+
+def test_size_queries():
+    L = w4.lib()
+    assert L.w4a4_act_codes_bytes(0, 2048, 4096) == 2048 * 2048
+    assert L.w4a4_act_scales_bytes(0, 2048, 4096) == 2048 * 128
+    assert L.w4a4_act_scales_bytes(1, 2048, 4096) == 2048 * 256
+    assert L.w4a4_act_codes_bytes(0, 3, 33) == 0                 # K % G
+    assert L.w4a4_quantize_workspace_bytes(1, 16, 256) >= 4
+    assert L.w4a4_quantize_workspace_bytes(0, 16, 256) == 0
+    for fmt, G in ((0, 32), (1, 16), (2, 32)):
+        N, K = 28672, 4096
+        total = L.w4a4_packed_weight_bytes(fmt, N, K)
+        payload = N * K // 2 + N * K // G + 4 * N
+        assert payload <= total <= payload + 4 * 256 + (N // 16) * 64 * 4 * 1
+    assert L.w4a4_packed_weight_bytes(0, 100, 4096) == 0          # N % 16
+    assert L.w4a4_packed_weight_bytes(0, 128, 4000) == 0          # K % 128
+
+
+def test_table12_scale_bytes_from_the_library():
+    """Llama-3.1-8B's 224 linears: the MXFP4 blob payload is 3.49 GB of codes
+    plus 0.22 GB of scales (Appendix I, Table 12 byte counts)."""
+    L = w4.lib()
+    shapes = [(6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336)]
+    total = sum(L.w4a4_packed_weight_bytes(0, N, K) for N, K in shapes) * 32
+    codes = sum(L.w4a4_act_codes_bytes(0, N, K) for N, K in shapes) * 32
+    scales = sum(L.w4a4_act_scales_bytes(0, N, K) for N, K in shapes) * 32
+    assert round(codes / 1e9, 2) == 3.49 and round(scales / 1e9, 2) == 0.22
+    assert total - codes - scales < 0.01e9      # header, r and padding stay small
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # never dereferenced: validation fails first
+FAKE_MIS = ctypes.c_void_p((1 << 20) + 2)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((9, 16, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, None), 4),       # format
+    ((0, -1, 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None), 2),          # M < 0
+    ((0, 16, 250, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None), 2),          # K % 32
+    ((1, 16, 264, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None), 2),          # K % 16
+    ((0, 16, 256, None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None), 1),          # X NULL
+    ((0, 16, 256, FAKE_MIS, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None), 3),      # X misaligned
+    ((1, 16, 256, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None), 5),          # NVFP4 workspace
+    ((1, 16, 256, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4096, None), 1),       # NVFP4 t_act
+])
+def test_quantize_act_rejects(args, status):
+    L = w4.lib()
+    assert L.w4a4_quantize_act(*args) == status
+    assert L.w4a4_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 100, 256, FAKE, FAKE, None, FAKE, FAKE, None), 2),     # N % 16
+    ((0, 128, 200, FAKE, FAKE, None, FAKE, FAKE, None), 2),     # K % 128
+    ((0, 128, 256, None, FAKE, None, FAKE, FAKE, None), 1),
+    ((0, 128, 256, FAKE, FAKE, None, FAKE, ctypes.c_void_p((1 << 20) + 16), None), 3),  # blob 256-B
+    ((5, 128, 256, FAKE, FAKE, None, FAKE, FAKE, None), 4),
+])
+def test_pack_weight_rejects(args, status):
+    assert w4.lib().w4a4_pack_weight(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, -2, 128, 256, FAKE, FAKE, None, FAKE, FAKE, None, 0, None), 2),
+    ((0, 4, 120, 256, FAKE, FAKE, None, FAKE, FAKE, None, 0, None), 2),
+    ((0, 4, 128, 200, FAKE, FAKE, None, FAKE, FAKE, None, 0, None), 2),
+    ((0, 4, 128, 256, FAKE, None, None, FAKE, FAKE, None, 0, None), 1),
+    ((1, 4, 128, 256, FAKE, FAKE, None, FAKE, FAKE, None, 0, None), 1),     # NVFP4 t_act
+    ((0, 4, 128, 256, FAKE, FAKE, None, FAKE, FAKE_MIS, None, 0, None), 3),
+])
+def test_linear_rejects(args, status):
+    assert w4.lib().w4a4_linear(*args) == status
+
+
+def test_empty_linear_is_a_no_op():
+    # M = 0 returns OK without touching the pointers or the device
+    assert w4.lib().w4a4_linear(0, 0, 128, 256, None, None, None, None, None, None, 0, None) == 0

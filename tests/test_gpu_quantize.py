@@ -1,0 +1,142 @@
+"""GPU parity of w4a4_quantize_act (codes, scales, tensor scale) against the
+oracle: bit-exact, on seeded inputs of several shapes, the hand-worked golden
+blocks, edge values and the full activation tensors of every workload."""
+import numpy as np
+import pytest
+import torch
+
+from conftest import golden
+import oracle
+from oracle import formats as F
+from gpu_common import device, say, to_dev, gpu_quantize
+from w4a4_block_scaled_amd import inputs
+import w4a4_block_scaled_amd as w4
+
+pytestmark = pytest.mark.gpu
+FMTS = ["mxfp4", "nvfp4", "mxint4"]
+
+
+def _compare(x, c, fmt, label):
+    dev = device()
+    codes, scales, t = gpu_quantize(x, c, fmt, dev)
+    xf = x.float().numpy()
+    cc = np.ones(xf.shape[1], np.float32) if c is None else c
+    oc, os_, ot = oracle.quantize_act(xf, cc, fmt)
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    if fmt == "nvfp4":
+        gt = float(t.cpu().numpy()[0])
+        assert gt == float(ot), f"{label}: tensor scale {gt!r} != {float(ot)!r}"
+    if not np.array_equal(gs, os_):
+        i = np.argwhere(gs != os_)[0]
+        raise AssertionError(f"{label}: scale mismatch at {tuple(i)}: gpu {gs[tuple(i)]} oracle {os_[tuple(i)]} "
+                             f"({(gs != os_).sum()} total)")
+    if not np.array_equal(gc, oc):
+        i = np.argwhere(gc != oc)[0]
+        raise AssertionError(f"{label}: code mismatch at {tuple(i)}: gpu {gc[tuple(i)]:#04x} oracle {oc[tuple(i)]:#04x} "
+                             f"({(gc != oc).sum()} total)")
+    return codes, scales, t
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("M,K", [(1, 32), (5, 96), (16, 256), (37, 1024), (300, 4096), (64, 18944)])
+def test_quantize_matches_oracle(fmt, M, K):
+    if K % oracle.BLOCK[fmt]:
+        pytest.skip("K not a multiple of the block")
+    say(f"[quantize] {fmt} M={M} K={K}")
+    case = inputs.adhoc_case(fmt, M, 16, K, seed=100 + M + K, weights="none")
+    _compare(case.x, case.c, fmt, f"{fmt} {M}x{K}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_without_column_scales(fmt):
+    case = inputs.adhoc_case(fmt, 33, 16, 512, seed=7, weights="none")
+    _compare(case.x, None, fmt, f"{fmt} c=None")
+
+
+def test_golden_blocks_on_gpu():
+    dev = device()
+    g = golden("mxfp4_block.json")
+    for cs in g["cases"]:
+        x = torch.tensor([g["x"]], dtype=torch.float32).to(torch.bfloat16)
+        codes, scales, _ = gpu_quantize(x, np.full(32, cs["c"], np.float32), "mxfp4", dev)
+        assert codes.cpu().numpy()[0].tolist() == g["packed"]
+        assert scales.cpu().numpy()[0].tolist() == [cs["scale"]]
+    g = golden("mxint4_block.json")
+    x = torch.tensor([g["x"]], dtype=torch.float32).to(torch.bfloat16)
+    codes, scales, _ = gpu_quantize(x, np.ones(32, np.float32), "mxint4", dev)
+    assert oracle.unpack_nibbles(codes.cpu().numpy())[0].tolist() == g["codes"]
+    assert scales.cpu().numpy()[0].tolist() == [g["scale"]]
+    g = golden("nvfp4_blocks.json")
+    x = torch.tensor([g["x"]], dtype=torch.float32).to(torch.bfloat16)
+    codes, scales, t = gpu_quantize(x, np.ones(32, np.float32), "nvfp4", dev)
+    assert float(t.cpu()[0]) == g["t"]
+    assert scales.cpu().numpy()[0].tolist() == g["scales"]
+    assert oracle.unpack_nibbles(codes.cpu().numpy())[0].tolist() == g["codes"]
+
+
+def _edge_tensor(fmt, rng):
+    G = oracle.BLOCK[fmt]
+    K = 16 * G
+    x = (rng.standard_normal((8, K)) * 3).astype(np.float32)
+    x[0, :G] = 0.0                                             # all-zero block
+    x[0, G:2 * G] = -0.0                                       # negative zeros
+    x[1, :G] = np.float32(2.0 ** -133) * rng.integers(-3, 4, G)   # bf16 subnormals
+    x[1, G:2 * G] = np.float32(2.0 ** -126) * rng.integers(-100, 100, G)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.5, -0.25, -2.5, -5.0, 0.5, 3.0, 4.0, -6.0])
+    x[2, :16] = ties
+    x[2, 16:G] = 0.0
+    x[3, :G] = 3.0e38 * np.sign(rng.standard_normal(G))       # near the bf16 maximum
+    x[4, :G] = np.float32(2.0 ** 100)                          # constant block
+    x[5, :] = x[5, :] * np.float32(2.0 ** -60)
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_edge_values(fmt):
+    x = _edge_tensor(fmt, np.random.default_rng(11))
+    if fmt == "nvfp4":
+        x[3] = x[3] * 0  # keep the tensor amax moderate so that ties stay ties
+    _compare(x, np.ones(x.shape[1], np.float32), fmt, f"{fmt} edge")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+def test_quantize_nonfinite_convention(fmt):
+    x = torch.randn(4, 128).to(torch.bfloat16)
+    x[0, 5] = float("inf")
+    x[1, 70] = float("nan")
+    x[2, 127] = float("-inf")
+    _compare(x, np.ones(128, np.float32), fmt, f"{fmt} nonfinite")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_empty(fmt):
+    dev = device()
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    codes, scales, t = w4.quantize_act(x, None, fmt)
+    torch.cuda.synchronize()
+    assert codes.shape == (0, 128)
+    if fmt == "nvfp4":
+        assert float(t.cpu()[0]) == 1.0
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_deterministic(fmt):
+    dev = device()
+    case = inputs.adhoc_case(fmt, 129, 16, 2048, seed=5, weights="none")
+    a = gpu_quantize(case.x, case.c, fmt, dev)
+    b = gpu_quantize(case.x, case.c, fmt, dev)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+FULL = [("llama_prefill", 2048, ("qkv", "down")), ("llama_nvfp4", 4096, ("qkv", "down")),
+        ("qwen_mxint4", 4096, ("qkv", "down")), ("llama_decode", 16, ("qkv", "down")),
+        ("single", 16, ("single",))]
+
+
+@pytest.mark.parametrize("workload,M,lins", FULL)
+def test_quantize_full_activation_tensors(workload, M, lins):
+    """Full activation tensors of each workload (the two distinct K of each
+    model), compared bit for bit."""
+    for case in inputs.workload_cases(workload, M=M, linears=lins, build_weights=False):
+        say(f"[quantize full] {workload} {case.name} M={case.M} K={case.K}")
+        _compare(case.x, case.c, case.fmt, f"{workload}/{case.name}")

@@ -1,0 +1,179 @@
+"""Python binding of libw4a4 (the MI355X packed W4A4 block-scaled linear).
+
+Argument marshalling only: every step of the path runs in the gfx950
+kernels behind the C ABI declared in include/w4a4.h.  torch supplies device
+memory and the current HIP stream.  The raw C functions are available on
+``lib()`` under their C names; the wrappers below keep the same names
+without the ``w4a4_`` prefix:
+
+    codes, scales, t = quantize_act(x_bf16, c_fp32, "mxfp4")
+    blob             = pack_weight(w_codes, w_scales, t_w, r, "mxfp4")
+    y_bf16           = linear(codes, scales, t, blob, "mxfp4", N, K)
+
+There is no fallback: if the library is missing or fails to load, the
+functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["FORMATS", "lib", "library_path", "block_size", "quantize_act", "pack_weight",
+           "unpack_weight", "linear", "packed_weight_bytes", "W4A4Error"]
+
+FORMATS = {"mxfp4": 0, "nvfp4": 1, "mxint4": 2}
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class W4A4Error(RuntimeError):
+    """A non-OK status from the C ABI (message from w4a4_last_error)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"w4a4 status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libw4a4.so")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4a4.so (built in-tree by build.py); raise if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           f"`python -m w4a4_block_scaled_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(path)
+    i64, sz, vp, i32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+    L.w4a4_block_size.argtypes = [i32]
+    L.w4a4_block_size.restype = i32
+    for name in ("w4a4_act_codes_bytes", "w4a4_act_scales_bytes",
+                 "w4a4_quantize_workspace_bytes", "w4a4_packed_weight_bytes"):
+        getattr(L, name).argtypes = [i32, i64, i64]
+        getattr(L, name).restype = sz
+    L.w4a4_linear_workspace_bytes.argtypes = [i32, i64, i64, i64]
+    L.w4a4_linear_workspace_bytes.restype = sz
+    L.w4a4_quantize_act.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.w4a4_quantize_act.restype = i32
+    L.w4a4_pack_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.w4a4_pack_weight.restype = i32
+    L.w4a4_unpack_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.w4a4_unpack_weight.restype = i32
+    L.w4a4_linear.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.w4a4_linear.restype = i32
+    L.w4a4_last_error.argtypes = []
+    L.w4a4_last_error.restype = ctypes.c_char_p
+    L.w4a4_version.argtypes = []
+    L.w4a4_version.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        return FORMATS[fmt]
+    return int(fmt)
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise W4A4Error(status, lib().w4a4_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def block_size(fmt) -> int:
+    return lib().w4a4_block_size(_fmt(fmt))
+
+
+def packed_weight_bytes(fmt, N: int, K: int) -> int:
+    return lib().w4a4_packed_weight_bytes(_fmt(fmt), N, K)
+
+
+def quantize_act(x: torch.Tensor, c: Optional[torch.Tensor], fmt,
+                 out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                 workspace: Optional[torch.Tensor] = None):
+    """w4a4_quantize_act: x bf16 [M, K], c fp32 [K] or None -> (codes, scales, t).
+
+    codes uint8 [M, K/2], scales uint8 [M, K/G], t fp32 [1] (NVFP4 tensor
+    scale; unused for MX formats).
+    """
+    f = _fmt(fmt)
+    L = lib()
+    M, K = x.shape
+    G = L.w4a4_block_size(f)
+    if out is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((M, K // G), dtype=torch.uint8, device=x.device)
+        t = torch.ones(1, dtype=torch.float32, device=x.device)
+    else:
+        codes, scales, t = out
+    ws_bytes = L.w4a4_quantize_workspace_bytes(f, M, K)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    _check(L.w4a4_quantize_act(f, M, K, _ptr(x), _ptr(c), _ptr(codes), _ptr(scales), _ptr(t),
+                               _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                               _stream(x.device)))
+    return codes, scales, t
+
+
+def pack_weight(codes: torch.Tensor, scales: torch.Tensor, t_w: Optional[torch.Tensor],
+                r: torch.Tensor, fmt) -> torch.Tensor:
+    """w4a4_pack_weight: canonical codes [N, K/2], scales, t_w [1] or None, r [N] -> blob."""
+    f = _fmt(fmt)
+    L = lib()
+    N, K = codes.shape[0], codes.shape[1] * 2
+    nbytes = L.w4a4_packed_weight_bytes(f, N, K)
+    if nbytes == 0:
+        raise W4A4Error(2, f"invalid packed weight shape N={N} K={K}")
+    blob = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _check(L.w4a4_pack_weight(f, N, K, _ptr(codes), _ptr(scales), _ptr(t_w), _ptr(r), _ptr(blob),
+                              _stream(codes.device)))
+    return blob
+
+
+def unpack_weight(blob: torch.Tensor, fmt, N: int, K: int):
+    """w4a4_unpack_weight -> (codes [N, K/2], scales [N, K/G], r [N], t_w [1])."""
+    f = _fmt(fmt)
+    L = lib()
+    G = L.w4a4_block_size(f)
+    dev = blob.device
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // G), dtype=torch.uint8, device=dev)
+    r = torch.empty(N, dtype=torch.float32, device=dev)
+    t_w = torch.empty(1, dtype=torch.float32, device=dev)
+    _check(L.w4a4_unpack_weight(f, N, K, _ptr(blob), _ptr(codes), _ptr(scales), _ptr(r), _ptr(t_w),
+                                _stream(dev)))
+    return codes, scales, r, t_w
+
+
+def linear(a_codes: torch.Tensor, a_scales: torch.Tensor, t_act: Optional[torch.Tensor],
+           blob: torch.Tensor, fmt, N: int, K: int, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """w4a4_linear: quantized activations [M, K/2] x packed weight -> bf16 [M, N]."""
+    f = _fmt(fmt)
+    L = lib()
+    M = a_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
+    ws_bytes = L.w4a4_linear_workspace_bytes(f, M, N, K)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a_codes.device)
+    _check(L.w4a4_linear(f, M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(t_act), _ptr(blob),
+                         _ptr(out), _ptr(workspace),
+                         workspace.numel() if workspace is not None else 0,
+                         _stream(a_codes.device)))
+    return out

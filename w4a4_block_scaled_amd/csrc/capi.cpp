@@ -1,0 +1,161 @@
+// C ABI of libw4a4 (declared in include/w4a4.h): argument validation,
+// thread-local error messages and dispatch to the gfx950 kernels.  Nothing
+// here allocates device memory or synchronizes.
+#include "w4a4.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+w4a4_status fail(w4a4_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+w4a4_status ok() {
+  g_err[0] = 0;
+  return W4A4_OK;
+}
+
+bool valid_fmt(w4a4_format f) { return f == W4A4_MXFP4 || f == W4A4_NVFP4 || f == W4A4_MXINT4; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+w4a4_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(W4A4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// (K % 128, N % 16) shapes of the packed GEMM
+w4a4_status check_gemm_shape(w4a4_format fmt, int64_t N, int64_t K) {
+  if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
+  if (N <= 0 || K <= 0) return fail(W4A4_ERR_SHAPE, "N=%lld K=%lld must be positive",
+                                    (long long)N, (long long)K);
+  if (N % 16) return fail(W4A4_ERR_SHAPE, "N=%lld must be a multiple of 16", (long long)N);
+  if (K % 128) return fail(W4A4_ERR_SHAPE, "K=%lld must be a multiple of 128", (long long)K);
+  if (N > (int64_t(1) << 31) || K > (int64_t(1) << 31))
+    return fail(W4A4_ERR_SHAPE, "N or K too large");
+  return W4A4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a4_block_size(w4a4_format fmt) { return valid_fmt(fmt) ? w4a4::block_size(fmt) : 0; }
+
+size_t w4a4_act_codes_bytes(w4a4_format fmt, int64_t M, int64_t K) {
+  if (!valid_fmt(fmt) || M < 0 || K <= 0 || K % w4a4::block_size(fmt)) return 0;
+  return size_t(M) * size_t(K) / 2;
+}
+
+size_t w4a4_act_scales_bytes(w4a4_format fmt, int64_t M, int64_t K) {
+  if (!valid_fmt(fmt) || M < 0 || K <= 0 || K % w4a4::block_size(fmt)) return 0;
+  return size_t(M) * size_t(K / w4a4::block_size(fmt));
+}
+
+size_t w4a4_quantize_workspace_bytes(w4a4_format fmt, int64_t, int64_t) {
+  return fmt == W4A4_NVFP4 ? size_t(w4a4::kNvAmaxBlocks) * sizeof(float) : 0;
+}
+
+size_t w4a4_packed_weight_bytes(w4a4_format fmt, int64_t N, int64_t K) {
+  if (check_gemm_shape(fmt, N, K) != W4A4_OK) return 0;
+  return size_t(w4a4::blob_layout(fmt, N, K).total);
+}
+
+size_t w4a4_linear_workspace_bytes(w4a4_format fmt, int64_t M, int64_t N, int64_t K) {
+  if (!valid_fmt(fmt)) return 0;
+  return w4a4::linear_workspace_bytes(fmt, M, N, K);
+}
+
+w4a4_status w4a4_quantize_act(w4a4_format fmt, int64_t M, int64_t K, const void* X,
+                              const float* c, void* codes, void* scales, float* t_act,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
+  const int G = w4a4::block_size(fmt);
+  if (M < 0 || K <= 0 || K % G)
+    return fail(W4A4_ERR_SHAPE, "quantize_act: M=%lld K=%lld (need M >= 0, K > 0, K %% %d == 0)",
+                (long long)M, (long long)K, G);
+  if (M * K / 8 > (int64_t(1) << 40)) return fail(W4A4_ERR_SHAPE, "quantize_act: tensor too large");
+  if (M > 0 && (!X || !codes || !scales))
+    return fail(W4A4_ERR_NULL, "quantize_act: X, codes and scales must be non-NULL");
+  if (fmt == W4A4_NVFP4) {
+    if (!t_act) return fail(W4A4_ERR_NULL, "quantize_act: NVFP4 needs t_act");
+    if (!workspace || ws_bytes < w4a4_quantize_workspace_bytes(fmt, M, K))
+      return fail(W4A4_ERR_WORKSPACE, "quantize_act: NVFP4 needs %zu workspace bytes, got %zu",
+                  w4a4_quantize_workspace_bytes(fmt, M, K), workspace ? ws_bytes : size_t(0));
+    if (!aligned(workspace, 4) || !aligned(t_act, 4))
+      return fail(W4A4_ERR_ALIGN, "quantize_act: workspace and t_act must be 4-byte aligned");
+  }
+  if (!aligned(X, 16) || (c && !aligned(c, 16)) || !aligned(codes, 4))
+    return fail(W4A4_ERR_ALIGN, "quantize_act: X and c need 16-byte, codes 4-byte alignment");
+  return hip_status(w4a4::launch_quantize_act(fmt, M, K, X, c, codes, scales, t_act, workspace,
+                                              static_cast<hipStream_t>(stream)),
+                    "quantize_act launch");
+}
+
+w4a4_status w4a4_pack_weight(w4a4_format fmt, int64_t N, int64_t K, const void* codes,
+                             const void* scales, const float* t_w, const float* r, void* blob,
+                             void* stream) {
+  w4a4_status st = check_gemm_shape(fmt, N, K);
+  if (st != W4A4_OK) return st;
+  if (!codes || !scales || !r || !blob)
+    return fail(W4A4_ERR_NULL, "pack_weight: codes, scales, r and blob must be non-NULL");
+  if (!aligned(codes, 16) || !aligned(blob, 256) || !aligned(r, 4) || (t_w && !aligned(t_w, 4)))
+    return fail(W4A4_ERR_ALIGN, "pack_weight: codes 16-byte, blob 256-byte, r/t_w 4-byte alignment");
+  return hip_status(w4a4::launch_pack_weight(fmt, N, K, codes, scales, t_w, r, blob,
+                                             static_cast<hipStream_t>(stream)),
+                    "pack_weight launch");
+}
+
+w4a4_status w4a4_unpack_weight(w4a4_format fmt, int64_t N, int64_t K, const void* blob,
+                               void* codes, void* scales, float* r, float* t_w, void* stream) {
+  w4a4_status st = check_gemm_shape(fmt, N, K);
+  if (st != W4A4_OK) return st;
+  if (!blob) return fail(W4A4_ERR_NULL, "unpack_weight: blob must be non-NULL");
+  if (!aligned(blob, 256) || (codes && !aligned(codes, 16)) || (r && !aligned(r, 4)) ||
+      (t_w && !aligned(t_w, 4)))
+    return fail(W4A4_ERR_ALIGN, "unpack_weight: blob 256-byte, codes 16-byte, r/t_w 4-byte alignment");
+  return hip_status(w4a4::launch_unpack_weight(fmt, N, K, blob, codes, scales, r, t_w,
+                                               static_cast<hipStream_t>(stream)),
+                    "unpack_weight launch");
+}
+
+w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
+                        const void* a_scales, const float* t_act, const void* blob, void* Y,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  w4a4_status st = check_gemm_shape(fmt, N, K);
+  if (st != W4A4_OK) return st;
+  if (M < 0 || M > (int64_t(1) << 31)) return fail(W4A4_ERR_SHAPE, "linear: M=%lld out of range", (long long)M);
+  if (M == 0) return ok();
+  if (!a_codes || !a_scales || !blob || !Y)
+    return fail(W4A4_ERR_NULL, "linear: a_codes, a_scales, blob and Y must be non-NULL");
+  if (fmt == W4A4_NVFP4 && !t_act) return fail(W4A4_ERR_NULL, "linear: NVFP4 needs t_act");
+  const size_t need = w4a4_linear_workspace_bytes(fmt, M, N, K);
+  if (need && (!workspace || ws_bytes < need))
+    return fail(W4A4_ERR_WORKSPACE, "linear: needs %zu workspace bytes, got %zu", need,
+                workspace ? ws_bytes : size_t(0));
+  if (!aligned(a_codes, 16) || !aligned(a_scales, 16) || !aligned(blob, 256) || !aligned(Y, 16) ||
+      (t_act && !aligned(t_act, 4)))
+    return fail(W4A4_ERR_ALIGN,
+                "linear: a_codes/a_scales/Y need 16-byte, blob 256-byte, t_act 4-byte alignment");
+  return hip_status(w4a4::launch_linear(fmt, M, N, K, a_codes, a_scales, t_act, blob, Y, workspace,
+                                        ws_bytes, static_cast<hipStream_t>(stream)),
+                    "linear launch");
+}
+
+const char* w4a4_last_error(void) { return g_err; }
+
+const char* w4a4_version(void) { return "w4a4 1.0 gfx950"; }
+
+}  // extern "C"

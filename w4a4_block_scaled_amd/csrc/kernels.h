@@ -1,0 +1,32 @@
+// Host-side launchers of the gfx950 kernels (internal to libw4a4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace w4a4 {
+
+// NVFP4 tensor-amax pre-pass: at most this many partial maxima (4 bytes each)
+// live in the quantize workspace.
+constexpr int kNvAmaxBlocks = 1024;
+
+hipError_t launch_quantize_act(int fmt, int64_t M, int64_t K, const void* X, const float* c,
+                               void* codes, void* scales, float* t_act, void* workspace,
+                               hipStream_t stream);
+
+hipError_t launch_pack_weight(int fmt, int64_t N, int64_t K, const void* codes,
+                              const void* scales, const float* t_w, const float* r, void* blob,
+                              hipStream_t stream);
+
+hipError_t launch_unpack_weight(int fmt, int64_t N, int64_t K, const void* blob, void* codes,
+                                void* scales, float* r, float* t_w, hipStream_t stream);
+
+hipError_t launch_linear(int fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
+                         const void* a_scales, const float* t_act, const void* blob, void* Y,
+                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+size_t linear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
+
+}  // namespace w4a4

@@ -1,0 +1,275 @@
+// Fused activation rescale + block quantization for gfx950.
+//
+// DualQuant Section 4.4: the column scale is applied inside the activation
+// quantization kernel (no separate launch) and the format-native per-row
+// block scale is computed on the rescaled activations; eq. (3) gives the
+// rescaling X~ = X diag(c).  Section 3 gives the formats (MXFP4 / MXINT4:
+// blocks of 32 with an E8M0 scale; NVFP4: blocks of 16 with a UE4M3 scale)
+// and the quantizer (nearest grid point, clipped).
+//
+// One thread owns 8 consecutive elements of a row (one 16-byte load of bf16,
+// one 4-byte store of codes).  A block of 32 (16) elements is owned by 4 (2)
+// consecutive lanes; its amax is reduced with cross-lane shuffles.  Every
+// rounding decision is exact: MX scales come from exponent bits, elements
+// are compared against exact midpoints, NVFP4 scale/element decisions are
+// taken against thresholds computed exactly in fp64.
+#include "common.h"
+#include "kernels.h"
+
+#include <float.h>
+
+namespace w4a4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+// floor(log2 a) for finite a > 0 (subnormals included)
+__device__ __forceinline__ int floor_log2(float a) {
+  const uint32_t u = __float_as_uint(a);
+  const int ef = (u >> 23) & 0xff;
+  if (ef) return ef - 127;
+  return (31 - __clz(u & 0x7fffffu)) - 149;
+}
+
+__device__ __forceinline__ void load8(const uint4* __restrict__ X, const float* __restrict__ c,
+                                      int64_t g, int64_t col8, float (&x)[8]) {
+  const uint4 v = X[g];
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+  if (c) {
+    const float4 c0 = reinterpret_cast<const float4*>(c)[2 * col8];
+    const float4 c1 = reinterpret_cast<const float4*>(c)[2 * col8 + 1];
+    const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = __fmul_rn(x[i], cc[i]);  // one rounded fp32 multiply
+  }
+}
+
+// E2M1 magnitude index of v (>= 0) in units of the block scale: count of
+// midpoints below v, ties to the even code.
+__device__ __forceinline__ uint32_t e2m1_index(float v) {
+  return (v > 0.25f) + (v >= 0.75f) + (v > 1.25f) + (v >= 1.75f) + (v > 2.5f) + (v >= 3.5f) +
+         (v > 5.0f);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void quantize_mx_kernel(
+    const uint4* __restrict__ X, const float* __restrict__ c, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t n_groups, int64_t K8) {
+  const int64_t g_raw = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const bool live = g_raw < n_groups;
+  const int64_t g = live ? g_raw : n_groups - 1;  // every lane joins the shuffles
+  const int64_t row = g / K8;
+  const int64_t col8 = g - row * K8;
+
+  float x[8];
+  load8(X, c, g, col8, x);
+
+  float amax = 0.0f;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = fabsf(x[i]);
+    bad |= !(a <= FLT_MAX);  // Inf or NaN
+    amax = fmaxf(amax, a);
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  bad |= __shfl_xor(bad, 1);
+  bad |= __shfl_xor(bad, 2);
+
+  int e = -127;
+  if (amax > 0.0f) e = max(-127, min(127, floor_log2(amax) - 2));
+
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = ldexpf(x[i], -e);  // exact power-of-two scaling
+    uint32_t code;
+    if (FMT == MXFP4) {
+      code = e2m1_index(fabsf(v)) | ((__float_as_uint(x[i]) >> 28) & 8u);
+    } else {
+      const float q = fminf(rintf(v), 7.0f);  // |v| < 8, so only +8 needs clipping
+      code = uint32_t(int(q)) & 15u;
+    }
+    word |= code << (4 * i);
+  }
+  uint32_t sbyte = uint32_t(e + 127);
+  if (bad) {
+    word = 0;
+    sbyte = 0xff;
+  }
+  if (!live) return;
+  codes[g] = word;
+  if ((col8 & 3) == 0) scales[row * (K8 / 4) + (col8 >> 2)] = uint8_t(sbyte);
+}
+
+// ----------------------------------------------------------------- NVFP4 --
+
+__global__ __launch_bounds__(kThreads) void absmax_partial_kernel(
+    const uint4* __restrict__ X, const float* __restrict__ c, float* __restrict__ partial,
+    int64_t n_groups, int64_t K8) {
+  float m = 0.0f;
+  for (int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x; g < n_groups;
+       g += int64_t(gridDim.x) * kThreads) {
+    float x[8];
+    load8(X, c, g, g % K8, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+    partial[blockIdx.x] = r;
+  }
+}
+
+// t = fp32(A) / 2688 with A the tensor amax; t = 1 when A = 0 (or t underflows).
+__global__ __launch_bounds__(kThreads) void tensor_scale_kernel(const float* __restrict__ partial,
+                                                                int n, float* __restrict__ t_out) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, partial[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) a = fmaxf(a, red[i]);
+    float t = __fdiv_rn(a, 2688.0f);
+    if (a == 0.0f || t == 0.0f) t = 1.0f;
+    *t_out = t;
+  }
+}
+
+__device__ __forceinline__ double e4m3_value(int code) {
+  const int e = code >> 3, m = code & 7;
+  return e == 0 ? ldexp(double(m), -9) : ldexp(double(8 + m), e - 10);
+}
+
+// UE4M3 code of the exact quotient a / D (a >= 0 finite fp32, D > 0), round
+// to nearest even, saturating at 448 (0x7E).  A first guess from the rounded
+// fp64 quotient is settled by one exact comparison against the midpoint above
+// it (a and midpoint * D are exact in fp64).
+__device__ __forceinline__ int e4m3_rne_ratio(float a, double D) {
+  if (!(a > 0.0f)) return 0;
+  const double u = double(a) / D;
+  if (u >= 448.0) return 0x7e;
+  int c;
+  if (u < 0.015625) {
+    c = int(u * 512.0);  // subnormal codes 0..7
+  } else {
+    const uint64_t b = uint64_t(__double_as_longlong(u));
+    const int E = int((b >> 52) & 0x7ff) - 1023;  // -6 .. 8
+    c = ((E + 7) << 3) | int((b >> 49) & 7);
+  }
+  const double thr = 0.5 * (e4m3_value(c) + e4m3_value(c + 1)) * D;
+  const double ad = double(a);
+  if (ad > thr) return c + 1;
+  if (ad == thr) return ((c + 1) & 1) ? c : c + 1;
+  return c;
+}
+
+// Smallest fp32 >= T (T >= 0, exact double).  With strict = true: smallest
+// fp32 > T.  Turns "|x| > T" / "|x| >= T" for fp32 |x| into "|x| >= result".
+__device__ __forceinline__ float f32_threshold(double T, bool strict) {
+  float f = float(T);
+  if (double(f) < T || (strict && double(f) == T)) f = nextafterf(f, INFINITY);
+  return f;
+}
+
+__global__ __launch_bounds__(kThreads) void quantize_nv_kernel(
+    const uint4* __restrict__ X, const float* __restrict__ c, const float* __restrict__ t_ptr,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t n_groups, int64_t K8) {
+  const int64_t g_raw = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const bool live = g_raw < n_groups;
+  const int64_t g = live ? g_raw : n_groups - 1;
+  const int64_t row = g / K8;
+  const int64_t col8 = g - row * K8;
+
+  float x[8];
+  load8(X, c, g, col8, x);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+
+  const float t = *t_ptr;
+  const int s = e4m3_rne_ratio(amax, 6.0 * double(t));  // 6 t is exact in fp64
+
+  uint32_t word = 0;
+  if (s == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= ((__float_as_uint(x[i]) >> 28) & 8u) << (4 * i);
+  } else {
+    const double unit = e4m3_value(s) * double(t);  // exact: 4 + 24 significant bits
+    const float t0 = f32_threshold(0.25 * unit, true);
+    const float t1 = f32_threshold(0.75 * unit, false);
+    const float t2 = f32_threshold(1.25 * unit, true);
+    const float t3 = f32_threshold(1.75 * unit, false);
+    const float t4 = f32_threshold(2.5 * unit, true);
+    const float t5 = f32_threshold(3.5 * unit, false);
+    const float t6 = f32_threshold(5.0 * unit, true);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a = fabsf(x[i]);
+      const uint32_t idx = (a >= t0) + (a >= t1) + (a >= t2) + (a >= t3) + (a >= t4) +
+                           (a >= t5) + (a >= t6);
+      word |= (idx | ((__float_as_uint(x[i]) >> 28) & 8u)) << (4 * i);
+    }
+  }
+  if (!live) return;
+  codes[g] = word;
+  if ((col8 & 1) == 0) scales[row * (K8 / 2) + (col8 >> 1)] = uint8_t(s);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_act(int fmt, int64_t M, int64_t K, const void* X, const float* c,
+                               void* codes, void* scales, float* t_act, void* workspace,
+                               hipStream_t stream) {
+  const int64_t n_groups = M * K / 8;
+  if (n_groups == 0) {
+    if (fmt == NVFP4) {
+      // an empty tensor has amax 0: t = 1
+      hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(kThreads), 0, stream,
+                         static_cast<const float*>(workspace), 0, t_act);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  }
+  const int64_t K8 = K / 8;
+  const dim3 grid(unsigned((n_groups + kThreads - 1) / kThreads));
+  const uint4* Xv = static_cast<const uint4*>(X);
+  uint32_t* cw = static_cast<uint32_t*>(codes);
+  uint8_t* sb = static_cast<uint8_t*>(scales);
+  if (fmt == MXFP4) {
+    hipLaunchKernelGGL(quantize_mx_kernel<MXFP4>, grid, dim3(kThreads), 0, stream, Xv, c, cw, sb,
+                       n_groups, K8);
+  } else if (fmt == MXINT4) {
+    hipLaunchKernelGGL(quantize_mx_kernel<MXINT4>, grid, dim3(kThreads), 0, stream, Xv, c, cw, sb,
+                       n_groups, K8);
+  } else {
+    float* partial = static_cast<float*>(workspace);
+    const int nparts = int(std::min<int64_t>(kNvAmaxBlocks, (n_groups + kThreads - 1) / kThreads));
+    hipLaunchKernelGGL(absmax_partial_kernel, dim3(nparts), dim3(kThreads), 0, stream, Xv, c,
+                       partial, n_groups, K8);
+    hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(kThreads), 0, stream, partial, nparts,
+                       t_act);
+    hipLaunchKernelGGL(quantize_nv_kernel, grid, dim3(kThreads), 0, stream, Xv, c, t_act, cw, sb,
+                       n_groups, K8);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace w4a4

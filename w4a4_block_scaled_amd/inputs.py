@@ -187,8 +187,9 @@ def adhoc_case(fmt: str, M: int, N: int, K: int, seed: int,
                weights: str = "prescaled") -> LinearCase:
     """A case of any shape with the single-linear activation law.
 
-    weights = "prescaled" (N(0,0.02)/(r c), quantized by the method) or
-    "codes" (random codes with E8M0 exponents in {-6..1}; MX formats only).
+    weights = "prescaled" (N(0,0.02)/(r c), quantized by the method),
+    "codes" (random codes with E8M0 exponents in {-6..1}; MX formats only)
+    or "none".
     """
     rx, rc, rr, rw = _rngs(seed, 4)
     family = "ue4m3" if fmt == "nvfp4" else "e8m0"
@@ -196,6 +197,8 @@ def adhoc_case(fmt: str, M: int, N: int, K: int, seed: int,
     r = admissible_scales(rr, N, family)
     x = outlier_activations(rx, M, K, int(round(2 * K / 256)), 50.0)
     case = LinearCase("adhoc", f"adhoc_{M}x{N}x{K}", fmt, M, N, K, x, c, r)
+    if weights == "none":
+        return case
     if weights == "codes":
         case.w_codes, case.w_scales = random_codes(rw, N, K, BLOCK[fmt], -6, 1)
     else:
