@@ -7,9 +7,8 @@
 // owning 16 bytes of row l%16 (for FP4 the canonical bytes of K chunk l/16;
 // for MXINT4 two 8-byte halves, see unit_dest).  A wave loads a
 // tile with one coalesced 16-byte load per lane.  The block scales are
-// regrouped so that one dword per lane carries the scales of several
-// consecutive K-steps (selected per K-step by the MFMA's byte select or by a
-// shift).
+// regrouped per K-step so that one dword per lane carries the scale bytes of
+// several 16-row groups (picked by the MFMA's byte select).
 #include <string.h>
 
 #include "common.h"
@@ -70,38 +69,36 @@ __global__ __launch_bounds__(kThreads) void unpack_codes_kernel(int fmt,
   dst[q] = src[(((n >> 4) * KS + ks) * 64 + lane) * 2 + (off >> 3)];
 }
 
-// canonical scale byte index of (lane, K-step slot j, half h) within group (ng, kg)
-__device__ __forceinline__ int64_t scale_src(int fmt, int64_t ng, int64_t kg, int lane, int j,
-                                             int h, int64_t KS, int64_t KB, bool* valid) {
-  const int64_t n = ng * 16 + (lane & 15);
+// Canonical scale byte index for byte b of scale word (sg, ks, lane);
+// *valid is false for bytes of row groups beyond N/16.
+__device__ __forceinline__ int64_t scale_src(int fmt, int64_t sg, int64_t ks, int lane, int b,
+                                             int64_t NG, int64_t KB, bool* valid) {
   const int cgrp = lane >> 4;
-  int64_t ks, blk;
+  int64_t ng, blk;
   if (fmt == NVFP4) {
-    ks = kg * 2 + j;
-    blk = ks * 8 + 2 * cgrp + h;
+    ng = sg * 2 + (b >> 1);
+    blk = ks * 8 + 2 * cgrp + (b & 1);
   } else {
-    ks = kg * 4 + j;
+    ng = sg * 4 + b;
     blk = ks * 4 + cgrp;
   }
-  *valid = ks < KS;
-  return n * KB + blk;
+  *valid = ng < NG;
+  return (ng * 16 + (lane & 15)) * KB + blk;
 }
 
 __global__ __launch_bounds__(kThreads) void pack_scales_kernel(
     int fmt, const uint8_t* __restrict__ src, uint32_t* __restrict__ dst, int64_t total,
-    int64_t KG, int64_t KS, int64_t KB) {
+    int64_t KS, int64_t NG, int64_t KB) {
   const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= total) return;
   const int lane = int(i & 63);
-  const int64_t grp = i >> 6;
-  const int64_t ng = grp / KG, kg = grp - ng * KG;
+  const int64_t t = i >> 6;
+  const int64_t sg = t / KS, ks = t - sg * KS;
   uint32_t w = 0;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const int j = fmt == NVFP4 ? (b >> 1) : b;
-    const int h = fmt == NVFP4 ? (b & 1) : 0;
     bool valid;
-    const int64_t s = scale_src(fmt, ng, kg, lane, j, h, KS, KB, &valid);
+    const int64_t s = scale_src(fmt, sg, ks, lane, b, NG, KB, &valid);
     if (valid) w |= uint32_t(src[s]) << (8 * b);
   }
   dst[i] = w;
@@ -109,19 +106,17 @@ __global__ __launch_bounds__(kThreads) void pack_scales_kernel(
 
 __global__ __launch_bounds__(kThreads) void unpack_scales_kernel(
     int fmt, const uint32_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t total,
-    int64_t KG, int64_t KS, int64_t KB) {
+    int64_t KS, int64_t NG, int64_t KB) {
   const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= total) return;
   const int lane = int(i & 63);
-  const int64_t grp = i >> 6;
-  const int64_t ng = grp / KG, kg = grp - ng * KG;
+  const int64_t t = i >> 6;
+  const int64_t sg = t / KS, ks = t - sg * KS;
   const uint32_t w = src[i];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const int j = fmt == NVFP4 ? (b >> 1) : b;
-    const int h = fmt == NVFP4 ? (b & 1) : 0;
     bool valid;
-    const int64_t s = scale_src(fmt, ng, kg, lane, j, h, KS, KB, &valid);
+    const int64_t s = scale_src(fmt, sg, ks, lane, b, NG, KB, &valid);
     if (valid) dst[s] = uint8_t(w >> (8 * b));
   }
 }
@@ -181,11 +176,11 @@ hipError_t launch_pack_weight(int fmt, int64_t N, int64_t K, const void* codes,
     hipLaunchKernelGGL(pack_codes_kernel, dim3(blocks_for(n_units)), dim3(kThreads), 0, stream, fmt,
                        static_cast<const uint2*>(codes), reinterpret_cast<uint2*>(b + L.code_off),
                        n_units, K / 16, L.KS);
-  const int64_t n_sw = L.NG * L.KG * 64;
+  const int64_t n_sw = L.NSG * L.KS * 64;
   if (n_sw)
     hipLaunchKernelGGL(pack_scales_kernel, dim3(blocks_for(n_sw)), dim3(kThreads), 0, stream, fmt,
                        static_cast<const uint8_t*>(scales),
-                       reinterpret_cast<uint32_t*>(b + L.scale_off), n_sw, L.KG, L.KS,
+                       reinterpret_cast<uint32_t*>(b + L.scale_off), n_sw, L.KS, L.NG,
                        K / block_size(fmt));
   hipLaunchKernelGGL(pack_tail_kernel, dim3(std::max(1u, std::min(64u, blocks_for(N)))),
                      dim3(kThreads), 0, stream, fmt, N, K, t_w, r, b);
@@ -201,11 +196,11 @@ hipError_t launch_unpack_weight(int fmt, int64_t N, int64_t K, const void* blob,
     hipLaunchKernelGGL(unpack_codes_kernel, dim3(blocks_for(n_units)), dim3(kThreads), 0, stream,
                        fmt, reinterpret_cast<const uint2*>(b + L.code_off),
                        static_cast<uint2*>(codes), n_units, K / 16, L.KS);
-  const int64_t n_sw = L.NG * L.KG * 64;
+  const int64_t n_sw = L.NSG * L.KS * 64;
   if (scales && n_sw)
     hipLaunchKernelGGL(unpack_scales_kernel, dim3(blocks_for(n_sw)), dim3(kThreads), 0, stream,
                        fmt, reinterpret_cast<const uint32_t*>(b + L.scale_off),
-                       static_cast<uint8_t*>(scales), n_sw, L.KG, L.KS, K / block_size(fmt));
+                       static_cast<uint8_t*>(scales), n_sw, L.KS, L.NG, K / block_size(fmt));
   if (r || t_w)
     hipLaunchKernelGGL(unpack_tail_kernel, dim3(std::max(1u, std::min(64u, blocks_for(N)))),
                        dim3(kThreads), 0, stream, fmt, N, K, b, r, t_w);
