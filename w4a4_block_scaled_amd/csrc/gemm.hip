@@ -175,8 +175,8 @@ __device__ __forceinline__ float epilogue_factor(int fmt, const float* __restric
 
 // ======================================================== tiled kernel ==
 //
-// Workgroup tile BN (n) x BM (m), 4 waves as 2 (n) x 2 (m), wave tile
-// BN/2 x BM/2.  Each 128-wide K-step is one pipeline stage.  A stage's
+// Workgroup tile BN (n) x BM (m), WN x WM waves (n x m), wave tile
+// BN/WN x BM/WM.  Each 128-wide K-step is one pipeline stage.  A stage's
 // operands (activation fragments, weight tiles, activation scales, weight
 // scale words) are copied global -> LDS by the waves' direct-to-LDS loads
 // (global_load_lds, no VGPR staging) into a ring of DEPTH stage buffers; up
@@ -194,10 +194,12 @@ __device__ __forceinline__ float epilogue_factor(int fmt, const float* __restric
 // Rows beyond M and row groups beyond N/16 are loaded from clamped valid
 // addresses; they only feed outputs that are never stored.
 
-template <int FMT, int BN, int BM, int DEPTH>
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
 struct TileCfg {
-  static constexpr int FN = BN / 32;  // weight fragments per wave
-  static constexpr int FM = BM / 32;  // activation fragments per wave
+  static constexpr int WAVES = WN * WM;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int FN = BN / 16 / WN;  // weight fragments per wave
+  static constexpr int FM = BM / 16 / WM;  // activation fragments per wave
   static constexpr int GPW = groups_per_scale_word(FMT);
   static constexpr int ASB = FMT == NVFP4 ? 8 : 4;  // activation scale bytes per row per K-step
   static constexpr int A_BYTES = BM * 64;
@@ -205,14 +207,15 @@ struct TileCfg {
   static constexpr int AS_BYTES = BM * ASB;
   static constexpr int WS_BYTES = (BN / 16 / GPW) * 256;
   static constexpr int STAGE = A_BYTES + W_BYTES + AS_BYTES + WS_BYTES;
-  static constexpr int A_DMA = BM / 64;        // 1 KiB copies per wave
-  static constexpr int W_DMA = BN / 64;
-  static constexpr int AS_DW = AS_BYTES / 16;  // scale dwords per wave
-  static constexpr int WS_DW = WS_BYTES / 16;
+  static constexpr int A_DMA = BM / 16 / WAVES;  // 1 KiB copies per wave
+  static constexpr int W_DMA = BN / 16 / WAVES;
+  static constexpr int AS_DW = AS_BYTES / 4 / WAVES;  // scale dwords per wave
+  static constexpr int WS_DW = WS_BYTES / 4 / WAVES;
   static constexpr int AS_DMA = (AS_DW + 63) / 64;
   static constexpr int WS_DMA = (WS_DW + 63) / 64;
   static constexpr int COPIES = A_DMA + W_DMA + AS_DMA + WS_DMA;  // per wave per stage
-  static_assert(BN % 64 == 0 && BM % 64 == 0, "tile sizes");
+  static_assert(A_DMA * WAVES * 16 == BM && W_DMA * WAVES * 16 == BN, "tile / wave split");
+  static_assert(FN % GPW == 0, "scale words per wave");
   static_assert(AS_DW <= 64 || AS_DW % 64 == 0, "activation scale copy split");
   static_assert(WS_DW <= 64 || WS_DW % 64 == 0, "weight scale copy split");
   static_assert(DEPTH * STAGE <= 160 * 1024, "LDS");
@@ -227,7 +230,7 @@ __device__ __forceinline__ constexpr int vmcnt_encoding(int v) {
 // this wave, then barrier.  The asm statement keeps LDS reads below it.
 template <int C, int DEPTH>
 __device__ __forceinline__ void stage_ready(int after) {
-  static_assert((DEPTH - 2) * C < 64, "vmcnt range");
+  static_assert((DEPTH - 2) * C < 64 && DEPTH <= 6, "vmcnt range");
   switch (after) {
     case 0: __builtin_amdgcn_s_waitcnt(vmcnt_encoding(0)); break;
     case 1: __builtin_amdgcn_s_waitcnt(vmcnt_encoding(C)); break;
@@ -249,10 +252,10 @@ struct TileArgs {
 };
 
 // Copy the operands of K-step ks into stage buffer `dst` (this wave's share).
-template <int FMT, int BN, int BM, int DEPTH>
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
 __device__ __forceinline__ void issue_stage(const TileArgs& t, int64_t ks, LDS uint8_t* dst,
                                             int wave, int lane) {
-  using C = TileCfg<FMT, BN, BM, DEPTH>;
+  using C = TileCfg<FMT, BN, BM, WN, WM, DEPTH>;
   const int r = lane & 15, c = lane >> 4;
   // activation fragments (FP4 fragment order for every format)
 #pragma unroll
@@ -303,16 +306,16 @@ __device__ __forceinline__ void issue_stage(const TileArgs& t, int64_t ks, LDS u
 // then run the MFMAs of the stage held in `cur`.  The two buffers are
 // distinct, which the restrict qualifiers state; the ordering against copies
 // of earlier steps is enforced by stage_ready().
-template <int FMT, int BN, int BM, int DEPTH>
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
 __device__ __forceinline__ void tile_step(const TileArgs& t, const LDS uint8_t* __restrict__ cur,
                                           LDS uint8_t* __restrict__ nxt, int64_t ks_next,
                                           bool issue, int wave, int lane,
-                                          v4f (&acc)[BN / 32][BM / 32]) {
-  using C = TileCfg<FMT, BN, BM, DEPTH>;
+                                          v4f (&acc)[BN / 16 / WN][BM / 16 / WM]) {
+  using C = TileCfg<FMT, BN, BM, WN, WM, DEPTH>;
   constexpr int FN = C::FN, FM = C::FM;
-  if (issue) issue_stage<FMT, BN, BM, DEPTH>(t, ks_next, nxt, wave, lane);
+  if (issue) issue_stage<FMT, BN, BM, WN, WM, DEPTH>(t, ks_next, nxt, wave, lane);
 
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % WN, wm = wave / WN;
   const int r = lane & 15, c = lane >> 4;
   const LDS u32x4* A = reinterpret_cast<const LDS u32x4*>(cur);
   const LDS u32x4* W = reinterpret_cast<const LDS u32x4*>(cur + C::A_BYTES);
@@ -380,12 +383,12 @@ __device__ __forceinline__ void tile_step(const TileArgs& t, const LDS uint8_t* 
   }
 }
 
-template <int FMT, int BN, int BM, int DEPTH>
-__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__global__ __launch_bounds__(64 * WN * WM, 1) void gemm_tile_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ t_act, const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y,
     int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_total, int per_xcd) {
-  using C = TileCfg<FMT, BN, BM, DEPTH>;
+  using C = TileCfg<FMT, BN, BM, WN, WM, DEPTH>;
   constexpr int FN = C::FN, FM = C::FM;
   // XCD-aware order: the hardware deals workgroups round-robin to the 8 XCDs;
   // give each XCD a contiguous run of tiles (m fastest), so the workgroups
@@ -422,19 +425,20 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(
   const int64_t KS = L.KS;
 #pragma unroll
   for (int s = 0; s < DEPTH - 1; ++s)
-    if (s < KS) issue_stage<FMT, BN, BM, DEPTH>(t, s, base + s * C::STAGE, wave, lane);
+    if (s < KS) issue_stage<FMT, BN, BM, WN, WM, DEPTH>(t, s, base + s * C::STAGE, wave, lane);
 
   for (int64_t s = 0; s < KS; ++s) {
     const int64_t after = KS - 1 - s < DEPTH - 2 ? KS - 1 - s : DEPTH - 2;
     stage_ready<C::COPIES, DEPTH>(int(after));
     const int64_t nx = s + DEPTH - 1;
-    tile_step<FMT, BN, BM, DEPTH>(t, base + (s % DEPTH) * C::STAGE, base + (nx % DEPTH) * C::STAGE,
-                                  nx, nx < KS, wave, lane, acc);
+    tile_step<FMT, BN, BM, WN, WM, DEPTH>(t, base + (s % DEPTH) * C::STAGE,
+                                          base + (nx % DEPTH) * C::STAGE, nx, nx < KS, wave, lane,
+                                          acc);
   }
 
   const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
   const float f = epilogue_factor(FMT, t_act, blob);
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave % WN, wm = wave / WN;
   v4f rs[FN];
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
@@ -535,15 +539,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   if (mvalid) store4(Y, N, m, ng * 16 + 4 * c, acc, v4f{r.x * f, r.y * f, r.z * f, r.w * f});
 }
 
-template <int FMT, int BN, int BM, int DEPTH>
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
 hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                        const float* t_act, const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
   const int tiles_n = int((N + BN - 1) / BN);
   const int tiles_m = int((M + BM - 1) / BM);
   const int total = tiles_n * tiles_m;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL((gemm_tile_kernel<FMT, BN, BM, DEPTH>), dim3(unsigned(per_xcd * 8)),
-                     dim3(256), 0, stream, ac, as, t_act, blob, Y, M, N, K, tiles_m, total,
+  hipLaunchKernelGGL((gemm_tile_kernel<FMT, BN, BM, WN, WM, DEPTH>), dim3(unsigned(per_xcd * 8)),
+                     dim3(64 * WN * WM), 0, stream, ac, as, t_act, blob, Y, M, N, K, tiles_m, total,
                      per_xcd);
   return hipGetLastError();
 }
@@ -551,18 +555,26 @@ hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const
 template <int FMT>
 hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                       const float* t_act, const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
-  if constexpr (FMT != NVFP4) {
+  if constexpr (FMT == NVFP4) {
+    // NVFP4 runs four fp16 MFMAs per fragment pair, so its K-step is long
+    // enough for 64 x 64 wave tiles at any shape, and it holds expanded fp16
+    // fragments that would not fit the register budget of a 128 x 64 tile.
+    return launch_tile<FMT, 256, 128, 4, 2, 5>(M, N, K, ac, as, t_act, blob, Y, stream);
+  } else {
     if (M <= 16) {
       hipLaunchKernelGGL(gemm_decode_kernel<FMT>, dim3(unsigned(N / 16)), dim3(64 * kDecodeWaves),
                          0, stream, ac, as, blob, Y, M, N, K);
       return hipGetLastError();
     }
+    // 8 waves per workgroup (two per SIMD, so one wave's memory and barrier
+    // stalls are covered by the other's MFMAs).  256x256 tiles (waves 2 x 4,
+    // 128 x 64 each) unless that leaves more than ~30% of the 256 CUs idle;
+    // then 256 (n) x 128 (m) tiles (waves 4 x 2, 64 x 64 each).
+    const int64_t big = ((N + 255) / 256) * ((M + 255) / 256);
+    if (big >= 180)
+      return launch_tile<FMT, 256, 256, 2, 4, 4>(M, N, K, ac, as, t_act, blob, Y, stream);
+    return launch_tile<FMT, 256, 128, 4, 2, 5>(M, N, K, ac, as, t_act, blob, Y, stream);
   }
-  // Tile shape: 256x256 when that still yields >= one workgroup per CU,
-  // else 256 (n) x 128 (m) for better occupancy of the 256 CUs.
-  const int64_t big = ((N + 255) / 256) * ((M + 255) / 256);
-  if (big >= 256) return launch_tile<FMT, 256, 256, 4>(M, N, K, ac, as, t_act, blob, Y, stream);
-  return launch_tile<FMT, 256, 128, 4>(M, N, K, ac, as, t_act, blob, Y, stream);
 }
 
 }  // namespace
