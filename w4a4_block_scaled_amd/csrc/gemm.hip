@@ -154,16 +154,24 @@ __device__ __forceinline__ int act_scale_mx(const uint8_t* __restrict__ s, int64
 
 // ------------------------------------------------------------ epilogue --
 
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16, round to nearest even (one V_CVT_PK_BF16_F32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, bf2));
+}
+
+// bf16(acc[i] * rs[i]) for i = 0..3, packed
+__device__ __forceinline__ u32x2 scale_pack4(const v4f& acc, const v4f& rs) {
+  return u32x2{pack_bf16x2(acc[0] * rs[0], acc[1] * rs[1]),
+               pack_bf16x2(acc[2] * rs[2], acc[3] * rs[3])};
+}
+
 // Y[m, n..n+3] = bf16(acc[i] * rs[i]) with rs = r[n..n+3] * f
 __device__ __forceinline__ void store4(uint16_t* __restrict__ Y, int64_t N, int64_t m, int64_t n,
                                        const v4f& acc, const v4f& rs) {
-  uint32_t b[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) b[i] = f32_to_bf16_rne(acc[i] * rs[i]);
-  uint2 v;
-  v.x = b[0] | (b[1] << 16);
-  v.y = b[2] | (b[3] << 16);
-  *reinterpret_cast<uint2*>(Y + m * N + n) = v;
+  *reinterpret_cast<u32x2*>(Y + m * N + n) = scale_pack4(acc, rs);
 }
 
 __device__ __forceinline__ float epilogue_factor(int fmt, const float* __restrict__ t_act,
@@ -447,16 +455,36 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_tile_kernel(
     const float4 r = *reinterpret_cast<const float4*>(R + ng * 16 + 4 * (lane >> 4));
     rs[i] = v4f{r.x * f, r.y * f, r.z * f, r.w * f};
   }
+  // Epilogue through LDS: every wave writes its BF16 tile (WMT rows x WNT
+  // columns) into its own region of the now idle stage ring, 16-byte chunks of
+  // a row XOR-swizzled by the row index (conflict-free writes of the MFMA
+  // layout), then reads it back row-major and stores full 16-byte chunks.
+  constexpr int WNT = BN / WN, WMT = BM / WM;  // wave tile: n x m
+  constexpr int CH = WNT / 8;                  // 16-byte chunks per row
+  constexpr int ROWB = 2 * WNT;
+  static_assert(WN * WM * WMT * ROWB <= DEPTH * C::STAGE, "epilogue staging");
+  __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
+  asm volatile("" ::: "memory");
+  LDS uint8_t* ep = base + wave * (WMT * ROWB);
+  const int c = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < FN; ++i) {
-    const int64_t ng = t.ng0 + wn * FN + i;
-    if (ng >= L.NG) continue;
-    const int64_t n = ng * 16 + 4 * (lane >> 4);
+  for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int64_t m = t.m0 + (wm * FM + j) * 16 + (lane & 15);
-      if (m < M) store4(Y, N, m, n, acc[i][j], rs[i]);
+      const int m = 16 * j + (lane & 15);
+      const int chunk = 2 * i + (c >> 1);
+      const int off = m * ROWB + ((chunk ^ (m % CH)) * 16) + 8 * (c & 1);
+      *reinterpret_cast<LDS u32x2*>(ep + off) = scale_pack4(acc[i][j], rs[i]);
     }
+  const int64_t nbase = (t.ng0 + wn * FN) * 16;
+  const int64_t mbase = t.m0 + wm * WMT;
+#pragma unroll
+  for (int q = 0; q < WMT * CH / 64; ++q) {
+    const int idx = q * 64 + lane;
+    const int row = idx / CH, chunk = idx % CH;
+    const u32x4 v = *reinterpret_cast<const LDS u32x4*>(ep + row * ROWB + ((chunk ^ (row % CH)) * 16));
+    const int64_t m = mbase + row, n = nbase + 8 * chunk;
+    if (m < M && n < N) *reinterpret_cast<u32x4*>(Y + m * N + n) = v;
   }
 }
 
