@@ -83,6 +83,7 @@ class Layer:
     def flops(self):
         return 2.0 * self.M * self.N * self.K
 
+    @property
     def gemm_bytes(self):
         G = w4.block_size(self.fmt)
         return (self.N * self.K / 2 + self.N * self.K / G + 4 * self.N + self.M * self.K / 2 +
@@ -159,7 +160,7 @@ def decode_bandwidth(dev, steps, copies=32):
     return out
 
 
-def cpu_baseline(workload, M, rows=64, cols=1024):
+def cpu_baseline(workload, M, rows=512, cols=4096):
     """The oracle as it stands, on a bounded sample: `rows` activation rows and
     `cols` weight rows of each linear (quantization of both plus the fp64
     linear).  Reported in the workload's unit (TFLOP/s of the sampled GEMM)."""
@@ -195,16 +196,34 @@ def cpu_baseline(workload, M, rows=64, cols=1024):
 
 
 def traffic_record(kernel):
-    """HBM bytes per launch from committed rocprofv3 counters, if they were
-    taken on the current kernel source; else None."""
+    """Measured HBM bytes per GEMM launch (FETCH_SIZE + WRITE_SIZE, each scaled
+    by its reading for a 1 GiB copy), averaged over the workload's launches,
+    from the committed rocprofv3 counter summary -- None unless the counters
+    were taken on the current GEMM source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     src = open(os.path.join(ROOT, "w4a4_block_scaled_amd", "csrc", "gemm.hip"), "rb").read()
-    if rec.get("gemm_source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("gemm_source_sha256") != hashlib.sha256(src).hexdigest() or kernel not in rec:
         return None
-    return rec.get(kernel)
+    return round(rec[kernel]["traffic_bytes_per_launch"])
+
+
+def traffic_probe(layers, dev):
+    """One device-to-device copy of exactly 1 GiB (the counter calibration:
+    its FETCH_SIZE / WRITE_SIZE should read 1 GiB each), then one pass of the
+    workload's kernels, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for L in layers:
+        L.quantize()
+        L.gemm()
+    torch.cuda.synchronize()
 
 
 def main():
@@ -216,6 +235,8 @@ def main():
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run a 1 GiB calibration copy and one pass of the kernels, print nothing")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -228,6 +249,9 @@ def main():
     log(f"[bench] building {a.workload} M={M} ({fmt})")
     layers = [Layer(c, dev) for c in inputs.workload_cases(a.workload, M=M)]
     torch.cuda.synchronize()
+    if a.traffic_probe:
+        traffic_probe(layers, dev)
+        return
     log("[bench] timing")
     ms, gemm_ms = time_steps(layers, a.steps, a.warmup)
     flops = sum(L.flops for L in layers)
@@ -237,6 +261,8 @@ def main():
     roof = {"bound": bound, "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12,
             "unit": unit, "frac": round(achieved / peak, 4),
             "traffic": traffic_record(f"gemm_{a.workload}_M{M}"),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes_per_launch": round(sum(L.gemm_bytes for L in layers) / len(layers)),
             "kernel": f"gemm_tile_kernel<{fmt}>" if M > 16 or fmt == "nvfp4" else f"gemm_decode_kernel<{fmt}>",
             "per_linear": {L.case.name: {"us": round(t * 1e3, 2),
                                          "TFLOP/s": round(L.flops / (t * 1e-3) / 1e12, 1),
