@@ -34,16 +34,23 @@ def test_pack_round_trip(fmt, N, K):
 
 
 def test_pack_layout_is_fragment_order():
-    """Tile (ng, ks) lane l holds the 16 canonical bytes of row 16 ng + l%16,
-    K chunk 4 ks + l/16."""
+    """MXFP4: tile (g, h) lane l holds the 16 canonical bytes of row 32 g + l%32,
+    K chunk 2 h + l/32 (32 codes each); rows of a partial last group are zero.
+    NVFP4: tile (g, h) lane l holds row 16 g + l%16, K chunk 4 h + l/16."""
     dev = device()
-    N, K = 32, 256
-    codes = torch.arange(N * K // 2, dtype=torch.int64).remainder(251).to(torch.uint8).reshape(N, K // 2)
-    scales = torch.zeros((N, K // 32), dtype=torch.uint8)
-    blob = w4.pack_weight(codes.to(dev), scales.to(dev), None, torch.ones(N).to(dev), "mxfp4").cpu()
-    frag = blob[256:256 + N * K // 2].reshape(N // 16, K // 128, 64, 16)
-    for ng in range(N // 16):
-        for ks in range(K // 128):
-            for l in range(64):
-                row, chunk = 16 * ng + l % 16, 4 * ks + l // 16
-                assert torch.equal(frag[ng, ks, l], codes[row, 16 * chunk:16 * chunk + 16])
+    for fmt, rows, kt, N in (("mxfp4", 32, 64, 48), ("nvfp4", 16, 128, 48)):
+        K = 256
+        G = w4.block_size(fmt)
+        codes = torch.arange(N * K // 2, dtype=torch.int64).remainder(251).to(torch.uint8).reshape(N, K // 2)
+        scales = torch.zeros((N, K // G), dtype=torch.uint8)
+        blob = w4.pack_weight(codes.to(dev), scales.to(dev), None, torch.ones(N).to(dev), fmt).cpu()
+        NG = -(-N // rows)
+        frag = blob[256:256 + NG * rows * K // 2].reshape(NG, K // kt, 64, 16)
+        per = 64 // rows  # 32-code chunks per lane group
+        for g in range(NG):
+            for h in range(K // kt):
+                for l in range(64):
+                    row, chunk = rows * g + l % rows, (kt // 32) * h + l // rows
+                    want = codes[row, 16 * chunk:16 * chunk + 16] if row < N else torch.zeros(16, dtype=torch.uint8)
+                    assert torch.equal(frag[g, h, l], want), (fmt, g, h, l)
+        assert per in (2, 4)

@@ -14,21 +14,29 @@ __host__ __device__ constexpr int block_size(int fmt) { return fmt == NVFP4 ? 16
 // Packed-weight blob.
 //
 //   [0, 256)            header (BlobHeader)
-//   [code_off, ...)     codes, MFMA fragment order: tile (ng, ks) covers output
-//                       rows 16*ng .. +16 and K range 128*ks .. +128 and is
-//                       1 KiB: lane l (0..63) owns 16 bytes = the 32 canonical
-//                       codes of row 16*ng + l%16, K = 128*ks + 32*(l/16) .. +32
-//                       (same nibble order as the canonical layout).
+//   [code_off, ...)     codes in 1 KiB fragment tiles, the operand order of the
+//                       MFMA that consumes them; rows beyond N are zero.
+//     MXFP4  (layout 2): tile (g, h) covers rows 32 g .. +32 and K 64 h .. +64;
+//                        lane l (0..63) owns 16 bytes = the 32 canonical codes
+//                        of row 32 g + l%32, K = 64 h + 32 (l/32) .. +32
+//                        (V_MFMA_SCALE_F32_32X32X64_F8F6F4 with FP4 operands).
+//     NVFP4, MXINT4 (layout 1): tile (g, h) covers rows 16 g .. +16 and K
+//                        128 h .. +128; lane l owns 16 bytes of row 16 g + l%16
+//                        (K chunk l/16 for NVFP4; the FP8 arrangement of the
+//                        16x16x128 MFMA for MXINT4, see pack.hip).
+//                       Tiles are ordered g-major: ((g * KT) + h) * 1 KiB.
 //   [scale_off, ...)    block scales as "scale words": one dword per
-//                       (row-group quad/pair sg, K-step ks, lane l), laid out
-//                       [sg][ks][lane].  Each byte serves one 16-row group so
-//                       that a single VGPR feeds the MFMA scale operand of
-//                       several weight fragments (byte picked by op_sel).
-//                         MX : 4 groups per word; byte j = scale of row
-//                              16*(4 sg + j) + l%16, block 4 ks + l/16.
-//                         NV : 2 groups per word; byte 2j+h = scale of row
-//                              16*(2 sg + j) + l%16, block 8 ks + 2 (l/16) + h.
-//                       Bytes of groups beyond N/16 are zero.
+//                       (row-group set sg, K tile h, lane l), laid out
+//                       [sg][h][lane].  Each byte serves one row group so that
+//                       a single VGPR feeds the MFMA scale operand of several
+//                       weight tiles (byte picked by op_sel).
+//                         MXFP4 : byte j = scale of row 32 (4 sg + j) + l%32,
+//                                 block 2 h + l/32.
+//                         MXINT4: byte j = scale of row 16 (4 sg + j) + l%16,
+//                                 block 4 h + l/16.
+//                         NVFP4 : byte 2j+b = scale of row 16 (2 sg + j) + l%16,
+//                                 block 8 h + 2 (l/16) + b.
+//                       Bytes of row groups beyond N are zero.
 //   [r_off, ...)        fp32 row scales r[N].
 // ---------------------------------------------------------------------------
 struct BlobHeader {
@@ -36,20 +44,26 @@ struct BlobHeader {
   uint32_t version;   // 1
   uint32_t format;
   int64_t N, K;
-  uint32_t layout;    // 1: 16x128 fragment tiles
+  uint32_t layout;    // 1: 16-row x 128-K tiles, 2: 32-row x 64-K tiles
   float t_w;
   uint64_t code_off, scale_off, r_off, total;
   uint8_t pad[256 - 8 - 4 - 4 - 16 - 4 - 4 - 32];
 };
 static_assert(sizeof(BlobHeader) == 256, "blob header must be 256 bytes");
 
+__host__ __device__ constexpr int blob_layout_id(int fmt) { return fmt == MXFP4 ? 2 : 1; }
+__host__ __device__ constexpr int tile_rows(int fmt) { return fmt == MXFP4 ? 32 : 16; }
+__host__ __device__ constexpr int tile_k(int fmt) { return fmt == MXFP4 ? 64 : 128; }
+__host__ __device__ constexpr int groups_per_scale_word(int fmt) { return fmt == NVFP4 ? 2 : 4; }
+
 struct BlobLayout {
-  int64_t N, K, NG, KS;
-  int64_t NSG;  // scale-word row groups: ceil(NG / groups_per_word)
+  int64_t N, K;
+  int64_t NG;   // row groups of tile_rows(fmt) rows (N rounded up)
+  int64_t KT;   // K tiles of tile_k(fmt)
+  int64_t KS;   // 128-wide K-steps
+  int64_t NSG;  // scale-word row-group sets: ceil(NG / groups_per_scale_word)
   int64_t code_off, scale_off, r_off, total;
 };
-
-__host__ __device__ constexpr int groups_per_scale_word(int fmt) { return fmt == NVFP4 ? 2 : 4; }
 
 __host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
@@ -57,13 +71,15 @@ __host__ __device__ inline BlobLayout blob_layout(int fmt, int64_t N, int64_t K)
   BlobLayout L;
   L.N = N;
   L.K = K;
-  L.NG = N / 16;
+  const int rows = tile_rows(fmt);
+  L.NG = (N + rows - 1) / rows;
+  L.KT = K / tile_k(fmt);
   L.KS = K / 128;
   const int gpw = groups_per_scale_word(fmt);
   L.NSG = (L.NG + gpw - 1) / gpw;
   L.code_off = 256;
-  L.scale_off = align256(L.code_off + N * K / 2);
-  L.r_off = align256(L.scale_off + L.NSG * L.KS * 64 * 4);
+  L.scale_off = align256(L.code_off + L.NG * rows * (K / 2));
+  L.r_off = align256(L.scale_off + L.NSG * L.KT * 64 * 4);
   L.total = align256(L.r_off + 4 * N);
   return L;
 }
@@ -72,6 +88,7 @@ __host__ __device__ inline BlobLayout blob_layout(int fmt, int64_t N, int64_t K)
 // Device helpers
 // ---------------------------------------------------------------------------
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));

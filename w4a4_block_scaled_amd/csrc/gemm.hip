@@ -39,6 +39,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
+// Direct-to-LDS copies: 16 (4) bytes per lane from `src`, lane l writing
+// `dst` + 16 l (4 l); `dst` is wave-uniform.
+__device__ __forceinline__ void lds_copy16(const void* src, LDS void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(const void* src, LDS void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+
 // ------------------------------------------------------------- MFMA ops --
 
 template <int OPW>
@@ -181,6 +190,65 @@ __device__ __forceinline__ float epilogue_factor(int fmt, const float* __restric
   return 1.0f;
 }
 
+// ------------------------------------------------------- tile epilogue --
+//
+// Y = bf16(acc * r[n] * f) for a wave tile of FN x FM fragments.  Every wave
+// writes its BF16 tile (16 FM rows x 16 FN columns) into its own region of the
+// idle stage ring, 16-byte chunks of a row XOR-swizzled by the row index
+// (conflict-free writes of the MFMA layout), then reads it back row-major and
+// stores full 16-byte chunks.  The caller has passed a barrier after the last
+// LDS read of the main loop.
+struct TileArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint4* Wc;
+  const uint32_t* Ws;
+  int64_t M, K2, KB, KS, NG, NSG;
+  int64_t m0, ng0;
+};
+
+template <int FN, int FM, int WN, int WM>
+__device__ __forceinline__ void tile_epilogue(const v4f (&acc)[FN][FM], LDS uint8_t* base,
+                                              const TileArgs& t, const uint8_t* __restrict__ blob,
+                                              const BlobLayout& L, float f,
+                                              uint16_t* __restrict__ Y, int64_t M, int64_t N,
+                                              int wave, int lane) {
+  const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
+  const int wn = wave % WN, wm = wave / WN;
+  v4f rs[FN];
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    int64_t ng = t.ng0 + wn * FN + i;
+    ng = ng < L.NG ? ng : L.NG - 1;
+    const float4 r = *reinterpret_cast<const float4*>(R + ng * 16 + 4 * (lane >> 4));
+    rs[i] = v4f{r.x * f, r.y * f, r.z * f, r.w * f};
+  }
+  constexpr int WNT = 16 * FN, WMT = 16 * FM;  // wave tile: n x m
+  constexpr int CH = WNT / 8;                  // 16-byte chunks per row
+  constexpr int ROWB = 2 * WNT;
+  LDS uint8_t* ep = base + wave * (WMT * ROWB);
+  const int c = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = 16 * j + (lane & 15);
+      const int chunk = 2 * i + (c >> 1);
+      const int off = m * ROWB + ((chunk ^ (m % CH)) * 16) + 8 * (c & 1);
+      *reinterpret_cast<LDS u32x2*>(ep + off) = scale_pack4(acc[i][j], rs[i]);
+    }
+  const int64_t nbase = (t.ng0 + wn * FN) * 16;
+  const int64_t mbase = t.m0 + wm * WMT;
+#pragma unroll
+  for (int q = 0; q < WMT * CH / 64; ++q) {
+    const int idx = q * 64 + lane;
+    const int row = idx / CH, chunk = idx % CH;
+    const u32x4 v = *reinterpret_cast<const LDS u32x4*>(ep + row * ROWB + ((chunk ^ (row % CH)) * 16));
+    const int64_t m = mbase + row, n = nbase + 8 * chunk;
+    if (m < M && n < N) *reinterpret_cast<u32x4*>(Y + m * N + n) = v;
+  }
+}
+
 // ======================================================== tiled kernel ==
 //
 // Workgroup tile BN (n) x BM (m), WN x WM waves (n x m), wave tile
@@ -249,15 +317,6 @@ __device__ __forceinline__ void stage_ready(int after) {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-
-struct TileArgs {
-  const uint8_t* a_codes;
-  const uint8_t* a_scales;
-  const uint4* Wc;
-  const uint32_t* Ws;
-  int64_t M, K2, KB, KS, NG, NSG;
-  int64_t m0, ng0;
-};
 
 // Copy the operands of K-step ks into stage buffer `dst` (this wave's share).
 template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
@@ -444,40 +503,674 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_tile_kernel(
                                           acc);
   }
 
-  const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
-  const float f = epilogue_factor(FMT, t_act, blob);
-  const int wn = wave % WN, wm = wave / WN;
-  v4f rs[FN];
-#pragma unroll
-  for (int i = 0; i < FN; ++i) {
-    int64_t ng = t.ng0 + wn * FN + i;
-    ng = ng < L.NG ? ng : L.NG - 1;
-    const float4 r = *reinterpret_cast<const float4*>(R + ng * 16 + 4 * (lane >> 4));
-    rs[i] = v4f{r.x * f, r.y * f, r.z * f, r.w * f};
-  }
-  // Epilogue through LDS: every wave writes its BF16 tile (WMT rows x WNT
-  // columns) into its own region of the now idle stage ring, 16-byte chunks of
-  // a row XOR-swizzled by the row index (conflict-free writes of the MFMA
-  // layout), then reads it back row-major and stores full 16-byte chunks.
-  constexpr int WNT = BN / WN, WMT = BM / WM;  // wave tile: n x m
-  constexpr int CH = WNT / 8;                  // 16-byte chunks per row
-  constexpr int ROWB = 2 * WNT;
-  static_assert(WN * WM * WMT * ROWB <= DEPTH * C::STAGE, "epilogue staging");
+  static_assert(WN * WM * (16 * FM) * (32 * FN) <= DEPTH * C::STAGE, "epilogue staging");
   __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
   asm volatile("" ::: "memory");
-  LDS uint8_t* ep = base + wave * (WMT * ROWB);
-  const int c = lane >> 4;
+  tile_epilogue<FN, FM, WN, WM>(acc, base, t, blob, L, epilogue_factor(FMT, t_act, blob), Y, M, N,
+                                wave, lane);
+}
+
+// ===================================================== MX tiled kernel ==
+//
+// MXFP4 / MXINT4 for M > 16.  Workgroup tile BN (n) x BM (m) with WN x WM
+// waves, one 128-wide K-step per stage of a DEPTH-deep LDS ring filled by
+// direct-to-LDS copies, as above, but software-pipelined inside each wave:
+// while the MFMAs of K-step s run from registers, the wave already reads the
+// fragments of K-step s+1 from LDS (weight fragment i is re-read right after
+// its last MFMA; activation fragments, scales and scale words are double
+// buffered).  Once every wave holds K-step s+1 in registers the barrier at the
+// top of the next iteration releases its buffer, and the copy of K-step
+// s+1+DEPTH goes there, so DEPTH-1 stages stay in flight.
+//
+// LDS stage buffer: [A codes: BM/16 x 1 KiB][W codes: BN/16 x 1 KiB]
+// [scales: 256 B per wave].  One 4-byte copy per wave per stage fills that
+// wave's scale chunk: dwords [0, AS_DW) are the activation scale dwords (the
+// four blocks of one row) of rows wave*AS_DW.., dwords [AS_DW, AS_DW+WS_DW)
+// the weight scale words wave*WS_DW.. of the tile (word d: group d/64, lane
+// d%64); the remaining lanes copy a duplicate into padding.
+
+template <int BN, int BM, int WN, int WM, int DEPTH>
+struct MxCfg {
+  static constexpr int WAVES = WN * WM;
+  static constexpr int FN = BN / 16 / WN;
+  static constexpr int FM = BM / 16 / WM;
+  static constexpr int A_BYTES = BM * 64;
+  static constexpr int W_BYTES = BN * 64;
+  static constexpr int SC_BYTES = WAVES * 256;
+  static constexpr int STAGE = A_BYTES + W_BYTES + SC_BYTES;
+  static constexpr int A_DMA = BM / 16 / WAVES;
+  static constexpr int W_DMA = BN / 16 / WAVES;
+  static constexpr int AS_DW = BM / WAVES;  // activation scale rows per wave
+  static constexpr int WS_DW = BN / WAVES;  // weight scale words per wave (BN/64 groups x 64)
+  static constexpr int COPIES = A_DMA + W_DMA + 1;
+  static_assert(A_DMA * WAVES * 16 == BM && W_DMA * WAVES * 16 == BN, "tile / wave split");
+  static_assert(AS_DW + WS_DW <= 64, "scale chunk");
+  static_assert((AS_DW & (AS_DW - 1)) == 0 && (WS_DW & (WS_DW - 1)) == 0, "scale chunk split");
+  static_assert(FN % 4 == 0 && BN % 64 == 0, "scale words");
+  static_assert(DEPTH * STAGE <= 160 * 1024, "LDS");
+  static_assert(WAVES * (16 * FM) * (32 * FN) <= DEPTH * STAGE, "epilogue staging");
+};
+
+// s_waitcnt vmcnt(v) lgkmcnt(0)
+__device__ __forceinline__ constexpr int vm_lgkm0_encoding(int v) {
+  return (v & 15) | (7 << 4) | (0 << 8) | (((v >> 4) & 3) << 14);
+}
+
+// Wait until this wave has at most `after` stages of copies outstanding and
+// no LDS reads in flight, then barrier.
+template <int C, int DEPTH>
+__device__ __forceinline__ void mx_sync(int after) {
+  static_assert((DEPTH - 1) * C < 64 && DEPTH <= 6, "vmcnt range");
+  switch (after) {
+    case 0: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(C)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(2 * C)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(3 * C)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(4 * C)); break;
+    default: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(5 * C)); break;
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// (FMT only keeps the specializations of different kernels apart.)
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__device__ __forceinline__ void mx_issue(const TileArgs& t, int64_t ks, LDS uint8_t* dst, int wave,
+                                         int lane) {
+  using C = MxCfg<BN, BM, WN, WM, DEPTH>;
+  const int r = lane & 15, c = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < C::A_DMA; ++i) {
+    const int f = wave * C::A_DMA + i;
+    int64_t row = t.m0 + 16 * f + r;
+    row = row < t.M ? row : t.M - 1;
+    __builtin_amdgcn_global_load_lds(t.a_codes + row * t.K2 + ks * 64 + 16 * c, dst + f * 1024,
+                                     16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < C::W_DMA; ++i) {
+    const int f = wave * C::W_DMA + i;
+    int64_t ng = t.ng0 + f;
+    ng = ng < t.NG ? ng : t.NG - 1;
+    __builtin_amdgcn_global_load_lds(t.Wc + (ng * t.KS + ks) * 64 + lane,
+                                     dst + C::A_BYTES + f * 1024, 16, 0, 0);
+  }
+  const bool is_a = lane < C::AS_DW;
+  const bool is_w = !is_a && lane < C::AS_DW + C::WS_DW;
+  int64_t row = t.m0 + wave * C::AS_DW + (is_a ? lane : 0);
+  row = row < t.M ? row : t.M - 1;
+  const int d = wave * C::WS_DW + (is_w ? lane - C::AS_DW : 0);
+  int64_t sg = t.ng0 / 4 + d / 64;
+  sg = sg < t.NSG ? sg : t.NSG - 1;
+  const uint8_t* src = is_w ? reinterpret_cast<const uint8_t*>(t.Ws + (sg * t.KS + ks) * 64 + (d & 63))
+                            : t.a_scales + row * t.KB + ks * 4;
+  __builtin_amdgcn_global_load_lds(src, dst + C::A_BYTES + C::W_BYTES + wave * 256, 4, 0, 0);
+}
+
+// Register copies of one K-step's operands for a wave (besides the weight
+// fragments, which live in their own array).
+template <int FMT, int FN, int FM>
+struct MxFrags {
+  u32x4 a[FM];
+  int sa[FM];
+  uint32_t sw[FN / 4];
+};
+
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__device__ __forceinline__ u32x4 mx_load_w(const LDS uint8_t* __restrict__ st, int wn, int i,
+                                           int lane) {
+  using C = MxCfg<BN, BM, WN, WM, DEPTH>;
+  const LDS u32x4* W = reinterpret_cast<const LDS u32x4*>(st + C::A_BYTES);
+  return W[(wn * C::FN + i) * 64 + lane];
+}
+
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__device__ __forceinline__ void mx_load_rest(const LDS uint8_t* __restrict__ st, int wn, int wm,
+                                             int lane, MxFrags<FMT, BN / 16 / WN, BM / 16 / WM>& fr) {
+  using C = MxCfg<BN, BM, WN, WM, DEPTH>;
+  const int r = lane & 15, c = lane >> 4;
+  const LDS u32x4* A = reinterpret_cast<const LDS u32x4*>(st);
+  const LDS uint8_t* SC = st + C::A_BYTES + C::W_BYTES;
+#pragma unroll
+  for (int j = 0; j < C::FM; ++j) {
+    const int f = wm * C::FM + j;
+    if constexpr (FMT == MXINT4) {
+      // half (c & 1) of blocks c >> 1 and 2 + (c >> 1) of row r
+      const LDS u32x2* b = reinterpret_cast<const LDS u32x2*>(A + f * 64);
+      const u32x2 lo = b[(r + 16 * (c >> 1)) * 2 + (c & 1)];
+      const u32x2 hi = b[(r + 16 * (2 + (c >> 1))) * 2 + (c & 1)];
+      fr.a[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    } else {
+      fr.a[j] = A[f * 64 + lane];
+    }
+    const int R = 16 * f + r;
+    fr.sa[j] = SC[(R / C::AS_DW) * 256 + (R % C::AS_DW) * 4 + c];
+  }
+#pragma unroll
+  for (int q = 0; q < C::FN / 4; ++q) {
+    const int d = (wn * C::FN / 4 + q) * 64 + lane;
+    fr.sw[q] = *reinterpret_cast<const LDS uint32_t*>(SC + (d / C::WS_DW) * 256 +
+                                                      (C::AS_DW + d % C::WS_DW) * 4);
+  }
+}
+
+template <int FMT, int FN, int FM>
+__device__ __forceinline__ void mx_mfma_row(v4f (&acc)[FN][FM], int i, const u32x4& wf,
+                                            const MxFrags<FMT, FN, FM>& fr,
+                                            const v8i (&a8)[FMT == MXINT4 ? FM : 1]) {
+  if constexpr (FMT == MXFP4) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      acc[i][j] = mfma_fp4(i % 4, wf, fr.a[j], acc[i][j], int(fr.sw[i / 4]), fr.sa[j]);
+  } else {
+    const v8i w8 = int4_frag_to_fp8(wf);
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      acc[i][j] = mfma_fp8(i % 4, w8, a8[j], acc[i][j], int(fr.sw[i / 4]), fr.sa[j]);
+  }
+}
+
+// MFMAs of the K-step held in registers, while the fragments of the next
+// K-step are read from its stage buffer `nx`.
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__device__ __forceinline__ void mx_step(const LDS uint8_t* __restrict__ nx, int wn, int wm, int lane,
+                                        v4f (&acc)[BN / 16 / WN][BM / 16 / WM],
+                                        u32x4 (&wf)[BN / 16 / WN],
+                                        MxFrags<FMT, BN / 16 / WN, BM / 16 / WM>& fr) {
+  constexpr int FN = BN / 16 / WN, FM = BM / 16 / WM;
+  v8i a8[FMT == MXINT4 ? FM : 1];
+  if constexpr (FMT == MXINT4) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) a8[j] = int4_frag_to_fp8(fr.a[j]);
+  }
+  MxFrags<FMT, FN, FM> fn;
+  mx_load_rest<FMT, BN, BM, WN, WM, DEPTH>(nx, wn, wm, lane, fn);
+  // the last weight fragment is double-buffered so that no LDS read has to
+  // wait for the final MFMA
+  const u32x4 wlast = mx_load_w<FMT, BN, BM, WN, WM, DEPTH>(nx, wn, FN - 1, lane);
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    mx_mfma_row<FMT, FN, FM>(acc, i, wf[i], fr, a8);
+    if (i < FN - 1) wf[i] = mx_load_w<FMT, BN, BM, WN, WM, DEPTH>(nx, wn, i, lane);
+  }
+  wf[FN - 1] = wlast;
+  fr = fn;
+}
+
+// Instruction interleave of one loop iteration: the copies of the next stage
+// and the reads of the next K-step's activation fragments and scales go
+// between the first MFMAs, the weight-fragment reads after the MFMAs of the
+// row they replace.
+template <int FN, int FM, int COPIES>
+__device__ __forceinline__ void mx_schedule() {
+  constexpr int MFMA = 0x008, DS_READ = 0x100, VMEM = 0x020;
+  constexpr int REST = FM + FM + FN / 4 + 1;  // A frags (up to 2 reads each), scales, last W
+#pragma unroll
+  for (int k = 0; k < COPIES; ++k) {
+    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(VMEM, 1, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < REST; ++k) {
+    __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(DS_READ, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < FN - 1; ++i) {
+    __builtin_amdgcn_sched_group_barrier(MFMA, FM, 0);
+    __builtin_amdgcn_sched_group_barrier(DS_READ, 1, 0);
+  }
+}
+
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int tiles_m, int tiles_total, int per_xcd) {
+  using C = MxCfg<BN, BM, WN, WM, DEPTH>;
+  constexpr int FN = C::FN, FM = C::FM;
+  const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (tile >= tiles_total) return;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+
+  const BlobLayout L = blob_layout(FMT, N, K);
+  TileArgs t;
+  t.a_codes = a_codes;
+  t.a_scales = a_scales;
+  t.Wc = reinterpret_cast<const uint4*>(blob + L.code_off);
+  t.Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+  t.M = M;
+  t.K2 = K / 2;
+  t.KB = K / 32;
+  t.KS = L.KS;
+  t.NG = L.NG;
+  t.NSG = L.NSG;
+  t.m0 = int64_t(tm) * BM;
+  t.ng0 = int64_t(tn) * (BN / 16);
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * C::STAGE];
+  LDS uint8_t* base = (LDS uint8_t*)smem;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wn = wave % WN, wm = wave / WN;
+
+  v4f acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int m = 16 * j + (lane & 15);
-      const int chunk = 2 * i + (c >> 1);
-      const int off = m * ROWB + ((chunk ^ (m % CH)) * 16) + 8 * (c & 1);
-      *reinterpret_cast<LDS u32x2*>(ep + off) = scale_pack4(acc[i][j], rs[i]);
+    for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t KS = L.KS;
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s)
+    if (s < KS) mx_issue<FMT, BN, BM, WN, WM, DEPTH>(t, s, base + s * C::STAGE, wave, lane);
+  mx_sync<C::COPIES, DEPTH>(int((KS < DEPTH ? KS : DEPTH) - 1));
+
+  u32x4 wf[FN];
+  MxFrags<FMT, FN, FM> fr;
+#pragma unroll
+  for (int i = 0; i < FN; ++i) wf[i] = mx_load_w<FMT, BN, BM, WN, WM, DEPTH>(base, wn, i, lane);
+  mx_load_rest<FMT, BN, BM, WN, WM, DEPTH>(base, wn, wm, lane, fr);
+
+  // Main part: every iteration also starts the copy of K-step s+DEPTH (one
+  // basic block, so the MFMAs, LDS reads and copies can be interleaved);
+  // tail: the last DEPTH-1 iterations have nothing left to copy.
+  int64_t s = 0;
+  for (; s + DEPTH < KS; ++s) {
+    mx_sync<C::COPIES, DEPTH>(DEPTH - 2);
+    mx_issue<FMT, BN, BM, WN, WM, DEPTH>(t, s + DEPTH, base + (s % DEPTH) * C::STAGE, wave, lane);
+    mx_step<FMT, BN, BM, WN, WM, DEPTH>(base + ((s + 1) % DEPTH) * C::STAGE, wn, wm, lane, acc, wf,
+                                        fr);
+    mx_schedule<FN, FM, C::COPIES>();
+  }
+  for (; s + 1 < KS; ++s) {
+    mx_sync<C::COPIES, DEPTH>(int(KS - (s + 2)));
+    mx_step<FMT, BN, BM, WN, WM, DEPTH>(base + ((s + 1) % DEPTH) * C::STAGE, wn, wm, lane, acc, wf,
+                                        fr);
+    mx_schedule<FN, FM, 0>();
+  }
+  {
+    v8i a8[FMT == MXINT4 ? FM : 1];
+    if constexpr (FMT == MXINT4) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) a8[j] = int4_frag_to_fp8(fr.a[j]);
     }
-  const int64_t nbase = (t.ng0 + wn * FN) * 16;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) mx_mfma_row<FMT, FN, FM>(acc, i, wf[i], fr, a8);
+  }
+
+  __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
+  asm volatile("" ::: "memory");
+  tile_epilogue<FN, FM, WN, WM>(acc, base, t, blob, L, epilogue_factor(FMT, nullptr, blob), Y, M,
+                                N, wave, lane);
+}
+
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+hipError_t launch_mx(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                     const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  const int tiles_n = int((N + BN - 1) / BN);
+  const int tiles_m = int((M + BM - 1) / BM);
+  const int total = tiles_n * tiles_m;
+  const int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL((gemm_mx_kernel<FMT, BN, BM, WN, WM, DEPTH>), dim3(unsigned(per_xcd * 8)),
+                     dim3(64 * WN * WM), 0, stream, ac, as, blob, Y, M, N, K, tiles_m, total,
+                     per_xcd);
+  return hipGetLastError();
+}
+
+// ================================================ MXFP4, 32x32x64 MFMA ==
+//
+// MXFP4 runs on V_MFMA_SCALE_F32_32X32X64_F8F6F4: a single wave per SIMD
+// keeps that instruction's pipeline full, so a workgroup is 4 waves (2 x 2),
+// each with a 128 x 128 (or 128 x 64) output tile held in 256 (128)
+// accumulator registers.  Operand fragments (1 KiB: 32 rows x 64 K, lane l
+// holding the 32 codes of row l%32, K chunk l/32) come from the packed
+// weight tiles as they are and from the canonical activation rows.  Scales:
+// lane l of a fragment supplies the E8M0 scale of its row and block;
+// weights take theirs from a scale word (byte = row group, op_sel), the
+// activations from the row's scale dword shifted by 8 (l/32) (op_sel 0 or 2
+// for the first or second 64-K half of the K-step).
+//
+// Pipeline: a DEPTH-deep LDS ring of 128-wide K-steps filled by
+// direct-to-LDS copies; every wave holds the fragments of K-step s in
+// registers while it reads those of K-step s+1 and runs the MFMAs of s.
+
+template <int OPW, int OPA>
+__device__ __forceinline__ v16f mfma32_fp4_op(const u32x4& w, const u32x4& a, const v16f& acc,
+                                              int sw, int sa) {
+  const v8i A = {int(w.x), int(w.y), int(w.z), int(w.w), 0, 0, 0, 0};
+  const v8i B = {int(a.x), int(a.y), int(a.z), int(a.w), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, acc, 4, 4, OPW, sw, OPA, sa);
+}
+
+template <int BN, int BM, int DEPTH>
+struct Fp4Cfg {
+  static constexpr int WN = 2, WM = 2, WAVES = 4;
+  static constexpr int FN = BN / WN / 32;  // 32-row weight groups per wave
+  static constexpr int FM = BM / WM / 32;  // 32-row activation groups per wave
+  // 1 KiB copies per K-step: activations 16 rows x 64 B, weights one fragment tile
+  static constexpr int A_TILES = BM / 16, W_TILES = BN / 32 * 2;
+  static constexpr int A_BYTES = A_TILES * 1024, W_BYTES = W_TILES * 1024;
+  static constexpr int AS_DW = BM / WAVES;                // activation scale dwords per wave
+  static constexpr int WS_DW = BN / 128 * 2 * 64 / WAVES;  // weight scale words per wave
+  static constexpr int SC_COPIES = (AS_DW + WS_DW + 63) / 64;
+  static constexpr int SCW = SC_COPIES * 256;             // scale chunk bytes per wave
+  static constexpr int STAGE = A_BYTES + W_BYTES + WAVES * SCW;
+  static constexpr int A_DMA = A_TILES / WAVES, W_DMA = W_TILES / WAVES;
+  static constexpr int COPIES = A_DMA + W_DMA + SC_COPIES;
+  static constexpr int EPI_BYTES = WAVES * (32 * FM) * (64 * FN);
+  static_assert(A_DMA * WAVES == A_TILES && W_DMA * WAVES == W_TILES, "tile / wave split");
+  static_assert(BN % 128 == 0 && FN >= 1 && FN <= 4 && FM >= 1, "wave tile");
+  static_assert((AS_DW & (AS_DW - 1)) == 0 && (WS_DW & (WS_DW - 1)) == 0, "scale chunk split");
+  static_assert(DEPTH * STAGE <= 160 * 1024 && EPI_BYTES <= DEPTH * STAGE, "LDS");
+  static_assert((DEPTH - 1) * COPIES < 64, "vmcnt range");
+};
+
+struct Fp4Args {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint4* Wc;
+  const uint32_t* Ws;
+  int64_t M, K2, KB, KT, NG, NSG;
+  int64_t m0, g0;  // first activation row, first 32-row weight group
+};
+
+template <int FN, int FM>
+struct Fp4Frags {
+  u32x4 w[FN][2];
+  u32x4 a[FM][2];
+  int sa[FM];
+  int sw[2];
+};
+
+// Read a wave's fragments of one stage buffer.
+template <int BN, int BM, int DEPTH>
+__device__ __forceinline__ void fp4_read(const LDS uint8_t* __restrict__ st, int wn, int wm, int lane,
+                                         Fp4Frags<BN / 64, BM / 64>& fr) {
+  using C = Fp4Cfg<BN, BM, DEPTH>;
+  const LDS uint8_t* SC = st + C::A_BYTES + C::W_BYTES;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j)
+      // fragment lane l: row 32 g + l%32 (16-row block 2 g + (l%32)/16),
+      // 16-byte chunk 2 hh + l/32 of its K-step bytes
+      fr.a[j][hh] = *reinterpret_cast<const LDS u32x4*>(
+          st + (2 * (wm * C::FM + j) + ((lane >> 4) & 1)) * 1024 + (2 * hh + (lane >> 5)) * 256 +
+          (lane & 15) * 16);
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+      fr.w[i][hh] = *reinterpret_cast<const LDS u32x4*>(st + C::A_BYTES + ((wn * C::FN + i) * 2 + hh) * 1024 +
+                                                        lane * 16);
+    const int e = ((wn * C::FN / 4) * 2 + hh) * 64 + lane;
+    const uint32_t wsw = *reinterpret_cast<const LDS uint32_t*>(SC + (e / C::WS_DW) * C::SCW +
+                                                                (C::AS_DW + e % C::WS_DW) * 4);
+    // byte i of the shifted word is the scale of the wave's weight group i
+    fr.sw[hh] = int(C::FN == 4 ? wsw : wsw >> (8 * ((wn * C::FN) & 3)));
+  }
+#pragma unroll
+  for (int j = 0; j < C::FM; ++j) {
+    const int R = 32 * (wm * C::FM + j) + (lane & 31);
+    const uint32_t d = *reinterpret_cast<const LDS uint32_t*>(SC + (R / C::AS_DW) * C::SCW + (R % C::AS_DW) * 4);
+    fr.sa[j] = int(d >> (8 * (lane >> 5)));
+  }
+}
+
+// MFMAs of one K-step: weight group I (scale byte I of the word), 64-K half
+// H (activation scale byte 2H), every activation group j.
+template <int FN, int FM, int I, int H>
+struct Fp4Row {
+  static __device__ __forceinline__ void run(v16f (&acc)[FN][FM], const Fp4Frags<FN, FM>& fr) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      acc[I][j] = mfma32_fp4_op<I, 2 * H>(fr.w[I][H], fr.a[j][H], acc[I][j], fr.sw[H], fr.sa[j]);
+    if constexpr (I + 1 < FN) Fp4Row<FN, FM, I + 1, H>::run(acc, fr);
+    else if constexpr (H == 0) Fp4Row<FN, FM, 0, 1>::run(acc, fr);
+  }
+};
+
+template <int FN, int FM>
+__device__ __forceinline__ void fp4_mfmas(v16f (&acc)[FN][FM], const Fp4Frags<FN, FM>& fr) {
+  Fp4Row<FN, FM, 0, 0>::run(acc, fr);
+}
+
+// s_waitcnt vmcnt(v) lgkmcnt(0), then barrier
+template <int C, int DEPTH>
+__device__ __forceinline__ void fp4_sync(int after) {
+  switch (after) {
+    case 0: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(C)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(2 * C)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(3 * C)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(4 * C)); break;
+    default: __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(5 * C)); break;
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Copy number k of a wave's share of K-step ks (activation copies, weight
+// copies, then scale copies), so that the copies can be spread over a step.
+template <int BN, int BM, int DEPTH>
+__device__ __forceinline__ void fp4_copy(const Fp4Args& t, int64_t ks, LDS uint8_t* dst, int wave,
+                                         int lane, int k) {
+  using C = Fp4Cfg<BN, BM, DEPTH>;
+  if (k < C::A_DMA) {
+    // 16 rows x 64 contiguous bytes (one K-step): lane l takes the 16-byte
+    // chunk l/16 of row 16 f + l%16
+    const int f = wave * C::A_DMA + k;
+    int64_t row = t.m0 + 16 * f + (lane & 15);
+    row = row < t.M ? row : t.M - 1;
+    lds_copy16(t.a_codes + row * t.K2 + ks * 64 + (lane >> 4) * 16, dst + f * 1024);
+  } else if (k < C::A_DMA + C::W_DMA) {
+    const int f = wave * C::W_DMA + (k - C::A_DMA);
+    int64_t g = t.g0 + (f >> 1);
+    g = g < t.NG ? g : t.NG - 1;
+    lds_copy16(t.Wc + (g * t.KT + 2 * ks + (f & 1)) * 64 + lane, dst + C::A_BYTES + f * 1024);
+  } else {
+    const int kk = k - C::A_DMA - C::W_DMA;
+    const int d = kk * 64 + lane;
+    const bool is_a = d < C::AS_DW;
+    const bool is_w = !is_a && d < C::AS_DW + C::WS_DW;
+    int64_t row = t.m0 + wave * C::AS_DW + (is_a ? d : 0);
+    row = row < t.M ? row : t.M - 1;
+    const int e = wave * C::WS_DW + (is_w ? d - C::AS_DW : 0);  // (sg local, half, lane)
+    int64_t sg = t.g0 / 4 + (e >> 7);
+    sg = sg < t.NSG ? sg : t.NSG - 1;
+    const uint8_t* src =
+        is_w ? reinterpret_cast<const uint8_t*>(t.Ws + (sg * t.KT + 2 * ks + ((e >> 6) & 1)) * 64 + (e & 63))
+             : t.a_scales + row * t.KB + ks * 4;
+    lds_copy4(src, dst + C::A_BYTES + C::W_BYTES + wave * C::SCW + kk * 256);
+  }
+}
+
+// All copies of a wave's share of K-step ks.
+template <int BN, int BM, int DEPTH>
+__device__ __forceinline__ void fp4_issue(const Fp4Args& t, int64_t ks, LDS uint8_t* dst, int wave,
+                                          int lane) {
+#pragma unroll
+  for (int k = 0; k < Fp4Cfg<BN, BM, DEPTH>::COPIES; ++k) fp4_copy<BN, BM, DEPTH>(t, ks, dst, wave, lane, k);
+}
+
+// LDS read number r of a wave's fragments of one stage buffer: activation
+// fragments, weight fragments, weight scale words, activation scale dwords.
+// LDS read number r of a wave's fragments of one stage buffer: activation
+// scale dwords (raw; fp4_fix_scales applies the lane's byte shift once the
+// reads have landed), weight scale words, activation fragments, weight
+// fragments.
+template <int BN, int BM, int DEPTH>
+__device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st, int wn, int wm,
+                                              int lane, Fp4Frags<BN / 64, BM / 64>& fr, int r) {
+  using C = Fp4Cfg<BN, BM, DEPTH>;
+  const LDS uint8_t* SC = st + C::A_BYTES + C::W_BYTES;
+  if (r < C::FM) {
+    const int j = r;
+    const int R = 32 * (wm * C::FM + j) + (lane & 31);
+    fr.sa[j] = *reinterpret_cast<const LDS int*>(SC + (R / C::AS_DW) * C::SCW + (R % C::AS_DW) * 4);
+  } else if (r < C::FM + 2) {
+    const int hh = r - C::FM;
+    const int e = ((wn * C::FN / 4) * 2 + hh) * 64 + lane;
+    const uint32_t wsw = *reinterpret_cast<const LDS uint32_t*>(SC + (e / C::WS_DW) * C::SCW +
+                                                                (C::AS_DW + e % C::WS_DW) * 4);
+    // byte i of the shifted word is the scale of the wave's weight group i
+    fr.sw[hh] = int(C::FN == 4 ? wsw : wsw >> (8 * ((wn * C::FN) & 3)));
+  } else if (r < 3 * C::FM + 2) {
+    const int q = r - C::FM - 2, j = q >> 1, hh = q & 1;
+    // fragment lane l: row 32 g + l%32 (16-row block 2 g + (l%32)/16),
+    // 16-byte chunk 2 hh + l/32 of its K-step bytes
+    fr.a[j][hh] = *reinterpret_cast<const LDS u32x4*>(
+        st + (2 * (wm * C::FM + j) + ((lane >> 4) & 1)) * 1024 + (2 * hh + (lane >> 5)) * 256 +
+        (lane & 15) * 16);
+  } else {
+    const int q = r - 3 * C::FM - 2, i = q >> 1, hh = q & 1;
+    fr.w[i][hh] = *reinterpret_cast<const LDS u32x4*>(st + C::A_BYTES + ((wn * C::FN + i) * 2 + hh) * 1024 +
+                                                      lane * 16);
+  }
+}
+
+// activation scale byte of lane l: block 2 hh + l/32 is byte 2 hh of the shifted dword
+template <int FM>
+__device__ __forceinline__ void fp4_fix_scales(int (&sa)[FM], int lane) {
+#pragma unroll
+  for (int j = 0; j < FM; ++j) sa[j] = int(uint32_t(sa[j]) >> (8 * (lane >> 5)));
+}
+
+// One pipeline step as 2 FN groups of FM MFMAs (64-K half H, weight group I);
+// after each group this wave issues its share of the copies of the stage
+// DEPTH steps ahead and of the LDS reads of the next step, and a scheduling
+// barrier keeps that order: the texture unit gets the copies at a rate it can
+// take (a burst of them stalls the issuing wave and starves the MFMAs) and
+// every read is in flight long before the step ends.
+template <int BN, int BM, int DEPTH, bool ISSUE, int G>
+struct Fp4Group {
+  using C = Fp4Cfg<BN, BM, DEPTH>;
+  static constexpr int FN = C::FN, FM = C::FM, NGRP = 2 * FN;
+  static constexpr int READS = 2 * (FN + FM) + 2 + FM;
+  static __device__ __forceinline__ void run(v16f (&acc)[FN][FM], const Fp4Frags<FN, FM>& cur,
+                                             Fp4Frags<FN, FM>& nxt, const Fp4Args& t, int64_t ks_copy,
+                                             LDS uint8_t* dst, const LDS uint8_t* __restrict__ st,
+                                             int wave, int wn, int wm, int lane) {
+    constexpr int H = G / FN, I = G % FN;
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      acc[I][j] = mfma32_fp4_op<I, 2 * H>(cur.w[I][H], cur.a[j][H], acc[I][j], cur.sw[H], cur.sa[j]);
+    if constexpr (ISSUE) {
+#pragma unroll
+      for (int k = G * C::COPIES / NGRP; k < (G + 1) * C::COPIES / NGRP; ++k)
+        fp4_copy<BN, BM, DEPTH>(t, ks_copy, dst, wave, lane, k);
+    }
+    // the reads go in the first RG groups, so that they have landed by the end of the step
+    constexpr int RG = NGRP > 2 ? NGRP - 2 : NGRP;
+    if constexpr (G < RG) {
+#pragma unroll
+      for (int r = G * READS / RG; r < (G + 1) * READS / RG; ++r)
+        fp4_read_item<BN, BM, DEPTH>(st, wn, wm, lane, nxt, r);
+    }
+    if constexpr (G + 1 == NGRP) fp4_fix_scales<FM>(nxt.sa, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (G + 1 < NGRP)
+      Fp4Group<BN, BM, DEPTH, ISSUE, G + 1>::run(acc, cur, nxt, t, ks_copy, dst, st, wave, wn, wm, lane);
+  }
+};
+
+template <int BN, int BM, int DEPTH>
+__global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int tiles_m, int tiles_total, int per_xcd) {
+  using C = Fp4Cfg<BN, BM, DEPTH>;
+  constexpr int FN = C::FN, FM = C::FM;
+  const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (tile >= tiles_total) return;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+
+  const BlobLayout L = blob_layout(MXFP4, N, K);
+  Fp4Args t;
+  t.a_codes = a_codes;
+  t.a_scales = a_scales;
+  t.Wc = reinterpret_cast<const uint4*>(blob + L.code_off);
+  t.Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+  t.M = M;
+  t.K2 = K / 2;
+  t.KB = K / 32;
+  t.KT = L.KT;
+  t.NG = L.NG;
+  t.NSG = L.NSG;
+  t.m0 = int64_t(tm) * BM;
+  t.g0 = int64_t(tn) * (BN / 32);
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * C::STAGE];
+  LDS uint8_t* base = (LDS uint8_t*)smem;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wn = wave % C::WN, wm = wave / C::WN;
+
+  v16f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int64_t KS = L.KS;
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s)
+    if (s < KS) fp4_issue<BN, BM, DEPTH>(t, s, base + s * C::STAGE, wave, lane);
+  fp4_sync<C::COPIES, DEPTH>(int((KS < DEPTH ? KS : DEPTH) - 1));
+  Fp4Frags<FN, FM> fa, fb;
+  fp4_read<BN, BM, DEPTH>(base, wn, wm, lane, fa);
+
+  // Main part, two steps per iteration (the fragment buffers swap roles),
+  // each step also copying K-step s+DEPTH into the buffer K-step s came
+  // from; tail: nothing left to copy.
+  int64_t s = 0;
+  for (; s + 1 + DEPTH < KS; s += 2) {
+    fp4_sync<C::COPIES, DEPTH>(DEPTH - 2);
+    Fp4Group<BN, BM, DEPTH, true, 0>::run(acc, fa, fb, t, s + DEPTH, base + (s % DEPTH) * C::STAGE,
+                                          base + ((s + 1) % DEPTH) * C::STAGE, wave, wn, wm, lane);
+    fp4_sync<C::COPIES, DEPTH>(DEPTH - 2);
+    Fp4Group<BN, BM, DEPTH, true, 0>::run(acc, fb, fa, t, s + 1 + DEPTH,
+                                          base + ((s + 1) % DEPTH) * C::STAGE,
+                                          base + ((s + 2) % DEPTH) * C::STAGE, wave, wn, wm, lane);
+  }
+  for (; s + 1 < KS; ++s) {
+    const int64_t issued = KS < s + DEPTH ? KS : s + DEPTH;
+    fp4_sync<C::COPIES, DEPTH>(int(issued - (s + 2)));
+    if (s + DEPTH < KS)
+      fp4_issue<BN, BM, DEPTH>(t, s + DEPTH, base + (s % DEPTH) * C::STAGE, wave, lane);
+    fp4_read<BN, BM, DEPTH>(base + ((s + 1) % DEPTH) * C::STAGE, wn, wm, lane, fb);
+    fp4_mfmas<FN, FM>(acc, fa);
+    fa = fb;
+  }
+  fp4_mfmas<FN, FM>(acc, fa);
+
+  // epilogue: Y = bf16(acc * r) through LDS (see tile_epilogue), 32x32 blocks:
+  // acc[i][j] element e of lane l is n = 32 i + 8 (e/4) + 4 (l/32) + e%4,
+  // m = 32 j + l%32 within the wave tile
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
+  constexpr int WNT = 32 * FN, WMT = 32 * FM;
+  constexpr int CH = WNT / 8, ROWB = 2 * WNT;
+  LDS uint8_t* ep = base + wave * (WMT * ROWB);
+  const int64_t nbase = (t.g0 + wn * FN) * 32;
   const int64_t mbase = t.m0 + wm * WMT;
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int64_t n = nbase + 32 * i + 8 * q + 4 * (lane >> 5);
+      n = n < N ? n : N - 4;
+      const float4 r = *reinterpret_cast<const float4*>(R + n);
+      const v4f rs = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int m = 32 * j + (lane & 31);
+        const int chunk = 4 * i + q;
+        const int off = m * ROWB + ((chunk ^ (m % CH)) * 16) + 8 * (lane >> 5);
+        const v4f a = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        *reinterpret_cast<LDS u32x2*>(ep + off) = scale_pack4(a, rs);
+      }
+    }
 #pragma unroll
   for (int q = 0; q < WMT * CH / 64; ++q) {
     const int idx = q * 64 + lane;
@@ -486,6 +1179,108 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_tile_kernel(
     const int64_t m = mbase + row, n = nbase + 8 * chunk;
     if (m < M && n < N) *reinterpret_cast<u32x4*>(Y + m * N + n) = v;
   }
+}
+
+template <int BN, int BM, int DEPTH>
+hipError_t launch_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                      const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  const int tiles_n = int((N + BN - 1) / BN);
+  const int tiles_m = int((M + BM - 1) / BM);
+  const int total = tiles_n * tiles_m;
+  const int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL((gemm_fp4_kernel<BN, BM, DEPTH>), dim3(unsigned(per_xcd * 8)), dim3(256), 0,
+                     stream, ac, as, blob, Y, M, N, K, tiles_m, total, per_xcd);
+  return hipGetLastError();
+}
+
+// MXFP4 weight streaming for M <= 32: one workgroup per 32 output features,
+// WAVES waves splitting its 64-K tiles into contiguous ranges.  Each wave
+// streams its tiles from HBM straight into registers in batches of U (U
+// coalesced 1 KiB loads in flight per wave, no LDS); the activation rows are
+// the MFMA's second operand (rows >= M are zero, and their lanes load
+// nothing).  Partial sums are added through LDS and wave 0 runs the
+// epilogue.  WAVES is chosen per shape so that the grid keeps every CU busy.
+template <int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  const BlobLayout L = blob_layout(MXFP4, N, K);
+  const u32x4* __restrict__ Wc = reinterpret_cast<const u32x4*>(blob + L.code_off);
+  const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+  const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
+
+  const int64_t g = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5;
+  const int64_t m = lane & 31;
+  const bool mvalid = m < M;
+  const int64_t row = mvalid ? m : 0;
+  const int64_t KT = L.KT, K2 = K / 2, KB = K / 32;
+  const int64_t per = (KT + WAVES - 1) / WAVES;
+  const int64_t k_begin = wave * per;
+  const int64_t k_end = k_begin + per < KT ? k_begin + per : KT;
+  const int sw_shift = 8 * int(g & 3);
+  const uint32_t* __restrict__ Wsg = Ws + (g >> 2) * KT * 64 + lane;
+  const u32x4* __restrict__ Wg = Wc + g * KT * 64 + lane;
+  const uint8_t* __restrict__ arow = a_codes + row * K2 + 16 * half;
+  const uint8_t* __restrict__ srow = a_scales + row * KB + half;
+
+  v16f acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int64_t h0 = k_begin; h0 < k_end; h0 += U) {
+    u32x4 wf[U], af[U];
+    uint32_t swd[U];
+    int sab[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t h = h0 + u;
+      const bool ok = h < k_end;
+      const int64_t hc = ok ? h : k_end - 1;  // clamped: loads stay in range
+      wf[u] = Wg[hc * 64];
+      swd[u] = Wsg[hc * 64];
+      u32x4 a = {0u, 0u, 0u, 0u};
+      int sb = 127;
+      if (mvalid) {
+        a = *reinterpret_cast<const u32x4*>(arow + hc * 32);
+        sb = srow[hc * 2];
+      }
+      af[u] = ok ? a : u32x4{0u, 0u, 0u, 0u};
+      sab[u] = sb;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      acc = mfma32_fp4_op<0, 0>(wf[u], af[u], acc, int(swd[u] >> sw_shift), sab[u]);
+  }
+
+  __shared__ v16f red[WAVES > 1 ? WAVES - 1 : 1][64];
+  if (wave != 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll 1
+  for (int w = 0; w < WAVES - 1; ++w) {
+    const v16f o = red[w][lane];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] += o[e];
+  }
+  if (!mvalid) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t n = g * 32 + 8 * q + 4 * half;
+    if (n < N) {
+      const float4 r = *reinterpret_cast<const float4*>(R + n);
+      store4(Y, N, m, n, v4f{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]},
+             v4f{r.x, r.y, r.z, r.w});
+    }
+  }
+}
+
+template <int WAVES, int U>
+hipError_t launch_fp4_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                             const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_fp4_decode_kernel<WAVES, U>), dim3(unsigned((N + 31) / 32)), dim3(64 * WAVES),
+                     0, stream, ac, as, blob, Y, M, N, K);
+  return hipGetLastError();
 }
 
 // ====================================================== decode kernel ==
@@ -588,20 +1383,30 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
     // enough for 64 x 64 wave tiles at any shape, and it holds expanded fp16
     // fragments that would not fit the register budget of a 128 x 64 tile.
     return launch_tile<FMT, 256, 128, 4, 2, 5>(M, N, K, ac, as, t_act, blob, Y, stream);
+  } else if constexpr (FMT == MXFP4) {
+    if (M <= 32) {
+      // about 8 waves per CU over the grid of 32-row groups
+      const int64_t groups = (N + 31) / 32;
+      // (16-wave groups hold 4 tiles per batch to stay within 128 registers)
+      if (groups >= 512) return launch_fp4_decode<4, 8>(M, N, K, ac, as, blob, Y, stream);
+      if (groups >= 256) return launch_fp4_decode<8, 8>(M, N, K, ac, as, blob, Y, stream);
+      return launch_fp4_decode<16, 4>(M, N, K, ac, as, blob, Y, stream);
+    }
+    // 256 x 256 tiles (4 waves of 128 x 128) unless that leaves more than
+    // ~30% of the 256 CUs idle; then 256 (n) x 128 (m) tiles.
+    const int64_t big = ((N + 255) / 256) * ((M + 255) / 256);
+    if (big >= 180) return launch_fp4<256, 256, 4>(M, N, K, ac, as, blob, Y, stream);
+    return launch_fp4<256, 128, 5>(M, N, K, ac, as, blob, Y, stream);
   } else {
     if (M <= 16) {
       hipLaunchKernelGGL(gemm_decode_kernel<FMT>, dim3(unsigned(N / 16)), dim3(64 * kDecodeWaves),
                          0, stream, ac, as, blob, Y, M, N, K);
       return hipGetLastError();
     }
-    // 8 waves per workgroup (two per SIMD, so one wave's memory and barrier
-    // stalls are covered by the other's MFMAs).  256x256 tiles (waves 2 x 4,
-    // 128 x 64 each) unless that leaves more than ~30% of the 256 CUs idle;
-    // then 256 (n) x 128 (m) tiles (waves 4 x 2, 64 x 64 each).
-    const int64_t big = ((N + 255) / 256) * ((M + 255) / 256);
-    if (big >= 180)
-      return launch_tile<FMT, 256, 256, 2, 4, 4>(M, N, K, ac, as, t_act, blob, Y, stream);
-    return launch_tile<FMT, 256, 128, 4, 2, 5>(M, N, K, ac, as, t_act, blob, Y, stream);
+    // MXINT4: 8 waves (two per SIMD) of 64 x 64 on the 16x16x128 FP8 MFMA;
+    // its fragments are widened to FP8 in registers, which leaves no room for
+    // larger wave tiles.
+    return launch_mx<FMT, 256, 128, 4, 2, 4>(M, N, K, ac, as, blob, Y, stream);
   }
 }
 
