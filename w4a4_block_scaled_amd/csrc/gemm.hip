@@ -850,19 +850,24 @@ struct Fp4Cfg {
   // 1 KiB copies per K-step: activations 16 rows x 64 B, weights one fragment tile
   static constexpr int A_TILES = BM / 16, W_TILES = BN / 32 * 2;
   static constexpr int A_BYTES = A_TILES * 1024, W_BYTES = W_TILES * 1024;
-  static constexpr int AS_DW = BM / WAVES;                // activation scale dwords per wave
   static constexpr int WS_DW = BN / 128 * 2 * 64 / WAVES;  // weight scale words per wave
-  static constexpr int SC_COPIES = (AS_DW + WS_DW + 63) / 64;
-  static constexpr int SCW = SC_COPIES * 256;             // scale chunk bytes per wave
-  static constexpr int STAGE = A_BYTES + W_BYTES + WAVES * SCW;
+  static constexpr int STAGE = A_BYTES + W_BYTES + WAVES * 256;
   static constexpr int A_DMA = A_TILES / WAVES, W_DMA = W_TILES / WAVES;
-  static constexpr int COPIES = A_DMA + W_DMA + SC_COPIES;
+  // per wave per K-step: activation and weight tiles, one copy of weight
+  // scale words, one quarter of an activation scale block
+  static constexpr int COPIES = A_DMA + W_DMA + 2;
+  // activation scale blocks: 4 K-steps x BM rows of scale dwords; a wave
+  // owns ASR rows, copied as 4 quarters of 16 rows x 4 K-steps
+  static constexpr int ASR = 64;
+  static constexpr int ASB = WAVES * ASR * 16;  // bytes per block
+  static constexpr int AS_OFF = DEPTH * STAGE;  // 3 blocks after the ring
+  static constexpr int LDS_BYTES = AS_OFF + 3 * ASB;
   static constexpr int EPI_BYTES = WAVES * (32 * FM) * (64 * FN);
   static_assert(A_DMA * WAVES == A_TILES && W_DMA * WAVES == W_TILES, "tile / wave split");
   static_assert(BN % 128 == 0 && FN >= 1 && FN <= 4 && FM >= 1, "wave tile");
-  static_assert((AS_DW & (AS_DW - 1)) == 0 && (WS_DW & (WS_DW - 1)) == 0, "scale chunk split");
-  static_assert(DEPTH * STAGE <= 160 * 1024 && EPI_BYTES <= DEPTH * STAGE, "LDS");
-  static_assert((DEPTH - 1) * COPIES < 64, "vmcnt range");
+  static_assert(WS_DW <= 64 && BM <= WAVES * ASR, "scale copies");
+  static_assert(LDS_BYTES <= 160 * 1024 && EPI_BYTES <= DEPTH * STAGE, "LDS");
+  static_assert((DEPTH - 1) * COPIES + 4 < 64 && DEPTH <= 5, "vmcnt range / scale block reuse");
 };
 
 struct Fp4Args {
@@ -872,6 +877,8 @@ struct Fp4Args {
   const uint32_t* Ws;
   int64_t M, K2, KB, KT, NG, NSG;
   int64_t m0, g0;  // first activation row, first 32-row weight group
+  int64_t KS;      // 128-wide K-steps
+  LDS uint8_t* smem;
 };
 
 template <int FN, int FM>
@@ -881,39 +888,6 @@ struct Fp4Frags {
   int sa[FM];
   int sw[2];
 };
-
-// Read a wave's fragments of one stage buffer.
-template <int BN, int BM, int DEPTH>
-__device__ __forceinline__ void fp4_read(const LDS uint8_t* __restrict__ st, int wn, int wm, int lane,
-                                         Fp4Frags<BN / 64, BM / 64>& fr) {
-  using C = Fp4Cfg<BN, BM, DEPTH>;
-  const LDS uint8_t* SC = st + C::A_BYTES + C::W_BYTES;
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-    for (int j = 0; j < C::FM; ++j)
-      // fragment lane l: row 32 g + l%32 (16-row block 2 g + (l%32)/16),
-      // 16-byte chunk 2 hh + l/32 of its K-step bytes
-      fr.a[j][hh] = *reinterpret_cast<const LDS u32x4*>(
-          st + (2 * (wm * C::FM + j) + ((lane >> 4) & 1)) * 1024 + (2 * hh + (lane >> 5)) * 256 +
-          (lane & 15) * 16);
-#pragma unroll
-    for (int i = 0; i < C::FN; ++i)
-      fr.w[i][hh] = *reinterpret_cast<const LDS u32x4*>(st + C::A_BYTES + ((wn * C::FN + i) * 2 + hh) * 1024 +
-                                                        lane * 16);
-    const int e = ((wn * C::FN / 4) * 2 + hh) * 64 + lane;
-    const uint32_t wsw = *reinterpret_cast<const LDS uint32_t*>(SC + (e / C::WS_DW) * C::SCW +
-                                                                (C::AS_DW + e % C::WS_DW) * 4);
-    // byte i of the shifted word is the scale of the wave's weight group i
-    fr.sw[hh] = int(C::FN == 4 ? wsw : wsw >> (8 * ((wn * C::FN) & 3)));
-  }
-#pragma unroll
-  for (int j = 0; j < C::FM; ++j) {
-    const int R = 32 * (wm * C::FM + j) + (lane & 31);
-    const uint32_t d = *reinterpret_cast<const LDS uint32_t*>(SC + (R / C::AS_DW) * C::SCW + (R % C::AS_DW) * 4);
-    fr.sa[j] = int(d >> (8 * (lane >> 5)));
-  }
-}
 
 // MFMAs of one K-step: weight group I (scale byte I of the word), 64-K half
 // H (activation scale byte 2H), every activation group j.
@@ -948,6 +922,33 @@ __device__ __forceinline__ void fp4_sync(int after) {
   asm volatile("" ::: "memory");
 }
 
+// Quarter q of activation scale block b (the scale dwords of K-steps
+// 4b..4b+3): lane l of wave w copies the dword of row w*ASR + 16q + l/4,
+// K-step 4b + l%4, so one copy touches 16 rows instead of 64.  Rows beyond
+// M and K-steps beyond KS copy a valid duplicate.  Block b lives in buffer
+// b % 3 after the stage ring; it is copied together with the stages of
+// block b-1, one quarter per stage.
+template <int BN, int BM, int DEPTH>
+__device__ __forceinline__ void fp4_copy_scale_quarter(const Fp4Args& t, int64_t b, int q, int wave,
+                                                       int lane) {
+  using C = Fp4Cfg<BN, BM, DEPTH>;
+  int64_t row = t.m0 + wave * C::ASR + 16 * q + (lane >> 2);
+  row = row < t.M ? row : t.M - 1;
+  int64_t ks = 4 * b + (lane & 3);
+  ks = ks < t.KS ? ks : t.KS - 1;
+  lds_copy4(t.a_scales + row * t.KB + 4 * ks,
+            t.smem + C::AS_OFF + int(b % 3) * C::ASB + wave * (C::ASR * 16) + q * 256);
+}
+
+// LDS byte offset of the scale dword of local activation row R, K-step ks
+template <int BN, int BM, int DEPTH>
+__device__ __forceinline__ int fp4_scale_offset(int R, int64_t ks) {
+  using C = Fp4Cfg<BN, BM, DEPTH>;
+  const int w = R / C::ASR, r = R % C::ASR;
+  return C::AS_OFF + int((ks / 4) % 3) * C::ASB + w * (C::ASR * 16) + (r >> 4) * 256 + (r & 15) * 16 +
+         int(ks & 3) * 4;
+}
+
 // Copy number k of a wave's share of K-step ks (activation copies, weight
 // copies, then scale copies), so that the copies can be spread over a step.
 template <int BN, int BM, int DEPTH>
@@ -966,20 +967,15 @@ __device__ __forceinline__ void fp4_copy(const Fp4Args& t, int64_t ks, LDS uint8
     int64_t g = t.g0 + (f >> 1);
     g = g < t.NG ? g : t.NG - 1;
     lds_copy16(t.Wc + (g * t.KT + 2 * ks + (f & 1)) * 64 + lane, dst + C::A_BYTES + f * 1024);
-  } else {
-    const int kk = k - C::A_DMA - C::W_DMA;
-    const int d = kk * 64 + lane;
-    const bool is_a = d < C::AS_DW;
-    const bool is_w = !is_a && d < C::AS_DW + C::WS_DW;
-    int64_t row = t.m0 + wave * C::AS_DW + (is_a ? d : 0);
-    row = row < t.M ? row : t.M - 1;
-    const int e = wave * C::WS_DW + (is_w ? d - C::AS_DW : 0);  // (sg local, half, lane)
+  } else if (k == C::A_DMA + C::W_DMA) {
+    // weight scale words of K-step ks: word e = (sg local, half, lane)
+    const int e = wave * C::WS_DW + (lane < C::WS_DW ? lane : 0);
     int64_t sg = t.g0 / 4 + (e >> 7);
     sg = sg < t.NSG ? sg : t.NSG - 1;
-    const uint8_t* src =
-        is_w ? reinterpret_cast<const uint8_t*>(t.Ws + (sg * t.KT + 2 * ks + ((e >> 6) & 1)) * 64 + (e & 63))
-             : t.a_scales + row * t.KB + ks * 4;
-    lds_copy4(src, dst + C::A_BYTES + C::W_BYTES + wave * C::SCW + kk * 256);
+    lds_copy4(t.Ws + (sg * t.KT + 2 * ks + ((e >> 6) & 1)) * 64 + (e & 63),
+              dst + C::A_BYTES + C::W_BYTES + wave * 256);
+  } else {
+    fp4_copy_scale_quarter<BN, BM, DEPTH>(t, ks / 4 + 1, int(ks & 3), wave, lane);
   }
 }
 
@@ -991,26 +987,32 @@ __device__ __forceinline__ void fp4_issue(const Fp4Args& t, int64_t ks, LDS uint
   for (int k = 0; k < Fp4Cfg<BN, BM, DEPTH>::COPIES; ++k) fp4_copy<BN, BM, DEPTH>(t, ks, dst, wave, lane, k);
 }
 
-// LDS read number r of a wave's fragments of one stage buffer: activation
-// fragments, weight fragments, weight scale words, activation scale dwords.
-// LDS read number r of a wave's fragments of one stage buffer: activation
-// scale dwords (raw; fp4_fix_scales applies the lane's byte shift once the
-// reads have landed), weight scale words, activation fragments, weight
-// fragments.
+// activation scale byte of lane l: block 2 hh + l/32 is byte 2 hh of the shifted dword
+template <int FM>
+__device__ __forceinline__ void fp4_fix_scales(int (&sa)[FM], int lane) {
+#pragma unroll
+  for (int j = 0; j < FM; ++j) sa[j] = int(uint32_t(sa[j]) >> (8 * (lane >> 5)));
+}
+
+// LDS read number r of a wave's fragments of K-step kstep (stage buffer
+// `st`): activation scale dwords (raw, from the scale block; fp4_fix_scales
+// applies the lane's byte shift once the reads have landed), weight scale
+// words, activation fragments, weight fragments.
 template <int BN, int BM, int DEPTH>
-__device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st, int wn, int wm,
-                                              int lane, Fp4Frags<BN / 64, BM / 64>& fr, int r) {
+__device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st,
+                                              const LDS uint8_t* __restrict__ base, int64_t kstep,
+                                              int wn, int wm, int lane, Fp4Frags<BN / 64, BM / 64>& fr,
+                                              int r) {
   using C = Fp4Cfg<BN, BM, DEPTH>;
-  const LDS uint8_t* SC = st + C::A_BYTES + C::W_BYTES;
   if (r < C::FM) {
     const int j = r;
     const int R = 32 * (wm * C::FM + j) + (lane & 31);
-    fr.sa[j] = *reinterpret_cast<const LDS int*>(SC + (R / C::AS_DW) * C::SCW + (R % C::AS_DW) * 4);
+    fr.sa[j] = *reinterpret_cast<const LDS int*>(base + fp4_scale_offset<BN, BM, DEPTH>(R, kstep));
   } else if (r < C::FM + 2) {
     const int hh = r - C::FM;
     const int e = ((wn * C::FN / 4) * 2 + hh) * 64 + lane;
-    const uint32_t wsw = *reinterpret_cast<const LDS uint32_t*>(SC + (e / C::WS_DW) * C::SCW +
-                                                                (C::AS_DW + e % C::WS_DW) * 4);
+    const uint32_t wsw = *reinterpret_cast<const LDS uint32_t*>(st + C::A_BYTES + C::W_BYTES +
+                                                                (e / C::WS_DW) * 256 + (e % C::WS_DW) * 4);
     // byte i of the shifted word is the scale of the wave's weight group i
     fr.sw[hh] = int(C::FN == 4 ? wsw : wsw >> (8 * ((wn * C::FN) & 3)));
   } else if (r < 3 * C::FM + 2) {
@@ -1027,12 +1029,17 @@ __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st
   }
 }
 
-// activation scale byte of lane l: block 2 hh + l/32 is byte 2 hh of the shifted dword
-template <int FM>
-__device__ __forceinline__ void fp4_fix_scales(int (&sa)[FM], int lane) {
+template <int BN, int BM, int DEPTH>
+__device__ __forceinline__ void fp4_read_all(const LDS uint8_t* __restrict__ st,
+                                             const LDS uint8_t* __restrict__ base, int64_t kstep,
+                                             int wn, int wm, int lane, Fp4Frags<BN / 64, BM / 64>& fr) {
+  using C = Fp4Cfg<BN, BM, DEPTH>;
 #pragma unroll
-  for (int j = 0; j < FM; ++j) sa[j] = int(uint32_t(sa[j]) >> (8 * (lane >> 5)));
+  for (int r = 0; r < 3 * C::FM + 2 + 2 * C::FN; ++r)
+    fp4_read_item<BN, BM, DEPTH>(st, base, kstep, wn, wm, lane, fr, r);
+  fp4_fix_scales<C::FM>(fr.sa, lane);
 }
+
 
 // One pipeline step as 2 FN groups of FM MFMAs (64-K half H, weight group I);
 // after each group this wave issues its share of the copies of the stage
@@ -1044,11 +1051,11 @@ template <int BN, int BM, int DEPTH, bool ISSUE, int G>
 struct Fp4Group {
   using C = Fp4Cfg<BN, BM, DEPTH>;
   static constexpr int FN = C::FN, FM = C::FM, NGRP = 2 * FN;
-  static constexpr int READS = 2 * (FN + FM) + 2 + FM;
+  static constexpr int READS = 3 * FM + 2 + 2 * FN;
   static __device__ __forceinline__ void run(v16f (&acc)[FN][FM], const Fp4Frags<FN, FM>& cur,
                                              Fp4Frags<FN, FM>& nxt, const Fp4Args& t, int64_t ks_copy,
                                              LDS uint8_t* dst, const LDS uint8_t* __restrict__ st,
-                                             int wave, int wn, int wm, int lane) {
+                                             int64_t ks_read, int wave, int wn, int wm, int lane) {
     constexpr int H = G / FN, I = G % FN;
 #pragma unroll
     for (int j = 0; j < FM; ++j)
@@ -1063,12 +1070,13 @@ struct Fp4Group {
     if constexpr (G < RG) {
 #pragma unroll
       for (int r = G * READS / RG; r < (G + 1) * READS / RG; ++r)
-        fp4_read_item<BN, BM, DEPTH>(st, wn, wm, lane, nxt, r);
+        fp4_read_item<BN, BM, DEPTH>(st, t.smem, ks_read, wn, wm, lane, nxt, r);
     }
     if constexpr (G + 1 == NGRP) fp4_fix_scales<FM>(nxt.sa, lane);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (G + 1 < NGRP)
-      Fp4Group<BN, BM, DEPTH, ISSUE, G + 1>::run(acc, cur, nxt, t, ks_copy, dst, st, wave, wn, wm, lane);
+      Fp4Group<BN, BM, DEPTH, ISSUE, G + 1>::run(acc, cur, nxt, t, ks_copy, dst, st, ks_read, wave, wn,
+                                                  wm, lane);
   }
 };
 
@@ -1097,9 +1105,11 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(
   t.NSG = L.NSG;
   t.m0 = int64_t(tm) * BM;
   t.g0 = int64_t(tn) * (BN / 32);
+  t.KS = L.KS;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
   LDS uint8_t* base = (LDS uint8_t*)smem;
+  t.smem = base;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wn = wave % C::WN, wm = wave / C::WN;
 
@@ -1112,12 +1122,15 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int64_t KS = L.KS;
+  // activation scale block 0 (the stages of block b-1 carry block b)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) fp4_copy_scale_quarter<BN, BM, DEPTH>(t, 0, q, wave, lane);
 #pragma unroll
   for (int s = 0; s < DEPTH; ++s)
     if (s < KS) fp4_issue<BN, BM, DEPTH>(t, s, base + s * C::STAGE, wave, lane);
   fp4_sync<C::COPIES, DEPTH>(int((KS < DEPTH ? KS : DEPTH) - 1));
   Fp4Frags<FN, FM> fa, fb;
-  fp4_read<BN, BM, DEPTH>(base, wn, wm, lane, fa);
+  fp4_read_all<BN, BM, DEPTH>(base, base, 0, wn, wm, lane, fa);
 
   // Main part, two steps per iteration (the fragment buffers swap roles),
   // each step also copying K-step s+DEPTH into the buffer K-step s came
@@ -1126,18 +1139,20 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(
   for (; s + 1 + DEPTH < KS; s += 2) {
     fp4_sync<C::COPIES, DEPTH>(DEPTH - 2);
     Fp4Group<BN, BM, DEPTH, true, 0>::run(acc, fa, fb, t, s + DEPTH, base + (s % DEPTH) * C::STAGE,
-                                          base + ((s + 1) % DEPTH) * C::STAGE, wave, wn, wm, lane);
+                                          base + ((s + 1) % DEPTH) * C::STAGE, s + 1, wave, wn, wm,
+                                          lane);
     fp4_sync<C::COPIES, DEPTH>(DEPTH - 2);
     Fp4Group<BN, BM, DEPTH, true, 0>::run(acc, fb, fa, t, s + 1 + DEPTH,
                                           base + ((s + 1) % DEPTH) * C::STAGE,
-                                          base + ((s + 2) % DEPTH) * C::STAGE, wave, wn, wm, lane);
+                                          base + ((s + 2) % DEPTH) * C::STAGE, s + 2, wave, wn, wm,
+                                          lane);
   }
   for (; s + 1 < KS; ++s) {
     const int64_t issued = KS < s + DEPTH ? KS : s + DEPTH;
     fp4_sync<C::COPIES, DEPTH>(int(issued - (s + 2)));
     if (s + DEPTH < KS)
       fp4_issue<BN, BM, DEPTH>(t, s + DEPTH, base + (s % DEPTH) * C::STAGE, wave, lane);
-    fp4_read<BN, BM, DEPTH>(base + ((s + 1) % DEPTH) * C::STAGE, wn, wm, lane, fb);
+    fp4_read_all<BN, BM, DEPTH>(base + ((s + 1) % DEPTH) * C::STAGE, base, s + 1, wn, wm, lane, fb);
     fp4_mfmas<FN, FM>(acc, fa);
     fa = fb;
   }
@@ -1198,8 +1213,7 @@ hipError_t launch_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
 // streams its tiles from HBM straight into registers in batches of U (U
 // coalesced 1 KiB loads in flight per wave, no LDS); the activation rows are
 // the MFMA's second operand (rows >= M are zero, and their lanes load
-// nothing).  Partial sums are added through LDS and wave 0 runs the
-// epilogue.  WAVES is chosen per shape so that the grid keeps every CU busy.
+// nothing).  Partial sums are added through LDS and wave 0 runs the epilogue.
 template <int WAVES, int U>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
@@ -1278,8 +1292,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode_kernel(
 template <int WAVES, int U>
 hipError_t launch_fp4_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                              const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_fp4_decode_kernel<WAVES, U>), dim3(unsigned((N + 31) / 32)), dim3(64 * WAVES),
-                     0, stream, ac, as, blob, Y, M, N, K);
+  hipLaunchKernelGGL((gemm_fp4_decode_kernel<WAVES, U>), dim3(unsigned((N + 31) / 32)),
+                     dim3(64 * WAVES), 0, stream, ac, as, blob, Y, M, N, K);
   return hipGetLastError();
 }
 
@@ -1377,7 +1391,8 @@ hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const
 
 template <int FMT>
 hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
-                      const float* t_act, const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+                      const float* t_act, const uint8_t* blob, uint16_t* Y, void* workspace,
+                      hipStream_t stream) {
   if constexpr (FMT == NVFP4) {
     // NVFP4 runs four fp16 MFMAs per fragment pair, so its K-step is long
     // enough for 64 x 64 wave tiles at any shape, and it holds expanded fp16
@@ -1385,12 +1400,10 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
     return launch_tile<FMT, 256, 128, 4, 2, 5>(M, N, K, ac, as, t_act, blob, Y, stream);
   } else if constexpr (FMT == MXFP4) {
     if (M <= 32) {
-      // about 8 waves per CU over the grid of 32-row groups
-      const int64_t groups = (N + 31) / 32;
-      // (16-wave groups hold 4 tiles per batch to stay within 128 registers)
-      if (groups >= 512) return launch_fp4_decode<4, 8>(M, N, K, ac, as, blob, Y, stream);
-      if (groups >= 256) return launch_fp4_decode<8, 8>(M, N, K, ac, as, blob, Y, stream);
-      return launch_fp4_decode<16, 4>(M, N, K, ac, as, blob, Y, stream);
+      // large grids: 4 waves streaming 8 tiles each per batch; small grids
+      // (fewer groups than about two per CU): 8 waves of 4
+      if ((N + 31) / 32 >= 512) return launch_fp4_decode<4, 8>(M, N, K, ac, as, blob, Y, stream);
+      return launch_fp4_decode<8, 4>(M, N, K, ac, as, blob, Y, stream);
     }
     // 256 x 256 tiles (4 waves of 128 x 128) unless that leaves more than
     // ~30% of the 256 CUs idle; then 256 (n) x 128 (m) tiles.
@@ -1416,16 +1429,16 @@ size_t linear_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
 
 hipError_t launch_linear(int fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
                          const void* a_scales, const float* t_act, const void* blob, void* Y,
-                         void*, size_t, hipStream_t stream) {
+                         void* workspace, size_t, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const uint8_t* ac = static_cast<const uint8_t*>(a_codes);
   const uint8_t* as = static_cast<const uint8_t*>(a_scales);
   const uint8_t* b = static_cast<const uint8_t*>(blob);
   uint16_t* y = static_cast<uint16_t*>(Y);
   switch (fmt) {
-    case MXFP4: return launch_fmt<MXFP4>(M, N, K, ac, as, t_act, b, y, stream);
-    case MXINT4: return launch_fmt<MXINT4>(M, N, K, ac, as, t_act, b, y, stream);
-    default: return launch_fmt<NVFP4>(M, N, K, ac, as, t_act, b, y, stream);
+    case MXFP4: return launch_fmt<MXFP4>(M, N, K, ac, as, t_act, b, y, workspace, stream);
+    case MXINT4: return launch_fmt<MXINT4>(M, N, K, ac, as, t_act, b, y, workspace, stream);
+    default: return launch_fmt<NVFP4>(M, N, K, ac, as, t_act, b, y, workspace, stream);
   }
 }
 
