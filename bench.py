@@ -84,6 +84,12 @@ class Layer:
         return 2.0 * self.M * self.N * self.K
 
     @property
+    def quant_bytes(self):
+        """quantize_act algorithmic bytes: X in, c in, codes and scales out."""
+        G = w4.block_size(self.fmt)
+        return 2 * self.M * self.K + 4 * self.K + self.M * self.K / 2 + self.M * self.K / G
+
+    @property
     def gemm_bytes(self):
         G = w4.block_size(self.fmt)
         return (self.N * self.K / 2 + self.N * self.K / G + 4 * self.N + self.M * self.K / 2 +
@@ -91,34 +97,40 @@ class Layer:
 
 
 def time_steps(layers, steps, warmup, with_events=True):
-    """Run warmup + timed steps; returns (ms per step, per-layer GEMM ms list)."""
+    """Run warmup + timed steps; returns (ms per step, per-layer GEMM ms list,
+    per-layer quantize_act ms list), the per-layer figures from HIP events
+    recorded on the stream the kernels run on."""
     for _ in range(warmup):
         for L in layers:
             L.quantize()
             L.gemm()
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in layers] for _ in range(steps)] if with_events else None
+    ev = [[tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in layers]
+          for _ in range(steps)] if with_events else None
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
     for s in range(steps):
         for i, L in enumerate(layers):
-            L.quantize()
             if with_events:
                 ev[s][i][0].record()
-            L.gemm()
+            L.quantize()
             if with_events:
                 ev[s][i][1].record()
+            L.gemm()
+            if with_events:
+                ev[s][i][2].record()
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    gemm_ms = None
+    gemm_ms = quant_ms = None
     if with_events:
-        gemm_ms = [float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]))
+        gemm_ms = [float(np.mean([ev[s][i][1].elapsed_time(ev[s][i][2]) for s in range(steps)]))
                    for i in range(len(layers))]
-    return ms, gemm_ms
+        quant_ms = [float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]))
+                    for i in range(len(layers))]
+    return ms, gemm_ms, quant_ms
 
 
 def decode_bandwidth(dev, steps, copies=32):
@@ -253,7 +265,7 @@ def main():
         traffic_probe(layers, dev)
         return
     log("[bench] timing")
-    ms, gemm_ms = time_steps(layers, a.steps, a.warmup)
+    ms, gemm_ms, quant_ms = time_steps(layers, a.steps, a.warmup)
     flops = sum(L.flops for L in layers)
     value = flops / (ms * 1e-3) / 1e12
     peak, unit, bound = PEAK[fmt]
@@ -276,6 +288,9 @@ def main():
                       "linears": [[L.case.name, L.N, L.K] for L in layers],
                       "step": "quantize_act + linear for each linear; weights packed once"},
            "tokens_per_s": round(M / (ms * 1e-3), 1),
+           "quantize_act": {L.case.name: {"us": round(t * 1e3, 2),
+                                          "GB/s": round(L.quant_bytes / (t * 1e-3) / 1e9, 1)}
+                            for L, t in zip(layers, quant_ms)},
            "roofline": roof}
     del layers
     torch.cuda.empty_cache()

@@ -140,3 +140,20 @@ def test_quantize_full_activation_tensors(workload, M, lins):
     for case in inputs.workload_cases(workload, M=M, linears=lins, build_weights=False):
         say(f"[quantize full] {workload} {case.name} M={case.M} K={case.K}")
         _compare(case.x, case.c, case.fmt, f"{workload}/{case.name}")
+
+
+def test_mxfp4_ties_at_many_scales():
+    """Every E2M1 midpoint (and its negative) at block exponents from -100 to
+    +100: codes and scales bit-exact against the oracle (ties to the even
+    code, saturation at 6, sign kept on values that round to zero)."""
+    dev = device()
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, 0.125, 7.0, 1.0, 3.0], np.float64)
+    rows = []
+    for k in range(-100, 101, 7):
+        blk = np.zeros(32, np.float64)
+        blk[:12] = mids
+        blk[12:24] = -mids
+        blk[24] = 7.5                      # fixes the block exponent at 0 before scaling
+        rows.append(blk * 2.0 ** k)
+    x = torch.from_numpy(np.array(rows, np.float32)).to(torch.bfloat16)
+    _compare(x, np.ones(32, np.float32), "mxfp4", "mxfp4 ties")

@@ -9,7 +9,7 @@
 //
 // One thread owns 8 consecutive elements of a row (one 16-byte load of bf16,
 // one 4-byte store of codes).  A block of 32 (16) elements is owned by 4 (2)
-// consecutive lanes; its amax is reduced with cross-lane shuffles.  Every
+// consecutive lanes; its amax is reduced with cross-lane exchanges.  Every
 // rounding decision is exact: MX scales come from exponent bits, elements
 // are compared against exact midpoints, NVFP4 scale/element decisions are
 // taken against thresholds computed exactly in fp64.
@@ -56,19 +56,20 @@ __device__ __forceinline__ uint32_t e2m1_index(float v) {
          (v > 5.0f);
 }
 
+// value of the lane whose index differs in bit 0 / bit 1 (within a quad)
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ int quad_xor1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true); }
+__device__ __forceinline__ int quad_xor2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true); }
+
+// Codes and the scale byte of one 32-block from this lane's 8 elements (the
+// block is spread over 4 consecutive lanes, which must all be present).
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void quantize_mx_kernel(
-    const uint4* __restrict__ X, const float* __restrict__ c, uint32_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, int64_t n_groups, int64_t K8) {
-  const int64_t g_raw = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  const bool live = g_raw < n_groups;
-  const int64_t g = live ? g_raw : n_groups - 1;  // every lane joins the shuffles
-  const int64_t row = g / K8;
-  const int64_t col8 = g - row * K8;
-
-  float x[8];
-  load8(X, c, g, col8, x);
-
+__device__ __forceinline__ void quant8_mx(const float (&x)[8], uint32_t& word, uint32_t& sbyte) {
   float amax = 0.0f;
   int bad = 0;
 #pragma unroll
@@ -77,35 +78,83 @@ __global__ __launch_bounds__(kThreads) void quantize_mx_kernel(
     bad |= !(a <= FLT_MAX);  // Inf or NaN
     amax = fmaxf(amax, a);
   }
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-  amax = fmaxf(amax, __shfl_xor(amax, 2));
-  bad |= __shfl_xor(bad, 1);
-  bad |= __shfl_xor(bad, 2);
+  // the 4 lanes of a block form a quad: two DPP quad permutations
+  amax = fmaxf(amax, quad_xor1(amax));
+  amax = fmaxf(amax, quad_xor2(amax));
+  bad |= quad_xor1(bad);
+  bad |= quad_xor2(bad);
 
   int e = -127;
   if (amax > 0.0f) e = max(-127, min(127, floor_log2(amax) - 2));
 
-  uint32_t word = 0;
+  word = 0;
+  if (FMT == MXFP4) {
+    // the hardware FP4 conversion (round to nearest even, saturating, sign
+    // kept for values that round to zero) of the exactly scaled values
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(x[0], -e), ldexpf(x[1], -e), 1.0f, 0);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(x[2], -e), ldexpf(x[3], -e), 1.0f, 1);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(x[4], -e), ldexpf(x[5], -e), 1.0f, 2);
+    word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, ldexpf(x[6], -e), ldexpf(x[7], -e), 1.0f, 3);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float v = ldexpf(x[i], -e);  // exact power-of-two scaling
-    uint32_t code;
-    if (FMT == MXFP4) {
-      code = e2m1_index(fabsf(v)) | ((__float_as_uint(x[i]) >> 28) & 8u);
-    } else {
-      const float q = fminf(rintf(v), 7.0f);  // |v| < 8, so only +8 needs clipping
-      code = uint32_t(int(q)) & 15u;
+    for (int i = 0; i < 8; ++i) {
+      const float q = fminf(rintf(ldexpf(x[i], -e)), 7.0f);  // |v| < 8, so only +8 needs clipping
+      word |= (uint32_t(int(q)) & 15u) << (4 * i);
     }
-    word |= code << (4 * i);
   }
-  uint32_t sbyte = uint32_t(e + 127);
+  sbyte = uint32_t(e + 127);
   if (bad) {
     word = 0;
     sbyte = 0xff;
   }
-  if (!live) return;
-  codes[g] = word;
-  if ((col8 & 3) == 0) scales[row * (K8 / 4) + (col8 >> 2)] = uint8_t(sbyte);
+}
+
+// Grid x: chunks of R rows, grid y: 256-wide runs of 8-column groups.  A
+// thread owns 8 consecutive columns (one 16-byte load of bf16 per row, one
+// 4-byte store of codes): it loads their column scales once and quantizes
+// those columns of R rows, with all R loads in flight together.
+template <int FMT, int R>
+__global__ __launch_bounds__(kThreads) void quantize_mx_kernel(
+    const uint4* __restrict__ X, const float* __restrict__ c, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t M, int64_t K8) {
+  const int64_t col_raw = int64_t(blockIdx.y) * kThreads + threadIdx.x;
+  const bool live_c = col_raw < K8;
+  const int64_t col8 = live_c ? col_raw : K8 - 1;  // every lane joins the shuffles
+  const int64_t r0 = int64_t(blockIdx.x) * R;
+  float cc[8];
+  if (c) {
+    const float4 c0 = reinterpret_cast<const float4*>(c)[2 * col8];
+    const float4 c1 = reinterpret_cast<const float4*>(c)[2 * col8 + 1];
+    cc[0] = c0.x; cc[1] = c0.y; cc[2] = c0.z; cc[3] = c0.w;
+    cc[4] = c1.x; cc[5] = c1.y; cc[6] = c1.z; cc[7] = c1.w;
+  }
+  uint4 v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = r0 + r < M ? r0 + r : M - 1;
+    v[r] = X[row * K8 + col8];
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+      x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+    if (c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = __fmul_rn(x[i], cc[i]);  // one rounded fp32 multiply
+    }
+    uint32_t word, sbyte;
+    quant8_mx<FMT>(x, word, sbyte);
+    const int64_t row = r0 + r;
+    if (live_c && row < M) {
+      codes[row * K8 + col8] = word;
+      if ((col8 & 3) == 0) scales[row * (K8 / 4) + (col8 >> 2)] = uint8_t(sbyte);
+    }
+  }
 }
 
 // ----------------------------------------------------------------- NVFP4 --
@@ -253,12 +302,28 @@ hipError_t launch_quantize_act(int fmt, int64_t M, int64_t K, const void* X, con
   const uint4* Xv = static_cast<const uint4*>(X);
   uint32_t* cw = static_cast<uint32_t*>(codes);
   uint8_t* sb = static_cast<uint8_t*>(scales);
-  if (fmt == MXFP4) {
-    hipLaunchKernelGGL(quantize_mx_kernel<MXFP4>, grid, dim3(kThreads), 0, stream, Xv, c, cw, sb,
-                       n_groups, K8);
-  } else if (fmt == MXINT4) {
-    hipLaunchKernelGGL(quantize_mx_kernel<MXINT4>, grid, dim3(kThreads), 0, stream, Xv, c, cw, sb,
-                       n_groups, K8);
+  if (fmt == MXFP4 || fmt == MXINT4) {
+    // 4 rows per thread once there are enough rows to fill the chip
+    const unsigned gy = unsigned((K8 + kThreads - 1) / kThreads);
+    if (M >= 1024) {
+      const dim3 g2(unsigned((M + 7) / 8), gy);
+      if (fmt == MXFP4)
+        hipLaunchKernelGGL((quantize_mx_kernel<MXFP4, 8>), g2, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
+      else
+        hipLaunchKernelGGL((quantize_mx_kernel<MXINT4, 8>), g2, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
+    } else if (M >= 256) {
+      const dim3 g2(unsigned((M + 3) / 4), gy);
+      if (fmt == MXFP4)
+        hipLaunchKernelGGL((quantize_mx_kernel<MXFP4, 4>), g2, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
+      else
+        hipLaunchKernelGGL((quantize_mx_kernel<MXINT4, 4>), g2, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
+    } else {
+      const dim3 g1(unsigned(M), gy);
+      if (fmt == MXFP4)
+        hipLaunchKernelGGL((quantize_mx_kernel<MXFP4, 1>), g1, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
+      else
+        hipLaunchKernelGGL((quantize_mx_kernel<MXINT4, 1>), g1, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
+    }
   } else {
     float* partial = static_cast<float*>(workspace);
     const int nparts = int(std::min<int64_t>(kNvAmaxBlocks, (n_groups + kThreads - 1) / kThreads));
