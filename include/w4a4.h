@@ -164,7 +164,9 @@ w4a4_status w4a4_unpack_weight(w4a4_format fmt, int64_t N, int64_t K,
  *   blob     device, a blob packed for the same fmt, N, K, 256-byte aligned.
  *   Y        device, out, bf16 [M x N], 16-byte aligned.
  *   workspace/ws_bytes: device scratch of at least
- *            w4a4_linear_workspace_bytes() bytes (may be 0).
+ *            w4a4_linear_workspace_bytes() bytes, 16-byte aligned (that
+ *            size is 0 for every format and shape in this version, and
+ *            NULL is accepted then).
  *
  * Requires M >= 0, N % 16 == 0, K % 128 == 0.  The blob's fmt, N and K are
  * trusted, not re-read from device memory.

@@ -58,6 +58,14 @@ def test_size_queries():
     assert L.w4a4_packed_weight_bytes(0, 128, 4000) == 0          # K % 128
 
 
+def test_linear_workspace_sizes():
+    """No GEMM path needs scratch memory: the workspace size is 0."""
+    L = w4.lib()
+    for fmt in (0, 1, 2):
+        for M, N, K in ((2048, 28672, 4096), (2048, 4096, 14336), (16, 4096, 4096)):
+            assert L.w4a4_linear_workspace_bytes(fmt, M, N, K) == 0
+
+
 def test_table12_scale_bytes_from_the_library():
     """Llama-3.1-8B's 224 linears: the MXFP4 blob payload is 3.49 GB of codes
     plus 0.22 GB of scales (Appendix I, Table 12 byte counts)."""

@@ -1,0 +1,81 @@
+"""GPU parity of the MXFP4 persistent GEMM against the oracle.
+
+MXFP4 shapes with at least 192 tiles of 256 x 256 and K a multiple of 512 run
+one workgroup per CU that walks its tiles as one stream of K-steps (the copy
+ring crosses tile boundaries).  Covered here, all outputs compared: several
+tiles per workgroup, tile counts that are not a multiple of the 8 XCDs,
+ragged M and N, one-quad tiles (K = 512: every tile's only quad also copies
+the next tile's first), bit-exactness where accumulation is exact, and
+repeated calls."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import device, say, to_dev, bf16_bits, check_linear
+from test_gpu_linear import gpu_layer, oracle_layer
+from w4a4_block_scaled_amd import inputs
+import w4a4_block_scaled_amd as w4
+
+pytestmark = pytest.mark.gpu
+
+
+def persistent(M, N, K):
+    """The host-side condition for the persistent kernel (MXFP4)."""
+    tiles = ((M + 255) // 256) * ((N + 255) // 256)
+    return M > 32 and K % 512 == 0 and tiles >= 192
+
+
+# (M, N, K): what the tile walk does with it (256 workgroups, 32 per XCD)
+PERSIST = [
+    (512, 40960, 1024),    # 320 tiles: 40 per XCD, 8 workgroups take two
+    (300, 24592, 1024),    # 194 tiles (24 or 25 per XCD), ragged M and N
+    (1100, 16400, 2048),   # 325 tiles, ragged M and N, 4 quads per tile
+    (512, 49152, 512),     # 384 tiles of one quad each
+]
+
+
+@pytest.mark.parametrize("M,N,K", PERSIST)
+def test_persistent_matches_oracle(M, N, K):
+    dev = device()
+    assert persistent(M, N, K)
+    say(f"[persistent] mxfp4 M={M} N={N} K={K}")
+    case = inputs.adhoc_case("mxfp4", M, N, K, seed=M + 7 * N + K)
+    Y, *_ = gpu_layer(case, dev)
+    y, S, _, _ = oracle_layer(case)
+    elem, row = check_linear(bf16_bits(Y), y, S, K, f"persistent {M}x{N}x{K}")
+    say(f"    max elementwise rel err {elem:.2e}, max row rel-L2 {row:.2e}")
+
+
+def test_persistent_bit_exact_when_accumulation_is_exact():
+    """All block scales of an operand equal: every fp32 partial sum is
+    exact, so Y equals the oracle's BF16 rounding bit for bit."""
+    dev = device()
+    M, N, K = 512, 24576, 1024
+    assert persistent(M, N, K)
+    say(f"[persistent bit-exact] M={M} N={N} K={K}")
+    rng = np.random.default_rng(11)
+    w_codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    w_scales = np.full((N, K // 32), 126, np.uint8)
+    r = np.ldexp(1.0, rng.integers(-3, 4, N)).astype(np.float32)
+    a_codes = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    a_scales = np.full((M, K // 32), 128, np.uint8)
+    blob = w4.pack_weight(to_dev(w_codes, dev), to_dev(w_scales, dev), None, to_dev(r, dev), "mxfp4")
+    Y = w4.linear(to_dev(a_codes, dev), to_dev(a_scales, dev), None, blob, "mxfp4", N, K)
+    bits, _ = oracle.linear_bf16(a_codes, a_scales, None, w_codes, w_scales, 1.0, r, "mxfp4")
+    got = bf16_bits(Y)
+    assert np.array_equal(got, bits), f"{(got != bits).sum()} of {bits.size} outputs differ"
+
+
+def test_persistent_repeated_calls():
+    """Same inputs twice around a call of another shape: identical results."""
+    dev = device()
+    a = inputs.adhoc_case("mxfp4", 512, 40960, 1024, seed=5)
+    b = inputs.adhoc_case("mxfp4", 300, 24592, 1024, seed=6)
+    say("[persistent repeat] 512x40960x1024 / 300x24592x1024")
+    Y1, blob, (ac, as_, ta), _ = gpu_layer(a, dev)
+    Yb1, blob_b, (bc, bs, bt), _ = gpu_layer(b, dev)
+    Y2 = w4.linear(ac, as_, ta, blob, "mxfp4", a.N, a.K)
+    Yb2 = w4.linear(bc, bs, bt, blob_b, "mxfp4", b.N, b.K)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(Yb1, Yb2)

@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["FORMATS", "lib", "library_path", "block_size", "quantize_act", "pack_weight",
-           "unpack_weight", "linear", "packed_weight_bytes", "W4A4Error"]
+           "unpack_weight", "linear", "linear_workspace", "packed_weight_bytes", "W4A4Error"]
 
 FORMATS = {"mxfp4": 0, "nvfp4": 1, "mxint4": 2}
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -160,10 +160,28 @@ def unpack_weight(blob: torch.Tensor, fmt, N: int, K: int):
     return codes, scales, r, t_w
 
 
+_LINEAR_WS = {}
+
+
+def linear_workspace(device, nbytes: int) -> torch.Tensor:
+    """A cached, zero-filled linear workspace of `device`, at least `nbytes`
+    long (w4a4_linear_workspace_bytes is 0 in this version; the cache keeps
+    the binding ready for paths that need one)."""
+    device = torch.device(device)
+    ws = _LINEAR_WS.get(device)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _LINEAR_WS[device] = ws
+    return ws
+
+
 def linear(a_codes: torch.Tensor, a_scales: torch.Tensor, t_act: Optional[torch.Tensor],
            blob: torch.Tensor, fmt, N: int, K: int, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """w4a4_linear: quantized activations [M, K/2] x packed weight -> bf16 [M, N]."""
+    """w4a4_linear: quantized activations [M, K/2] x packed weight -> bf16 [M, N].
+
+    Without `workspace`, shapes that need one use linear_workspace().
+    """
     f = _fmt(fmt)
     L = lib()
     M = a_codes.shape[0]
@@ -171,7 +189,7 @@ def linear(a_codes: torch.Tensor, a_scales: torch.Tensor, t_act: Optional[torch.
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
     ws_bytes = L.w4a4_linear_workspace_bytes(f, M, N, K)
     if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a_codes.device)
+        workspace = linear_workspace(a_codes.device, ws_bytes)
     _check(L.w4a4_linear(f, M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(t_act), _ptr(blob),
                          _ptr(out), _ptr(workspace),
                          workspace.numel() if workspace is not None else 0,

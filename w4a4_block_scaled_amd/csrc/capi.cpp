@@ -146,9 +146,10 @@ w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K, const 
     return fail(W4A4_ERR_WORKSPACE, "linear: needs %zu workspace bytes, got %zu", need,
                 workspace ? ws_bytes : size_t(0));
   if (!aligned(a_codes, 16) || !aligned(a_scales, 16) || !aligned(blob, 256) || !aligned(Y, 16) ||
-      (t_act && !aligned(t_act, 4)))
+      (t_act && !aligned(t_act, 4)) || (need && !aligned(workspace, 16)))
     return fail(W4A4_ERR_ALIGN,
-                "linear: a_codes/a_scales/Y need 16-byte, blob 256-byte, t_act 4-byte alignment");
+                "linear: a_codes/a_scales/Y/workspace need 16-byte, blob 256-byte, t_act 4-byte "
+                "alignment");
   return hip_status(w4a4::launch_linear(fmt, M, N, K, a_codes, a_scales, t_act, blob, Y, workspace,
                                         ws_bytes, static_cast<hipStream_t>(stream)),
                     "linear launch");

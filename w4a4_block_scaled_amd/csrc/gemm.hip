@@ -941,11 +941,12 @@ __device__ __forceinline__ void fp4_copy_scale_quarter(const Fp4Args& t, int64_t
 }
 
 // LDS byte offset of the scale dword of local activation row R, K-step ks
-template <int BN, int BM, int DEPTH>
+// (NB scale block buffers)
+template <int BN, int BM, int DEPTH, int NB = 3>
 __device__ __forceinline__ int fp4_scale_offset(int R, int64_t ks) {
   using C = Fp4Cfg<BN, BM, DEPTH>;
   const int w = R / C::ASR, r = R % C::ASR;
-  return C::AS_OFF + int((ks / 4) % 3) * C::ASB + w * (C::ASR * 16) + (r >> 4) * 256 + (r & 15) * 16 +
+  return C::AS_OFF + int((ks / 4) % NB) * C::ASB + w * (C::ASR * 16) + (r >> 4) * 256 + (r & 15) * 16 +
          int(ks & 3) * 4;
 }
 
@@ -998,7 +999,7 @@ __device__ __forceinline__ void fp4_fix_scales(int (&sa)[FM], int lane) {
 // `st`): activation scale dwords (raw, from the scale block; fp4_fix_scales
 // applies the lane's byte shift once the reads have landed), weight scale
 // words, activation fragments, weight fragments.
-template <int BN, int BM, int DEPTH>
+template <int BN, int BM, int DEPTH, int NB = 3>
 __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st,
                                               const LDS uint8_t* __restrict__ base, int64_t kstep,
                                               int wn, int wm, int lane, Fp4Frags<BN / 64, BM / 64>& fr,
@@ -1007,7 +1008,7 @@ __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st
   if (r < C::FM) {
     const int j = r;
     const int R = 32 * (wm * C::FM + j) + (lane & 31);
-    fr.sa[j] = *reinterpret_cast<const LDS int*>(base + fp4_scale_offset<BN, BM, DEPTH>(R, kstep));
+    fr.sa[j] = *reinterpret_cast<const LDS int*>(base + fp4_scale_offset<BN, BM, DEPTH, NB>(R, kstep));
   } else if (r < C::FM + 2) {
     const int hh = r - C::FM;
     const int e = ((wn * C::FN / 4) * 2 + hh) * 64 + lane;
@@ -1029,14 +1030,14 @@ __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st
   }
 }
 
-template <int BN, int BM, int DEPTH>
+template <int BN, int BM, int DEPTH, int NB = 3>
 __device__ __forceinline__ void fp4_read_all(const LDS uint8_t* __restrict__ st,
                                              const LDS uint8_t* __restrict__ base, int64_t kstep,
                                              int wn, int wm, int lane, Fp4Frags<BN / 64, BM / 64>& fr) {
   using C = Fp4Cfg<BN, BM, DEPTH>;
 #pragma unroll
   for (int r = 0; r < 3 * C::FM + 2 + 2 * C::FN; ++r)
-    fp4_read_item<BN, BM, DEPTH>(st, base, kstep, wn, wm, lane, fr, r);
+    fp4_read_item<BN, BM, DEPTH, NB>(st, base, kstep, wn, wm, lane, fr, r);
   fp4_fix_scales<C::FM>(fr.sa, lane);
 }
 
@@ -1205,6 +1206,394 @@ hipError_t launch_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
   const int per_xcd = (total + 7) / 8;
   hipLaunchKernelGGL((gemm_fp4_kernel<BN, BM, DEPTH>), dim3(unsigned(per_xcd * 8)), dim3(256), 0,
                      stream, ac, as, blob, Y, M, N, K, tiles_m, total, per_xcd);
+  return hipGetLastError();
+}
+
+// ===================================== MXFP4, persistent with stream-K ==
+//
+// Large MXFP4 GEMMs (256 x 256 tiles, K a multiple of 512) run one
+// workgroup per CU.  Tiles go to the 8 XCDs in contiguous chunks, each chunk
+// in the tile order of gemm_fp4_kernel (m fastest); within an XCD the 32
+// workgroups take its tiles round-robin, so each round of 32 concurrent
+// tiles shares activation rows and weight groups in that XCD's L2.
+//
+// The tiles of a workgroup form one stream of K-steps, and the DEPTH-deep
+// copy ring runs over that stream: the next tile's first K-steps are in
+// flight while a tile finishes, so there is no per-tile pipeline fill.  The
+// epilogue stores from the accumulators through a per-wave LDS staging
+// block; its buffer stores drop rows beyond M and columns beyond N at the
+// buffer's bounds.
+
+struct Fp4P {
+  static constexpr int BN = 256, BM = 256, DEPTH = 4, XCDS = 8, PER_XCD = 32;
+  using C = Fp4Cfg<BN, BM, DEPTH>;
+  static constexpr int NSB = 2;                      // activation scale block buffers
+  static constexpr int R_OFF = C::AS_OFF + NSB * C::ASB;  // r of two items, 1 KiB each
+  static constexpr int EPI_ROW = 80;                 // staging row stride (bytes)
+  static constexpr int EPI_OFF = R_OFF + 2 * 1024;   // per wave: 32 rows of 32 bf16
+  static constexpr int LDS_BYTES = EPI_OFF + C::WAVES * 32 * EPI_ROW;
+  // copies per wave with K-step j of a quad: activation and weight tiles,
+  // weight scale words, and with j = 0 the 4 quarters of the quad's
+  // activation scale block
+  static constexpr int STAGE_COPIES = C::A_DMA + C::W_DMA + 1;
+  static constexpr int copies(int j) { return STAGE_COPIES + (j == 0 ? 4 : 0); }
+  // copies younger than the stage the step at quad position j reads next
+  // (those of the two K-steps after it)
+  static constexpr int younger(int j) { return copies((j + 2) & 3) + copies((j + 3) & 3); }
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(DEPTH == 4, "one quad of K-steps in flight");
+};
+static_assert(Fp4P::younger(1) < 64 && Fp4P::younger(2) < 64, "vmcnt range");
+
+// The tiles of workgroup b: its XCD x = b % 8 and index i = b / 8 within it
+// (workgroups are dealt to the XCDs round-robin) give tiles tb + i + 32 k of
+// the XCD's chunk [tb, te).
+struct Fp4PSched {
+  int tiles_m, KS, tb, i, n_items;
+
+  __device__ __forceinline__ void init(int T, int tiles_m_, int KS_, int b) {
+    tiles_m = tiles_m_;
+    KS = KS_;
+    const int x = b % Fp4P::XCDS;
+    i = b / Fp4P::XCDS;
+    tb = int(int64_t(x) * T / Fp4P::XCDS);
+    const int te = int(int64_t(x + 1) * T / Fp4P::XCDS);
+    n_items = te - tb > i ? (te - tb - i + Fp4P::PER_XCD - 1) / Fp4P::PER_XCD : 0;
+  }
+  __device__ __forceinline__ int tile(int k) const { return tb + i + Fp4P::PER_XCD * k; }
+};
+
+// Where item k (the k-th tile) of the stream reads: its tile origin and
+// K-steps [ks0, ks0 + len).  Past the last tile it repeats the last tile's
+// last quad, so copies beyond the end of the stream read valid sources.
+struct Fp4PDesc {
+  int m0, g0;  // first activation row, first 32-row weight group
+  int ks0, len;
+};
+
+__device__ __forceinline__ Fp4PDesc fp4p_desc(const Fp4PSched& S, int k) {
+  const bool over = k >= S.n_items;
+  const int t = S.tile(over ? S.n_items - 1 : k);
+  Fp4PDesc d;
+  d.m0 = (t % S.tiles_m) * Fp4P::BM;
+  d.g0 = (t / S.tiles_m) * (Fp4P::BN / 32);
+  d.ks0 = over ? S.KS - 4 : 0;
+  d.len = over ? 4 : S.KS;
+  return d;
+}
+
+// Copies go straight into LDS as buffer loads (BUFFER_LOAD ... LDS): a scalar
+// resource (base, size in bytes) and a per-lane 32-bit offset.  Lanes whose
+// bytes lie beyond the size read zeros, which takes care of rows and weight
+// groups past the end of an operand; lane l writes `dst` + size * l.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, LDS void* lds, int size,
+                                                          int voffset, int soffset, int offset,
+                                                          int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// resource for the bytes [off, n) of `base` (offsets fit 31 bits: checked
+// on the host)
+__device__ __forceinline__ i32x4 buf_rsrc(const uint8_t* base, int off, int n) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base) + uint32_t(off);
+  return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xffff), n - off, 0x00020000};
+}
+
+// The operands as byte ranges.
+struct Fp4PSrc {
+  const uint8_t *ac, *as, *wc, *ws, *r;
+  int ac_n, as_n, wc_n, ws_n, r_n;
+  int K2, KB, KT;
+};
+
+// Per-lane offsets of the copies (fixed for the whole kernel): activation
+// tile k and weight tile k of the wave, weight scale word, activation scale
+// quarter (relative to its first row).
+struct Fp4PLane {
+  int a[4], w[4], ws, as;
+};
+
+__device__ __forceinline__ Fp4PLane fp4p_lane(const Fp4PSrc& b, int wave, int lane) {
+  using C = Fp4P::C;
+  static_assert(C::A_DMA == 4 && C::W_DMA == 4 && C::WS_DW == 64, "lane offsets");
+  Fp4PLane o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int f = wave * 4 + k;
+    // activation tile f: 16 rows x 64 B, lane l takes 16-byte chunk l/16 of row 16 f + l%16
+    o.a[k] = (16 * f + (lane & 15)) * b.K2 + (lane >> 4) * 16;
+    // weight tile f: group f/2, 64-K half f%2, lane l's 16 bytes
+    o.w[k] = ((f >> 1) * b.KT + (f & 1)) * 1024 + lane * 16;
+  }
+  const int e = wave * 64 + lane;  // weight scale word: (scale group, half, lane)
+  o.ws = ((e >> 7) * b.KT * 64 + ((e >> 6) & 1) * 64 + (e & 63)) * 4;
+  o.as = (wave * C::ASR + (lane >> 2)) * b.KB + 4 * (lane & 3);
+  return o;
+}
+
+// The copies of one quad of 4 K-steps (all in one item): the stage copies of
+// its K-step ks + j (tile at m0, g0) and the 4 quarters of its activation
+// scale block, into scale buffer sbuf.
+struct Fp4PQuad {
+  int m0, g0, ks;
+  int sbuf;
+};
+
+// Copy number k of a wave's share of K-step j of quad q (activation tiles,
+// weight tiles, weight scale words, then with j = 0 the scale quarters).
+template <int J>
+__device__ __forceinline__ void fp4p_copy(const Fp4PSrc& b, const Fp4PQuad& q, const Fp4PLane& o,
+                                          LDS uint8_t* smem, LDS uint8_t* dst, int wave, int k) {
+  using C = Fp4P::C;
+  const int ks = q.ks + J;
+  if (k < C::A_DMA) {
+    llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.ac, q.m0 * b.K2 + ks * 64, b.ac_n),
+                                    dst + (wave * C::A_DMA + k) * 1024, 16, o.a[k], 0, 0, 0);
+  } else if (k < C::A_DMA + C::W_DMA) {
+    llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.wc, (q.g0 * b.KT + 2 * ks) * 1024, b.wc_n),
+                                    dst + C::A_BYTES + (wave * C::W_DMA + k - C::A_DMA) * 1024, 16,
+                                    o.w[k - C::A_DMA], 0, 0, 0);
+  } else if (k == C::A_DMA + C::W_DMA) {
+    llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.ws, ((q.g0 / 4) * b.KT + 2 * ks) * 256, b.ws_n),
+                                    dst + C::A_BYTES + C::W_BYTES + wave * 256, 4, o.ws, 0, 0, 0);
+  } else {
+    const int qq = k - (C::A_DMA + C::W_DMA + 1);
+    llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.as, (q.m0 + 16 * qq) * b.KB + 4 * q.ks, b.as_n),
+                                    smem + C::AS_OFF + q.sbuf * C::ASB + wave * (C::ASR * 16) + qq * 256, 4,
+                                    o.as, 0, 0, 0);
+  }
+}
+
+// The lane index, read from the hardware where it is used.  Values derived
+// from it for the per-item code (r copy, first reads, epilogue) are then
+// computed there instead of being hoisted out of the item loop and held, or
+// spilled, across it: reloading a spill would wait for every copy in flight.
+__device__ __forceinline__ int fp4p_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// r of an item (256 output features from n = 32 g0) into r buffer `rbuf`
+__device__ __forceinline__ void fp4p_copy_r(const Fp4PSrc& b, LDS uint8_t* smem, int g0, int rbuf,
+                                            int wave) {
+  const int lane = fp4p_lane_id();
+  llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.r, g0 * 128, b.r_n),
+                                  smem + Fp4P::R_OFF + rbuf * 1024 + wave * 256, 4, (wave * 64 + lane) * 4, 0,
+                                  0, 0);
+}
+
+// One K-step of the stream, as Fp4Group: FN x 2 groups of FM MFMAs, each
+// followed by its share of the step's copies (K-step J of quad q) and of the
+// reads of stream K-step pr.
+template <int J, int G>
+struct Fp4PGroup {
+  using C = Fp4P::C;
+  static constexpr int FN = C::FN, FM = C::FM, NGRP = 2 * FN, NC = Fp4P::copies(J);
+  static constexpr int READS = 3 * FM + 2 + 2 * FN;
+  static __device__ __forceinline__ void run(v16f (&acc)[FN][FM], const Fp4Frags<FN, FM>& cur,
+                                             Fp4Frags<FN, FM>& nxt, LDS uint8_t* smem,
+                                             const Fp4PSrc& b, const Fp4PQuad& q, const Fp4PLane& o,
+                                             LDS uint8_t* dst, const LDS uint8_t* __restrict__ st,
+                                             int64_t pr, int wave, int wn, int wm, int lane) {
+    constexpr int H = G / FN, I = G % FN;
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      acc[I][j] = mfma32_fp4_op<I, 2 * H>(cur.w[I][H], cur.a[j][H], acc[I][j], cur.sw[H], cur.sa[j]);
+#pragma unroll
+    for (int k = G * NC / NGRP; k < (G + 1) * NC / NGRP; ++k) fp4p_copy<J>(b, q, o, smem, dst, wave, k);
+    constexpr int RG = NGRP - 2;
+    if constexpr (G < RG) {
+#pragma unroll
+      for (int r = G * READS / RG; r < (G + 1) * READS / RG; ++r)
+        fp4_read_item<Fp4P::BN, Fp4P::BM, Fp4P::DEPTH, Fp4P::NSB>(st, smem, pr, wn, wm, lane, nxt, r);
+    }
+    if constexpr (G + 1 == NGRP) fp4_fix_scales<FM>(nxt.sa, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (G + 1 < NGRP)
+      Fp4PGroup<J, G + 1>::run(acc, cur, nxt, smem, b, q, o, dst, st, pr, wave, wn, wm, lane);
+  }
+};
+
+// Step p = 4 p4 + J of the stream (position J of its quad; quads start at
+// multiples of 4, so K-step p is in stage J): wait for the stage of K-step
+// p + 1 (at most younger(J) copies of this wave issued after it in flight;
+// vector memory operations complete in issue order, so anything else issued
+// later only makes the wait stricter) and barrier, then MFMAs of K-step p
+// from `cur`, copies of stream K-step p + DEPTH (K-step J of quad q) into
+// stage J, reads of K-step p + 1 into `nxt`.  The stage indices are
+// compile-time, so the LDS reads use immediate offsets.
+template <int J>
+__device__ __forceinline__ void fp4p_step(v16f (&acc)[4][4], const Fp4Frags<4, 4>& cur,
+                                          Fp4Frags<4, 4>& nxt, LDS uint8_t* smem, const Fp4PSrc& b,
+                                          const Fp4PQuad& q, const Fp4PLane& o, int p4, int wave, int wn,
+                                          int wm, int lane) {
+  using C = Fp4P::C;
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(Fp4P::younger(J)));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  Fp4PGroup<J, 0>::run(acc, cur, nxt, smem, b, q, o, smem + J * C::STAGE, smem + ((J + 1) & 3) * C::STAGE,
+                       4 * int64_t(p4) + J + 1, wave, wn, wm, lane);
+}
+
+// Y[m0.., n0..] = bf16(acc * r) for the wave's 128 x 128 block (straight-line
+// code, so the accumulators are read where they are used).  Each 32 x 32
+// block goes through the wave's staging rows, then out as 16-byte buffer
+// stores (two per lane).
+__device__ __forceinline__ void fp4p_epilogue(const v16f (&acc)[4][4], LDS uint8_t* base, int rbuf,
+                                              uint16_t* __restrict__ Y, int64_t M, int64_t N,
+                                              int64_t m0, int64_t n0, int wave, int wn, int wm) {
+  const int lane = fp4p_lane_id();
+  const LDS uint8_t* rb = base + Fp4P::R_OFF + rbuf * 1024;
+  LDS uint8_t* ep = base + Fp4P::EPI_OFF + wave * (32 * Fp4P::EPI_ROW);
+  const int64_t rows = M - m0 < Fp4P::BM ? M - m0 : Fp4P::BM;
+  const __amdgpu_buffer_rsrc_t ys =
+      __builtin_amdgcn_make_buffer_rsrc(Y + m0 * N, 0, int(rows * N * 2), 0x00020000);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v4f rs[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = wn * 128 + 32 * i + 8 * q + 4 * (lane >> 5);
+      rs[q] = *reinterpret_cast<const LDS v4f*>(rb + n * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = lane & 31;
+      // read this block's accumulators here, not all of them up front
+      v16f av = acc[i][j];
+      asm volatile("" : "+a"(av));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f a = {av[4 * q], av[4 * q + 1], av[4 * q + 2], av[4 * q + 3]};
+        *reinterpret_cast<LDS u32x2*>(ep + row * Fp4P::EPI_ROW + q * 16 + 8 * (lane >> 5)) =
+            scale_pack4(a, rs[q]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int idx = h * 64 + lane, rr = idx >> 2, ch = idx & 3;
+        const u32x4 v = *reinterpret_cast<const LDS u32x4*>(ep + rr * Fp4P::EPI_ROW + ch * 16);
+        const int m = wm * 128 + 32 * j + rr;
+        const int64_t n = n0 + wn * 128 + 32 * i + 8 * ch;
+        const int off = n < N ? int((m * N + n) * 2) : -1;  // -1: beyond the buffer, dropped
+        __builtin_amdgcn_raw_buffer_store_b128(v, ys, off, 0, 0);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int tiles_m, int tiles_total) {
+  using C = Fp4P::C;
+  constexpr int FN = C::FN, FM = C::FM, DEPTH = Fp4P::DEPTH;
+  const BlobLayout L = blob_layout(MXFP4, N, K);
+  Fp4PSched S;
+  S.init(tiles_total, tiles_m, int(L.KS), int(blockIdx.x));
+  if (S.n_items == 0) return;
+
+  Fp4PSrc b;
+  b.ac = a_codes;
+  b.as = a_scales;
+  b.wc = blob + L.code_off;
+  b.ws = blob + L.scale_off;
+  b.r = blob + L.r_off;
+  b.K2 = int(K / 2);
+  b.KB = int(K / 32);
+  b.KT = int(L.KT);
+  b.ac_n = int(M * b.K2);
+  b.as_n = int(M * b.KB);
+  b.wc_n = int(L.NG * L.KT * 1024);
+  b.ws_n = int(L.NSG * L.KT * 256);
+  b.r_n = int(N * 4);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Fp4P::LDS_BYTES];
+  LDS uint8_t* base = (LDS uint8_t*)smem;
+  // the wave index as a scalar, so that wave-dependent LDS addresses are too
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  const Fp4PLane o = fp4p_lane(b, wave, lane);
+
+  // prologue: r of item 0 and the copies of stream quad 0 (item 0's first)
+  {
+    const Fp4PDesc d0 = fp4p_desc(S, 0);
+    fp4p_copy_r(b, base, d0.g0, 0, wave);
+    const Fp4PQuad q{d0.m0, d0.g0, d0.ks0, 0};
+#pragma unroll
+    for (int k = 0; k < Fp4P::copies(0); ++k) fp4p_copy<0>(b, q, o, base, base, wave, k);
+#pragma unroll
+    for (int k = 0; k < Fp4P::copies(1); ++k) fp4p_copy<1>(b, q, o, base, base + C::STAGE, wave, k);
+#pragma unroll
+    for (int k = 0; k < Fp4P::copies(2); ++k) fp4p_copy<2>(b, q, o, base, base + 2 * C::STAGE, wave, k);
+#pragma unroll
+    for (int k = 0; k < Fp4P::copies(3); ++k) fp4p_copy<3>(b, q, o, base, base + 3 * C::STAGE, wave, k);
+  }
+  // stage 0 (and scale block 0) landed: 3 K-steps of copies issued after it
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(Fp4P::copies(1) + Fp4P::copies(2) + Fp4P::copies(3)));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  int64_t p = 0;  // stream K-step whose MFMAs run next
+  for (int k = 0; k < S.n_items; ++k) {
+    const Fp4PDesc d0 = fp4p_desc(S, k), d1 = fp4p_desc(S, k + 1);
+    v16f acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    // The stage of K-step p has landed (the wait of the previous step, or of
+    // the prologue), and every wave is past item k-1's epilogue: r of item
+    // k+1 goes into the r buffer item k-1 used.
+    __builtin_amdgcn_s_barrier();
+    fp4p_copy_r(b, base, d1.g0, (k + 1) & 1, wave);
+    // the item's first fragments (read here rather than carried from the
+    // previous item's last step, so that none are live in its epilogue)
+    Fp4Frags<FN, FM> fa, fb;
+    fp4_read_all<Fp4P::BN, Fp4P::BM, DEPTH, Fp4P::NSB>(base, base, 4 * int64_t(p >> 2), wn, wm,
+                                                       fp4p_lane_id(), fa);
+    // one quad per iteration; it copies the next quad, in this item or (in
+    // its last iteration) the first of the next item
+    for (int u = 0; u < d0.len; u += 4) {
+      const bool nx = u + 4 >= d0.len;
+      Fp4PQuad q;
+      q.m0 = nx ? d1.m0 : d0.m0;
+      q.g0 = nx ? d1.g0 : d0.g0;
+      q.ks = nx ? d1.ks0 : d0.ks0 + u + 4;
+      const int p4 = int((p + u) >> 2);
+      q.sbuf = (p4 + 1) & 1;
+      fp4p_step<0>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+      fp4p_step<1>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+      fp4p_step<2>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+      fp4p_step<3>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    }
+    p += d0.len;
+
+    const int64_t n0 = int64_t(d0.g0) * 32;
+    fp4p_epilogue(acc, base, k & 1, Y, M, N, d0.m0, n0, wave, wn, wm);
+  }
+  // every copy (the last ones repeat valid sources) lands before the end
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// The persistent kernel's conditions: at least 192 tiles of 256 x 256 (below
+// that the one-tile-per-workgroup kernel does as well), K in whole quads of
+// 128-wide K-steps, operands and Y's tile rows addressable by 32-bit buffer
+// offsets.
+bool fp4_persistent_fits(int64_t M, int64_t N, int64_t K) {
+  const int64_t T = ((N + 255) / 256) * ((M + 255) / 256);
+  return M > 32 && K % 512 == 0 && T >= 192 && T < (int64_t(1) << 24) &&
+         int64_t(Fp4P::BM) * N * 2 < (int64_t(1) << 31) && M * (K / 2) < (int64_t(1) << 31) &&
+         ((N + 31) / 32) * 32 * (K / 2) < (int64_t(1) << 31);
+}
+
+hipError_t launch_fp4_persistent(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
+                                 const uint8_t* as, const uint8_t* blob, uint16_t* Y,
+                                 hipStream_t stream) {
+  const int tiles_m = int((M + 255) / 256);
+  const int total = int((N + 255) / 256) * tiles_m;
+  hipLaunchKernelGGL(gemm_fp4_persistent_kernel, dim3(Fp4P::XCDS * Fp4P::PER_XCD), dim3(256), 0,
+                     stream, ac, as, blob, Y, M, N, K, tiles_m, total);
   return hipGetLastError();
 }
 
@@ -1405,8 +1794,10 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
       if ((N + 31) / 32 >= 512) return launch_fp4_decode<4, 8>(M, N, K, ac, as, blob, Y, stream);
       return launch_fp4_decode<8, 4>(M, N, K, ac, as, blob, Y, stream);
     }
+    // large problems: the persistent kernel (256 x 256 tiles); otherwise
     // 256 x 256 tiles (4 waves of 128 x 128) unless that leaves more than
-    // ~30% of the 256 CUs idle; then 256 (n) x 128 (m) tiles.
+    // ~30% of the 256 CUs idle, then 256 (n) x 128 (m) tiles.
+    if (fp4_persistent_fits(M, N, K)) return launch_fp4_persistent(M, N, K, ac, as, blob, Y, stream);
     const int64_t big = ((N + 255) / 256) * ((M + 255) / 256);
     if (big >= 180) return launch_fp4<256, 256, 4>(M, N, K, ac, as, blob, Y, stream);
     return launch_fp4<256, 128, 5>(M, N, K, ac, as, blob, Y, stream);
