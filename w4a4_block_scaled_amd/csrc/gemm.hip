@@ -1481,6 +1481,49 @@ __device__ __forceinline__ void fp4p_epilogue(const v16f (&acc)[4][4], LDS uint8
   }
 }
 
+// Prologue of a stream: r of its first item (buffer 0) and the copies of
+// its first quad.
+__device__ __forceinline__ void fp4p_prologue(const Fp4PSrc& b, const Fp4PLane& o, LDS uint8_t* base,
+                                              const Fp4PDesc& d0, int wave) {
+  using C = Fp4P::C;
+  fp4p_copy_r(b, base, d0.g0, 0, wave);
+  const Fp4PQuad q{d0.m0, d0.g0, d0.ks0, 0};
+#pragma unroll
+  for (int k = 0; k < Fp4P::copies(0); ++k) fp4p_copy<0>(b, q, o, base, base, wave, k);
+#pragma unroll
+  for (int k = 0; k < Fp4P::copies(1); ++k) fp4p_copy<1>(b, q, o, base, base + C::STAGE, wave, k);
+#pragma unroll
+  for (int k = 0; k < Fp4P::copies(2); ++k) fp4p_copy<2>(b, q, o, base, base + 2 * C::STAGE, wave, k);
+#pragma unroll
+  for (int k = 0; k < Fp4P::copies(3); ++k) fp4p_copy<3>(b, q, o, base, base + 3 * C::STAGE, wave, k);
+  // stage 0 (and scale block 0) landed: 3 K-steps of copies issued after it
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(Fp4P::copies(1) + Fp4P::copies(2) + Fp4P::copies(3)));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The K-steps of item d0 (stream K-steps p..p + d0.len - 1, p a multiple
+// of 4), one quad per iteration; each quad copies the next one, in this
+// item or (in its last iteration) the first of item d1.
+__device__ __forceinline__ void fp4p_item(v16f (&acc)[4][4], Fp4Frags<4, 4>& fa, Fp4Frags<4, 4>& fb,
+                                          LDS uint8_t* base, const Fp4PSrc& b, const Fp4PLane& o,
+                                          const Fp4PDesc& d0, const Fp4PDesc& d1, int64_t p, int wave,
+                                          int wn, int wm, int lane) {
+  for (int u = 0; u < d0.len; u += 4) {
+    const bool nx = u + 4 >= d0.len;
+    Fp4PQuad q;
+    q.m0 = nx ? d1.m0 : d0.m0;
+    q.g0 = nx ? d1.g0 : d0.g0;
+    q.ks = nx ? d1.ks0 : d0.ks0 + u + 4;
+    const int p4 = int((p + u) >> 2);
+    q.sbuf = (p4 + 1) & 1;
+    fp4p_step<0>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<1>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<2>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<3>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+  }
+}
+
 __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
@@ -1513,24 +1556,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
   const int wn = wave % C::WN, wm = wave / C::WN;
   const Fp4PLane o = fp4p_lane(b, wave, lane);
 
-  // prologue: r of item 0 and the copies of stream quad 0 (item 0's first)
-  {
-    const Fp4PDesc d0 = fp4p_desc(S, 0);
-    fp4p_copy_r(b, base, d0.g0, 0, wave);
-    const Fp4PQuad q{d0.m0, d0.g0, d0.ks0, 0};
-#pragma unroll
-    for (int k = 0; k < Fp4P::copies(0); ++k) fp4p_copy<0>(b, q, o, base, base, wave, k);
-#pragma unroll
-    for (int k = 0; k < Fp4P::copies(1); ++k) fp4p_copy<1>(b, q, o, base, base + C::STAGE, wave, k);
-#pragma unroll
-    for (int k = 0; k < Fp4P::copies(2); ++k) fp4p_copy<2>(b, q, o, base, base + 2 * C::STAGE, wave, k);
-#pragma unroll
-    for (int k = 0; k < Fp4P::copies(3); ++k) fp4p_copy<3>(b, q, o, base, base + 3 * C::STAGE, wave, k);
-  }
-  // stage 0 (and scale block 0) landed: 3 K-steps of copies issued after it
-  __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(Fp4P::copies(1) + Fp4P::copies(2) + Fp4P::copies(3)));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  fp4p_prologue(b, o, base, fp4p_desc(S, 0), wave);
 
   int64_t p = 0;  // stream K-step whose MFMAs run next
   for (int k = 0; k < S.n_items; ++k) {
@@ -1552,21 +1578,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
     Fp4Frags<FN, FM> fa, fb;
     fp4_read_all<Fp4P::BN, Fp4P::BM, DEPTH, Fp4P::NSB>(base, base, 4 * int64_t(p >> 2), wn, wm,
                                                        fp4p_lane_id(), fa);
-    // one quad per iteration; it copies the next quad, in this item or (in
-    // its last iteration) the first of the next item
-    for (int u = 0; u < d0.len; u += 4) {
-      const bool nx = u + 4 >= d0.len;
-      Fp4PQuad q;
-      q.m0 = nx ? d1.m0 : d0.m0;
-      q.g0 = nx ? d1.g0 : d0.g0;
-      q.ks = nx ? d1.ks0 : d0.ks0 + u + 4;
-      const int p4 = int((p + u) >> 2);
-      q.sbuf = (p4 + 1) & 1;
-      fp4p_step<0>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-      fp4p_step<1>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
-      fp4p_step<2>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-      fp4p_step<3>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
-    }
+    fp4p_item(acc, fa, fb, base, b, o, d0, d1, p, wave, wn, wm, lane);
     p += d0.len;
 
     const int64_t n0 = int64_t(d0.g0) * 32;
