@@ -207,6 +207,18 @@ def cpu_baseline(workload, M, rows=512, cols=4096):
                       f"(quantize both + fp64 linear), {secs:.1f} s"}
 
 
+def gemm_kernel_label(fmt, M):
+    """The GEMM kernels behind the roofline figure (all launches of a step)."""
+    if fmt == "mxfp4":
+        if M <= 32:
+            return "gemm_fp4_decode_kernel"
+        return ("gemm_fp4_persistent_kernel (linears of 192+ tiles of 256x256) and "
+                "gemm_fp4_kernel (the others)")
+    if fmt == "mxint4":
+        return "gemm_decode_kernel<mxint4>" if M <= 16 else "gemm_mx_kernel<mxint4>"
+    return "gemm_tile_kernel<nvfp4>"
+
+
 def traffic_record(kernel):
     """Measured HBM bytes per GEMM launch (FETCH_SIZE + WRITE_SIZE, each scaled
     by its reading for a 1 GiB copy), averaged over the workload's launches,
@@ -275,7 +287,7 @@ def main():
             "traffic": traffic_record(f"gemm_{a.workload}_M{M}"),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes_per_launch": round(sum(L.gemm_bytes for L in layers) / len(layers)),
-            "kernel": f"gemm_tile_kernel<{fmt}>" if M > 16 or fmt == "nvfp4" else f"gemm_decode_kernel<{fmt}>",
+            "kernel": gemm_kernel_label(fmt, M),
             "per_linear": {L.case.name: {"us": round(t * 1e3, 2),
                                          "TFLOP/s": round(L.flops / (t * 1e-3) / 1e12, 1),
                                          "frac": round(L.flops / (t * 1e-3) / peak, 4)}
