@@ -922,6 +922,15 @@ __device__ __forceinline__ void fp4_sync(int after) {
   asm volatile("" ::: "memory");
 }
 
+// Activation tiles (16 rows x the 64 bytes of one K-step) are copied with
+// lane l taking row l / 4 and 16-byte chunk (l % 4) ^ fp4_swz(l / 4): four
+// consecutive lanes read the 64 contiguous bytes of one row (one request per
+// lane quad instead of four), and the LDS tile holds chunk c of row r at
+// position 4 r + (c ^ fp4_swz(r)).  The swizzle keeps the fragment reads
+// (16 consecutive rows, one chunk) free of bank conflicts for 32 and for 64
+// LDS banks.
+__device__ __forceinline__ int fp4_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
 // Quarter q of activation scale block b (the scale dwords of K-steps
 // 4b..4b+3): lane l of wave w copies the dword of row w*ASR + 16q + l/4,
 // K-step 4b + l%4, so one copy touches 16 rows instead of 64.  Rows beyond
@@ -957,12 +966,11 @@ __device__ __forceinline__ void fp4_copy(const Fp4Args& t, int64_t ks, LDS uint8
                                          int lane, int k) {
   using C = Fp4Cfg<BN, BM, DEPTH>;
   if (k < C::A_DMA) {
-    // 16 rows x 64 contiguous bytes (one K-step): lane l takes the 16-byte
-    // chunk l/16 of row 16 f + l%16
+    // 16 rows x 64 contiguous bytes (one K-step), rows in lane quads (fp4_swz)
     const int f = wave * C::A_DMA + k;
-    int64_t row = t.m0 + 16 * f + (lane & 15);
+    int64_t row = t.m0 + 16 * f + (lane >> 2);
     row = row < t.M ? row : t.M - 1;
-    lds_copy16(t.a_codes + row * t.K2 + ks * 64 + (lane >> 4) * 16, dst + f * 1024);
+    lds_copy16(t.a_codes + row * t.K2 + ks * 64 + ((lane & 3) ^ fp4_swz(lane >> 2)) * 16, dst + f * 1024);
   } else if (k < C::A_DMA + C::W_DMA) {
     const int f = wave * C::W_DMA + (k - C::A_DMA);
     int64_t g = t.g0 + (f >> 1);
@@ -1018,11 +1026,12 @@ __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st
     fr.sw[hh] = int(C::FN == 4 ? wsw : wsw >> (8 * ((wn * C::FN) & 3)));
   } else if (r < 3 * C::FM + 2) {
     const int q = r - C::FM - 2, j = q >> 1, hh = q & 1;
-    // fragment lane l: row 32 g + l%32 (16-row block 2 g + (l%32)/16),
-    // 16-byte chunk 2 hh + l/32 of its K-step bytes
+    // fragment lane l: row 32 g + l%32 (16-row tile 2 g + (l%32)/16, row
+    // l%16 in it), 16-byte chunk 2 hh + l/32 of its K-step bytes (fp4_swz)
+    const int rr = lane & 15;
     fr.a[j][hh] = *reinterpret_cast<const LDS u32x4*>(
-        st + (2 * (wm * C::FM + j) + ((lane >> 4) & 1)) * 1024 + (2 * hh + (lane >> 5)) * 256 +
-        (lane & 15) * 16);
+        st + (2 * (wm * C::FM + j) + ((lane >> 4) & 1)) * 1024 +
+        (4 * rr + ((2 * hh + (lane >> 5)) ^ fp4_swz(rr))) * 16);
   } else {
     const int q = r - 3 * C::FM - 2, i = q >> 1, hh = q & 1;
     fr.w[i][hh] = *reinterpret_cast<const LDS u32x4*>(st + C::A_BYTES + ((wn * C::FN + i) * 2 + hh) * 1024 +
@@ -1209,7 +1218,7 @@ hipError_t launch_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
   return hipGetLastError();
 }
 
-// ===================================== MXFP4, persistent with stream-K ==
+// ===================================== MXFP4, persistent ==
 //
 // Large MXFP4 GEMMs (256 x 256 tiles, K a multiple of 512) run one
 // workgroup per CU.  Tiles go to the 8 XCDs in contiguous chunks, each chunk
@@ -1220,18 +1229,21 @@ hipError_t launch_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
 // The tiles of a workgroup form one stream of K-steps, and the DEPTH-deep
 // copy ring runs over that stream: the next tile's first K-steps are in
 // flight while a tile finishes, so there is no per-tile pipeline fill.  The
-// epilogue stores from the accumulators through a per-wave LDS staging
-// block; its buffer stores drop rows beyond M and columns beyond N at the
-// buffer's bounds.
+// epilogue stores straight from registers (a lane swap gives each lane 8
+// consecutive outputs of its row); its buffer stores drop rows beyond M and
+// columns beyond N at the buffer's bounds.
 
 struct Fp4P {
   static constexpr int BN = 256, BM = 256, DEPTH = 4, XCDS = 8, PER_XCD = 32;
   using C = Fp4Cfg<BN, BM, DEPTH>;
   static constexpr int NSB = 2;                      // activation scale block buffers
   static constexpr int R_OFF = C::AS_OFF + NSB * C::ASB;  // r of two items, 1 KiB each
-  static constexpr int EPI_ROW = 80;                 // staging row stride (bytes)
-  static constexpr int EPI_OFF = R_OFF + 2 * 1024;   // per wave: 32 rows of 32 bf16
-  static constexpr int LDS_BYTES = EPI_OFF + C::WAVES * 32 * EPI_ROW;
+  static constexpr int LDS_BYTES = R_OFF + 2 * 1024;
+  // vector memory operations of a wave between the copies of one item's
+  // last quad and the first K-step of the next: the epilogue's stores (two
+  // per 32 x 32 block) and the copy of the following item's r
+  static constexpr int EPI_STORES = 2 * C::FN * C::FM;
+  static constexpr int ITEM_OPS = EPI_STORES + 1;
   // copies per wave with K-step j of a quad: activation and weight tiles,
   // weight scale words, and with j = 0 the 4 quarters of the quad's
   // activation scale block
@@ -1243,7 +1255,9 @@ struct Fp4P {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(DEPTH == 4, "one quad of K-steps in flight");
 };
-static_assert(Fp4P::younger(1) < 64 && Fp4P::younger(2) < 64, "vmcnt range");
+static_assert(Fp4P::younger(1) + Fp4P::ITEM_OPS < 64 && Fp4P::younger(2) + Fp4P::ITEM_OPS < 64 &&
+                  Fp4P::copies(1) + Fp4P::copies(2) + Fp4P::copies(3) + Fp4P::EPI_STORES < 64,
+              "vmcnt range");
 
 // The tiles of workgroup b: its XCD x = b % 8 and index i = b / 8 within it
 // (workgroups are dealt to the XCDs round-robin) give tiles tb + i + 32 k of
@@ -1319,8 +1333,8 @@ __device__ __forceinline__ Fp4PLane fp4p_lane(const Fp4PSrc& b, int wave, int la
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int f = wave * 4 + k;
-    // activation tile f: 16 rows x 64 B, lane l takes 16-byte chunk l/16 of row 16 f + l%16
-    o.a[k] = (16 * f + (lane & 15)) * b.K2 + (lane >> 4) * 16;
+    // activation tile f: 16 rows x 64 B, rows in lane quads (fp4_swz)
+    o.a[k] = (16 * f + (lane >> 2)) * b.K2 + ((lane & 3) ^ fp4_swz(lane >> 2)) * 16;
     // weight tile f: group f/2, 64-K half f%2, lane l's 16 bytes
     o.w[k] = ((f >> 1) * b.KT + (f & 1)) * 1024 + lane * 16;
   }
@@ -1416,75 +1430,99 @@ struct Fp4PGroup {
 
 // Step p = 4 p4 + J of the stream (position J of its quad; quads start at
 // multiples of 4, so K-step p is in stage J): wait for the stage of K-step
-// p + 1 (at most younger(J) copies of this wave issued after it in flight;
-// vector memory operations complete in issue order, so anything else issued
-// later only makes the wait stricter) and barrier, then MFMAs of K-step p
-// from `cur`, copies of stream K-step p + DEPTH (K-step J of quad q) into
-// stage J, reads of K-step p + 1 into `nxt`.  The stage indices are
+// p + 1 and barrier, then MFMAs of K-step p from `cur`, copies of stream
+// K-step p + DEPTH (K-step J of quad q) into stage J, reads of K-step p + 1
+// into `nxt`.  The wait leaves in flight the younger(J) copies this wave
+// issued after that stage, plus X other operations issued after it (in the
+// first quad of an item: the previous item's epilogue stores and the r
+// copy); vector memory operations complete in issue order, so anything
+// else issued later only makes the wait stricter.  The stage indices are
 // compile-time, so the LDS reads use immediate offsets.
-template <int J>
+template <int J, int X>
 __device__ __forceinline__ void fp4p_step(v16f (&acc)[4][4], const Fp4Frags<4, 4>& cur,
                                           Fp4Frags<4, 4>& nxt, LDS uint8_t* smem, const Fp4PSrc& b,
                                           const Fp4PQuad& q, const Fp4PLane& o, int p4, int wave, int wn,
                                           int wm, int lane) {
   using C = Fp4P::C;
-  __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(Fp4P::younger(J)));
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(Fp4P::younger(J) + X));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   Fp4PGroup<J, 0>::run(acc, cur, nxt, smem, b, q, o, smem + J * C::STAGE, smem + ((J + 1) & 3) * C::STAGE,
                        4 * int64_t(p4) + J + 1, wave, wn, wm, lane);
 }
 
-// Y[m0.., n0..] = bf16(acc * r) for the wave's 128 x 128 block (straight-line
-// code, so the accumulators are read where they are used).  Each 32 x 32
-// block goes through the wave's staging rows, then out as 16-byte buffer
-// stores (two per lane).
+// Y[m0.., n0..] = bf16(acc * r) for the wave's 128 x 128 block, straight
+// from the accumulators.  In a 32 x 32 block, lane l holds row l % 32 and
+// for g = 0..3 the 4 columns 8 g + 4 (l / 32) + 0..3.  Two lane exchanges
+// give each lane 8 consecutive columns: swapping the upper lane half of the
+// group-2p words with the lower lane half of the group-(2p+1) words leaves
+// lane l with columns 16 p + 8 (l / 32) + 0..7 of row l % 32 (p = 0, 1);
+// swapping 16-lane rows 1 and 3 of the p = 0 set with rows 0 and 2 of the
+// p = 1 set then leaves the first set with rows 0..15 and the second with
+// rows 16..31, lane l holding row l % 16, columns 8 c + 0..7 with
+// c = 2 ((l / 16) % 2) + l / 32.  Each 16-byte-per-lane store thus writes
+// 16 rows x 64 bytes.  Blocks go out row band by row band (j outer), so a
+// band's rows are written as whole 256-byte segments back to back.  Exactly
+// EPI_STORES buffer stores per wave (the first K-steps of the next item
+// count them).
 __device__ __forceinline__ void fp4p_epilogue(const v16f (&acc)[4][4], LDS uint8_t* base, int rbuf,
                                               uint16_t* __restrict__ Y, int64_t M, int64_t N,
-                                              int64_t m0, int64_t n0, int wave, int wn, int wm) {
-  const int lane = fp4p_lane_id();
+                                              int64_t m0, int64_t n0, int wn, int wm) {
+  const int lane = fp4p_lane_id(), h = lane >> 5;
   const LDS uint8_t* rb = base + Fp4P::R_OFF + rbuf * 1024;
-  LDS uint8_t* ep = base + Fp4P::EPI_OFF + wave * (32 * Fp4P::EPI_ROW);
   const int64_t rows = M - m0 < Fp4P::BM ? M - m0 : Fp4P::BM;
   const __amdgpu_buffer_rsrc_t ys =
       __builtin_amdgcn_make_buffer_rsrc(Y + m0 * N, 0, int(rows * N * 2), 0x00020000);
+  v4f rs[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v4f rs[4];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = wn * 128 + 32 * i + 8 * q + 4 * (lane >> 5);
-      rs[q] = *reinterpret_cast<const LDS v4f*>(rb + n * 4);
-    }
+    for (int g = 0; g < 4; ++g)
+      rs[i][g] = *reinterpret_cast<const LDS v4f*>(rb + (wn * 128 + 32 * i + 8 * g + 4 * h) * 4);
+  // 32-bit offsets: the host checks 256 N * 2 < 2^31
+  const int N32 = int(N), row = wm * 128 + (lane & 15);
+  const int n32 = int(n0) + wn * 128 + 8 * (2 * ((lane >> 4) & 1) + h);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = lane & 31;
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       // read this block's accumulators here, not all of them up front
       v16f av = acc[i][j];
       asm volatile("" : "+a"(av));
+      u32x4 v[2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const v4f a = {av[4 * q], av[4 * q + 1], av[4 * q + 2], av[4 * q + 3]};
-        *reinterpret_cast<LDS u32x2*>(ep + row * Fp4P::EPI_ROW + q * 16 + 8 * (lane >> 5)) =
-            scale_pack4(a, rs[q]);
+      for (int p = 0; p < 2; ++p) {
+        const v4f a0 = {av[8 * p], av[8 * p + 1], av[8 * p + 2], av[8 * p + 3]};
+        const v4f a1 = {av[8 * p + 4], av[8 * p + 5], av[8 * p + 6], av[8 * p + 7]};
+        const u32x2 lo = scale_pack4(a0, rs[i][2 * p]), hi = scale_pack4(a1, rs[i][2 * p + 1]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(lo.x, hi.x, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(lo.y, hi.y, false, false);
+        v[p] = u32x4{s0[0], s1[0], s0[1], s1[1]};
       }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int idx = h * 64 + lane, rr = idx >> 2, ch = idx & 3;
-        const u32x4 v = *reinterpret_cast<const LDS u32x4*>(ep + rr * Fp4P::EPI_ROW + ch * 16);
-        const int m = wm * 128 + 32 * j + rr;
-        const int64_t n = n0 + wn * 128 + 32 * i + 8 * ch;
-        const int off = n < N ? int((m * N + n) * 2) : -1;  // -1: beyond the buffer, dropped
-        __builtin_amdgcn_raw_buffer_store_b128(v, ys, off, 0, 0);
+      for (int d = 0; d < 4; ++d) {
+        const auto t = __builtin_amdgcn_permlane16_swap(v[0][d], v[1][d], false, false);
+        v[0][d] = t[0];
+        v[1][d] = t[1];
+      }
+      // columns beyond N: offset -1 (beyond the buffer, dropped), formed
+      // without a compare so that every store is issued (the wave counts them)
+      const int n = n32 + 32 * i;
+      const int past = (N32 - 1 - n) >> 31;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int m = row + 32 * j + 16 * hh;
+        __builtin_amdgcn_raw_buffer_store_b128(v[hh], ys, ((m * N32 + n) * 2) | past, 0, 0);
       }
     }
-  }
 }
 
-// Prologue of a stream: r of its first item (buffer 0) and the copies of
-// its first quad.
+// Prologue of a stream: r of its first item (buffer 0), the copies of its
+// first quad, then EPI_STORES stores that write nothing (offsets beyond an
+// empty buffer), so that the first item's first quad finds as many
+// operations after its copies as every later item does (an epilogue's).
 __device__ __forceinline__ void fp4p_prologue(const Fp4PSrc& b, const Fp4PLane& o, LDS uint8_t* base,
-                                              const Fp4PDesc& d0, int wave) {
+                                              const Fp4PDesc& d0, uint16_t* Y, int wave) {
   using C = Fp4P::C;
   fp4p_copy_r(b, base, d0.g0, 0, wave);
   const Fp4PQuad q{d0.m0, d0.g0, d0.ks0, 0};
@@ -1496,31 +1534,56 @@ __device__ __forceinline__ void fp4p_prologue(const Fp4PSrc& b, const Fp4PLane& 
   for (int k = 0; k < Fp4P::copies(2); ++k) fp4p_copy<2>(b, q, o, base, base + 2 * C::STAGE, wave, k);
 #pragma unroll
   for (int k = 0; k < Fp4P::copies(3); ++k) fp4p_copy<3>(b, q, o, base, base + 3 * C::STAGE, wave, k);
-  // stage 0 (and scale block 0) landed: 3 K-steps of copies issued after it
-  __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(Fp4P::copies(1) + Fp4P::copies(2) + Fp4P::copies(3)));
+  const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(Y, 0, 0, 0x00020000);
+  // (16-byte stores 32 bytes apart: nothing for the compiler to merge)
+#pragma unroll
+  for (int k = 0; k < Fp4P::EPI_STORES; ++k)
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, none, 32 * k, 0, 0);
+  // stage 0 (and scale block 0) landed: 3 K-steps of copies and the stores
+  // issued after it
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(Fp4P::copies(1) + Fp4P::copies(2) + Fp4P::copies(3) +
+                                               Fp4P::EPI_STORES));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
+// The quad of an item starting at item position u (stream K-step p + u):
+// its copies are of the next quad, in this item or (the item's last quad)
+// the first of item d1.
+__device__ __forceinline__ Fp4PQuad fp4p_quad(const Fp4PDesc& d0, const Fp4PDesc& d1, int64_t p, int u) {
+  const bool nx = u + 4 >= d0.len;
+  Fp4PQuad q;
+  q.m0 = nx ? d1.m0 : d0.m0;
+  q.g0 = nx ? d1.g0 : d0.g0;
+  q.ks = nx ? d1.ks0 : d0.ks0 + u + 4;
+  q.sbuf = int(((p + u) >> 2) + 1) & 1;
+  return q;
+}
+
 // The K-steps of item d0 (stream K-steps p..p + d0.len - 1, p a multiple
-// of 4), one quad per iteration; each quad copies the next one, in this
-// item or (in its last iteration) the first of item d1.
+// of 4), one quad at a time.  The first quad's waits for stages copied
+// before the previous epilogue also leave that epilogue's stores and the r
+// copy (ITEM_OPS) in flight.
 __device__ __forceinline__ void fp4p_item(v16f (&acc)[4][4], Fp4Frags<4, 4>& fa, Fp4Frags<4, 4>& fb,
                                           LDS uint8_t* base, const Fp4PSrc& b, const Fp4PLane& o,
                                           const Fp4PDesc& d0, const Fp4PDesc& d1, int64_t p, int wave,
                                           int wn, int wm, int lane) {
-  for (int u = 0; u < d0.len; u += 4) {
-    const bool nx = u + 4 >= d0.len;
-    Fp4PQuad q;
-    q.m0 = nx ? d1.m0 : d0.m0;
-    q.g0 = nx ? d1.g0 : d0.g0;
-    q.ks = nx ? d1.ks0 : d0.ks0 + u + 4;
+  constexpr int X = Fp4P::ITEM_OPS;
+  {
+    const Fp4PQuad q = fp4p_quad(d0, d1, p, 0);
+    const int p4 = int(p >> 2);
+    fp4p_step<0, X>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<1, X>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<2, X>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<3, 0>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+  }
+  for (int u = 4; u < d0.len; u += 4) {
+    const Fp4PQuad q = fp4p_quad(d0, d1, p, u);
     const int p4 = int((p + u) >> 2);
-    q.sbuf = (p4 + 1) & 1;
-    fp4p_step<0>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<1>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<2>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<3>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<0, 0>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<1, 0>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<2, 0>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<3, 0>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
   }
 }
 
@@ -1556,7 +1619,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
   const int wn = wave % C::WN, wm = wave / C::WN;
   const Fp4PLane o = fp4p_lane(b, wave, lane);
 
-  fp4p_prologue(b, o, base, fp4p_desc(S, 0), wave);
+  fp4p_prologue(b, o, base, fp4p_desc(S, 0), Y, wave);
 
   int64_t p = 0;  // stream K-step whose MFMAs run next
   for (int k = 0; k < S.n_items; ++k) {
@@ -1582,7 +1645,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
     p += d0.len;
 
     const int64_t n0 = int64_t(d0.g0) * 32;
-    fp4p_epilogue(acc, base, k & 1, Y, M, N, d0.m0, n0, wave, wn, wm);
+    fp4p_epilogue(acc, base, k & 1, Y, M, N, d0.m0, n0, wn, wm);
   }
   // every copy (the last ones repeat valid sources) lands before the end
   __builtin_amdgcn_s_waitcnt(0);
