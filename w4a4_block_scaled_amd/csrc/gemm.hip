@@ -1761,6 +1761,106 @@ hipError_t launch_fp4_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
   return hipGetLastError();
 }
 
+// MXFP4 weight streaming for M <= 16: one workgroup per 16 output features
+// (one half of a 32-row weight group), on the 16x16x128 scaled MFMA with the
+// activation rows as its 16 columns (columns >= M are zero).  Twice as many
+// workgroups as with 32-feature groups, so every CU streams even when N is
+// only 4096.  Workgroup b takes slice (b % 8) S + b / 8 (S slices per XCD):
+// consecutive slices, which share 1 KiB weight tiles and scale words, run on
+// one XCD at about the same time.  The WAVES waves split the 128-wide
+// K-steps into contiguous ranges; each wave issues the loads of up to U
+// K-steps at once, then their MFMAs.  Weight fragment lane l holds row
+// l % 16 and 32-wide K chunk l / 16 of a K-step: the tile of 64-K half
+// (l / 16) / 2 and, in it, tile lane 32 ((l / 16) % 2) + 16 h + l % 16 for
+// slice half h, so each 16-lane group reads 256 contiguous bytes; the weight
+// stream is read once, with non-temporal loads.  Activation codes are loaded
+// with lane l taking row l / 4, 16-byte chunk l % 4 (a row's 64 bytes per
+// lane quad), then moved to the fragment lane (chunk l / 16 of row l % 16)
+// with a lane permutation.  Partial sums of the waves are added through LDS
+// and wave 0 runs the epilogue.
+template <int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode16_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  const BlobLayout L = blob_layout(MXFP4, N, K);
+  const int64_t F = N / 16, per_x = (F + 7) / 8;
+  const int64_t f = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8, g = f >> 1;
+  if (f >= F) return;
+  const int hf = int(f & 1);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, c = lane >> 4;
+  const int tl = 32 * (c & 1) + 16 * hf + r;
+  const int64_t KT = L.KT, KS = L.KS, K2 = K / 2, KB = K / 32;
+  const u32x4* __restrict__ W = reinterpret_cast<const u32x4*>(blob + L.code_off) + (g * KT + (c >> 1)) * 64 + tl;
+  const uint32_t* __restrict__ S =
+      reinterpret_cast<const uint32_t*>(blob + L.scale_off) + ((g >> 2) * KT + (c >> 1)) * 64 + tl;
+  const int sw_shift = 8 * int(g & 3);
+  const bool mvalid = r < M;
+  // activation loads: lane l takes row l / 4, chunk l % 4; fragment lane l
+  // then reads it from lane 4 (l % 16) + l / 16
+  const int lr = lane >> 2;
+  const bool lvalid = lr < M;
+  const uint8_t* __restrict__ arow = a_codes + (lvalid ? lr : 0) * K2 + 16 * (lane & 3);
+  const int perm = 4 * (4 * r + c);
+  const uint8_t* __restrict__ srow = a_scales + (mvalid ? r : 0) * KB + c;
+  const int64_t per = (KS + WAVES - 1) / WAVES;
+  const int64_t s_begin = wave * per;
+  const int64_t s_end = s_begin + per < KS ? s_begin + per : KS;
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t s0 = s_begin; s0 < s_end; s0 += U) {
+    u32x4 wf[U], af[U];
+    uint32_t swd[U];
+    int sab[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t s = s0 + u;
+      const bool ok = s < s_end;
+      const int64_t sc = ok ? s : s_end - 1;  // clamped: loads stay in range
+      wf[u] = __builtin_nontemporal_load(&W[sc * 128]);
+      swd[u] = __builtin_nontemporal_load(&S[sc * 128]);
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (lvalid) a = *reinterpret_cast<const u32x4*>(arow + sc * 64);
+      af[u] = ok ? a : u32x4{0u, 0u, 0u, 0u};
+      sab[u] = mvalid ? int(srow[sc * 4]) : 127;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      u32x4 a;
+      a.x = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].x)));
+      a.y = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].y)));
+      a.z = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].z)));
+      a.w = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].w)));
+      acc = mfma_fp4_op<0>(wf[u], a, acc, int(swd[u] >> sw_shift), sab[u]);
+    }
+  }
+
+  __shared__ v4f red[WAVES > 1 ? WAVES - 1 : 1][64];
+  if (wave != 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < WAVES - 1; ++w) {
+    const v4f o = red[w][lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += o[e];
+  }
+  // lane l: activation row l % 16, features 4 (l / 16) + 0..3 of the slice
+  if (!mvalid) return;
+  const int64_t n = f * 16 + 4 * c;
+  const float4 rv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(blob + L.r_off) + n);
+  store4(Y, N, r, n, acc, v4f{rv.x, rv.y, rv.z, rv.w});
+}
+
+template <int WAVES>
+hipError_t launch_fp4_decode16(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                               const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_fp4_decode16_kernel<WAVES, 8>), dim3(unsigned((N / 16 + 7) / 8 * 8)), dim3(64 * WAVES), 0,
+                     stream,
+                     ac, as, blob, Y, M, N, K);
+  return hipGetLastError();
+}
+
 // ====================================================== decode kernel ==
 //
 // M <= 16 (MX formats): weight streaming.  One workgroup per 16 output
@@ -1863,6 +1963,13 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
     // fragments that would not fit the register budget of a 128 x 64 tile.
     return launch_tile<FMT, 256, 128, 4, 2, 5>(M, N, K, ac, as, t_act, blob, Y, stream);
   } else if constexpr (FMT == MXFP4) {
+    if (M <= 16) {
+      // 16-feature workgroups; waves enough for at most 8 K-steps each
+      const int64_t ks = K / 128;
+      if (ks <= 32) return launch_fp4_decode16<4>(M, N, K, ac, as, blob, Y, stream);
+      if (ks <= 64) return launch_fp4_decode16<8>(M, N, K, ac, as, blob, Y, stream);
+      return launch_fp4_decode16<16>(M, N, K, ac, as, blob, Y, stream);
+    }
     if (M <= 32) {
       // large grids: 4 waves streaming 8 tiles each per batch; small grids
       // (fewer groups than about two per CU): 8 waves of 4
