@@ -56,7 +56,7 @@ def oracle_layer(case, rows=None, cols=None):
 
 
 SMALL = [(1, 16, 128), (5, 272, 640), (16, 512, 1152), (17, 144, 384), (129, 272, 640),
-         (300, 400, 1152), (64, 1024, 4096)]
+         (300, 400, 1152), (64, 1024, 4096), (3, 528, 6144)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
