@@ -128,8 +128,12 @@ w4a4_status w4a4_quantize_act(w4a4_format fmt, int64_t M, int64_t K,
  *
  * Blob contents (opaque to callers apart from this description): a 256-byte
  * header (magic "W4A4PK01", format, N, K, t_w), then the codes in MFMA
- * fragment order (16 output rows x 128 K per 1 KiB tile), the block scales
- * regrouped per lane and K-step, and r.  Requires N % 16 == 0, K % 128 == 0.
+ * fragment order (1 KiB tiles, lane l holding 16 bytes of one row: 32 output
+ * rows x 64 K for MXFP4, 16 rows x 128 K for NVFP4 and MXINT4), the block
+ * scales regrouped per K tile and lane (one dword carries the scale bytes of
+ * 4 row groups for the MX formats, of 2 groups x 2 blocks for NVFP4), and r.
+ * Rows past N up to the last full row group are zero.  Requires
+ * N % 16 == 0, K % 128 == 0.
  */
 w4a4_status w4a4_pack_weight(w4a4_format fmt, int64_t N, int64_t K,
                              const void* codes, const void* scales,

@@ -1796,8 +1796,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode16_kernel(
       reinterpret_cast<const uint32_t*>(blob + L.scale_off) + ((g >> 2) * KT + (c >> 1)) * 64 + tl;
   const int sw_shift = 8 * int(g & 3);
   const bool mvalid = r < M;
-  // activation loads: lane l takes row l / 4, chunk l % 4; fragment lane l
-  // then reads it from lane 4 (l % 16) + l / 16
+  // activation loads: lane l takes row l / 4, chunk l % 4 (only the lanes of
+  // rows < M load); fragment lane l then reads it from lane 4 (l % 16) + l / 16
   const int lr = lane >> 2;
   const bool lvalid = lr < M;
   const uint8_t* __restrict__ arow = a_codes + (lvalid ? lr : 0) * K2 + 16 * (lane & 3);
@@ -1863,18 +1863,18 @@ hipError_t launch_fp4_decode16(int64_t M, int64_t N, int64_t K, const uint8_t* a
 
 // ====================================================== decode kernel ==
 //
-// M <= 16 (MX formats): weight streaming.  One workgroup per 16 output
-// features; its waves split K into contiguous ranges and stream the weight
-// tiles straight from HBM into registers (one coalesced 16-byte load per
-// lane per K-step, no LDS).  The activation rows (<= 16) are the MFMA's second
+// M <= 16, MXINT4: weight streaming.  One workgroup per 16 output features
+// (one 16-row weight group); workgroup b takes group (b % 8) S + b / 8 (S
+// groups per XCD), so neighbouring groups, which share scale words, run on
+// one XCD at about the same time.  The WAVES waves split K into contiguous
+// ranges of 128-wide K-steps and each issues the loads of up to U K-steps at
+// once (the weight tiles straight from HBM into registers, one coalesced
+// 16-byte load per lane per K-step, non-temporal: the stream is read once),
+// then their MFMAs.  The activation rows (<= 16) are the MFMA's second
 // operand; rows >= M are zero.  Partial sums of the waves are added through
 // LDS and wave 0 runs the epilogue.
-
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeUnroll = 4;
-
-template <int FMT>
-__global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
+template <int FMT, int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
   const BlobLayout L = blob_layout(FMT, N, K);
@@ -1882,62 +1882,78 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode_kernel(
   const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
   const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
 
-  const int64_t ng = blockIdx.x;
+  const int64_t F = N / 16, per_x = (F + 7) / 8;
+  const int64_t ng = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8;
+  if (ng >= F) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane >> 4;
   const int64_t m = lane & 15;
   const bool mvalid = m < M;
   const int64_t row = mvalid ? m : 0;
   const int64_t KS = L.KS, K2 = K / 2, KB = K / 32;
-  const int64_t per = (KS + kDecodeWaves - 1) / kDecodeWaves;
+  const int64_t per = (KS + WAVES - 1) / WAVES;
   const int64_t k_begin = wave * per;
   const int64_t k_end = k_begin + per < KS ? k_begin + per : KS;
   const int sw_shift = 8 * int(ng & 3);
   const uint32_t* __restrict__ Wsg = Ws + (ng >> 2) * KS * 64 + lane;
+  const u32x4* __restrict__ Wg = Wc + ng * KS * 64 + lane;
+  // activations through buffer loads over the M rows only: lanes of rows
+  // >= M read zeros, without a branch or a memory request
+  static_assert(FMT == MXINT4, "activation fragment layout");
+  const __amdgpu_buffer_rsrc_t ar =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_codes), 0, int(M * K2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_scales), 0, int(M * KB), 0x00020000);
+  const int aoff = int(m) * int(K2) + 16 * (c >> 1) + 8 * (c & 1);
+  const int soff = int(m) * int(KB);
 
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t k0 = k_begin; k0 < k_end; k0 += kDecodeUnroll) {
-    u32x4 wf[kDecodeUnroll], af[kDecodeUnroll];
-    uint32_t swd[kDecodeUnroll];
-    int sab[kDecodeUnroll];
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += U) {
+    u32x4 wf[U], af[U];
+    uint32_t swd[U];
+    int sab[U];
 #pragma unroll
-    for (int u = 0; u < kDecodeUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int64_t ks = k0 + u;
       const bool ok = ks < k_end;
       const int64_t ksc = ok ? ks : k_end - 1;  // clamped: loads stay in range
-      const u32x4 w = Wc[(ng * KS + ksc) * 64 + lane];
-      const u32x4 a = load_act_frag<FMT>(a_codes + row * K2, ksc, c);
-      const bool oka = ok && mvalid;
+      const u32x4 w = __builtin_nontemporal_load(&Wg[ksc * 64]);
+      // the activation fragment (see load_act_frag) and scale dword
+      const int ao = aoff + int(ksc) * 64;
+      const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(ar, ao, 0, 0);
+      const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(ar, ao + 32, 0, 0);
+      const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(sr, soff + int(ksc) * 4, 0, 0);
       wf[u] = ok ? w : u32x4{0u, 0u, 0u, 0u};
-      af[u] = oka ? a : u32x4{0u, 0u, 0u, 0u};
-      swd[u] = Wsg[ksc * 64] >> sw_shift;
-      sab[u] = act_scale_mx(a_scales, row, KB, ksc, c);
+      af[u] = ok ? u32x4{lo.x, lo.y, hi.x, hi.y} : u32x4{0u, 0u, 0u, 0u};
+      swd[u] = __builtin_nontemporal_load(&Wsg[ksc * 64]) >> sw_shift;
+      sab[u] = int(sw >> (8 * c));
     }
 #pragma unroll
-    for (int u = 0; u < kDecodeUnroll; ++u) {
-      if constexpr (FMT == MXFP4)
-        acc = mfma_fp4_op<0>(wf[u], af[u], acc, int(swd[u]), sab[u]);
-      else
-        acc = mfma_fp8_op<0>(int4_frag_to_fp8(wf[u]), int4_frag_to_fp8(af[u]), acc, int(swd[u]),
-                             sab[u]);
-    }
+    for (int u = 0; u < U; ++u)
+      acc = mfma_fp8_op<0>(int4_frag_to_fp8(wf[u]), int4_frag_to_fp8(af[u]), acc, int(swd[u]), sab[u]);
   }
 
-  __shared__ v4f red[kDecodeWaves][64];
-  red[wave][lane] = acc;
+  __shared__ v4f red[WAVES > 1 ? WAVES - 1 : 1][64];
+  if (wave != 0) red[wave - 1][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 1; w < kDecodeWaves; ++w) {
+  for (int w = 0; w < WAVES - 1; ++w) {
     const v4f o = red[w][lane];
-    acc[0] += o[0];
-    acc[1] += o[1];
-    acc[2] += o[2];
-    acc[3] += o[3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += o[e];
   }
   const float f = epilogue_factor(FMT, nullptr, blob);
   const float4 r = *reinterpret_cast<const float4*>(R + ng * 16 + 4 * c);
   if (mvalid) store4(Y, N, m, ng * 16 + 4 * c, acc, v4f{r.x * f, r.y * f, r.z * f, r.w * f});
+}
+
+template <int FMT, int WAVES, int U>
+hipError_t launch_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                         const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_decode_kernel<FMT, WAVES, U>), dim3(unsigned((N / 16 + 7) / 8 * 8)), dim3(64 * WAVES), 0,
+                     stream, ac, as, blob, Y, M, N, K);
+  return hipGetLastError();
 }
 
 template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
@@ -1985,9 +2001,12 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
     return launch_fp4<256, 128, 5>(M, N, K, ac, as, blob, Y, stream);
   } else {
     if (M <= 16) {
-      hipLaunchKernelGGL(gemm_decode_kernel<FMT>, dim3(unsigned(N / 16)), dim3(64 * kDecodeWaves),
-                         0, stream, ac, as, blob, Y, M, N, K);
-      return hipGetLastError();
+      // waves enough for at most 7, 8 or 10 K-steps each
+      const int64_t ks = K / 128;
+      if (ks <= 28) return launch_decode<FMT, 4, 7>(M, N, K, ac, as, blob, Y, stream);
+      if (ks <= 32) return launch_decode<FMT, 4, 8>(M, N, K, ac, as, blob, Y, stream);
+      if (ks <= 64) return launch_decode<FMT, 8, 8>(M, N, K, ac, as, blob, Y, stream);
+      return launch_decode<FMT, 16, 10>(M, N, K, ac, as, blob, Y, stream);
     }
     // MXINT4: 8 waves (two per SIMD) of 64 x 64 on the 16x16x128 FP8 MFMA;
     // its fragments are widened to FP8 in registers, which leaves no room for
