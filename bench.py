@@ -259,8 +259,8 @@ def gemm_kernel_label(fmt, M):
     if fmt == "mxfp4":
         if M <= 32:
             return "gemm_fp4_decode_kernel"
-        return ("gemm_fp4_persistent_kernel (linears of 192+ tiles of 256x256) and "
-                "gemm_fp4_kernel (the others)")
+        return ("gemm_fp4_persistent_kernel (linears of 192+ tiles of 256x256), "
+                "gemm_fp4_splitk_kernel (64..128 tiles, K >= 8192) and gemm_fp4_kernel (the others)")
     if fmt == "mxint4":
         return "gemm_decode_kernel<mxint4>" if M <= 16 else "gemm_mx_kernel<mxint4>"
     return "gemm_tile_kernel<nvfp4>"

@@ -168,9 +168,14 @@ w4a4_status w4a4_unpack_weight(w4a4_format fmt, int64_t N, int64_t K,
  *   blob     device, a blob packed for the same fmt, N, K, 256-byte aligned.
  *   Y        device, out, bf16 [M x N], 16-byte aligned.
  *   workspace/ws_bytes: device scratch of at least
- *            w4a4_linear_workspace_bytes() bytes, 16-byte aligned (that
- *            size is 0 for every format and shape in this version, and
- *            NULL is accepted then).
+ *            w4a4_linear_workspace_bytes() bytes, 16-byte aligned.  The size
+ *            is 0 (and NULL accepted) except for MXFP4 shapes that split K
+ *            across two workgroups (M > 32, 64..128 tiles of 256 x 256,
+ *            K % 1024 == 0, K >= 8192): 4 KiB of synchronization words plus
+ *            256 KiB of fp32 partial sums per tile.  The first 4 KiB must be
+ *            zero before the first call that uses the buffer; every call
+ *            leaves them zero again.  Calls sharing a workspace must not run
+ *            concurrently (issue them in order on one stream).
  *
  * Requires M >= 0, N % 16 == 0, K % 128 == 0.  The blob's fmt, N and K are
  * trusted, not re-read from device memory.

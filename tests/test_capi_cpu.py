@@ -58,12 +58,29 @@ def test_size_queries():
     assert L.w4a4_packed_weight_bytes(0, 128, 4000) == 0          # K % 128
 
 
+def split_k(M, N, K):
+    """The host-side condition of the MXFP4 split-K GEMM: 64..128 tiles of
+    256 x 256 and K a multiple of 1024, at least 8192."""
+    T = ((N + 255) // 256) * ((M + 255) // 256)
+    return M > 32 and K % 1024 == 0 and K >= 8192 and 64 <= T <= 128
+
+
 def test_linear_workspace_sizes():
-    """No GEMM path needs scratch memory: the workspace size is 0."""
+    """Only the MXFP4 split-K GEMM needs scratch: a fixed 4 KiB block of
+    tickets and flags (8 bytes per wave slot of up to 128 tiles), then per
+    tile 4 wave slots of 64 KiB of fp32 partial sums."""
     L = w4.lib()
+    shapes = ((2048, 28672, 4096), (2048, 4096, 14336), (2048, 4096, 4096), (16, 4096, 4096),
+              (2048, 6144, 4096), (300, 8208, 8192), (2048, 4096, 9216))
     for fmt in (0, 1, 2):
-        for M, N, K in ((2048, 28672, 4096), (2048, 4096, 14336), (16, 4096, 4096)):
-            assert L.w4a4_linear_workspace_bytes(fmt, M, N, K) == 0
+        for M, N, K in shapes:
+            got = L.w4a4_linear_workspace_bytes(fmt, M, N, K)
+            if fmt == 0 and split_k(M, N, K):
+                T = ((N + 255) // 256) * ((M + 255) // 256)
+                assert got == 4096 + T * 4 * 65536, (M, N, K)
+            else:
+                assert got == 0, (fmt, M, N, K)
+    assert split_k(2048, 4096, 14336) and not split_k(2048, 4096, 4096) and not split_k(2048, 6144, 14336)
 
 
 def test_table12_scale_bytes_from_the_library():

@@ -16,10 +16,12 @@ import w4a4_block_scaled_amd as w4
 
 pytestmark = pytest.mark.gpu
 
-# (format, M, N, K): the persistent MXFP4 GEMM, the tile GEMM, the decode
-# kernels, and the NVFP4 path (tensor amax pre-pass with its workspace)
+# (format, M, N, K): the persistent MXFP4 GEMM, the split-K GEMM (with its
+# workspace), the tile GEMM, the decode kernels, and the NVFP4 path (tensor
+# amax pre-pass with its workspace)
 CASES = [
     ("mxfp4", 512, 49152, 512),
+    ("mxfp4", 300, 8208, 8192),
     ("mxfp4", 300, 1024, 1024),
     ("mxfp4", 4, 4096, 4096),
     ("mxint4", 16, 2048, 1024),

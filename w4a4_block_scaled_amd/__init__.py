@@ -165,8 +165,9 @@ _LINEAR_WS = {}
 
 def linear_workspace(device, nbytes: int) -> torch.Tensor:
     """A cached, zero-filled linear workspace of `device`, at least `nbytes`
-    long (w4a4_linear_workspace_bytes is 0 in this version; the cache keeps
-    the binding ready for paths that need one)."""
+    long (needed by the MXFP4 split-K GEMM; its synchronization words start
+    at zero and every call leaves them at zero, so the one buffer serves all
+    calls issued in order on one stream)."""
     device = torch.device(device)
     ws = _LINEAR_WS.get(device)
     if ws is None or ws.numel() < nbytes:

@@ -1672,6 +1672,239 @@ hipError_t launch_fp4_persistent(int64_t M, int64_t N, int64_t K, const uint8_t*
   return hipGetLastError();
 }
 
+// ========================== MXFP4, K split in two across workgroups ==
+//
+// Shapes with too few 256 x 256 tiles to fill the chip (64..128 tiles) and a
+// long K (such as the 4096 x 14336 down projection at M = 2048) split each
+// tile's K-steps into two
+// halves, run by two workgroups with the persistent kernel's prologue, copy
+// ring and K loop (one item each; items are part-major, so each XCD works on
+// one K half of its tiles).  The halves meet per wave slot, the 128 x 128
+// block of wave (wm, wn) (64 KiB of fp32): of the two waves holding a slot,
+// the one that takes the slot's ticket first writes its partial sums
+// (agent-coherent write-through stores) and raises the slot's flag; the
+// second waits for the flag, adds those sums to its own and runs the
+// epilogue, then clears the ticket and the flag, so the synchronization
+// words are zero again after every call.  The second wave only waits for a
+// wave that is already past its K loop, so no wait depends on how the
+// workgroups are scheduled.
+
+// Workspace: the tickets and flags of up to MAX_TILES tiles at fixed places
+// (one 4 KiB block, whatever the shape, so that shapes sharing a workspace
+// never write partial sums over each other's synchronization words), then
+// the partial-sum slots.
+struct Fp4S {
+  static constexpr int SLOTS = 4;                   // wave slots per tile
+  static constexpr int MAX_TILES = 128;
+  static constexpr int SLOT_BYTES = 64 * 1024;      // 128 x 128 fp32
+  static constexpr int SYNC_BYTES = MAX_TILES * SLOTS * 8;
+  static constexpr int CACHE_THROUGH = 16;          // sc1: agent-coherent, past the L2s
+};
+static_assert(Fp4S::SYNC_BYTES == 4096, "sync block");
+
+// The partner's partial sums for the blocks in epilogue order e = 4 j + i:
+// quarter q of block e is 1 KiB at (4 e + q) KiB, lane l's 16 bytes at 16 l
+// (each store or load instruction moves one contiguous KiB; write-through
+// of partial lines was 4x slower), 8 blocks in flight.
+__device__ __forceinline__ v16f fp4s_load_block(__amdgpu_buffer_rsrc_t pr, int e, int lane) {
+  v16f v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(pr, ((e * 4 + q) * 64 + lane) * 16, 0,
+                                                          Fp4S::CACHE_THROUGH);
+    v[4 * q] = __uint_as_float(w.x);
+    v[4 * q + 1] = __uint_as_float(w.y);
+    v[4 * q + 2] = __uint_as_float(w.z);
+    v[4 * q + 3] = __uint_as_float(w.w);
+  }
+  return v;
+}
+
+// As fp4p_epilogue, with the partner's partial sums added to each block.
+__device__ __forceinline__ void fp4s_epilogue(const v16f (&acc)[4][4], __amdgpu_buffer_rsrc_t pr,
+                                              LDS uint8_t* base, int rbuf, uint16_t* __restrict__ Y,
+                                              int64_t M, int64_t N, int64_t m0, int64_t n0, int wn,
+                                              int wm) {
+  const int lane = fp4p_lane_id(), h = lane >> 5;
+  const LDS uint8_t* rb = base + Fp4P::R_OFF + rbuf * 1024;
+  const int64_t rows = M - m0 < Fp4P::BM ? M - m0 : Fp4P::BM;
+  const __amdgpu_buffer_rsrc_t ys =
+      __builtin_amdgcn_make_buffer_rsrc(Y + m0 * N, 0, int(rows * N * 2), 0x00020000);
+  v16f pb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pb[e] = fp4s_load_block(pr, e, lane);
+  v4f rs[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      rs[i][g] = *reinterpret_cast<const LDS v4f*>(rb + (wn * 128 + 32 * i + 8 * g + 4 * h) * 4);
+  const int N32 = int(N), row = wm * 128 + (lane & 15);
+  const int n32 = int(n0) + wn * 128 + 8 * (2 * ((lane >> 4) & 1) + h);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * j + i;
+      v16f av = acc[i][j];
+      asm volatile("" : "+a"(av));
+      av += pb[e & 7];
+      if (e + 8 < 16) pb[e & 7] = fp4s_load_block(pr, e + 8, lane);
+      u32x4 v[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const v4f a0 = {av[8 * p], av[8 * p + 1], av[8 * p + 2], av[8 * p + 3]};
+        const v4f a1 = {av[8 * p + 4], av[8 * p + 5], av[8 * p + 6], av[8 * p + 7]};
+        const u32x2 lo = scale_pack4(a0, rs[i][2 * p]), hi = scale_pack4(a1, rs[i][2 * p + 1]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(lo.x, hi.x, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(lo.y, hi.y, false, false);
+        v[p] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const auto t = __builtin_amdgcn_permlane16_swap(v[0][d], v[1][d], false, false);
+        v[0][d] = t[0];
+        v[1][d] = t[1];
+      }
+      const int n = n32 + 32 * i;
+      const int past = (N32 - 1 - n) >> 31;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int m = row + 32 * j + 16 * hh;
+        __builtin_amdgcn_raw_buffer_store_b128(v[hh], ys, ((m * N32 + n) * 2) | past, 0, 0);
+      }
+    }
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_fp4_splitk_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int tiles_m, int T, uint8_t* __restrict__ ws) {
+  using C = Fp4P::C;
+  constexpr int FN = C::FN, FM = C::FM, DEPTH = Fp4P::DEPTH;
+  const BlobLayout L = blob_layout(MXFP4, N, K);
+  // the 2T items (part-major) in the XCD chunks of Fp4PSched: one per workgroup
+  Fp4PSched S;
+  S.init(2 * T, tiles_m, int(L.KS), int(blockIdx.x));
+  if (S.n_items == 0) return;
+  const int item = S.tile(0), part = item / T, t = item % T;
+  const int half = int(L.KS / 2);
+  Fp4PDesc d0;
+  d0.m0 = (t % tiles_m) * Fp4P::BM;
+  d0.g0 = (t / tiles_m) * (Fp4P::BN / 32);
+  d0.ks0 = part * half;
+  d0.len = half;
+  Fp4PDesc d1 = d0;  // nothing follows: the ring copies this item's last quad again
+  d1.ks0 = d0.ks0 + half - 4;
+  d1.len = 4;
+
+  Fp4PSrc b;
+  b.ac = a_codes;
+  b.as = a_scales;
+  b.wc = blob + L.code_off;
+  b.ws = blob + L.scale_off;
+  b.r = blob + L.r_off;
+  b.K2 = int(K / 2);
+  b.KB = int(K / 32);
+  b.KT = int(L.KT);
+  b.ac_n = int(M * b.K2);
+  b.as_n = int(M * b.KB);
+  b.wc_n = int(L.NG * L.KT * 1024);
+  b.ws_n = int(L.NSG * L.KT * 256);
+  b.r_n = int(N * 4);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Fp4P::LDS_BYTES];
+  LDS uint8_t* base = (LDS uint8_t*)smem;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  const Fp4PLane o = fp4p_lane(b, wave, lane);
+
+  fp4p_prologue(b, o, base, d0, Y, wave);
+  v16f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  // as the persistent kernel's item start (its r copy goes to the unused
+  // buffer 1, keeping the first quad's wait counts)
+  __builtin_amdgcn_s_barrier();
+  fp4p_copy_r(b, base, d0.g0, 1, wave);
+  Fp4Frags<FN, FM> fa, fb;
+  fp4_read_all<Fp4P::BN, Fp4P::BM, DEPTH, Fp4P::NSB>(base, base, 0, wn, wm, fp4p_lane_id(), fa);
+  fp4p_item(acc, fa, fb, base, b, o, d0, d1, 0, wave, wn, wm, lane);
+
+  // the meeting of the two halves at this wave's slot
+  const int slot = t * Fp4S::SLOTS + wm * 2 + wn;
+  int* tickets = reinterpret_cast<int*>(ws);
+  int* flags = tickets + Fp4S::MAX_TILES * Fp4S::SLOTS;
+  uint8_t* pslot = ws + Fp4S::SYNC_BYTES + int64_t(slot) * Fp4S::SLOT_BYTES;
+  const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(pslot, 0, Fp4S::SLOT_BYTES, 0x00020000);
+  int first = 0;
+  if (lane == 0) first = __hip_atomic_fetch_add(&tickets[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
+  first = __builtin_amdgcn_readfirstlane(first);
+  if (first) {
+    const int l = fp4p_lane_id();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v16f av = acc[i][j];
+        asm volatile("" : "+a"(av));
+        const int e = 4 * j + i;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4{__float_as_uint(av[4 * q]), __float_as_uint(av[4 * q + 1]), __float_as_uint(av[4 * q + 2]),
+                    __float_as_uint(av[4 * q + 3])},
+              pr, ((e * 4 + q) * 64 + l) * 16, 0, Fp4S::CACHE_THROUGH);
+      }
+    // the sums have reached the coherent level before the flag is raised
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) __hip_atomic_store(&flags[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    // the other wave is past its K loop: it raises the flag after its stores
+    if (lane == 0) {
+      for (int n = 0; n < (1 << 20); ++n) {
+        if (__hip_atomic_load(&flags[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    fp4s_epilogue(acc, pr, base, 0, Y, M, N, d0.m0, int64_t(d0.g0) * 32, wn, wm);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) {
+      __hip_atomic_store(&flags[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&tickets[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Split-K conditions: 64..128 tiles of 256 x 256 (2T <= 256 workgroups),
+// each K half whole quads, offsets in 32 bits, and K >= 8192: the exchange
+// of the halves costs about as much as 16 K-steps (at K = 4096 the
+// 256 x 128 tile kernel is faster, at K = 14336 the split is 16% faster).
+bool fp4_splitk_fits(int64_t M, int64_t N, int64_t K) {
+  const int64_t T = ((N + 255) / 256) * ((M + 255) / 256);
+  return M > 32 && K % 1024 == 0 && K >= 8192 && T >= 64 && T <= Fp4S::MAX_TILES &&
+         int64_t(Fp4P::BM) * N * 2 < (int64_t(1) << 31) && M * (K / 2) < (int64_t(1) << 31) &&
+         ((N + 31) / 32) * 32 * (K / 2) < (int64_t(1) << 31);
+}
+
+size_t fp4_splitk_workspace(int64_t M, int64_t N) {
+  const int64_t T = ((N + 255) / 256) * ((M + 255) / 256);
+  return size_t(Fp4S::SYNC_BYTES + T * Fp4S::SLOTS * int64_t(Fp4S::SLOT_BYTES));
+}
+
+hipError_t launch_fp4_splitk(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                             const uint8_t* blob, uint16_t* Y, void* workspace, hipStream_t stream) {
+  const int tiles_m = int((M + 255) / 256);
+  const int T = int((N + 255) / 256) * tiles_m;
+  hipLaunchKernelGGL(gemm_fp4_splitk_kernel, dim3(Fp4P::XCDS * Fp4P::PER_XCD), dim3(256), 0, stream, ac, as,
+                     blob, Y, M, N, K, tiles_m, T, static_cast<uint8_t*>(workspace));
+  return hipGetLastError();
+}
+
 // MXFP4 weight streaming for M <= 32: one workgroup per 32 output features,
 // WAVES waves splitting its 64-K tiles into contiguous ranges.  Each wave
 // streams its tiles from HBM straight into registers in batches of U (U
@@ -1996,6 +2229,7 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
     // 256 x 256 tiles (4 waves of 128 x 128) unless that leaves more than
     // ~30% of the 256 CUs idle, then 256 (n) x 128 (m) tiles.
     if (fp4_persistent_fits(M, N, K)) return launch_fp4_persistent(M, N, K, ac, as, blob, Y, stream);
+    if (fp4_splitk_fits(M, N, K)) return launch_fp4_splitk(M, N, K, ac, as, blob, Y, workspace, stream);
     const int64_t big = ((N + 255) / 256) * ((M + 255) / 256);
     if (big >= 180) return launch_fp4<256, 256, 4>(M, N, K, ac, as, blob, Y, stream);
     return launch_fp4<256, 128, 5>(M, N, K, ac, as, blob, Y, stream);
@@ -2017,7 +2251,10 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
 
 }  // namespace
 
-size_t linear_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
+size_t linear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K) {
+  if (fmt == MXFP4 && fp4_splitk_fits(M, N, K)) return fp4_splitk_workspace(M, N);
+  return 0;
+}
 
 hipError_t launch_linear(int fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
                          const void* a_scales, const float* t_act, const void* blob, void* Y,
