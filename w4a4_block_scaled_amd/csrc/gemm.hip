@@ -41,6 +41,16 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 // Direct-to-LDS copies: 16 (4) bytes per lane from `src`, lane l writing
 // `dst` + 16 l (4 l); `dst` is wave-uniform.
+// Activation tiles (16 rows x the 64 bytes of one 128-wide K-step) are
+// copied with lane l taking row l / 4 and 16-byte chunk (l % 4) ^ fp4_swz(l
+// / 4): four consecutive lanes read the 64 contiguous bytes of one row (one
+// request per lane quad instead of four), and the LDS tile holds chunk c of
+// row r at 16-byte position a_tile_pos(r, c) = 4 r + (c ^ fp4_swz(r)).  The
+// swizzle keeps the fragment reads (16 consecutive rows, one chunk) free of
+// bank conflicts for 32 and for 64 LDS banks.
+__device__ __forceinline__ int fp4_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int a_tile_pos(int r, int c) { return 4 * r + (c ^ fp4_swz(r)); }
+
 __device__ __forceinline__ void lds_copy16(const void* src, LDS void* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
@@ -323,14 +333,13 @@ template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
 __device__ __forceinline__ void issue_stage(const TileArgs& t, int64_t ks, LDS uint8_t* dst,
                                             int wave, int lane) {
   using C = TileCfg<FMT, BN, BM, WN, WM, DEPTH>;
-  const int r = lane & 15, c = lane >> 4;
-  // activation fragments (FP4 fragment order for every format)
+  // activation tiles, rows in lane quads (a_tile_pos)
 #pragma unroll
   for (int i = 0; i < C::A_DMA; ++i) {
     const int f = wave * C::A_DMA + i;
-    int64_t row = t.m0 + 16 * f + r;
+    int64_t row = t.m0 + 16 * f + (lane >> 2);
     row = row < t.M ? row : t.M - 1;
-    __builtin_amdgcn_global_load_lds(t.a_codes + row * t.K2 + ks * 64 + 16 * c,
+    __builtin_amdgcn_global_load_lds(t.a_codes + row * t.K2 + ks * 64 + ((lane & 3) ^ fp4_swz(lane >> 2)) * 16,
                                      dst + f * 1024, 16, 0, 0);
   }
   // weight tiles
@@ -400,7 +409,7 @@ __device__ __forceinline__ void tile_step(const TileArgs& t, const LDS uint8_t* 
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int f = wm * FM + j;
-      const u32x4 af = A[f * 64 + lane];
+      const u32x4 af = A[f * 64 + a_tile_pos(r, c)];
       const int sa = AS[(16 * f + r) * 4 + c];
 #pragma unroll
       for (int i = 0; i < FN; ++i)
@@ -416,8 +425,8 @@ __device__ __forceinline__ void tile_step(const TileArgs& t, const LDS uint8_t* 
       // MXINT4 operand order from the FP4-ordered LDS copy: half (c & 1) of
       // blocks c >> 1 and 2 + (c >> 1) of row r
       const LDS u32x2* base = reinterpret_cast<const LDS u32x2*>(A + f * 64);
-      const u32x2 lo = base[(r + 16 * (c >> 1)) * 2 + (c & 1)];
-      const u32x2 hi = base[(r + 16 * (2 + (c >> 1))) * 2 + (c & 1)];
+      const u32x2 lo = base[a_tile_pos(r, c >> 1) * 2 + (c & 1)];
+      const u32x2 hi = base[a_tile_pos(r, 2 + (c >> 1)) * 2 + (c & 1)];
       const v8i a8 = int4_frag_to_fp8(u32x4{lo.x, lo.y, hi.x, hi.y});
       const int sa = AS[(16 * f + r) * 4 + c];
 #pragma unroll
@@ -430,7 +439,7 @@ __device__ __forceinline__ void tile_step(const TileArgs& t, const LDS uint8_t* 
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int f = wm * FM + j;
-      af[j] = A[f * 64 + lane];
+      af[j] = A[f * 64 + a_tile_pos(r, c)];
       sa[j] = *reinterpret_cast<const LDS uint16_t*>(AS + (16 * f + r) * 8 + 2 * c);
     }
 #pragma unroll
@@ -578,14 +587,14 @@ template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
 __device__ __forceinline__ void mx_issue(const TileArgs& t, int64_t ks, LDS uint8_t* dst, int wave,
                                          int lane) {
   using C = MxCfg<BN, BM, WN, WM, DEPTH>;
-  const int r = lane & 15, c = lane >> 4;
+  // activation tiles, rows in lane quads (a_tile_pos)
 #pragma unroll
   for (int i = 0; i < C::A_DMA; ++i) {
     const int f = wave * C::A_DMA + i;
-    int64_t row = t.m0 + 16 * f + r;
+    int64_t row = t.m0 + 16 * f + (lane >> 2);
     row = row < t.M ? row : t.M - 1;
-    __builtin_amdgcn_global_load_lds(t.a_codes + row * t.K2 + ks * 64 + 16 * c, dst + f * 1024,
-                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds(t.a_codes + row * t.K2 + ks * 64 + ((lane & 3) ^ fp4_swz(lane >> 2)) * 16,
+                                     dst + f * 1024, 16, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < C::W_DMA; ++i) {
@@ -637,11 +646,11 @@ __device__ __forceinline__ void mx_load_rest(const LDS uint8_t* __restrict__ st,
     if constexpr (FMT == MXINT4) {
       // half (c & 1) of blocks c >> 1 and 2 + (c >> 1) of row r
       const LDS u32x2* b = reinterpret_cast<const LDS u32x2*>(A + f * 64);
-      const u32x2 lo = b[(r + 16 * (c >> 1)) * 2 + (c & 1)];
-      const u32x2 hi = b[(r + 16 * (2 + (c >> 1))) * 2 + (c & 1)];
+      const u32x2 lo = b[a_tile_pos(r, c >> 1) * 2 + (c & 1)];
+      const u32x2 hi = b[a_tile_pos(r, 2 + (c >> 1)) * 2 + (c & 1)];
       fr.a[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
     } else {
-      fr.a[j] = A[f * 64 + lane];
+      fr.a[j] = A[f * 64 + a_tile_pos(r, c)];
     }
     const int R = 16 * f + r;
     fr.sa[j] = SC[(R / C::AS_DW) * 256 + (R % C::AS_DW) * 4 + c];
@@ -922,15 +931,6 @@ __device__ __forceinline__ void fp4_sync(int after) {
   asm volatile("" ::: "memory");
 }
 
-// Activation tiles (16 rows x the 64 bytes of one K-step) are copied with
-// lane l taking row l / 4 and 16-byte chunk (l % 4) ^ fp4_swz(l / 4): four
-// consecutive lanes read the 64 contiguous bytes of one row (one request per
-// lane quad instead of four), and the LDS tile holds chunk c of row r at
-// position 4 r + (c ^ fp4_swz(r)).  The swizzle keeps the fragment reads
-// (16 consecutive rows, one chunk) free of bank conflicts for 32 and for 64
-// LDS banks.
-__device__ __forceinline__ int fp4_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
-
 // Quarter q of activation scale block b (the scale dwords of K-steps
 // 4b..4b+3): lane l of wave w copies the dword of row w*ASR + 16q + l/4,
 // K-step 4b + l%4, so one copy touches 16 rows instead of 64.  Rows beyond
@@ -1028,10 +1028,8 @@ __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st
     const int q = r - C::FM - 2, j = q >> 1, hh = q & 1;
     // fragment lane l: row 32 g + l%32 (16-row tile 2 g + (l%32)/16, row
     // l%16 in it), 16-byte chunk 2 hh + l/32 of its K-step bytes (fp4_swz)
-    const int rr = lane & 15;
     fr.a[j][hh] = *reinterpret_cast<const LDS u32x4*>(
-        st + (2 * (wm * C::FM + j) + ((lane >> 4) & 1)) * 1024 +
-        (4 * rr + ((2 * hh + (lane >> 5)) ^ fp4_swz(rr))) * 16);
+        st + (2 * (wm * C::FM + j) + ((lane >> 4) & 1)) * 1024 + a_tile_pos(lane & 15, 2 * hh + (lane >> 5)) * 16);
   } else {
     const int q = r - 3 * C::FM - 2, i = q >> 1, hh = q & 1;
     fr.w[i][hh] = *reinterpret_cast<const LDS u32x4*>(st + C::A_BYTES + ((wn * C::FN + i) * 2 + hh) * 1024 +
