@@ -261,7 +261,7 @@ __device__ __forceinline__ void tile_epilogue(const v4f (&acc)[FN][FM], LDS uint
 
 // ======================================================== tiled kernel ==
 //
-// Workgroup tile BN (n) x BM (m), WN x WM waves (n x m), wave tile
+// NVFP4, all M.  Workgroup tile BN (n) x BM (m), WN x WM waves (n x m), wave tile
 // BN/WN x BM/WM.  Each 128-wide K-step is one pipeline stage.  A stage's
 // operands (activation fragments, weight tiles, activation scales, weight
 // scale words) are copied global -> LDS by the waves' direct-to-LDS loads
@@ -273,7 +273,8 @@ __device__ __forceinline__ void tile_epilogue(const v4f (&acc)[FN][FM], LDS uint
 // the workgroup and also frees the buffer computed in the previous step.
 //
 // LDS stage buffer layout:
-//   [A codes: BM/16 fragments x 64 lanes x 16 B, FP4 fragment order]
+//   [A codes: BM/16 tiles of 16 rows x 64 B; chunk c of row r at 16-byte
+//    position a_tile_pos(r, c)]
 //   [W codes: BN/16 tiles x 1 KiB, copied from the blob as is]
 //   [A scales: BM rows x (4 B MX | 8 B NVFP4): this K-step's scale bytes]
 //   [W scale words: groups x 64 lanes x 4 B]
@@ -405,35 +406,8 @@ __device__ __forceinline__ void tile_step(const TileArgs& t, const LDS uint8_t* 
 #pragma unroll
   for (int q = 0; q < FN / C::GPW; ++q) sw[q] = WS[(wn * FN / C::GPW + q) * 64 + lane];
 
-  if constexpr (FMT == MXFP4) {
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int f = wm * FM + j;
-      const u32x4 af = A[f * 64 + a_tile_pos(r, c)];
-      const int sa = AS[(16 * f + r) * 4 + c];
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-        acc[i][j] = mfma_fp4(i % 4, wf[i], af, acc[i][j], int(sw[i / 4]), sa);
-    }
-  } else if constexpr (FMT == MXINT4) {
-    v8i w8[FN];
-#pragma unroll
-    for (int i = 0; i < FN; ++i) w8[i] = int4_frag_to_fp8(wf[i]);
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int f = wm * FM + j;
-      // MXINT4 operand order from the FP4-ordered LDS copy: half (c & 1) of
-      // blocks c >> 1 and 2 + (c >> 1) of row r
-      const LDS u32x2* base = reinterpret_cast<const LDS u32x2*>(A + f * 64);
-      const u32x2 lo = base[a_tile_pos(r, c >> 1) * 2 + (c & 1)];
-      const u32x2 hi = base[a_tile_pos(r, 2 + (c >> 1)) * 2 + (c & 1)];
-      const v8i a8 = int4_frag_to_fp8(u32x4{lo.x, lo.y, hi.x, hi.y});
-      const int sa = AS[(16 * f + r) * 4 + c];
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-        acc[i][j] = mfma_fp8(i % 4, w8[i], a8, acc[i][j], int(sw[i / 4]), sa);
-    }
-  } else {  // NVFP4: fp16 MFMA, four per K-step
+  static_assert(FMT == NVFP4, "the tiled kernel serves NVFP4");
+  {  // fp16 MFMA, four per K-step
     u32x4 af[FM];
     uint32_t sa[FM];
 #pragma unroll
@@ -521,7 +495,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_tile_kernel(
 
 // ===================================================== MX tiled kernel ==
 //
-// MXFP4 / MXINT4 for M > 16.  Workgroup tile BN (n) x BM (m) with WN x WM
+// MXINT4 for M > 16.  Workgroup tile BN (n) x BM (m) with WN x WM
 // waves, one 128-wide K-step per stage of a DEPTH-deep LDS ring filled by
 // direct-to-LDS copies, as above, but software-pipelined inside each wave:
 // while the MFMAs of K-step s run from registers, the wave already reads the
@@ -643,15 +617,11 @@ __device__ __forceinline__ void mx_load_rest(const LDS uint8_t* __restrict__ st,
 #pragma unroll
   for (int j = 0; j < C::FM; ++j) {
     const int f = wm * C::FM + j;
-    if constexpr (FMT == MXINT4) {
-      // half (c & 1) of blocks c >> 1 and 2 + (c >> 1) of row r
-      const LDS u32x2* b = reinterpret_cast<const LDS u32x2*>(A + f * 64);
-      const u32x2 lo = b[a_tile_pos(r, c >> 1) * 2 + (c & 1)];
-      const u32x2 hi = b[a_tile_pos(r, 2 + (c >> 1)) * 2 + (c & 1)];
-      fr.a[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
-    } else {
-      fr.a[j] = A[f * 64 + a_tile_pos(r, c)];
-    }
+    // MXINT4 operand order: half (c & 1) of blocks c >> 1 and 2 + (c >> 1) of row r
+    const LDS u32x2* b = reinterpret_cast<const LDS u32x2*>(A + f * 64);
+    const u32x2 lo = b[a_tile_pos(r, c >> 1) * 2 + (c & 1)];
+    const u32x2 hi = b[a_tile_pos(r, 2 + (c >> 1)) * 2 + (c & 1)];
+    fr.a[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
     const int R = 16 * f + r;
     fr.sa[j] = SC[(R / C::AS_DW) * 256 + (R % C::AS_DW) * 4 + c];
   }
@@ -666,17 +636,11 @@ __device__ __forceinline__ void mx_load_rest(const LDS uint8_t* __restrict__ st,
 template <int FMT, int FN, int FM>
 __device__ __forceinline__ void mx_mfma_row(v4f (&acc)[FN][FM], int i, const u32x4& wf,
                                             const MxFrags<FMT, FN, FM>& fr,
-                                            const v8i (&a8)[FMT == MXINT4 ? FM : 1]) {
-  if constexpr (FMT == MXFP4) {
+                                            const v8i (&a8)[FM]) {
+  const v8i w8 = int4_frag_to_fp8(wf);
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
-      acc[i][j] = mfma_fp4(i % 4, wf, fr.a[j], acc[i][j], int(fr.sw[i / 4]), fr.sa[j]);
-  } else {
-    const v8i w8 = int4_frag_to_fp8(wf);
-#pragma unroll
-    for (int j = 0; j < FM; ++j)
-      acc[i][j] = mfma_fp8(i % 4, w8, a8[j], acc[i][j], int(fr.sw[i / 4]), fr.sa[j]);
-  }
+  for (int j = 0; j < FM; ++j)
+    acc[i][j] = mfma_fp8(i % 4, w8, a8[j], acc[i][j], int(fr.sw[i / 4]), fr.sa[j]);
 }
 
 // MFMAs of the K-step held in registers, while the fragments of the next
@@ -687,11 +651,10 @@ __device__ __forceinline__ void mx_step(const LDS uint8_t* __restrict__ nx, int 
                                         u32x4 (&wf)[BN / 16 / WN],
                                         MxFrags<FMT, BN / 16 / WN, BM / 16 / WM>& fr) {
   constexpr int FN = BN / 16 / WN, FM = BM / 16 / WM;
-  v8i a8[FMT == MXINT4 ? FM : 1];
-  if constexpr (FMT == MXINT4) {
+  static_assert(FMT == MXINT4, "the MX tiled kernel serves MXINT4");
+  v8i a8[FM];
 #pragma unroll
-    for (int j = 0; j < FM; ++j) a8[j] = int4_frag_to_fp8(fr.a[j]);
-  }
+  for (int j = 0; j < FM; ++j) a8[j] = int4_frag_to_fp8(fr.a[j]);
   MxFrags<FMT, FN, FM> fn;
   mx_load_rest<FMT, BN, BM, WN, WM, DEPTH>(nx, wn, wm, lane, fn);
   // the last weight fragment is double-buffered so that no LDS read has to
@@ -2120,7 +2083,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(
   const int c = lane >> 4;
   const int64_t m = lane & 15;
   const bool mvalid = m < M;
-  const int64_t row = mvalid ? m : 0;
   const int64_t KS = L.KS, K2 = K / 2, KB = K / 32;
   const int64_t per = (KS + WAVES - 1) / WAVES;
   const int64_t k_begin = wave * per;
