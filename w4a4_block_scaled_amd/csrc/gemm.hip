@@ -2090,15 +2090,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(
   const int sw_shift = 8 * int(ng & 3);
   const uint32_t* __restrict__ Wsg = Ws + (ng >> 2) * KS * 64 + lane;
   const u32x4* __restrict__ Wg = Wc + ng * KS * 64 + lane;
-  // activations through buffer loads over the M rows only: lanes of rows
-  // >= M read zeros, without a branch or a memory request
+  // activation codes: lane l loads row l / 4, 16-byte chunk l % 4 of the
+  // K-step; fragment lane l (row m = l % 16, group c = l / 16) takes half
+  // c % 2 of chunks c / 2 and 2 + c / 2 of row m (see load_act_frag) from
+  // lanes 4 m + c / 2 and 4 m + 2 + c / 2.  Lanes of rows >= M read zeros:
+  // for batches of up to 8 K-steps only the lanes of rows < M load (exec
+  // mask); for longer batches a branch around the loads makes the compiler
+  // drain the batch at its join, so there buffer loads bounded to the M rows
+  // return zeros without a branch.
   static_assert(FMT == MXINT4, "activation fragment layout");
+  constexpr bool MASKED = U <= 8;
+  const int lr = lane >> 2;
+  const bool lvalid = lr < M;
+  const uint8_t* __restrict__ arow = a_codes + (lvalid ? lr : 0) * K2 + 16 * (lane & 3);
+  const uint8_t* __restrict__ srow = a_scales + (mvalid ? m : 0) * KB + c;
   const __amdgpu_buffer_rsrc_t ar =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_codes), 0, int(M * K2), 0x00020000);
   const __amdgpu_buffer_rsrc_t sr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_scales), 0, int(M * KB), 0x00020000);
-  const int aoff = int(m) * int(K2) + 16 * (c >> 1) + 8 * (c & 1);
-  const int soff = int(m) * int(KB);
+  const int aoff = (lane >> 2) * int(K2) + 16 * (lane & 3);
+  const int soff = int(m) * int(KB) + c;
+  const int src_lo = 4 * (4 * int(m) + (c >> 1)), src_hi = src_lo + 8;
+  const bool odd = c & 1;
 
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   for (int64_t k0 = k_begin; k0 < k_end; k0 += U) {
@@ -2111,19 +2124,32 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(
       const bool ok = ks < k_end;
       const int64_t ksc = ok ? ks : k_end - 1;  // clamped: loads stay in range
       const u32x4 w = __builtin_nontemporal_load(&Wg[ksc * 64]);
-      // the activation fragment (see load_act_frag) and scale dword
-      const int ao = aoff + int(ksc) * 64;
-      const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(ar, ao, 0, 0);
-      const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(ar, ao + 32, 0, 0);
-      const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(sr, soff + int(ksc) * 4, 0, 0);
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if constexpr (MASKED) {
+        if (lvalid) a = *reinterpret_cast<const u32x4*>(arow + ksc * 64);
+        sab[u] = mvalid ? int(srow[ksc * 4]) : 127;
+      } else {
+        a = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff + int(ksc) * 64, 0, 0);
+        sab[u] = int(__builtin_amdgcn_raw_buffer_load_b8(sr, soff + int(ksc) * 4, 0, 0));
+      }
       wf[u] = ok ? w : u32x4{0u, 0u, 0u, 0u};
-      af[u] = ok ? u32x4{lo.x, lo.y, hi.x, hi.y} : u32x4{0u, 0u, 0u, 0u};
+      af[u] = ok ? a : u32x4{0u, 0u, 0u, 0u};
       swd[u] = __builtin_nontemporal_load(&Wsg[ksc * 64]) >> sw_shift;
-      sab[u] = int(sw >> (8 * c));
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      acc = mfma_fp8_op<0>(int4_frag_to_fp8(wf[u]), int4_frag_to_fp8(af[u]), acc, int(swd[u]), sab[u]);
+    for (int u = 0; u < U; ++u) {
+      // the halves of the two chunks this fragment lane takes
+      const uint32_t l0 = uint32_t(__builtin_amdgcn_ds_bpermute(src_lo, int(af[u].x)));
+      const uint32_t l1 = uint32_t(__builtin_amdgcn_ds_bpermute(src_lo, int(af[u].y)));
+      const uint32_t l2 = uint32_t(__builtin_amdgcn_ds_bpermute(src_lo, int(af[u].z)));
+      const uint32_t l3 = uint32_t(__builtin_amdgcn_ds_bpermute(src_lo, int(af[u].w)));
+      const uint32_t h0 = uint32_t(__builtin_amdgcn_ds_bpermute(src_hi, int(af[u].x)));
+      const uint32_t h1 = uint32_t(__builtin_amdgcn_ds_bpermute(src_hi, int(af[u].y)));
+      const uint32_t h2 = uint32_t(__builtin_amdgcn_ds_bpermute(src_hi, int(af[u].z)));
+      const uint32_t h3 = uint32_t(__builtin_amdgcn_ds_bpermute(src_hi, int(af[u].w)));
+      const u32x4 a = odd ? u32x4{l2, l3, h2, h3} : u32x4{l0, l1, h0, h1};
+      acc = mfma_fp8_op<0>(int4_frag_to_fp8(wf[u]), int4_frag_to_fp8(a), acc, int(swd[u]), sab[u]);
+    }
   }
 
   __shared__ v4f red[WAVES > 1 ? WAVES - 1 : 1][64];
