@@ -15,9 +15,10 @@ durations.
 Printed: one JSON line with the workload's throughput (TFLOP/s, whole step),
 the GEMM kernel's roofline position (algorithmic flops per launch over its
 HIP-event-timed average duration, against the MI355X dense MXFP4 peak),
-decode weight-streaming bandwidth (M = 1, 4, 16, cycling 32 layer copies so
-that the 256 MB last-level cache cannot hold the weights), and the CPU
-oracle timed on a bounded sample of the same workload.
+decode weight-streaming bandwidth (MXFP4 Llama linears at M = 1, 4, 16 and
+MXINT4 Qwen linears at M = 1, cycling 32 layer copies so that the 256 MB
+last-level cache cannot hold the weights), and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -172,30 +173,33 @@ def time_graph(layers, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def decode_bandwidth(dev, steps, copies=32):
-    """Weight-streaming rate of the GEMM at M = 1, 4, 16 (MXFP4 Llama shapes).
+def decode_bandwidth(dev, steps, workload="llama_decode", Ms=(1, 4, 16), copies=32):
+    """Weight-streaming rate of the GEMM at small M (default: MXFP4 Llama
+    shapes at M = 1, 4, 16).
 
     Each step runs the four linears of one "layer"; 32 distinct copies of the
-    packed weights (3.7 GB, like the 32 layers of the model) are cycled so
-    that no copy is still cached.  The 32 layers are captured as one HIP
-    graph and replayed, so the figure is the GPU's, not the host's launch
-    rate.
+    packed weights (3.7 GB for Llama, like the 32 layers of the model) are
+    cycled so that no copy is still cached.  The 32 layers are captured as
+    one HIP graph and replayed, so the figure is the GPU's, not the host's
+    launch rate.
     """
     out = {}
-    base = [Layer(c, dev) for c in inputs.workload_cases("llama_decode", M=16)]
+    fmt = inputs.WORKLOADS[workload][1]
+    base = [Layer(c, dev) for c in inputs.workload_cases(workload, M=max(Ms))]
     blobs = [[L.blob.clone() for L in base] for _ in range(copies)]
-    for M in (1, 4, 16):
-        cases = inputs.workload_cases("llama_decode", M=M, build_weights=False)
+    for M in Ms:
+        cases = inputs.workload_cases(workload, M=M, build_weights=False)
         act = [(c.x.to(dev), torch.from_numpy(c.c).to(dev)) for c in cases]
         # quantized activations for this M
-        q = [w4.quantize_act(x, c, "mxfp4") for x, c in act]
+        q = [w4.quantize_act(x, c, fmt) for x, c in act]
         ys = [torch.empty((M, L.N), dtype=torch.bfloat16, device=dev) for L in base]
-        nbytes = sum(L.N * L.K / 2 + L.N * L.K / 32 + 4 * L.N + M * L.K / 2 + M * L.K / 32 +
+        G = w4.block_size(fmt)
+        nbytes = sum(L.N * L.K / 2 + L.N * L.K / G + 4 * L.N + M * L.K / 2 + M * L.K / G +
                      2 * M * L.N for L in base)
 
         def run_layer(k):
             for j, L in enumerate(base):
-                w4.linear(q[j][0], q[j][1], q[j][2], blobs[k % copies][j], "mxfp4", L.N, L.K, out=ys[j])
+                w4.linear(q[j][0], q[j][1], q[j][2], blobs[k % copies][j], fmt, L.N, L.K, out=ys[j])
 
         def run_model():
             for k in range(copies):
@@ -360,6 +364,8 @@ def main():
     if not a.no_decode:
         log("[bench] decode bandwidth")
         out["decode_hbm"] = decode_bandwidth(dev, a.steps)
+        torch.cuda.empty_cache()
+        out["decode_hbm_qwen_mxint4"] = decode_bandwidth(dev, a.steps, "qwen_mxint4", (1,))
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(a.workload, M)
