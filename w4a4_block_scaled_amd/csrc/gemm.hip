@@ -2221,8 +2221,11 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
     return launch_fp4<256, 128, 5>(M, N, K, ac, as, blob, Y, stream);
   } else {
     if (M <= 16) {
-      // waves enough for at most 7, 8 or 10 K-steps each
-      const int64_t ks = K / 128;
+      // waves enough for at most 7, 8 or 10 K-steps each; with K <= 4096,
+      // more waves (shorter per-wave chains) when there are few groups
+      const int64_t ks = K / 128, groups = N / 16;
+      if (ks <= 32 && groups < 256) return launch_decode<FMT, 16, 2>(M, N, K, ac, as, blob, Y, stream);
+      if (ks <= 32 && groups < 1024) return launch_decode<FMT, 8, 4>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 28) return launch_decode<FMT, 4, 7>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 32) return launch_decode<FMT, 4, 8>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 64) return launch_decode<FMT, 8, 8>(M, N, K, ac, as, blob, Y, stream);
