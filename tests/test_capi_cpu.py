@@ -138,6 +138,21 @@ def test_linear_rejects(args, status):
     assert w4.lib().w4a4_linear(*args) == status
 
 
+def test_linear_split_k_workspace_checks():
+    """The split-K MXFP4 shape (2048 x 4096 x 14336) needs its workspace: a
+    missing or short one is rejected (W4A4_ERR_WORKSPACE), a misaligned one
+    too (W4A4_ERR_ALIGN), before anything is launched."""
+    L = w4.lib()
+    M, N, K = 2048, 4096, 14336
+    need = L.w4a4_linear_workspace_bytes(0, M, N, K)
+    assert need > 0
+    base = (0, M, N, K, FAKE, FAKE, None, FAKE, FAKE)
+    assert L.w4a4_linear(*base, None, need, None) == 5
+    assert L.w4a4_linear(*base, FAKE, need - 1, None) == 5
+    assert "workspace" in L.w4a4_last_error().decode()
+    assert L.w4a4_linear(*base, FAKE_MIS, need, None) == 3
+
+
 def test_empty_linear_is_a_no_op():
     # M = 0 returns OK without touching the pointers or the device
     assert w4.lib().w4a4_linear(0, 0, 128, 256, None, None, None, None, None, None, 0, None) == 0
