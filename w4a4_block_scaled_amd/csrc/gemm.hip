@@ -1866,12 +1866,15 @@ hipError_t launch_fp4_splitk(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
   return hipGetLastError();
 }
 
-// MXFP4 weight streaming for M <= 32: one workgroup per 32 output features,
-// WAVES waves splitting its 64-K tiles into contiguous ranges.  Each wave
-// streams its tiles from HBM straight into registers in batches of U (U
-// coalesced 1 KiB loads in flight per wave, no LDS); the activation rows are
-// the MFMA's second operand (rows >= M are zero, and their lanes load
-// nothing).  Partial sums are added through LDS and wave 0 runs the epilogue.
+// MXFP4 weight streaming for M <= 32: one workgroup per 32 output features
+// (groups run on XCD b % 8 in contiguous per-XCD ranges, as in the 16-feature
+// kernel), WAVES waves splitting its 64-K tiles into contiguous ranges.  Each
+// wave streams its tiles from HBM straight into registers in batches of U
+// (U coalesced 1 KiB non-temporal loads in flight per wave, no LDS); the
+// activation rows are the MFMA's second operand (rows >= M are zero, and
+// their lanes load nothing), loaded as row-contiguous lane pairs and moved to
+// the fragment lanes with a lane permutation.  Partial sums are added
+// through LDS and wave 0 runs the epilogue.
 template <int WAVES, int U>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
@@ -1881,7 +1884,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode_kernel(
   const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
   const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
 
-  const int64_t g = blockIdx.x;
+  const int64_t G = (N + 31) / 32, per_x = (G + 7) / 8;
+  const int64_t g = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8;
+  if (g >= G) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5;
   const int64_t m = lane & 31;
@@ -1894,7 +1899,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode_kernel(
   const int sw_shift = 8 * int(g & 3);
   const uint32_t* __restrict__ Wsg = Ws + (g >> 2) * KT * 64 + lane;
   const u32x4* __restrict__ Wg = Wc + g * KT * 64 + lane;
-  const uint8_t* __restrict__ arow = a_codes + row * K2 + 16 * half;
+  // activation codes: lane l loads row l / 2, 16-byte half l % 2 of the
+  // tile's 32 bytes (only the lanes of rows < M load); fragment lane l
+  // (row l % 32, half l / 32) reads it from lane 2 (l % 32) + l / 32
+  const int lr = lane >> 1;
+  const bool lvalid = lr < M;
+  const uint8_t* __restrict__ arow = a_codes + (lvalid ? lr : 0) * K2 + 16 * (lane & 1);
+  const int perm = 4 * (2 * int(m) + half);
   const uint8_t* __restrict__ srow = a_scales + row * KB + half;
 
   v16f acc;
@@ -1909,20 +1920,22 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode_kernel(
       const int64_t h = h0 + u;
       const bool ok = h < k_end;
       const int64_t hc = ok ? h : k_end - 1;  // clamped: loads stay in range
-      wf[u] = Wg[hc * 64];
-      swd[u] = Wsg[hc * 64];
+      wf[u] = __builtin_nontemporal_load(&Wg[hc * 64]);
+      swd[u] = __builtin_nontemporal_load(&Wsg[hc * 64]);
       u32x4 a = {0u, 0u, 0u, 0u};
-      int sb = 127;
-      if (mvalid) {
-        a = *reinterpret_cast<const u32x4*>(arow + hc * 32);
-        sb = srow[hc * 2];
-      }
+      if (lvalid) a = *reinterpret_cast<const u32x4*>(arow + hc * 32);
       af[u] = ok ? a : u32x4{0u, 0u, 0u, 0u};
-      sab[u] = sb;
+      sab[u] = mvalid ? int(srow[hc * 2]) : 127;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      acc = mfma32_fp4_op<0, 0>(wf[u], af[u], acc, int(swd[u] >> sw_shift), sab[u]);
+    for (int u = 0; u < U; ++u) {
+      u32x4 a;
+      a.x = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].x)));
+      a.y = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].y)));
+      a.z = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].z)));
+      a.w = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].w)));
+      acc = mfma32_fp4_op<0, 0>(wf[u], a, acc, int(swd[u] >> sw_shift), sab[u]);
+    }
   }
 
   __shared__ v16f red[WAVES > 1 ? WAVES - 1 : 1][64];
@@ -1950,7 +1963,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode_kernel(
 template <int WAVES, int U>
 hipError_t launch_fp4_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                              const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_fp4_decode_kernel<WAVES, U>), dim3(unsigned((N + 31) / 32)),
+  hipLaunchKernelGGL((gemm_fp4_decode_kernel<WAVES, U>), dim3(unsigned(((N + 31) / 32 + 7) / 8 * 8)),
                      dim3(64 * WAVES), 0, stream, ac, as, blob, Y, M, N, K);
   return hipGetLastError();
 }
