@@ -114,33 +114,23 @@ __device__ __forceinline__ v8i int4_frag_to_fp8(const u32x4& f) {
   return r;
 }
 
-// E4M3 byte -> its value as fp16 (exact)
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t b) {
-  const int e = (b >> 3) & 15, m = b & 7;
-  const float v = e == 0 ? ldexpf(float(m), -9) : ldexpf(float(8 + m), e - 10);
-  return _Float16(v);
-}
-
-// 8 E2M1 codes (one dword) times an fp16 scale -> 8 fp16 values (exact)
-__device__ __forceinline__ v8h e2m1x8_to_f16(uint32_t d, _Float16 s) {
-  // high byte of the fp16 encoding of E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
-  // (the low byte is always 0)
-  const uint32_t tlo = 0x3e3c3800u, thi = 0x46444240u;
-  const uint32_t e = d & 0x0f0f0f0fu;
-  const uint32_t o = (d >> 4) & 0x0f0f0f0fu;
-  const uint32_t he = __builtin_amdgcn_perm(thi, tlo, e & 0x07070707u) | ((e & 0x08080808u) << 4);
-  const uint32_t ho = __builtin_amdgcn_perm(thi, tlo, o & 0x07070707u) | ((o & 0x08080808u) << 4);
-  const h2 ss = {s, s};
-  v8h out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t sel = 0x040c000cu + 0x01000100u * uint32_t(i);
-    const uint32_t w = __builtin_amdgcn_perm(ho, he, sel);  // [0, he.b_i, 0, ho.b_i]
-    const h2 v = __builtin_bit_cast(h2, w) * ss;
-    out[2 * i] = v[0];
-    out[2 * i + 1] = v[1];
-  }
-  return out;
+// 8 E2M1 codes (one dword) times the E4M3 scale byte `sb` -> 8 fp16 values
+// (exact).  The scale, converted exactly to fp32, splits into 2^E (its
+// exponent bits) and 1 + f/8 (its mantissa bits): the hardware conversion
+// v_cvt_scalef32_pk_f16_fp4 takes only the power of two (code x 2^E, at most
+// 2 significant bits, within fp16's normal range), and a packed fp16
+// multiply by 1 + f/8 adds at most 4 more bits, so every product (at most
+// 6 x 448) is an fp16 value.  A zero scale gives zeros.
+__device__ __forceinline__ v8h e2m1x8_scaled_f16(uint32_t d, uint32_t sb) {
+  const float sv = __builtin_amdgcn_cvt_f32_fp8(int(sb), 0);
+  const float p2 = __uint_as_float(__float_as_uint(sv) & 0xff800000u);
+  const _Float16 fr = _Float16(__uint_as_float((__float_as_uint(sv) & 0x007fffffu) | 0x3f800000u));
+  const h2 ff = {fr, fr};
+  const h2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 0) * ff;
+  const h2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 1) * ff;
+  const h2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 2) * ff;
+  const h2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 3) * ff;
+  return v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
 __device__ __forceinline__ v4f mfma_f16(const v8h& w, const v8h& a, v4f acc) {
@@ -421,11 +411,10 @@ __device__ __forceinline__ void tile_step(const TileArgs& t, const LDS uint8_t* 
       v8h wh[FN];
 #pragma unroll
       for (int i = 0; i < FN; ++i)
-        wh[i] = e2m1x8_to_f16(wf[i][jj],
-                              e4m3_to_f16((sw[i / 2] >> (8 * (2 * (i % 2) + (jj >> 1)))) & 0xffu));
+        wh[i] = e2m1x8_scaled_f16(wf[i][jj], (sw[i / 2] >> (8 * (2 * (i % 2) + (jj >> 1)))) & 0xffu);
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const v8h ah = e2m1x8_to_f16(af[j][jj], e4m3_to_f16((sa[j] >> (8 * (jj >> 1))) & 0xffu));
+        const v8h ah = e2m1x8_scaled_f16(af[j][jj], (sa[j] >> (8 * (jj >> 1))) & 0xffu);
 #pragma unroll
         for (int i = 0; i < FN; ++i) acc[i][j] = mfma_f16(wh[i], ah, acc[i][j]);
       }
