@@ -94,22 +94,37 @@ __device__ __forceinline__ v4f mfma_fp8(int opw, const v8i& w, const v8i& a, v4f
   }
 }
 
-// four int4 codes (low nibble of each byte) -> E4M3 bytes of q * 2^-9:
-// q >= 0 -> byte q; q < 0 -> 0x80 | -q.
-__device__ __forceinline__ uint32_t int4x4_to_e4m3(uint32_t nib) {
-  const uint32_t neg_lo = 0x85868788u;  // nibbles 8..11 (q = -8..-5)
-  const uint32_t neg_hi = 0x81828384u;  // nibbles 12..15 (q = -4..-1)
-  const uint32_t neg = __builtin_amdgcn_perm(neg_hi, neg_lo, nib & 0x07070707u);
-  const uint32_t sel = ((nib >> 1) & 0x04040404u) | 0x03020100u;
-  return __builtin_amdgcn_perm(neg, nib, sel);
+// A constant in a VGPR that the compiler cannot see through.  Three-operand
+// (VOP3) instructions take no literal here and at most one SGPR, so with the
+// constants in VGPRs `(x & c) | c'` becomes one v_and_or_b32 and v_perm_b32
+// reads both table words from registers; with literals the compiler splits
+// them into two instructions.  Free of side effects, so the copies are hoisted
+// out of loops and merged.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  uint32_t v;
+  asm("v_mov_b32 %0, %1" : "=v"(v) : "i"(c));
+  return v;
+}
+
+// four int4 codes (the low nibbles of the bytes of `d`; the high nibbles are
+// ignored) -> E4M3 bytes of q * 2^-9: q >= 0 -> byte q; q < 0 -> 0x80 | -q.
+// Five instructions: the low three bits index the table of negative codes,
+// and bit 3 selects, per byte, that entry or the three bits themselves.
+__device__ __forceinline__ uint32_t int4x4_to_e4m3(uint32_t d) {
+  const uint32_t neg_lo = vgpr_const(0x85868788u);  // nibbles 8..11 (q = -8..-5)
+  const uint32_t neg_hi = vgpr_const(0x81828384u);  // nibbles 12..15 (q = -4..-1)
+  const uint32_t g = d & 0x07070707u;
+  const uint32_t neg = __builtin_amdgcn_perm(neg_hi, neg_lo, g);
+  const uint32_t sel = ((d >> 1) & vgpr_const(0x04040404u)) | vgpr_const(0x03020100u);
+  return __builtin_amdgcn_perm(neg, g, sel);
 }
 
 __device__ __forceinline__ v8i int4_frag_to_fp8(const u32x4& f) {
   v8i r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r[2 * i] = int(int4x4_to_e4m3(f[i] & 0x0f0f0f0fu));
-    r[2 * i + 1] = int(int4x4_to_e4m3((f[i] >> 4) & 0x0f0f0f0fu));
+    r[2 * i] = int(int4x4_to_e4m3(f[i]));
+    r[2 * i + 1] = int(int4x4_to_e4m3(f[i] >> 4));
   }
   return r;
 }
@@ -508,15 +523,27 @@ struct MxCfg {
   static constexpr int FM = BM / 16 / WM;
   static constexpr int A_BYTES = BM * 64;
   static constexpr int W_BYTES = BN * 64;
-  static constexpr int SC_BYTES = WAVES * 256;
-  static constexpr int STAGE = A_BYTES + W_BYTES + SC_BYTES;
   static constexpr int A_DMA = BM / 16 / WAVES;
   static constexpr int W_DMA = BN / 16 / WAVES;
   static constexpr int AS_DW = BM / WAVES;  // activation scale rows per wave
   static constexpr int WS_DW = BN / WAVES;  // weight scale words per wave (BN/64 groups x 64)
-  static constexpr int COPIES = A_DMA + W_DMA + 1;
+  // A wave copies its scale dwords with one 64-lane load (activation rows,
+  // then weight words) or, when they are more than 64, with two (one each).
+  static constexpr bool SC_SPLIT = AS_DW + WS_DW > 64;
+  static constexpr int SC_LOADS = SC_SPLIT ? 2 : 1;
+  static constexpr int SC_BYTES = WAVES * 256 * SC_LOADS;
+  static constexpr int STAGE = A_BYTES + W_BYTES + SC_BYTES;
+  static constexpr int COPIES = A_DMA + W_DMA + SC_LOADS;
+  // byte offsets in the scale area: activation row R's scale dword, weight word d
+  static constexpr int a_sc(int R) {
+    return (R / AS_DW) * 256 * SC_LOADS + (R % AS_DW) * 4;
+  }
+  static constexpr int w_sc(int d) {
+    return SC_SPLIT ? (d / WS_DW) * 512 + 256 + (d % WS_DW) * 4
+                    : (d / WS_DW) * 256 + (AS_DW + d % WS_DW) * 4;
+  }
   static_assert(A_DMA * WAVES * 16 == BM && W_DMA * WAVES * 16 == BN, "tile / wave split");
-  static_assert(AS_DW + WS_DW <= 64, "scale chunk");
+  static_assert(AS_DW <= 64 && WS_DW <= 64, "scale chunk");
   static_assert((AS_DW & (AS_DW - 1)) == 0 && (WS_DW & (WS_DW - 1)) == 0, "scale chunk split");
   static_assert(FN % 4 == 0 && BN % 64 == 0, "scale words");
   static_assert(DEPTH * STAGE <= 160 * 1024, "LDS");
@@ -567,16 +594,23 @@ __device__ __forceinline__ void mx_issue(const TileArgs& t, int64_t ks, LDS uint
     __builtin_amdgcn_global_load_lds(t.Wc + (ng * t.KS + ks) * 64 + lane,
                                      dst + C::A_BYTES + f * 1024, 16, 0, 0);
   }
+  LDS uint8_t* sc = dst + C::A_BYTES + C::W_BYTES + wave * 256 * C::SC_LOADS;
+  const int wl = C::SC_SPLIT ? lane : lane - C::AS_DW;  // this lane's weight word, if any
   const bool is_a = lane < C::AS_DW;
-  const bool is_w = !is_a && lane < C::AS_DW + C::WS_DW;
+  const bool is_w = wl >= 0 && wl < C::WS_DW;
   int64_t row = t.m0 + wave * C::AS_DW + (is_a ? lane : 0);
   row = row < t.M ? row : t.M - 1;
-  const int d = wave * C::WS_DW + (is_w ? lane - C::AS_DW : 0);
+  const int d = wave * C::WS_DW + (is_w ? wl : 0);
   int64_t sg = t.ng0 / 4 + d / 64;
   sg = sg < t.NSG ? sg : t.NSG - 1;
-  const uint8_t* src = is_w ? reinterpret_cast<const uint8_t*>(t.Ws + (sg * t.KS + ks) * 64 + (d & 63))
-                            : t.a_scales + row * t.KB + ks * 4;
-  __builtin_amdgcn_global_load_lds(src, dst + C::A_BYTES + C::W_BYTES + wave * 256, 4, 0, 0);
+  const uint8_t* wsrc = reinterpret_cast<const uint8_t*>(t.Ws + (sg * t.KS + ks) * 64 + (d & 63));
+  const uint8_t* asrc = t.a_scales + row * t.KB + ks * 4;
+  if constexpr (C::SC_SPLIT) {
+    __builtin_amdgcn_global_load_lds(asrc, sc, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(wsrc, sc + 256, 4, 0, 0);
+  } else {
+    __builtin_amdgcn_global_load_lds(is_a ? asrc : wsrc, sc, 4, 0, 0);
+  }
 }
 
 // Register copies of one K-step's operands for a wave (besides the weight
@@ -612,13 +646,12 @@ __device__ __forceinline__ void mx_load_rest(const LDS uint8_t* __restrict__ st,
     const u32x2 hi = b[a_tile_pos(r, 2 + (c >> 1)) * 2 + (c & 1)];
     fr.a[j] = u32x4{lo.x, lo.y, hi.x, hi.y};
     const int R = 16 * f + r;
-    fr.sa[j] = SC[(R / C::AS_DW) * 256 + (R % C::AS_DW) * 4 + c];
+    fr.sa[j] = SC[C::a_sc(R) + c];
   }
 #pragma unroll
   for (int q = 0; q < C::FN / 4; ++q) {
     const int d = (wn * C::FN / 4 + q) * 64 + lane;
-    fr.sw[q] = *reinterpret_cast<const LDS uint32_t*>(SC + (d / C::WS_DW) * 256 +
-                                                      (C::AS_DW + d % C::WS_DW) * 4);
+    fr.sw[q] = *reinterpret_cast<const LDS uint32_t*>(SC + C::w_sc(d));
   }
 }
 
@@ -2233,10 +2266,12 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
       if (ks <= 64) return launch_decode<FMT, 8, 8>(M, N, K, ac, as, blob, Y, stream);
       return launch_decode<FMT, 16, 10>(M, N, K, ac, as, blob, Y, stream);
     }
-    // MXINT4: 8 waves (two per SIMD) of 64 x 64 on the 16x16x128 FP8 MFMA;
-    // its fragments are widened to FP8 in registers, which leaves no room for
-    // larger wave tiles.
-    return launch_mx<FMT, 256, 128, 4, 2, 4>(M, N, K, ac, as, blob, Y, stream);
+    // MXINT4: 4 waves (one per SIMD) of 128 x 64 on the 16x16x128 FP8 MFMA.
+    // Fragments are widened to FP8 in registers by every wave that uses them,
+    // so the VALU work per MFMA falls as the wave tile grows: 12 widened
+    // fragments per 32 MFMAs here against 8 per 16 with 8 waves of 64 x 64
+    // (22-28% faster on the Qwen linears).  128 x 128 spills.
+    return launch_mx<FMT, 256, 128, 2, 2, 4>(M, N, K, ac, as, blob, Y, stream);
   }
 }
 
