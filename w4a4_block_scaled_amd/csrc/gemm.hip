@@ -119,6 +119,21 @@ __device__ __forceinline__ uint32_t int4x4_to_e4m3(uint32_t d) {
   return __builtin_amdgcn_perm(neg, g, sel);
 }
 
+// int4 codes biased by 8 (u = q + 8 in 0..15, the code with bit 3 flipped):
+// the E4M3 byte u encodes u * 2^-9 exactly (subnormals 0..7 and the first
+// binade 8..15 are evenly spaced), so no table is needed.  Same byte order
+// as int4_frag_to_fp8.
+__device__ __forceinline__ v8i int4_frag_biased_fp8(const u32x4& f) {
+  v8i r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = f[i] ^ 0x88888888u;
+    r[2 * i] = int(x & 0x0f0f0f0fu);
+    r[2 * i + 1] = int((x >> 4) & 0x0f0f0f0fu);
+  }
+  return r;
+}
+
 __device__ __forceinline__ v8i int4_frag_to_fp8(const u32x4& f) {
   v8i r;
 #pragma unroll
@@ -2102,6 +2117,15 @@ hipError_t launch_fp4_decode16(int64_t M, int64_t N, int64_t K, const uint8_t* a
 // then their MFMAs.  The activation rows (<= 16) are the MFMA's second
 // operand; rows >= M are zero.  Partial sums of the waves are added through
 // LDS and wave 0 runs the epilogue.
+//
+// Codes enter the FP8 MFMA biased by 8 (u = q + 8, one XOR and a nibble
+// split instead of the sign-magnitude table), and the product is expanded as
+// (u - 8)(v - 8) = u v - 8 v - 8 u + 64: four MFMAs per K-step instead of one
+// but a third of the VALU work, which here bounds the rate.  Every product is
+// exact; the fp32 accumulator rounds partial sums up to ~(15 * 15 * 128) per
+// K-step and block-scale unit where the direct form rounds ~(8 * 8 * 128),
+// well inside the output tolerance, and with equal block scales all partial
+// sums are integers below 2^24 units, so the result is the same exact value.
 template <int FMT, int WAVES, int U>
 __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
@@ -2183,7 +2207,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(
       const uint32_t h2 = uint32_t(__builtin_amdgcn_ds_bpermute(src_hi, int(af[u].z)));
       const uint32_t h3 = uint32_t(__builtin_amdgcn_ds_bpermute(src_hi, int(af[u].w)));
       const u32x4 a = odd ? u32x4{l2, l3, h2, h3} : u32x4{l0, l1, h0, h1};
-      acc = mfma_fp8_op<0>(int4_frag_to_fp8(wf[u]), int4_frag_to_fp8(a), acc, int(swd[u]), sab[u]);
+      const int sw = int(swd[u]), sa = sab[u];
+      // q_w q_a = (u - 8)(v - 8) = u v - 8 v - 8 u + 64 with the biased codes
+      // u, v: four MFMAs into the same accumulator under the same block
+      // scales, two of them against the constant -8 (E4M3 0x88 = -8 * 2^-9)
+      const v8i m8 = {-0x77777778, -0x77777778, -0x77777778, -0x77777778,
+                      -0x77777778, -0x77777778, -0x77777778, -0x77777778};
+      const v8i wu = int4_frag_biased_fp8(wf[u]), av = int4_frag_biased_fp8(a);
+      acc = mfma_fp8_op<0>(m8, av, acc, sw, sa);
+      acc = mfma_fp8_op<0>(wu, av, acc, sw, sa);
+      acc = mfma_fp8_op<0>(wu, m8, acc, sw, sa);
+      acc = mfma_fp8_op<0>(m8, m8, acc, sw, sa);
     }
   }
 
