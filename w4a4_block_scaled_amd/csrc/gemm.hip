@@ -2152,23 +2152,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(
   // activation codes: lane l loads row l / 4, 16-byte chunk l % 4 of the
   // K-step; fragment lane l (row m = l % 16, group c = l / 16) takes half
   // c % 2 of chunks c / 2 and 2 + c / 2 of row m (see load_act_frag) from
-  // lanes 4 m + c / 2 and 4 m + 2 + c / 2.  Lanes of rows >= M read zeros:
-  // for batches of up to 8 K-steps only the lanes of rows < M load (exec
-  // mask); for longer batches a branch around the loads makes the compiler
-  // drain the batch at its join, so there buffer loads bounded to the M rows
-  // return zeros without a branch.
+  // lanes 4 m + c / 2 and 4 m + 2 + c / 2.  Lanes of rows >= M take zeros:
+  // only the lanes of rows < M load (exec mask).  Batches stay at <= 8
+  // K-steps: around longer batches that branch made the compiler drain the
+  // whole batch at its join.
   static_assert(FMT == MXINT4, "activation fragment layout");
-  constexpr bool MASKED = U <= 8;
+  static_assert(U <= 8, "masked activation loads");
   const int lr = lane >> 2;
   const bool lvalid = lr < M;
   const uint8_t* __restrict__ arow = a_codes + (lvalid ? lr : 0) * K2 + 16 * (lane & 3);
   const uint8_t* __restrict__ srow = a_scales + (mvalid ? m : 0) * KB + c;
-  const __amdgpu_buffer_rsrc_t ar =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_codes), 0, int(M * K2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t sr =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_scales), 0, int(M * KB), 0x00020000);
-  const int aoff = (lane >> 2) * int(K2) + 16 * (lane & 3);
-  const int soff = int(m) * int(KB) + c;
   const int src_lo = 4 * (4 * int(m) + (c >> 1)), src_hi = src_lo + 8;
   const bool odd = c & 1;
 
@@ -2184,13 +2177,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(
       const int64_t ksc = ok ? ks : k_end - 1;  // clamped: loads stay in range
       const u32x4 w = __builtin_nontemporal_load(&Wg[ksc * 64]);
       u32x4 a = {0u, 0u, 0u, 0u};
-      if constexpr (MASKED) {
-        if (lvalid) a = *reinterpret_cast<const u32x4*>(arow + ksc * 64);
-        sab[u] = mvalid ? int(srow[ksc * 4]) : 127;
-      } else {
-        a = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff + int(ksc) * 64, 0, 0);
-        sab[u] = int(__builtin_amdgcn_raw_buffer_load_b8(sr, soff + int(ksc) * 4, 0, 0));
-      }
+      if (lvalid) a = *reinterpret_cast<const u32x4*>(arow + ksc * 64);
+      sab[u] = mvalid ? int(srow[ksc * 4]) : 127;
       wf[u] = ok ? w : u32x4{0u, 0u, 0u, 0u};
       af[u] = ok ? a : u32x4{0u, 0u, 0u, 0u};
       swd[u] = __builtin_nontemporal_load(&Wsg[ksc * 64]) >> sw_shift;
@@ -2290,15 +2278,18 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
     return launch_fp4<256, 128, 5>(M, N, K, ac, as, blob, Y, stream);
   } else {
     if (M <= 16) {
-      // waves enough for at most 7, 8 or 10 K-steps each; with K <= 4096,
-      // more waves (shorter per-wave chains) when there are few groups
+      // waves enough for at most 7 or 8 K-steps each; with K <= 4096, more
+      // waves (shorter per-wave chains) when there are few groups; long K:
+      // 16 waves taking their K-steps in batches of 5, so that the MFMAs of
+      // one batch overlap the loads of the next (Qwen down, K = 18944: 12.5
+      // -> 9.8 us against one batch of 10)
       const int64_t ks = K / 128, groups = N / 16;
       if (ks <= 32 && groups < 256) return launch_decode<FMT, 16, 2>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 32 && groups < 1024) return launch_decode<FMT, 8, 4>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 28) return launch_decode<FMT, 4, 7>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 32) return launch_decode<FMT, 4, 8>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 64) return launch_decode<FMT, 8, 8>(M, N, K, ac, as, blob, Y, stream);
-      return launch_decode<FMT, 16, 10>(M, N, K, ac, as, blob, Y, stream);
+      return launch_decode<FMT, 16, 5>(M, N, K, ac, as, blob, Y, stream);
     }
     // MXINT4: 4 waves (one per SIMD) of 128 x 64 on the 16x16x128 FP8 MFMA.
     // Fragments are widened to FP8 in registers by every wave that uses them,
