@@ -16,8 +16,6 @@
 #include "common.h"
 #include "kernels.h"
 
-#include <float.h>
-
 namespace w4a4 {
 namespace {
 
@@ -70,22 +68,19 @@ __device__ __forceinline__ int quad_xor2(int v) { return __builtin_amdgcn_mov_dp
 // block is spread over 4 consecutive lanes, which must all be present).
 template <int FMT>
 __device__ __forceinline__ void quant8_mx(const float (&x)[8], uint32_t& word, uint32_t& sbyte) {
-  float amax = 0.0f;
-  int bad = 0;
+  // block amax as the integer maximum of the magnitude bit patterns: for
+  // finite values they order as the values do, and any Inf or NaN gives a
+  // pattern above the largest finite one, so one reduction yields both
+  uint32_t abits = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = fabsf(x[i]);
-    bad |= !(a <= FLT_MAX);  // Inf or NaN
-    amax = fmaxf(amax, a);
-  }
+  for (int i = 0; i < 8; ++i) abits = max(abits, __float_as_uint(x[i]) & 0x7fffffffu);
   // the 4 lanes of a block form a quad: two DPP quad permutations
-  amax = fmaxf(amax, quad_xor1(amax));
-  amax = fmaxf(amax, quad_xor2(amax));
-  bad |= quad_xor1(bad);
-  bad |= quad_xor2(bad);
+  abits = max(abits, uint32_t(quad_xor1(int(abits))));
+  abits = max(abits, uint32_t(quad_xor2(int(abits))));
+  const bool bad = abits > 0x7f7fffffu;  // Inf or NaN in the block
 
   int e = -127;
-  if (amax > 0.0f) e = max(-127, min(127, floor_log2(amax) - 2));
+  if (abits != 0) e = max(-127, min(127, floor_log2(__uint_as_float(abits)) - 2));
 
   word = 0;
   if (FMT == MXFP4) {
@@ -305,15 +300,15 @@ hipError_t launch_quantize_act(int fmt, int64_t M, int64_t K, const void* X, con
   uint32_t* cw = static_cast<uint32_t*>(codes);
   uint8_t* sb = static_cast<uint8_t*>(scales);
   if (fmt == MXFP4 || fmt == MXINT4) {
-    // 4 rows per thread once there are enough rows to fill the chip (8 or
-    // 16 rows per thread measured slower on 2048-row activations)
+    // 2 rows per thread once there are enough rows to fill the chip (1, 4,
+    // 8 or 16 rows per thread measured slower on 2048-row activations)
     const unsigned gy = unsigned((K8 + kThreads - 1) / kThreads);
     if (M >= 256) {
-      const dim3 g2(unsigned((M + 3) / 4), gy);
+      const dim3 g2(unsigned((M + 1) / 2), gy);
       if (fmt == MXFP4)
-        hipLaunchKernelGGL((quantize_mx_kernel<MXFP4, 4>), g2, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
+        hipLaunchKernelGGL((quantize_mx_kernel<MXFP4, 2>), g2, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
       else
-        hipLaunchKernelGGL((quantize_mx_kernel<MXINT4, 4>), g2, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
+        hipLaunchKernelGGL((quantize_mx_kernel<MXINT4, 2>), g2, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
     } else {
       const dim3 g1(unsigned(M), gy);
       if (fmt == MXFP4)
