@@ -813,6 +813,103 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx_kernel(
                                 N, wave, lane);
 }
 
+// Two waves per SIMD (8 waves of 128 x 64): a wave's widening, copies and
+// LDS reads then overlap the other wave's MFMAs.  To fit 256 registers a
+// wave keeps nothing of the next K-step in registers: after the barrier it
+// reads the K-step's activation fragments and scales from the stage buffer,
+// widens them, and walks the weight fragments one row ahead.  The copy of
+// stage s + DEPTH - 1 goes out right after the barrier of K-step s, into the
+// buffer that K-step s - 1 has just released.
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__device__ __forceinline__ void mx_lean_step(const LDS uint8_t* __restrict__ st, int wn, int wm,
+                                             int lane, v4f (&acc)[BN / 16 / WN][BM / 16 / WM]) {
+  constexpr int FN = BN / 16 / WN, FM = BM / 16 / WM;
+  static_assert(FMT == MXINT4, "the MX tiled kernel serves MXINT4");
+  MxFrags<FMT, FN, FM> fr;
+  mx_load_rest<FMT, BN, BM, WN, WM, DEPTH>(st, wn, wm, lane, fr);
+  u32x4 wcur = mx_load_w<FMT, BN, BM, WN, WM, DEPTH>(st, wn, 0, lane);
+  v8i a8[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) a8[j] = int4_frag_to_fp8(fr.a[j]);
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    u32x4 wnext = wcur;
+    if (i + 1 < FN) wnext = mx_load_w<FMT, BN, BM, WN, WM, DEPTH>(st, wn, i + 1, lane);
+    mx_mfma_row<FMT, FN, FM>(acc, i, wcur, fr, a8);
+    wcur = wnext;
+  }
+}
+
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx_lean_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int tiles_m, int tiles_total, int per_xcd) {
+  using C = MxCfg<BN, BM, WN, WM, DEPTH>;
+  constexpr int FN = C::FN, FM = C::FM;
+  const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (tile >= tiles_total) return;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+
+  const BlobLayout L = blob_layout(FMT, N, K);
+  TileArgs t;
+  t.a_codes = a_codes;
+  t.a_scales = a_scales;
+  t.Wc = reinterpret_cast<const uint4*>(blob + L.code_off);
+  t.Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+  t.M = M;
+  t.K2 = K / 2;
+  t.KB = K / 32;
+  t.KS = L.KS;
+  t.NG = L.NG;
+  t.NSG = L.NSG;
+  t.m0 = int64_t(tm) * BM;
+  t.ng0 = int64_t(tn) * (BN / 16);
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * C::STAGE];
+  LDS uint8_t* base = (LDS uint8_t*)smem;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wn = wave % WN, wm = wave / WN;
+
+  v4f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t KS = L.KS;
+#pragma unroll
+  for (int s = 0; s < DEPTH - 1; ++s)
+    if (s < KS) mx_issue<FMT, BN, BM, WN, WM, DEPTH>(t, s, base + s * C::STAGE, wave, lane);
+  for (int64_t s = 0; s < KS; ++s) {
+    // stages issued after s: min(DEPTH - 2, KS - 1 - s)
+    const int64_t left = KS - 1 - s;
+    mx_sync<C::COPIES, DEPTH>(int(left < DEPTH - 2 ? left : DEPTH - 2));
+    if (s + DEPTH - 1 < KS)
+      mx_issue<FMT, BN, BM, WN, WM, DEPTH>(t, s + DEPTH - 1, base + ((s + DEPTH - 1) % DEPTH) * C::STAGE,
+                                           wave, lane);
+    mx_lean_step<FMT, BN, BM, WN, WM, DEPTH>(base + (s % DEPTH) * C::STAGE, wn, wm, lane, acc);
+  }
+
+  __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
+  asm volatile("" ::: "memory");
+  tile_epilogue<FN, FM, WN, WM>(acc, base, t, blob, L, epilogue_factor(FMT, nullptr, blob), Y, M,
+                                N, wave, lane);
+}
+
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+hipError_t launch_mx_lean(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                          const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  const int tiles_n = int((N + BN - 1) / BN);
+  const int tiles_m = int((M + BM - 1) / BM);
+  const int total = tiles_n * tiles_m;
+  const int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL((gemm_mx_lean_kernel<FMT, BN, BM, WN, WM, DEPTH>), dim3(unsigned(per_xcd * 8)),
+                     dim3(64 * WN * WM), 0, stream, ac, as, blob, Y, M, N, K, tiles_m, total,
+                     per_xcd);
+  return hipGetLastError();
+}
+
 template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
 hipError_t launch_mx(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                      const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
@@ -2291,11 +2388,18 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
       if (ks <= 64) return launch_decode<FMT, 8, 8>(M, N, K, ac, as, blob, Y, stream);
       return launch_decode<FMT, 16, 5>(M, N, K, ac, as, blob, Y, stream);
     }
-    // MXINT4: 4 waves (one per SIMD) of 128 x 64 on the 16x16x128 FP8 MFMA.
+    // MXINT4 on the 16x16x128 FP8 MFMA with wave tiles of 128 x 64.
     // Fragments are widened to FP8 in registers by every wave that uses them,
     // so the VALU work per MFMA falls as the wave tile grows: 12 widened
-    // fragments per 32 MFMAs here against 8 per 16 with 8 waves of 64 x 64
-    // (22-28% faster on the Qwen linears).  128 x 128 spills.
+    // fragments per 32 MFMAs against 8 per 16 with 64 x 64 (22-28% faster on
+    // the Qwen linears); 128 x 128 spills.  256 x 256 tiles with two waves per
+    // SIMD run ~8% more per tile than 256 x 128 tiles with one, so they are
+    // taken unless their coarser rounds over the 256 CUs cost more.
+    const int64_t tn = (N + 255) / 256;
+    const int64_t rounds_lean = (tn * ((M + 255) / 256) + 255) / 256;
+    const int64_t rounds_one = (tn * ((M + 127) / 128) + 255) / 256;
+    if (100 * rounds_lean <= 54 * rounds_one)
+      return launch_mx_lean<FMT, 256, 256, 2, 4, 4>(M, N, K, ac, as, blob, Y, stream);
     return launch_mx<FMT, 256, 128, 2, 2, 4>(M, N, K, ac, as, blob, Y, stream);
   }
 }
