@@ -436,17 +436,19 @@ __device__ __forceinline__ void tile_step(const TileArgs& t, const LDS uint8_t* 
       af[j] = A[f * 64 + a_tile_pos(r, c)];
       sa[j] = *reinterpret_cast<const LDS uint16_t*>(AS + (16 * f + r) * 8 + 2 * c);
     }
+    // per 32-wide K part: the activation fragments expanded once and held,
+    // the weight fragments expanded one at a time
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      v8h wh[FN];
+      v8h ah[FM];
 #pragma unroll
-      for (int i = 0; i < FN; ++i)
-        wh[i] = e2m1x8_scaled_f16(wf[i][jj], (sw[i / 2] >> (8 * (2 * (i % 2) + (jj >> 1)))) & 0xffu);
+      for (int j = 0; j < FM; ++j)
+        ah[j] = e2m1x8_scaled_f16(af[j][jj], (sa[j] >> (8 * (jj >> 1))) & 0xffu);
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const v8h ah = e2m1x8_scaled_f16(af[j][jj], (sa[j] >> (8 * (jj >> 1))) & 0xffu);
+      for (int i = 0; i < FN; ++i) {
+        const v8h wh = e2m1x8_scaled_f16(wf[i][jj], (sw[i / 2] >> (8 * (2 * (i % 2) + (jj >> 1)))) & 0xffu);
 #pragma unroll
-        for (int i = 0; i < FN; ++i) acc[i][j] = mfma_f16(wh[i], ah, acc[i][j]);
+        for (int j = 0; j < FM; ++j) acc[i][j] = mfma_f16(wh, ah[j], acc[i][j]);
       }
     }
   }
