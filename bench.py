@@ -15,9 +15,10 @@ durations.
 Printed: one JSON line with the workload's throughput (TFLOP/s, whole step),
 the GEMM kernel's roofline position (algorithmic flops per launch over its
 HIP-event-timed average duration, against the MI355X dense MXFP4 peak),
-decode weight-streaming bandwidth (MXFP4 Llama linears at M = 1, 4, 16 and
-MXINT4 Qwen linears at M = 1, cycling 32 layer copies so that the 256 MB
-last-level cache cannot hold the weights), and the CPU oracle timed on a
+decode weight-streaming bandwidth (MXFP4 Llama linears at M = 1, 4, 16,
+MXINT4 Qwen linears and NVFP4 Llama linears at M = 1, cycling 32 layer
+copies so that the 256 MB last-level cache cannot hold the weights), and the
+CPU oracle timed on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -261,13 +262,18 @@ def cpu_baseline(workload, M, rows=512, cols=4096):
 def gemm_kernel_label(fmt, M):
     """The GEMM kernels behind the roofline figure (all launches of a step)."""
     if fmt == "mxfp4":
+        if M <= 16:
+            return "gemm_fp4_decode16_kernel"
         if M <= 32:
             return "gemm_fp4_decode_kernel"
         return ("gemm_fp4_persistent_kernel (linears of 192+ tiles of 256x256), "
                 "gemm_fp4_splitk_kernel (64..128 tiles, K >= 8192) and gemm_fp4_kernel (the others)")
     if fmt == "mxint4":
-        return "gemm_decode_kernel<mxint4>" if M <= 16 else "gemm_mx_kernel<mxint4>"
-    return "gemm_tile_kernel<nvfp4>"
+        if M <= 16:
+            return "gemm_decode_kernel<mxint4>"
+        return ("gemm_mx_lean_kernel<mxint4> (256x256 tiles, where their rounds over the CUs are not "
+                "coarser) and gemm_mx_kernel<mxint4> (256x128 tiles)")
+    return "gemm_nv_decode_kernel" if M <= 16 else "gemm_tile_kernel<nvfp4>"
 
 
 def traffic_record(kernel):
@@ -366,6 +372,8 @@ def main():
         out["decode_hbm"] = decode_bandwidth(dev, a.steps)
         torch.cuda.empty_cache()
         out["decode_hbm_qwen_mxint4"] = decode_bandwidth(dev, a.steps, "qwen_mxint4", (1,))
+        torch.cuda.empty_cache()
+        out["decode_hbm_llama_nvfp4"] = decode_bandwidth(dev, a.steps, "llama_nvfp4", (1,))
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(a.workload, M)

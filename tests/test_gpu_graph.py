@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 # (format, M, N, K): the persistent MXFP4 GEMM, the split-K GEMM (with its
 # workspace), the tile GEMM, the decode kernels, and the NVFP4 path (tensor
-# amax pre-pass with its workspace)
+# amax pre-pass with its workspace; tile and decode GEMMs)
 CASES = [
     ("mxfp4", 512, 49152, 512),
     ("mxfp4", 300, 8208, 8192),
@@ -26,6 +26,7 @@ CASES = [
     ("mxfp4", 4, 4096, 4096),
     ("mxint4", 16, 2048, 1024),
     ("nvfp4", 260, 1024, 1024),
+    ("nvfp4", 3, 1024, 1024),
 ]
 
 

@@ -121,7 +121,7 @@ def _sample(n, count, rng):
 
 
 WORKLOADS = [("single", 16), ("llama_decode", 1), ("llama_decode", 4), ("llama_decode", 16),
-             ("llama_prefill", 2048), ("llama_nvfp4", 4096), ("qwen_mxint4", 1),
+             ("llama_prefill", 2048), ("llama_nvfp4", 16), ("llama_nvfp4", 4096), ("qwen_mxint4", 1),
              ("qwen_mxint4", 512), ("qwen_mxint4", 4096)]
 
 
@@ -149,7 +149,7 @@ def test_workload_full_size(workload, M):
         del Y, blob
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_decode_and_tile_kernels_agree(fmt):
     """M <= 16 runs the weight-streaming kernel, larger M the tiled one; the
     first 16 rows of an M = 40 call equal an M = 16 call within G1."""

@@ -2331,6 +2331,101 @@ hipError_t launch_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
   return hipGetLastError();
 }
 
+// ================================================= NVFP4 decode kernel ==
+//
+// M <= 16, NVFP4: weight streaming like the MXINT4 decode kernel (one
+// workgroup per 16 output features, groups per XCD, the WAVES waves splitting
+// K into contiguous ranges of K-steps loaded U at a time, weights
+// non-temporal), on the 16x16x32 fp16 MFMA.  Both operands' lanes hold the
+// same K positions, so no permutation is needed: lane (m = l % 16, c = l / 16)
+// of the weight tile holds the 32 codes of K-chunk c (blocks 2c and 2c + 1)
+// of row m, and the activation lane loads the same 16 bytes of row m with its
+// two block-scale bytes.  Each 32-wide part is expanded exactly into fp16
+// (code times E4M3 scale) on both sides; t_a t_w and r come in the epilogue.
+template <int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void gemm_nv_decode_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ t_act, const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y,
+    int64_t M, int64_t N, int64_t K) {
+  const BlobLayout L = blob_layout(NVFP4, N, K);
+  const u32x4* __restrict__ Wc = reinterpret_cast<const u32x4*>(blob + L.code_off);
+  const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+  const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
+
+  const int64_t F = N / 16, per_x = (F + 7) / 8;
+  const int64_t ng = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8;
+  if (ng >= F) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane >> 4;
+  const int64_t m = lane & 15;
+  const bool mvalid = m < M;
+  const int64_t KS = L.KS, K2 = K / 2, KB = K / 16;
+  const int64_t per = (KS + WAVES - 1) / WAVES;
+  const int64_t k_begin = wave * per;
+  const int64_t k_end = k_begin + per < KS ? k_begin + per : KS;
+  // scale word: bytes 2 (ng % 2) and 2 (ng % 2) + 1 hold blocks 2c and 2c + 1
+  const int sw_shift = 16 * int(ng & 1);
+  const uint32_t* __restrict__ Wsg = Ws + (ng >> 1) * KS * 64 + lane;
+  const u32x4* __restrict__ Wg = Wc + ng * KS * 64 + lane;
+  const uint8_t* __restrict__ arow = a_codes + (mvalid ? m : 0) * K2 + 16 * c;
+  const uint8_t* __restrict__ srow = a_scales + (mvalid ? m : 0) * KB + 2 * c;
+  static_assert(U <= 8, "masked activation loads");
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += U) {
+    u32x4 wf[U], af[U];
+    uint32_t swd[U], sad[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t ks = k0 + u;
+      const bool ok = ks < k_end;
+      const int64_t ksc = ok ? ks : k_end - 1;  // clamped: loads stay in range
+      const u32x4 w = __builtin_nontemporal_load(&Wg[ksc * 64]);
+      u32x4 a = {0u, 0u, 0u, 0u};
+      uint32_t sa = 0;
+      if (mvalid) {
+        a = *reinterpret_cast<const u32x4*>(arow + ksc * 64);
+        sa = *reinterpret_cast<const uint16_t*>(srow + ksc * 8);
+      }
+      wf[u] = ok ? w : u32x4{0u, 0u, 0u, 0u};
+      af[u] = ok ? a : u32x4{0u, 0u, 0u, 0u};
+      swd[u] = __builtin_nontemporal_load(&Wsg[ksc * 64]) >> sw_shift;
+      sad[u] = sa;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const v8h wh = e2m1x8_scaled_f16(wf[u][jj], (swd[u] >> (8 * (jj >> 1))) & 0xffu);
+        const v8h ah = e2m1x8_scaled_f16(af[u][jj], (sad[u] >> (8 * (jj >> 1))) & 0xffu);
+        acc = mfma_f16(wh, ah, acc);
+      }
+    }
+  }
+
+  __shared__ v4f red[WAVES > 1 ? WAVES - 1 : 1][64];
+  if (wave != 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < WAVES - 1; ++w) {
+    const v4f o = red[w][lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += o[e];
+  }
+  const float f = epilogue_factor(NVFP4, t_act, blob);
+  const float4 r = *reinterpret_cast<const float4*>(R + ng * 16 + 4 * c);
+  if (mvalid) store4(Y, N, m, ng * 16 + 4 * c, acc, v4f{r.x * f, r.y * f, r.z * f, r.w * f});
+}
+
+template <int WAVES, int U>
+hipError_t launch_nv_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                            const float* t_act, const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_nv_decode_kernel<WAVES, U>), dim3(unsigned((N / 16 + 7) / 8 * 8)), dim3(64 * WAVES),
+                     0, stream, ac, as, t_act, blob, Y, M, N, K);
+  return hipGetLastError();
+}
+
 template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
 hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                        const float* t_act, const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
@@ -2349,6 +2444,16 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
                       const float* t_act, const uint8_t* blob, uint16_t* Y, void* workspace,
                       hipStream_t stream) {
   if constexpr (FMT == NVFP4) {
+    if (M <= 16) {
+      // weight streaming; waves enough for at most 8 K-steps each, more
+      // waves when there are few groups
+      const int64_t ks = K / 128, groups = N / 16;
+      if (ks <= 32 && groups < 256) return launch_nv_decode<16, 2>(M, N, K, ac, as, t_act, blob, Y, stream);
+      if (ks <= 32 && groups < 1024) return launch_nv_decode<8, 4>(M, N, K, ac, as, t_act, blob, Y, stream);
+      if (ks <= 32) return launch_nv_decode<4, 8>(M, N, K, ac, as, t_act, blob, Y, stream);
+      if (ks <= 64) return launch_nv_decode<8, 8>(M, N, K, ac, as, t_act, blob, Y, stream);
+      return launch_nv_decode<16, 8>(M, N, K, ac, as, t_act, blob, Y, stream);
+    }
     // NVFP4 runs four fp16 MFMAs per fragment pair, so its K-step is long
     // enough for 64 x 64 wave tiles at any shape, and it holds expanded fp16
     // fragments that would not fit the register budget of a 128 x 64 tile.
