@@ -237,6 +237,28 @@ struct TileArgs {
   int64_t m0, ng0;
 };
 
+// operands of the workgroup tile whose first activation row is m0 and first
+// weight row group ng0
+__device__ __forceinline__ TileArgs tile_args(int fmt, const uint8_t* a_codes,
+                                              const uint8_t* a_scales, const uint8_t* blob,
+                                              const BlobLayout& L, int64_t M, int64_t K, int64_t m0,
+                                              int64_t ng0) {
+  TileArgs t;
+  t.a_codes = a_codes;
+  t.a_scales = a_scales;
+  t.Wc = reinterpret_cast<const uint4*>(blob + L.code_off);
+  t.Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+  t.M = M;
+  t.K2 = K / 2;
+  t.KB = K / block_size(fmt);
+  t.KS = L.KS;
+  t.NG = L.NG;
+  t.NSG = L.NSG;
+  t.m0 = m0;
+  t.ng0 = ng0;
+  return t;
+}
+
 template <int FN, int FM, int WN, int WM>
 __device__ __forceinline__ void tile_epilogue(const v4f (&acc)[FN][FM], LDS uint8_t* base,
                                               const TileArgs& t, const uint8_t* __restrict__ blob,
@@ -469,19 +491,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_tile_kernel(
   const int tm = tile % tiles_m, tn = tile / tiles_m;
 
   const BlobLayout L = blob_layout(FMT, N, K);
-  TileArgs t;
-  t.a_codes = a_codes;
-  t.a_scales = a_scales;
-  t.Wc = reinterpret_cast<const uint4*>(blob + L.code_off);
-  t.Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
-  t.M = M;
-  t.K2 = K / 2;
-  t.KB = K / block_size(FMT);
-  t.KS = L.KS;
-  t.NG = L.NG;
-  t.NSG = L.NSG;
-  t.m0 = int64_t(tm) * BM;
-  t.ng0 = int64_t(tn) * (BN / 16);
+  const TileArgs t = tile_args(FMT, a_codes, a_scales, blob, L, M, K, int64_t(tm) * BM,
+                               int64_t(tn) * (BN / 16));
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * C::STAGE];
   LDS uint8_t* base = (LDS uint8_t*)smem;
@@ -745,19 +756,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx_kernel(
   const int tm = tile % tiles_m, tn = tile / tiles_m;
 
   const BlobLayout L = blob_layout(FMT, N, K);
-  TileArgs t;
-  t.a_codes = a_codes;
-  t.a_scales = a_scales;
-  t.Wc = reinterpret_cast<const uint4*>(blob + L.code_off);
-  t.Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
-  t.M = M;
-  t.K2 = K / 2;
-  t.KB = K / 32;
-  t.KS = L.KS;
-  t.NG = L.NG;
-  t.NSG = L.NSG;
-  t.m0 = int64_t(tm) * BM;
-  t.ng0 = int64_t(tn) * (BN / 16);
+  const TileArgs t = tile_args(FMT, a_codes, a_scales, blob, L, M, K, int64_t(tm) * BM,
+                               int64_t(tn) * (BN / 16));
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * C::STAGE];
   LDS uint8_t* base = (LDS uint8_t*)smem;
@@ -854,19 +854,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx_lean_kernel(
   const int tm = tile % tiles_m, tn = tile / tiles_m;
 
   const BlobLayout L = blob_layout(FMT, N, K);
-  TileArgs t;
-  t.a_codes = a_codes;
-  t.a_scales = a_scales;
-  t.Wc = reinterpret_cast<const uint4*>(blob + L.code_off);
-  t.Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
-  t.M = M;
-  t.K2 = K / 2;
-  t.KB = K / 32;
-  t.KS = L.KS;
-  t.NG = L.NG;
-  t.NSG = L.NSG;
-  t.m0 = int64_t(tm) * BM;
-  t.ng0 = int64_t(tn) * (BN / 16);
+  const TileArgs t = tile_args(FMT, a_codes, a_scales, blob, L, M, K, int64_t(tm) * BM,
+                               int64_t(tn) * (BN / 16));
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * C::STAGE];
   LDS uint8_t* base = (LDS uint8_t*)smem;
