@@ -16,7 +16,7 @@ float8 codecs, exact rational brute force (fractions.Fraction), scaling and
 sign invariances, hand-worked golden blocks, a closed-form single block, and
 the packed-size arithmetic of the paper's Table 12.
 """
-from . import formats, quant, linear  # noqa: F401
+from . import formats, quant, linear, solver  # noqa: F401
 from .quant import (BLOCK, quantize_act, quantize_weight, quantize_rows,  # noqa: F401
                     pack_nibbles, unpack_nibbles, dequantize, rescale, nv_tensor_scale)
 from .linear import linear as linear_bf16, linear_f64, layer, layer_prescaled  # noqa: F401
