@@ -42,7 +42,7 @@ Readings where the pages leave a step open:
     the same order reaches the same projected scales:
       rows:    8 consecutive terms sequentially, the four such partials of a
                32-block as ((p0 + p1) + p2) + p3, then the blocks in order;
-      columns: rows in chunks of 64, each chunk sequentially, then the chunks
+      columns: rows in chunks of 16, each chunk sequentially, then the chunks
                in order.
     beta_0 uses the column order; alpha_0 is an exact maximum.
   * The projection is to the nearest power of two 2^e, e in [-127, 127], in
@@ -60,7 +60,7 @@ from .quant import quantize_rows, pack_nibbles, dequantize
 
 E8M0_MIN = 2.0 ** -127
 E8M0_MAX = 2.0 ** 127
-COL_CHUNK = 64
+COL_CHUNK = 16
 
 
 def project_e8m0(u):

@@ -156,3 +156,35 @@ def test_linear_split_k_workspace_checks():
 def test_empty_linear_is_a_no_op():
     # M = 0 returns OK without touching the pointers or the device
     assert w4.lib().w4a4_linear(0, 0, 128, 256, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_dualquant_workspace_bytes():
+    """fp64 partial sums per (row, 32-block) and per (16-row chunk, column),
+    two of each, and the current fp32 scales, each 256-byte aligned."""
+    L = w4.lib()
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    for N, K in [(64, 256), (100, 4096), (4096, 14336)]:
+        want = 2 * a256(N * (K // 32) * 8) + 2 * a256((N + 15) // 16 * K * 8) + a256(4 * N) + a256(4 * K)
+        assert L.w4a4_dualquant_workspace_bytes(0, N, K) == want
+        assert L.w4a4_dualquant_workspace_bytes(2, N, K) == want
+    assert L.w4a4_dualquant_workspace_bytes(1, 64, 256) == 0      # NVFP4: not covered
+    assert L.w4a4_dualquant_workspace_bytes(0, 64, 48) == 0       # K % 32
+    assert L.w4a4_dualquant_workspace_bytes(0, 0, 256) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 4),      # NVFP4
+    ((0, 64, 48, FAKE, 15, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 2),       # K % 32
+    ((0, 64, 256, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 2),       # iters < 1
+    ((0, 64, 256, None, 15, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 1),      # W NULL
+    ((0, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, None, 1 << 30, None), 5),      # no workspace
+    ((0, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, None), 5),         # short
+    ((0, 64, 256, FAKE_MIS, 15, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 3),  # W 16-byte
+])
+def test_dualquant_solve_rejects(args, status):
+    L = w4.lib()
+    assert L.w4a4_dualquant_solve(*args) == status
+    assert L.w4a4_last_error().decode()

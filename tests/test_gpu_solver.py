@@ -1,0 +1,103 @@
+"""GPU parity of the dual-scale solver (w4a4_dualquant_solve, MX formats).
+
+The solver's decisions (projections of fp64 sums, block quantization of the
+rescaled weight) are taken in the same precision and summation order as the
+oracle's, so r, c, codes and scales must equal the oracle's exactly.  At a
+full Llama size, where the oracle's full run is too slow, properties that
+hold at any size once Q^ has stabilized are checked: r and c are powers of
+two, the codes are the quantization of Diag(1/r) W Diag(1/c) (oracle
+quantizer on sampled rows), and r and c are fixed points of the oracle's
+closed-form updates for those codes (rows sampled, columns over all rows)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import solver as S
+import oracle
+from gpu_common import device, say
+import w4a4_block_scaled_amd as w4
+
+pytestmark = pytest.mark.gpu
+
+
+def weights(seed, N, K, zero_row=None, zero_col=None):
+    rng = np.random.default_rng(seed)
+    w = rng.normal(0, 0.02, (N, K)).astype(np.float32)
+    w[:, rng.choice(K, max(1, K // 64), replace=False)] *= 20
+    w *= np.exp(rng.normal(0, 0.5, (1, K))).astype(np.float32)
+    w *= np.exp(rng.normal(0, 0.3, (N, 1))).astype(np.float32)
+    if zero_row is not None:
+        w[zero_row] = 0
+    if zero_col is not None:
+        w[:, zero_col] = 0
+    return w
+
+
+def gpu_solve(w, fmt, iters, dev):
+    r, c, codes, scales = w4.dualquant_solve(torch.from_numpy(w).to(dev), fmt, iters)
+    torch.cuda.synchronize()
+    return r.cpu().numpy(), c.cpu().numpy(), codes.cpu().numpy(), scales.cpu().numpy()
+
+
+# (N, K, iters, zero row, zero column): ragged 16-row chunks, one 32-block,
+# one row, one iteration, degenerate rows and columns
+CASES = [
+    (64, 256, 15, None, None),
+    (100, 512, 15, 7, 33),
+    (1, 64, 3, None, None),
+    (37, 32, 15, None, None),
+    (256, 2048, 15, None, None),
+    (48, 1024, 1, 0, 0),
+]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+@pytest.mark.parametrize("N,K,iters,zr,zc", CASES)
+def test_solver_matches_oracle(fmt, N, K, iters, zr, zc):
+    dev = device()
+    say(f"[solver] {fmt} N={N} K={K} T={iters}")
+    w = weights(N * 7 + K, N, K, zr, zc)
+    r, c, codes, scales = gpu_solve(w, fmt, iters, dev)
+    r_o, c_o, codes_o, scales_o = S.solve(w, fmt, iters)
+    assert np.array_equal(r, r_o), f"{(r != r_o).sum()} of {N} row scales differ"
+    assert np.array_equal(c, c_o), f"{(c != c_o).sum()} of {K} column scales differ"
+    assert np.array_equal(scales, scales_o), f"{(scales != scales_o).sum()} scales differ"
+    assert np.array_equal(codes, codes_o), f"{(codes != codes_o).sum()} code bytes differ"
+
+
+def test_solver_repeated_calls_are_identical():
+    dev = device()
+    w = weights(3, 128, 512)
+    a = gpu_solve(w, "mxfp4", 5, dev)
+    b = gpu_solve(weights(4, 64, 256), "mxint4", 5, dev)
+    a2 = gpu_solve(w, "mxfp4", 5, dev)
+    assert all(np.array_equal(x, y) for x, y in zip(a, a2))
+    assert b[0].shape == (64,)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+def test_solver_full_size_properties(fmt):
+    """Llama O projection size (4096 x 4096), T = 15."""
+    dev = device()
+    N, K = 4096, 4096
+    say(f"[solver full] {fmt} N={N} K={K}")
+    w = weights(11, N, K)
+    r, c, codes, scales = gpu_solve(w, fmt, 15, dev)
+    for v in (r, c):
+        m, _ = np.frexp(v)
+        assert np.all(m == 0.5) and np.all(v > 0)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 24, replace=False)]))
+    alpha = (1.0 / r.astype(np.float64)).astype(np.float32)
+    beta = (1.0 / c.astype(np.float64)).astype(np.float32)
+    oc, osc, _ = oracle.quantize_rows(S.rescaled(w[rows], alpha[rows], beta), fmt)
+    assert np.array_equal(codes[rows], oracle.pack_nibbles(oc))
+    assert np.array_equal(scales[rows], osc)
+    q = oracle.dequantize(codes[rows], scales[rows], fmt)
+    assert np.array_equal(S.row_update(w[rows], q, beta).astype(np.float32), r[rows])
+    q_all = oracle.dequantize(codes, scales, fmt)
+    assert np.array_equal(S.col_update(w, q_all, alpha).astype(np.float32), c)
+    err = S.mse(w[rows], r[rows], c, q)
+    qr, sr, _ = oracle.quantize_rows(w[rows], fmt)
+    rtn = S.mse(w[rows], np.ones(len(rows)), np.ones(K), oracle.dequantize(oracle.pack_nibbles(qr), sr, fmt))
+    say(f"    sampled-row error {err:.4g}, round-to-nearest {rtn:.4g}")

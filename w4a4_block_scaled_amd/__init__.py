@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
     L.w4a4_unpack_weight.restype = i32
     L.w4a4_linear.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     L.w4a4_linear.restype = i32
+    L.w4a4_dualquant_workspace_bytes.argtypes = [i32, i64, i64]
+    L.w4a4_dualquant_workspace_bytes.restype = sz
+    L.w4a4_dualquant_solve.argtypes = [i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.w4a4_dualquant_solve.restype = i32
     L.w4a4_last_error.argtypes = []
     L.w4a4_last_error.restype = ctypes.c_char_p
     L.w4a4_version.argtypes = []
@@ -196,3 +200,28 @@ def linear(a_codes: torch.Tensor, a_scales: torch.Tensor, t_act: Optional[torch.
                          workspace.numel() if workspace is not None else 0,
                          _stream(a_codes.device)))
     return out
+
+
+def dualquant_solve(w: torch.Tensor, fmt, iters: int = 15, workspace: Optional[torch.Tensor] = None):
+    """w4a4_dualquant_solve: fp32 weights [N, K] -> (r [N], c [K], codes [N, K/2], scales [N, K/32]).
+
+    The offline dual-scale solver (MXFP4, MXINT4); W ~ diag(r) Q diag(c).
+    Without `workspace`, one of w4a4_dualquant_workspace_bytes() bytes is
+    allocated here.
+    """
+    f = _fmt(fmt)
+    L = lib()
+    N, K = w.shape
+    ws_bytes = L.w4a4_dualquant_workspace_bytes(f, N, K)
+    if ws_bytes == 0:
+        raise W4A4Error(2, f"dualquant_solve: unsupported format or shape N={N} K={K}")
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=w.device)
+    r = torch.empty(N, dtype=torch.float32, device=w.device)
+    c = torch.empty(K, dtype=torch.float32, device=w.device)
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+    _check(L.w4a4_dualquant_solve(f, N, K, _ptr(w), int(iters), _ptr(r), _ptr(c), _ptr(codes),
+                                  _ptr(scales), _ptr(workspace), workspace.numel(),
+                                  _stream(w.device)))
+    return r, c, codes, scales

@@ -538,11 +538,15 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_tile_kernel(
 // s+1+DEPTH goes there, so DEPTH-1 stages stay in flight.
 //
 // LDS stage buffer: [A codes: BM/16 x 1 KiB][W codes: BN/16 x 1 KiB]
-// [scales: 256 B per wave].  One 4-byte copy per wave per stage fills that
-// wave's scale chunk: dwords [0, AS_DW) are the activation scale dwords (the
-// four blocks of one row) of rows wave*AS_DW.., dwords [AS_DW, AS_DW+WS_DW)
-// the weight scale words wave*WS_DW.. of the tile (word d: group d/64, lane
-// d%64); the remaining lanes copy a duplicate into padding.
+// [scales: 256 B per wave, or 512 B when a wave's scale dwords exceed 64].
+// One 4-byte copy per wave per stage fills that wave's scale chunk: dwords
+// [0, AS_DW) are the activation scale dwords (the four blocks of one row) of
+// rows wave*AS_DW.., dwords [AS_DW, AS_DW+WS_DW) the weight scale words
+// wave*WS_DW.. of the tile (word d: group d/64, lane d%64); the remaining
+// lanes copy a duplicate into padding.  With 512 B the activation dwords
+// fill the first 256 B and the weight words the second, one copy each.
+// (gemm_mx_lean_kernel below shares the ring, copies and fragment reads but
+// keeps nothing of the next K-step in registers.)
 
 template <int BN, int BM, int WN, int WM, int DEPTH>
 struct MxCfg {

@@ -1,0 +1,280 @@
+// DualQuant's offline dual-scale solver for the MX formats on gfx950.
+//
+// Algorithm 1 of the DualQuant paper (Section 4.3, block coordinate descent
+// with closed-form scale updates): starting from alpha_0 = 1 / row absmax and
+// beta_0 = 1 / column l1 norm, each of T iterations
+//   - quantizes W~ = Diag(alpha) W Diag(beta) row-wise (the format's block
+//     quantizer, the same device code as the activation quantizer), forms
+//     R = Q^ Diag(beta)^-1 and sets r_i = alpha_i^-1 to the power of two
+//     nearest to <W_i, R_i> / ||R_i||^2 (the row's closed-form minimizer,
+//     projected as in Appendix C, Remark 1);
+//   - re-quantizes with the new alpha, forms S = Diag(alpha)^-1 Q^ and sets
+//     c_j = beta_j^-1 likewise over the columns.
+// A final pass emits Q(Diag(alpha) W Diag(beta)) as canonical codes and
+// scales; W ~ Diag(r) Q Diag(c).
+//
+// Every projection is a discrete decision taken on fp64 sums, so the sums
+// follow one fixed order (which a CPU restatement can follow too):
+//   rows:    a lane sums its 8 consecutive terms in order; the 4 lanes of a
+//            32-block combine as ((p0 + p1) + p2) + p3; the row-finalize
+//            thread adds the block sums in order;
+//   columns: a thread sums its column over a chunk of 16 rows in order; the
+//            column-finalize thread adds the chunk sums in order.
+// Per pass each element is read once (fp32 W), one grid covering W: threads
+// own 8 consecutive columns (one 32-byte read per row) of a 16-row chunk.
+#include "common.h"
+#include "kernels.h"
+#include "mx_quant.h"
+
+namespace w4a4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 16;  // rows per column partial sum
+
+enum PassMode { kInit = 0, kRows = 1, kCols = 2, kEmit = 3 };
+
+// value of 4-bit code `q` of the format (exact)
+template <int FMT>
+__device__ __forceinline__ double code_value(uint32_t q) {
+  if (FMT == MXINT4) return double(int(q << 28) >> 28);
+  // E2M1: exponent field e, mantissa bit m: 0.5 m (e = 0), (1 + m/2) 2^(e-1)
+  const int e = int(q >> 1) & 3, m = int(q & 1);
+  const double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return (q & 8) ? -v : v;
+}
+
+// Nearest power of two 2^e, e in [-127, 127], to u in linear distance; an
+// exact tie 1.5 * 2^e goes up; non-positive (or NaN) u gives 2^-127.
+__device__ __forceinline__ double project_e8m0(double u) {
+  if (!(u > 0.0)) return 0x1p-127;
+  int e;
+  (void)frexp(u, &e);  // 2^(e-1) <= u < 2^e
+  const double lo = ldexp(1.0, e - 1);
+  const double near = u >= 1.5 * lo ? 2.0 * lo : lo;
+  return fmin(fmax(near, 0x1p-127), 0x1p127);
+}
+
+__device__ __forceinline__ double shfl_lane(double v, int src) {
+  return __shfl(v, src, 64);
+}
+
+// One pass over W [N, K] fp32.  Grid x: 16-row chunks, grid y: 256-wide runs
+// of 8-column groups.  Rows: per (row, 32-block) fp64 sums of W*R and R*R
+// (lane 4q of the quad writes them).  Cols: per (chunk, column) fp64 sums of
+// W*S and S*S.  Init: per (row, 32-block) max |W| and per (chunk, column)
+// sum |W|.  Emit: codes and scales.
+template <int FMT, int MODE>
+__global__ __launch_bounds__(kThreads) void dq_pass_kernel(
+    const float* __restrict__ W, const float* __restrict__ alpha, const float* __restrict__ beta,
+    int64_t N, int64_t K8, double* __restrict__ row_a, double* __restrict__ row_b,
+    double* __restrict__ col_a, double* __restrict__ col_b, uint32_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  const int64_t col_raw = int64_t(blockIdx.y) * kThreads + threadIdx.x;
+  const bool live_c = col_raw < K8;
+  const int64_t col8 = live_c ? col_raw : K8 - 1;  // every lane joins the quad exchanges
+  const int64_t K = K8 * 8, KB = K8 / 4;
+  const int64_t r0 = int64_t(blockIdx.x) * kChunk;
+  const int lane = threadIdx.x & 63;
+  const int quad0 = lane & ~3;
+  float b8[8];
+  if (MODE != kInit) {
+    const float4 b0 = reinterpret_cast<const float4*>(beta)[2 * col8];
+    const float4 b1 = reinterpret_cast<const float4*>(beta)[2 * col8 + 1];
+    b8[0] = b0.x; b8[1] = b0.y; b8[2] = b0.z; b8[3] = b0.w;
+    b8[4] = b1.x; b8[5] = b1.y; b8[6] = b1.z; b8[7] = b1.w;
+  }
+  double ca[8], cb[8];  // column sums over this chunk
+  const int64_t rows = N - r0 < kChunk ? N - r0 : kChunk;
+  for (int64_t i = 0; i < rows; ++i) {
+    const int64_t row = r0 + i;
+    const float4 w0 = reinterpret_cast<const float4*>(W + row * K)[2 * col8];
+    const float4 w1 = reinterpret_cast<const float4*>(W + row * K)[2 * col8 + 1];
+    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    if (MODE == kInit) {
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        m = fmaxf(m, fabsf(w[e]));
+        const double a = fabs(double(w[e]));
+        ca[e] = i == 0 ? a : ca[e] + a;
+      }
+      m = fmaxf(m, quad_xor1(m));
+      m = fmaxf(m, quad_xor2(m));
+      if (live_c && (col8 & 3) == 0) row_a[row * KB + (col8 >> 2)] = double(m);
+      continue;
+    }
+    const float a = alpha[row];
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(__fmul_rn(a, w[e]), b8[e]);
+    uint32_t word, sbyte;
+    quant8_mx<FMT>(x, word, sbyte);
+    if (MODE == kEmit) {
+      if (live_c) {
+        codes[row * K8 + col8] = word;
+        if ((col8 & 3) == 0) scales[row * KB + (col8 >> 2)] = uint8_t(sbyte);
+      }
+      continue;
+    }
+    const double bscale = ldexp(1.0, int(sbyte) - 127);
+    if (MODE == kRows) {
+      double pa = 0.0, pb = 0.0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double R = (code_value<FMT>((word >> (4 * e)) & 15u) * bscale) / double(b8[e]);
+        const double ta = double(w[e]) * R, tb = R * R;
+        pa = e == 0 ? ta : pa + ta;
+        pb = e == 0 ? tb : pb + tb;
+      }
+      const double a1 = shfl_lane(pa, quad0 + 1), a2 = shfl_lane(pa, quad0 + 2),
+                   a3 = shfl_lane(pa, quad0 + 3);
+      const double b1 = shfl_lane(pb, quad0 + 1), b2 = shfl_lane(pb, quad0 + 2),
+                   b3 = shfl_lane(pb, quad0 + 3);
+      if (live_c && (col8 & 3) == 0) {
+        row_a[row * KB + (col8 >> 2)] = ((pa + a1) + a2) + a3;
+        row_b[row * KB + (col8 >> 2)] = ((pb + b1) + b2) + b3;
+      }
+    } else {  // kCols
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double S = (code_value<FMT>((word >> (4 * e)) & 15u) * bscale) / double(a);
+        const double ta = double(w[e]) * S, tb = S * S;
+        ca[e] = i == 0 ? ta : ca[e] + ta;
+        cb[e] = i == 0 ? tb : cb[e] + tb;
+      }
+    }
+  }
+  if ((MODE == kInit || MODE == kCols) && live_c && rows > 0) {
+    const int64_t off = int64_t(blockIdx.x) * K + col8 * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      col_a[off + e] = ca[e];
+      if (MODE == kCols) col_b[off + e] = cb[e];
+    }
+  }
+}
+
+// One thread per row.  Init: alpha_0 = 1 / max|W_i| (1 for a zero row).
+// Update: r_i = Pi(sum W*R / sum R*R), alpha_i = 1 / r_i (r = alpha = 1 when
+// the row's Q^ is all zero).
+template <bool INIT>
+__global__ __launch_bounds__(kThreads) void dq_row_finalize_kernel(
+    const double* __restrict__ row_a, const double* __restrict__ row_b, int64_t N, int64_t KB,
+    float* __restrict__ r, float* __restrict__ alpha) {
+  const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= N) return;
+  const double* pa = row_a + i * KB;
+  if (INIT) {
+    double m = 0.0;
+    for (int64_t b = 0; b < KB; ++b) m = fmax(m, pa[b]);
+    alpha[i] = m > 0.0 ? float(1.0 / m) : 1.0f;
+    return;
+  }
+  const double* pb = row_b + i * KB;
+  double num = pa[0], den = pb[0];
+  for (int64_t b = 1; b < KB; ++b) {
+    num = num + pa[b];
+    den = den + pb[b];
+  }
+  const double ri = den > 0.0 ? project_e8m0(num / den) : 1.0;
+  r[i] = float(ri);
+  alpha[i] = float(1.0 / ri);
+}
+
+// One thread per column, the same over the 16-row chunk sums.
+template <bool INIT>
+__global__ __launch_bounds__(kThreads) void dq_col_finalize_kernel(
+    const double* __restrict__ col_a, const double* __restrict__ col_b, int64_t chunks, int64_t K,
+    float* __restrict__ c, float* __restrict__ beta) {
+  const int64_t j = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (j >= K) return;
+  double num = col_a[j];
+  double den = INIT ? 0.0 : col_b[j];
+  for (int64_t h = 1; h < chunks; ++h) {
+    num = num + col_a[h * K + j];
+    if (!INIT) den = den + col_b[h * K + j];
+  }
+  if (INIT) {
+    beta[j] = num > 0.0 ? float(1.0 / num) : 1.0f;
+    return;
+  }
+  const double cj = den > 0.0 ? project_e8m0(num / den) : 1.0;
+  c[j] = float(cj);
+  beta[j] = float(1.0 / cj);
+}
+
+struct SolverWs {
+  float* alpha;
+  float* beta;
+  double *row_a, *row_b, *col_a, *col_b;
+};
+
+SolverWs carve(void* ws, int64_t N, int64_t K) {
+  const int64_t KB = K / 32, chunks = (N + kChunk - 1) / kChunk;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  SolverWs s;
+  s.row_a = reinterpret_cast<double*>(p);
+  p += align256(N * KB * 8);
+  s.row_b = reinterpret_cast<double*>(p);
+  p += align256(N * KB * 8);
+  s.col_a = reinterpret_cast<double*>(p);
+  p += align256(chunks * K * 8);
+  s.col_b = reinterpret_cast<double*>(p);
+  p += align256(chunks * K * 8);
+  s.alpha = reinterpret_cast<float*>(p);
+  p += align256(N * 4);
+  s.beta = reinterpret_cast<float*>(p);
+  return s;
+}
+
+template <int FMT, int MODE>
+void pass(const float* W, const SolverWs& s, int64_t N, int64_t K, uint32_t* codes,
+          uint8_t* scales, hipStream_t stream) {
+  const int64_t K8 = K / 8;
+  const dim3 grid(unsigned((N + kChunk - 1) / kChunk), unsigned((K8 + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL((dq_pass_kernel<FMT, MODE>), grid, dim3(kThreads), 0, stream, W, s.alpha,
+                     s.beta, N, K8, s.row_a, s.row_b, s.col_a, s.col_b, codes, scales);
+}
+
+template <int FMT>
+hipError_t solve(int64_t N, int64_t K, const float* W, int iters, float* r, float* c,
+                 void* codes, void* scales, void* ws, hipStream_t stream) {
+  const SolverWs s = carve(ws, N, K);
+  const int64_t KB = K / 32, chunks = (N + kChunk - 1) / kChunk;
+  const dim3 gr(unsigned((N + kThreads - 1) / kThreads)), gc(unsigned((K + kThreads - 1) / kThreads));
+  uint32_t* cw = static_cast<uint32_t*>(codes);
+  uint8_t* sb = static_cast<uint8_t*>(scales);
+  pass<FMT, kInit>(W, s, N, K, cw, sb, stream);
+  hipLaunchKernelGGL((dq_row_finalize_kernel<true>), gr, dim3(kThreads), 0, stream, s.row_a, s.row_b,
+                     N, KB, r, s.alpha);
+  hipLaunchKernelGGL((dq_col_finalize_kernel<true>), gc, dim3(kThreads), 0, stream, s.col_a, s.col_b,
+                     chunks, K, c, s.beta);
+  for (int t = 0; t < iters; ++t) {
+    pass<FMT, kRows>(W, s, N, K, cw, sb, stream);
+    hipLaunchKernelGGL((dq_row_finalize_kernel<false>), gr, dim3(kThreads), 0, stream, s.row_a,
+                       s.row_b, N, KB, r, s.alpha);
+    pass<FMT, kCols>(W, s, N, K, cw, sb, stream);
+    hipLaunchKernelGGL((dq_col_finalize_kernel<false>), gc, dim3(kThreads), 0, stream, s.col_a,
+                       s.col_b, chunks, K, c, s.beta);
+  }
+  pass<FMT, kEmit>(W, s, N, K, cw, sb, stream);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t solver_workspace_bytes(int64_t N, int64_t K) {
+  const int64_t KB = K / 32, chunks = (N + kChunk - 1) / kChunk;
+  return size_t(2 * align256(N * KB * 8) + 2 * align256(chunks * K * 8) + align256(N * 4) +
+                align256(K * 4));
+}
+
+hipError_t launch_dualquant_solve(int fmt, int64_t N, int64_t K, const float* W, int iters,
+                                  float* r, float* c, void* codes, void* scales, void* workspace,
+                                  hipStream_t stream) {
+  if (fmt == MXFP4) return solve<MXFP4>(N, K, W, iters, r, c, codes, scales, workspace, stream);
+  return solve<MXINT4>(N, K, W, iters, r, c, codes, scales, workspace, stream);
+}
+
+}  // namespace w4a4
