@@ -17,8 +17,9 @@ the GEMM kernel's roofline position (algorithmic flops per launch over its
 HIP-event-timed average duration, against the MI355X dense MXFP4 peak),
 decode weight-streaming bandwidth (MXFP4 Llama linears at M = 1, 4, 16,
 MXINT4 Qwen linears and NVFP4 Llama linears at M = 1, cycling 32 layer
-copies so that the 256 MB last-level cache cannot hold the weights), and the
-CPU oracle timed on a
+copies so that the 256 MB last-level cache cannot hold the weights), the
+offline dual-scale solver on fp32 weights of the Llama linears' shapes, and
+the CPU oracle timed on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -174,6 +175,40 @@ def time_graph(layers, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def solver_rate(dev, iters=15):
+    """The offline dual-scale solver (w4a4_dualquant_solve, MXFP4) on fp32
+    weights of each Llama linear's shape: synthetic N(0, 0.02) weights with
+    1/64 of the columns scaled x20 and lognormal column and row scales.  One
+    warm-up solve, then one timed solve per linear.  Every pass reads W once
+    (fp32), 2T + 2 passes per solve; the rate is those reads over the time
+    (the passes are HBM-bound), against 8 TB/s."""
+    g = torch.Generator(device="cpu").manual_seed(7)
+    out = {}
+    total = 0.0
+    for name, N, K in inputs.LLAMA_LINEARS:
+        w = torch.randn((N, K), generator=g) * 0.02
+        cols = torch.randperm(K, generator=g)[: K // 64]
+        w[:, cols] *= 20
+        w *= torch.exp(0.5 * torch.randn((1, K), generator=g)) * torch.exp(0.3 * torch.randn((N, 1), generator=g))
+        w = w.to(dev)
+        ws = torch.empty(w4.lib().w4a4_dualquant_workspace_bytes(0, N, K), dtype=torch.uint8, device=dev)
+        w4.dualquant_solve(w, "mxfp4", iters, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        w4.dualquant_solve(w, "mxfp4", iters, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        total += ms
+        rate = (2 * iters + 2) * 4.0 * N * K / (ms * 1e-3) / 1e9
+        out[name] = {"N": N, "K": K, "ms": round(ms, 3), "W_read_GB/s": round(rate, 1),
+                     "frac_of_8TBps": round(rate / 8000.0, 3)}
+        del w, ws
+        torch.cuda.empty_cache()
+    return {"format": "mxfp4", "iters": iters, "layer_ms": round(total, 3), "per_linear": out}
+
+
 def decode_bandwidth(dev, steps, workload="llama_decode", Ms=(1, 4, 16), copies=32):
     """Weight-streaming rate of the GEMM at small M (default: MXFP4 Llama
     shapes at M = 1, 4, 16).
@@ -316,6 +351,7 @@ def main():
     ap.add_argument("--M", type=int, default=None)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-solver", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB calibration copy and one pass of the kernels, print nothing")
     a = ap.parse_args()
@@ -374,6 +410,9 @@ def main():
         out["decode_hbm_qwen_mxint4"] = decode_bandwidth(dev, a.steps, "qwen_mxint4", (1,))
         torch.cuda.empty_cache()
         out["decode_hbm_llama_nvfp4"] = decode_bandwidth(dev, a.steps, "llama_nvfp4", (1,))
+    if not a.no_solver:
+        log("[bench] dual-scale solver")
+        out["dualquant_solver"] = solver_rate(dev)
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(a.workload, M)

@@ -21,7 +21,11 @@
 //   columns: a thread sums its column over a chunk of 16 rows in order; the
 //            column-finalize thread adds the chunk sums in order.
 // Per pass each element is read once (fp32 W), one grid covering W: threads
-// own 8 consecutive columns (one 32-byte read per row) of a 16-row chunk.
+// own 8 consecutive columns (one 32-byte read per row) of a 16-row chunk and
+// issue the 16 reads before any arithmetic.  R = Q^ / beta and S = Q^ / alpha
+// are fp64 quotients; once the scales are powers of two (every pass after the
+// first row pass: alpha = 1/r, beta = 1/c) the quotient equals the product
+// with the exact reciprocal, which the kernel uses instead of a division.
 #include "common.h"
 #include "kernels.h"
 #include "mx_quant.h"
@@ -30,7 +34,8 @@ namespace w4a4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 16;  // rows per column partial sum
+constexpr int kChunk = 16;  // rows per column partial sum (and per thread in those passes)
+constexpr int kRowTile = 4;  // rows per thread in the row and emit passes
 
 enum PassMode { kInit = 0, kRows = 1, kCols = 2, kEmit = 3 };
 
@@ -59,12 +64,12 @@ __device__ __forceinline__ double shfl_lane(double v, int src) {
   return __shfl(v, src, 64);
 }
 
-// One pass over W [N, K] fp32.  Grid x: 16-row chunks, grid y: 256-wide runs
-// of 8-column groups.  Rows: per (row, 32-block) fp64 sums of W*R and R*R
-// (lane 4q of the quad writes them).  Cols: per (chunk, column) fp64 sums of
+// One pass over W [N, K] fp32.  Grid x: chunks of ROWS rows (16 where column
+// sums are formed, 4 otherwise), grid y: 256-wide runs of 8-column groups.  Rows: per (32-block, row) fp64 sums of W*R and R*R,
+// block-major (lane 4q of the quad writes them).  Cols: per (chunk, column) fp64 sums of
 // W*S and S*S.  Init: per (row, 32-block) max |W| and per (chunk, column)
 // sum |W|.  Emit: codes and scales.
-template <int FMT, int MODE>
+template <int FMT, int MODE, bool DIV, int ROWS>
 __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
     const float* __restrict__ W, const float* __restrict__ alpha, const float* __restrict__ beta,
     int64_t N, int64_t K8, double* __restrict__ row_a, double* __restrict__ row_b,
@@ -74,22 +79,35 @@ __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
   const bool live_c = col_raw < K8;
   const int64_t col8 = live_c ? col_raw : K8 - 1;  // every lane joins the quad exchanges
   const int64_t K = K8 * 8, KB = K8 / 4;
-  const int64_t r0 = int64_t(blockIdx.x) * kChunk;
+  static_assert((MODE == kInit || MODE == kCols) == (ROWS == kChunk), "column sums per 16 rows");
+  const int64_t r0 = int64_t(blockIdx.x) * ROWS;
   const int lane = threadIdx.x & 63;
   const int quad0 = lane & ~3;
   float b8[8];
+  double ib8[8];  // exact reciprocals of the column scales (powers of two)
   if (MODE != kInit) {
     const float4 b0 = reinterpret_cast<const float4*>(beta)[2 * col8];
     const float4 b1 = reinterpret_cast<const float4*>(beta)[2 * col8 + 1];
     b8[0] = b0.x; b8[1] = b0.y; b8[2] = b0.z; b8[3] = b0.w;
     b8[4] = b1.x; b8[5] = b1.y; b8[6] = b1.z; b8[7] = b1.w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ib8[e] = 1.0 / double(b8[e]);
   }
   double ca[8], cb[8];  // column sums over this chunk
-  const int64_t rows = N - r0 < kChunk ? N - r0 : kChunk;
-  for (int64_t i = 0; i < rows; ++i) {
+  const int64_t rows = N - r0 < ROWS ? N - r0 : ROWS;
+  // all reads of the chunk in flight at once (rows past N re-read row N-1)
+  float4 wv[ROWS][2];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    const int64_t row = r0 + i < N ? r0 + i : N - 1;
+    wv[i][0] = reinterpret_cast<const float4*>(W + row * K)[2 * col8];
+    wv[i][1] = reinterpret_cast<const float4*>(W + row * K)[2 * col8 + 1];
+  }
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    if (i >= rows) break;
     const int64_t row = r0 + i;
-    const float4 w0 = reinterpret_cast<const float4*>(W + row * K)[2 * col8];
-    const float4 w1 = reinterpret_cast<const float4*>(W + row * K)[2 * col8 + 1];
+    const float4 w0 = wv[i][0], w1 = wv[i][1];
     const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     if (MODE == kInit) {
       float m = 0.0f;
@@ -101,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
       }
       m = fmaxf(m, quad_xor1(m));
       m = fmaxf(m, quad_xor2(m));
-      if (live_c && (col8 & 3) == 0) row_a[row * KB + (col8 >> 2)] = double(m);
+      if (live_c && (col8 & 3) == 0) row_a[(col8 >> 2) * N + row] = double(m);
       continue;
     }
     const float a = alpha[row];
@@ -122,7 +140,8 @@ __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
       double pa = 0.0, pb = 0.0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const double R = (code_value<FMT>((word >> (4 * e)) & 15u) * bscale) / double(b8[e]);
+        const double q = code_value<FMT>((word >> (4 * e)) & 15u) * bscale;
+        const double R = DIV ? q / double(b8[e]) : q * ib8[e];
         const double ta = double(w[e]) * R, tb = R * R;
         pa = e == 0 ? ta : pa + ta;
         pb = e == 0 ? tb : pb + tb;
@@ -132,13 +151,14 @@ __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
       const double b1 = shfl_lane(pb, quad0 + 1), b2 = shfl_lane(pb, quad0 + 2),
                    b3 = shfl_lane(pb, quad0 + 3);
       if (live_c && (col8 & 3) == 0) {
-        row_a[row * KB + (col8 >> 2)] = ((pa + a1) + a2) + a3;
-        row_b[row * KB + (col8 >> 2)] = ((pb + b1) + b2) + b3;
+        row_a[(col8 >> 2) * N + row] = ((pa + a1) + a2) + a3;
+        row_b[(col8 >> 2) * N + row] = ((pb + b1) + b2) + b3;
       }
     } else {  // kCols
+      const double ia = 1.0 / double(a);  // exact: alpha = 1/r is a power of two
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const double S = (code_value<FMT>((word >> (4 * e)) & 15u) * bscale) / double(a);
+        const double S = (code_value<FMT>((word >> (4 * e)) & 15u) * bscale) * ia;
         const double ta = double(w[e]) * S, tb = S * S;
         ca[e] = i == 0 ? ta : ca[e] + ta;
         cb[e] = i == 0 ? tb : cb[e] + tb;
@@ -155,6 +175,25 @@ __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
   }
 }
 
+// Sum of the n values p[0], p[stride], ... in order; loads go out kBatch at a
+// time ahead of the (sequential) additions.
+constexpr int kBatch = 16;
+
+__device__ __forceinline__ double ordered_sum(const double* __restrict__ p, int64_t n,
+                                              int64_t stride) {
+  double s = p[0];
+  int64_t k = 1;
+  for (; k + kBatch <= n; k += kBatch) {
+    double v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) v[u] = p[(k + u) * stride];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) s = s + v[u];
+  }
+  for (; k < n; ++k) s = s + p[k * stride];
+  return s;
+}
+
 // One thread per row.  Init: alpha_0 = 1 / max|W_i| (1 for a zero row).
 // Update: r_i = Pi(sum W*R / sum R*R), alpha_i = 1 / r_i (r = alpha = 1 when
 // the row's Q^ is all zero).
@@ -164,19 +203,14 @@ __global__ __launch_bounds__(kThreads) void dq_row_finalize_kernel(
     float* __restrict__ r, float* __restrict__ alpha) {
   const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= N) return;
-  const double* pa = row_a + i * KB;
   if (INIT) {
     double m = 0.0;
-    for (int64_t b = 0; b < KB; ++b) m = fmax(m, pa[b]);
+    for (int64_t b = 0; b < KB; ++b) m = fmax(m, row_a[b * N + i]);
     alpha[i] = m > 0.0 ? float(1.0 / m) : 1.0f;
     return;
   }
-  const double* pb = row_b + i * KB;
-  double num = pa[0], den = pb[0];
-  for (int64_t b = 1; b < KB; ++b) {
-    num = num + pa[b];
-    den = den + pb[b];
-  }
+  const double num = ordered_sum(row_a + i, KB, N);
+  const double den = ordered_sum(row_b + i, KB, N);
   const double ri = den > 0.0 ? project_e8m0(num / den) : 1.0;
   r[i] = float(ri);
   alpha[i] = float(1.0 / ri);
@@ -189,12 +223,8 @@ __global__ __launch_bounds__(kThreads) void dq_col_finalize_kernel(
     float* __restrict__ c, float* __restrict__ beta) {
   const int64_t j = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (j >= K) return;
-  double num = col_a[j];
-  double den = INIT ? 0.0 : col_b[j];
-  for (int64_t h = 1; h < chunks; ++h) {
-    num = num + col_a[h * K + j];
-    if (!INIT) den = den + col_b[h * K + j];
-  }
+  const double num = ordered_sum(col_a + j, chunks, K);
+  const double den = INIT ? 0.0 : ordered_sum(col_b + j, chunks, K);
   if (INIT) {
     beta[j] = num > 0.0 ? float(1.0 / num) : 1.0f;
     return;
@@ -228,12 +258,13 @@ SolverWs carve(void* ws, int64_t N, int64_t K) {
   return s;
 }
 
-template <int FMT, int MODE>
+template <int FMT, int MODE, bool DIV = false>
 void pass(const float* W, const SolverWs& s, int64_t N, int64_t K, uint32_t* codes,
           uint8_t* scales, hipStream_t stream) {
+  constexpr int ROWS = (MODE == kInit || MODE == kCols) ? kChunk : kRowTile;
   const int64_t K8 = K / 8;
-  const dim3 grid(unsigned((N + kChunk - 1) / kChunk), unsigned((K8 + kThreads - 1) / kThreads));
-  hipLaunchKernelGGL((dq_pass_kernel<FMT, MODE>), grid, dim3(kThreads), 0, stream, W, s.alpha,
+  const dim3 grid(unsigned((N + ROWS - 1) / ROWS), unsigned((K8 + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL((dq_pass_kernel<FMT, MODE, DIV, ROWS>), grid, dim3(kThreads), 0, stream, W, s.alpha,
                      s.beta, N, K8, s.row_a, s.row_b, s.col_a, s.col_b, codes, scales);
 }
 
@@ -251,7 +282,11 @@ hipError_t solve(int64_t N, int64_t K, const float* W, int iters, float* r, floa
   hipLaunchKernelGGL((dq_col_finalize_kernel<true>), gc, dim3(kThreads), 0, stream, s.col_a, s.col_b,
                      chunks, K, c, s.beta);
   for (int t = 0; t < iters; ++t) {
-    pass<FMT, kRows>(W, s, N, K, cw, sb, stream);
+    // beta_0 = 1 / l1 is not a power of two: the first row pass divides
+    if (t == 0)
+      pass<FMT, kRows, true>(W, s, N, K, cw, sb, stream);
+    else
+      pass<FMT, kRows>(W, s, N, K, cw, sb, stream);
     hipLaunchKernelGGL((dq_row_finalize_kernel<false>), gr, dim3(kThreads), 0, stream, s.row_a,
                        s.row_b, N, KB, r, s.alpha);
     pass<FMT, kCols>(W, s, N, K, cw, sb, stream);
