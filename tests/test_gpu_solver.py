@@ -101,3 +101,27 @@ def test_solver_full_size_properties(fmt):
     qr, sr, _ = oracle.quantize_rows(w[rows], fmt)
     rtn = S.mse(w[rows], np.ones(len(rows)), np.ones(K), oracle.dequantize(oracle.pack_nibbles(qr), sr, fmt))
     say(f"    sampled-row error {err:.4g}, round-to-nearest {rtn:.4g}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+def test_solver_feeds_the_linear(fmt):
+    """Offline solve, then the inference path with its outputs: the weight
+    packed from (codes, scales, r), the activations quantized with c (Section
+    4.4), the GEMM; against the oracle's layer built from the oracle solver."""
+    from gpu_common import bf16_bits, check_linear
+    dev = device()
+    N, K, M = 256, 1024, 48
+    w = weights(31, N, K)
+    x = np.random.default_rng(32).normal(0, 1, (M, K)).astype(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    r, c, codes, scales = w4.dualquant_solve(torch.from_numpy(w).to(dev), fmt, 15)
+    blob = w4.pack_weight(codes, scales, None, r, fmt)
+    ac, asc, ta = w4.quantize_act(xb.to(dev), c, fmt)
+    Y = w4.linear(ac, asc, ta, blob, fmt, N, K)
+    torch.cuda.synchronize()
+    r_o, c_o, codes_o, scales_o = S.solve(w, fmt, 15)
+    a_o, as_o, _ = oracle.quantize_act(xb.float().numpy(), c_o, fmt)
+    assert np.array_equal(ac.cpu().numpy(), a_o) and np.array_equal(asc.cpu().numpy(), as_o)
+    bits, y = oracle.linear_bf16(a_o, as_o, None, codes_o, scales_o, 1.0, r_o, fmt)
+    S_abs = oracle.linear.linear_abs_sum(a_o, as_o, None, codes_o, scales_o, 1.0, r_o, fmt)
+    check_linear(bf16_bits(Y), y, S_abs, K, f"solver+linear {fmt}")
