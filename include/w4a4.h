@@ -186,17 +186,19 @@ w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K,
                         void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * w4a4_dualquant_solve - the offline dual-scale solver for MXFP4 / MXINT4.
+ * w4a4_dualquant_solve - the offline dual-scale solver.
  *
  * DualQuant Algorithm 1 (Section 4.3, block coordinate descent with
  * closed-form scale updates; initialization and T from Section 5): finds the
- * row scales r (= alpha^-1) and column scales c (= beta^-1), both powers of
- * two (E8M0), and the codes Q = Q(Diag(alpha) W Diag(beta)) so that
- * W ~ Diag(r) Q Diag(c).  r and the codes/scales go to w4a4_pack_weight, c
- * to w4a4_quantize_act.  Starting from alpha_0 = 1 / row absmax and
+ * row scales r (= alpha^-1) and column scales c (= beta^-1) in the format's
+ * admissible set (powers of two, E8M0, for MXFP4 / MXINT4; positive E4M3
+ * values, UE4M3, for NVFP4) and the codes Q = Q(Diag(alpha) W Diag(beta)) so
+ * that W ~ Diag(r) Q Diag(c).  r, t_w and the codes/scales go to
+ * w4a4_pack_weight, c to w4a4_quantize_act.  Starting from alpha_0 = 1 / row absmax and
  * beta_0 = 1 / column l1 norm, each iteration sets r_i to the power of two
  * nearest to <W_i, R_i> / ||R_i||^2 with R = Q^ Diag(beta)^-1 (Q^ the
- * quantized rescaled weight), re-quantizes, then sets c_j likewise from
+ * quantized rescaled weight; for NVFP4 with the fp32 tensor scale of that
+ * rescaled weight, as in w4a4_quantize_act), re-quantizes, then sets c_j likewise from
  * S = Diag(alpha)^-1 Q^ over the columns.  A row or column whose Q^ is all
  * zero gets scale 1.  The inner products and norms are fp64 sums in a fixed
  * order (rows: 8 terms, then ((p0 + p1) + p2) + p3 per 32-block, then the
@@ -209,20 +211,23 @@ w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K,
  *   r        device, out, fp32 [N], 4-byte aligned.
  *   c        device, out, fp32 [K], 4-byte aligned.
  *   codes    device, out, [N x K/2] canonical codes, 4-byte aligned.
- *   scales   device, out, [N x K/32] E8M0 bytes.
+ *   scales   device, out, [N x K/G] scale bytes (E8M0; UE4M3 for NVFP4).
+ *   t_w      device, out, one fp32: the NVFP4 tensor scale of the returned
+ *            codes (required for NVFP4, not written for MX formats; may be
+ *            NULL there).
  *   workspace/ws_bytes: device scratch of at least
  *            w4a4_dualquant_workspace_bytes() bytes, 256-byte aligned
  *            (fp64 partial sums: 16 B per 32-block and per 16-row chunk and
  *            column, and the current scales); no initial contents needed.
  *
- * Requires fmt MXFP4 or MXINT4 (else W4A4_ERR_FORMAT), N > 0, K % 32 == 0,
- * N*K <= 2^36.  Kernels are enqueued on `stream`; nothing is allocated.
+ * Requires N > 0, K % 32 == 0 (for every format), N*K <= 2^36.  Kernels are
+ * enqueued on `stream`; nothing is allocated.
  */
 size_t w4a4_dualquant_workspace_bytes(w4a4_format fmt, int64_t N, int64_t K);
 w4a4_status w4a4_dualquant_solve(w4a4_format fmt, int64_t N, int64_t K,
                                  const float* W, int iters, float* r, float* c,
-                                 void* codes, void* scales, void* workspace,
-                                 size_t ws_bytes, void* stream);
+                                 void* codes, void* scales, float* t_w,
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* w4a4_last_error(void);

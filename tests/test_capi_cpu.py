@@ -160,29 +160,33 @@ def test_empty_linear_is_a_no_op():
 
 def test_dualquant_workspace_bytes():
     """fp64 partial sums per (row, 32-block) and per (16-row chunk, column),
-    two of each, and the current fp32 scales, each 256-byte aligned."""
+    two of each, the current fp32 scales, 1024 partial maxima and the tensor
+    scale (NVFP4), each 256-byte aligned."""
     L = w4.lib()
 
     def a256(x):
         return (x + 255) // 256 * 256
 
     for N, K in [(64, 256), (100, 4096), (4096, 14336)]:
-        want = 2 * a256(N * (K // 32) * 8) + 2 * a256((N + 15) // 16 * K * 8) + a256(4 * N) + a256(4 * K)
-        assert L.w4a4_dualquant_workspace_bytes(0, N, K) == want
-        assert L.w4a4_dualquant_workspace_bytes(2, N, K) == want
-    assert L.w4a4_dualquant_workspace_bytes(1, 64, 256) == 0      # NVFP4: not covered
+        want = (2 * a256(N * (K // 32) * 8) + 2 * a256((N + 15) // 16 * K * 8) + a256(4 * N) +
+                a256(4 * K) + 4096 + 256)
+        for fmt in (0, 1, 2):
+            assert L.w4a4_dualquant_workspace_bytes(fmt, N, K) == want
+    assert L.w4a4_dualquant_workspace_bytes(9, 64, 256) == 0      # unknown format
     assert L.w4a4_dualquant_workspace_bytes(0, 64, 48) == 0       # K % 32
     assert L.w4a4_dualquant_workspace_bytes(0, 0, 256) == 0
 
 
 @pytest.mark.parametrize("args,status", [
-    ((1, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 4),      # NVFP4
-    ((0, 64, 48, FAKE, 15, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 2),       # K % 32
-    ((0, 64, 256, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 2),       # iters < 1
-    ((0, 64, 256, None, 15, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 1),      # W NULL
-    ((0, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, None, 1 << 30, None), 5),      # no workspace
-    ((0, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, None), 5),         # short
-    ((0, 64, 256, FAKE_MIS, 15, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 3),  # W 16-byte
+    ((9, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 4),      # format
+    ((0, 64, 48, FAKE, 15, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None), 2),       # K % 32
+    ((1, 64, 48, FAKE, 15, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None), 2),       # NVFP4 K % 32
+    ((0, 64, 256, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None), 2),       # iters < 1
+    ((0, 64, 256, None, 15, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None), 1),      # W NULL
+    ((1, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None), 1),      # NVFP4 t_w
+    ((0, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, None, None, 1 << 30, None), 5),      # no workspace
+    ((0, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1024, None), 5),         # short
+    ((0, 64, 256, FAKE_MIS, 15, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None), 3),  # W 16-byte
 ])
 def test_dualquant_solve_rejects(args, status):
     L = w4.lib()

@@ -1,13 +1,14 @@
-"""GPU parity of the dual-scale solver (w4a4_dualquant_solve, MX formats).
+"""GPU parity of the dual-scale solver (w4a4_dualquant_solve).
 
 The solver's decisions (projections of fp64 sums, block quantization of the
 rescaled weight) are taken in the same precision and summation order as the
-oracle's, so r, c, codes and scales must equal the oracle's exactly.  At a
-full Llama size, where the oracle's full run is too slow, properties that
-hold at any size once Q^ has stabilized are checked: r and c are powers of
-two, the codes are the quantization of Diag(1/r) W Diag(1/c) (oracle
-quantizer on sampled rows), and r and c are fixed points of the oracle's
-closed-form updates for those codes (rows sampled, columns over all rows)."""
+oracle's, so r, c, codes, scales and (NVFP4) t_w must equal the oracle's
+exactly.  At a full Llama size, where the oracle's full run is too slow,
+properties that hold at any size are checked: r and c lie in the admissible
+set, the codes (and t_w) are the quantization of Diag(1/r) W Diag(1/c)
+(oracle quantizer on sampled rows), and, for the MX formats, whose Q^
+stabilizes, r and c are fixed points of the oracle's closed-form updates for
+those codes (rows sampled, columns over all rows)."""
 import numpy as np
 import pytest
 import torch
@@ -34,9 +35,10 @@ def weights(seed, N, K, zero_row=None, zero_col=None):
 
 
 def gpu_solve(w, fmt, iters, dev):
-    r, c, codes, scales = w4.dualquant_solve(torch.from_numpy(w).to(dev), fmt, iters)
+    r, c, codes, scales, t_w = w4.dualquant_solve(torch.from_numpy(w).to(dev), fmt, iters)
     torch.cuda.synchronize()
-    return r.cpu().numpy(), c.cpu().numpy(), codes.cpu().numpy(), scales.cpu().numpy()
+    t = np.float32(t_w.item()) if t_w is not None else np.float32(1.0)
+    return r.cpu().numpy(), c.cpu().numpy(), codes.cpu().numpy(), scales.cpu().numpy(), t
 
 
 # (N, K, iters, zero row, zero column): ragged 16-row chunks, one 32-block,
@@ -51,14 +53,15 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4", "nvfp4"])
 @pytest.mark.parametrize("N,K,iters,zr,zc", CASES)
 def test_solver_matches_oracle(fmt, N, K, iters, zr, zc):
     dev = device()
     say(f"[solver] {fmt} N={N} K={K} T={iters}")
     w = weights(N * 7 + K, N, K, zr, zc)
-    r, c, codes, scales = gpu_solve(w, fmt, iters, dev)
-    r_o, c_o, codes_o, scales_o = S.solve(w, fmt, iters)
+    r, c, codes, scales, t = gpu_solve(w, fmt, iters, dev)
+    r_o, c_o, codes_o, scales_o, t_o = S.solve(w, fmt, iters)
+    assert t == t_o
     assert np.array_equal(r, r_o), f"{(r != r_o).sum()} of {N} row scales differ"
     assert np.array_equal(c, c_o), f"{(c != c_o).sum()} of {K} column scales differ"
     assert np.array_equal(scales, scales_o), f"{(scales != scales_o).sum()} scales differ"
@@ -69,41 +72,45 @@ def test_solver_repeated_calls_are_identical():
     dev = device()
     w = weights(3, 128, 512)
     a = gpu_solve(w, "mxfp4", 5, dev)
-    b = gpu_solve(weights(4, 64, 256), "mxint4", 5, dev)
+    b = gpu_solve(weights(4, 64, 256), "nvfp4", 5, dev)
     a2 = gpu_solve(w, "mxfp4", 5, dev)
     assert all(np.array_equal(x, y) for x, y in zip(a, a2))
     assert b[0].shape == (64,)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4", "nvfp4"])
 def test_solver_full_size_properties(fmt):
     """Llama O projection size (4096 x 4096), T = 15."""
     dev = device()
     N, K = 4096, 4096
     say(f"[solver full] {fmt} N={N} K={K}")
     w = weights(11, N, K)
-    r, c, codes, scales = gpu_solve(w, fmt, 15, dev)
+    r, c, codes, scales, t = gpu_solve(w, fmt, 15, dev)
     for v in (r, c):
-        m, _ = np.frexp(v)
-        assert np.all(m == 0.5) and np.all(v > 0)
+        if fmt == "nvfp4":
+            assert np.all(np.isin(v.astype(np.float64), S.E4M3_POS))
+        else:
+            m, _ = np.frexp(v)
+            assert np.all(m == 0.5) and np.all(v > 0)
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 24, replace=False)]))
     alpha = (1.0 / r.astype(np.float64)).astype(np.float32)
     beta = (1.0 / c.astype(np.float64)).astype(np.float32)
-    oc, osc, _ = oracle.quantize_rows(S.rescaled(w[rows], alpha[rows], beta), fmt)
+    # NVFP4: the tensor scale is over the whole W~, so it is given to the row sample
+    t_all = oracle.nv_tensor_scale(S.rescaled(w, alpha, beta)) if fmt == "nvfp4" else None
+    oc, osc, _ = oracle.quantize_rows(S.rescaled(w[rows], alpha[rows], beta), fmt, t=t_all)
     assert np.array_equal(codes[rows], oracle.pack_nibbles(oc))
     assert np.array_equal(scales[rows], osc)
+    if fmt == "nvfp4":
+        assert t == t_all
+        return
     q = oracle.dequantize(codes[rows], scales[rows], fmt)
     assert np.array_equal(S.row_update(w[rows], q, beta).astype(np.float32), r[rows])
     q_all = oracle.dequantize(codes, scales, fmt)
     assert np.array_equal(S.col_update(w, q_all, alpha).astype(np.float32), c)
-    err = S.mse(w[rows], r[rows], c, q)
-    qr, sr, _ = oracle.quantize_rows(w[rows], fmt)
-    rtn = S.mse(w[rows], np.ones(len(rows)), np.ones(K), oracle.dequantize(oracle.pack_nibbles(qr), sr, fmt))
-    say(f"    sampled-row error {err:.4g}, round-to-nearest {rtn:.4g}")
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4", "nvfp4"])
 def test_solver_feeds_the_linear(fmt):
     """Offline solve, then the inference path with its outputs: the weight
     packed from (codes, scales, r), the activations quantized with c (Section
@@ -114,14 +121,14 @@ def test_solver_feeds_the_linear(fmt):
     w = weights(31, N, K)
     x = np.random.default_rng(32).normal(0, 1, (M, K)).astype(np.float32)
     xb = torch.from_numpy(x).to(torch.bfloat16)
-    r, c, codes, scales = w4.dualquant_solve(torch.from_numpy(w).to(dev), fmt, 15)
-    blob = w4.pack_weight(codes, scales, None, r, fmt)
+    r, c, codes, scales, t_w = w4.dualquant_solve(torch.from_numpy(w).to(dev), fmt, 15)
+    blob = w4.pack_weight(codes, scales, t_w, r, fmt)
     ac, asc, ta = w4.quantize_act(xb.to(dev), c, fmt)
     Y = w4.linear(ac, asc, ta, blob, fmt, N, K)
     torch.cuda.synchronize()
-    r_o, c_o, codes_o, scales_o = S.solve(w, fmt, 15)
-    a_o, as_o, _ = oracle.quantize_act(xb.float().numpy(), c_o, fmt)
+    r_o, c_o, codes_o, scales_o, tw_o = S.solve(w, fmt, 15)
+    a_o, as_o, ta_o = oracle.quantize_act(xb.float().numpy(), c_o, fmt)
     assert np.array_equal(ac.cpu().numpy(), a_o) and np.array_equal(asc.cpu().numpy(), as_o)
-    bits, y = oracle.linear_bf16(a_o, as_o, None, codes_o, scales_o, 1.0, r_o, fmt)
-    S_abs = oracle.linear.linear_abs_sum(a_o, as_o, None, codes_o, scales_o, 1.0, r_o, fmt)
+    bits, y = oracle.linear_bf16(a_o, as_o, ta_o, codes_o, scales_o, tw_o, r_o, fmt)
+    S_abs = oracle.linear.linear_abs_sum(a_o, as_o, ta_o, codes_o, scales_o, tw_o, r_o, fmt)
     check_linear(bf16_bits(Y), y, S_abs, K, f"solver+linear {fmt}")

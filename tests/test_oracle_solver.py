@@ -3,13 +3,34 @@ what the mathematics fixes: the projection against a brute-force search of
 the admissible set, the closed-form updates against 1-D least squares and a
 brute-force search of the projected objective (Appendix C, Remark 1), the
 descent guarantee once Q^ has stabilized (Theorem 1), the degenerate-row
-convention, the initialization, and exact power-of-two equivariance."""
+convention, the initialization, and exact power-of-two equivariance (MX).
+For NVFP4 the admissible set is the positive E4M3 values."""
 import numpy as np
 import pytest
 
 from oracle import solver as S
 
 E8M0 = np.ldexp(1.0, np.arange(-127, 128))
+# positive finite E4M3 values with their codes, from the bit layout
+E4M3 = [(np.ldexp(float(m), -9) if e == 0 else np.ldexp(float(8 + m), e - 10), 8 * e + m)
+        for e in range(16) for m in range(8) if 0 < 8 * e + m < 127]
+
+
+def brute_nearest_e4m3(u):
+    """argmin over the positive E4M3 values of |u - v|, ties to the even code."""
+    out = []
+    for x in np.asarray(u, np.float64):
+        d = [(abs(v - x), code % 2, v) for v, code in E4M3]
+        out.append(min(d)[2])
+    return np.array(out)
+
+
+def candidates(fmt):
+    return np.array([v for v, _ in E4M3]) if fmt == "nvfp4" else E8M0
+
+
+def brute(fmt, u):
+    return brute_nearest_e4m3(u) if fmt == "nvfp4" else brute_nearest_e8m0(u)
 
 
 def brute_nearest_e8m0(u):
@@ -45,6 +66,16 @@ def test_project_e8m0_matches_brute_force():
     assert np.array_equal(S.project_e8m0(x), brute_nearest_e8m0(x))
 
 
+def test_project_ue4m3_matches_brute_force():
+    rng = np.random.default_rng(7)
+    vals = np.array([v for v, _ in E4M3])
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    x = np.concatenate([np.ldexp(rng.uniform(0.5, 1.0, 3000), rng.integers(-14, 11, 3000)),
+                        mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf), vals,
+                        [0.0, -2.0, 2.0 ** -11, 2.0 ** -10, 450.0, 480.0, 1e9]])
+    assert np.array_equal(S.project_ue4m3(x), brute_nearest_e4m3(x))
+
+
 def test_fixed_order_sums_are_sums():
     rng = np.random.default_rng(1)
     P = rng.normal(size=(70, 96))
@@ -73,7 +104,7 @@ def sum_seq(v):
     return acc
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4", "nvfp4"])
 def test_row_update_is_projected_least_squares(fmt):
     """For fixed Q^ and beta, the row scale minimizes the row's squared error
     over the admissible set: the unconstrained minimizer is the 1-D least
@@ -83,7 +114,7 @@ def test_row_update_is_projected_least_squares(fmt):
     alpha = np.ldexp(1.0, rng.integers(-2, 3, 24)).astype(np.float32) * np.float32(7.3)
     beta = np.exp(rng.normal(0, 0.7, 128)).astype(np.float32)
     q = S.qhat(w, alpha, beta, fmt)
-    r = S.row_update(w, q, beta)
+    r = S.row_update(w, q, beta, fmt)
     R = q / beta.astype(np.float64)[None, :]
     wd = w.astype(np.float64)
     for i in range(24):
@@ -92,19 +123,19 @@ def test_row_update_is_projected_least_squares(fmt):
             continue
         ls = np.linalg.lstsq(R[i][:, None], wd[i], rcond=None)[0][0]
         assert np.isclose(ls, np.dot(wd[i], R[i]) / np.dot(R[i], R[i]), rtol=1e-12)
-        assert r[i] == brute_nearest_e8m0([ls])[0]
-        err = [np.sum((wd[i] - v * R[i]) ** 2) for v in E8M0]
+        assert r[i] == brute(fmt, [ls])[0]
+        err = [np.sum((wd[i] - v * R[i]) ** 2) for v in candidates(fmt)]
         assert np.sum((wd[i] - r[i] * R[i]) ** 2) <= min(err) * (1 + 1e-12)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4", "nvfp4"])
 def test_col_update_is_projected_least_squares(fmt):
     w = synthetic_weights(4, N=40, K=64)
     rng = np.random.default_rng(5)
     alpha = np.exp(rng.normal(0, 0.5, 40)).astype(np.float32)
     beta = np.ldexp(1.0, rng.integers(-3, 3, 64)).astype(np.float32)
     q = S.qhat(w, alpha, beta, fmt)
-    c = S.col_update(w, q, alpha)
+    c = S.col_update(w, q, alpha, fmt)
     Sm = q / alpha.astype(np.float64)[:, None]
     wd = w.astype(np.float64)
     for j in range(64):
@@ -112,8 +143,8 @@ def test_col_update_is_projected_least_squares(fmt):
             assert c[j] == 1.0
             continue
         ls = np.dot(wd[:, j], Sm[:, j]) / np.dot(Sm[:, j], Sm[:, j])
-        assert c[j] == brute_nearest_e8m0([ls])[0]
-        err = [np.sum((wd[:, j] - v * Sm[:, j]) ** 2) for v in E8M0]
+        assert c[j] == brute(fmt, [ls])[0]
+        err = [np.sum((wd[:, j] - v * Sm[:, j]) ** 2) for v in candidates(fmt)]
         assert np.sum((wd[:, j] - c[j] * Sm[:, j]) ** 2) <= min(err) * (1 + 1e-12)
 
 
@@ -121,7 +152,8 @@ def test_col_update_is_projected_least_squares(fmt):
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_descent_after_stabilization(fmt, seed):
     """Theorem 1 (i): once Q^ no longer changes, every half-step keeps or
-    lowers the objective."""
+    lowers the objective.  (MX only: with NVFP4 the tensor scale of W~ moves
+    with every rescaling, so Q^ need not stabilize.)"""
     w = synthetic_weights(10 + seed)
     hist = []
     S.solve(w, fmt, 6, hist)
@@ -135,8 +167,8 @@ def test_degenerate_rows_and_columns():
     w = synthetic_weights(20)
     w[5] = 0
     w[:, 7] = 0
-    for fmt in ("mxfp4", "mxint4"):
-        r, c, codes, scales = S.solve(w, fmt, 3)
+    for fmt in ("mxfp4", "mxint4", "nvfp4"):
+        r, c, codes, scales, _ = S.solve(w, fmt, 3)
         assert r[5] == 1.0 and c[7] == 1.0
         assert not np.any(codes[5]) and scales[5].max() == 0
 
@@ -155,8 +187,8 @@ def test_power_of_two_equivariance(fmt):
     quantizer is equivariant under powers of two, so r and c scale by 2^k and
     the codes stay the same (the reconstruction scales by 2^k)."""
     w = synthetic_weights(22)
-    r, c, codes, scales = S.solve(w, fmt, 4)
-    r2, c2, codes2, scales2 = S.solve(np.ldexp(w, 3).astype(np.float32), fmt, 4)
+    r, c, codes, scales, _ = S.solve(w, fmt, 4)
+    r2, c2, codes2, scales2, _ = S.solve(np.ldexp(w, 3).astype(np.float32), fmt, 4)
     assert np.array_equal(r2, np.ldexp(r, 3)) and np.array_equal(c2, np.ldexp(c, 3))
     assert np.array_equal(codes2, codes)
     assert np.array_equal(scales2.astype(int), scales.astype(int) - 3)

@@ -70,7 +70,7 @@ def lib() -> ctypes.CDLL:
     L.w4a4_linear.restype = i32
     L.w4a4_dualquant_workspace_bytes.argtypes = [i32, i64, i64]
     L.w4a4_dualquant_workspace_bytes.restype = sz
-    L.w4a4_dualquant_solve.argtypes = [i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.w4a4_dualquant_solve.argtypes = [i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.w4a4_dualquant_solve.restype = i32
     L.w4a4_last_error.argtypes = []
     L.w4a4_last_error.restype = ctypes.c_char_p
@@ -203,9 +203,10 @@ def linear(a_codes: torch.Tensor, a_scales: torch.Tensor, t_act: Optional[torch.
 
 
 def dualquant_solve(w: torch.Tensor, fmt, iters: int = 15, workspace: Optional[torch.Tensor] = None):
-    """w4a4_dualquant_solve: fp32 weights [N, K] -> (r [N], c [K], codes [N, K/2], scales [N, K/32]).
+    """w4a4_dualquant_solve: fp32 weights [N, K] -> (r [N], c [K], codes [N, K/2],
+    scales [N, K/G], t_w [1] for NVFP4 else None).
 
-    The offline dual-scale solver (MXFP4, MXINT4); W ~ diag(r) Q diag(c).
+    The offline dual-scale solver; W ~ diag(r) Q diag(c) (x t_w for NVFP4).
     Without `workspace`, one of w4a4_dualquant_workspace_bytes() bytes is
     allocated here.
     """
@@ -220,8 +221,9 @@ def dualquant_solve(w: torch.Tensor, fmt, iters: int = 15, workspace: Optional[t
     r = torch.empty(N, dtype=torch.float32, device=w.device)
     c = torch.empty(K, dtype=torch.float32, device=w.device)
     codes = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
-    scales = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, K // block_size(fmt)), dtype=torch.uint8, device=w.device)
+    t_w = torch.ones(1, dtype=torch.float32, device=w.device) if f == FORMATS["nvfp4"] else None
     _check(L.w4a4_dualquant_solve(f, N, K, _ptr(w), int(iters), _ptr(r), _ptr(c), _ptr(codes),
-                                  _ptr(scales), _ptr(workspace), workspace.numel(),
+                                  _ptr(scales), _ptr(t_w), _ptr(workspace), workspace.numel(),
                                   _stream(w.device)))
-    return r, c, codes, scales
+    return r, c, codes, scales, t_w

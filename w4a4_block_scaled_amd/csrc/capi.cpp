@@ -156,34 +156,33 @@ w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K, const 
 }
 
 size_t w4a4_dualquant_workspace_bytes(w4a4_format fmt, int64_t N, int64_t K) {
-  if ((fmt != W4A4_MXFP4 && fmt != W4A4_MXINT4) || N <= 0 || K <= 0 || K % 32 ||
+  if (!valid_fmt(fmt) || N <= 0 || K <= 0 || K % 32 ||
       N * K > (int64_t(1) << 36))
     return 0;
   return w4a4::solver_workspace_bytes(N, K);
 }
 
 w4a4_status w4a4_dualquant_solve(w4a4_format fmt, int64_t N, int64_t K, const float* W, int iters,
-                                 float* r, float* c, void* codes, void* scales, void* workspace,
-                                 size_t ws_bytes, void* stream) {
-  if (fmt != W4A4_MXFP4 && fmt != W4A4_MXINT4)
-    return fail(W4A4_ERR_FORMAT, "dualquant_solve: format %d (the solver covers MXFP4 and MXINT4)",
-                int(fmt));
+                                 float* r, float* c, void* codes, void* scales, float* t_w,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
   if (N <= 0 || K <= 0 || K % 32 || N * K > (int64_t(1) << 36) || iters < 1)
     return fail(W4A4_ERR_SHAPE,
                 "dualquant_solve: N=%lld K=%lld iters=%d (need N > 0, K > 0, K %% 32 == 0, "
                 "N*K <= 2^36, iters >= 1)",
                 (long long)N, (long long)K, iters);
-  if (!W || !r || !c || !codes || !scales)
-    return fail(W4A4_ERR_NULL, "dualquant_solve: W, r, c, codes and scales must be non-NULL");
+  if (!W || !r || !c || !codes || !scales || (fmt == W4A4_NVFP4 && !t_w))
+    return fail(W4A4_ERR_NULL,
+                "dualquant_solve: W, r, c, codes, scales (and t_w for NVFP4) must be non-NULL");
   const size_t need = w4a4::solver_workspace_bytes(N, K);
   if (!workspace || ws_bytes < need)
     return fail(W4A4_ERR_WORKSPACE, "dualquant_solve: needs %zu workspace bytes, got %zu", need,
                 workspace ? ws_bytes : size_t(0));
   if (!aligned(W, 16) || !aligned(r, 4) || !aligned(c, 4) || !aligned(codes, 4) ||
-      !aligned(workspace, 256))
+      (t_w && !aligned(t_w, 4)) || !aligned(workspace, 256))
     return fail(W4A4_ERR_ALIGN,
-                "dualquant_solve: W 16-byte, r/c/codes 4-byte, workspace 256-byte alignment");
-  return hip_status(w4a4::launch_dualquant_solve(fmt, N, K, W, iters, r, c, codes, scales,
+                "dualquant_solve: W 16-byte, r/c/codes/t_w 4-byte, workspace 256-byte alignment");
+  return hip_status(w4a4::launch_dualquant_solve(fmt, N, K, W, iters, r, c, codes, scales, t_w,
                                                  workspace, static_cast<hipStream_t>(stream)),
                     "dualquant_solve launch");
 }

@@ -29,11 +29,11 @@ hipError_t launch_linear(int fmt, int64_t M, int64_t N, int64_t K, const void* a
 
 size_t linear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
-// DualQuant's dual-scale solver (MX formats): workspace bytes and launch.
+// DualQuant's dual-scale solver: workspace bytes and launch.
 size_t solver_workspace_bytes(int64_t N, int64_t K);
 
 hipError_t launch_dualquant_solve(int fmt, int64_t N, int64_t K, const float* W, int iters,
-                                  float* r, float* c, void* codes, void* scales, void* workspace,
-                                  hipStream_t stream);
+                                  float* r, float* c, void* codes, void* scales, float* t_w,
+                                  void* workspace, hipStream_t stream);
 
 }  // namespace w4a4

@@ -16,6 +16,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "mx_quant.h"
+#include "nv_quant.h"
 
 namespace w4a4 {
 namespace {
@@ -141,42 +142,6 @@ __global__ __launch_bounds__(kThreads) void tensor_scale_kernel(const float* __r
   }
 }
 
-__device__ __forceinline__ double e4m3_value(int code) {
-  const int e = code >> 3, m = code & 7;
-  return e == 0 ? ldexp(double(m), -9) : ldexp(double(8 + m), e - 10);
-}
-
-// UE4M3 code of the exact quotient a / D (a >= 0 finite fp32, D > 0), round
-// to nearest even, saturating at 448 (0x7E).  A first guess from the rounded
-// fp64 quotient is settled by one exact comparison against the midpoint above
-// it (a and midpoint * D are exact in fp64).
-__device__ __forceinline__ int e4m3_rne_ratio(float a, double D) {
-  if (!(a > 0.0f)) return 0;
-  const double u = double(a) / D;
-  if (u >= 448.0) return 0x7e;
-  int c;
-  if (u < 0.015625) {
-    c = int(u * 512.0);  // subnormal codes 0..7
-  } else {
-    const uint64_t b = uint64_t(__double_as_longlong(u));
-    const int E = int((b >> 52) & 0x7ff) - 1023;  // -6 .. 8
-    c = ((E + 7) << 3) | int((b >> 49) & 7);
-  }
-  const double thr = 0.5 * (e4m3_value(c) + e4m3_value(c + 1)) * D;
-  const double ad = double(a);
-  if (ad > thr) return c + 1;
-  if (ad == thr) return ((c + 1) & 1) ? c : c + 1;
-  return c;
-}
-
-// Smallest fp32 >= T (T >= 0, exact double).  With strict = true: smallest
-// fp32 > T.  Turns "|x| > T" / "|x| >= T" for fp32 |x| into "|x| >= result".
-__device__ __forceinline__ float f32_threshold(double T, bool strict) {
-  float f = float(T);
-  if (double(f) < T || (strict && double(f) == T)) f = nextafterf(f, INFINITY);
-  return f;
-}
-
 __global__ __launch_bounds__(kThreads) void quantize_nv_kernel(
     const uint4* __restrict__ X, const float* __restrict__ c, const float* __restrict__ t_ptr,
     uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t n_groups, int64_t K8) {
@@ -188,35 +153,9 @@ __global__ __launch_bounds__(kThreads) void quantize_nv_kernel(
 
   float x[8];
   load8(X, c, g, col8, x);
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 1));
-
-  const float t = *t_ptr;
-  const int s = e4m3_rne_ratio(amax, 6.0 * double(t));  // 6 t is exact in fp64
-
-  uint32_t word = 0;
-  if (s == 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) word |= ((__float_as_uint(x[i]) >> 28) & 8u) << (4 * i);
-  } else {
-    const double unit = e4m3_value(s) * double(t);  // exact: 4 + 24 significant bits
-    const float t0 = f32_threshold(0.25 * unit, true);
-    const float t1 = f32_threshold(0.75 * unit, false);
-    const float t2 = f32_threshold(1.25 * unit, true);
-    const float t3 = f32_threshold(1.75 * unit, false);
-    const float t4 = f32_threshold(2.5 * unit, true);
-    const float t5 = f32_threshold(3.5 * unit, false);
-    const float t6 = f32_threshold(5.0 * unit, true);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float a = fabsf(x[i]);
-      const uint32_t idx = (a >= t0) + (a >= t1) + (a >= t2) + (a >= t3) + (a >= t4) +
-                           (a >= t5) + (a >= t6);
-      word |= (idx | ((__float_as_uint(x[i]) >> 28) & 8u)) << (4 * i);
-    }
-  }
+  uint32_t word;
+  int s;
+  quant8_nv(x, *t_ptr, word, s);
   if (!live) return;
   codes[g] = word;
   if ((col8 & 1) == 0) scales[row * (K8 / 2) + (col8 >> 1)] = uint8_t(s);

@@ -1,4 +1,4 @@
-// DualQuant's offline dual-scale solver for the MX formats on gfx950.
+// DualQuant's offline dual-scale solver on gfx950 (MXFP4, MXINT4, NVFP4).
 //
 // Algorithm 1 of the DualQuant paper (Section 4.3, block coordinate descent
 // with closed-form scale updates): starting from alpha_0 = 1 / row absmax and
@@ -11,7 +11,11 @@
 //   - re-quantizes with the new alpha, forms S = Diag(alpha)^-1 Q^ and sets
 //     c_j = beta_j^-1 likewise over the columns.
 // A final pass emits Q(Diag(alpha) W Diag(beta)) as canonical codes and
-// scales; W ~ Diag(r) Q Diag(c).
+// scales; W ~ Diag(r) Q Diag(c).  The scales are projected to powers of two
+// (E8M0) for the MX formats and to positive E4M3 values (UE4M3) for NVFP4,
+// whose quantizer also takes the fp32 tensor scale of the W~ it quantizes:
+// an amax pass over W~ precedes each NVFP4 quantization, and the last one
+// gives the returned t_w.
 //
 // Every projection is a discrete decision taken on fp64 sums, so the sums
 // follow one fixed order (which a CPU restatement can follow too):
@@ -29,6 +33,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "mx_quant.h"
+#include "nv_quant.h"
 
 namespace w4a4 {
 namespace {
@@ -60,6 +65,30 @@ __device__ __forceinline__ double project_e8m0(double u) {
   return fmin(fmax(near, 0x1p-127), 0x1p127);
 }
 
+// Nearest positive finite E4M3 value to u in linear distance, ties to the
+// even code; saturating at 448; u at or below 2^-9 (or NaN) gives 2^-9.
+__device__ __forceinline__ double project_ue4m3(double u) {
+  if (!(u > 0x1p-9)) return 0x1p-9;
+  if (u >= 448.0) return 448.0;
+  int c;  // value(c) <= u < value(c + 1)
+  if (u < 0.015625) {
+    c = int(u * 512.0);  // subnormal codes 1..7
+  } else {
+    const uint64_t b = uint64_t(__double_as_longlong(u));
+    const int E = int((b >> 52) & 0x7ff) - 1023;  // -6 .. 8
+    c = ((E + 7) << 3) | int((b >> 49) & 7);
+  }
+  const double lo = e4m3_value(c), hi = e4m3_value(c + 1), mid = 0.5 * (lo + hi);
+  if (u > mid) return hi;
+  if (u < mid) return lo;
+  return (c & 1) ? hi : lo;
+}
+
+template <int FMT>
+__device__ __forceinline__ double project_scale(double u) {
+  return FMT == NVFP4 ? project_ue4m3(u) : project_e8m0(u);
+}
+
 __device__ __forceinline__ double shfl_lane(double v, int src) {
   return __shfl(v, src, 64);
 }
@@ -72,7 +101,8 @@ __device__ __forceinline__ double shfl_lane(double v, int src) {
 template <int FMT, int MODE, bool DIV, int ROWS>
 __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
     const float* __restrict__ W, const float* __restrict__ alpha, const float* __restrict__ beta,
-    int64_t N, int64_t K8, double* __restrict__ row_a, double* __restrict__ row_b,
+    const float* __restrict__ tsc, int64_t N, int64_t K8, double* __restrict__ row_a,
+    double* __restrict__ row_b,
     double* __restrict__ col_a, double* __restrict__ col_b, uint32_t* __restrict__ codes,
     uint8_t* __restrict__ scales) {
   const int64_t col_raw = int64_t(blockIdx.y) * kThreads + threadIdx.x;
@@ -127,15 +157,25 @@ __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(__fmul_rn(a, w[e]), b8[e]);
     uint32_t word, sbyte;
-    quant8_mx<FMT>(x, word, sbyte);
+    double bscale;  // block scale (times t for NVFP4), exact
+    if constexpr (FMT == NVFP4) {
+      const float t = *tsc;
+      int sc;
+      quant8_nv(x, t, word, sc);
+      sbyte = uint32_t(sc);
+      bscale = e4m3_value(sc) * double(t);
+    } else {
+      quant8_mx<FMT>(x, word, sbyte);
+      bscale = ldexp(1.0, int(sbyte) - 127);
+    }
     if (MODE == kEmit) {
       if (live_c) {
         codes[row * K8 + col8] = word;
-        if ((col8 & 3) == 0) scales[row * KB + (col8 >> 2)] = uint8_t(sbyte);
+        if (FMT == NVFP4 && (col8 & 1) == 0) scales[row * (K8 / 2) + (col8 >> 1)] = uint8_t(sbyte);
+        if (FMT != NVFP4 && (col8 & 3) == 0) scales[row * KB + (col8 >> 2)] = uint8_t(sbyte);
       }
       continue;
     }
-    const double bscale = ldexp(1.0, int(sbyte) - 127);
     if (MODE == kRows) {
       double pa = 0.0, pb = 0.0;
 #pragma unroll
@@ -155,10 +195,11 @@ __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
         row_b[(col8 >> 2) * N + row] = ((pb + b1) + b2) + b3;
       }
     } else {  // kCols
-      const double ia = 1.0 / double(a);  // exact: alpha = 1/r is a power of two
+      const double ia = 1.0 / double(a);  // exact for MX: alpha = 1/r is a power of two
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const double S = (code_value<FMT>((word >> (4 * e)) & 15u) * bscale) * ia;
+        const double q = code_value<FMT>((word >> (4 * e)) & 15u) * bscale;
+        const double S = DIV ? q / double(a) : q * ia;
         const double ta = double(w[e]) * S, tb = S * S;
         ca[e] = i == 0 ? ta : ca[e] + ta;
         cb[e] = i == 0 ? tb : cb[e] + tb;
@@ -172,6 +213,61 @@ __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
       col_a[off + e] = ca[e];
       if (MODE == kCols) col_b[off + e] = cb[e];
     }
+  }
+}
+
+// NVFP4: per-block maxima of |W~| = |fp32(fp32(alpha_i W_ij) beta_j)|, then
+// t = fp32(amax) / 2688 (t = 1 for an all-zero W~ or when that underflows),
+// the activation quantizer's tensor scale rule applied to W~.
+constexpr int kAmaxBlocks = 1024;
+
+__global__ __launch_bounds__(kThreads) void dq_amax_kernel(
+    const float* __restrict__ W, const float* __restrict__ alpha, const float* __restrict__ beta,
+    int64_t N, int64_t K8, float* __restrict__ part) {
+  float m = 0.0f;
+  const int64_t n = N * K8;
+  for (int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x; g < n;
+       g += int64_t(gridDim.x) * kThreads) {
+    const int64_t row = g / K8, col8 = g - row * K8;
+    const float a = alpha[row];
+    const float4 w0 = reinterpret_cast<const float4*>(W + row * K8 * 8)[2 * col8];
+    const float4 w1 = reinterpret_cast<const float4*>(W + row * K8 * 8)[2 * col8 + 1];
+    const float4 b0 = reinterpret_cast<const float4*>(beta)[2 * col8];
+    const float4 b1 = reinterpret_cast<const float4*>(beta)[2 * col8 + 1];
+    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(__fmul_rn(__fmul_rn(a, w[e]), b[e])));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+    part[blockIdx.x] = r;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void dq_tscale_kernel(const float* __restrict__ part, int n,
+                                                             float* __restrict__ t_out,
+                                                             float* __restrict__ t_copy) {
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, part[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) a = fmaxf(a, red[i]);
+    float t = __fdiv_rn(a, 2688.0f);
+    if (a == 0.0f || t == 0.0f) t = 1.0f;
+    *t_out = t;
+    if (t_copy) *t_copy = t;
   }
 }
 
@@ -197,7 +293,7 @@ __device__ __forceinline__ double ordered_sum(const double* __restrict__ p, int6
 // One thread per row.  Init: alpha_0 = 1 / max|W_i| (1 for a zero row).
 // Update: r_i = Pi(sum W*R / sum R*R), alpha_i = 1 / r_i (r = alpha = 1 when
 // the row's Q^ is all zero).
-template <bool INIT>
+template <int FMT, bool INIT>
 __global__ __launch_bounds__(kThreads) void dq_row_finalize_kernel(
     const double* __restrict__ row_a, const double* __restrict__ row_b, int64_t N, int64_t KB,
     float* __restrict__ r, float* __restrict__ alpha) {
@@ -211,13 +307,13 @@ __global__ __launch_bounds__(kThreads) void dq_row_finalize_kernel(
   }
   const double num = ordered_sum(row_a + i, KB, N);
   const double den = ordered_sum(row_b + i, KB, N);
-  const double ri = den > 0.0 ? project_e8m0(num / den) : 1.0;
+  const double ri = den > 0.0 ? project_scale<FMT>(num / den) : 1.0;
   r[i] = float(ri);
   alpha[i] = float(1.0 / ri);
 }
 
 // One thread per column, the same over the 16-row chunk sums.
-template <bool INIT>
+template <int FMT, bool INIT>
 __global__ __launch_bounds__(kThreads) void dq_col_finalize_kernel(
     const double* __restrict__ col_a, const double* __restrict__ col_b, int64_t chunks, int64_t K,
     float* __restrict__ c, float* __restrict__ beta) {
@@ -229,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void dq_col_finalize_kernel(
     beta[j] = num > 0.0 ? float(1.0 / num) : 1.0f;
     return;
   }
-  const double cj = den > 0.0 ? project_e8m0(num / den) : 1.0;
+  const double cj = den > 0.0 ? project_scale<FMT>(num / den) : 1.0;
   c[j] = float(cj);
   beta[j] = float(1.0 / cj);
 }
@@ -237,6 +333,8 @@ __global__ __launch_bounds__(kThreads) void dq_col_finalize_kernel(
 struct SolverWs {
   float* alpha;
   float* beta;
+  float* amax;  // kAmaxBlocks partial maxima (NVFP4)
+  float* t;     // tensor scale of the current W~ (NVFP4)
   double *row_a, *row_b, *col_a, *col_b;
 };
 
@@ -255,6 +353,10 @@ SolverWs carve(void* ws, int64_t N, int64_t K) {
   s.alpha = reinterpret_cast<float*>(p);
   p += align256(N * 4);
   s.beta = reinterpret_cast<float*>(p);
+  p += align256(K * 4);
+  s.amax = reinterpret_cast<float*>(p);
+  p += align256(kAmaxBlocks * 4);
+  s.t = reinterpret_cast<float*>(p);
   return s;
 }
 
@@ -265,34 +367,51 @@ void pass(const float* W, const SolverWs& s, int64_t N, int64_t K, uint32_t* cod
   const int64_t K8 = K / 8;
   const dim3 grid(unsigned((N + ROWS - 1) / ROWS), unsigned((K8 + kThreads - 1) / kThreads));
   hipLaunchKernelGGL((dq_pass_kernel<FMT, MODE, DIV, ROWS>), grid, dim3(kThreads), 0, stream, W, s.alpha,
-                     s.beta, N, K8, s.row_a, s.row_b, s.col_a, s.col_b, codes, scales);
+                     s.beta, s.t, N, K8, s.row_a, s.row_b, s.col_a, s.col_b, codes, scales);
+}
+
+// NVFP4: the tensor scale of W~ at the current scales (into s.t, and into
+// t_copy when given)
+void tensor_scale(const float* W, const SolverWs& s, int64_t N, int64_t K, float* t_copy,
+                  hipStream_t stream) {
+  const int64_t n = N * (K / 8);
+  const int blocks = int(n / kThreads + 1 < kAmaxBlocks ? n / kThreads + 1 : kAmaxBlocks);
+  hipLaunchKernelGGL(dq_amax_kernel, dim3(blocks), dim3(kThreads), 0, stream, W, s.alpha, s.beta, N,
+                     K / 8, s.amax);
+  hipLaunchKernelGGL(dq_tscale_kernel, dim3(1), dim3(kThreads), 0, stream, s.amax, blocks, s.t,
+                     t_copy);
 }
 
 template <int FMT>
 hipError_t solve(int64_t N, int64_t K, const float* W, int iters, float* r, float* c,
-                 void* codes, void* scales, void* ws, hipStream_t stream) {
+                 void* codes, void* scales, float* t_w, void* ws, hipStream_t stream) {
+  constexpr bool NV = FMT == NVFP4;
   const SolverWs s = carve(ws, N, K);
   const int64_t KB = K / 32, chunks = (N + kChunk - 1) / kChunk;
   const dim3 gr(unsigned((N + kThreads - 1) / kThreads)), gc(unsigned((K + kThreads - 1) / kThreads));
   uint32_t* cw = static_cast<uint32_t*>(codes);
   uint8_t* sb = static_cast<uint8_t*>(scales);
   pass<FMT, kInit>(W, s, N, K, cw, sb, stream);
-  hipLaunchKernelGGL((dq_row_finalize_kernel<true>), gr, dim3(kThreads), 0, stream, s.row_a, s.row_b,
-                     N, KB, r, s.alpha);
-  hipLaunchKernelGGL((dq_col_finalize_kernel<true>), gc, dim3(kThreads), 0, stream, s.col_a, s.col_b,
-                     chunks, K, c, s.beta);
+  hipLaunchKernelGGL((dq_row_finalize_kernel<FMT, true>), gr, dim3(kThreads), 0, stream, s.row_a,
+                     s.row_b, N, KB, r, s.alpha);
+  hipLaunchKernelGGL((dq_col_finalize_kernel<FMT, true>), gc, dim3(kThreads), 0, stream, s.col_a,
+                     s.col_b, chunks, K, c, s.beta);
   for (int t = 0; t < iters; ++t) {
-    // beta_0 = 1 / l1 is not a power of two: the first row pass divides
-    if (t == 0)
+    if (NV) tensor_scale(W, s, N, K, nullptr, stream);
+    // beta_0 = 1 / l1 is not a power of two: the first row pass divides (and
+    // every NVFP4 pass: UE4M3 scales are not powers of two)
+    if (t == 0 || NV)
       pass<FMT, kRows, true>(W, s, N, K, cw, sb, stream);
     else
       pass<FMT, kRows>(W, s, N, K, cw, sb, stream);
-    hipLaunchKernelGGL((dq_row_finalize_kernel<false>), gr, dim3(kThreads), 0, stream, s.row_a,
+    hipLaunchKernelGGL((dq_row_finalize_kernel<FMT, false>), gr, dim3(kThreads), 0, stream, s.row_a,
                        s.row_b, N, KB, r, s.alpha);
-    pass<FMT, kCols>(W, s, N, K, cw, sb, stream);
-    hipLaunchKernelGGL((dq_col_finalize_kernel<false>), gc, dim3(kThreads), 0, stream, s.col_a,
+    if (NV) tensor_scale(W, s, N, K, nullptr, stream);
+    pass<FMT, kCols, NV>(W, s, N, K, cw, sb, stream);
+    hipLaunchKernelGGL((dq_col_finalize_kernel<FMT, false>), gc, dim3(kThreads), 0, stream, s.col_a,
                        s.col_b, chunks, K, c, s.beta);
   }
+  if (NV) tensor_scale(W, s, N, K, t_w, stream);
   pass<FMT, kEmit>(W, s, N, K, cw, sb, stream);
   return hipGetLastError();
 }
@@ -302,14 +421,15 @@ hipError_t solve(int64_t N, int64_t K, const float* W, int iters, float* r, floa
 size_t solver_workspace_bytes(int64_t N, int64_t K) {
   const int64_t KB = K / 32, chunks = (N + kChunk - 1) / kChunk;
   return size_t(2 * align256(N * KB * 8) + 2 * align256(chunks * K * 8) + align256(N * 4) +
-                align256(K * 4));
+                align256(K * 4) + align256(kAmaxBlocks * 4) + 256);
 }
 
 hipError_t launch_dualquant_solve(int fmt, int64_t N, int64_t K, const float* W, int iters,
-                                  float* r, float* c, void* codes, void* scales, void* workspace,
-                                  hipStream_t stream) {
-  if (fmt == MXFP4) return solve<MXFP4>(N, K, W, iters, r, c, codes, scales, workspace, stream);
-  return solve<MXINT4>(N, K, W, iters, r, c, codes, scales, workspace, stream);
+                                  float* r, float* c, void* codes, void* scales, float* t_w,
+                                  void* workspace, hipStream_t stream) {
+  if (fmt == MXFP4) return solve<MXFP4>(N, K, W, iters, r, c, codes, scales, t_w, workspace, stream);
+  if (fmt == NVFP4) return solve<NVFP4>(N, K, W, iters, r, c, codes, scales, t_w, workspace, stream);
+  return solve<MXINT4>(N, K, W, iters, r, c, codes, scales, t_w, workspace, stream);
 }
 
 }  // namespace w4a4
