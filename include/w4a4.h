@@ -111,6 +111,29 @@ w4a4_status w4a4_quantize_act(w4a4_format fmt, int64_t M, int64_t K,
                               void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * w4a4_quantize_act_multi - one activation X quantized under P column-scale
+ * vectors (per-projection c on a fused input, e.g. the q, k and v
+ * projections of one hidden state: DualQuant deploys one beta per linear,
+ * Section 4.4 and Appendix I).  X is read once; output p is what
+ * w4a4_quantize_act(fmt, M, K, X, c[p], codes[p], scales[p], t_act[p]) would
+ * write, bit for bit.
+ *
+ *   P        1 .. 4.
+ *   c        host array of P device pointers, fp32 [K] each, 16-byte aligned.
+ *   codes    host array of P device pointers, [M x K/2] each, 4-byte aligned.
+ *   scales   host array of P device pointers, [M x K/G] each.
+ *   t_act    host array of P device pointers to one fp32 each (NVFP4 only;
+ *            may be NULL for MX formats).
+ *   workspace/ws_bytes: NVFP4 needs P times w4a4_quantize_workspace_bytes()
+ *            (4-byte aligned); MX formats need none.
+ */
+w4a4_status w4a4_quantize_act_multi(w4a4_format fmt, int64_t M, int64_t K,
+                                    const void* X, int P, const float* const* c,
+                                    void* const* codes, void* const* scales,
+                                    float* const* t_act, void* workspace,
+                                    size_t ws_bytes, void* stream);
+
+/*
  * w4a4_pack_weight - pack a quantized weight into the GEMM storage layout.
  *
  * DualQuant Appendix I: the per-layer artifacts (quantized weight Q, row

@@ -192,3 +192,22 @@ def test_dualquant_solve_rejects(args, status):
     L = w4.lib()
     assert L.w4a4_dualquant_solve(*args) == status
     assert L.w4a4_last_error().decode()
+
+
+def test_quantize_act_multi_rejects():
+    L = w4.lib()
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    nul = (ctypes.c_void_p * 4)(FAKE, None, FAKE, FAKE)
+    base = (0, 16, 256, FAKE)
+    assert L.w4a4_quantize_act_multi(*base, 0, arr, arr, arr, None, None, 0, None) == 2    # P < 1
+    assert L.w4a4_quantize_act_multi(*base, 5, arr, arr, arr, None, None, 0, None) == 2    # P > 4
+    assert L.w4a4_quantize_act_multi(*base, 2, None, arr, arr, None, None, 0, None) == 1   # arrays
+    assert L.w4a4_quantize_act_multi(*base, 2, nul, arr, arr, None, None, 0, None) == 1    # c[1]
+    assert L.w4a4_quantize_act_multi(9, 16, 256, FAKE, 2, arr, arr, arr, None, None, 0, None) == 4
+    nv = (1, 16, 256, FAKE, 2, arr, arr, arr)
+    assert L.w4a4_quantize_act_multi(*nv, None, FAKE, 1 << 20, None) == 1                  # t_act
+    assert L.w4a4_quantize_act_multi(*nv, arr, None, 0, None) == 5                         # workspace
+    need = 2 * L.w4a4_quantize_workspace_bytes(1, 16, 256)
+    assert L.w4a4_quantize_act_multi(*nv, arr, FAKE, need - 1, None) == 5
+    mis = (ctypes.c_void_p * 4)(FAKE_MIS, FAKE, FAKE, FAKE)
+    assert L.w4a4_quantize_act_multi(*base, 2, mis, arr, arr, None, None, 0, None) == 3    # c align

@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
     L.w4a4_linear_workspace_bytes.restype = sz
     L.w4a4_quantize_act.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     L.w4a4_quantize_act.restype = i32
+    L.w4a4_quantize_act_multi.argtypes = [i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.w4a4_quantize_act_multi.restype = i32
     L.w4a4_pack_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp]
     L.w4a4_pack_weight.restype = i32
     L.w4a4_unpack_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp]
@@ -132,6 +134,33 @@ def quantize_act(x: torch.Tensor, c: Optional[torch.Tensor], fmt,
                                _ptr(workspace), workspace.numel() if workspace is not None else 0,
                                _stream(x.device)))
     return codes, scales, t
+
+
+def quantize_act_multi(x: torch.Tensor, cs, fmt, workspace: Optional[torch.Tensor] = None):
+    """w4a4_quantize_act_multi: bf16 [M, K] and P column-scale vectors -> a list of
+    (codes [M, K/2], scales [M, K/G], t [1] for NVFP4 else None), X read once."""
+    f = _fmt(fmt)
+    L = lib()
+    M, K = x.shape
+    P = len(cs)
+    G = block_size(fmt)
+    outs = [(torch.empty((M, K // 2), dtype=torch.uint8, device=x.device),
+             torch.empty((M, K // G), dtype=torch.uint8, device=x.device),
+             torch.ones(1, dtype=torch.float32, device=x.device) if f == FORMATS["nvfp4"] else None)
+            for _ in range(P)]
+    ws_bytes = P * L.w4a4_quantize_workspace_bytes(f, M, K)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    arr = ctypes.c_void_p * max(P, 1)
+    c_arr = arr(*[_ptr(c) for c in cs])
+    codes_arr = arr(*[_ptr(o[0]) for o in outs])
+    scales_arr = arr(*[_ptr(o[1]) for o in outs])
+    t_arr = arr(*[_ptr(o[2]) for o in outs])
+    _check(L.w4a4_quantize_act_multi(f, M, K, _ptr(x), P, c_arr, codes_arr, scales_arr,
+                                     t_arr if f == FORMATS["nvfp4"] else None, _ptr(workspace),
+                                     workspace.numel() if workspace is not None else 0,
+                                     _stream(x.device)))
+    return outs
 
 
 def pack_weight(codes: torch.Tensor, scales: torch.Tensor, t_w: Optional[torch.Tensor],

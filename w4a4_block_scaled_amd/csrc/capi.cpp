@@ -104,6 +104,39 @@ w4a4_status w4a4_quantize_act(w4a4_format fmt, int64_t M, int64_t K, const void*
                     "quantize_act launch");
 }
 
+w4a4_status w4a4_quantize_act_multi(w4a4_format fmt, int64_t M, int64_t K, const void* X, int P,
+                                    const float* const* c, void* const* codes,
+                                    void* const* scales, float* const* t_act, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+  if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
+  const int G = w4a4::block_size(fmt);
+  if (M < 0 || K <= 0 || K % G || P < 1 || P > w4a4::kMaxOutputs)
+    return fail(W4A4_ERR_SHAPE,
+                "quantize_act_multi: M=%lld K=%lld P=%d (need M >= 0, K > 0, K %% %d == 0, "
+                "1 <= P <= %d)",
+                (long long)M, (long long)K, P, G, w4a4::kMaxOutputs);
+  if (M * K / 8 > (int64_t(1) << 40)) return fail(W4A4_ERR_SHAPE, "quantize_act_multi: tensor too large");
+  if (!c || !codes || !scales || (fmt == W4A4_NVFP4 && !t_act))
+    return fail(W4A4_ERR_NULL, "quantize_act_multi: the pointer arrays must be non-NULL");
+  for (int p = 0; p < P; ++p) {
+    if (!c[p] || (M > 0 && (!X || !codes[p] || !scales[p])) || (fmt == W4A4_NVFP4 && !t_act[p]))
+      return fail(W4A4_ERR_NULL, "quantize_act_multi: output %d has a NULL pointer", p);
+    if (!aligned(c[p], 16) || !aligned(codes[p], 4) || (fmt == W4A4_NVFP4 && !aligned(t_act[p], 4)))
+      return fail(W4A4_ERR_ALIGN, "quantize_act_multi: c needs 16-byte, codes/t_act 4-byte alignment");
+  }
+  if (!aligned(X, 16)) return fail(W4A4_ERR_ALIGN, "quantize_act_multi: X needs 16-byte alignment");
+  if (fmt == W4A4_NVFP4) {
+    const size_t need = size_t(P) * w4a4_quantize_workspace_bytes(fmt, M, K);
+    if (!workspace || ws_bytes < need)
+      return fail(W4A4_ERR_WORKSPACE, "quantize_act_multi: NVFP4 needs %zu workspace bytes, got %zu",
+                  need, workspace ? ws_bytes : size_t(0));
+    if (!aligned(workspace, 4)) return fail(W4A4_ERR_ALIGN, "quantize_act_multi: workspace 4-byte alignment");
+  }
+  return hip_status(w4a4::launch_quantize_act_multi(fmt, M, K, X, P, c, codes, scales, t_act,
+                                                    workspace, static_cast<hipStream_t>(stream)),
+                    "quantize_act_multi launch");
+}
+
 w4a4_status w4a4_pack_weight(w4a4_format fmt, int64_t N, int64_t K, const void* codes,
                              const void* scales, const float* t_w, const float* r, void* blob,
                              void* stream) {

@@ -16,6 +16,14 @@ hipError_t launch_quantize_act(int fmt, int64_t M, int64_t K, const void* X, con
                                void* codes, void* scales, float* t_act, void* workspace,
                                hipStream_t stream);
 
+// One X quantized under up to kMaxOutputs column-scale vectors (X read once).
+constexpr int kMaxOutputs = 4;
+
+hipError_t launch_quantize_act_multi(int fmt, int64_t M, int64_t K, const void* X, int P,
+                                     const float* const* c, void* const* codes,
+                                     void* const* scales, float* const* t_act, void* workspace,
+                                     hipStream_t stream);
+
 hipError_t launch_pack_weight(int fmt, int64_t N, int64_t K, const void* codes,
                               const void* scales, const float* t_w, const float* r, void* blob,
                               hipStream_t stream);

@@ -161,6 +161,159 @@ __global__ __launch_bounds__(kThreads) void quantize_nv_kernel(
   if ((col8 & 1) == 0) scales[row * (K8 / 2) + (col8 >> 1)] = uint8_t(s);
 }
 
+// ------------------------------------------------ several column scales --
+//
+// One X, P column-scale vectors (per-projection c on a fused input, e.g. the
+// q, k and v projections of one hidden state): X is read once and each of the
+// P rescalings is quantized as quantize_act would quantize it.
+
+struct MultiOut {
+  const float* c[kMaxOutputs];
+  uint32_t* codes[kMaxOutputs];
+  uint8_t* scales[kMaxOutputs];
+  float* t[kMaxOutputs];
+  float* partial[kMaxOutputs];
+};
+
+__device__ __forceinline__ void load_c8(const float* __restrict__ c, int64_t col8, float (&cc)[8]) {
+  const float4 c0 = reinterpret_cast<const float4*>(c)[2 * col8];
+  const float4 c1 = reinterpret_cast<const float4*>(c)[2 * col8 + 1];
+  cc[0] = c0.x; cc[1] = c0.y; cc[2] = c0.z; cc[3] = c0.w;
+  cc[4] = c1.x; cc[5] = c1.y; cc[6] = c1.z; cc[7] = c1.w;
+}
+
+__device__ __forceinline__ void bf16x8(const uint4& v, float (&x)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+    x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+  }
+}
+
+template <int FMT, int R, int P>
+__global__ __launch_bounds__(kThreads) void quantize_mx_multi_kernel(const uint4* __restrict__ X,
+                                                                     MultiOut o, int64_t M,
+                                                                     int64_t K8) {
+  const int64_t col_raw = int64_t(blockIdx.y) * kThreads + threadIdx.x;
+  const bool live_c = col_raw < K8;
+  const int64_t col8 = live_c ? col_raw : K8 - 1;
+  const int64_t r0 = int64_t(blockIdx.x) * R;
+  float cc[P][8];
+#pragma unroll
+  for (int p = 0; p < P; ++p) load_c8(o.c[p], col8, cc[p]);
+  typedef unsigned ux4 __attribute__((ext_vector_type(4)));
+  ux4 v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = r0 + r < M ? r0 + r : M - 1;
+    v[r] = __builtin_nontemporal_load(reinterpret_cast<const ux4*>(X) + row * K8 + col8);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float x0[8];
+    bf16x8(uint4{v[r].x, v[r].y, v[r].z, v[r].w}, x0);
+    const int64_t row = r0 + r;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = __fmul_rn(x0[i], cc[p][i]);
+      uint32_t word, sbyte;
+      quant8_mx<FMT>(x, word, sbyte);
+      if (live_c && row < M) {
+        o.codes[p][row * K8 + col8] = word;
+        if ((col8 & 3) == 0) o.scales[p][row * (K8 / 4) + (col8 >> 2)] = uint8_t(sbyte);
+      }
+    }
+  }
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void absmax_multi_kernel(const uint4* __restrict__ X,
+                                                                MultiOut o, int64_t n_groups,
+                                                                int64_t K8) {
+  float m[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) m[p] = 0.0f;
+  for (int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x; g < n_groups;
+       g += int64_t(gridDim.x) * kThreads) {
+    float x0[8];
+    bf16x8(X[g], x0);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      float cc[8];
+      load_c8(o.c[p], g % K8, cc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m[p] = fmaxf(m[p], fabsf(__fmul_rn(x0[i], cc[i])));
+    }
+  }
+  __shared__ float red[P][kThreads / 64];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m[p] = fmaxf(m[p], __shfl_xor(m[p], off));
+    if ((threadIdx.x & 63) == 0) red[p][threadIdx.x >> 6] = m[p];
+  }
+  __syncthreads();
+  if (threadIdx.x < P) {
+    const int p = threadIdx.x;
+    float r = red[p][0];
+    for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[p][i]);
+    o.partial[p][blockIdx.x] = r;
+  }
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads) void quantize_nv_multi_kernel(const uint4* __restrict__ X,
+                                                                     MultiOut o, int64_t n_groups,
+                                                                     int64_t K8) {
+  const int64_t g_raw = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const bool live = g_raw < n_groups;
+  const int64_t g = live ? g_raw : n_groups - 1;
+  const int64_t row = g / K8;
+  const int64_t col8 = g - row * K8;
+  float x0[8];
+  bf16x8(X[g], x0);
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    float cc[8], x[8];
+    load_c8(o.c[p], col8, cc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = __fmul_rn(x0[i], cc[i]);
+    uint32_t word;
+    int s;
+    quant8_nv(x, *o.t[p], word, s);
+    if (live) {
+      o.codes[p][g] = word;
+      if ((col8 & 1) == 0) o.scales[p][row * (K8 / 2) + (col8 >> 1)] = uint8_t(s);
+    }
+  }
+}
+
+template <int P>
+hipError_t launch_multi(int fmt, int64_t M, int64_t K, const uint4* Xv, MultiOut o,
+                        hipStream_t stream) {
+  const int64_t K8 = K / 8, n_groups = M * K8;
+  if (fmt == MXFP4 || fmt == MXINT4) {
+    const dim3 grid(unsigned((M + 1) / 2), unsigned((K8 + kThreads - 1) / kThreads));
+    if (fmt == MXFP4)
+      hipLaunchKernelGGL((quantize_mx_multi_kernel<MXFP4, 2, P>), grid, dim3(kThreads), 0, stream, Xv, o, M, K8);
+    else
+      hipLaunchKernelGGL((quantize_mx_multi_kernel<MXINT4, 2, P>), grid, dim3(kThreads), 0, stream, Xv, o, M, K8);
+    return hipGetLastError();
+  }
+  const int nparts = int(std::min<int64_t>(kNvAmaxBlocks, (n_groups + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL((absmax_multi_kernel<P>), dim3(nparts), dim3(kThreads), 0, stream, Xv, o,
+                     n_groups, K8);
+  for (int p = 0; p < P; ++p)
+    hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(kThreads), 0, stream, o.partial[p], nparts,
+                       o.t[p]);
+  hipLaunchKernelGGL((quantize_nv_multi_kernel<P>), dim3(unsigned((n_groups + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, Xv, o, n_groups, K8);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quantize_act(int fmt, int64_t M, int64_t K, const void* X, const float* c,
@@ -209,6 +362,28 @@ hipError_t launch_quantize_act(int fmt, int64_t M, int64_t K, const void* X, con
                        n_groups, K8);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_act_multi(int fmt, int64_t M, int64_t K, const void* X, int P,
+                                     const float* const* c, void* const* codes,
+                                     void* const* scales, float* const* t_act, void* workspace,
+                                     hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  MultiOut o{};
+  for (int p = 0; p < P; ++p) {
+    o.c[p] = c[p];
+    o.codes[p] = static_cast<uint32_t*>(codes[p]);
+    o.scales[p] = static_cast<uint8_t*>(scales[p]);
+    o.t[p] = fmt == NVFP4 ? t_act[p] : nullptr;
+    o.partial[p] = fmt == NVFP4 ? static_cast<float*>(workspace) + int64_t(p) * kNvAmaxBlocks : nullptr;
+  }
+  const uint4* Xv = static_cast<const uint4*>(X);
+  switch (P) {
+    case 1: return launch_multi<1>(fmt, M, K, Xv, o, stream);
+    case 2: return launch_multi<2>(fmt, M, K, Xv, o, stream);
+    case 3: return launch_multi<3>(fmt, M, K, Xv, o, stream);
+    default: return launch_multi<4>(fmt, M, K, Xv, o, stream);
+  }
 }
 
 }  // namespace w4a4
