@@ -18,8 +18,9 @@ HIP-event-timed average duration, against the MI355X dense MXFP4 peak),
 decode weight-streaming bandwidth (MXFP4 Llama linears at M = 1, 4, 16,
 MXINT4 Qwen linears and NVFP4 Llama linears at M = 1, cycling 32 layer
 copies so that the 256 MB last-level cache cannot hold the weights), the
-offline dual-scale solver on fp32 weights of the Llama linears' shapes, and
-the CPU oracle timed on a
+offline dual-scale solver on fp32 weights of the Llama linears' shapes, one
+activation quantized under three column scales against three calls, and the
+CPU oracle timed on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -173,6 +174,35 @@ def time_graph(layers, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def quantize_multi_rate(dev, M=2048, K=4096, P=3, reps=50):
+    """Per-projection c on a fused input (the Llama q, k, v projections of one
+    hidden state, MXFP4): one w4a4_quantize_act_multi call with P column-scale
+    vectors against P w4a4_quantize_act calls, each replayed from a HIP graph.
+    HBM bytes: X once (2MK) plus P outputs (MK/2 + MK/32 each) and P c
+    vectors."""
+    g = torch.Generator(device="cpu").manual_seed(9)
+    x = (torch.randn((M, K), generator=g)).to(torch.bfloat16).to(dev)
+    cs = [torch.ldexp(torch.ones(K), torch.randint(-2, 3, (K,), generator=g)).to(dev) for _ in range(P)]
+
+    def timed(fn):
+        # reps calls captured in one HIP graph: GPU time, not the host's
+        g = capture(lambda: [fn() for _ in range(reps)])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    multi = timed(lambda: w4.quantize_act_multi(x, cs, "mxfp4"))
+    separate = timed(lambda: [w4.quantize_act(x, c, "mxfp4") for c in cs])
+    nbytes = 2 * M * K + P * (M * K // 2 + M * K // 32 + 4 * K)
+    return {"M": M, "K": K, "P": P, "multi_us": round(multi, 2), "separate_us": round(separate, 2),
+            "multi_GB/s": round(nbytes / (multi * 1e-6) / 1e9, 1)}
 
 
 def solver_rate(dev, iters=15):
@@ -413,6 +443,8 @@ def main():
     if not a.no_solver:
         log("[bench] dual-scale solver")
         out["dualquant_solver"] = solver_rate(dev)
+        log("[bench] per-projection c: one X, three column scales")
+        out["quantize_multi"] = quantize_multi_rate(dev)
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(a.workload, M)
