@@ -18,9 +18,10 @@ HIP-event-timed average duration, against the MI355X dense MXFP4 peak),
 decode weight-streaming bandwidth (MXFP4 Llama linears at M = 1, 4, 16,
 MXINT4 Qwen linears and NVFP4 Llama linears at M = 1, cycling 32 layer
 copies so that the 256 MB last-level cache cannot hold the weights), the
-offline dual-scale solver on fp32 weights of the Llama linears' shapes, one
-activation quantized under three column scales against three calls, and the
-CPU oracle timed on a
+offline dual-scale solver on fp32 weights of the Llama linears' shapes, the
+q, k, v projections with their own column scales (one multi-output quantize
+and one grouped GEMM against three separate pairs), and the CPU oracle timed
+on a
 bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -176,33 +177,61 @@ def time_graph(layers, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def quantize_multi_rate(dev, M=2048, K=4096, P=3, reps=50):
-    """Per-projection c on a fused input (the Llama q, k, v projections of one
-    hidden state, MXFP4): one w4a4_quantize_act_multi call with P column-scale
-    vectors against P w4a4_quantize_act calls, each replayed from a HIP graph.
-    HBM bytes: X once (2MK) plus P outputs (MK/2 + MK/32 each) and P c
-    vectors."""
+def per_projection_rate(dev, M=2048, K=4096, Ns=(4096, 1024, 1024), reps=50):
+    """Per-projection c on a fused input: the Llama q, k, v projections of one
+    hidden state (MXFP4), each with its own column scale.  Against three
+    separate (quantize_act, linear) pairs: one w4a4_quantize_act_multi
+    (X read once) and one w4a4_linear_grouped (the three problems' tiles in
+    one launch).  Every variant replayed from a HIP graph of `reps` steps;
+    random codes stand in for the weights (the kernels' work does not depend
+    on the values)."""
     g = torch.Generator(device="cpu").manual_seed(9)
-    x = (torch.randn((M, K), generator=g)).to(torch.bfloat16).to(dev)
+    x = torch.randn((M, K), generator=g).to(torch.bfloat16).to(dev)
+    P = len(Ns)
     cs = [torch.ldexp(torch.ones(K), torch.randint(-2, 3, (K,), generator=g)).to(dev) for _ in range(P)]
+    blobs = []
+    for N in Ns:
+        wc = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, generator=g).to(dev)
+        wsc = torch.randint(118, 124, (N, K // 32), dtype=torch.uint8, generator=g).to(dev)
+        blobs.append(w4.pack_weight(wc, wsc, None, torch.ones(N, device=dev), "mxfp4"))
+    q = [w4.quantize_act(x, c, "mxfp4") for c in cs]
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for N in Ns]
 
     def timed(fn):
-        # reps calls captured in one HIP graph: GPU time, not the host's
-        g = capture(lambda: [fn() for _ in range(reps)])
-        g.replay()
+        gr = capture(lambda: [fn() for _ in range(reps)])
+        gr.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        g.replay()
+        gr.replay()
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps
 
-    multi = timed(lambda: w4.quantize_act_multi(x, cs, "mxfp4"))
-    separate = timed(lambda: [w4.quantize_act(x, c, "mxfp4") for c in cs])
-    nbytes = 2 * M * K + P * (M * K // 2 + M * K // 32 + 4 * K)
-    return {"M": M, "K": K, "P": P, "multi_us": round(multi, 2), "separate_us": round(separate, 2),
-            "multi_GB/s": round(nbytes / (multi * 1e-6) / 1e9, 1)}
+    problems = [(q[p][0], q[p][1], None, blobs[p], Ns[p]) for p in range(P)]
+    quant_multi = timed(lambda: w4.quantize_act_multi(x, cs, "mxfp4"))
+    quant_sep = timed(lambda: [w4.quantize_act(x, c, "mxfp4") for c in cs])
+    gemm_grouped = timed(lambda: w4.linear_grouped(problems, "mxfp4", K, outs=ys))
+    gemm_sep = timed(lambda: [w4.linear(q[p][0], q[p][1], None, blobs[p], "mxfp4", Ns[p], K, out=ys[p])
+                              for p in range(P)])
+
+    def step_fused():
+        qs = w4.quantize_act_multi(x, cs, "mxfp4")
+        w4.linear_grouped([(qs[p][0], qs[p][1], None, blobs[p], Ns[p]) for p in range(P)], "mxfp4", K, outs=ys)
+
+    def step_sep():
+        for p in range(P):
+            a, s_, _ = w4.quantize_act(x, cs[p], "mxfp4")
+            w4.linear(a, s_, None, blobs[p], "mxfp4", Ns[p], K, out=ys[p])
+
+    fused = timed(step_fused)
+    sep = timed(step_sep)
+    flops = 2.0 * M * K * sum(Ns)
+    return {"M": M, "K": K, "N": list(Ns), "quantize_multi_us": round(quant_multi, 2),
+            "quantize_separate_us": round(quant_sep, 2), "gemm_grouped_us": round(gemm_grouped, 2),
+            "gemm_separate_us": round(gemm_sep, 2),
+            "gemm_grouped_TFLOP/s": round(flops / (gemm_grouped * 1e-6) / 1e12, 1),
+            "step_fused_us": round(fused, 2), "step_separate_us": round(sep, 2)}
 
 
 def solver_rate(dev, iters=15):
@@ -443,8 +472,8 @@ def main():
     if not a.no_solver:
         log("[bench] dual-scale solver")
         out["dualquant_solver"] = solver_rate(dev)
-        log("[bench] per-projection c: one X, three column scales")
-        out["quantize_multi"] = quantize_multi_rate(dev)
+        log("[bench] per-projection c: q, k, v with their own column scales")
+        out["per_projection"] = per_projection_rate(dev)
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(a.workload, M)

@@ -209,6 +209,27 @@ w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K,
                         void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * w4a4_linear_grouped - P linears of one M and K (the per-projection linears
+ * of a fused input, e.g. q, k and v with their own column scales, after
+ * w4a4_quantize_act_multi): output p is what w4a4_linear(fmt, M, N[p], K,
+ * a_codes[p], a_scales[p], t_act[p], blobs[p], Y[p]) computes, within the
+ * same accumulation-order tolerance.  For MXFP4 with M > 32 the problems'
+ * 256 x 128 tiles run in one launch, unless each would take the persistent
+ * kernel on its own; otherwise (and for the other formats) they run one
+ * after another on their usual kernels.  No workspace is needed.
+ *
+ *   P        1 .. 4.
+ *   N        host array of P output widths (each % 16 == 0).
+ *   a_codes, a_scales, blobs, Y: host arrays of P device pointers, with the
+ *            alignments of w4a4_linear.
+ *   t_act    host array of P device pointers (NVFP4 only; may be NULL for MX).
+ */
+w4a4_status w4a4_linear_grouped(w4a4_format fmt, int P, int64_t M, int64_t K,
+                                const int64_t* N, const void* const* a_codes,
+                                const void* const* a_scales, const float* const* t_act,
+                                const void* const* blobs, void* const* Y, void* stream);
+
+/*
  * w4a4_dualquant_solve - the offline dual-scale solver.
  *
  * DualQuant Algorithm 1 (Section 4.3, block coordinate descent with

@@ -211,3 +211,16 @@ def test_quantize_act_multi_rejects():
     assert L.w4a4_quantize_act_multi(*nv, arr, FAKE, need - 1, None) == 5
     mis = (ctypes.c_void_p * 4)(FAKE_MIS, FAKE, FAKE, FAKE)
     assert L.w4a4_quantize_act_multi(*base, 2, mis, arr, arr, None, None, 0, None) == 3    # c align
+
+
+def test_linear_grouped_rejects():
+    L = w4.lib()
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    Ns = (ctypes.c_int64 * 4)(256, 128, 128, 64)
+    bad_n = (ctypes.c_int64 * 4)(256, 100, 128, 64)
+    assert L.w4a4_linear_grouped(0, 0, 64, 256, Ns, arr, arr, None, arr, arr, None) == 2   # P < 1
+    assert L.w4a4_linear_grouped(0, 5, 64, 256, Ns, arr, arr, None, arr, arr, None) == 2   # P > 4
+    assert L.w4a4_linear_grouped(0, 2, 64, 256, None, arr, arr, None, arr, arr, None) == 1
+    assert L.w4a4_linear_grouped(0, 2, 64, 256, bad_n, arr, arr, None, arr, arr, None) == 2  # N % 16
+    assert L.w4a4_linear_grouped(1, 2, 64, 256, Ns, arr, arr, None, arr, arr, None) == 1   # NVFP4 t_act
+    assert L.w4a4_linear_grouped(7, 2, 64, 256, Ns, arr, arr, None, arr, arr, None) == 4

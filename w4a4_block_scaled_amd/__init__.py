@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.w4a4_quantize_act.restype = i32
     L.w4a4_quantize_act_multi.argtypes = [i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     L.w4a4_quantize_act_multi.restype = i32
+    L.w4a4_linear_grouped.argtypes = [i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+    L.w4a4_linear_grouped.restype = i32
     L.w4a4_pack_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp]
     L.w4a4_pack_weight.restype = i32
     L.w4a4_unpack_weight.argtypes = [i32, i64, i64, vp, vp, vp, vp, vp, vp]
@@ -256,3 +258,23 @@ def dualquant_solve(w: torch.Tensor, fmt, iters: int = 15, workspace: Optional[t
                                   _ptr(scales), _ptr(t_w), _ptr(workspace), workspace.numel(),
                                   _stream(w.device)))
     return r, c, codes, scales, t_w
+
+
+def linear_grouped(problems, fmt, K: int, outs=None):
+    """w4a4_linear_grouped: problems = [(a_codes, a_scales, t_act, blob, N), ...]
+    sharing M and K -> list of bf16 [M, N_p] outputs."""
+    f = _fmt(fmt)
+    L = lib()
+    P = len(problems)
+    M = problems[0][0].shape[0]
+    dev = problems[0][0].device
+    if outs is None:
+        outs = [torch.empty((M, pr[4]), dtype=torch.bfloat16, device=dev) for pr in problems]
+    arr = ctypes.c_void_p * P
+    Ns = (ctypes.c_int64 * P)(*[int(pr[4]) for pr in problems])
+    _check(L.w4a4_linear_grouped(f, P, M, K, Ns, arr(*[_ptr(pr[0]) for pr in problems]),
+                                 arr(*[_ptr(pr[1]) for pr in problems]),
+                                 arr(*[_ptr(pr[2]) for pr in problems]) if f == FORMATS["nvfp4"] else None,
+                                 arr(*[_ptr(pr[3]) for pr in problems]), arr(*[_ptr(o) for o in outs]),
+                                 _stream(dev)))
+    return outs

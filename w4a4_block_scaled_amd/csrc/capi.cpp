@@ -188,6 +188,33 @@ w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K, const 
                     "linear launch");
 }
 
+w4a4_status w4a4_linear_grouped(w4a4_format fmt, int P, int64_t M, int64_t K, const int64_t* N,
+                                const void* const* a_codes, const void* const* a_scales,
+                                const float* const* t_act, const void* const* blobs,
+                                void* const* Y, void* stream) {
+  if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
+  if (P < 1 || P > w4a4::kMaxGroup || M < 0)
+    return fail(W4A4_ERR_SHAPE, "linear_grouped: P=%d M=%lld (need 1 <= P <= %d, M >= 0)", P,
+                (long long)M, w4a4::kMaxGroup);
+  if (!N || !a_codes || !a_scales || !blobs || !Y || (fmt == W4A4_NVFP4 && !t_act))
+    return fail(W4A4_ERR_NULL, "linear_grouped: the arrays must be non-NULL");
+  for (int p = 0; p < P; ++p) {
+    w4a4_status st = check_gemm_shape(fmt, N[p], K);
+    if (st != W4A4_OK) return st;
+    if (M == 0) continue;
+    if (!a_codes[p] || !a_scales[p] || !blobs[p] || !Y[p] || (fmt == W4A4_NVFP4 && !t_act[p]))
+      return fail(W4A4_ERR_NULL, "linear_grouped: problem %d has a NULL pointer", p);
+    if (!aligned(a_codes[p], 16) || !aligned(a_scales[p], 16) || !aligned(Y[p], 16) ||
+        !aligned(blobs[p], 256) || (fmt == W4A4_NVFP4 && !aligned(t_act[p], 4)))
+      return fail(W4A4_ERR_ALIGN,
+                  "linear_grouped: a_codes/a_scales/Y need 16-byte, blob 256-byte, t_act 4-byte "
+                  "alignment");
+  }
+  return hip_status(w4a4::launch_linear_grouped(fmt, P, M, K, N, a_codes, a_scales, t_act, blobs,
+                                                Y, static_cast<hipStream_t>(stream)),
+                    "linear_grouped launch");
+}
+
 size_t w4a4_dualquant_workspace_bytes(w4a4_format fmt, int64_t N, int64_t K) {
   if (!valid_fmt(fmt) || N <= 0 || K <= 0 || K % 32 ||
       N * K > (int64_t(1) << 36))

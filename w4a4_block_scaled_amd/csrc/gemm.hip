@@ -1180,17 +1180,15 @@ struct Fp4Group {
   }
 };
 
+// One BN x BM output tile (row tile tm, column tile tn) of one problem.
 template <int BN, int BM, int DEPTH>
-__global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(
-    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
-    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
-    int tiles_m, int tiles_total, int per_xcd) {
+__device__ __forceinline__ void fp4_tile(const uint8_t* __restrict__ a_codes,
+                                         const uint8_t* __restrict__ a_scales,
+                                         const uint8_t* __restrict__ blob,
+                                         uint16_t* __restrict__ Y, int64_t M, int64_t N,
+                                         int64_t K, int tm, int tn) {
   using C = Fp4Cfg<BN, BM, DEPTH>;
   constexpr int FN = C::FN, FM = C::FM;
-  const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
-  if (tile >= tiles_total) return;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
-
   const BlobLayout L = blob_layout(MXFP4, N, K);
   Fp4Args t;
   t.a_codes = a_codes;
@@ -1294,6 +1292,42 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(
     const int64_t m = mbase + row, n = nbase + 8 * chunk;
     if (m < M && n < N) *reinterpret_cast<u32x4*>(Y + m * N + n) = v;
   }
+}
+
+template <int BN, int BM, int DEPTH>
+__global__ __launch_bounds__(256, 1) void gemm_fp4_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int tiles_m, int tiles_total, int per_xcd) {
+  const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (tile >= tiles_total) return;
+  fp4_tile<BN, BM, DEPTH>(a_codes, a_scales, blob, Y, M, N, K, tile % tiles_m, tile / tiles_m);
+}
+
+// Several problems of one M and K in one launch (per-projection linears of a
+// fused input): problem p owns tiles [first[p], first[p + 1]) of the launch;
+// the XCD-contiguous tile order runs over the problems in turn.
+struct Fp4Problems {
+  const uint8_t* ac[kMaxGroup];
+  const uint8_t* as[kMaxGroup];
+  const uint8_t* blob[kMaxGroup];
+  uint16_t* Y[kMaxGroup];
+  int64_t N[kMaxGroup];
+  int first[kMaxGroup + 1];
+  int P;
+};
+
+template <int BN, int BM, int DEPTH>
+__global__ __launch_bounds__(256, 1) void gemm_fp4_grouped_kernel(Fp4Problems g, int64_t M, int64_t K,
+                                                                  int tiles_m, int per_xcd) {
+  const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (tile >= g.first[g.P]) return;
+  int p = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxGroup; ++q) p += (q < g.P && tile >= g.first[q]) ? 1 : 0;
+  const int lt = tile - g.first[p];
+  fp4_tile<BN, BM, DEPTH>(g.ac[p], g.as[p], g.blob[p], g.Y[p], M, g.N[p], K, lt % tiles_m,
+                          lt / tiles_m);
 }
 
 template <int BN, int BM, int DEPTH>
@@ -2528,6 +2562,43 @@ hipError_t launch_linear(int fmt, int64_t M, int64_t N, int64_t K, const void* a
     case MXINT4: return launch_fmt<MXINT4>(M, N, K, ac, as, t_act, b, y, workspace, stream);
     default: return launch_fmt<NVFP4>(M, N, K, ac, as, t_act, b, y, workspace, stream);
   }
+}
+
+hipError_t launch_linear_grouped(int fmt, int P, int64_t M, int64_t K, const int64_t* N,
+                                 const void* const* a_codes, const void* const* a_scales,
+                                 const float* const* t_act, const void* const* blobs,
+                                 void* const* Y, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  bool all_persistent = true;
+  for (int p = 0; p < P; ++p) all_persistent &= fmt == MXFP4 && fp4_persistent_fits(M, N[p], K);
+  if (fmt != MXFP4 || M <= 32 || all_persistent) {
+    // one after another, each on its own kernel (none of these needs a workspace)
+    for (int p = 0; p < P; ++p) {
+      const hipError_t e = launch_linear(fmt, M, N[p], K, a_codes[p], a_scales[p],
+                                         t_act ? t_act[p] : nullptr, blobs[p], Y[p], nullptr, 0,
+                                         stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  // 256 (n) x 128 (m) tiles of all problems in one launch
+  Fp4Problems g{};
+  const int tiles_m = int((M + 127) / 128);
+  g.P = P;
+  g.first[0] = 0;
+  for (int p = 0; p < P; ++p) {
+    g.ac[p] = static_cast<const uint8_t*>(a_codes[p]);
+    g.as[p] = static_cast<const uint8_t*>(a_scales[p]);
+    g.blob[p] = static_cast<const uint8_t*>(blobs[p]);
+    g.Y[p] = static_cast<uint16_t*>(Y[p]);
+    g.N[p] = N[p];
+    g.first[p + 1] = g.first[p] + int((N[p] + 255) / 256) * tiles_m;
+  }
+  for (int p = P; p < kMaxGroup; ++p) g.first[p + 1] = g.first[P];
+  const int per_xcd = (g.first[P] + 7) / 8;
+  hipLaunchKernelGGL((gemm_fp4_grouped_kernel<256, 128, 5>), dim3(unsigned(per_xcd * 8)), dim3(256),
+                     0, stream, g, M, K, tiles_m, per_xcd);
+  return hipGetLastError();
 }
 
 }  // namespace w4a4

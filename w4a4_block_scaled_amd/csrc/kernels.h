@@ -37,6 +37,16 @@ hipError_t launch_linear(int fmt, int64_t M, int64_t N, int64_t K, const void* a
 
 size_t linear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
+// Up to kMaxGroup linears of one M and K (per-projection linears of a fused
+// input): one launch where that pays (MXFP4, M > 32, unless every problem
+// takes the persistent kernel on its own), else one after another.
+constexpr int kMaxGroup = 4;
+
+hipError_t launch_linear_grouped(int fmt, int P, int64_t M, int64_t K, const int64_t* N,
+                                 const void* const* a_codes, const void* const* a_scales,
+                                 const float* const* t_act, const void* const* blobs,
+                                 void* const* Y, hipStream_t stream);
+
 // DualQuant's dual-scale solver: workspace bytes and launch.
 size_t solver_workspace_bytes(int64_t N, int64_t K);
 
