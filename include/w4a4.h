@@ -239,7 +239,7 @@ w4a4_status w4a4_linear_grouped(w4a4_format fmt, int P, int64_t M, int64_t K,
  * values, UE4M3, for NVFP4) and the codes Q = Q(Diag(alpha) W Diag(beta)) so
  * that W ~ Diag(r) Q Diag(c).  r, t_w and the codes/scales go to
  * w4a4_pack_weight, c to w4a4_quantize_act.  Starting from alpha_0 = 1 / row absmax and
- * beta_0 = 1 / column l1 norm, each iteration sets r_i to the power of two
+ * beta_0 = 1 / column l1 norm, each iteration sets r_i to the admissible value
  * nearest to <W_i, R_i> / ||R_i||^2 with R = Q^ Diag(beta)^-1 (Q^ the
  * quantized rescaled weight; for NVFP4 with the fp32 tensor scale of that
  * rescaled weight, as in w4a4_quantize_act), re-quantizes, then sets c_j likewise from

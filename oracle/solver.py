@@ -31,8 +31,8 @@ Readings where the pages leave a step open:
     i.e. the inverse scales start at those magnitudes (the extracted text
     shows the magnitudes without an inverse marker).  Taken literally (alpha_0
     = absmax) the solver ends about 2x above round-to-nearest on synthetic
-    weights with outlier columns; with the inverse it ends 2-3x below, and
-    beta then follows a weight-only smoothing scale, as the pages report.
+    weights with outlier columns; with the inverse it ends 1.3-1.9x below
+    (MX formats), and beta then follows a weight-only smoothing scale, as the pages report.
     alpha_0 = fp32(1 / absmax) and beta_0 = fp32(1 / l1) from fp64 quotients;
     an all-zero row or column starts at 1.
   * The rescaled weight is W~_ij = fp32(fp32(alpha_i * W_ij) * beta_j), with
