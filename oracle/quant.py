@@ -28,11 +28,20 @@ What is computed (DualQuant):
 * Elements: MXFP4 code = RNE_E2M1(x~ * 2^-e); MXINT4 code =
   clip(RNE(x~ * 2^-e), -8, 7); NVFP4 code = RNE_E2M1(x~ / (s t)), all
   decided exactly.  NVFP4 blocks whose scale rounds to 0 keep only the sign.
-* MX blocks holding a non-finite value get scale byte 0xFF and zero codes
-  (inputs are expected finite; this only fixes what happens otherwise).
+* INT4 with G = 64 and BF16 block scales (the paper's packed deployment
+  format, Section 4.2 "admissible sets" with BF16 for INT4; Section 3's
+  symmetric scale Delta = max|x| / q_max with q_max = 7 for INT4):
+  Delta = BF16(amax / 7), rounded once to nearest even from the exact
+  quotient; code = clip(RNE(x~ / Delta), -8, 7) decided exactly (ties to
+  the even integer); an all-zero block (or one whose Delta rounds to 0)
+  gets Delta = 0 and zero codes.
+* MX and INT4 G=64 blocks holding a non-finite value get scale byte 0xFF
+  (BF16 0x7FC0) and zero codes (inputs are expected finite; this only fixes
+  what happens otherwise).
 
 Canonical storage: codes [rows, K/2] bytes, element 2j in the low nibble of
-byte j and 2j+1 in the high nibble; scales [rows, K/G] bytes, row-major.
+byte j and 2j+1 in the high nibble; scales [rows, K/G] bytes, row-major
+(uint16 BF16 bit patterns for INT4 G=64).
 """
 from __future__ import annotations
 
@@ -40,7 +49,8 @@ import numpy as np
 
 from . import formats as F
 
-BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32}
+BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32, "int4g64": 64}
+INT4_QMAX = 7                      # symmetric INT4 grid maximum
 EMAX_ELEM = 2                      # floor(log2) of the largest element magnitude
 NV_TENSOR_DIVISOR = np.float32(6.0 * 448.0)   # 2688
 ROW_CHUNK = 256
@@ -86,6 +96,25 @@ def _quantize_chunk(xt, fmt, t):
             codes = F.int4_encode(np.clip(np.rint(v), -8, 7))
         scales = np.where(nonfinite, np.uint8(255), scales)
         codes = np.where(nonfinite[..., None], np.uint8(0), codes)
+    elif fmt == "int4g64":
+        nonfinite = ~np.isfinite(blocks).all(axis=-1)
+        amax = np.where(nonfinite, 0.0, amax)
+        # amax / 7 in fp64 then one rounding to BF16: the fp64 quotient can only
+        # land on a BF16 midpoint when the exact quotient is that midpoint, so
+        # this is the single correct rounding of amax / 7
+        bits = F.bf16_from_f64(amax / INT4_QMAX)
+        delta = F.bf16_value(bits)
+        live = delta > 0
+        # x~ (24 bits) / Delta (8 bits) in fp64: a quotient that is not a
+        # half-integer differs from one by far more than the fp64 rounding,
+        # so rint of the fp64 quotient is the exact nearest-even decision
+        with np.errstate(invalid="ignore", over="ignore"):
+            v = np.where(live[..., None] & np.isfinite(blocks),
+                         blocks / np.where(live, delta, 1.0)[..., None], 0.0)
+        codes = F.int4_encode(np.clip(np.rint(v), -8, 7))
+        scales = np.where(nonfinite, np.uint16(0x7FC0), np.where(live, bits, np.uint16(0)))
+        codes = np.where(nonfinite[..., None], np.uint8(0), codes)
+        return codes.reshape(R, K).astype(np.uint8), scales.astype(np.uint16)
     else:
         den = 6.0 * np.float64(t)                  # exact: 2 + 24 significant bits
         scales = F.e4m3_encode_ratio(amax, den)
@@ -112,7 +141,7 @@ def quantize_rows(xt, fmt, t=None):
     if fmt == "nvfp4" and t is None:
         t = nv_tensor_scale(xt)
     codes = np.empty((R, K), np.uint8)
-    scales = np.empty((R, K // G), np.uint8)
+    scales = np.empty((R, K // G), np.uint16 if fmt == "int4g64" else np.uint8)
     for r0 in range(0, R, ROW_CHUNK):
         codes[r0:r0 + ROW_CHUNK], scales[r0:r0 + ROW_CHUNK] = \
             _quantize_chunk(xt[r0:r0 + ROW_CHUNK], fmt, t)
@@ -158,9 +187,14 @@ def dequantize(packed, scales, fmt):
     codes = unpack_nibbles(packed)
     R, K = codes.shape
     G = BLOCK[fmt]
-    if fmt == "mxint4":
+    if fmt in ("mxint4", "int4g64"):
         elem = F.int4_value(codes)
     else:
         elem = F.e2m1_value(codes)
-    svals = F.e8m0_value(scales) if fmt in ("mxfp4", "mxint4") else F.e4m3_value(scales)
+    if fmt == "int4g64":
+        svals = F.bf16_value(scales)
+    elif fmt in ("mxfp4", "mxint4"):
+        svals = F.e8m0_value(scales)
+    else:
+        svals = F.e4m3_value(scales)
     return (elem.reshape(R, K // G, G) * svals[..., None]).reshape(R, K)
