@@ -48,8 +48,26 @@ extern "C" {
 typedef enum {
   W4A4_MXFP4 = 0,   /* E2M1 elements, G = 32, E8M0 block scale             */
   W4A4_NVFP4 = 1,   /* E2M1 elements, G = 16, UE4M3 block scale + fp32 t   */
-  W4A4_MXINT4 = 2   /* int4 elements, G = 32, E8M0 block scale             */
+  W4A4_MXINT4 = 2,  /* int4 elements, G = 32, E8M0 block scale             */
+  W4A4_INT4G64 = 3  /* int4 elements, G = 64, BF16 block scale (see below)  */
 } w4a4_format;
+
+/*
+ * W4A4_INT4G64 - the paper's packed deployment format (Appendix I: INT4,
+ * G = 64, BF16 group scales; Section 3's symmetric quantizer with q_max = 7;
+ * Section 4.2's BF16 admissible set for INT4).  A block's scale is
+ * Delta = BF16(amax / 7), rounded once to nearest even; codes are
+ * clip(RNE(x~ / Delta), -8, 7); a zero block has Delta = 0 and zero codes; a
+ * block with a non-finite value gets Delta = 0x7FC0 and zero codes.  Scales
+ * are stored as BF16 bit patterns, [rows x K/64] uint16 (two bytes per block,
+ * w4a4_act_scales_bytes counts bytes).  K % 64 == 0 and N % 16 == 0 (no K % 128
+ * requirement); there is no tensor scale (t_act and t_w are ignored; unpack
+ * writes t_w = 1).  Supported by the size queries, w4a4_quantize_act,
+ * w4a4_pack_weight, w4a4_unpack_weight and w4a4_linear (no workspace); the
+ * multi-output quantizer, the grouped linear and the solver return
+ * W4A4_ERR_FORMAT for it.  The GEMM runs one int8 MFMA (16x16x64) per 64-block
+ * and applies Delta_a * Delta_w to each block sum in fp32.
+ */
 
 typedef enum {
   W4A4_OK = 0,

@@ -224,3 +224,48 @@ def test_linear_grouped_rejects():
     assert L.w4a4_linear_grouped(0, 2, 64, 256, bad_n, arr, arr, None, arr, arr, None) == 2  # N % 16
     assert L.w4a4_linear_grouped(1, 2, 64, 256, Ns, arr, arr, None, arr, arr, None) == 1   # NVFP4 t_act
     assert L.w4a4_linear_grouped(7, 2, 64, 256, Ns, arr, arr, None, arr, arr, None) == 4
+
+
+def test_int4g64_size_queries():
+    """INT4 G=64 with BF16 scales: G = 64, two scale bytes per block (as many
+    as E8M0 at G = 32), K % 64 suffices, no workspaces."""
+    L = w4.lib()
+    assert L.w4a4_block_size(3) == 64
+    assert L.w4a4_act_codes_bytes(3, 5, 192) == 5 * 96
+    assert L.w4a4_act_scales_bytes(3, 5, 192) == 5 * 3 * 2
+    assert L.w4a4_act_scales_bytes(3, 7, 4096) == L.w4a4_act_scales_bytes(0, 7, 4096)
+    assert L.w4a4_act_scales_bytes(3, 5, 96) == 0                  # K % 64
+    assert L.w4a4_quantize_workspace_bytes(3, 5, 192) == 0
+    assert L.w4a4_linear_workspace_bytes(3, 2048, 4096, 4096) == 0
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    for N, K in [(16, 64), (48, 192), (4096, 14336)]:
+        assert L.w4a4_packed_weight_bytes(3, N, K) == a256(a256(256 + N * K // 2) + N * K // 64 * 2) + a256(4 * N)
+    assert L.w4a4_packed_weight_bytes(3, 24, 192) == 0              # N % 16
+    assert L.w4a4_packed_weight_bytes(3, 16, 96) == 0               # K % 64
+    assert L.w4a4_dualquant_workspace_bytes(3, 64, 256) == 0        # no solver for this format
+
+
+def test_int4g64_rejects():
+    L = w4.lib()
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    n = (ctypes.c_int64 * 4)(64, 64, 64, 64)
+    # quantize_act: K % 64, NULL X, misaligned X
+    assert L.w4a4_quantize_act(3, 4, 96, FAKE, None, FAKE, FAKE, None, None, 0, None) == 2
+    assert L.w4a4_quantize_act(3, 4, 128, None, None, FAKE, FAKE, None, None, 0, None) == 1
+    assert L.w4a4_quantize_act(3, 4, 128, FAKE_MIS, None, FAKE, FAKE, None, None, 0, None) == 3
+    # pack / linear: N % 16, K % 64, NULL r, misaligned blob
+    assert L.w4a4_pack_weight(3, 24, 128, FAKE, FAKE, None, FAKE, FAKE, None) == 2
+    assert L.w4a4_pack_weight(3, 16, 96, FAKE, FAKE, None, FAKE, FAKE, None) == 2
+    assert L.w4a4_pack_weight(3, 16, 128, FAKE, FAKE, None, None, FAKE, None) == 1
+    assert L.w4a4_linear(3, 4, 16, 96, FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == 2
+    assert L.w4a4_linear(3, 4, 16, 128, FAKE, FAKE, None, FAKE_MIS, FAKE, None, 0, None) == 3
+    assert L.w4a4_linear(3, 0, 16, 128, None, None, None, None, None, None, 0, None) == 0
+    # the multi-output quantizer, grouped linear and solver do not take this format
+    assert L.w4a4_quantize_act_multi(3, 4, 128, FAKE, 1, arr, arr, arr, None, None, 0, None) == 4
+    assert L.w4a4_linear_grouped(3, 1, 4, 128, n, arr, arr, None, arr, arr, None) == 4
+    assert L.w4a4_dualquant_solve(3, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                  1 << 30, None) == 4
+    assert "INT4 G=64" in L.w4a4_last_error().decode()

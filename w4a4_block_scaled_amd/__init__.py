@@ -21,10 +21,10 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["FORMATS", "lib", "library_path", "block_size", "quantize_act", "pack_weight",
+__all__ = ["FORMATS", "lib", "library_path", "block_size", "scale_dtype", "quantize_act", "pack_weight",
            "unpack_weight", "linear", "linear_workspace", "packed_weight_bytes", "W4A4Error"]
 
-FORMATS = {"mxfp4": 0, "nvfp4": 1, "mxint4": 2}
+FORMATS = {"mxfp4": 0, "nvfp4": 1, "mxint4": 2, "int4g64": 3}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
@@ -103,6 +103,11 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def scale_dtype(fmt) -> torch.dtype:
+    """Element type of block scales: bytes (E8M0 / UE4M3), BF16 for INT4 G=64."""
+    return torch.bfloat16 if _fmt(fmt) == FORMATS["int4g64"] else torch.uint8
+
+
 def block_size(fmt) -> int:
     return lib().w4a4_block_size(_fmt(fmt))
 
@@ -116,8 +121,8 @@ def quantize_act(x: torch.Tensor, c: Optional[torch.Tensor], fmt,
                  workspace: Optional[torch.Tensor] = None):
     """w4a4_quantize_act: x bf16 [M, K], c fp32 [K] or None -> (codes, scales, t).
 
-    codes uint8 [M, K/2], scales uint8 [M, K/G], t fp32 [1] (NVFP4 tensor
-    scale; unused for MX formats).
+    codes uint8 [M, K/2], scales [M, K/G] (uint8; bfloat16 for INT4 G=64),
+    t fp32 [1] (NVFP4 tensor scale; unused for the other formats).
     """
     f = _fmt(fmt)
     L = lib()
@@ -125,7 +130,7 @@ def quantize_act(x: torch.Tensor, c: Optional[torch.Tensor], fmt,
     G = L.w4a4_block_size(f)
     if out is None:
         codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((M, K // G), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((M, K // G), dtype=scale_dtype(fmt), device=x.device)
         t = torch.ones(1, dtype=torch.float32, device=x.device)
     else:
         codes, scales, t = out
@@ -187,7 +192,7 @@ def unpack_weight(blob: torch.Tensor, fmt, N: int, K: int):
     G = L.w4a4_block_size(f)
     dev = blob.device
     codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((N, K // G), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // G), dtype=scale_dtype(fmt), device=dev)
     r = torch.empty(N, dtype=torch.float32, device=dev)
     t_w = torch.empty(1, dtype=torch.float32, device=dev)
     _check(L.w4a4_unpack_weight(f, N, K, _ptr(blob), _ptr(codes), _ptr(scales), _ptr(r), _ptr(t_w),

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw4a4.so")
-SOURCES = ["quantize.hip", "pack.hip", "gemm.hip", "solver.hip", "capi.cpp"]
+SOURCES = ["quantize.hip", "pack.hip", "gemm.hip", "solver.hip", "int4g64.hip", "capi.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -29,6 +29,20 @@ w4a4_status ok() {
 
 bool valid_fmt(w4a4_format f) { return f == W4A4_MXFP4 || f == W4A4_NVFP4 || f == W4A4_MXINT4; }
 
+// INT4 with G = 64 and BF16 scales has its own kernels (int4g64.hip)
+bool is_i4(w4a4_format f) { return f == W4A4_INT4G64; }
+
+w4a4_status check_i4_shape(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N % 16 || K % 64 || N > (int64_t(1) << 31) || K > (int64_t(1) << 31))
+    return fail(W4A4_ERR_SHAPE, "INT4 G=64: N=%lld K=%lld (need N > 0, N %% 16 == 0, K > 0, K %% 64 == 0)",
+                (long long)N, (long long)K);
+  return W4A4_OK;
+}
+
+w4a4_status not_for_i4(const char* what) {
+  return fail(W4A4_ERR_FORMAT, "%s: not available for INT4 G=64 (MX and NVFP4 formats only)", what);
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 w4a4_status hip_status(hipError_t e, const char* what) {
@@ -52,14 +66,19 @@ w4a4_status check_gemm_shape(w4a4_format fmt, int64_t N, int64_t K) {
 
 extern "C" {
 
-int w4a4_block_size(w4a4_format fmt) { return valid_fmt(fmt) ? w4a4::block_size(fmt) : 0; }
+int w4a4_block_size(w4a4_format fmt) {
+  if (is_i4(fmt)) return 64;
+  return valid_fmt(fmt) ? w4a4::block_size(fmt) : 0;
+}
 
 size_t w4a4_act_codes_bytes(w4a4_format fmt, int64_t M, int64_t K) {
+  if (is_i4(fmt)) return (M < 0 || K <= 0 || K % 64) ? 0 : size_t(M) * size_t(K) / 2;
   if (!valid_fmt(fmt) || M < 0 || K <= 0 || K % w4a4::block_size(fmt)) return 0;
   return size_t(M) * size_t(K) / 2;
 }
 
 size_t w4a4_act_scales_bytes(w4a4_format fmt, int64_t M, int64_t K) {
+  if (is_i4(fmt)) return (M < 0 || K <= 0 || K % 64) ? 0 : size_t(M) * size_t(K / 64) * 2;
   if (!valid_fmt(fmt) || M < 0 || K <= 0 || K % w4a4::block_size(fmt)) return 0;
   return size_t(M) * size_t(K / w4a4::block_size(fmt));
 }
@@ -69,6 +88,7 @@ size_t w4a4_quantize_workspace_bytes(w4a4_format fmt, int64_t, int64_t) {
 }
 
 size_t w4a4_packed_weight_bytes(w4a4_format fmt, int64_t N, int64_t K) {
+  if (is_i4(fmt)) return check_i4_shape(N, K) == W4A4_OK ? w4a4::int4g64_packed_weight_bytes(N, K) : 0;
   if (check_gemm_shape(fmt, N, K) != W4A4_OK) return 0;
   return size_t(w4a4::blob_layout(fmt, N, K).total);
 }
@@ -81,6 +101,19 @@ size_t w4a4_linear_workspace_bytes(w4a4_format fmt, int64_t M, int64_t N, int64_
 w4a4_status w4a4_quantize_act(w4a4_format fmt, int64_t M, int64_t K, const void* X,
                               const float* c, void* codes, void* scales, float* t_act,
                               void* workspace, size_t ws_bytes, void* stream) {
+  if (is_i4(fmt)) {
+    if (M < 0 || K <= 0 || K % 64)
+      return fail(W4A4_ERR_SHAPE, "quantize_act: M=%lld K=%lld (need M >= 0, K > 0, K %% 64 == 0)",
+                  (long long)M, (long long)K);
+    if (M * K / 8 > (int64_t(1) << 40)) return fail(W4A4_ERR_SHAPE, "quantize_act: tensor too large");
+    if (M > 0 && (!X || !codes || !scales))
+      return fail(W4A4_ERR_NULL, "quantize_act: X, codes and scales must be non-NULL");
+    if (!aligned(X, 16) || (c && !aligned(c, 16)) || !aligned(codes, 4) || !aligned(scales, 2))
+      return fail(W4A4_ERR_ALIGN, "quantize_act: X and c need 16-byte, codes 4-byte, scales 2-byte alignment");
+    return hip_status(w4a4::launch_quantize_int4g64(M, K, X, c, codes, scales,
+                                                    static_cast<hipStream_t>(stream)),
+                      "quantize_act launch");
+  }
   if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
   const int G = w4a4::block_size(fmt);
   if (M < 0 || K <= 0 || K % G)
@@ -108,6 +141,7 @@ w4a4_status w4a4_quantize_act_multi(w4a4_format fmt, int64_t M, int64_t K, const
                                     const float* const* c, void* const* codes,
                                     void* const* scales, float* const* t_act, void* workspace,
                                     size_t ws_bytes, void* stream) {
+  if (is_i4(fmt)) return not_for_i4("quantize_act_multi");
   if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
   const int G = w4a4::block_size(fmt);
   if (M < 0 || K <= 0 || K % G || P < 1 || P > w4a4::kMaxOutputs)
@@ -140,6 +174,17 @@ w4a4_status w4a4_quantize_act_multi(w4a4_format fmt, int64_t M, int64_t K, const
 w4a4_status w4a4_pack_weight(w4a4_format fmt, int64_t N, int64_t K, const void* codes,
                              const void* scales, const float* t_w, const float* r, void* blob,
                              void* stream) {
+  if (is_i4(fmt)) {
+    w4a4_status st = check_i4_shape(N, K);
+    if (st != W4A4_OK) return st;
+    if (!codes || !scales || !r || !blob)
+      return fail(W4A4_ERR_NULL, "pack_weight: codes, scales, r and blob must be non-NULL");
+    if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(blob, 256) || !aligned(r, 4))
+      return fail(W4A4_ERR_ALIGN, "pack_weight: codes 16-byte, scales 2-byte, blob 256-byte, r 4-byte alignment");
+    return hip_status(w4a4::launch_pack_int4g64(N, K, codes, scales, r, blob,
+                                                static_cast<hipStream_t>(stream)),
+                      "pack_weight launch");
+  }
   w4a4_status st = check_gemm_shape(fmt, N, K);
   if (st != W4A4_OK) return st;
   if (!codes || !scales || !r || !blob)
@@ -153,6 +198,17 @@ w4a4_status w4a4_pack_weight(w4a4_format fmt, int64_t N, int64_t K, const void* 
 
 w4a4_status w4a4_unpack_weight(w4a4_format fmt, int64_t N, int64_t K, const void* blob,
                                void* codes, void* scales, float* r, float* t_w, void* stream) {
+  if (is_i4(fmt)) {
+    w4a4_status st = check_i4_shape(N, K);
+    if (st != W4A4_OK) return st;
+    if (!blob) return fail(W4A4_ERR_NULL, "unpack_weight: blob must be non-NULL");
+    if (!aligned(blob, 256) || (codes && !aligned(codes, 16)) || (scales && !aligned(scales, 2)) ||
+        (r && !aligned(r, 4)) || (t_w && !aligned(t_w, 4)))
+      return fail(W4A4_ERR_ALIGN, "unpack_weight: blob 256-byte, codes 16-byte, scales 2-byte, r/t_w 4-byte alignment");
+    return hip_status(w4a4::launch_unpack_int4g64(N, K, blob, codes, scales, r, t_w,
+                                                  static_cast<hipStream_t>(stream)),
+                      "unpack_weight launch");
+  }
   w4a4_status st = check_gemm_shape(fmt, N, K);
   if (st != W4A4_OK) return st;
   if (!blob) return fail(W4A4_ERR_NULL, "unpack_weight: blob must be non-NULL");
@@ -167,6 +223,19 @@ w4a4_status w4a4_unpack_weight(w4a4_format fmt, int64_t N, int64_t K, const void
 w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
                         const void* a_scales, const float* t_act, const void* blob, void* Y,
                         void* workspace, size_t ws_bytes, void* stream) {
+  if (is_i4(fmt)) {
+    w4a4_status st = check_i4_shape(N, K);
+    if (st != W4A4_OK) return st;
+    if (M < 0 || M > (int64_t(1) << 31)) return fail(W4A4_ERR_SHAPE, "linear: M=%lld out of range", (long long)M);
+    if (M == 0) return ok();
+    if (!a_codes || !a_scales || !blob || !Y)
+      return fail(W4A4_ERR_NULL, "linear: a_codes, a_scales, blob and Y must be non-NULL");
+    if (!aligned(a_codes, 16) || !aligned(a_scales, 16) || !aligned(blob, 256) || !aligned(Y, 16))
+      return fail(W4A4_ERR_ALIGN, "linear: a_codes/a_scales/Y need 16-byte, blob 256-byte alignment");
+    return hip_status(w4a4::launch_linear_int4g64(M, N, K, a_codes, a_scales, blob, Y,
+                                                  static_cast<hipStream_t>(stream)),
+                      "linear launch");
+  }
   w4a4_status st = check_gemm_shape(fmt, N, K);
   if (st != W4A4_OK) return st;
   if (M < 0 || M > (int64_t(1) << 31)) return fail(W4A4_ERR_SHAPE, "linear: M=%lld out of range", (long long)M);
@@ -192,6 +261,7 @@ w4a4_status w4a4_linear_grouped(w4a4_format fmt, int P, int64_t M, int64_t K, co
                                 const void* const* a_codes, const void* const* a_scales,
                                 const float* const* t_act, const void* const* blobs,
                                 void* const* Y, void* stream) {
+  if (is_i4(fmt)) return not_for_i4("linear_grouped");
   if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
   if (P < 1 || P > w4a4::kMaxGroup || M < 0)
     return fail(W4A4_ERR_SHAPE, "linear_grouped: P=%d M=%lld (need 1 <= P <= %d, M >= 0)", P,
@@ -225,6 +295,7 @@ size_t w4a4_dualquant_workspace_bytes(w4a4_format fmt, int64_t N, int64_t K) {
 w4a4_status w4a4_dualquant_solve(w4a4_format fmt, int64_t N, int64_t K, const float* W, int iters,
                                  float* r, float* c, void* codes, void* scales, float* t_w,
                                  void* workspace, size_t ws_bytes, void* stream) {
+  if (is_i4(fmt)) return not_for_i4("dualquant_solve");
   if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
   if (N <= 0 || K <= 0 || K % 32 || N * K > (int64_t(1) << 36) || iters < 1)
     return fail(W4A4_ERR_SHAPE,

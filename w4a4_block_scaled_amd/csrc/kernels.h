@@ -54,4 +54,21 @@ hipError_t launch_dualquant_solve(int fmt, int64_t N, int64_t K, const float* W,
                                   float* r, float* c, void* codes, void* scales, float* t_w,
                                   void* workspace, hipStream_t stream);
 
+// INT4 with G = 64 and BF16 block scales (int4g64.hip): canonical codes
+// [rows x K/2], scales [rows x K/64] BF16 bit patterns.
+size_t int4g64_packed_weight_bytes(int64_t N, int64_t K);
+
+hipError_t launch_quantize_int4g64(int64_t M, int64_t K, const void* X, const float* c,
+                                   void* codes, void* scales, hipStream_t stream);
+
+hipError_t launch_pack_int4g64(int64_t N, int64_t K, const void* codes, const void* scales,
+                               const float* r, void* blob, hipStream_t stream);
+
+hipError_t launch_unpack_int4g64(int64_t N, int64_t K, const void* blob, void* codes, void* scales,
+                                 float* r, float* t_w, hipStream_t stream);
+
+hipError_t launch_linear_int4g64(int64_t M, int64_t N, int64_t K, const void* a_codes,
+                                 const void* a_scales, const void* blob, void* Y,
+                                 hipStream_t stream);
+
 }  // namespace w4a4

@@ -42,8 +42,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-FORMATS = ("mxfp4", "nvfp4", "mxint4")
-BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32}
+FORMATS = ("mxfp4", "nvfp4", "mxint4", "int4g64")
+BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32, "int4g64": 64}
 
 LLAMA_LINEARS = (("qkv", 6144, 4096), ("o", 4096, 4096),
                  ("gate_up", 28672, 4096), ("down", 4096, 14336))
@@ -57,6 +57,8 @@ WORKLOADS = {
     "llama_prefill": (3, "mxfp4", (2048,), LLAMA_LINEARS),
     "llama_nvfp4": (4, "nvfp4", (4096,), LLAMA_LINEARS),
     "qwen_mxint4": (5, "mxint4", (1, 512, 4096), QWEN_LINEARS),
+    # INT4 G=64 with BF16 scales: Llama shapes, prefill and decode
+    "llama_int4g64": (6, "int4g64", (2048, 1), LLAMA_LINEARS),
 }
 
 
@@ -70,7 +72,8 @@ class LinearCase:
     w_prescaled : torch.bfloat16 [N, K] weights already divided by r and c,
                   to be quantized by the method's quantizer (or None)
     w_codes     : uint8 [N, K/2] canonical packed codes (or None)
-    w_scales    : uint8 [N, K/G] block scale bytes (or None)
+    w_scales    : uint8 [N, K/G] block scale bytes (uint16 BF16 patterns for
+                  int4g64) (or None)
     t_w         : float tensor scale of the weights when codes are drawn
     """
     workload: str
@@ -110,7 +113,22 @@ def admissible_scales(rng: np.random.Generator, n: int, family: str) -> np.ndarr
         e = np.floor(z).astype(np.int64)
         m = rng.integers(0, 8, n)
         return np.ldexp(1.0 + m / 8.0, e).astype(np.float32)
+    if family == "bf16":
+        return to_bf16(np.exp(z * math.log(2.0)).astype(np.float32)).float().numpy()
     raise ValueError(family)
+
+
+def scale_family(fmt: str) -> str:
+    return {"nvfp4": "ue4m3", "int4g64": "bf16"}.get(fmt, "e8m0")
+
+
+def random_codes_bf16(rng: np.random.Generator, N: int, K: int, exp_lo: int, exp_hi: int):
+    """Canonical packed codes uniform over all 16 nibbles and BF16 block scales
+    2^e (1 + m/128), e in U{lo..hi}, m in U{0..127} (uint16 bit patterns, G = 64)."""
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    e = rng.integers(exp_lo, exp_hi + 1, size=(N, K // 64))
+    m = rng.integers(0, 128, size=(N, K // 64))
+    return codes, (((127 + e) << 7) | m).astype(np.uint16)
 
 
 def outlier_activations(rng: np.random.Generator, M: int, K: int, n_out: int,
@@ -148,19 +166,21 @@ def make_case(workload: str, name: str, fmt: str, M: int, N: int, K: int,
     """Build one linear of a workload; the seed fixes every tensor."""
     rx, rc, rr, rw = _rngs(seed, 4)
     G = BLOCK[fmt]
-    family = "ue4m3" if fmt == "nvfp4" else "e8m0"
+    family = scale_family(fmt)
     c = admissible_scales(rc, K, family)
     r = admissible_scales(rr, N, family)
     if workload == "llama_nvfp4":
         x = student_t_activations(rx, M, K)
-    elif workload in ("llama_decode", "llama_prefill"):
+    elif workload in ("llama_decode", "llama_prefill", "llama_int4g64"):
         x = outlier_activations(rx, M, K, int(round(0.01 * K)), 30.0)
     else:  # single, qwen_mxint4 and ad-hoc cases: the single-linear distributions
         x = outlier_activations(rx, M, K, int(round(2 * K / 256)), 50.0)
     case = LinearCase(workload, name, fmt, M, N, K, x, c, r)
     if not build_weights:
         return case
-    if workload in ("single", "qwen_mxint4"):
+    if workload == "llama_int4g64":
+        case.w_codes, case.w_scales = random_codes_bf16(rw, N, K, -9, -6)
+    elif workload in ("single", "qwen_mxint4"):
         lo = -6 if fmt == "mxfp4" else -7
         case.w_codes, case.w_scales = random_codes(rw, N, K, G, lo, 1)
     else:
@@ -192,7 +212,7 @@ def adhoc_case(fmt: str, M: int, N: int, K: int, seed: int,
     or "none".
     """
     rx, rc, rr, rw = _rngs(seed, 4)
-    family = "ue4m3" if fmt == "nvfp4" else "e8m0"
+    family = scale_family(fmt)
     c = admissible_scales(rc, K, family)
     r = admissible_scales(rr, N, family)
     x = outlier_activations(rx, M, K, int(round(2 * K / 256)), 50.0)
