@@ -46,9 +46,12 @@ PEAK = {  # MI355X published dense peaks
     "mxfp4": (10.1e15, "TFLOP/s", "mfma"),   # FP4 / FP6 MFMA
     "mxint4": (5.0e15, "TFLOP/s", "mfma"),   # runs on the FP8 scaled MFMA
     "nvfp4": (2.5e15, "TFLOP/s", "mfma"),    # runs on the fp16 MFMA
+    "int4g64": (5.0e15, "TOP/s", "mfma"),    # int8 MFMA (5.0 POP/s dense)
 }
 HBM_PEAK = 8.0e12
-DTYPE = {"mxfp4": "fp4", "nvfp4": "fp4xe4m3->fp16", "mxint4": "int4->fp8"}
+DTYPE = {"mxfp4": "fp4", "nvfp4": "fp4xe4m3->fp16", "mxint4": "int4->fp8",
+         "int4g64": "int4->int8 (bf16 block scales)"}
+SCALE_BYTES = {"int4g64": 2}   # bytes per block scale (1 for E8M0 / UE4M3)
 
 
 def log(*a):
@@ -64,6 +67,8 @@ class Layer:
         if case.w_codes is not None:
             wc = torch.from_numpy(case.w_codes).to(dev)
             ws = torch.from_numpy(case.w_scales).to(dev)
+            if case.fmt == "int4g64":                       # BF16 bit patterns
+                ws = torch.from_numpy(case.w_scales.view(np.int16)).to(dev).view(torch.bfloat16)
             tw = torch.tensor([case.t_w], dtype=torch.float32, device=dev)
         else:
             wc, ws, tw = w4.quantize_act(case.w_prescaled.to(dev), None, case.fmt)
@@ -73,7 +78,7 @@ class Layer:
         self.c = torch.from_numpy(case.c).to(dev)
         G = w4.block_size(case.fmt)
         self.codes = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device=dev)
-        self.scales = torch.empty((self.M, self.K // G), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((self.M, self.K // G), dtype=w4.scale_dtype(case.fmt), device=dev)
         self.t = torch.ones(1, dtype=torch.float32, device=dev)
         self.ws = torch.empty(max(16, w4.lib().w4a4_quantize_workspace_bytes(
             w4.FORMATS[case.fmt], self.M, self.K)), dtype=torch.uint8, device=dev)
@@ -94,12 +99,12 @@ class Layer:
     @property
     def quant_bytes(self):
         """quantize_act algorithmic bytes: X in, c in, codes and scales out."""
-        G = w4.block_size(self.fmt)
+        G = w4.block_size(self.fmt) / SCALE_BYTES.get(self.fmt, 1)
         return 2 * self.M * self.K + 4 * self.K + self.M * self.K / 2 + self.M * self.K / G
 
     @property
     def gemm_bytes(self):
-        G = w4.block_size(self.fmt)
+        G = w4.block_size(self.fmt) / SCALE_BYTES.get(self.fmt, 1)
         return (self.N * self.K / 2 + self.N * self.K / G + 4 * self.N + self.M * self.K / 2 +
                 self.M * self.K / G + 2 * self.M * self.N)
 
@@ -268,6 +273,33 @@ def solver_rate(dev, iters=15):
     return {"format": "mxfp4", "iters": iters, "layer_ms": round(total, 3), "per_linear": out}
 
 
+def int4g64_rates(dev, steps, warmup, M=2048):
+    """INT4 G=64 with BF16 block scales (the pages' packed deployment format)
+    on the Llama linears: prefill at M tokens (quantize_act + linear per
+    linear, graph-timed step; GEMM rates from per-launch events, against the
+    int8 MFMA peak) and the decode weight-streaming rate at M = 1."""
+    layers = [Layer(c, dev) for c in inputs.workload_cases("llama_int4g64", M=M)]
+    torch.cuda.synchronize()
+    _, gemm_ms, quant_ms = time_steps(layers, steps, warmup)
+    ms = time_graph(layers, steps, warmup)
+    peak = PEAK["int4g64"][0]
+    ops = sum(L.flops for L in layers)
+    out = {"prefill_M%d" % M: {
+        "step_ms": round(ms, 4), "TOP/s_step": round(ops / (ms * 1e-3) / 1e12, 1),
+        "TOP/s_gemm": round(ops / (sum(gemm_ms) * 1e-3) / 1e12, 1),
+        "frac_of_int8_peak": round(ops / (sum(gemm_ms) * 1e-3) / peak, 4),
+        "traffic": traffic_record(f"gemm_llama_int4g64_M{M}", "int4g64"),
+        "kernel": gemm_kernel_label("int4g64", M),
+        "per_linear": {L.case.name: {"gemm_us": round(t * 1e3, 2),
+                                     "TOP/s": round(L.flops / (t * 1e-3) / 1e12, 1),
+                                     "quantize_us": round(qt * 1e3, 2)}
+                       for L, t, qt in zip(layers, gemm_ms, quant_ms)}}}
+    del layers
+    torch.cuda.empty_cache()
+    out["decode_hbm"] = decode_bandwidth(dev, steps, "llama_int4g64", (1,))
+    return out
+
+
 def decode_bandwidth(dev, steps, workload="llama_decode", Ms=(1, 4, 16), copies=32):
     """Weight-streaming rate of the GEMM at small M (default: MXFP4 Llama
     shapes at M = 1, 4, 16).
@@ -288,7 +320,7 @@ def decode_bandwidth(dev, steps, workload="llama_decode", Ms=(1, 4, 16), copies=
         # quantized activations for this M
         q = [w4.quantize_act(x, c, fmt) for x, c in act]
         ys = [torch.empty((M, L.N), dtype=torch.bfloat16, device=dev) for L in base]
-        G = w4.block_size(fmt)
+        G = w4.block_size(fmt) / SCALE_BYTES.get(fmt, 1)
         nbytes = sum(L.N * L.K / 2 + L.N * L.K / G + 4 * L.N + M * L.K / 2 + M * L.K / G +
                      2 * M * L.N for L in base)
 
@@ -367,10 +399,12 @@ def gemm_kernel_label(fmt, M):
             return "gemm_decode_kernel<mxint4>"
         return ("gemm_mx_lean_kernel<mxint4> (256x256 tiles, where their rounds over the CUs are not "
                 "coarser) and gemm_mx_kernel<mxint4> (256x128 tiles)")
+    if fmt == "int4g64":
+        return "gemm_int4g64_decode_kernel" if M <= 16 else "gemm_int4g64_tile_kernel<4, 4>"
     return "gemm_nv_decode_kernel" if M <= 16 else "gemm_tile_kernel<nvfp4>"
 
 
-def traffic_record(kernel):
+def traffic_record(kernel, fmt="mxfp4"):
     """Measured HBM bytes per GEMM launch (FETCH_SIZE + WRITE_SIZE, each scaled
     by its reading for a 1 GiB copy), averaged over the workload's launches,
     from the committed rocprofv3 counter summary -- None unless the counters
@@ -379,8 +413,12 @@ def traffic_record(kernel):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "w4a4_block_scaled_amd", "csrc", "gemm.hip"), "rb").read()
-    if rec.get("gemm_source_sha256") != hashlib.sha256(src).hexdigest() or kernel not in rec:
+    name = "int4g64.hip" if fmt == "int4g64" else "gemm.hip"
+    src = open(os.path.join(ROOT, "w4a4_block_scaled_amd", "csrc", name), "rb").read()
+    if kernel not in rec:
+        return None
+    want = rec[kernel].get("source_sha256", rec.get("gemm_source_sha256"))
+    if want != hashlib.sha256(src).hexdigest():
         return None
     return round(rec[kernel]["traffic_bytes_per_launch"])
 
@@ -411,6 +449,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-solver", action="store_true")
+    ap.add_argument("--no-int4g64", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB calibration copy and one pass of the kernels, print nothing")
     a = ap.parse_args()
@@ -439,7 +478,7 @@ def main():
     achieved = sum(L.flops for L in layers) / (sum(gemm_ms) * 1e-3)   # per-launch average
     roof = {"bound": bound, "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12,
             "unit": unit, "frac": round(achieved / peak, 4),
-            "traffic": traffic_record(f"gemm_{a.workload}_M{M}"),
+            "traffic": traffic_record(f"gemm_{a.workload}_M{M}", fmt),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes_per_launch": round(sum(L.gemm_bytes for L in layers) / len(layers)),
             "kernel": gemm_kernel_label(fmt, M),
@@ -474,6 +513,9 @@ def main():
         out["dualquant_solver"] = solver_rate(dev)
         log("[bench] per-projection c: q, k, v with their own column scales")
         out["per_projection"] = per_projection_rate(dev)
+    if not a.no_int4g64 and a.workload != "llama_int4g64":
+        log("[bench] INT4 G=64 with BF16 scales (Llama, prefill and decode)")
+        out["int4g64"] = int4g64_rates(dev, a.steps, a.warmup)
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(a.workload, M)

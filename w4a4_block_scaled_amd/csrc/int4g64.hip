@@ -203,20 +203,40 @@ __device__ inline v4i mfma_block(v4i a, v4i w) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, w, zero, 0, 0, 0);
 }
 
-// acc[v] += sum * Delta_a[row v] * Delta_w[col] * 2^-8; sw8 = Delta_w * 2^-8
-// (exact: BF16 values keep at most 8 significant bits above 2^-141).
-__device__ inline void scale_add(float* acc, v4i s, const float* sa, float sw8) {
+// Both GEMM kernels put the weight fragment in the MFMA's row operand and the
+// activation fragment in its column operand, so lane l holds the outputs
+// (activation row l % 16, weight columns 4 (l / 16) .. +4): one activation
+// scale per fragment, the four weight scales in one 8-byte load and the four
+// outputs in one 8-byte store.
+__device__ inline void store4(uint16_t* y, const float* acc, const float* rn) {
+  uint16_t o[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) acc[v] = fmaf(float(s[v]), sa[v] * sw8, acc[v]);
+  for (int v = 0; v < 4; ++v) bf16_round_f32(acc[v] * rn[v], &o[v]);
+  *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(o[0]) | (uint32_t(o[1]) << 16),
+                                            uint32_t(o[2]) | (uint32_t(o[3]) << 16));
+}
+
+// acc[v] += sum[v] * Delta_a * Delta_w[v] * 2^-8 with sw8 = Delta_w * 2^-8
+// (exact: BF16 values keep at most 8 significant bits above 2^-141).
+__device__ inline void scale_add4(float* acc, v4i s, float sa, const float* sw8) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) acc[v] = fmaf(float(s[v]), sa * sw8[v], acc[v]);
+}
+
+__device__ inline void unpack_sw8(uint2 w, float* sw8) {
+  sw8[0] = bf16_bits_to_f32(w.x & 0xFFFFu) * 0.00390625f;
+  sw8[1] = bf16_bits_to_f32(w.x >> 16) * 0.00390625f;
+  sw8[2] = bf16_bits_to_f32(w.y & 0xFFFFu) * 0.00390625f;
+  sw8[3] = bf16_bits_to_f32(w.y >> 16) * 0.00390625f;
 }
 
 // Tile kernel: 4 waves as 2 (M) x 2 (N); a wave owns FM x FN fragments of
 // 16 x 16 outputs, the workgroup (2 FM 16) x (2 FN 16).  Operands come
-// straight from global memory (activation rows clamped to M - 1, weight row
-// groups to NG - 1, so every load is in bounds); outputs outside M x N are
-// not stored.
+// straight from global memory, the next K block's while the current one is
+// multiplied (activation rows clamped to M - 1, weight row groups to NG - 1,
+// so every load is in bounds); outputs outside M x N are not stored.
 template <int FM, int FN>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_int4g64_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
                          const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M,
                          int64_t N, int64_t K) {
@@ -224,25 +244,21 @@ gemm_int4g64_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t m0 = int64_t(blockIdx.y) * (2 * FM * 16) + (wave >> 1) * (FM * 16);
   const int64_t g0 = int64_t(blockIdx.x) * (2 * FN) + (wave & 1) * FN;
-  const uint8_t* wcodes = blob + L.code_off;
-  const uint16_t* wscales = reinterpret_cast<const uint16_t*>(blob + L.scale_off);
-  const int64_t kb2 = K / 2;
+  const uint8_t* wcodes = blob + L.code_off + lane * 8;
+  const uint16_t* wscales = reinterpret_cast<const uint16_t*>(blob + L.scale_off) + 4 * (lane >> 4);
 
   const uint8_t* arow[FM];
-  const uint16_t* srow[FM][4];
+  const uint16_t* srow[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    int64_t m = m0 + i * 16 + (lane & 15);
-    arow[i] = a_codes + (m < M ? m : M - 1) * kb2 + (lane >> 4) * 8;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      int64_t mv = m0 + i * 16 + 4 * (lane >> 4) + v;
-      srow[i][v] = a_scales + (mv < M ? mv : M - 1) * L.KB;
-    }
+    const int64_t m = m0 + i * 16 + (lane & 15);
+    const int64_t mc = m < M ? m : M - 1;
+    arow[i] = a_codes + mc * (K / 2) + (lane >> 4) * 8;
+    srow[i] = a_scales + mc * L.KB;
   }
-  int64_t gidx[FN];
+  int64_t gbase[FN];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) gidx[j] = g0 + j < L.NG ? g0 + j : L.NG - 1;
+  for (int j = 0; j < FN; ++j) gbase[j] = (g0 + j < L.NG ? g0 + j : L.NG - 1) * L.KB;
 
   float acc[FM][FN][4];
 #pragma unroll
@@ -252,121 +268,131 @@ gemm_int4g64_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
 
-  for (int64_t b = 0; b < L.KB; ++b) {
-    v4i A[FM], W[FN];
-    float sa[FM][4], sw8[FN];
+  uint2 ca[FM], cw[FN], csw[FN];
+  uint16_t csa[FM];
+  auto load = [&](int64_t b, uint2* a, uint16_t* sa, uint2* w, uint2* sw) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      A[i] = widen(*reinterpret_cast<const uint2*>(arow[i] + b * 32));
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sa[i][v] = bf16_bits_to_f32(srow[i][v][b]);
+      a[i] = *reinterpret_cast<const uint2*>(arow[i] + b * 32);
+      sa[i] = srow[i][b];
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int64_t tile = gidx[j] * L.KB + b;
-      W[j] = widen(*reinterpret_cast<const uint2*>(wcodes + tile * 512 + lane * 8));
-      sw8[j] = bf16_bits_to_f32(wscales[tile * 16 + (lane & 15)]) * 0.00390625f;
+      const int64_t tile = gbase[j] + b;
+      w[j] = *reinterpret_cast<const uint2*>(wcodes + tile * 512);
+      sw[j] = *reinterpret_cast<const uint2*>(wscales + tile * 16);
+    }
+  };
+  load(0, ca, csa, cw, csw);
+  for (int64_t b = 0; b < L.KB; ++b) {
+    uint2 na[FM], nw[FN], nsw[FN];
+    uint16_t nsa[FM];
+    load(b + 1 < L.KB ? b + 1 : b, na, nsa, nw, nsw);
+    v4i A[FM];
+    float sa[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      A[i] = widen(ca[i]);
+      sa[i] = bf16_bits_to_f32(csa[i]);
     }
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int j = 0; j < FN; ++j) {
+      const v4i W = widen(cw[j]);
+      float sw8[4];
+      unpack_sw8(csw[j], sw8);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) scale_add(acc[i][j], mfma_block(A[i], W[j]), sa[i], sw8[j]);
+      for (int i = 0; i < FM; ++i) scale_add4(acc[i][j], mfma_block(W, A[i]), sa[i], sw8);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      ca[i] = na[i];
+      csa[i] = nsa[i];
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      cw[j] = nw[j];
+      csw[j] = nsw[j];
+    }
   }
 
   const float* r = reinterpret_cast<const float*>(blob + L.r_off);
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     if (g0 + j >= L.NG) continue;
-    const int64_t n = (g0 + j) * 16 + (lane & 15);
-    const float rn = r[n];
+    const int64_t n = (g0 + j) * 16 + 4 * (lane >> 4);
+    const float4 r4 = *reinterpret_cast<const float4*>(r + n);
+    const float rn[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = m0 + i * 16 + 4 * (lane >> 4) + v;
-        if (m < M) {
-          uint16_t o;
-          bf16_round_f32(acc[i][j][v] * rn, &o);
-          Y[m * N + n] = o;
-        }
-      }
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + i * 16 + (lane & 15);
+      if (m < M) store4(Y + m * N + n, acc[i][j], rn);
+    }
   }
 }
 
-// Decode kernel (M <= 16): a workgroup owns one 16-column group g; its 4
-// waves take the K blocks b = wave, wave + 4, ... and their partial sums are
-// added through LDS in wave order, so results do not depend on timing.
-__global__ void __launch_bounds__(256)
+// Decode kernel (M <= 16): a workgroup owns one 16-column group g; its
+// WAVES waves take the K blocks b = wave, wave + WAVES, ... with U blocks'
+// loads in flight, and their partial sums are added through LDS in wave
+// order, so results do not depend on timing.
+template <int WAVES, int U>
+__global__ void __launch_bounds__(64 * WAVES)
 gemm_int4g64_decode_kernel(const uint8_t* __restrict__ a_codes,
                            const uint16_t* __restrict__ a_scales, const uint8_t* __restrict__ blob,
                            uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
-  constexpr int U = 4;
   const I4Layout L = i4_layout(N, K);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t g = blockIdx.x;
   const int64_t ma = (lane & 15) < M ? (lane & 15) : M - 1;
   const uint8_t* arow = a_codes + ma * (K / 2) + (lane >> 4) * 8;
-  const uint16_t* srow[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t mv = 4 * (lane >> 4) + v;
-    srow[v] = a_scales + (mv < M ? mv : M - 1) * L.KB;
-  }
+  const uint16_t* srow = a_scales + ma * L.KB;
   const uint8_t* wtile = blob + L.code_off + g * L.KB * 512 + lane * 8;
-  const uint16_t* wsc = reinterpret_cast<const uint16_t*>(blob + L.scale_off) + g * L.KB * 16 + (lane & 15);
+  const uint16_t* wsc = reinterpret_cast<const uint16_t*>(blob + L.scale_off) + g * L.KB * 16 +
+                        4 * (lane >> 4);
 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   int64_t b = wave;
-  for (; b + 4 * (U - 1) < L.KB; b += 4 * U) {
-    uint2 wa[U], aa[U];
-    uint16_t ws[U], as[U][4];
+  for (; b + WAVES * (U - 1) < L.KB; b += WAVES * U) {
+    uint2 wa[U], aa[U], ws[U];
+    uint16_t as[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t bb = b + 4 * u;
+      const int64_t bb = b + WAVES * u;
       wa[u] = *reinterpret_cast<const uint2*>(wtile + bb * 512);
-      ws[u] = wsc[bb * 16];
+      ws[u] = *reinterpret_cast<const uint2*>(wsc + bb * 16);
       aa[u] = *reinterpret_cast<const uint2*>(arow + bb * 32);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) as[u][v] = srow[v][bb];
+      as[u] = srow[bb];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float sa[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sa[v] = bf16_bits_to_f32(as[u][v]);
-      scale_add(acc, mfma_block(widen(aa[u]), widen(wa[u])), sa,
-                bf16_bits_to_f32(ws[u]) * 0.00390625f);
+      float sw8[4];
+      unpack_sw8(ws[u], sw8);
+      scale_add4(acc, mfma_block(widen(wa[u]), widen(aa[u])), bf16_bits_to_f32(as[u]), sw8);
     }
   }
-  for (; b < L.KB; b += 4) {
-    float sa[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sa[v] = bf16_bits_to_f32(srow[v][b]);
-    scale_add(acc,
-              mfma_block(widen(*reinterpret_cast<const uint2*>(arow + b * 32)),
-                         widen(*reinterpret_cast<const uint2*>(wtile + b * 512))),
-              sa, bf16_bits_to_f32(wsc[b * 16]) * 0.00390625f);
+  for (; b < L.KB; b += WAVES) {
+    float sw8[4];
+    unpack_sw8(*reinterpret_cast<const uint2*>(wsc + b * 16), sw8);
+    scale_add4(acc,
+               mfma_block(widen(*reinterpret_cast<const uint2*>(wtile + b * 512)),
+                          widen(*reinterpret_cast<const uint2*>(arow + b * 32))),
+               bf16_bits_to_f32(srow[b]), sw8);
   }
 
-  __shared__ float part[3][64][4];
+  __shared__ float part[WAVES - 1][64][4];
   if (wave > 0) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) part[wave - 1][lane][v] = acc[v];
   }
   __syncthreads();
   if (wave == 0) {
-    const int64_t n = g * 16 + (lane & 15);
-    const float rn = reinterpret_cast<const float*>(blob + L.r_off)[n];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float s = ((acc[v] + part[0][lane][v]) + part[1][lane][v]) + part[2][lane][v];
-      const int64_t m = 4 * (lane >> 4) + v;
-      if (m < M) {
-        uint16_t o;
-        bf16_round_f32(s * rn, &o);
-        Y[m * N + n] = o;
-      }
-    }
+    for (int w = 0; w < WAVES - 1; ++w)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += part[w][lane][v];
+    const int64_t n = g * 16 + 4 * (lane >> 4);
+    const float4 r4 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(blob + L.r_off) + n);
+    const float rn[4] = {r4.x, r4.y, r4.z, r4.w};
+    if ((lane & 15) < M) store4(Y + int64_t(lane & 15) * N + n, acc, rn);
   }
 }
 
@@ -418,8 +444,9 @@ hipError_t launch_linear_int4g64(int64_t M, int64_t N, int64_t K, const void* a_
   const auto* bl = static_cast<const uint8_t*>(blob);
   auto* y = static_cast<uint16_t*>(Y);
   if (M <= 16) {
-    hipLaunchKernelGGL(gemm_int4g64_decode_kernel, dim3(unsigned(N / 16)), dim3(256), 0, stream,
-                       ac, as, bl, y, M, N, K);
+    constexpr int WAVES = 8, U = 8;
+    hipLaunchKernelGGL((gemm_int4g64_decode_kernel<WAVES, U>), dim3(unsigned(N / 16)),
+                       dim3(64 * WAVES), 0, stream, ac, as, bl, y, M, N, K);
   } else {
     constexpr int FM = 4, FN = 4;
     const dim3 grid(unsigned((N / 16 + 2 * FN - 1) / (2 * FN)),
