@@ -232,7 +232,7 @@ __device__ inline void unpack_sw8(uint2 w, float* sw8) {
 
 // Tile kernel: 4 waves as 2 (M) x 2 (N); a wave owns FM x FN fragments of
 // 16 x 16 outputs, the workgroup (2 FM 16) x (2 FN 16).  Operands come
-// straight from global memory, the next K block's while the current one is
+// straight from global memory, two K blocks ahead of the one being
 // multiplied (activation rows clamped to M - 1, weight row groups to NG - 1,
 // so every load is in bounds); outputs outside M x N are not stored.
 template <int FM, int FN>
@@ -268,51 +268,57 @@ gemm_int4g64_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
 
-  uint2 ca[FM], cw[FN], csw[FN];
-  uint16_t csa[FM];
-  auto load = [&](int64_t b, uint2* a, uint16_t* sa, uint2* w, uint2* sw) {
+  // two register sets: block b + 2's loads go out while block b + 1's are
+  // still in flight, so the in-order load counter only waits for the older set
+  struct Ops {
+    uint2 a[FM], w[FN], sw[FN];
+    uint16_t sa[FM];
+  };
+  auto load = [&](int64_t b, Ops& o) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      a[i] = *reinterpret_cast<const uint2*>(arow[i] + b * 32);
-      sa[i] = srow[i][b];
+      o.a[i] = *reinterpret_cast<const uint2*>(arow[i] + b * 32);
+      o.sa[i] = srow[i][b];
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t tile = gbase[j] + b;
-      w[j] = *reinterpret_cast<const uint2*>(wcodes + tile * 512);
-      sw[j] = *reinterpret_cast<const uint2*>(wscales + tile * 16);
+      o.w[j] = *reinterpret_cast<const uint2*>(wcodes + tile * 512);
+      o.sw[j] = *reinterpret_cast<const uint2*>(wscales + tile * 16);
     }
   };
-  load(0, ca, csa, cw, csw);
-  for (int64_t b = 0; b < L.KB; ++b) {
-    uint2 na[FM], nw[FN], nsw[FN];
-    uint16_t nsa[FM];
-    load(b + 1 < L.KB ? b + 1 : b, na, nsa, nw, nsw);
+  auto compute = [&](const Ops& o) {
     v4i A[FM];
     float sa[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      A[i] = widen(ca[i]);
-      sa[i] = bf16_bits_to_f32(csa[i]);
+      A[i] = widen(o.a[i]);
+      sa[i] = bf16_bits_to_f32(o.sa[i]);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const v4i W = widen(cw[j]);
+      const v4i W = widen(o.w[j]);
       float sw8[4];
-      unpack_sw8(csw[j], sw8);
+      unpack_sw8(o.sw[j], sw8);
 #pragma unroll
       for (int i = 0; i < FM; ++i) scale_add4(acc[i][j], mfma_block(W, A[i]), sa[i], sw8);
     }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      ca[i] = na[i];
-      csa[i] = nsa[i];
+  };
+  const int64_t last = L.KB - 1;
+  Ops p0, p1;
+  load(0, p0);
+  load(last < 1 ? last : 1, p1);
+  // the scheduling barriers keep each set's unpacking (and so its load wait)
+  // after the other set's loads have been issued
+  for (int64_t b = 0; b < L.KB; b += 2) {
+    compute(p0);
+    load(b + 2 < last ? b + 2 : last, p0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (b + 1 < L.KB) {
+      compute(p1);
+      load(b + 3 < last ? b + 3 : last, p1);
     }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      cw[j] = nw[j];
-      csw[j] = nsw[j];
-    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   const float* r = reinterpret_cast<const float*>(blob + L.r_off);
