@@ -454,8 +454,8 @@ def main():
                     help="run a 1 GiB calibration copy and one pass of the kernels, print nothing")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the hot path would shard by tokens or output features; see DESIGN.md)",
+        print("bench.py measures one GPU only: there is no multi-GPU path "
+              "(the hot path would shard by tokens or by output features)",
               file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
