@@ -79,6 +79,11 @@ typedef enum {
   W4A4_ERR_HIP = 6         /* a HIP call or kernel launch failed                */
 } w4a4_status;
 
+/* Split-K workspace of w4a4_linear: bytes of synchronization words and
+ * status at its start, and the byte offset of the int32 status word. */
+#define W4A4_SPLITK_SYNC_BYTES 4352
+#define W4A4_SPLITK_STATUS_OFFSET 4096
+
 /* Block size G of a format (32, 16 or 32); 0 for an unknown format. */
 int w4a4_block_size(w4a4_format fmt);
 
@@ -212,11 +217,18 @@ w4a4_status w4a4_unpack_weight(w4a4_format fmt, int64_t N, int64_t K,
  *            w4a4_linear_workspace_bytes() bytes, 16-byte aligned.  The size
  *            is 0 (and NULL accepted) except for MXFP4 shapes that split K
  *            across two workgroups (M > 32, 64..128 tiles of 256 x 256,
- *            K % 1024 == 0, K >= 8192): 4 KiB of synchronization words plus
- *            256 KiB of fp32 partial sums per tile.  The first 4 KiB must be
- *            zero before the first call that uses the buffer; every call
- *            leaves them zero again.  Calls sharing a workspace must not run
- *            concurrently (issue them in order on one stream).
+ *            K % 1024 == 0, K >= 8192): W4A4_SPLITK_SYNC_BYTES of
+ *            synchronization words and status, then 256 KiB of fp32 partial
+ *            sums per tile.  The first W4A4_SPLITK_SYNC_BYTES must be zero
+ *            before the first call that uses the buffer; every call leaves
+ *            the synchronization words zero again.  The int32 at byte
+ *            W4A4_SPLITK_STATUS_OFFSET is a sticky status: a workgroup whose
+ *            partner half never signalled (the synchronization words were not
+ *            zero at the call) gives up after a bounded wait (about a
+ *            second), ORs 1 into it and writes its 128 x 128 block of Y as
+ *            BF16 NaN; the caller clears the word to reset it.  Calls sharing
+ *            a workspace must not run concurrently (issue them in order on
+ *            one stream).
  *
  * Requires M >= 0, N % 16 == 0, K % 128 == 0.  The blob's fmt, N and K are
  * trusted, not re-read from device memory.

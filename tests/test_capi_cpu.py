@@ -67,8 +67,9 @@ def split_k(M, N, K):
 
 def test_linear_workspace_sizes():
     """Only the MXFP4 split-K GEMM needs scratch: a fixed 4 KiB block of
-    tickets and flags (8 bytes per wave slot of up to 128 tiles), then per
-    tile 4 wave slots of 64 KiB of fp32 partial sums."""
+    tickets and flags (8 bytes per wave slot of up to 128 tiles) and a
+    256-byte status block, then per tile 4 wave slots of 64 KiB of fp32
+    partial sums."""
     L = w4.lib()
     shapes = ((2048, 28672, 4096), (2048, 4096, 14336), (2048, 4096, 4096), (16, 4096, 4096),
               (2048, 6144, 4096), (300, 8208, 8192), (2048, 4096, 9216))
@@ -77,7 +78,7 @@ def test_linear_workspace_sizes():
             got = L.w4a4_linear_workspace_bytes(fmt, M, N, K)
             if fmt == 0 and split_k(M, N, K):
                 T = ((N + 255) // 256) * ((M + 255) // 256)
-                assert got == 4096 + T * 4 * 65536, (M, N, K)
+                assert got == 4096 + 256 + T * 4 * 65536, (M, N, K)
             else:
                 assert got == 0, (fmt, M, N, K)
     assert split_k(2048, 4096, 14336) and not split_k(2048, 4096, 4096) and not split_k(2048, 6144, 14336)

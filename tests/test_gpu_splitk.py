@@ -101,5 +101,42 @@ def test_splitk_repeated_calls_and_clean_workspace():
         Yb2 = w4.linear(ab, sb, tb, blob_b, "mxfp4", b.N, b.K, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(Ya, Y2) and torch.equal(Yb, Yb2)
-        sync_words = ws[:4096].view(torch.int32)
+        sync_words = ws[:4352].view(torch.int32)
         assert int(sync_words.abs().sum()) == 0, "tickets/flags not cleared"
+
+
+def test_splitk_dirty_sync_word_is_reported_not_silent():
+    """A ticket left non-zero before the call (the documented precondition
+    broken on purpose from the host): both halves of that wave slot find a
+    non-zero ticket, neither writes partial sums, and each gives up after
+    its bounded wait.  The call must not return a silently wrong Y: that
+    slot's 128 x 128 block of Y is BF16 NaN, the status word is set, the
+    synchronization words are zero again, every other output equals the
+    clean run, and the next call (status cleared) is clean."""
+    dev = device()
+    M, N, K = 300, 8208, 8192
+    assert split_k(M, N, K)
+    say(f"[split-k dirty ticket] mxfp4 M={M} N={N} K={K}")
+    case = inputs.adhoc_case("mxfp4", M, N, K, seed=31)
+    Ya, blob, (ac, sc, ta), _ = gpu_layer(case, dev)
+    nb = w4.lib().w4a4_linear_workspace_bytes(0, M, N, K)
+    ws = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    words = ws[:4352].view(torch.int32)
+    words[0] = 1                                  # ticket of tile 0, wave slot 0 (rows 0..127, cols 0..127)
+    torch.cuda.synchronize()
+    Y = w4.linear(ac, sc, ta, blob, "mxfp4", N, K, workspace=ws)
+    torch.cuda.synchronize()
+    got = bf16_bits(Y)
+    ref = bf16_bits(Ya)
+    assert np.all(got[:128, :128] == 0x7FC0), "the abandoned block is not NaN"
+    mask = np.ones_like(got, bool)
+    mask[:128, :128] = False
+    assert np.array_equal(got[mask], ref[mask]), "outputs outside the abandoned block changed"
+    w = words.cpu().numpy()
+    assert w[4096 // 4] == 1, "status word not set"
+    assert np.all(w[:4096 // 4] == 0), "tickets/flags not cleared after the timeout"
+    words[4096 // 4] = 0
+    Y2 = w4.linear(ac, sc, ta, blob, "mxfp4", N, K, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Y2, Ya)
+    assert int(words.abs().sum()) == 0

@@ -28,8 +28,10 @@
 //            (16x16x32) accumulates in fp32.  A lane feeds dword j of its
 //            fragment to the j-th of four MFMAs; the same permutation of K
 //            applies to both operands, so the dot products are unchanged.
+#include "w4a4.h"
 #include "common.h"
 #include "kernels.h"
+
 
 namespace w4a4 {
 namespace {
@@ -1815,16 +1817,22 @@ hipError_t launch_fp4_persistent(int64_t M, int64_t N, int64_t K, const uint8_t*
 
 // Workspace: the tickets and flags of up to MAX_TILES tiles at fixed places
 // (one 4 KiB block, whatever the shape, so that shapes sharing a workspace
-// never write partial sums over each other's synchronization words), then
-// the partial-sum slots.
+// never write partial sums over each other's synchronization words), a
+// status word (non-zero once a wave gave up waiting for its partner; the
+// block it owns is then written as NaN), then the partial-sum slots.
 struct Fp4S {
   static constexpr int SLOTS = 4;                   // wave slots per tile
   static constexpr int MAX_TILES = 128;
   static constexpr int SLOT_BYTES = 64 * 1024;      // 128 x 128 fp32
-  static constexpr int SYNC_BYTES = MAX_TILES * SLOTS * 8;
+  static constexpr int WORDS_BYTES = MAX_TILES * SLOTS * 8;
+  static constexpr int STATUS_OFF = WORDS_BYTES;
+  static constexpr int SYNC_BYTES = WORDS_BYTES + 256;
   static constexpr int CACHE_THROUGH = 16;          // sc1: agent-coherent, past the L2s
+  static constexpr int SPIN_LIMIT = 1 << 20;        // polls of the partner's flag (~1 s)
 };
-static_assert(Fp4S::SYNC_BYTES == 4096, "sync block");
+static_assert(Fp4S::WORDS_BYTES == 4096 && Fp4S::SYNC_BYTES == W4A4_SPLITK_SYNC_BYTES &&
+                  Fp4S::STATUS_OFF == W4A4_SPLITK_STATUS_OFFSET,
+              "split-K workspace layout");
 
 // The partner's partial sums for the blocks in epilogue order e = 4 j + i:
 // quarter q of block e is 1 KiB at (4 e + q) KiB, lane l's 16 bytes at 16 l
@@ -1845,15 +1853,35 @@ __device__ __forceinline__ v16f fp4s_load_block(__amdgpu_buffer_rsrc_t pr, int e
 }
 
 // As fp4p_epilogue, with the partner's partial sums added to each block.
+// With met == false (the partner's flag never came) the wave's 128 x 128
+// block of Y is written as BF16 NaN instead, and no partial sum is read.
 __device__ __forceinline__ void fp4s_epilogue(const v16f (&acc)[4][4], __amdgpu_buffer_rsrc_t pr,
                                               LDS uint8_t* base, int rbuf, uint16_t* __restrict__ Y,
                                               int64_t M, int64_t N, int64_t m0, int64_t n0, int wn,
-                                              int wm) {
+                                              int wm, bool met) {
   const int lane = fp4p_lane_id(), h = lane >> 5;
   const LDS uint8_t* rb = base + Fp4P::R_OFF + rbuf * 1024;
   const int64_t rows = M - m0 < Fp4P::BM ? M - m0 : Fp4P::BM;
   const __amdgpu_buffer_rsrc_t ys =
       __builtin_amdgcn_make_buffer_rsrc(Y + m0 * N, 0, int(rows * N * 2), 0x00020000);
+  if (!met) {
+    const int N32 = int(N), row = wm * 128 + (lane & 15);
+    const int n32 = int(n0) + wn * 128 + 8 * (2 * ((lane >> 4) & 1) + h);
+    const u32x4 nan = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n32 + 32 * i;
+        const int past = (N32 - 1 - n) >> 31;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int m = row + 32 * j + 16 * hh;
+          __builtin_amdgcn_raw_buffer_store_b128(nan, ys, ((m * N32 + n) * 2) | past, 0, 0);
+        }
+      }
+    return;
+  }
   v16f pb[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) pb[e] = fp4s_load_block(pr, e, lane);
@@ -1983,18 +2011,43 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_splitk_kernel(
                     __float_as_uint(av[4 * q + 3])},
               pr, ((e * 4 + q) * 64 + l) * 16, 0, Fp4S::CACHE_THROUGH);
       }
-    // the sums have reached the coherent level before the flag is raised
+    // The sums are device-scope write-through stores: once they have
+    // completed (waitcnt) they are at the coherent level, and a
+    // workgroup-scope release fence keeps the flag store behind them.  (An
+    // agent-scope release would also write back this XCD's whole L2, none
+    // of it ours: measured +11 us on the 4096 x 14336 projection.)
     __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     if (lane == 0) __hip_atomic_store(&flags[slot], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    // the other wave is past its K loop: it raises the flag after its stores
+    // the other wave is past its K loop: it raises the flag after its
+    // stores.  The poll is bounded; a wave that gives up (the partner never
+    // raised the flag: synchronization words left non-zero by a caller, or
+    // a partner that never arrived) records it in the status word and
+    // writes its block as NaN rather than adding a slot nobody filled.
+    // The partial sums are read with device-scope (sc1) loads, which see
+    // the coherent level, so the acquire only has to keep them behind the
+    // flag: the poll is an agent-scope load, then a workgroup-scope acquire
+    // fence orders what follows.  (An agent-scope acquire would also
+    // invalidate this XCD's L2, which cost the other workgroups' cached
+    // tiles ~32 us on the 4096 x 14336 projection at M = 2048.)
+    int met = 1;
     if (lane == 0) {
-      for (int n = 0; n < (1 << 20); ++n) {
-        if (__hip_atomic_load(&flags[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+      met = 0;
+      for (int n = 0; n < Fp4S::SPIN_LIMIT; ++n) {
+        if (__hip_atomic_load(&flags[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          met = 1;
+          break;
+        }
         __builtin_amdgcn_s_sleep(2);
       }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      if (!met)
+        __hip_atomic_fetch_or(reinterpret_cast<int*>(ws + Fp4S::STATUS_OFF), 1, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
     }
-    fp4s_epilogue(acc, pr, base, 0, Y, M, N, d0.m0, int64_t(d0.g0) * 32, wn, wm);
+    met = __builtin_amdgcn_readfirstlane(met);
+    fp4s_epilogue(acc, pr, base, 0, Y, M, N, d0.m0, int64_t(d0.g0) * 32, wn, wm, met != 0);
     __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0) {
       __hip_atomic_store(&flags[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
