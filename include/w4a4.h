@@ -22,7 +22,8 @@
  *     of the device that owns `stream` (a hipStream_t; NULL = the null
  *     stream of the current device).  The caller owns all buffers; the
  *     library never allocates, frees or synchronizes, and keeps no pointer
- *     after a call returns.  Work is enqueued on `stream`; buffers must stay
+ *     after a call returns (w4a4_linear_noalloc's scratch array is the
+ *     library's own, see there).  Work is enqueued on `stream`; buffers must stay
  *     valid until the stream has executed it.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     non-OK status means nothing was enqueued.  w4a4_last_error() then
@@ -33,7 +34,8 @@
  *     low nibble of byte j and element 2j+1 in the high nibble.  FP4 codes
  *     are E2M1 (sign bit 3), INT4 codes two's complement.  Canonical scale
  *     layout: [rows x K/G] bytes (E8M0 for MX formats, UE4M3 for NVFP4).
- *   - Calls are reentrant; the library has no mutable global state.
+ *   - Calls are reentrant; the library has no mutable global state, apart
+ *     from the per-device scratch array of w4a4_linear_noalloc.
  */
 #ifndef W4A4_H_
 #define W4A4_H_
@@ -237,6 +239,34 @@ w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K,
                         const void* a_codes, const void* a_scales,
                         const float* t_act, const void* blob, void* Y,
                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * w4a4_linear_noalloc - w4a4_linear for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments as w4a4_linear without the workspace; the same
+ * kernels run and Y is bit for bit what w4a4_linear writes.
+ *
+ * Scratch: the split-K workspace (the only one w4a4_linear uses) is taken
+ * from a device array inside the library, W4A4_NOALLOC_SCRATCH_BYTES
+ * (32 MiB + 4352 B, the largest split-K workspace), one copy on every device
+ * the library runs on, held until the process ends.  Its address on a device
+ * is looked up on the first call on that device (with that device current).
+ * Each split-K call first clears the array's synchronization words and
+ * status with a small kernel on `stream`.  Every call on a device shares
+ * that device's array: calls that overlap on one device (other streams,
+ * other threads, other graphs) race and must be serialized by the caller.
+ * A split-K wave that gives up waiting for its partner writes its 128 x 128
+ * block of Y as BF16 NaN (see w4a4_linear); the status word stays inside the
+ * library.  Shapes whose workspace would exceed the array return
+ * W4A4_ERR_WORKSPACE (none does: split-K shapes have at most 128 tiles).
+ * Nothing is allocated, freed or synchronized.  Not available for
+ * W4A4_INT4G64 (W4A4_ERR_FORMAT).
+ */
+#define W4A4_NOALLOC_SCRATCH_BYTES (4352 + 128 * 4 * 65536)
+w4a4_status w4a4_linear_noalloc(w4a4_format fmt, int64_t M, int64_t N, int64_t K,
+                                const void* a_codes, const void* a_scales,
+                                const float* t_act, const void* blob, void* Y,
+                                void* stream);
 
 /*
  * w4a4_linear_grouped - P linears of one M and K (the per-projection linears

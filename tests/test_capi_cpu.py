@@ -270,3 +270,20 @@ def test_int4g64_rejects():
     assert L.w4a4_dualquant_solve(3, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, None, FAKE,
                                   1 << 30, None) == 4
     assert "INT4 G=64" in L.w4a4_last_error().decode()
+
+
+def test_linear_noalloc_validation():
+    """w4a4_linear_noalloc checks its arguments on the host like w4a4_linear
+    (no workspace argument: the split-K scratch is the library's own)."""
+    L = w4.lib()
+    base = (FAKE, FAKE, None, FAKE, FAKE, None)
+    assert L.w4a4_linear_noalloc(0, 0, 128, 256, None, None, None, None, None, None) == 0  # M = 0
+    assert L.w4a4_linear_noalloc(0, 4, 100, 256, *base) == 2        # N % 16
+    assert L.w4a4_linear_noalloc(0, 4, 128, 200, *base) == 2        # K % 128
+    assert L.w4a4_linear_noalloc(9, 4, 128, 256, *base) == 4        # unknown format
+    assert L.w4a4_linear_noalloc(3, 4, 128, 256, *base) == 4        # INT4 G=64
+    assert L.w4a4_linear_noalloc(1, 4, 128, 256, *base) == 1        # NVFP4 without t_act
+    assert L.w4a4_linear_noalloc(0, 4, 128, 256, None, FAKE, None, FAKE, FAKE, None) == 1
+    assert L.w4a4_linear_noalloc(0, 4, 128, 256, FAKE_MIS, FAKE, None, FAKE, FAKE, None) == 3
+    # the largest split-K workspace fits the scratch array
+    assert L.w4a4_linear_workspace_bytes(0, 2048, 4096, 8192) == 4352 + 128 * 4 * 65536

@@ -22,7 +22,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["FORMATS", "lib", "library_path", "block_size", "scale_dtype", "quantize_act", "pack_weight",
-           "unpack_weight", "linear", "linear_workspace", "packed_weight_bytes", "W4A4Error"]
+           "unpack_weight", "linear", "linear_noalloc", "linear_workspace", "packed_weight_bytes", "W4A4Error"]
 
 FORMATS = {"mxfp4": 0, "nvfp4": 1, "mxint4": 2, "int4g64": 3}
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.w4a4_unpack_weight.restype = i32
     L.w4a4_linear.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     L.w4a4_linear.restype = i32
+    L.w4a4_linear_noalloc.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.w4a4_linear_noalloc.restype = i32
     L.w4a4_dualquant_workspace_bytes.argtypes = [i32, i64, i64]
     L.w4a4_dualquant_workspace_bytes.restype = sz
     L.w4a4_dualquant_solve.argtypes = [i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -235,6 +237,21 @@ def linear(a_codes: torch.Tensor, a_scales: torch.Tensor, t_act: Optional[torch.
                          _ptr(out), _ptr(workspace),
                          workspace.numel() if workspace is not None else 0,
                          _stream(a_codes.device)))
+    return out
+
+
+def linear_noalloc(a_codes: torch.Tensor, a_scales: torch.Tensor, t_act: Optional[torch.Tensor],
+                   blob: torch.Tensor, fmt, N: int, K: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """w4a4_linear_noalloc: as linear(), with the split-K workspace taken from
+    the library's own per-device scratch array (nothing is allocated by the
+    library; `out` is allocated here only when not given)."""
+    f = _fmt(fmt)
+    L = lib()
+    M = a_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a_codes.device)
+    _check(L.w4a4_linear_noalloc(f, M, N, K, _ptr(a_codes), _ptr(a_scales), _ptr(t_act), _ptr(blob),
+                                 _ptr(out), _stream(a_codes.device)))
     return out
 
 

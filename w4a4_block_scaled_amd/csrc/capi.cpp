@@ -10,6 +10,8 @@
 #include "common.h"
 #include "kernels.h"
 
+static_assert(W4A4_NOALLOC_SCRATCH_BYTES == w4a4::kNoAllocScratchBytes, "scratch size");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -255,6 +257,32 @@ w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K, const 
   return hip_status(w4a4::launch_linear(fmt, M, N, K, a_codes, a_scales, t_act, blob, Y, workspace,
                                         ws_bytes, static_cast<hipStream_t>(stream)),
                     "linear launch");
+}
+
+w4a4_status w4a4_linear_noalloc(w4a4_format fmt, int64_t M, int64_t N, int64_t K,
+                                const void* a_codes, const void* a_scales, const float* t_act,
+                                const void* blob, void* Y, void* stream) {
+  if (is_i4(fmt)) return not_for_i4("linear_noalloc");
+  w4a4_status st = check_gemm_shape(fmt, N, K);
+  if (st != W4A4_OK) return st;
+  if (M < 0 || M > (int64_t(1) << 31))
+    return fail(W4A4_ERR_SHAPE, "linear_noalloc: M=%lld out of range", (long long)M);
+  if (M == 0) return ok();
+  if (!a_codes || !a_scales || !blob || !Y)
+    return fail(W4A4_ERR_NULL, "linear_noalloc: a_codes, a_scales, blob and Y must be non-NULL");
+  if (fmt == W4A4_NVFP4 && !t_act) return fail(W4A4_ERR_NULL, "linear_noalloc: NVFP4 needs t_act");
+  const size_t need = w4a4_linear_workspace_bytes(fmt, M, N, K);
+  if (need > w4a4::kNoAllocScratchBytes)
+    return fail(W4A4_ERR_WORKSPACE, "linear_noalloc: needs %zu scratch bytes, the maximum is %zu",
+                need, w4a4::kNoAllocScratchBytes);
+  if (!aligned(a_codes, 16) || !aligned(a_scales, 16) || !aligned(blob, 256) || !aligned(Y, 16) ||
+      (t_act && !aligned(t_act, 4)))
+    return fail(W4A4_ERR_ALIGN,
+                "linear_noalloc: a_codes/a_scales/Y need 16-byte, blob 256-byte, t_act 4-byte "
+                "alignment");
+  return hip_status(w4a4::launch_linear_noalloc(fmt, M, N, K, a_codes, a_scales, t_act, blob, Y,
+                                                static_cast<hipStream_t>(stream)),
+                    "linear_noalloc");
 }
 
 w4a4_status w4a4_linear_grouped(w4a4_format fmt, int P, int64_t M, int64_t K, const int64_t* N,

@@ -32,6 +32,7 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <mutex>
 
 namespace w4a4 {
 namespace {
@@ -1833,6 +1834,9 @@ struct Fp4S {
 static_assert(Fp4S::WORDS_BYTES == 4096 && Fp4S::SYNC_BYTES == W4A4_SPLITK_SYNC_BYTES &&
                   Fp4S::STATUS_OFF == W4A4_SPLITK_STATUS_OFFSET,
               "split-K workspace layout");
+static_assert(kNoAllocScratchBytes ==
+                  size_t(Fp4S::SYNC_BYTES) + size_t(Fp4S::MAX_TILES) * Fp4S::SLOTS * Fp4S::SLOT_BYTES,
+              "the allocation-free scratch holds the largest split-K workspace");
 
 // The partner's partial sums for the blocks in epilogue order e = 4 j + i:
 // quarter q of block e is 1 KiB at (4 e + q) KiB, lane l's 16 bytes at 16 l
@@ -2615,6 +2619,69 @@ hipError_t launch_linear(int fmt, int64_t M, int64_t N, int64_t K, const void* a
     case MXINT4: return launch_fmt<MXINT4>(M, N, K, ac, as, t_act, b, y, workspace, stream);
     default: return launch_fmt<NVFP4>(M, N, K, ac, as, t_act, b, y, workspace, stream);
   }
+}
+
+// ------------------------------------------------ allocation-free linear --
+//
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc): the split-K workspace comes from
+// `scratch`, a device array of this library, one copy per device, that lives
+// until the process ends.  Its address on a device is looked up once, with
+// that device current, and kept per device; the array's name is only a host
+// stand-in and never reaches a kernel.  Every call on a device shares that
+// device's copy, so calls that overlap on one device race.
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// zero the synchronization words and the status of the split-K workspace
+// (a kernel, not hipMemsetAsync, so that the call can be captured in a graph)
+__global__ __launch_bounds__(256) void clear_sync_kernel(uint8_t* __restrict__ ws) {
+  for (int i = int(threadIdx.x); i < Fp4S::SYNC_BYTES / 16; i += 256)
+    reinterpret_cast<u32x4*>(ws)[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+    if (slot.err == hipSuccess && slot.ptr == nullptr) slot.err = hipErrorInvalidSymbol;
+  });
+  *out = slot.ptr;
+  return slot.err;
+}
+
+hipError_t launch_linear_noalloc(int fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
+                                 const void* a_scales, const float* t_act, const void* blob,
+                                 void* Y, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const size_t need = linear_workspace_bytes(fmt, M, N, K);
+  if (need == 0)
+    return launch_linear(fmt, M, N, K, a_codes, a_scales, t_act, blob, Y, nullptr, 0, stream);
+  if (need > kNoAllocScratchBytes) return hipErrorInvalidValue;  // rejected on the host first
+  void* ws = nullptr;
+  hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(clear_sync_kernel, dim3(1), dim3(256), 0, stream, static_cast<uint8_t*>(ws));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_linear(fmt, M, N, K, a_codes, a_scales, t_act, blob, Y, ws, need, stream);
 }
 
 hipError_t launch_linear_grouped(int fmt, int P, int64_t M, int64_t K, const int64_t* N,

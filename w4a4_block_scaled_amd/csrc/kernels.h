@@ -37,6 +37,16 @@ hipError_t launch_linear(int fmt, int64_t M, int64_t N, int64_t K, const void* a
 
 size_t linear_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K);
 
+// The allocation-free linear: the split-K workspace (the only scratch of
+// w4a4_linear) lives in a device array of the library of this many bytes,
+// one per device (the largest split-K workspace: the status block plus 128
+// tiles of 256 KiB).
+constexpr size_t kNoAllocScratchBytes = size_t(4352) + size_t(128) * 4 * 65536;
+
+hipError_t launch_linear_noalloc(int fmt, int64_t M, int64_t N, int64_t K, const void* a_codes,
+                                 const void* a_scales, const float* t_act, const void* blob,
+                                 void* Y, hipStream_t stream);
+
 // Up to kMaxGroup linears of one M and K (per-projection linears of a fused
 // input): one launch where that pays (MXFP4, M > 32, unless every problem
 // takes the persistent kernel on its own), else one after another.
