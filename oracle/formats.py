@@ -8,7 +8,8 @@ it; the product path never does.
 Formats (DualQuant, Section 3 "Quantization preliminaries": MXFP4 and
 MXINT4 use blocks of 32 with a shared power-of-two E8M0 scale, NVFP4 uses
 blocks of 16 with an FP8 UE4M3 scale; the element grids are the integer grid
-for INT formats and the exponent-mantissa grid for FP formats).  The bit
+for INT formats and the exponent-mantissa grid for FP formats; Appendix G.2
+adds the 8-bit MXFP8 and MXINT8, blocks of 32 with E8M0 scales).  The bit
 layouts are the OCP Microscaling / OCP FP8 definitions that section cites:
 
 * E2M1 : sign, 2 exponent bits (bias 1), 1 mantissa bit; magnitudes
@@ -17,6 +18,8 @@ layouts are the OCP Microscaling / OCP FP8 definitions that section cites:
          0x7F / 0xFF are NaN, no infinities.
 * E8M0 : unsigned exponent, value 2^(b-127), 0xFF is NaN.
 * INT4 : two's complement nibble, -8..7.
+* INT8 : two's complement byte, -128..127 (the MXINT8 elements, Appendix
+         G.2's 8-bit variants).
 * BF16 : IEEE-style 1/8/7; results are rounded once, from fp64, to nearest
          with ties to even.
 
@@ -112,6 +115,21 @@ def e4m3_encode_ratio(num, den):
     return _rne_index(num, thr).astype(np.uint8)
 
 
+def e4m3_encode(x, unit):
+    """Signed E4M3 code of x / unit, round to nearest even, saturating at +-448.
+
+    x    : fp64 array (exact values); the sign bit of x becomes the code's
+           bit 7, so negative inputs that round to zero give 0x80.
+    unit : positive fp64 power of two, broadcastable to x (every midpoint *
+           unit is then exact in fp64).
+    """
+    x = np.asarray(x, np.float64)
+    unit = np.asarray(unit, np.float64)
+    idx = e4m3_encode_ratio(np.abs(x), unit)
+    sign = np.signbit(x).astype(np.int64) << 7
+    return (idx.astype(np.int64) | sign).astype(np.uint8)
+
+
 # ----------------------------------------------------------------- E8M0 ----
 
 
@@ -131,6 +149,19 @@ def int4_value(nibble):
 def int4_encode(v):
     """Two's complement nibble of integer-valued v in [-8, 7]."""
     return (np.asarray(v).astype(np.int64) & 15).astype(np.uint8)
+
+
+# ----------------------------------------------------------------- INT8 ----
+
+
+def int8_value(byte):
+    b = np.asarray(byte).astype(np.int64) & 255
+    return np.where(b >= 128, b - 256, b).astype(np.float64)
+
+
+def int8_encode(v):
+    """Two's complement byte of integer-valued v in [-128, 127]."""
+    return (np.asarray(v).astype(np.int64) & 255).astype(np.uint8)
 
 
 # ----------------------------------------------------------------- BF16 ----

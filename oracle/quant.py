@@ -35,6 +35,14 @@ What is computed (DualQuant):
   quotient; code = clip(RNE(x~ / Delta), -8, 7) decided exactly (ties to
   the even integer); an all-zero block (or one whose Delta rounds to 0)
   gets Delta = 0 and zero codes.
+* 8-bit MX formats (Appendix G.2, Table 9: MXFP8 and MXINT8 with G = 32 and
+  E8M0 scales), with the same OCP shared-exponent rule: MXFP8 elements are
+  E4M3 (emax_elem = 8, 448 = 1.75 * 2^8), code = RNE_E4M3(x~ * 2^-e)
+  saturating at +-448, sign kept for -0 (0x80); MXINT8 elements are
+  two's-complement bytes with value code * 2^e, emax_elem = 6 (127 < 2^7),
+  code = clip(RNE(x~ * 2^-e), -128, 127) (the OCP fixed-point convention
+  with 6 fraction bits gives the same values with the scale byte 6 higher).
+  Codes are stored one byte per element, [rows, K].
 * MX and INT4 G=64 blocks holding a non-finite value get scale byte 0xFF
   (BF16 0x7FC0) and zero codes (inputs are expected finite; this only fixes
   what happens otherwise).
@@ -49,9 +57,13 @@ import numpy as np
 
 from . import formats as F
 
-BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32, "int4g64": 64}
+BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32, "int4g64": 64, "mxfp8": 32, "mxint8": 32}
+MX_FORMATS = ("mxfp4", "mxint4", "mxfp8", "mxint8")
+CODE_BITS = {"mxfp4": 4, "nvfp4": 4, "mxint4": 4, "int4g64": 4, "mxfp8": 8, "mxint8": 8}
 INT4_QMAX = 7                      # symmetric INT4 grid maximum
-EMAX_ELEM = 2                      # floor(log2) of the largest element magnitude
+# floor(log2) of the largest element magnitude of each MX element grid:
+# E2M1 6 = 1.5 * 2^2; int4 7 < 2^3; E4M3 448 = 1.75 * 2^8; int8 127 < 2^7
+EMAX_ELEM = {"mxfp4": 2, "mxint4": 2, "mxfp8": 8, "mxint8": 6}
 NV_TENSOR_DIVISOR = np.float32(6.0 * 448.0)   # 2688
 ROW_CHUNK = 256
 
@@ -72,10 +84,10 @@ def nv_tensor_scale(xt):
     return t
 
 
-def _mx_scale_exponent(amax):
-    """Shared exponent e = clamp(floor(log2 amax) - 2, -127, 127); 0 blocks -> -127."""
+def _mx_scale_exponent(amax, emax_elem=2):
+    """Shared exponent e = clamp(floor(log2 amax) - emax_elem, -127, 127); 0 blocks -> -127."""
     _, E = np.frexp(amax)                       # amax = f * 2^E, f in [0.5, 1)
-    e = np.clip(E - 1 - EMAX_ELEM, -127, 127)
+    e = np.clip(E - 1 - emax_elem, -127, 127)
     return np.where(amax == 0, -127, e).astype(np.int64)
 
 
@@ -84,15 +96,20 @@ def _quantize_chunk(xt, fmt, t):
     G = BLOCK[fmt]
     blocks = xt.astype(np.float64).reshape(R, K // G, G)
     amax = np.abs(blocks).max(axis=-1)
-    if fmt in ("mxfp4", "mxint4"):
+    if fmt in MX_FORMATS:
         nonfinite = ~np.isfinite(blocks).all(axis=-1)
         amax = np.where(nonfinite, 0.0, amax)
-        e = _mx_scale_exponent(amax)
+        e = _mx_scale_exponent(amax, EMAX_ELEM[fmt])
         scales = (e + 127).astype(np.uint8)
+        finite = np.where(np.isfinite(blocks), blocks, 0.0)
         if fmt == "mxfp4":
             codes = F.e2m1_encode(blocks, np.ldexp(1.0, e)[..., None])
+        elif fmt == "mxfp8":
+            codes = F.e4m3_encode(finite, np.ldexp(1.0, e)[..., None])
+        elif fmt == "mxint8":
+            codes = F.int8_encode(np.clip(np.rint(np.ldexp(finite, -e[..., None])), -128, 127))
         else:
-            v = np.ldexp(np.where(np.isfinite(blocks), blocks, 0.0), -e[..., None])
+            v = np.ldexp(finite, -e[..., None])
             codes = F.int4_encode(np.clip(np.rint(v), -8, 7))
         scales = np.where(nonfinite, np.uint8(255), scales)
         codes = np.where(nonfinite[..., None], np.uint8(0), codes)
@@ -128,7 +145,10 @@ def _quantize_chunk(xt, fmt, t):
 
 
 def quantize_rows(xt, fmt, t=None):
-    """Quantize the rows of X~ (fp32 [R, K]) -> (codes [R,K] nibbles, scales [R,K/G], t).
+    """Quantize the rows of X~ (fp32 [R, K]) -> (codes [R,K], scales [R,K/G], t).
+
+    codes hold one element each: a nibble for the 4-bit formats, a byte for
+    MXFP8 / MXINT8.
 
     t is the NVFP4 tensor scale (computed from X~ when not given); None for
     MX formats.
@@ -146,6 +166,16 @@ def quantize_rows(xt, fmt, t=None):
         codes[r0:r0 + ROW_CHUNK], scales[r0:r0 + ROW_CHUNK] = \
             _quantize_chunk(xt[r0:r0 + ROW_CHUNK], fmt, t)
     return codes, scales, (np.float32(t) if fmt == "nvfp4" else None)
+
+
+def pack_codes(codes, fmt):
+    """Canonical storage of element codes: nibble pairs for 4-bit formats
+    (pack_nibbles), the bytes themselves for the 8-bit formats."""
+    return pack_nibbles(codes) if CODE_BITS[fmt] == 4 else np.asarray(codes, np.uint8).copy()
+
+
+def unpack_codes(packed, fmt):
+    return unpack_nibbles(packed) if CODE_BITS[fmt] == 4 else np.asarray(packed, np.uint8).copy()
 
 
 def pack_nibbles(codes):
@@ -166,34 +196,40 @@ def quantize_act(x, c, fmt):
     """Activation side: rescale by c then quantize rows.
 
     x : fp32 values of the BF16 activations [M, K]; c : fp32 [K].
-    Returns (packed codes [M, K/2], scales [M, K/G], t or None).
+    Returns (packed codes [M, K/2] (8-bit formats: [M, K]), scales [M, K/G],
+    t or None).
     """
     codes, scales, t = quantize_rows(rescale(x, c), fmt)
-    return pack_nibbles(codes), scales, t
+    return pack_codes(codes, fmt), scales, t
 
 
 def quantize_weight(w, fmt):
     """Weight side: quantize rows of the already divided weights W / (r c^T).
 
     w : fp32 values of the BF16 prescaled weights [N, K].
-    Returns (packed codes [N, K/2], scales [N, K/G], t_w (1.0 for MX)).
+    Returns (packed codes [N, K/2] (8-bit formats: [N, K]), scales [N, K/G],
+    t_w (1.0 for MX)).
     """
     codes, scales, t = quantize_rows(np.asarray(w, np.float32), fmt)
-    return pack_nibbles(codes), scales, (np.float32(1.0) if t is None else t)
+    return pack_codes(codes, fmt), scales, (np.float32(1.0) if t is None else t)
 
 
 def dequantize(packed, scales, fmt):
     """Values code * block_scale in fp64 (exact); the NVFP4 tensor scale is not applied."""
-    codes = unpack_nibbles(packed)
+    codes = unpack_codes(packed, fmt)
     R, K = codes.shape
     G = BLOCK[fmt]
     if fmt in ("mxint4", "int4g64"):
         elem = F.int4_value(codes)
+    elif fmt == "mxfp8":
+        elem = F.e4m3_value(codes)
+    elif fmt == "mxint8":
+        elem = F.int8_value(codes)
     else:
         elem = F.e2m1_value(codes)
     if fmt == "int4g64":
         svals = F.bf16_value(scales)
-    elif fmt in ("mxfp4", "mxint4"):
+    elif fmt in MX_FORMATS:
         svals = F.e8m0_value(scales)
     else:
         svals = F.e4m3_value(scales)
