@@ -51,8 +51,31 @@ typedef enum {
   W4A4_MXFP4 = 0,   /* E2M1 elements, G = 32, E8M0 block scale             */
   W4A4_NVFP4 = 1,   /* E2M1 elements, G = 16, UE4M3 block scale + fp32 t   */
   W4A4_MXINT4 = 2,  /* int4 elements, G = 32, E8M0 block scale             */
-  W4A4_INT4G64 = 3  /* int4 elements, G = 64, BF16 block scale (see below)  */
+  W4A4_INT4G64 = 3, /* int4 elements, G = 64, BF16 block scale (see below)  */
+  W4A4_MXFP8 = 4,   /* E4M3 elements, G = 32, E8M0 block scale (8-bit)     */
+  W4A4_MXINT8 = 5   /* int8 elements, G = 32, E8M0 block scale (8-bit)     */
 } w4a4_format;
+
+/*
+ * W4A4_MXFP8, W4A4_MXINT8 - the 8-bit MX variants of Appendix G.2 (Table 9:
+ * MXFP8 and MXINT8 with G = 32), for the same quantize / pack / linear path.
+ * Codes take one byte each: canonical codes are [rows x K] bytes (E4M3 bytes,
+ * or two's-complement int8), scales [rows x K/32] E8M0 bytes.  The block
+ * scale follows the OCP shared-exponent rule with the element grid's largest
+ * binade: e = floor(log2 amax) - 8 for E4M3 (448 = 1.75 * 2^8; elements
+ * RNE_E4M3(x~ * 2^-e) saturating at +-448, sign kept for -0), and
+ * e = floor(log2 amax) - 6 for int8 (127 < 2^7; elements clamp(RNE(x~ *
+ * 2^-e), -128, 127)).  Supported by the size queries, w4a4_quantize_act,
+ * w4a4_pack_weight, w4a4_unpack_weight, w4a4_linear and w4a4_linear_noalloc
+ * (no workspace); the multi-output quantizer, the grouped linear and the
+ * solver return W4A4_ERR_FORMAT.  MXINT8 runs on the scaled FP8 MFMA
+ * (16x16x128, E8M0 block scales in hardware) with each int8 code split into
+ * 16 h + l (h = q >> 4 in [-8, 7], l = q & 15), both parts exact in E4M3,
+ * four MFMAs per K-step.  MXFP8 codes are expanded with their block scales
+ * into bf16 (exact) for the bf16 MFMA: the FP8 MFMA drops small products
+ * next to large ones within a block (about 14 bits kept), which E4M3's 36
+ * binades of product range would expose.
+ */
 
 /*
  * W4A4_INT4G64 - the paper's packed deployment format (Appendix I: INT4,
@@ -76,7 +99,7 @@ typedef enum {
   W4A4_ERR_NULL = 1,       /* a required pointer is NULL                        */
   W4A4_ERR_SHAPE = 2,      /* M < 0, N or K out of range, K % G, N % 16, K % 128 */
   W4A4_ERR_ALIGN = 3,      /* a pointer misses its documented alignment         */
-  W4A4_ERR_FORMAT = 4,     /* unknown format value                              */
+  W4A4_ERR_FORMAT = 4,     /* unknown format, or not supported by this call    */
   W4A4_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required        */
   W4A4_ERR_HIP = 6         /* a HIP call or kernel launch failed                */
 } w4a4_status;
@@ -91,7 +114,7 @@ int w4a4_block_size(w4a4_format fmt);
 
 /* Byte sizes, so that callers allocate every buffer.  Return 0 for invalid
  * arguments. */
-size_t w4a4_act_codes_bytes(w4a4_format fmt, int64_t M, int64_t K);   /* M*K/2 */
+size_t w4a4_act_codes_bytes(w4a4_format fmt, int64_t M, int64_t K);   /* M*K/2 (8-bit: M*K) */
 size_t w4a4_act_scales_bytes(w4a4_format fmt, int64_t M, int64_t K);  /* M*K/G */
 size_t w4a4_quantize_workspace_bytes(w4a4_format fmt, int64_t M, int64_t K);
 size_t w4a4_packed_weight_bytes(w4a4_format fmt, int64_t N, int64_t K);
@@ -108,7 +131,8 @@ size_t w4a4_linear_workspace_bytes(w4a4_format fmt, int64_t M, int64_t N, int64_
  *   X      device, bf16 [M x K], 16-byte aligned.
  *   c      device, fp32 [K], 16-byte aligned; NULL means c = 1 (this is how
  *          weights W / (r c^T) are quantized before packing).
- *   codes  device, out, [M x K/2] canonical codes, 4-byte aligned.
+ *   codes  device, out, [M x K/2] canonical codes, 4-byte aligned ([M x K]
+ *          bytes, 8-byte aligned, for MXFP8 and MXINT8).
  *   scales device, out, [M x K/G] canonical scale bytes.
  *   t_act  device, out, one fp32: the NVFP4 tensor scale
  *          t = fp32(max|X~|) / 2688 (t = 1 for an all-zero tensor).  Ignored

@@ -121,7 +121,7 @@ def test_quantize_act_rejects(args, status):
     ((0, 128, 200, FAKE, FAKE, None, FAKE, FAKE, None), 2),     # K % 128
     ((0, 128, 256, None, FAKE, None, FAKE, FAKE, None), 1),
     ((0, 128, 256, FAKE, FAKE, None, FAKE, ctypes.c_void_p((1 << 20) + 16), None), 3),  # blob 256-B
-    ((5, 128, 256, FAKE, FAKE, None, FAKE, FAKE, None), 4),
+    ((9, 128, 256, FAKE, FAKE, None, FAKE, FAKE, None), 4),
 ])
 def test_pack_weight_rejects(args, status):
     assert w4.lib().w4a4_pack_weight(*args) == status
@@ -287,3 +287,27 @@ def test_linear_noalloc_validation():
     assert L.w4a4_linear_noalloc(0, 4, 128, 256, FAKE_MIS, FAKE, None, FAKE, FAKE, None) == 3
     # the largest split-K workspace fits the scratch array
     assert L.w4a4_linear_workspace_bytes(0, 2048, 4096, 8192) == 4352 + 128 * 4 * 65536
+
+
+def test_mx8_size_queries_and_unsupported_calls():
+    """The 8-bit MX formats (4 = MXFP8, 5 = MXINT8): one byte per code,
+    32-blocks, a blob of N*K code bytes + N*K/32 scale bytes + r; the
+    multi-output quantizer, the grouped linear and the solver reject them."""
+    L = w4.lib()
+    for f in (4, 5):
+        assert L.w4a4_block_size(f) == 32
+        assert L.w4a4_act_codes_bytes(f, 2048, 4096) == 2048 * 4096
+        assert L.w4a4_act_scales_bytes(f, 2048, 4096) == 2048 * 128
+        assert L.w4a4_quantize_workspace_bytes(f, 2048, 4096) == 0
+        assert L.w4a4_linear_workspace_bytes(f, 2048, 4096, 14336) == 0
+        N, K = 4096, 14336
+        got = L.w4a4_packed_weight_bytes(f, N, K)
+        assert N * K + N * K // 32 + 4 * N <= got < N * K + N * K // 32 + 4 * N + 1024
+        assert L.w4a4_dualquant_workspace_bytes(f, 64, 256) == 0
+        arr = (ctypes.c_void_p * 1)(FAKE)
+        assert L.w4a4_quantize_act_multi(f, 4, 256, FAKE, 1, arr, arr, arr, None, None, 0, None) == 4
+        Ns = (ctypes.c_int64 * 1)(256)
+        assert L.w4a4_linear_grouped(f, 1, 4, 256, Ns, arr, arr, None, arr, arr, None) == 4
+        # 8-byte code alignment for the 8-bit quantizer
+        assert L.w4a4_quantize_act(f, 4, 256, FAKE, None, ctypes.c_void_p((1 << 20) + 4), FAKE, None,
+                                   None, 0, None) == 3

@@ -9,7 +9,7 @@ import torch
 from conftest import golden
 import oracle
 from oracle import formats as F
-from oracle.quant import quantize_rows, rescale, nv_tensor_scale, pack_nibbles
+from oracle.quant import quantize_rows, rescale, nv_tensor_scale, pack_nibbles, pack_codes
 from gpu_common import device, say, to_dev, bf16_bits, check_linear
 from w4a4_block_scaled_amd import inputs
 import w4a4_block_scaled_amd as w4
@@ -41,14 +41,14 @@ def oracle_layer(case, rows=None, cols=None):
     xt_full = rescale(x, case.c)
     t_a = nv_tensor_scale(xt_full) if fmt == "nvfp4" else None
     a_codes, a_scales, _ = quantize_rows(xt_full[rows], fmt, t=t_a)
-    a_codes = pack_nibbles(a_codes)
+    a_codes = pack_codes(a_codes, fmt)
     if case.w_codes is not None:
         w_codes, w_scales, t_w = case.w_codes[cols], case.w_scales[cols], np.float32(case.t_w)
     else:
         w = case.w_prescaled.float().numpy()
         t_w = nv_tensor_scale(w) if fmt == "nvfp4" else np.float32(1.0)
         wc, w_scales, _ = quantize_rows(w[cols], fmt, t=t_w if fmt == "nvfp4" else None)
-        w_codes = pack_nibbles(wc)
+        w_codes = pack_codes(wc, fmt)
     r = case.r[cols]
     y = oracle.linear_f64(a_codes, a_scales, t_a, w_codes, w_scales, t_w, r, fmt)
     S = oracle.linear.linear_abs_sum(a_codes, a_scales, t_a, w_codes, w_scales, t_w, r, fmt)

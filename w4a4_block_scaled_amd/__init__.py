@@ -24,7 +24,7 @@ import torch
 __all__ = ["FORMATS", "lib", "library_path", "block_size", "scale_dtype", "quantize_act", "pack_weight",
            "unpack_weight", "linear", "linear_noalloc", "linear_workspace", "packed_weight_bytes", "W4A4Error"]
 
-FORMATS = {"mxfp4": 0, "nvfp4": 1, "mxint4": 2, "int4g64": 3}
+FORMATS = {"mxfp4": 0, "nvfp4": 1, "mxint4": 2, "int4g64": 3, "mxfp8": 4, "mxint8": 5}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
@@ -110,6 +110,11 @@ def scale_dtype(fmt) -> torch.dtype:
     return torch.bfloat16 if _fmt(fmt) == FORMATS["int4g64"] else torch.uint8
 
 
+def code_cols(fmt, K: int) -> int:
+    """Bytes of canonical codes per row of K elements (K/2; K for the 8-bit formats)."""
+    return K if _fmt(fmt) in (FORMATS["mxfp8"], FORMATS["mxint8"]) else K // 2
+
+
 def block_size(fmt) -> int:
     return lib().w4a4_block_size(_fmt(fmt))
 
@@ -123,7 +128,8 @@ def quantize_act(x: torch.Tensor, c: Optional[torch.Tensor], fmt,
                  workspace: Optional[torch.Tensor] = None):
     """w4a4_quantize_act: x bf16 [M, K], c fp32 [K] or None -> (codes, scales, t).
 
-    codes uint8 [M, K/2], scales [M, K/G] (uint8; bfloat16 for INT4 G=64),
+    codes uint8 [M, K/2] ([M, K] for MXFP8 / MXINT8), scales [M, K/G] (uint8;
+    bfloat16 for INT4 G=64),
     t fp32 [1] (NVFP4 tensor scale; unused for the other formats).
     """
     f = _fmt(fmt)
@@ -131,7 +137,7 @@ def quantize_act(x: torch.Tensor, c: Optional[torch.Tensor], fmt,
     M, K = x.shape
     G = L.w4a4_block_size(f)
     if out is None:
-        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        codes = torch.empty((M, code_cols(fmt, K)), dtype=torch.uint8, device=x.device)
         scales = torch.empty((M, K // G), dtype=scale_dtype(fmt), device=x.device)
         t = torch.ones(1, dtype=torch.float32, device=x.device)
     else:
@@ -174,10 +180,12 @@ def quantize_act_multi(x: torch.Tensor, cs, fmt, workspace: Optional[torch.Tenso
 
 def pack_weight(codes: torch.Tensor, scales: torch.Tensor, t_w: Optional[torch.Tensor],
                 r: torch.Tensor, fmt) -> torch.Tensor:
-    """w4a4_pack_weight: canonical codes [N, K/2], scales, t_w [1] or None, r [N] -> blob."""
+    """w4a4_pack_weight: canonical codes [N, K/2] ([N, K] for the 8-bit formats),
+    scales, t_w [1] or None, r [N] -> blob."""
     f = _fmt(fmt)
     L = lib()
-    N, K = codes.shape[0], codes.shape[1] * 2
+    N = codes.shape[0]
+    K = codes.shape[1] if f in (FORMATS["mxfp8"], FORMATS["mxint8"]) else codes.shape[1] * 2
     nbytes = L.w4a4_packed_weight_bytes(f, N, K)
     if nbytes == 0:
         raise W4A4Error(2, f"invalid packed weight shape N={N} K={K}")
@@ -193,7 +201,7 @@ def unpack_weight(blob: torch.Tensor, fmt, N: int, K: int):
     L = lib()
     G = L.w4a4_block_size(f)
     dev = blob.device
-    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    codes = torch.empty((N, code_cols(fmt, K)), dtype=torch.uint8, device=dev)
     scales = torch.empty((N, K // G), dtype=scale_dtype(fmt), device=dev)
     r = torch.empty(N, dtype=torch.float32, device=dev)
     t_w = torch.empty(1, dtype=torch.float32, device=dev)

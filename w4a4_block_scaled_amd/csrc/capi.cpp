@@ -29,7 +29,18 @@ w4a4_status ok() {
   return W4A4_OK;
 }
 
-bool valid_fmt(w4a4_format f) { return f == W4A4_MXFP4 || f == W4A4_NVFP4 || f == W4A4_MXINT4; }
+bool valid_fmt(w4a4_format f) {
+  return f == W4A4_MXFP4 || f == W4A4_NVFP4 || f == W4A4_MXINT4 || f == W4A4_MXFP8 ||
+         f == W4A4_MXINT8;
+}
+
+// the 8-bit MX variants (one byte per code) run through quantize, pack and
+// linear only
+bool is_mx8(w4a4_format f) { return f == W4A4_MXFP8 || f == W4A4_MXINT8; }
+
+w4a4_status not_for_mx8(const char* what) {
+  return fail(W4A4_ERR_FORMAT, "%s: not available for the 8-bit MX formats", what);
+}
 
 // INT4 with G = 64 and BF16 scales has its own kernels (int4g64.hip)
 bool is_i4(w4a4_format f) { return f == W4A4_INT4G64; }
@@ -76,7 +87,7 @@ int w4a4_block_size(w4a4_format fmt) {
 size_t w4a4_act_codes_bytes(w4a4_format fmt, int64_t M, int64_t K) {
   if (is_i4(fmt)) return (M < 0 || K <= 0 || K % 64) ? 0 : size_t(M) * size_t(K) / 2;
   if (!valid_fmt(fmt) || M < 0 || K <= 0 || K % w4a4::block_size(fmt)) return 0;
-  return size_t(M) * size_t(K) / 2;
+  return size_t(M) * size_t(w4a4::code_row_bytes(fmt, K));
 }
 
 size_t w4a4_act_scales_bytes(w4a4_format fmt, int64_t M, int64_t K) {
@@ -132,8 +143,9 @@ w4a4_status w4a4_quantize_act(w4a4_format fmt, int64_t M, int64_t K, const void*
     if (!aligned(workspace, 4) || !aligned(t_act, 4))
       return fail(W4A4_ERR_ALIGN, "quantize_act: workspace and t_act must be 4-byte aligned");
   }
-  if (!aligned(X, 16) || (c && !aligned(c, 16)) || !aligned(codes, 4))
-    return fail(W4A4_ERR_ALIGN, "quantize_act: X and c need 16-byte, codes 4-byte alignment");
+  if (!aligned(X, 16) || (c && !aligned(c, 16)) || !aligned(codes, is_mx8(fmt) ? 8 : 4))
+    return fail(W4A4_ERR_ALIGN,
+                "quantize_act: X and c need 16-byte, codes 4-byte (8-bit formats: 8-byte) alignment");
   return hip_status(w4a4::launch_quantize_act(fmt, M, K, X, c, codes, scales, t_act, workspace,
                                               static_cast<hipStream_t>(stream)),
                     "quantize_act launch");
@@ -144,6 +156,7 @@ w4a4_status w4a4_quantize_act_multi(w4a4_format fmt, int64_t M, int64_t K, const
                                     void* const* scales, float* const* t_act, void* workspace,
                                     size_t ws_bytes, void* stream) {
   if (is_i4(fmt)) return not_for_i4("quantize_act_multi");
+  if (is_mx8(fmt)) return not_for_mx8("quantize_act_multi");
   if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
   const int G = w4a4::block_size(fmt);
   if (M < 0 || K <= 0 || K % G || P < 1 || P > w4a4::kMaxOutputs)
@@ -290,6 +303,7 @@ w4a4_status w4a4_linear_grouped(w4a4_format fmt, int P, int64_t M, int64_t K, co
                                 const float* const* t_act, const void* const* blobs,
                                 void* const* Y, void* stream) {
   if (is_i4(fmt)) return not_for_i4("linear_grouped");
+  if (is_mx8(fmt)) return not_for_mx8("linear_grouped");
   if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
   if (P < 1 || P > w4a4::kMaxGroup || M < 0)
     return fail(W4A4_ERR_SHAPE, "linear_grouped: P=%d M=%lld (need 1 <= P <= %d, M >= 0)", P,
@@ -314,7 +328,7 @@ w4a4_status w4a4_linear_grouped(w4a4_format fmt, int P, int64_t M, int64_t K, co
 }
 
 size_t w4a4_dualquant_workspace_bytes(w4a4_format fmt, int64_t N, int64_t K) {
-  if (!valid_fmt(fmt) || N <= 0 || K <= 0 || K % 32 ||
+  if (!valid_fmt(fmt) || is_mx8(fmt) || N <= 0 || K <= 0 || K % 32 ||
       N * K > (int64_t(1) << 36))
     return 0;
   return w4a4::solver_workspace_bytes(N, K);
@@ -324,6 +338,7 @@ w4a4_status w4a4_dualquant_solve(w4a4_format fmt, int64_t N, int64_t K, const fl
                                  float* r, float* c, void* codes, void* scales, float* t_w,
                                  void* workspace, size_t ws_bytes, void* stream) {
   if (is_i4(fmt)) return not_for_i4("dualquant_solve");
+  if (is_mx8(fmt)) return not_for_mx8("dualquant_solve");
   if (!valid_fmt(fmt)) return fail(W4A4_ERR_FORMAT, "unknown format %d", int(fmt));
   if (N <= 0 || K <= 0 || K % 32 || N * K > (int64_t(1) << 36) || iters < 1)
     return fail(W4A4_ERR_SHAPE,

@@ -6,9 +6,17 @@
 
 namespace w4a4 {
 
-enum Fmt : int { MXFP4 = 0, NVFP4 = 1, MXINT4 = 2 };
+// MXFP8 and MXINT8 are the 8-bit MX variants (E4M3 or int8 elements, one
+// byte each, blocks of 32 with E8M0 scales); value 3 is INT4 with G = 64,
+// which has its own kernels (int4g64.hip).
+enum Fmt : int { MXFP4 = 0, NVFP4 = 1, MXINT4 = 2, MXFP8 = 4, MXINT8 = 5 };
 
 __host__ __device__ constexpr int block_size(int fmt) { return fmt == NVFP4 ? 16 : 32; }
+__host__ __device__ constexpr bool is_mx8(int fmt) { return fmt == MXFP8 || fmt == MXINT8; }
+// bytes of codes per row of K elements
+__host__ __device__ constexpr int64_t code_row_bytes(int fmt, int64_t K) {
+  return is_mx8(fmt) ? K : K / 2;
+}
 
 // ---------------------------------------------------------------------------
 // Packed-weight blob.
@@ -24,7 +32,11 @@ __host__ __device__ constexpr int block_size(int fmt) { return fmt == NVFP4 ? 16
 //                        128 h .. +128; lane l owns 16 bytes of row 16 g + l%16
 //                        (K chunk l/16 for NVFP4; the FP8 arrangement of the
 //                        16x16x128 MFMA for MXINT4, see pack.hip).
-//                       Tiles are ordered g-major: ((g * KT) + h) * 1 KiB.
+//     MXFP8, MXINT8 (layout 3): 2 KiB tiles of 16 rows x 128 K (one byte per
+//                        code); lane l owns 32 bytes of row 16 g + l%16: the
+//                        codes of K 16c .. +16 and 64 + 16c .. +16 with
+//                        c = l/16, the FP8 operand order of the 16x16x128 MFMA.
+//                       Tiles are ordered g-major: ((g * KT) + h) * tile bytes.
 //   [scale_off, ...)    block scales as "scale words": one dword per
 //                       (row-group set sg, K tile h, lane l), laid out
 //                       [sg][h][lane].  Each byte serves one row group so that
@@ -32,8 +44,8 @@ __host__ __device__ constexpr int block_size(int fmt) { return fmt == NVFP4 ? 16
 //                       weight tiles (byte picked by op_sel).
 //                         MXFP4 : byte j = scale of row 32 (4 sg + j) + l%32,
 //                                 block 2 h + l/32.
-//                         MXINT4: byte j = scale of row 16 (4 sg + j) + l%16,
-//                                 block 4 h + l/16.
+//                         MXINT4, MXFP8, MXINT8: byte j = scale of row
+//                                 16 (4 sg + j) + l%16, block 4 h + l/16.
 //                         NVFP4 : byte 2j+b = scale of row 16 (2 sg + j) + l%16,
 //                                 block 8 h + 2 (l/16) + b.
 //                       Bytes of row groups beyond N are zero.
@@ -44,14 +56,16 @@ struct BlobHeader {
   uint32_t version;   // 1
   uint32_t format;
   int64_t N, K;
-  uint32_t layout;    // 1: 16-row x 128-K tiles, 2: 32-row x 64-K tiles
+  uint32_t layout;    // 1: 16-row x 128-K tiles, 2: 32-row x 64-K tiles, 3: 8-bit 16 x 128
   float t_w;
   uint64_t code_off, scale_off, r_off, total;
   uint8_t pad[256 - 8 - 4 - 4 - 16 - 4 - 4 - 32];
 };
 static_assert(sizeof(BlobHeader) == 256, "blob header must be 256 bytes");
 
-__host__ __device__ constexpr int blob_layout_id(int fmt) { return fmt == MXFP4 ? 2 : 1; }
+__host__ __device__ constexpr int blob_layout_id(int fmt) {
+  return fmt == MXFP4 ? 2 : is_mx8(fmt) ? 3 : 1;
+}
 __host__ __device__ constexpr int tile_rows(int fmt) { return fmt == MXFP4 ? 32 : 16; }
 __host__ __device__ constexpr int tile_k(int fmt) { return fmt == MXFP4 ? 64 : 128; }
 __host__ __device__ constexpr int groups_per_scale_word(int fmt) { return fmt == NVFP4 ? 2 : 4; }
@@ -78,7 +92,7 @@ __host__ __device__ inline BlobLayout blob_layout(int fmt, int64_t N, int64_t K)
   const int gpw = groups_per_scale_word(fmt);
   L.NSG = (L.NG + gpw - 1) / gpw;
   L.code_off = 256;
-  L.scale_off = align256(L.code_off + L.NG * rows * (K / 2));
+  L.scale_off = align256(L.code_off + L.NG * rows * code_row_bytes(fmt, K));
   L.r_off = align256(L.scale_off + L.NSG * L.KT * 64 * 4);
   L.total = align256(L.r_off + 4 * N);
   return L;

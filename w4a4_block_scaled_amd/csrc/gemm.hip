@@ -2510,6 +2510,455 @@ hipError_t launch_nv_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, 
   return hipGetLastError();
 }
 
+// ================================================ 8-bit MX (MXFP8, MXINT8) ==
+//
+// Codes are one byte each.  A fragment lane l (row r = l % 16, group c =
+// l / 16) holds 32 bytes of its row for a 128-wide K-step: K 16c..16c+15 in
+// its first four dwords and 64+16c..64+16c+15 in the last four, the FP8
+// operand order of V_MFMA_SCALE_F32_16X16X128_F8F6F4 (so the first half
+// lies in block c/2 and the second in block 2 + c/2).
+//   MXFP8 : the scaled FP8 MFMA does not add the 32 products of a block
+//           exactly when their magnitudes spread: measured, a product 2^-6
+//           next to 448 x 1 in the same group of eight is dropped (about 14
+//           bits kept below the group's largest product), and E4M3 products
+//           span 36 binades.  So each code is expanded with its block scale
+//           into bf16 (v_cvt_scalef32_pk_bf16_fp8: code x 2^e has 4
+//           significant bits, exact), and the bf16 MFMA (16x16x32, products
+//           kept to ~26 bits, measured) runs four times per K-step, MFMA j
+//           taking elements 8j..8j+7 of every lane on both operands (the same
+//           K permutation on both sides, each element already carrying its
+//           block scale).
+//   MXINT8: q = 16 h + l with h = q >> 4 in [-8, 7] and l = q & 15.  h enters
+//           as the E4M3 byte of h * 2^-5 and l as that of l * 2^-9 (bytes
+//           0..15 encode u * 2^-9 exactly), so q * 2^-9 = h 2^-5 + l 2^-9 and
+//           q_w q_a 2^-18 is the sum of four exact MFMA products under the
+//           same block scales; the epilogue multiplies by 2^18.
+
+// four int8 codes (the bytes of d) -> E4M3 bytes of (q >> 4) * 2^-5.  The low
+// three bits of the high nibble index a table of positive and one of negative
+// values; bit 7 of each byte picks, per byte, which.
+__device__ __forceinline__ uint32_t int8x4_hi_e4m3(uint32_t d) {
+  const uint32_t pos_lo = vgpr_const(0x1C181000u);  // h = 0..3
+  const uint32_t pos_hi = vgpr_const(0x26242220u);  // h = 4..7
+  const uint32_t neg_lo = vgpr_const(0xA2A4A6A8u);  // h = -8..-5
+  const uint32_t neg_hi = vgpr_const(0x90989CA0u);  // h = -4..-1
+  const uint32_t g = (d >> 4) & vgpr_const(0x07070707u);
+  const uint32_t pos = __builtin_amdgcn_perm(pos_hi, pos_lo, g);
+  const uint32_t neg = __builtin_amdgcn_perm(neg_hi, neg_lo, g);
+  const uint32_t sel = ((d >> 5) & vgpr_const(0x04040404u)) | vgpr_const(0x03020100u);
+  return __builtin_amdgcn_perm(neg, pos, sel);
+}
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// E8M0 byte -> the fp32 scale 2^(b - 127) (only its exponent is used by the
+// conversion)
+__device__ __forceinline__ float e8m0_scale(uint32_t b) { return __uint_as_float((b & 0xffu) << 23); }
+
+// 32 E4M3 codes of a fragment lane, the first 16 under scale s0 and the last
+// 16 under s1, as four groups of 8 bf16 values (exact)
+struct Bf16Frag {
+  v8bf p[4];
+};
+
+__device__ __forceinline__ Bf16Frag e4m3_frag_bf16(const v8i& f, float s0, float s1) {
+  Bf16Frag o;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const float sc = d < 4 ? s0 : s1;
+    const bf2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(uint32_t(f[d]), sc, false);
+    const bf2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(uint32_t(f[d]), sc, true);
+    o.p[d >> 1][4 * (d & 1) + 0] = lo[0];
+    o.p[d >> 1][4 * (d & 1) + 1] = lo[1];
+    o.p[d >> 1][4 * (d & 1) + 2] = hi[0];
+    o.p[d >> 1][4 * (d & 1) + 3] = hi[1];
+  }
+  return o;
+}
+
+__device__ __forceinline__ v4f mfma_bf16x4(const Bf16Frag& w, const Bf16Frag& a, v4f acc) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w.p[j], a.p[j], acc, 0, 0, 0);
+  return acc;
+}
+
+struct Mx8Split {
+  v8i hi, lo;
+};
+
+__device__ __forceinline__ Mx8Split int8_frag_split(const v8i& f) {
+  Mx8Split s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s.hi[i] = int(int8x4_hi_e4m3(uint32_t(f[i])));
+    s.lo[i] = int(uint32_t(f[i]) & 0x0f0f0f0fu);
+  }
+  return s;
+}
+
+// acc += w . a for one fragment pair (byte `OPW` of sw is the weight scale)
+template <int FMT, int OPW>
+__device__ __forceinline__ v4f mx8_mfma_op(const v8i& w, const Mx8Split& ws, const v8i& a,
+                                           const Mx8Split& as, v4f acc, int sw, int sa) {
+  if constexpr (FMT == MXFP8) {
+    return mfma_fp8_op<OPW>(w, a, acc, sw, sa);
+  } else {
+    acc = mfma_fp8_op<OPW>(ws.hi, as.hi, acc, sw, sa);
+    acc = mfma_fp8_op<OPW>(ws.hi, as.lo, acc, sw, sa);
+    acc = mfma_fp8_op<OPW>(ws.lo, as.hi, acc, sw, sa);
+    return mfma_fp8_op<OPW>(ws.lo, as.lo, acc, sw, sa);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ v4f mx8_mfma(int opw, const v8i& w, const Mx8Split& ws, const v8i& a,
+                                        const Mx8Split& as, v4f acc, int sw, int sa) {
+  switch (opw & 3) {
+    case 0: return mx8_mfma_op<FMT, 0>(w, ws, a, as, acc, sw, sa);
+    case 1: return mx8_mfma_op<FMT, 1>(w, ws, a, as, acc, sw, sa);
+    case 2: return mx8_mfma_op<FMT, 2>(w, ws, a, as, acc, sw, sa);
+    default: return mx8_mfma_op<FMT, 3>(w, ws, a, as, acc, sw, sa);
+  }
+}
+
+__device__ __forceinline__ v8i v8i_of(const u32x4& lo, const u32x4& hi) {
+  return v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+}
+
+__device__ __forceinline__ float mx8_epilogue_factor(int fmt) {
+  return fmt == MXINT8 ? 262144.0f : 1.0f;  // undo 2^-9 on both operands (MXINT8)
+}
+
+// ---------------------------------------------------- 8-bit decode (M <= 16)
+//
+// Weight streaming, as the MXINT4 decode kernel: one workgroup per 16 output
+// features, workgroup b taking group (b % 8) S + b / 8 (S groups per XCD),
+// WAVES waves splitting the K-steps into contiguous ranges, each issuing the
+// loads of up to U K-steps at once (the 2 KiB weight tile of a K-step with
+// two coalesced 16-byte non-temporal loads per lane).  The activation rows
+// (<= 16) are the MFMA's second operand: lane (m, c) loads its two 16-byte
+// chunks of row m straight in fragment order (the four lanes of a row read
+// 64 contiguous bytes per load); lanes of rows >= M load nothing and hold
+// zeros.  Partial sums meet in LDS; wave 0 applies r and stores.
+template <int FMT, int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void gemm_mx8_decode_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  static_assert(FMT == MXFP8 || FMT == MXINT8, "8-bit MX formats");
+  const BlobLayout L = blob_layout(FMT, N, K);
+  const u32x4* __restrict__ Wc = reinterpret_cast<const u32x4*>(blob + L.code_off);
+  const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+  const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
+
+  const int64_t F = N / 16, per_x = (F + 7) / 8;
+  const int64_t ng = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8;
+  if (ng >= F) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane >> 4;
+  const int64_t m = lane & 15;
+  const bool mvalid = m < M;
+  const int64_t KS = L.KS, KB = K / 32;
+  const int64_t per = (KS + WAVES - 1) / WAVES;
+  const int64_t k_begin = wave * per;
+  const int64_t k_end = k_begin + per < KS ? k_begin + per : KS;
+  const int sw_shift = 8 * int(ng & 3);
+  const uint32_t* __restrict__ Wsg = Ws + (ng >> 2) * KS * 64 + lane;
+  const u32x4* __restrict__ Wg = Wc + (ng * KS * 64 + lane) * 2;
+  const uint8_t* __restrict__ arow = a_codes + (mvalid ? m : 0) * K + 16 * c;
+  // MXINT8: this lane group's block scale (the MFMA's scale lane); MXFP8: the
+  // scales of the two blocks this lane's halves lie in (c / 2 and 2 + c / 2)
+  const int b0 = FMT == MXFP8 ? (c >> 1) : c;
+  const uint8_t* __restrict__ srow = a_scales + (mvalid ? m : 0) * KB + b0;
+  const uint32_t* __restrict__ Wsg0 = Wsg - lane + (lane & 15) + 16 * b0;  // lane group b0's word
+  static_assert(U <= 8, "masked activation loads");
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += U) {
+    u32x4 w0[U], w1[U], a0[U], a1[U];
+    uint32_t swd[U], swd2[U];
+    int sab[U], sab2[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t ks = k0 + u;
+      const bool ok = ks < k_end;
+      const int64_t ksc = ok ? ks : k_end - 1;  // clamped: loads stay in range
+      const u32x4 x0 = __builtin_nontemporal_load(&Wg[ksc * 128]);
+      const u32x4 x1 = __builtin_nontemporal_load(&Wg[ksc * 128 + 1]);
+      u32x4 y0 = {0u, 0u, 0u, 0u}, y1 = {0u, 0u, 0u, 0u};
+      if (mvalid) {
+        y0 = *reinterpret_cast<const u32x4*>(arow + ksc * 128);
+        y1 = *reinterpret_cast<const u32x4*>(arow + ksc * 128 + 64);
+      }
+      sab[u] = mvalid ? int(srow[ksc * 4]) : 127;
+      w0[u] = ok ? x0 : u32x4{0u, 0u, 0u, 0u};
+      w1[u] = ok ? x1 : u32x4{0u, 0u, 0u, 0u};
+      a0[u] = ok ? y0 : u32x4{0u, 0u, 0u, 0u};
+      a1[u] = ok ? y1 : u32x4{0u, 0u, 0u, 0u};
+      swd[u] = __builtin_nontemporal_load(&Wsg0[ksc * 64]) >> sw_shift;
+      if constexpr (FMT == MXFP8) {
+        sab2[u] = mvalid ? int(srow[ksc * 4 + 2]) : 127;
+        swd2[u] = __builtin_nontemporal_load(&Wsg0[ksc * 64 + 32]) >> sw_shift;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const v8i w = v8i_of(w0[u], w1[u]), a = v8i_of(a0[u], a1[u]);
+      if constexpr (FMT == MXFP8) {
+        const Bf16Frag wb = e4m3_frag_bf16(w, e8m0_scale(swd[u]), e8m0_scale(swd2[u]));
+        const Bf16Frag ab = e4m3_frag_bf16(a, e8m0_scale(uint32_t(sab[u])), e8m0_scale(uint32_t(sab2[u])));
+        acc = mfma_bf16x4(wb, ab, acc);
+      } else {
+        const Mx8Split ws = int8_frag_split(w), as = int8_frag_split(a);
+        acc = mx8_mfma_op<FMT, 0>(w, ws, a, as, acc, int(swd[u]), sab[u]);
+      }
+    }
+  }
+
+  __shared__ v4f red[WAVES > 1 ? WAVES - 1 : 1][64];
+  if (wave != 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < WAVES - 1; ++w) {
+    const v4f o = red[w][lane];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += o[e];
+  }
+  // lane l: activation row l % 16, features 4 (l / 16) + 0..3 of the group
+  if (!mvalid) return;
+  const int64_t n = ng * 16 + 4 * c;
+  const float f = mx8_epilogue_factor(FMT);
+  const float4 rv = *reinterpret_cast<const float4*>(R + n);
+  store4(Y, N, m, n, acc, v4f{rv.x * f, rv.y * f, rv.z * f, rv.w * f});
+}
+
+template <int FMT, int WAVES, int U>
+hipError_t launch_mx8_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                             const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_mx8_decode_kernel<FMT, WAVES, U>), dim3(unsigned((N / 16 + 7) / 8 * 8)),
+                     dim3(64 * WAVES), 0, stream, ac, as, blob, Y, M, N, K);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ 8-bit tiled (M > 16)
+//
+// Workgroup tile BN (n) x BM (m) with WN x WM waves; one 128-wide K-step per
+// pipeline stage, DEPTH stages in a ring, copied global -> LDS with
+// direct-to-LDS loads (16 bytes per lane, 1 KiB per instruction; every wave
+// issues the same COPIES per stage, so a stage is complete for a wave when
+// its vmcnt has dropped to COPIES x the stages issued after it, and a
+// barrier makes it complete for the workgroup).
+//
+// Stage layout:
+//   A codes   BM rows x 128 B; 16-byte chunk j of row r at chunk position
+//             8 r + (j ^ (r & 7)), so the fragment reads (16 rows, one chunk
+//             each) fall on distinct banks;
+//   W codes   BN/16 tiles of 2 KiB, copied from the blob as they are;
+//   A scales  BM rows x 4 B (the K-step's four block scales of a row);
+//   W scales  BN/64 scale-word sets x 64 lanes x 4 B.
+// Rows beyond M and row groups beyond N/16 are read from clamped valid
+// addresses; they only feed outputs that are never stored.
+template <int BN, int BM, int WN, int WM, int DEPTH>
+struct Mx8Cfg {
+  static constexpr int WAVES = WN * WM;
+  static constexpr int FN = BN / 16 / WN, FM = BM / 16 / WM;
+  static constexpr int A_BYTES = BM * 128, W_BYTES = BN * 128;
+  static constexpr int AS_BYTES = BM * 4, WS_BYTES = (BN / 64) * 256;
+  static constexpr int STAGE = A_BYTES + W_BYTES + AS_BYTES + WS_BYTES;
+  static constexpr int A_DMA = A_BYTES / 1024 / WAVES, W_DMA = W_BYTES / 1024 / WAVES;
+  static constexpr int AS_DW = BM / WAVES;              // activation scale dwords per wave
+  static constexpr int WS_SETS = BN / 64 / WAVES;       // scale-word sets per wave (0: shared)
+  static constexpr int COPIES = A_DMA + W_DMA + 1 + 1;
+  static_assert(A_DMA * WAVES * 1024 == A_BYTES && W_DMA * WAVES * 1024 == W_BYTES, "copy split");
+  static_assert(AS_DW <= 64 && (BN / 64) <= WAVES, "scale copies: one instruction per wave each");
+  static_assert(FN % 4 == 0, "weight scale words per wave");
+  static_assert(DEPTH * STAGE <= 160 * 1024, "LDS");
+  static_assert((DEPTH - 1) * COPIES < 64, "vmcnt range");
+};
+
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__device__ __forceinline__ void mx8_issue(const uint8_t* __restrict__ a_codes,
+                                          const uint8_t* __restrict__ a_scales,
+                                          const uint8_t* __restrict__ wc,
+                                          const uint32_t* __restrict__ wsw, int64_t M, int64_t K,
+                                          int64_t KS, int64_t NG, int64_t NSG, int64_t m0,
+                                          int64_t ng0, int64_t ks, LDS uint8_t* dst, int wave,
+                                          int lane) {
+  using C = Mx8Cfg<BN, BM, WN, WM, DEPTH>;
+  // activation rows: copy f covers rows 8 f .. 8 f + 7; lane L fills chunk
+  // position L % 8 of row L / 8 with the chunk that belongs there
+#pragma unroll
+  for (int i = 0; i < C::A_DMA; ++i) {
+    const int f = wave * C::A_DMA + i;
+    const int rr = 8 * f + (lane >> 3);
+    int64_t row = m0 + rr;
+    row = row < M ? row : M - 1;
+    const int j = (lane & 7) ^ (rr & 7);
+    __builtin_amdgcn_global_load_lds(a_codes + row * K + ks * 128 + 16 * j, dst + f * 1024, 16, 0, 0);
+  }
+  LDS uint8_t* wdst = dst + C::A_BYTES;
+#pragma unroll
+  for (int i = 0; i < C::W_DMA; ++i) {
+    const int f = wave * C::W_DMA + i;  // half (f % 2) of tile f / 2
+    int64_t ng = ng0 + f / 2;
+    ng = ng < NG ? ng : NG - 1;
+    __builtin_amdgcn_global_load_lds(wc + (ng * KS + ks) * 2048 + (f & 1) * 1024 + 16 * lane,
+                                     wdst + f * 1024, 16, 0, 0);
+  }
+  LDS uint8_t* asdst = wdst + C::W_BYTES;
+  if (lane < C::AS_DW) {
+    int64_t row = m0 + wave * C::AS_DW + lane;
+    row = row < M ? row : M - 1;
+    __builtin_amdgcn_global_load_lds(a_scales + row * (K / 32) + ks * 4, asdst + wave * C::AS_DW * 4,
+                                     4, 0, 0);
+  }
+  LDS uint8_t* wsdst = asdst + C::AS_BYTES;
+  if (wave < BN / 64) {
+    int64_t sg = ng0 / 4 + wave;
+    sg = sg < NSG ? sg : NSG - 1;
+    __builtin_amdgcn_global_load_lds(wsw + (sg * KS + ks) * 64 + lane, wsdst + wave * 256, 4, 0, 0);
+  } else {
+    // same copy count on every wave: the last set again (same bytes)
+    int64_t sg = ng0 / 4 + (BN / 64 - 1);
+    sg = sg < NSG ? sg : NSG - 1;
+    __builtin_amdgcn_global_load_lds(wsw + (sg * KS + ks) * 64 + lane,
+                                     wsdst + (BN / 64 - 1) * 256, 4, 0, 0);
+  }
+}
+
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__device__ __forceinline__ void mx8_step(const LDS uint8_t* __restrict__ st, int wn, int wm, int lane,
+                                         v4f (&acc)[BN / 16 / WN][BM / 16 / WM]) {
+  using C = Mx8Cfg<BN, BM, WN, WM, DEPTH>;
+  constexpr int FN = C::FN, FM = C::FM;
+  const int r = lane & 15, c = lane >> 4;
+  const LDS uint8_t* A = st;
+  const LDS uint8_t* W = st + C::A_BYTES;
+  const LDS uint8_t* AS = W + C::W_BYTES;
+  const LDS uint32_t* WS = reinterpret_cast<const LDS uint32_t*>(AS + C::AS_BYTES);
+  if constexpr (FMT == MXFP8) {
+    // bf16 expansion with the block scales folded in: the first half of a
+    // lane's bytes lies in block c / 2, the second in block 2 + c / 2
+    const int b0 = c >> 1;
+    Bf16Frag ab[FM];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int R = wm * (16 * FM) + 16 * j + r;
+      const u32x4 lo = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * (c ^ (R & 7)));
+      const u32x4 hi = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * ((4 + c) ^ (R & 7)));
+      ab[j] = e4m3_frag_bf16(v8i_of(lo, hi), e8m0_scale(AS[R * 4 + b0]), e8m0_scale(AS[R * 4 + 2 + b0]));
+    }
+    uint32_t sw0[FN / 4], sw1[FN / 4];
+#pragma unroll
+    for (int q = 0; q < FN / 4; ++q) {
+      sw0[q] = WS[(wn * (FN / 4) + q) * 64 + r + 16 * b0];
+      sw1[q] = WS[(wn * (FN / 4) + q) * 64 + r + 16 * (2 + b0)];
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const LDS uint8_t* wt = W + (wn * FN + i) * 2048 + 32 * lane;
+      const u32x4 wlo = *reinterpret_cast<const LDS u32x4*>(wt);
+      const u32x4 whi = *reinterpret_cast<const LDS u32x4*>(wt + 16);
+      const int sh = 8 * (i % 4);
+      const Bf16Frag wb = e4m3_frag_bf16(v8i_of(wlo, whi), e8m0_scale(sw0[i / 4] >> sh),
+                                         e8m0_scale(sw1[i / 4] >> sh));
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = mfma_bf16x4(wb, ab[j], acc[i][j]);
+    }
+  } else {
+    v8i af[FM];
+    Mx8Split as[FM];
+    int sa[FM];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int R = wm * (16 * FM) + 16 * j + r;
+      const u32x4 lo = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * (c ^ (R & 7)));
+      const u32x4 hi = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * ((4 + c) ^ (R & 7)));
+      af[j] = v8i_of(lo, hi);
+      sa[j] = AS[R * 4 + c];
+      as[j] = int8_frag_split(af[j]);
+    }
+    uint32_t sw[FN / 4];
+#pragma unroll
+    for (int q = 0; q < FN / 4; ++q) sw[q] = WS[(wn * (FN / 4) + q) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const LDS uint8_t* wt = W + (wn * FN + i) * 2048 + 32 * lane;
+      const u32x4 wlo = *reinterpret_cast<const LDS u32x4*>(wt);
+      const u32x4 whi = *reinterpret_cast<const LDS u32x4*>(wt + 16);
+      const v8i w = v8i_of(wlo, whi);
+      const Mx8Split ws = int8_frag_split(w);
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+        acc[i][j] = mx8_mfma<FMT>(i % 4, w, ws, af[j], as[j], acc[i][j], int(sw[i / 4]), sa[j]);
+    }
+  }
+}
+
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+__global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx8_tile_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
+    int tiles_m, int tiles_total, int per_xcd) {
+  static_assert(FMT == MXFP8 || FMT == MXINT8, "8-bit MX formats");
+  using C = Mx8Cfg<BN, BM, WN, WM, DEPTH>;
+  constexpr int FN = C::FN, FM = C::FM;
+  const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (tile >= tiles_total) return;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+
+  const BlobLayout L = blob_layout(FMT, N, K);
+  const int64_t m0 = int64_t(tm) * BM, ng0 = int64_t(tn) * (BN / 16);
+  const uint8_t* wc = blob + L.code_off;
+  const uint32_t* wsw = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * C::STAGE];
+  LDS uint8_t* base = (LDS uint8_t*)smem;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int wn = wave % WN, wm = wave / WN;
+
+  v4f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t KS = L.KS;
+#pragma unroll
+  for (int s = 0; s < DEPTH - 1; ++s)
+    if (s < KS)
+      mx8_issue<FMT, BN, BM, WN, WM, DEPTH>(a_codes, a_scales, wc, wsw, M, K, KS, L.NG, L.NSG, m0,
+                                            ng0, s, base + s * C::STAGE, wave, lane);
+  for (int64_t s = 0; s < KS; ++s) {
+    // stages issued after s: min(DEPTH - 2, KS - 1 - s)
+    const int64_t left = KS - 1 - s;
+    stage_ready<C::COPIES, DEPTH>(int(left < DEPTH - 2 ? left : DEPTH - 2));
+    if (s + DEPTH - 1 < KS)
+      mx8_issue<FMT, BN, BM, WN, WM, DEPTH>(a_codes, a_scales, wc, wsw, M, K, KS, L.NG, L.NSG, m0,
+                                            ng0, s + DEPTH - 1,
+                                            base + ((s + DEPTH - 1) % DEPTH) * C::STAGE, wave, lane);
+    mx8_step<FMT, BN, BM, WN, WM, DEPTH>(base + (s % DEPTH) * C::STAGE, wn, wm, lane, acc);
+  }
+
+  __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
+  asm volatile("" ::: "memory");
+  const TileArgs t = tile_args(FMT, a_codes, a_scales, blob, L, M, K, m0, ng0);
+  tile_epilogue<FN, FM, WN, WM>(acc, base, t, blob, L, mx8_epilogue_factor(FMT), Y, M, N, wave, lane);
+}
+
+template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
+hipError_t launch_mx8_tile(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                           const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  const int tiles_n = int((N + BN - 1) / BN);
+  const int tiles_m = int((M + BM - 1) / BM);
+  const int total = tiles_n * tiles_m;
+  const int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL((gemm_mx8_tile_kernel<FMT, BN, BM, WN, WM, DEPTH>), dim3(unsigned(per_xcd * 8)),
+                     dim3(64 * WN * WM), 0, stream, ac, as, blob, Y, M, N, K, tiles_m, total,
+                     per_xcd);
+  return hipGetLastError();
+}
+
 template <int FMT, int BN, int BM, int WN, int WM, int DEPTH>
 hipError_t launch_tile(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                        const float* t_act, const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
@@ -2527,7 +2976,20 @@ template <int FMT>
 hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                       const float* t_act, const uint8_t* blob, uint16_t* Y, void* workspace,
                       hipStream_t stream) {
-  if constexpr (FMT == NVFP4) {
+  if constexpr (FMT == MXFP8 || FMT == MXINT8) {
+    if (M <= 16) {
+      // weight streaming; waves enough for at most 8 K-steps each, more
+      // waves when there are few groups
+      const int64_t ks = K / 128, groups = N / 16;
+      if (ks <= 32 && groups < 256) return launch_mx8_decode<FMT, 16, 2>(M, N, K, ac, as, blob, Y, stream);
+      if (ks <= 32 && groups < 1024) return launch_mx8_decode<FMT, 8, 4>(M, N, K, ac, as, blob, Y, stream);
+      if (ks <= 32) return launch_mx8_decode<FMT, 4, 8>(M, N, K, ac, as, blob, Y, stream);
+      // long K: 8 waves in batches of 8 K-steps (16 waves of 8 would not
+      // fit their loads in the 128 registers a wave of 1024 threads has)
+      return launch_mx8_decode<FMT, 8, 8>(M, N, K, ac, as, blob, Y, stream);
+    }
+    return launch_mx8_tile<FMT, 256, 128, 2, 2, 3>(M, N, K, ac, as, blob, Y, stream);
+  } else if constexpr (FMT == NVFP4) {
     if (M <= 16) {
       // weight streaming; waves enough for at most 8 K-steps each, more
       // waves when there are few groups
@@ -2617,6 +3079,8 @@ hipError_t launch_linear(int fmt, int64_t M, int64_t N, int64_t K, const void* a
   switch (fmt) {
     case MXFP4: return launch_fmt<MXFP4>(M, N, K, ac, as, t_act, b, y, workspace, stream);
     case MXINT4: return launch_fmt<MXINT4>(M, N, K, ac, as, t_act, b, y, workspace, stream);
+    case MXFP8: return launch_fmt<MXFP8>(M, N, K, ac, as, t_act, b, y, workspace, stream);
+    case MXINT8: return launch_fmt<MXINT8>(M, N, K, ac, as, t_act, b, y, workspace, stream);
     default: return launch_fmt<NVFP4>(M, N, K, ac, as, t_act, b, y, workspace, stream);
   }
 }

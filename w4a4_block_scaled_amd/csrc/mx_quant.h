@@ -66,4 +66,48 @@ __device__ __forceinline__ void quant8_mx(const float (&x)[8], uint32_t& word, u
   }
 }
 
+// The 8-bit MX variants (MXFP8: E4M3 elements, emax_elem = 8; MXINT8: int8
+// elements, emax_elem = 6): codes (one byte each) and the scale byte of one
+// 32-block from this lane's 8 elements, same lane-quad layout and the same
+// shared-exponent rule.
+template <int FMT>
+__device__ __forceinline__ void quant8_mx8(const float (&x)[8], uint32_t (&word)[2], uint32_t& sbyte) {
+  uint32_t abits = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) abits = max(abits, __float_as_uint(x[i]) & 0x7fffffffu);
+  abits = max(abits, uint32_t(quad_xor1(int(abits))));
+  abits = max(abits, uint32_t(quad_xor2(int(abits))));
+  const bool bad = abits > 0x7f7fffffu;  // Inf or NaN in the block
+  constexpr int EMAX = FMT == MXFP8 ? 8 : 6;
+  int e = -127;
+  if (abits != 0) e = max(-127, min(127, floor_log2(__uint_as_float(abits)) - EMAX));
+  word[0] = word[1] = 0;
+  if (FMT == MXFP8) {
+    // |x 2^-e| < 512: values above 448 saturate (448 converts exactly), the
+    // rest go through the hardware E4M3 conversion (nearest even, sign kept
+    // for values that round to zero)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = fmaxf(fminf(ldexpf(x[4 * h + i], -e), 448.0f), -448.0f);
+      int w = 0;
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], w, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+      word[h] = uint32_t(w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q = fminf(rintf(ldexpf(x[i], -e)), 127.0f);  // |v| < 128: only +128 clips
+      word[i >> 2] |= (uint32_t(int(q)) & 255u) << (8 * (i & 3));
+    }
+  }
+  sbyte = uint32_t(e + 127);
+  if (bad) {
+    word[0] = word[1] = 0;
+    sbyte = 0xff;
+  }
+}
+
 }  // namespace w4a4

@@ -29,9 +29,20 @@ constexpr int kThreads = 256;
 //            block b still comes from lane group b.  So lane group c carries
 //            half (c & 1) of block (c >> 1) in bytes 0..7 and the same half
 //            of block 2 + (c >> 1) in bytes 8..15.
+//   MXFP8, MXINT8: one byte per code, so unit u holds 8 codes; 2 KiB tiles of
+//            16 rows x 128 K, lane (n%16) + 16 c owning 32 bytes: K 16c..16c+15
+//            (units 0, 1 of the lane) and 64+16c..64+16c+15 (units 2, 3).
 __device__ __forceinline__ int64_t unit_dest(int fmt, int64_t n, int64_t u, int64_t KT) {
   int64_t g, h;
   int lane, off;
+  if (is_mx8(fmt)) {
+    g = n >> 4;
+    h = u >> 4;
+    const int v = int(u & 15);             // 8-code unit within the 128-K step
+    const int half = v >> 3, c = (v >> 1) & 3;
+    lane = int(n & 15) + 16 * c;
+    return ((g * KT + h) * 64 + lane) * 4 + 2 * half + (v & 1);
+  }
   if (fmt == MXFP4) {
     g = n >> 5;
     h = u >> 2;
@@ -55,6 +66,7 @@ __global__ __launch_bounds__(kThreads) void pack_codes_kernel(int fmt, const uin
                                                               uint2* __restrict__ dst,
                                                               int64_t n_units, int64_t N,
                                                               int64_t K16, int64_t KT) {
+  // K16: 8-byte units per canonical row
   const int64_t q = int64_t(blockIdx.x) * kThreads + threadIdx.x;
   if (q >= n_units) return;
   const int64_t n = q / K16, u = q - n * K16;
@@ -176,11 +188,12 @@ hipError_t launch_pack_weight(int fmt, int64_t N, int64_t K, const void* codes,
                               hipStream_t stream) {
   const BlobLayout L = blob_layout(fmt, N, K);
   uint8_t* b = static_cast<uint8_t*>(blob);
-  const int64_t n_units = L.NG * tile_rows(fmt) * (K / 16);  // padded rows included
+  const int64_t row_units = code_row_bytes(fmt, K) / 8;
+  const int64_t n_units = L.NG * tile_rows(fmt) * row_units;  // padded rows included
   if (n_units)
     hipLaunchKernelGGL(pack_codes_kernel, dim3(blocks_for(n_units)), dim3(kThreads), 0, stream, fmt,
                        static_cast<const uint2*>(codes), reinterpret_cast<uint2*>(b + L.code_off),
-                       n_units, N, K / 16, L.KT);
+                       n_units, N, row_units, L.KT);
   const int64_t n_sw = L.NSG * L.KT * 64;
   if (n_sw)
     hipLaunchKernelGGL(pack_scales_kernel, dim3(blocks_for(n_sw)), dim3(kThreads), 0, stream, fmt,
@@ -196,11 +209,12 @@ hipError_t launch_unpack_weight(int fmt, int64_t N, int64_t K, const void* blob,
                                 void* scales, float* r, float* t_w, hipStream_t stream) {
   const BlobLayout L = blob_layout(fmt, N, K);
   const uint8_t* b = static_cast<const uint8_t*>(blob);
-  const int64_t n_units = N * K / 16;
+  const int64_t row_units = code_row_bytes(fmt, K) / 8;
+  const int64_t n_units = N * row_units;
   if (codes && n_units)
     hipLaunchKernelGGL(unpack_codes_kernel, dim3(blocks_for(n_units)), dim3(kThreads), 0, stream,
                        fmt, reinterpret_cast<const uint2*>(b + L.code_off),
-                       static_cast<uint2*>(codes), n_units, K / 16, L.KT);
+                       static_cast<uint2*>(codes), n_units, row_units, L.KT);
   const int64_t n_sw = L.NSG * L.KT * 64;
   if (scales && n_sw)
     hipLaunchKernelGGL(unpack_scales_kernel, dim3(blocks_for(n_sw)), dim3(kThreads), 0, stream,

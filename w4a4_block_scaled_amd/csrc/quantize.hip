@@ -291,6 +291,53 @@ __global__ __launch_bounds__(kThreads) void quantize_nv_multi_kernel(const uint4
   }
 }
 
+// The 8-bit MX variants: as quantize_mx_kernel, with 8 code bytes per thread
+// and row (one 8-byte store).
+template <int FMT, int R>
+__global__ __launch_bounds__(kThreads) void quantize_mx8_kernel(
+    const uint4* __restrict__ X, const float* __restrict__ c, uint2* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t M, int64_t K8) {
+  const int64_t col_raw = int64_t(blockIdx.y) * kThreads + threadIdx.x;
+  const bool live_c = col_raw < K8;
+  const int64_t col8 = live_c ? col_raw : K8 - 1;  // every lane joins the shuffles
+  const int64_t r0 = int64_t(blockIdx.x) * R;
+  float cc[8];
+  if (c) {
+    const float4 c0 = reinterpret_cast<const float4*>(c)[2 * col8];
+    const float4 c1 = reinterpret_cast<const float4*>(c)[2 * col8 + 1];
+    cc[0] = c0.x; cc[1] = c0.y; cc[2] = c0.z; cc[3] = c0.w;
+    cc[4] = c1.x; cc[5] = c1.y; cc[6] = c1.z; cc[7] = c1.w;
+  }
+  typedef unsigned ux4 __attribute__((ext_vector_type(4)));
+  ux4 v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = r0 + r < M ? r0 + r : M - 1;
+    v[r] = __builtin_nontemporal_load(reinterpret_cast<const ux4*>(X) + row * K8 + col8);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+      x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+    if (c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = __fmul_rn(x[i], cc[i]);  // one rounded fp32 multiply
+    }
+    uint32_t word[2], sbyte;
+    quant8_mx8<FMT>(x, word, sbyte);
+    const int64_t row = r0 + r;
+    if (live_c && row < M) {
+      codes[row * K8 + col8] = uint2{word[0], word[1]};
+      if ((col8 & 3) == 0) scales[row * (K8 / 4) + (col8 >> 2)] = uint8_t(sbyte);
+    }
+  }
+}
+
 template <int P>
 hipError_t launch_multi(int fmt, int64_t M, int64_t K, const uint4* Xv, MultiOut o,
                         hipStream_t stream) {
@@ -334,7 +381,23 @@ hipError_t launch_quantize_act(int fmt, int64_t M, int64_t K, const void* X, con
   const uint4* Xv = static_cast<const uint4*>(X);
   uint32_t* cw = static_cast<uint32_t*>(codes);
   uint8_t* sb = static_cast<uint8_t*>(scales);
-  if (fmt == MXFP4 || fmt == MXINT4) {
+  if (is_mx8(fmt)) {
+    const unsigned gy = unsigned((K8 + kThreads - 1) / kThreads);
+    uint2* cw8 = static_cast<uint2*>(codes);
+    if (M >= 256) {
+      const dim3 g2(unsigned((M + 1) / 2), gy);
+      if (fmt == MXFP8)
+        hipLaunchKernelGGL((quantize_mx8_kernel<MXFP8, 2>), g2, dim3(kThreads), 0, stream, Xv, c, cw8, sb, M, K8);
+      else
+        hipLaunchKernelGGL((quantize_mx8_kernel<MXINT8, 2>), g2, dim3(kThreads), 0, stream, Xv, c, cw8, sb, M, K8);
+    } else {
+      const dim3 g1(unsigned(M), gy);
+      if (fmt == MXFP8)
+        hipLaunchKernelGGL((quantize_mx8_kernel<MXFP8, 1>), g1, dim3(kThreads), 0, stream, Xv, c, cw8, sb, M, K8);
+      else
+        hipLaunchKernelGGL((quantize_mx8_kernel<MXINT8, 1>), g1, dim3(kThreads), 0, stream, Xv, c, cw8, sb, M, K8);
+    }
+  } else if (fmt == MXFP4 || fmt == MXINT4) {
     // 2 rows per thread once there are enough rows to fill the chip (1, 4,
     // 8 or 16 rows per thread measured slower on 2048-row activations)
     const unsigned gy = unsigned((K8 + kThreads - 1) / kThreads);

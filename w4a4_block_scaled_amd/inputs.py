@@ -20,6 +20,8 @@ Qwen-7B-class linears; formats MXFP4 / NVFP4 / MXINT4 from Section 3):
   Activations N(0,1) with round(0.01 K) outlier channels x30.
 * ``llama_nvfp4`` : NVFP4, M=4096, same shapes; activations i.i.d.
   Student-t with 3 degrees of freedom.
+* ``llama_mxfp8`` / ``llama_mxint8`` : the 8-bit MX variants (Appendix G.2),
+  M in {2048, 1}, Llama shapes and laws as ``llama_prefill``.
 * ``qwen_mxint4`` : MXINT4, M in {1,512,4096}, Qwen-7B-class shapes (QKV
   3584->4608, O 3584->3584, gate+up 3584->37888, down 18944->3584).
   Weight codes drawn directly (uniform int4) with E8M0 exponents uniform in
@@ -42,8 +44,9 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-FORMATS = ("mxfp4", "nvfp4", "mxint4", "int4g64")
-BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32, "int4g64": 64}
+FORMATS = ("mxfp4", "nvfp4", "mxint4", "int4g64", "mxfp8", "mxint8")
+BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32, "int4g64": 64, "mxfp8": 32, "mxint8": 32}
+EIGHT_BIT = ("mxfp8", "mxint8")
 
 LLAMA_LINEARS = (("qkv", 6144, 4096), ("o", 4096, 4096),
                  ("gate_up", 28672, 4096), ("down", 4096, 14336))
@@ -59,6 +62,9 @@ WORKLOADS = {
     "qwen_mxint4": (5, "mxint4", (1, 512, 4096), QWEN_LINEARS),
     # INT4 G=64 with BF16 scales: Llama shapes, prefill and decode
     "llama_int4g64": (6, "int4g64", (2048, 1), LLAMA_LINEARS),
+    # the 8-bit MX variants (Appendix G.2, Table 9): Llama shapes, prefill and decode
+    "llama_mxfp8": (7, "mxfp8", (2048, 1), LLAMA_LINEARS),
+    "llama_mxint8": (8, "mxint8", (2048, 1), LLAMA_LINEARS),
 }
 
 
@@ -71,7 +77,8 @@ class LinearCase:
     r           : float32 [N]  row scales (multiplied into the output)
     w_prescaled : torch.bfloat16 [N, K] weights already divided by r and c,
                   to be quantized by the method's quantizer (or None)
-    w_codes     : uint8 [N, K/2] canonical packed codes (or None)
+    w_codes     : uint8 [N, K/2] canonical packed codes ([N, K] for 8-bit
+                  formats) (or None)
     w_scales    : uint8 [N, K/G] block scale bytes (uint16 BF16 patterns for
                   int4g64) (or None)
     t_w         : float tensor scale of the weights when codes are drawn
@@ -154,9 +161,16 @@ def prescaled_weights(rng: np.random.Generator, N: int, K: int, r: np.ndarray,
 
 
 def random_codes(rng: np.random.Generator, N: int, K: int, G: int,
-                 exp_lo: int, exp_hi: int):
-    """Canonical packed codes uniform over all 16 nibbles, E8M0 bytes 127+U{lo..hi}."""
-    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+                 exp_lo: int, exp_hi: int, fmt: str = "mxfp4"):
+    """Canonical codes and E8M0 bytes 127+U{lo..hi}: packed nibbles uniform over
+    all 16 values, or for the 8-bit formats one byte per element, uniform over
+    all 256 bytes except the E4M3 NaN codes 0x7F / 0xFF (MXFP8)."""
+    if fmt in EIGHT_BIT:
+        codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+        if fmt == "mxfp8":
+            codes = np.where((codes & 0x7F) == 0x7F, codes - 1, codes).astype(np.uint8)
+    else:
+        codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     scales = (127 + rng.integers(exp_lo, exp_hi + 1, size=(N, K // G))).astype(np.uint8)
     return codes, scales
 
@@ -171,7 +185,7 @@ def make_case(workload: str, name: str, fmt: str, M: int, N: int, K: int,
     r = admissible_scales(rr, N, family)
     if workload == "llama_nvfp4":
         x = student_t_activations(rx, M, K)
-    elif workload in ("llama_decode", "llama_prefill", "llama_int4g64"):
+    elif workload in ("llama_decode", "llama_prefill", "llama_int4g64", "llama_mxfp8", "llama_mxint8"):
         x = outlier_activations(rx, M, K, int(round(0.01 * K)), 30.0)
     else:  # single, qwen_mxint4 and ad-hoc cases: the single-linear distributions
         x = outlier_activations(rx, M, K, int(round(2 * K / 256)), 50.0)
@@ -220,7 +234,7 @@ def adhoc_case(fmt: str, M: int, N: int, K: int, seed: int,
     if weights == "none":
         return case
     if weights == "codes":
-        case.w_codes, case.w_scales = random_codes(rw, N, K, BLOCK[fmt], -6, 1)
+        case.w_codes, case.w_scales = random_codes(rw, N, K, BLOCK[fmt], -6, 1, fmt)
     else:
         case.w_prescaled = prescaled_weights(rw, N, K, r, c)
     return case
