@@ -2,53 +2,54 @@
 
 TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
-What is computed: Algorithm 1 of the pages ("DualQuant: Dual-Scale
-Quantization via Coordinate Descent", Section 4.3 "MSE optimization via block
-coordinate descent"), which minimizes the weight-reconstruction error
+What is minimized (DualQuant Section 4.3, eq. 4): the weight-reconstruction
+error
 
-    || W - Diag(alpha)^-1 Q(Diag(alpha) W Diag(beta)) Diag(beta)^-1 ||_F^2
+    E(alpha, beta) = || W - Diag(alpha)^-1 Q(Diag(alpha) W Diag(beta)) Diag(beta)^-1 ||_F^2
 
 over a row scale alpha (one per output row) and a column scale beta (one per
-input column) whose inverses live in the format's admissible set F (Section
-4.2; E8M0 for the MX formats, UE4M3 for NVFP4).  Q is the format's row-wise
-block quantizer (Section 3; `quant.quantize_rows`; for NVFP4 with the fp32
-tensor scale of the tensor it quantizes).  Each iteration:
+input column) whose inverses r = alpha^-1 and c = beta^-1 lie in the
+format's admissible set F (Section 4.2: E8M0 for the MX formats, UE4M3 for
+NVFP4).  Q is the format's row-wise block quantizer (Section 3;
+`quant.quantize_rows`; for NVFP4 with the fp32 tensor scale of the tensor it
+quantizes), and Q^ below is its value (code x block scale, x t for NVFP4).
 
-  1. Q^ = Q(Diag(alpha) W Diag(beta)); R = Q^ Diag(beta)^-1;
-     alpha^-1_i = Pi_F( <W_i, R_i> / ||R_i||^2 ), the closed-form minimizer
-     of the row's 1-D quadratic (Section 4.3, "Closed-form scale updates"),
-     projected to the nearest admissible value (Appendix C, Remark 1);
-  2. Q^ = Q(Diag(alpha) W Diag(beta)) with the new alpha; S = Diag(alpha)^-1 Q^;
-     beta^-1_j = Pi_F( <W_j, S_j> / ||S_j||^2 ) over the column.
+How (block coordinate descent with variable splitting, Section 4.3 and
+Appendices A-B, Algorithm 1 of the paper): with the quantized matrix Q^ held
+fixed, E is a sum of independent 1-D quadratics in the inverse scales of one
+axis, u = r_i along rows or v = c_j along columns,
 
-It returns r = alpha^-1, c = beta^-1 and Q(Diag(alpha) W Diag(beta)), so that
-W ~ Diag(r) Q Diag(c): r goes into the packed weight, c into the activation
-quantizer.  Initialization (Section 5, "Hyperparameter selection"): the
-row absmax and the column l1 norm; T = 15 by default.
+    || W_slice - u * D_slice ||^2,   D = Q^ / (the other axis' scale),
+
+whose minimizer is <W_slice, D_slice> / ||D_slice||^2 (Appendix B); the
+nearest admissible value is then the constrained minimizer (Appendix C,
+Remark 1).  One generic half-step, `half_step`, does this for one axis: it
+re-quantizes at the current scales (the inner copies are synchronized with
+the outer ones, Appendix A.1), then sets that axis' scales.  An iteration is
+the row half-step followed by the column half-step; T = 15 iterations by
+default (Section 5), stopping early when an iteration leaves (alpha, beta)
+unchanged, since every later iteration would then repeat it exactly.
 
 Readings where the pages leave a step open:
-  * Initialization: alpha_0,i^-1 = max_j |W_ij| and beta_0,j^-1 = sum_i |W_ij|,
-    i.e. the inverse scales start at those magnitudes (the extracted text
-    shows the magnitudes without an inverse marker).  Taken literally (alpha_0
-    = absmax) the solver ends about 2x above round-to-nearest on synthetic
-    weights with outlier columns; with the inverse it ends 1.3-1.9x below
-    (MX formats), and beta then follows a weight-only smoothing scale, as the pages report.
-    alpha_0 = fp32(1 / absmax) and beta_0 = fp32(1 / l1) from fp64 quotients;
-    an all-zero row or column starts at 1.
+  * Initialization (Section 5, "Hyperparameter selection": the row absmax and
+    the column l1 norm).  Read with the inverse-scale convention of Section
+    4.2: alpha_0^-1 = max_j |W_ij| and beta_0^-1 = sum_i |W_ij|, so beta_0
+    equalizes the columns.  This is the reading under which beta reproduces
+    Table 5 (beta correlates with SmoothQuant's weight-only scale
+    1 / max_i |W_ij|, Pearson 0.83-0.97 there; pinned by outcome in the
+    tests); taking the magnitudes as the multipliers themselves gives a
+    negative correlation, and starting from alpha = beta = 1 none.  alpha_0 =
+    fp32(1 / absmax), beta_0 = fp32(1 / l1) from fp64 quotients; an all-zero
+    row or column starts at 1.  These starting scales are not admissible;
+    the first half-steps project them.
   * The rescaled weight is W~_ij = fp32(fp32(alpha_i * W_ij) * beta_j), with
     alpha = fp32(1 / r) and beta = fp32(1 / c) (fp64 quotients rounded to
     fp32; exact for E8M0) and fp32 W.  For NVFP4, Q^ includes the tensor
     scale t of W~ (code x block scale x t, exact in fp64), and the returned
     codes come with the t of the final W~ (t_w; 1 for the MX formats).
-  * Q^, R and S are fp64 values (Q^ = code x block scale is exact; R and S
-    one fp64 division each); the inner products and squared norms are fp64
-    sums taken in a fixed order, so that another implementation following
-    the same order reaches the same projected scales:
-      rows:    8 consecutive terms sequentially, the four such partials of a
-               32-block as ((p0 + p1) + p2) + p3, then the blocks in order;
-      columns: rows in chunks of 16, each chunk sequentially, then the chunks
-               in order.
-    beta_0 uses the column order; alpha_0 is an exact maximum.
+  * Q^ and D are fp64 values (Q^ exact, D one fp64 division each); the inner
+    products and squared norms are exact sums of the fp64 products
+    (math.fsum), rounded once.
   * The projection is to the nearest admissible value in linear distance
     (Remark 1: the subproblem is a convex quadratic in the inverse scale).
     E8M0: the powers of two 2^e, e in [-127, 127]; an exact tie 1.5 * 2^e
@@ -58,8 +59,19 @@ Readings where the pages leave a step open:
     below 2^-9 (or non-positive) goes to 2^-9.
   * A row (column) whose Q^ is all zero has no minimizer; its scale is set to
     1 (the pages' convention for rows, applied to columns alike).
+
+What follows from these readings (recorded, and pinned where the pages fix
+an outcome): for the MX formats a power-of-two row scale is absorbed by the
+E8M0 block scales (Q(2^k x) = 2^k Q(x)), so row half-steps change the row
+scales but not the reconstruction (Table 4 shows the alpha-only variant equal
+to RTN on MXFP4 for the same reason); the column update fits the scale to
+values quantized at the current scale, so it moves only where quantization
+bias pushes the least-squares coefficient past a projection midpoint, and
+(alpha, beta) reach a fixed point within a few iterations.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -67,7 +79,6 @@ from .quant import quantize_rows, pack_nibbles, dequantize
 
 E8M0_MIN = 2.0 ** -127
 E8M0_MAX = 2.0 ** 127
-COL_CHUNK = 16
 
 
 def project_e8m0(u):
@@ -102,33 +113,11 @@ def project(u, fmt):
     return project_ue4m3(u) if fmt == "nvfp4" else project_e8m0(u)
 
 
-def row_sums(P):
-    """Sum of each row of P [N, K] (K % 32 == 0) in the fixed order above."""
+def exact_sums(P, axis):
+    """Correctly rounded sums of the fp64 array P along `axis` (math.fsum)."""
     P = np.asarray(P, np.float64)
-    N, K = P.shape
-    q = P.reshape(N, K // 32, 4, 8)
-    p = q[..., 0].copy()
-    for t in range(1, 8):
-        p = p + q[..., t]
-    b = ((p[..., 0] + p[..., 1]) + p[..., 2]) + p[..., 3]
-    s = b[:, 0].copy()
-    for j in range(1, K // 32):
-        s = s + b[:, j]
-    return s
-
-
-def col_sums(P):
-    """Sum of each column of P [N, K] in the fixed order above."""
-    P = np.asarray(P, np.float64)
-    N, K = P.shape
-    total = None
-    for r0 in range(0, N, COL_CHUNK):
-        blk = P[r0:r0 + COL_CHUNK]
-        s = blk[0].copy()
-        for i in range(1, blk.shape[0]):
-            s = s + blk[i]
-        total = s if total is None else total + s
-    return total
+    P = P if axis == 1 else P.T
+    return np.array([math.fsum(row) for row in P], np.float64)
 
 
 def rescaled(w, alpha, beta):
@@ -146,23 +135,28 @@ def qhat(w, alpha, beta, fmt):
     return q * np.float64(t) if fmt == "nvfp4" else q
 
 
-def _update(num, den, fmt):
+def axis_update(w, q, other, fmt, axis):
+    """Projected inverse scales along `axis` (1: rows, r; 0: columns, c) for a
+    fixed Q^ = q: each slice's 1-D least-squares coefficient of W against
+    D = Q^ / (the other axis' scale, broadcast across the slice), projected
+    to F; 1 where the slice of D is all zero."""
+    other = np.asarray(other, np.float32).astype(np.float64)
+    D = q / (other[None, :] if axis == 1 else other[:, None])
+    wd = np.asarray(w, np.float32).astype(np.float64)
+    num = exact_sums(wd * D, axis)
+    den = exact_sums(D * D, axis)
     ok = den > 0
     return np.where(ok, project(num / np.where(ok, den, 1.0), fmt), 1.0)
 
 
 def row_update(w, q, beta, fmt="mxfp4"):
     """Projected alpha^-1 (= r) from Q^ = q and the current beta."""
-    R = q / np.asarray(beta, np.float32).astype(np.float64)[None, :]
-    wd = np.asarray(w, np.float32).astype(np.float64)
-    return _update(row_sums(wd * R), row_sums(R * R), fmt)
+    return axis_update(w, q, beta, fmt, 1)
 
 
 def col_update(w, q, alpha, fmt="mxfp4"):
     """Projected beta^-1 (= c) from Q^ = q and the current alpha."""
-    S = q / np.asarray(alpha, np.float32).astype(np.float64)[:, None]
-    wd = np.asarray(w, np.float32).astype(np.float64)
-    return _update(col_sums(wd * S), col_sums(S * S), fmt)
+    return axis_update(w, q, alpha, fmt, 0)
 
 
 def _inverse(x):
@@ -174,7 +168,7 @@ def init_scales(w):
     """alpha_0 = 1 / row absmax, beta_0 = 1 / column l1 norm (fp32)."""
     w = np.asarray(w, np.float32)
     amax = np.max(np.abs(w), axis=1).astype(np.float64)
-    l1 = col_sums(np.abs(w).astype(np.float64))
+    l1 = exact_sums(np.abs(w).astype(np.float64), 0)
     return _inverse(amax), _inverse(l1)
 
 
@@ -185,14 +179,26 @@ def mse(w, r, c, q):
     return float(np.sum((wd - rec) ** 2))
 
 
-def solve(w, fmt, iters=15, history=None):
-    """Algorithm 1 on W (fp32 [N, K], K % 32 == 0).
+def half_step(w, alpha, beta, fmt, axis):
+    """Synchronize Q^ with the current scales, then set the scales of one axis
+    to their projected closed-form minimizers.  Returns (alpha, beta, inverse
+    scales of that axis, Q^ used)."""
+    q = qhat(w, alpha, beta, fmt)
+    if axis == 1:
+        r = axis_update(w, q, beta, fmt, 1)
+        return (1.0 / r).astype(np.float32), beta, r, q
+    c = axis_update(w, q, alpha, fmt, 0)
+    return alpha, (1.0 / c).astype(np.float32), c, q
+
+
+def solve(w, fmt, iters=15, history=None, stop_at_fixed_point=True):
+    """Block coordinate descent on W (fp32 [N, K], K % 32 == 0).
 
     Returns (r fp32 [N], c fp32 [K], packed codes [N, K/2], scales [N, K/G],
     t_w fp32: the NVFP4 tensor scale of the final W~, 1 for MX).
-    If `history` is a list, each half-step appends (phase, Q^, objective):
-    phase "row" or "col", Q^ = Q(Diag(alpha) W Diag(beta)) at the scales just
-    updated and the objective || W - Diag(alpha)^-1 Q^ Diag(beta)^-1 ||^2 there.
+    If `history` is a list, each half-step appends (axis, Q^, objective):
+    axis "row" or "col", Q^ = Q(Diag(alpha) W Diag(beta)) re-quantized at the
+    scales just set, and E there.
     """
     if fmt not in ("mxfp4", "mxint4", "nvfp4"):
         raise ValueError(f"unknown format {fmt}")
@@ -203,18 +209,19 @@ def solve(w, fmt, iters=15, history=None):
     alpha, beta = init_scales(w)
     r = c = None
     for _ in range(iters):
-        q = qhat(w, alpha, beta, fmt)
-        r = row_update(w, q, beta, fmt)
-        alpha = (1.0 / r).astype(np.float32)
-        q = qhat(w, alpha, beta, fmt)
-        if history is not None:
-            history.append(("row", q, mse(w, 1.0 / alpha.astype(np.float64),
-                                          1.0 / beta.astype(np.float64), q)))
-        c = col_update(w, q, alpha, fmt)
-        beta = (1.0 / c).astype(np.float32)
-        if history is not None:
-            qn = qhat(w, alpha, beta, fmt)
-            history.append(("col", qn, mse(w, r, c, qn)))
+        prev = (alpha, beta)
+        for axis, name in ((1, "row"), (0, "col")):
+            alpha, beta, s, _ = half_step(w, alpha, beta, fmt, axis)
+            if axis == 1:
+                r = s
+            else:
+                c = s
+            if history is not None:
+                q = qhat(w, alpha, beta, fmt)
+                history.append((name, q, mse(w, 1.0 / alpha.astype(np.float64),
+                                             1.0 / beta.astype(np.float64), q)))
+        if stop_at_fixed_point and np.array_equal(prev[0], alpha) and np.array_equal(prev[1], beta):
+            break              # a fixed point: the remaining iterations repeat this one
     codes, scales, t = quantize_rows(rescaled(w, alpha, beta), fmt)
     t_w = np.float32(t) if fmt == "nvfp4" else np.float32(1.0)
     return r.astype(np.float32), c.astype(np.float32), pack_nibbles(codes), scales, t_w

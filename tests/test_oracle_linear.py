@@ -183,3 +183,28 @@ def test_table12_storage_arithmetic():
     assert round(codes_bytes / 1e9, 2) == 3.49
     assert round(scale_bytes / 1e9, 2) == 0.22
     assert round(params * 2 / 1e9, 2) == 13.96
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4", "nvfp4"])
+def test_linear_abs_sum_matches_exact_rational_evaluation(fmt):
+    """The scale of gate G1's bound, S[m, n] = |r[n]| t sum_k |a^[m,k] w^[n,k]|,
+    against a Fraction evaluation built from first-principles decoding of the
+    codes and scales (independent of oracle.dequantize), to fp64 rounding."""
+    case = inputs.adhoc_case(fmt, 3, 5, 64, seed=12)
+    case.r = case.r * np.where(np.arange(5) % 2, -1.0, 1.0).astype(np.float32)   # |r| matters
+    x = case.x.float().numpy()
+    w_codes, w_scales, t_w = quantize_weight(case.w_prescaled.float().numpy(), fmt)
+    a_codes, a_scales, t_a = quantize_act(x, case.c, fmt)
+    S = oracle.linear.linear_abs_sum(a_codes, a_scales, t_a, w_codes, w_scales, t_w, case.r, fmt)
+    G = oracle.BLOCK[fmt]
+    ac, wc = unpack_nibbles(a_codes), unpack_nibbles(w_codes)
+    tt = Fraction(float(t_a)) * Fraction(float(t_w)) if fmt == "nvfp4" else Fraction(1)
+    for m in range(3):
+        for n in range(5):
+            s = Fraction(0)
+            for k in range(64):
+                s += abs(_exact_elem(int(ac[m, k]), fmt) * _exact_scale(a_scales[m, k // G], fmt) *
+                         _exact_elem(int(wc[n, k]), fmt) * _exact_scale(w_scales[n, k // G], fmt))
+            want = s * tt * abs(Fraction(float(case.r[n])))
+            assert want > 0
+            assert abs(Fraction(float(S[m, n])) - want) <= want * Fraction(1, 2 ** 50), (m, n)
