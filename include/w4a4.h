@@ -331,7 +331,8 @@ w4a4_status w4a4_linear_grouped(w4a4_format fmt, int P, int64_t M, int64_t K,
  * zero gets scale 1.  The inner products and norms are fp64 sums in a fixed
  * order (rows: 8 terms, then ((p0 + p1) + p2) + p3 per 32-block, then the
  * blocks in order; columns: 16-row chunks in order, then the chunks), so
- * results are deterministic.
+ * results are deterministic.  The iterations stop once one leaves (r, c)
+ * unchanged (a fixed point: the rest would repeat it).
  *
  *   W        device, fp32 [N x K] row-major (N output rows, K inputs),
  *            16-byte aligned; finite values.
@@ -346,7 +347,8 @@ w4a4_status w4a4_linear_grouped(w4a4_format fmt, int P, int64_t M, int64_t K,
  *   workspace/ws_bytes: device scratch of at least
  *            w4a4_dualquant_workspace_bytes() bytes, 256-byte aligned
  *            (fp64 partial sums: 16 B per 32-block and per 16-row chunk and
- *            column, and the current scales); no initial contents needed.
+ *            column, the current and previous scales, a flag); no initial
+ *            contents needed.
  *
  * Requires N > 0, K % 32 == 0 (for every format), N*K <= 2^36.  Kernels are
  * enqueued on `stream`; nothing is allocated.

@@ -161,16 +161,17 @@ def test_empty_linear_is_a_no_op():
 
 def test_dualquant_workspace_bytes():
     """fp64 partial sums per (row, 32-block) and per (16-row chunk, column),
-    two of each, the current fp32 scales, 1024 partial maxima and the tensor
-    scale (NVFP4), each 256-byte aligned."""
+    two of each, the current and the previous iteration's fp32 scales, 1024
+    partial maxima, the tensor scale (NVFP4) and the fixed-point flag, each
+    256-byte aligned."""
     L = w4.lib()
 
     def a256(x):
         return (x + 255) // 256 * 256
 
     for N, K in [(64, 256), (100, 4096), (4096, 14336)]:
-        want = (2 * a256(N * (K // 32) * 8) + 2 * a256((N + 15) // 16 * K * 8) + a256(4 * N) +
-                a256(4 * K) + 4096 + 256)
+        want = (2 * a256(N * (K // 32) * 8) + 2 * a256((N + 15) // 16 * K * 8) + 2 * a256(4 * N) +
+                2 * a256(4 * K) + 4096 + 256)
         for fmt in (0, 1, 2):
             assert L.w4a4_dualquant_workspace_bytes(fmt, N, K) == want
     assert L.w4a4_dualquant_workspace_bytes(9, 64, 256) == 0      # unknown format

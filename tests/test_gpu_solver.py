@@ -1,14 +1,20 @@
 """GPU parity of the dual-scale solver (w4a4_dualquant_solve).
 
-The solver's decisions (projections of fp64 sums, block quantization of the
-rescaled weight) are taken in the same precision and summation order as the
-oracle's, so r, c, codes, scales and (NVFP4) t_w must equal the oracle's
-exactly.  At a full Llama size, where the oracle's full run is too slow,
-properties that hold at any size are checked: r and c lie in the admissible
-set, the codes (and t_w) are the quantization of Diag(1/r) W Diag(1/c)
-(oracle quantizer on sampled rows), and, for the MX formats, whose Q^
-stabilizes, r and c are fixed points of the oracle's closed-form updates for
-those codes (rows sampled, columns over all rows)."""
+The GPU takes the solver's discrete decisions (projections of fp64 inner
+products and norms) on sums in its own fixed order; the oracle sums exactly
+(correctly rounded).  The two agree except where a minimizer lies within the
+sums' rounding of a projection midpoint, so the tests compare the GPU's
+(r, c) after T = 1, 2, ... iterations with the oracle's state after the same
+iterations: equal, or, at the first iteration where they differ, every
+differing scale's exact minimizer lies within 1e-12 (relative) of a
+midpoint of the admissible set (such cases are counted and reported; later
+iterations then legitimately differ).  At a full Llama size, where the
+oracle's full run is too slow, properties that hold at any size are checked:
+r and c lie in the admissible set, the codes (and t_w) are the quantization
+of Diag(1/r) W Diag(1/c) (oracle quantizer on sampled rows), and, for the MX
+formats, r and c are fixed points of the oracle's closed-form updates for
+those codes (rows sampled, columns over all rows), up to the same midpoint
+rule."""
 import numpy as np
 import pytest
 import torch
@@ -32,6 +38,57 @@ def weights(seed, N, K, zero_row=None, zero_col=None):
     if zero_col is not None:
         w[:, zero_col] = 0
     return w
+
+
+MIDPOINT_RTOL = 1e-12
+
+
+def midpoint_distance(u, fmt):
+    """Relative distance of u to the nearest projection midpoint of F."""
+    u = np.asarray(u, np.float64)
+    vals = S.E4M3_POS if fmt == "nvfp4" else np.ldexp(1.0, np.arange(-127, 128))
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    i = np.clip(np.searchsorted(mids, u), 1, len(mids) - 1)
+    d = np.minimum(np.abs(mids[i - 1] - u), np.abs(mids[i] - u))
+    return d / np.abs(u)
+
+
+def minimizers(w, q, other, fmt, axis):
+    """The unprojected closed-form minimizers along `axis` (oracle sums)."""
+    other = np.asarray(other, np.float32).astype(np.float64)
+    D = q / (other[None, :] if axis == 1 else other[:, None])
+    wd = np.asarray(w, np.float32).astype(np.float64)
+    num = S.exact_sums(wd * D, axis)
+    den = S.exact_sums(D * D, axis)
+    return num / np.where(den > 0, den, 1.0)
+
+
+def check_scales(got, want, u_star, fmt, label):
+    """got == want, except where the exact minimizer sits within MIDPOINT_RTOL
+    of a projection midpoint; returns the number of such cases."""
+    diff = got != want
+    if not diff.any():
+        return 0
+    dist = midpoint_distance(u_star[diff], fmt)
+    assert np.all(dist <= MIDPOINT_RTOL), \
+        f"{label}: {diff.sum()} scales differ, not at a midpoint (distance {dist.max():.2e})"
+    return int(diff.sum())
+
+
+def oracle_states(w, fmt, iters):
+    """(alpha, beta, r, c, u_rows, u_cols) after each iteration of the oracle,
+    with the unprojected minimizers of its two half-steps."""
+    alpha, beta = S.init_scales(w)
+    out = []
+    for _ in range(iters):
+        q = S.qhat(w, alpha, beta, fmt)
+        u_r = minimizers(w, q, beta, fmt, 1)
+        alpha, beta, r, _ = S.half_step(w, alpha, beta, fmt, 1)
+        q = S.qhat(w, alpha, beta, fmt)
+        u_c = minimizers(w, q, alpha, fmt, 0)
+        alpha, beta, c, _ = S.half_step(w, alpha, beta, fmt, 0)
+        out.append((alpha, beta, r.astype(np.float32), c.astype(np.float32), u_r, u_c))
+    return out
 
 
 def gpu_solve(w, fmt, iters, dev):
@@ -59,11 +116,21 @@ def test_solver_matches_oracle(fmt, N, K, iters, zr, zc):
     dev = device()
     say(f"[solver] {fmt} N={N} K={K} T={iters}")
     w = weights(N * 7 + K, N, K, zr, zc)
-    r, c, codes, scales, t = gpu_solve(w, fmt, iters, dev)
+    states = oracle_states(w, fmt, iters)
+    for t_it in range(1, iters + 1):
+        r, c, codes, scales, t = gpu_solve(w, fmt, t_it, dev)
+        _, _, r_o, c_o, u_r, u_c = states[t_it - 1]
+        near = check_scales(r, r_o, u_r, fmt, f"T={t_it} rows") if not np.array_equal(r, r_o) else 0
+        if near:
+            say(f"    T={t_it}: {near} row scales at a projection midpoint; stopping the comparison")
+            return
+        near = check_scales(c, c_o, u_c, fmt, f"T={t_it} cols")
+        if near:
+            say(f"    T={t_it}: {near} column scales at a projection midpoint; stopping the comparison")
+            return
     r_o, c_o, codes_o, scales_o, t_o = S.solve(w, fmt, iters)
+    assert np.array_equal(r, r_o) and np.array_equal(c, c_o)
     assert t == t_o
-    assert np.array_equal(r, r_o), f"{(r != r_o).sum()} of {N} row scales differ"
-    assert np.array_equal(c, c_o), f"{(c != c_o).sum()} of {K} column scales differ"
     assert np.array_equal(scales, scales_o), f"{(scales != scales_o).sum()} scales differ"
     assert np.array_equal(codes, codes_o), f"{(codes != codes_o).sum()} code bytes differ"
 
@@ -105,9 +172,12 @@ def test_solver_full_size_properties(fmt):
         assert t == t_all
         return
     q = oracle.dequantize(codes[rows], scales[rows], fmt)
-    assert np.array_equal(S.row_update(w[rows], q, beta).astype(np.float32), r[rows])
+    n_r = check_scales(r[rows], S.row_update(w[rows], q, beta).astype(np.float32),
+                       minimizers(w[rows], q, beta, fmt, 1), fmt, "full-size rows")
     q_all = oracle.dequantize(codes, scales, fmt)
-    assert np.array_equal(S.col_update(w, q_all, alpha).astype(np.float32), c)
+    n_c = check_scales(c, S.col_update(w, q_all, alpha).astype(np.float32),
+                       minimizers(w, q_all, alpha, fmt, 0), fmt, "full-size columns")
+    say(f"    scales at a projection midpoint: {n_r} rows, {n_c} columns")
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxint4", "nvfp4"])

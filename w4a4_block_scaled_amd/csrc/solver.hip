@@ -17,8 +17,15 @@
 // an amax pass over W~ precedes each NVFP4 quantization, and the last one
 // gives the returned t_w.
 //
-// Every projection is a discrete decision taken on fp64 sums, so the sums
-// follow one fixed order (which a CPU restatement can follow too):
+// The iterations stop early at a fixed point: after each iteration a small
+// kernel compares (alpha, beta) with the previous iteration's and, if
+// nothing changed, raises a flag on which the remaining passes return at
+// once (every later iteration would repeat the same one exactly).
+//
+// Every projection is a discrete decision taken on fp64 sums, taken here in
+// one fixed order (so results are deterministic; a correctly rounded sum
+// differs from it only in the last bits, which changes a projection only
+// when the minimizer lies within that distance of a projection midpoint):
 //   rows:    a lane sums its 8 consecutive terms in order; the 4 lanes of a
 //            32-block combine as ((p0 + p1) + p2) + p3; the row-finalize
 //            thread adds the block sums in order;
@@ -104,7 +111,8 @@ __global__ __launch_bounds__(kThreads) void dq_pass_kernel(
     const float* __restrict__ tsc, int64_t N, int64_t K8, double* __restrict__ row_a,
     double* __restrict__ row_b,
     double* __restrict__ col_a, double* __restrict__ col_b, uint32_t* __restrict__ codes,
-    uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ scales, const int* __restrict__ done) {
+  if ((MODE == kRows || MODE == kCols) && *done) return;  // at a fixed point: nothing changes
   const int64_t col_raw = int64_t(blockIdx.y) * kThreads + threadIdx.x;
   const bool live_c = col_raw < K8;
   const int64_t col8 = live_c ? col_raw : K8 - 1;  // every lane joins the quad exchanges
@@ -223,7 +231,8 @@ constexpr int kAmaxBlocks = 1024;
 
 __global__ __launch_bounds__(kThreads) void dq_amax_kernel(
     const float* __restrict__ W, const float* __restrict__ alpha, const float* __restrict__ beta,
-    int64_t N, int64_t K8, float* __restrict__ part) {
+    int64_t N, int64_t K8, float* __restrict__ part, const int* __restrict__ done) {
+  if (done && *done) return;
   float m = 0.0f;
   const int64_t n = N * K8;
   for (int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x; g < n;
@@ -253,7 +262,9 @@ __global__ __launch_bounds__(kThreads) void dq_amax_kernel(
 
 __global__ __launch_bounds__(kThreads) void dq_tscale_kernel(const float* __restrict__ part, int n,
                                                              float* __restrict__ t_out,
-                                                             float* __restrict__ t_copy) {
+                                                             float* __restrict__ t_copy,
+                                                             const int* __restrict__ done) {
+  if (done && *done) return;
   float m = 0.0f;
   for (int i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, part[i]);
 #pragma unroll
@@ -296,10 +307,14 @@ __device__ __forceinline__ double ordered_sum(const double* __restrict__ p, int6
 template <int FMT, bool INIT>
 __global__ __launch_bounds__(kThreads) void dq_row_finalize_kernel(
     const double* __restrict__ row_a, const double* __restrict__ row_b, int64_t N, int64_t KB,
-    float* __restrict__ r, float* __restrict__ alpha) {
+    float* __restrict__ r, float* __restrict__ alpha, float* __restrict__ alpha_prev,
+    int* __restrict__ done) {
   const int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (INIT && i == 0) *done = 0;
+  if (!INIT && *done) return;
   if (i >= N) return;
   if (INIT) {
+    alpha_prev[i] = __builtin_nanf("");  // never equal: the first iteration always runs
     double m = 0.0;
     for (int64_t b = 0; b < KB; ++b) m = fmax(m, row_a[b * N + i]);
     alpha[i] = m > 0.0 ? float(1.0 / m) : 1.0f;
@@ -316,9 +331,12 @@ __global__ __launch_bounds__(kThreads) void dq_row_finalize_kernel(
 template <int FMT, bool INIT>
 __global__ __launch_bounds__(kThreads) void dq_col_finalize_kernel(
     const double* __restrict__ col_a, const double* __restrict__ col_b, int64_t chunks, int64_t K,
-    float* __restrict__ c, float* __restrict__ beta) {
+    float* __restrict__ c, float* __restrict__ beta, float* __restrict__ beta_prev,
+    const int* __restrict__ done) {
   const int64_t j = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  if (!INIT && *done) return;
   if (j >= K) return;
+  if (INIT) beta_prev[j] = __builtin_nanf("");
   const double num = ordered_sum(col_a + j, chunks, K);
   const double den = INIT ? 0.0 : ordered_sum(col_b + j, chunks, K);
   if (INIT) {
@@ -330,9 +348,38 @@ __global__ __launch_bounds__(kThreads) void dq_col_finalize_kernel(
   beta[j] = float(1.0 / cj);
 }
 
+// After an iteration: if neither alpha nor beta changed, (alpha, beta) is a
+// fixed point and every later iteration would repeat it exactly, so `done`
+// is raised and the remaining passes return at once.  One workgroup; it also
+// keeps this iteration's scales for the next comparison.
+__global__ __launch_bounds__(1024) void dq_fixed_point_kernel(const float* __restrict__ alpha,
+                                                               const float* __restrict__ beta,
+                                                               float* __restrict__ alpha_prev,
+                                                               float* __restrict__ beta_prev,
+                                                               int64_t N, int64_t K,
+                                                               int* __restrict__ done) {
+  if (*done) return;
+  int changed = 0;
+  for (int64_t i = threadIdx.x; i < N; i += 1024) {
+    const float a = alpha[i];
+    changed |= __float_as_uint(a) != __float_as_uint(alpha_prev[i]);
+    alpha_prev[i] = a;
+  }
+  for (int64_t j = threadIdx.x; j < K; j += 1024) {
+    const float b = beta[j];
+    changed |= __float_as_uint(b) != __float_as_uint(beta_prev[j]);
+    beta_prev[j] = b;
+  }
+  changed = __syncthreads_or(changed);
+  if (threadIdx.x == 0 && !changed) *done = 1;
+}
+
 struct SolverWs {
   float* alpha;
   float* beta;
+  float* alpha_prev;
+  float* beta_prev;
+  int* done;
   float* amax;  // kAmaxBlocks partial maxima (NVFP4)
   float* t;     // tensor scale of the current W~ (NVFP4)
   double *row_a, *row_b, *col_a, *col_b;
@@ -354,9 +401,14 @@ SolverWs carve(void* ws, int64_t N, int64_t K) {
   p += align256(N * 4);
   s.beta = reinterpret_cast<float*>(p);
   p += align256(K * 4);
+  s.alpha_prev = reinterpret_cast<float*>(p);
+  p += align256(N * 4);
+  s.beta_prev = reinterpret_cast<float*>(p);
+  p += align256(K * 4);
   s.amax = reinterpret_cast<float*>(p);
   p += align256(kAmaxBlocks * 4);
   s.t = reinterpret_cast<float*>(p);
+  s.done = reinterpret_cast<int*>(p + 64);
   return s;
 }
 
@@ -367,19 +419,21 @@ void pass(const float* W, const SolverWs& s, int64_t N, int64_t K, uint32_t* cod
   const int64_t K8 = K / 8;
   const dim3 grid(unsigned((N + ROWS - 1) / ROWS), unsigned((K8 + kThreads - 1) / kThreads));
   hipLaunchKernelGGL((dq_pass_kernel<FMT, MODE, DIV, ROWS>), grid, dim3(kThreads), 0, stream, W, s.alpha,
-                     s.beta, s.t, N, K8, s.row_a, s.row_b, s.col_a, s.col_b, codes, scales);
+                     s.beta, s.t, N, K8, s.row_a, s.row_b, s.col_a, s.col_b, codes, scales, s.done);
 }
 
 // NVFP4: the tensor scale of W~ at the current scales (into s.t, and into
-// t_copy when given)
+// t_copy when given); inside the iterations it is skipped at a fixed point,
+// the final one (t_copy) always runs
 void tensor_scale(const float* W, const SolverWs& s, int64_t N, int64_t K, float* t_copy,
                   hipStream_t stream) {
   const int64_t n = N * (K / 8);
   const int blocks = int(n / kThreads + 1 < kAmaxBlocks ? n / kThreads + 1 : kAmaxBlocks);
+  const int* done = t_copy ? nullptr : s.done;
   hipLaunchKernelGGL(dq_amax_kernel, dim3(blocks), dim3(kThreads), 0, stream, W, s.alpha, s.beta, N,
-                     K / 8, s.amax);
+                     K / 8, s.amax, done);
   hipLaunchKernelGGL(dq_tscale_kernel, dim3(1), dim3(kThreads), 0, stream, s.amax, blocks, s.t,
-                     t_copy);
+                     t_copy, done);
 }
 
 template <int FMT>
@@ -393,9 +447,9 @@ hipError_t solve(int64_t N, int64_t K, const float* W, int iters, float* r, floa
   uint8_t* sb = static_cast<uint8_t*>(scales);
   pass<FMT, kInit>(W, s, N, K, cw, sb, stream);
   hipLaunchKernelGGL((dq_row_finalize_kernel<FMT, true>), gr, dim3(kThreads), 0, stream, s.row_a,
-                     s.row_b, N, KB, r, s.alpha);
+                     s.row_b, N, KB, r, s.alpha, s.alpha_prev, s.done);
   hipLaunchKernelGGL((dq_col_finalize_kernel<FMT, true>), gc, dim3(kThreads), 0, stream, s.col_a,
-                     s.col_b, chunks, K, c, s.beta);
+                     s.col_b, chunks, K, c, s.beta, s.beta_prev, s.done);
   for (int t = 0; t < iters; ++t) {
     if (NV) tensor_scale(W, s, N, K, nullptr, stream);
     // beta_0 = 1 / l1 is not a power of two: the first row pass divides (and
@@ -405,11 +459,13 @@ hipError_t solve(int64_t N, int64_t K, const float* W, int iters, float* r, floa
     else
       pass<FMT, kRows>(W, s, N, K, cw, sb, stream);
     hipLaunchKernelGGL((dq_row_finalize_kernel<FMT, false>), gr, dim3(kThreads), 0, stream, s.row_a,
-                       s.row_b, N, KB, r, s.alpha);
+                       s.row_b, N, KB, r, s.alpha, s.alpha_prev, s.done);
     if (NV) tensor_scale(W, s, N, K, nullptr, stream);
     pass<FMT, kCols, NV>(W, s, N, K, cw, sb, stream);
     hipLaunchKernelGGL((dq_col_finalize_kernel<FMT, false>), gc, dim3(kThreads), 0, stream, s.col_a,
-                       s.col_b, chunks, K, c, s.beta);
+                       s.col_b, chunks, K, c, s.beta, s.beta_prev, s.done);
+    hipLaunchKernelGGL(dq_fixed_point_kernel, dim3(1), dim3(1024), 0, stream, s.alpha, s.beta,
+                       s.alpha_prev, s.beta_prev, N, K, s.done);
   }
   if (NV) tensor_scale(W, s, N, K, t_w, stream);
   pass<FMT, kEmit>(W, s, N, K, cw, sb, stream);
@@ -420,8 +476,8 @@ hipError_t solve(int64_t N, int64_t K, const float* W, int iters, float* r, floa
 
 size_t solver_workspace_bytes(int64_t N, int64_t K) {
   const int64_t KB = K / 32, chunks = (N + kChunk - 1) / kChunk;
-  return size_t(2 * align256(N * KB * 8) + 2 * align256(chunks * K * 8) + align256(N * 4) +
-                align256(K * 4) + align256(kAmaxBlocks * 4) + 256);
+  return size_t(2 * align256(N * KB * 8) + 2 * align256(chunks * K * 8) + 2 * align256(N * 4) +
+                2 * align256(K * 4) + align256(kAmaxBlocks * 4) + 256);
 }
 
 hipError_t launch_dualquant_solve(int fmt, int64_t N, int64_t K, const float* W, int iters,
