@@ -15,14 +15,18 @@ durations.
 Printed: one JSON line with the workload's throughput (TFLOP/s, whole step),
 the GEMM kernel's roofline position (algorithmic flops per launch over its
 HIP-event-timed average duration, against the MI355X dense MXFP4 peak),
-decode weight-streaming bandwidth (MXFP4 Llama linears at M = 1, 4, 16,
-MXINT4 Qwen linears and NVFP4 Llama linears at M = 1, cycling 32 layer
-copies so that the 256 MB last-level cache cannot hold the weights), the
-offline dual-scale solver on fp32 weights of the Llama linears' shapes, the
-q, k, v projections with their own column scales (one multi-output quantize
-and one grouped GEMM against three separate pairs), and the CPU oracle timed
-on a
-bounded sample of the same workload.
+decode weight-streaming bandwidth and linear-layer tokens/s with the
+activation quantization included (MXFP4 Llama linears at M = 1, 4, 16;
+MXINT4 Qwen, NVFP4, MXFP8, MXINT8 and INT4 G=64 Llama linears at M = 1;
+32 layer copies cycled so that the 256 MB last-level cache cannot hold the
+weights), the other formats' prefill configurations (NVFP4 Llama at
+M = 4096, MXINT4 Qwen at M = 512 and 4096, MXFP8, MXINT8 and INT4 G=64 Llama
+at M = 2048), each against the peak of the MFMA it runs on, the offline
+dual-scale solver on fp32 weights of the Llama linears' shapes, the q, k, v
+projections with their own column scales (one multi-output quantize and one
+grouped GEMM against three separate pairs), and the CPU oracle timed on a
+bounded sample of the same workload (activation quantization and linear
+apart, with the host's core count and CPU model).
 """
 from __future__ import annotations
 
@@ -47,10 +51,13 @@ PEAK = {  # MI355X published dense peaks
     "mxint4": (5.0e15, "TFLOP/s", "mfma"),   # runs on the FP8 scaled MFMA
     "nvfp4": (2.5e15, "TFLOP/s", "mfma"),    # runs on the fp16 MFMA
     "int4g64": (5.0e15, "TOP/s", "mfma"),    # int8 MFMA (5.0 POP/s dense)
+    "mxfp8": (2.5e15, "TFLOP/s", "mfma"),    # exact bf16 expansion on the bf16 MFMA
+    "mxint8": (5.0e15, "TOP/s", "mfma"),     # FP8 scaled MFMA, four per int8 product
 }
 HBM_PEAK = 8.0e12
 DTYPE = {"mxfp4": "fp4", "nvfp4": "fp4xe4m3->fp16", "mxint4": "int4->fp8",
-         "int4g64": "int4->int8 (bf16 block scales)"}
+         "int4g64": "int4->int8 (bf16 block scales)", "mxfp8": "fp8->bf16", "mxint8": "int8->2xfp8"}
+CODE_BYTES = {"mxfp8": 1.0, "mxint8": 1.0}   # bytes per code (0.5 for the 4-bit formats)
 SCALE_BYTES = {"int4g64": 2}   # bytes per block scale (1 for E8M0 / UE4M3)
 
 
@@ -77,7 +84,7 @@ class Layer:
         self.x = case.x.to(dev)
         self.c = torch.from_numpy(case.c).to(dev)
         G = w4.block_size(case.fmt)
-        self.codes = torch.empty((self.M, self.K // 2), dtype=torch.uint8, device=dev)
+        self.codes = torch.empty((self.M, w4.code_cols(case.fmt, self.K)), dtype=torch.uint8, device=dev)
         self.scales = torch.empty((self.M, self.K // G), dtype=w4.scale_dtype(case.fmt), device=dev)
         self.t = torch.ones(1, dtype=torch.float32, device=dev)
         self.ws = torch.empty(max(16, w4.lib().w4a4_quantize_workspace_bytes(
@@ -100,13 +107,20 @@ class Layer:
     def quant_bytes(self):
         """quantize_act algorithmic bytes: X in, c in, codes and scales out."""
         G = w4.block_size(self.fmt) / SCALE_BYTES.get(self.fmt, 1)
-        return 2 * self.M * self.K + 4 * self.K + self.M * self.K / 2 + self.M * self.K / G
+        cb = CODE_BYTES.get(self.fmt, 0.5)
+        return 2 * self.M * self.K + 4 * self.K + cb * self.M * self.K + self.M * self.K / G
 
     @property
     def gemm_bytes(self):
-        G = w4.block_size(self.fmt) / SCALE_BYTES.get(self.fmt, 1)
-        return (self.N * self.K / 2 + self.N * self.K / G + 4 * self.N + self.M * self.K / 2 +
-                self.M * self.K / G + 2 * self.M * self.N)
+        return gemm_bytes(self.fmt, self.M, self.N, self.K)
+
+
+def gemm_bytes(fmt, M, N, K):
+    """GEMM algorithmic bytes: weight codes, scales and r, activation codes and
+    scales, BF16 output."""
+    G = w4.block_size(fmt) / SCALE_BYTES.get(fmt, 1)
+    cb = CODE_BYTES.get(fmt, 0.5)
+    return cb * N * K + N * K / G + 4 * N + cb * M * K + M * K / G + 2 * M * N
 
 
 def time_steps(layers, steps, warmup, with_events=True):
@@ -243,9 +257,8 @@ def solver_rate(dev, iters=15):
     """The offline dual-scale solver (w4a4_dualquant_solve, MXFP4) on fp32
     weights of each Llama linear's shape: synthetic N(0, 0.02) weights with
     1/64 of the columns scaled x20 and lognormal column and row scales.  One
-    warm-up solve, then one timed solve per linear.  Every pass reads W once
-    (fp32), 2T + 2 passes per solve; the rate is those reads over the time
-    (the passes are HBM-bound), against 8 TB/s."""
+    warm-up solve, then one timed solve per linear (T = 15; the solve stops
+    at a fixed point of the scales, so fewer passes may run)."""
     g = torch.Generator(device="cpu").manual_seed(7)
     out = {}
     total = 0.0
@@ -265,50 +278,53 @@ def solver_rate(dev, iters=15):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
         total += ms
-        rate = (2 * iters + 2) * 4.0 * N * K / (ms * 1e-3) / 1e9
-        out[name] = {"N": N, "K": K, "ms": round(ms, 3), "W_read_GB/s": round(rate, 1),
-                     "frac_of_8TBps": round(rate / 8000.0, 3)}
+        out[name] = {"N": N, "K": K, "ms": round(ms, 3),
+                     "W_bytes_per_pass_over_ms_GB/s": round(4.0 * N * K / (ms * 1e-3) / 1e9, 1)}
         del w, ws
         torch.cuda.empty_cache()
     return {"format": "mxfp4", "iters": iters, "layer_ms": round(total, 3), "per_linear": out}
 
 
-def int4g64_rates(dev, steps, warmup, M=2048):
-    """INT4 G=64 with BF16 block scales (the pages' packed deployment format)
-    on the Llama linears: prefill at M tokens (quantize_act + linear per
-    linear, graph-timed step; GEMM rates from per-launch events, against the
-    int8 MFMA peak) and the decode weight-streaming rate at M = 1."""
-    layers = [Layer(c, dev) for c in inputs.workload_cases("llama_int4g64", M=M)]
+def prefill_rates(dev, workload, M, steps, warmup):
+    """Prefill at M tokens for the linears of `workload` (quantize_act + linear
+    per linear): the graph-timed step, and the GEMM rate from per-launch HIP
+    events against the peak of the MFMA the format runs on."""
+    fmt = inputs.WORKLOADS[workload][1]
+    layers = [Layer(c, dev) for c in inputs.workload_cases(workload, M=M)]
     torch.cuda.synchronize()
     _, gemm_ms, quant_ms = time_steps(layers, steps, warmup)
     ms = time_graph(layers, steps, warmup)
-    peak = PEAK["int4g64"][0]
+    peak, unit, bound = PEAK[fmt]
     ops = sum(L.flops for L in layers)
-    out = {"prefill_M%d" % M: {
-        "step_ms": round(ms, 4), "TOP/s_step": round(ops / (ms * 1e-3) / 1e12, 1),
-        "TOP/s_gemm": round(ops / (sum(gemm_ms) * 1e-3) / 1e12, 1),
-        "frac_of_int8_peak": round(ops / (sum(gemm_ms) * 1e-3) / peak, 4),
-        "traffic": traffic_record(f"gemm_llama_int4g64_M{M}", "int4g64"),
-        "kernel": gemm_kernel_label("int4g64", M),
-        "per_linear": {L.case.name: {"gemm_us": round(t * 1e3, 2),
-                                     "TOP/s": round(L.flops / (t * 1e-3) / 1e12, 1),
-                                     "quantize_us": round(qt * 1e3, 2)}
-                       for L, t, qt in zip(layers, gemm_ms, quant_ms)}}}
+    achieved = ops / (sum(gemm_ms) * 1e-3)
+    out = {"format": fmt, "M": M, "dtype": DTYPE[fmt],
+           "step_ms": round(ms, 4), "tokens_per_s": round(M / (ms * 1e-3), 1),
+           unit + "_step": round(ops / (ms * 1e-3) / 1e12, 1),
+           "roofline": {"bound": bound, "achieved": round(achieved / 1e12, 1), "peak": peak / 1e12,
+                        "unit": unit, "frac": round(achieved / peak, 4),
+                        "traffic": traffic_record(f"gemm_{workload}_M{M}", fmt),
+                        "kernel": gemm_kernel_label(fmt, M)},
+           "per_linear": {L.case.name: {"gemm_us": round(t * 1e3, 2),
+                                        unit: round(L.flops / (t * 1e-3) / 1e12, 1),
+                                        "frac": round(L.flops / (t * 1e-3) / peak, 4),
+                                        "quantize_us": round(qt * 1e3, 2)}
+                          for L, t, qt in zip(layers, gemm_ms, quant_ms)}}
     del layers
     torch.cuda.empty_cache()
-    out["decode_hbm"] = decode_bandwidth(dev, steps, "llama_int4g64", (1,))
     return out
 
 
 def decode_bandwidth(dev, steps, workload="llama_decode", Ms=(1, 4, 16), copies=32):
-    """Weight-streaming rate of the GEMM at small M (default: MXFP4 Llama
-    shapes at M = 1, 4, 16).
+    """Decode at small M (default: MXFP4 Llama shapes at M = 1, 4, 16).
 
-    Each step runs the four linears of one "layer"; 32 distinct copies of the
-    packed weights (3.7 GB for Llama, like the 32 layers of the model) are
-    cycled so that no copy is still cached.  The 32 layers are captured as
-    one HIP graph and replayed, so the figure is the GPU's, not the host's
-    launch rate.
+    A "layer" is the workload's four linears; 32 distinct copies of the packed
+    weights (3.7 GB for the MXFP4 Llama linears, like the 32 layers of the
+    model) are cycled so that no copy is still cached in the 256 MB
+    last-level cache.  Two HIP graphs of the 32 layers are replayed: the
+    GEMMs alone (the weight-streaming rate: algorithmic GEMM bytes over their
+    time, against 8 TB/s) and quantize_act + GEMM per linear (tokens/s =
+    M / time per layer of the four linears with their quantizations; linear
+    layers only, not a whole transformer block).
     """
     out = {}
     fmt = inputs.WORKLOADS[workload][1]
@@ -317,51 +333,77 @@ def decode_bandwidth(dev, steps, workload="llama_decode", Ms=(1, 4, 16), copies=
     for M in Ms:
         cases = inputs.workload_cases(workload, M=M, build_weights=False)
         act = [(c.x.to(dev), torch.from_numpy(c.c).to(dev)) for c in cases]
-        # quantized activations for this M
+        # quantized activations for this M (one buffer set per linear)
         q = [w4.quantize_act(x, c, fmt) for x, c in act]
+        qws = [torch.empty(max(16, w4.lib().w4a4_quantize_workspace_bytes(w4.FORMATS[fmt], M, L.K)),
+                           dtype=torch.uint8, device=dev) for L in base]
         ys = [torch.empty((M, L.N), dtype=torch.bfloat16, device=dev) for L in base]
-        G = w4.block_size(fmt) / SCALE_BYTES.get(fmt, 1)
-        nbytes = sum(L.N * L.K / 2 + L.N * L.K / G + 4 * L.N + M * L.K / 2 + M * L.K / G +
-                     2 * M * L.N for L in base)
+        nbytes = sum(gemm_bytes(fmt, M, L.N, L.K) for L in base)
 
-        def run_layer(k):
-            for j, L in enumerate(base):
-                w4.linear(q[j][0], q[j][1], q[j][2], blobs[k % copies][j], fmt, L.N, L.K, out=ys[j])
-
-        def run_model():
+        def run_model(with_quant):
             for k in range(copies):
-                run_layer(k)
+                for j, L in enumerate(base):
+                    if with_quant:
+                        w4.quantize_act(act[j][0], act[j][1], fmt, out=q[j], workspace=qws[j])
+                    w4.linear(q[j][0], q[j][1], q[j][2], blobs[k][j], fmt, L.N, L.K, out=ys[j])
 
-        g = capture(run_model)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(1, (steps + copies - 1) // copies)
-        e0.record()
-        for _ in range(reps):
+        res = {}
+        for with_quant in (False, True):
+            g = capture(lambda: run_model(with_quant))
             g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
-        del g
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(1, (steps + copies - 1) // copies)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res[with_quant] = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+            del g
+        us, us_q = res[False], res[True]
         out[str(M)] = {"us_per_4_linears": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
-                       "frac_of_8TBps": round(nbytes / (us * 1e-6) / HBM_PEAK, 3)}
+                       "frac_of_8TBps": round(nbytes / (us * 1e-6) / HBM_PEAK, 3),
+                       "us_per_4_linears_with_quantize": round(us_q, 2),
+                       "tokens_per_s_linears": round(M / (us_q * 1e-6), 1)}
     del blobs
+    torch.cuda.empty_cache()
     return out
+
+
+def host_cpu():
+    """(cores this process may run on, CPU model string)."""
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        ncpu = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return ncpu, model
 
 
 def cpu_baseline(workload, M, rows=512, cols=4096):
     """The oracle as it stands, on a bounded sample: `rows` activation rows and
-    `cols` weight rows of each linear (quantization of both plus the fp64
-    linear).  Reported in the workload's unit (TFLOP/s of the sampled GEMM)."""
+    `cols` weight rows of each linear.  Timed separately: the activation
+    quantization (rescale, block scales, codes) and the linear (the weights'
+    quantization plus the fp64 product with one BF16 rounding).  Reported in
+    the workload's unit (TFLOP/s of the sampled GEMMs over both parts)."""
     import oracle
-    from oracle.quant import quantize_rows, rescale, nv_tensor_scale, pack_nibbles
+    from oracle.quant import quantize_rows, rescale, nv_tensor_scale, pack_codes
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        threads = 1
-    flops, secs = 0.0, 0.0
+        blas_threads = 1
+    ncpu, model = host_cpu()
+    flops, t_quant, t_lin = 0.0, 0.0, 0.0
     for case in inputs.workload_cases(workload, M=M):
         rr = np.arange(min(rows, case.M))
         cc = np.arange(min(cols, case.N))
@@ -370,19 +412,28 @@ def cpu_baseline(workload, M, rows=512, cols=4096):
         xt = rescale(x, case.c)
         ta = nv_tensor_scale(xt) if case.fmt == "nvfp4" else None
         ac, as_, _ = quantize_rows(xt, case.fmt, t=ta)
+        ac = pack_codes(ac, case.fmt)
+        t1 = time.perf_counter()
         if case.w_codes is not None:
             wc, ws, tw = case.w_codes[cc], case.w_scales[cc], case.t_w
         else:
             w = case.w_prescaled[cc].float().numpy()
             tw = nv_tensor_scale(w) if case.fmt == "nvfp4" else 1.0
             wq, ws, _ = quantize_rows(w, case.fmt, t=tw if case.fmt == "nvfp4" else None)
-            wc = pack_nibbles(wq)
-        oracle.linear_bf16(pack_nibbles(ac), as_, ta, wc, ws, tw, case.r[cc], case.fmt)
-        secs += time.perf_counter() - t0
+            wc = pack_codes(wq, case.fmt)
+        oracle.linear_bf16(ac, as_, ta, wc, ws, tw, case.r[cc], case.fmt)
+        t2 = time.perf_counter()
+        t_quant += t1 - t0
+        t_lin += t2 - t1
         flops += 2.0 * len(rr) * len(cc) * case.K
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    secs = t_quant + t_lin
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle", "nproc": ncpu, "cpu_model": model,
+            "quantize_act_s": round(t_quant, 3), "linear_s": round(t_lin, 3),
             "sample": f"{rows} activation rows x {cols} weight rows of each of the 4 linears "
-                      f"(quantize both + fp64 linear), {secs:.1f} s"}
+                      f"(activation quantization {t_quant:.1f} s, weight quantization + fp64 linear "
+                      f"{t_lin:.1f} s; the fp64 product on {blas_threads} BLAS threads, "
+                      f"the quantization on one)"}
 
 
 def gemm_kernel_label(fmt, M):
@@ -401,6 +452,9 @@ def gemm_kernel_label(fmt, M):
                 "coarser) and gemm_mx_kernel<mxint4> (256x128 tiles)")
     if fmt == "int4g64":
         return "gemm_int4g64_decode_kernel" if M <= 16 else "gemm_int4g64_tile_kernel<4, 4>"
+    if fmt in ("mxfp8", "mxint8"):
+        return (f"gemm_mx8_decode_kernel<{fmt}>" if M <= 16 else
+                f"gemm_mx8_tile_kernel<{fmt}, 256, 128, 2, 2, 3>")
     return "gemm_nv_decode_kernel" if M <= 16 else "gemm_tile_kernel<nvfp4>"
 
 
@@ -449,7 +503,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-solver", action="store_true")
-    ap.add_argument("--no-int4g64", action="store_true")
+    ap.add_argument("--no-formats", action="store_true",
+                    help="skip the other formats' prefill and decode figures")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB calibration copy and one pass of the kernels, print nothing")
     a = ap.parse_args()
@@ -502,20 +557,29 @@ def main():
     del layers
     torch.cuda.empty_cache()
     if not a.no_decode:
-        log("[bench] decode bandwidth")
+        log("[bench] decode: MXFP4 Llama linears at M = 1, 4, 16")
         out["decode_hbm"] = decode_bandwidth(dev, a.steps)
-        torch.cuda.empty_cache()
+        log("[bench] decode: MXINT4 Qwen, NVFP4 Llama at M = 1")
         out["decode_hbm_qwen_mxint4"] = decode_bandwidth(dev, a.steps, "qwen_mxint4", (1,))
-        torch.cuda.empty_cache()
         out["decode_hbm_llama_nvfp4"] = decode_bandwidth(dev, a.steps, "llama_nvfp4", (1,))
+    if not a.no_formats:
+        # the other formats' prefill configurations, each against the peak of
+        # the MFMA it runs on
+        steps = max(5, a.steps // 4)
+        out["prefill_formats"] = {}
+        for wl, Mp in (("llama_nvfp4", 4096), ("qwen_mxint4", 512), ("qwen_mxint4", 4096),
+                       ("llama_mxfp8", 2048), ("llama_mxint8", 2048), ("llama_int4g64", 2048)):
+            log(f"[bench] prefill {wl} M={Mp}")
+            out["prefill_formats"][f"{wl}_M{Mp}"] = prefill_rates(dev, wl, Mp, steps, min(a.warmup, 5))
+        if not a.no_decode:
+            for wl in ("llama_mxfp8", "llama_mxint8", "llama_int4g64"):
+                log(f"[bench] decode {wl} M=1")
+                out[f"decode_hbm_{wl}"] = decode_bandwidth(dev, a.steps, wl, (1,))
     if not a.no_solver:
         log("[bench] dual-scale solver")
         out["dualquant_solver"] = solver_rate(dev)
         log("[bench] per-projection c: q, k, v with their own column scales")
         out["per_projection"] = per_projection_rate(dev)
-    if not a.no_int4g64 and a.workload != "llama_int4g64":
-        log("[bench] INT4 G=64 with BF16 scales (Llama, prefill and decode)")
-        out["int4g64"] = int4g64_rates(dev, a.steps, a.warmup)
     if not a.no_cpu:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(a.workload, M)
