@@ -130,19 +130,29 @@ def test_workload_full_size(workload, M):
     """Every linear of the workload at its full size, in the launch
     configuration the benchmark times; the oracle computes sampled outputs
     (rows incl. the first and last, columns incl. a whole tile and the last
-    one) from its own quantization of the same seeded inputs."""
+    one) from its own quantization of the same seeded inputs.  The
+    activation codes of the sampled rows, and the weight codes, scales (and
+    t_w) of the sampled weight rows, must equal the oracle's bit for bit."""
     dev = device()
     rng = np.random.default_rng(M)
     for case in inputs.workload_cases(workload, M=M):
         say(f"[workload] {workload} {case.name} M={case.M} N={case.N} K={case.K}")
-        Y, blob, (ac, as_, ta), _ = gpu_layer(case, dev)
+        Y, blob, (ac, as_, ta), gpu_weights = gpu_layer(case, dev)
         rows = _sample(case.M, 12, rng)
         cols = np.unique(np.concatenate([np.arange(min(144, case.N)), _sample(case.N, 96, rng),
                                          np.arange(case.N - 16, case.N)]))
-        y, S, (oa, osc, ota), _ = oracle_layer(case, rows, cols)
+        y, S, (oa, osc, ota), (owc, ows, otw) = oracle_layer(case, rows, cols)
         # the GPU's activation codes of the sampled rows are the oracle's
         assert np.array_equal(ac.cpu().numpy()[rows], oa)
         assert np.array_equal(as_.cpu().numpy()[rows], osc)
+        if case.w_prescaled is not None:
+            # and so are the weight codes and scales the GPU quantizer made
+            # from the prescaled weights (sampled weight rows), and t_w
+            wc, ws, tw = gpu_weights
+            assert np.array_equal(wc.cpu().numpy()[cols], owc), "weight codes differ from the oracle"
+            assert np.array_equal(ws.cpu().numpy()[cols], ows), "weight scales differ from the oracle"
+            if case.fmt == "nvfp4":
+                assert float(tw.cpu().numpy()[0]) == float(otw)
         Yb = bf16_bits(Y)[np.ix_(rows, cols)]
         elem, row = check_linear(Yb, y, S, case.K, f"{workload}/{case.name}")
         say(f"    max elementwise rel err {elem:.2e}, max row rel-L2 {row:.2e}")
@@ -183,3 +193,22 @@ def test_linear_empty_batch(fmt):
     _, blob, (ac, as_, ta), _ = gpu_layer(case, dev)
     Y = w4.linear(ac[:0], as_[:0], ta, blob, fmt, case.N, case.K)
     assert Y.shape == (0, 32)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxint4", "mxfp8", "mxint8"])
+@pytest.mark.parametrize("M,N,K", [(3, 528, 640), (17, 272, 1152), (130, 400, 384)])
+def test_linear_writes_only_its_output(fmt, M, N, K):
+    """Y lives inside a larger buffer whose surroundings hold a sentinel: the
+    GEMM (decode and tiled kernels, ragged M and N) writes exactly M x N bf16
+    values and no byte around them."""
+    dev = device()
+    case = inputs.adhoc_case(fmt, M, N, K, seed=M + N + K + 3)
+    Y, blob, (ac, as_, ta), _ = gpu_layer(case, dev)
+    guard = 4096
+    buf = torch.full((guard + M * N * 2 + guard,), 0xA5, dtype=torch.uint8, device=dev)
+    out = buf[guard:guard + M * N * 2].view(torch.bfloat16).view(M, N)
+    w4.linear(ac, as_, ta, blob, fmt, N, K, out=out)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(b[:guard] == 0xA5) and np.all(b[guard + M * N * 2:] == 0xA5), "write outside Y"
+    assert torch.equal(out, Y)

@@ -157,3 +157,66 @@ def test_mxfp4_ties_at_many_scales():
         rows.append(blk * 2.0 ** k)
     x = torch.from_numpy(np.array(rows, np.float32)).to(torch.bfloat16)
     _compare(x, np.ones(32, np.float32), "mxfp4", "mxfp4 ties")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxint4", "mxfp8", "mxint8"])
+@pytest.mark.parametrize("M,K", [(1, 96), (17, 1024), (300, 4096)])
+def test_quantize_writes_only_its_outputs(fmt, M, K):
+    """codes and scales live inside larger buffers holding a sentinel: the
+    quantizer writes exactly their bytes (ragged M, K not a multiple of 256)."""
+    if K % oracle.BLOCK[fmt]:
+        pytest.skip("K not a multiple of the block")
+    dev = device()
+    case = inputs.adhoc_case(fmt, M, 16, K, seed=300 + M + K, weights="none")
+    ref_codes, ref_scales, ref_t = gpu_quantize(case.x, case.c, fmt, dev)
+    guard = 1024
+    nc, ns = ref_codes.numel(), ref_scales.numel()
+    cbuf = torch.full((guard + nc + guard,), 0xA5, dtype=torch.uint8, device=dev)
+    sbuf = torch.full((guard + ns + guard,), 0xA5, dtype=torch.uint8, device=dev)
+    codes = cbuf[guard:guard + nc].view(ref_codes.shape)
+    scales = sbuf[guard:guard + ns].view(ref_scales.shape)
+    t = torch.ones(1, dtype=torch.float32, device=dev)
+    w4.quantize_act(to_dev(case.x, dev), to_dev(case.c, dev), fmt, out=(codes, scales, t))
+    torch.cuda.synchronize()
+    for b, n in ((cbuf.cpu().numpy(), nc), (sbuf.cpu().numpy(), ns)):
+        assert np.all(b[:guard] == 0xA5) and np.all(b[guard + n:] == 0xA5), "write outside the outputs"
+    assert torch.equal(codes, ref_codes) and torch.equal(scales, ref_scales)
+
+
+def _midpoint_products(fmt, rng, n=64):
+    """(x bf16 values, c fp32) pairs whose exact product is off an
+    element-grid midpoint (E2M1 midpoints 0.25, 0.75, ..., 5, or integer + 0.5
+    for INT4, with the block scale at 2^0) but whose fp32 product rounds onto
+    it: the rescale's single fp32 rounding decides a tie.  c = fp32(t / x)
+    for a bf16 x and a midpoint t."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0] if fmt == "mxfp4" else
+                    [0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5])
+    trials = 4096
+    x = torch.from_numpy(np.exp(rng.normal(0, 0.7, trials)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    x = x * rng.choice([-1.0, 1.0], trials).astype(np.float32)
+    tgt = (mids[rng.integers(0, len(mids), trials)] * np.sign(x)).astype(np.float32)
+    c = (tgt / x).astype(np.float32)
+    hit = ((x * c).astype(np.float32) == tgt) & (x.astype(np.float64) * c.astype(np.float64) != tgt)
+    assert hit.sum() >= n
+    return x[hit][:n], c[hit][:n]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxint4"])
+def test_quantize_continuous_column_scales(fmt):
+    """c off the E8M0 grid (lognormal fp32 values): x~ = fp32(x * c) is a
+    rounded product, and codes must still equal the oracle's bit for bit,
+    including products that round onto an element-grid midpoint (ties)."""
+    rng = np.random.default_rng(17)
+    case = inputs.adhoc_case(fmt, 64, 16, 2048, seed=17, weights="none")
+    c = np.exp(rng.normal(0, 0.5, 2048)).astype(np.float32)
+    _compare(case.x, c, fmt, f"{fmt} continuous c")
+    xs, cs = _midpoint_products(fmt, rng)
+    K = 32 * len(xs)
+    x = np.zeros((1, K), np.float32)
+    cc = np.ones(K, np.float32)
+    for i, (xv, cv) in enumerate(zip(xs, cs)):
+        x[0, 32 * i] = xv
+        x[0, 32 * i + 1] = 6.0            # the block amax is 6 (or the tie itself, <= 6.5): scale 2^0
+        cc[32 * i] = cv
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    _compare(xb, cc, fmt, f"{fmt} midpoint ties")

@@ -11,7 +11,8 @@ Qwen-7B-class linears; formats MXFP4 / NVFP4 / MXINT4 from Section 3):
 
 * ``single``  : one MXFP4 linear, M=16, N=K=256.  Weight codes are drawn
   directly (uniform over all 16 nibbles) with E8M0 block exponents uniform
-  in {-6..1}; activations N(0,1) with 2 outlier channels x50.
+  in {-6..1}; activations N(0,1) with 2 outlier channels x50; r and c drawn
+  from lognormal(0, 0.5) as continuous fp32 values.
 * ``llama_decode`` / ``llama_prefill`` : MXFP4, M in {1,4,16} / 2048, the
   four Llama-3.1-8B linears (QKV 4096->6144, O 4096->4096, gate+up
   4096->28672, down 14336->4096).  Raw weights N(0, 0.02) are divided by
@@ -27,8 +28,8 @@ Qwen-7B-class linears; formats MXFP4 / NVFP4 / MXINT4 from Section 3):
   Weight codes drawn directly (uniform int4) with E8M0 exponents uniform in
   {-7..1}; activations N(0,1) with round(2K/256) outlier channels x50.
 
-Row and column scales r, c follow a lognormal(0, 0.5) law sampled on the
-admissible set of the format (Section 4.2: inverse scales live in E8M0 for
+Row and column scales r, c of the other workloads follow a lognormal(0, 0.5)
+law sampled on the admissible set of the format (Section 4.2: inverse scales live in E8M0 for
 MX formats, UE4M3 for NVFP4): for E8M0 the power-of-two exponent is a
 normal draw with standard deviation 0.5/ln 2 rounded to an integer; for
 UE4M3 the binade is the floor of that draw and the 3-bit mantissa is
@@ -125,6 +126,11 @@ def admissible_scales(rng: np.random.Generator, n: int, family: str) -> np.ndarr
     raise ValueError(family)
 
 
+def lognormal_scales(rng: np.random.Generator, n: int) -> np.ndarray:
+    """n draws of exp(N(0, 0.5^2)) as fp32 (not restricted to an admissible set)."""
+    return np.exp(rng.standard_normal(n) * 0.5).astype(np.float32)
+
+
 def scale_family(fmt: str) -> str:
     return {"nvfp4": "ue4m3", "int4g64": "bf16"}.get(fmt, "e8m0")
 
@@ -180,9 +186,16 @@ def make_case(workload: str, name: str, fmt: str, M: int, N: int, K: int,
     """Build one linear of a workload; the seed fixes every tensor."""
     rx, rc, rr, rw = _rngs(seed, 4)
     G = BLOCK[fmt]
-    family = scale_family(fmt)
-    c = admissible_scales(rc, K, family)
-    r = admissible_scales(rr, N, family)
+    if workload == "single":
+        # the single-linear configuration draws r and c from the lognormal law
+        # itself (continuous fp32 values), so the activation rescale is a
+        # rounded fp32 product
+        c = lognormal_scales(rc, K)
+        r = lognormal_scales(rr, N)
+    else:
+        family = scale_family(fmt)
+        c = admissible_scales(rc, K, family)
+        r = admissible_scales(rr, N, family)
     if workload == "llama_nvfp4":
         x = student_t_activations(rx, M, K)
     elif workload in ("llama_decode", "llama_prefill", "llama_int4g64", "llama_mxfp8", "llama_mxint8"):
