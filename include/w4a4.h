@@ -256,8 +256,11 @@ w4a4_status w4a4_unpack_weight(w4a4_format fmt, int64_t N, int64_t K,
  *            a workspace must not run concurrently (issue them in order on
  *            one stream).
  *
- * Requires M >= 0, N % 16 == 0, K % 128 == 0.  The blob's fmt, N and K are
- * trusted, not re-read from device memory.
+ * Requires M >= 0, N % 16 == 0, K % 128 == 0.  The blob's header (magic,
+ * format, N, K) is checked on the device by every GEMM kernel before it reads
+ * anything else of the blob: a blob packed for another format or shape gives
+ * Y = BF16 NaN everywhere (the status is W4A4_OK: the host does not read
+ * device memory), never a read past the blob.
  */
 w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K,
                         const void* a_codes, const void* a_scales,

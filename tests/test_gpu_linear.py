@@ -212,3 +212,60 @@ def test_linear_writes_only_its_output(fmt, M, N, K):
     b = buf.cpu().numpy()
     assert np.all(b[:guard] == 0xA5) and np.all(b[guard + M * N * 2:] == 0xA5), "write outside Y"
     assert torch.equal(out, Y)
+
+
+def _pack_into(buf, fmt, N, K, seed):
+    """Pack random codes for (fmt, N, K) into the front of `buf` (a buffer
+    larger than that blob) through the C ABI."""
+    import ctypes
+    dev = buf.device
+    rng = np.random.default_rng(seed)
+    cols = K if fmt in ("mxfp8", "mxint8") else K // 2
+    codes = to_dev(rng.integers(0, 112, (N, cols), dtype=np.uint8), dev)
+    scales = to_dev(np.full((N, K // oracle.BLOCK[fmt]), 120, np.uint8), dev)
+    r = torch.ones(N, dtype=torch.float32, device=dev)
+    L = w4.lib()
+    st = L.w4a4_pack_weight(w4.FORMATS[fmt], N, K, ctypes.c_void_p(codes.data_ptr()),
+                            ctypes.c_void_p(scales.data_ptr()), None, ctypes.c_void_p(r.data_ptr()),
+                            ctypes.c_void_p(buf.data_ptr()),
+                            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+
+
+# (format the blob is packed for, its N, K) -> (format, M, N, K of the call):
+# other shape or other format; the calls reach the decode, tiled,
+# persistent and split-K kernels
+MISMATCH = [
+    (("mxfp4", 256, 512), ("mxfp4", 4, 512, 1024)),
+    (("mxfp4", 256, 512), ("mxfp4", 300, 256, 1024)),
+    (("mxfp4", 12288, 512), ("mxfp4", 1024, 12288, 1024)),
+    (("mxfp4", 8208, 4096), ("mxfp4", 300, 8208, 8192)),
+    (("mxfp4", 256, 512), ("mxint4", 40, 256, 512)),
+    (("mxint4", 256, 512), ("nvfp4", 3, 256, 512)),
+    (("nvfp4", 256, 512), ("mxfp8", 70, 256, 512)),
+    (("mxfp8", 256, 512), ("mxint8", 5, 256, 512)),
+    (("mxint4", 256, 512), ("int4g64", 33, 256, 512)),
+]
+
+
+@pytest.mark.parametrize("packed,call", MISMATCH)
+def test_blob_of_another_format_or_shape_gives_nan(packed, call):
+    """The GEMM kernels check the blob header (magic, format, N, K) against
+    their arguments before reading anything else of it: a blob packed for
+    another format or shape yields an all-NaN Y, not a read past the blob.
+    The blob sits at the front of a buffer as large as the call's own blob,
+    so no read could leave it even if the check were missing."""
+    dev = device()
+    pf, pN, pK = packed
+    fmt, M, N, K = call
+    say(f"[blob mismatch] packed {pf} {pN}x{pK}, called {fmt} M={M} N={N} K={K}")
+    size = max(w4.packed_weight_bytes(f, N, K) for f in ("mxfp8", fmt))
+    buf = torch.zeros(size + 256, dtype=torch.uint8, device=dev)
+    _pack_into(buf, pf, pN, pK, seed=M + N)
+    x = torch.randn((M, K)).to(torch.bfloat16).to(dev)
+    ac, as_, ta = w4.quantize_act(x, None, fmt)
+    Y = torch.zeros((M, N), dtype=torch.bfloat16, device=dev)
+    w4.linear(ac, as_, ta, buf, fmt, N, K, out=Y)
+    torch.cuda.synchronize()
+    assert torch.isnan(Y.float()).all(), "a mismatched blob did not give NaN"

@@ -56,7 +56,8 @@ struct BlobHeader {
   uint32_t version;   // 1
   uint32_t format;
   int64_t N, K;
-  uint32_t layout;    // 1: 16-row x 128-K tiles, 2: 32-row x 64-K tiles, 3: 8-bit 16 x 128
+  uint32_t layout;    // 1: 16-row x 128-K tiles, 2: 32-row x 64-K tiles, 3: 8-bit 16 x 128,
+                      // 4: INT4 G=64 512-byte tiles (int4g64.hip)
   float t_w;
   uint64_t code_off, scale_off, r_off, total;
   uint8_t pad[256 - 8 - 4 - 4 - 16 - 4 - 4 - 32];
@@ -109,6 +110,40 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
+}
+
+// The blob header must name the format and shape the GEMM is called with:
+// every GEMM kernel checks it before it reads anything else of the blob, and
+// on a mismatch writes Y as BF16 NaN instead of reading a blob laid out for
+// another shape (which could run past its end).
+constexpr uint64_t kBlobMagic = 0x31304B5034413457ull;  // "W4A4PK01", little-endian
+
+__device__ __forceinline__ bool blob_header_ok(const uint8_t* blob, int fmt, int64_t N, int64_t K) {
+  const BlobHeader* h = reinterpret_cast<const BlobHeader*>(blob);
+  return *reinterpret_cast<const uint64_t*>(h->magic) == kBlobMagic && h->format == uint32_t(fmt) &&
+         h->N == N && h->K == K;
+}
+
+// Y [M x N] bf16 (N % 16 == 0, 16-byte aligned) <- NaN, spread over the
+// whole grid (1-D or 2-D): every workgroup writes its share.
+__device__ inline void fill_y_nan(uint16_t* Y, int64_t M, int64_t N) {
+  const int64_t chunks = M * N / 8;
+  const int64_t step = int64_t(gridDim.x) * gridDim.y * blockDim.x;
+  const int64_t first = (int64_t(blockIdx.y) * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+  const uint4 nan = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+  for (int64_t i = first; i < chunks; i += step) reinterpret_cast<uint4*>(Y)[i] = nan;
+}
+
+// The rows m0 .. m0+rows-1 and columns n0 .. n0+cols-1 of Y (clipped to
+// M x N; n0 and cols multiples of 8) <- NaN, by the threads of one workgroup.
+__device__ inline void fill_tile_nan(uint16_t* Y, int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                     int rows, int cols) {
+  const uint4 nan = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+  const int per_row = cols / 8;
+  for (int i = threadIdx.x; i < rows * per_row; i += blockDim.x) {
+    const int64_t m = m0 + i / per_row, n = n0 + 8 * (i % per_row);
+    if (m < M && n < N) *reinterpret_cast<uint4*>(Y + m * N + n) = nan;
+  }
 }
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.

@@ -484,6 +484,10 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_tile_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ t_act, const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y,
     int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_total, int per_xcd) {
+  if (!blob_header_ok(blob, FMT, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   using C = TileCfg<FMT, BN, BM, WN, WM, DEPTH>;
   constexpr int FN = C::FN, FM = C::FM;
   // XCD-aware order: the hardware deals workgroups round-robin to the 8 XCDs;
@@ -756,6 +760,10 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int tiles_m, int tiles_total, int per_xcd) {
+  if (!blob_header_ok(blob, FMT, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   using C = MxCfg<BN, BM, WN, WM, DEPTH>;
   constexpr int FN = C::FN, FM = C::FM;
   const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
@@ -854,6 +862,10 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx_lean_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int tiles_m, int tiles_total, int per_xcd) {
+  if (!blob_header_ok(blob, FMT, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   using C = MxCfg<BN, BM, WN, WM, DEPTH>;
   constexpr int FN = C::FN, FM = C::FM;
   const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
@@ -1190,6 +1202,10 @@ __device__ __forceinline__ void fp4_tile(const uint8_t* __restrict__ a_codes,
                                          const uint8_t* __restrict__ blob,
                                          uint16_t* __restrict__ Y, int64_t M, int64_t N,
                                          int64_t K, int tm, int tn) {
+  if (!blob_header_ok(blob, MXFP4, N, K)) {
+    fill_tile_nan(Y, M, N, int64_t(tm) * BM, int64_t(tn) * BN, BM, BN);
+    return;
+  }
   using C = Fp4Cfg<BN, BM, DEPTH>;
   constexpr int FN = C::FN, FM = C::FM;
   const BlobLayout L = blob_layout(MXFP4, N, K);
@@ -1718,6 +1734,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int tiles_m, int tiles_total) {
+  if (!blob_header_ok(blob, MXFP4, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   using C = Fp4P::C;
   constexpr int FN = C::FN, FM = C::FM, DEPTH = Fp4P::DEPTH;
   const BlobLayout L = blob_layout(MXFP4, N, K);
@@ -1936,6 +1956,10 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_splitk_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int tiles_m, int T, uint8_t* __restrict__ ws) {
+  if (!blob_header_ok(blob, MXFP4, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   using C = Fp4P::C;
   constexpr int FN = C::FN, FM = C::FM, DEPTH = Fp4P::DEPTH;
   const BlobLayout L = blob_layout(MXFP4, N, K);
@@ -2099,6 +2123,10 @@ template <int WAVES, int U>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, MXFP4, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   const BlobLayout L = blob_layout(MXFP4, N, K);
   const u32x4* __restrict__ Wc = reinterpret_cast<const u32x4*>(blob + L.code_off);
   const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
@@ -2209,6 +2237,10 @@ template <int WAVES, int U>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode16_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, MXFP4, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   const BlobLayout L = blob_layout(MXFP4, N, K);
   const int64_t F = N / 16, per_x = (F + 7) / 8;
   const int64_t f = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8, g = f >> 1;
@@ -2313,6 +2345,10 @@ template <int FMT, int WAVES, int U>
 __global__ __launch_bounds__(64 * WAVES) void gemm_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, FMT, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   const BlobLayout L = blob_layout(FMT, N, K);
   const u32x4* __restrict__ Wc = reinterpret_cast<const u32x4*>(blob + L.code_off);
   const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
@@ -2431,6 +2467,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_nv_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ t_act, const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y,
     int64_t M, int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, NVFP4, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   const BlobLayout L = blob_layout(NVFP4, N, K);
   const u32x4* __restrict__ Wc = reinterpret_cast<const u32x4*>(blob + L.code_off);
   const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
@@ -2644,6 +2684,10 @@ template <int FMT, int WAVES, int U>
 __global__ __launch_bounds__(64 * WAVES) void gemm_mx8_decode_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, FMT, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   static_assert(FMT == MXFP8 || FMT == MXINT8, "8-bit MX formats");
   const BlobLayout L = blob_layout(FMT, N, K);
   const u32x4* __restrict__ Wc = reinterpret_cast<const u32x4*>(blob + L.code_off);
@@ -2900,6 +2944,10 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx8_tile_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int tiles_m, int tiles_total, int per_xcd) {
+  if (!blob_header_ok(blob, FMT, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   static_assert(FMT == MXFP8 || FMT == MXINT8, "8-bit MX formats");
   using C = Mx8Cfg<BN, BM, WN, WM, DEPTH>;
   constexpr int FN = C::FN, FM = C::FM;

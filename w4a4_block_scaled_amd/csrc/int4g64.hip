@@ -165,24 +165,25 @@ pack_int4g64_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restric
   }
 }
 
+// The header is written field by field into the blob (the GEMM kernels check
+// its magic, format, N and K before reading the blob).
 __global__ void pack_int4g64_header_kernel(int64_t N, int64_t K, uint8_t* blob) {
+  if (threadIdx.x != 0) return;
   const I4Layout L = i4_layout(N, K);
-  BlobHeader h = {};
+  BlobHeader* h = reinterpret_cast<BlobHeader*>(blob);
   const char m[8] = {'W', '4', 'A', '4', 'P', 'K', '0', '1'};
-  for (int i = 0; i < 8; ++i) h.magic[i] = m[i];
-  h.version = 1;
-  h.format = 3;
-  h.N = N;
-  h.K = K;
-  h.layout = 3;
-  h.t_w = 1.0f;
-  h.code_off = L.code_off;
-  h.scale_off = L.scale_off;
-  h.r_off = L.r_off;
-  h.total = L.total;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(&h);
-  uint32_t* dst = reinterpret_cast<uint32_t*>(blob);
-  if (threadIdx.x < 64) dst[threadIdx.x] = src[threadIdx.x];
+  for (int i = 0; i < 8; ++i) h->magic[i] = m[i];
+  h->version = 1;
+  h->format = 3;
+  h->N = N;
+  h->K = K;
+  h->layout = 4;
+  h->t_w = 1.0f;
+  h->code_off = uint64_t(L.code_off);
+  h->scale_off = uint64_t(L.scale_off);
+  h->r_off = uint64_t(L.r_off);
+  h->total = uint64_t(L.total);
+  for (int i = 0; i < int(sizeof(h->pad)); ++i) h->pad[i] = 0;
 }
 
 // -------------------------------------------------------------------- GEMM --
@@ -240,6 +241,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_int4g64_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
                          const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M,
                          int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, 3, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   const I4Layout L = i4_layout(N, K);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t m0 = int64_t(blockIdx.y) * (2 * FM * 16) + (wave >> 1) * (FM * 16);
@@ -345,6 +350,10 @@ __global__ void __launch_bounds__(64 * WAVES)
 gemm_int4g64_decode_kernel(const uint8_t* __restrict__ a_codes,
                            const uint16_t* __restrict__ a_scales, const uint8_t* __restrict__ blob,
                            uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, 3, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
   const I4Layout L = i4_layout(N, K);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t g = blockIdx.x;
@@ -423,7 +432,7 @@ hipError_t launch_quantize_int4g64(int64_t M, int64_t K, const void* X, const fl
 
 hipError_t launch_pack_int4g64(int64_t N, int64_t K, const void* codes, const void* scales,
                                const float* r, void* blob, hipStream_t stream) {
-  hipLaunchKernelGGL(pack_int4g64_header_kernel, dim3(1), dim3(64), 0, stream, N, K,
+  hipLaunchKernelGGL(pack_int4g64_header_kernel, dim3(1), dim3(1), 0, stream, N, K,
                      static_cast<uint8_t*>(blob));
   const int64_t work = N * K / 16;
   hipLaunchKernelGGL(pack_int4g64_kernel, dim3(grid_for(work)), dim3(256), 0, stream,
