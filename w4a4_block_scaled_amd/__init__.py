@@ -38,7 +38,9 @@ class W4A4Error(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libw4a4.so")
+    """The in-tree libw4a4.so, or the file W4A4_LIBRARY names (a variant build
+    of the same sources, e.g. the AddressSanitizer one)."""
+    return os.environ.get("W4A4_LIBRARY") or os.path.join(_HERE, "libw4a4.so")
 
 
 def lib() -> ctypes.CDLL:

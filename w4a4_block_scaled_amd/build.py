@@ -69,8 +69,53 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     return LIB
 
 
+ASAN_DIR = os.path.join(HERE, "_build_asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libw4a4.so")
+
+
+def asan_runtime() -> str:
+    """The compiler's AddressSanitizer runtime (to preload into an
+    uninstrumented host process such as python)."""
+    res = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return path
+
+
+def build_asan(jobs: int = 4, verbose: bool = False) -> str:
+    """A variant of the library whose host code (the C ABI layer and the
+    launchers) is built with AddressSanitizer; the device code is unchanged.
+    Written to _build_asan/libw4a4.so; used with the runtime preloaded and
+    W4A4_LIBRARY pointing at it."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    host_flags = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    objs = [os.path.join(ASAN_DIR, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
+
+    def comp(src, obj):
+        cmd = [hipcc(), *FLAGS, *host_flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        list(ex.map(comp, SOURCES, objs))
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan",
+           "-Xarch_host", "-fsanitize=address", *objs, "-o", ASAN_LIB]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
+    ap.add_argument("--asan", action="store_true", help="also build the AddressSanitizer host variant")
     a = ap.parse_args()
     build(a.jobs, verbose=True)
+    if a.asan:
+        build_asan(a.jobs, verbose=True)
