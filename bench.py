@@ -123,41 +123,53 @@ def gemm_bytes(fmt, M, N, K):
     return cb * N * K + N * K / G + 4 * N + cb * M * K + M * K / G + 2 * M * N
 
 
-def time_steps(layers, steps, warmup, with_events=True):
-    """Run warmup + timed steps; returns (ms per step, per-layer GEMM ms list,
-    per-layer quantize_act ms list), the per-layer figures from HIP events
-    recorded on the stream the kernels run on."""
+def time_steps(layers, steps, warmup):
+    """ms per step, launched eagerly from the host (quantize_act + linear for
+    every linear)."""
     for _ in range(warmup):
         for L in layers:
             L.quantize()
             L.gemm()
     torch.cuda.synchronize()
-    ev = [[tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in layers]
-          for _ in range(steps)] if with_events else None
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
-    for s in range(steps):
-        for i, L in enumerate(layers):
-            if with_events:
-                ev[s][i][0].record()
+    for _ in range(steps):
+        for L in layers:
             L.quantize()
-            if with_events:
-                ev[s][i][1].record()
             L.gemm()
-            if with_events:
-                ev[s][i][2].record()
     t1.record()
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    gemm_ms = quant_ms = None
-    if with_events:
-        gemm_ms = [float(np.mean([ev[s][i][1].elapsed_time(ev[s][i][2]) for s in range(steps)]))
-                   for i in range(len(layers))]
-        quant_ms = [float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]))
-                    for i in range(len(layers))]
-    return ms, gemm_ms, quant_ms
+    return t0.elapsed_time(t1) / steps
+
+
+def time_launches(fn, reps=10, bursts=5):
+    """Average duration (ms) of one launch of fn: a HIP graph of `reps`
+    back-to-back calls is replayed `bursts` times between two HIP events on
+    the stream the kernels run on (the graph's own stream ordering leaves no
+    host gaps, and an event pair around every launch would add its own)."""
+    def many():
+        for _ in range(reps):
+            fn()
+    g = capture(many)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(bursts):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / (reps * bursts)
+
+
+def per_launch(layers, steps):
+    """Per-layer average GEMM and quantize_act launch durations (ms)."""
+    bursts = max(2, steps // 10)
+    gemm_ms = [time_launches(L.gemm, bursts=bursts) for L in layers]
+    quant_ms = [time_launches(L.quantize, bursts=bursts) for L in layers]
+    return gemm_ms, quant_ms
 
 
 def capture(fn):
@@ -292,7 +304,7 @@ def prefill_rates(dev, workload, M, steps, warmup):
     fmt = inputs.WORKLOADS[workload][1]
     layers = [Layer(c, dev) for c in inputs.workload_cases(workload, M=M)]
     torch.cuda.synchronize()
-    _, gemm_ms, quant_ms = time_steps(layers, steps, warmup)
+    gemm_ms, quant_ms = per_launch(layers, steps)
     ms = time_graph(layers, steps, warmup)
     peak, unit, bound = PEAK[fmt]
     ops = sum(L.flops for L in layers)
@@ -523,10 +535,11 @@ def main():
         traffic_probe(layers, dev)
         return
     log("[bench] timing")
-    # per-launch durations from HIP events around each launch (eager), then
-    # the step time from graph replays
-    ms_eager, gemm_ms, quant_ms = time_steps(layers, a.steps, a.warmup)
+    # the step time from graph replays (and launched eagerly), then the
+    # per-launch durations from graphs of back-to-back launches
+    ms_eager = time_steps(layers, a.steps, a.warmup)
     ms = time_graph(layers, a.steps, a.warmup)
+    gemm_ms, quant_ms = per_launch(layers, a.steps)
     flops = sum(L.flops for L in layers)
     value = flops / (ms * 1e-3) / 1e12
     peak, unit, bound = PEAK[fmt]
