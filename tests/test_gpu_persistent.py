@@ -2,11 +2,13 @@
 
 MXFP4 shapes with at least 192 tiles of 256 x 256 and K a multiple of 512 run
 one workgroup per CU that walks its tiles as one stream of K-steps (the copy
-ring crosses tile boundaries).  Covered here, all outputs compared: several
-tiles per workgroup, tile counts that are not a multiple of the 8 XCDs,
-ragged M and N, one-quad tiles (K = 512: every tile's only quad also copies
-the next tile's first), bit-exactness where accumulation is exact, and
-repeated calls."""
+ring crosses tile boundaries); with 96..128 tiles and M >= 1024 the items
+are the tiles' n halves of 128 features (two per tile).  Covered here, all
+outputs compared: several tiles per workgroup, tile counts that are not a
+multiple of the 8 XCDs, ragged M and N, one-quad tiles (K = 512: every
+tile's only quad also copies the next tile's first), halves (one per
+workgroup, and fewer halves than workgroups, with ragged M and N and a half
+past N), bit-exactness where accumulation is exact, and repeated calls."""
 import numpy as np
 import pytest
 import torch
@@ -22,8 +24,16 @@ pytestmark = pytest.mark.gpu
 
 def persistent(M, N, K):
     """The host-side condition for the persistent kernel (MXFP4)."""
-    tiles = ((M + 255) // 256) * ((N + 255) // 256)
-    return M > 32 and K % 512 == 0 and tiles >= 192
+    return M > 32 and K % 512 == 0 and (tiles(M, N) >= 192 or halves(M, N, K))
+
+
+def tiles(M, N):
+    return ((M + 255) // 256) * ((N + 255) // 256)
+
+
+def halves(M, N, K):
+    """The persistent kernel runs n halves of 128 features as its items."""
+    return M > 32 and K % 512 == 0 and M >= 1024 and 96 <= tiles(M, N) <= 128
 
 
 # (M, N, K): what the tile walk does with it (256 workgroups, 32 per XCD)
@@ -32,7 +42,16 @@ PERSIST = [
     (300, 24592, 1024),    # 194 tiles (24 or 25 per XCD), ragged M and N
     (1100, 16400, 2048),   # 325 tiles, ragged M and N, 4 quads per tile
     (512, 49152, 512),     # 384 tiles of one quad each
+    (1024, 8192, 1024),    # 128 tiles: 256 halves, one per workgroup
+    (2000, 4000, 1024),    # 128 tiles: halves, ragged M and N (the last half past N)
+    (1100, 6000, 512),     # 120 tiles: 240 halves, ragged M and N, one quad each
 ]
+
+
+def test_shapes_take_the_intended_path():
+    assert not any(halves(*s) for s in PERSIST[:4])
+    assert all(halves(*s) for s in PERSIST[4:])
+    assert tiles(2048, 4096) == 128 and halves(2048, 4096, 4096)       # Llama o_proj, M = 2048
 
 
 @pytest.mark.parametrize("M,N,K", PERSIST)

@@ -1113,8 +1113,11 @@ __device__ __forceinline__ void fp4_fix_scales(int (&sa)[FM], int lane) {
 // LDS read number r of a wave's fragments of K-step kstep (stage buffer
 // `st`): activation scale dwords (raw, from the scale block; fp4_fix_scales
 // applies the lane's byte shift once the reads have landed), weight scale
-// words, activation fragments, weight fragments.
-template <int BN, int BM, int DEPTH, int NB = 3>
+// words, activation fragments, weight fragments.  FNE (<= FN) is the number
+// of 32-row weight groups the wave uses: a tile whose waves cover only the
+// first FNE groups each (the first 64 FNE of its BN rows) reads the same
+// stage layout.
+template <int BN, int BM, int DEPTH, int NB = 3, int FNE = BN / 64>
 __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st,
                                               const LDS uint8_t* __restrict__ base, int64_t kstep,
                                               int wn, int wm, int lane, Fp4Frags<BN / 64, BM / 64>& fr,
@@ -1126,11 +1129,11 @@ __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st
     fr.sa[j] = *reinterpret_cast<const LDS int*>(base + fp4_scale_offset<BN, BM, DEPTH, NB>(R, kstep));
   } else if (r < C::FM + 2) {
     const int hh = r - C::FM;
-    const int e = ((wn * C::FN / 4) * 2 + hh) * 64 + lane;
+    const int e = ((wn * FNE / 4) * 2 + hh) * 64 + lane;
     const uint32_t wsw = *reinterpret_cast<const LDS uint32_t*>(st + C::A_BYTES + C::W_BYTES +
                                                                 (e / C::WS_DW) * 256 + (e % C::WS_DW) * 4);
     // byte i of the shifted word is the scale of the wave's weight group i
-    fr.sw[hh] = int(C::FN == 4 ? wsw : wsw >> (8 * ((wn * C::FN) & 3)));
+    fr.sw[hh] = int(FNE == 4 ? wsw : wsw >> (8 * ((wn * FNE) & 3)));
   } else if (r < 3 * C::FM + 2) {
     const int q = r - C::FM - 2, j = q >> 1, hh = q & 1;
     // fragment lane l: row 32 g + l%32 (16-row tile 2 g + (l%32)/16, row
@@ -1139,19 +1142,19 @@ __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st
         st + (2 * (wm * C::FM + j) + ((lane >> 4) & 1)) * 1024 + a_tile_pos(lane & 15, 2 * hh + (lane >> 5)) * 16);
   } else {
     const int q = r - 3 * C::FM - 2, i = q >> 1, hh = q & 1;
-    fr.w[i][hh] = *reinterpret_cast<const LDS u32x4*>(st + C::A_BYTES + ((wn * C::FN + i) * 2 + hh) * 1024 +
+    fr.w[i][hh] = *reinterpret_cast<const LDS u32x4*>(st + C::A_BYTES + ((wn * FNE + i) * 2 + hh) * 1024 +
                                                       lane * 16);
   }
 }
 
-template <int BN, int BM, int DEPTH, int NB = 3>
+template <int BN, int BM, int DEPTH, int NB = 3, int FNE = BN / 64>
 __device__ __forceinline__ void fp4_read_all(const LDS uint8_t* __restrict__ st,
                                              const LDS uint8_t* __restrict__ base, int64_t kstep,
                                              int wn, int wm, int lane, Fp4Frags<BN / 64, BM / 64>& fr) {
   using C = Fp4Cfg<BN, BM, DEPTH>;
 #pragma unroll
-  for (int r = 0; r < 3 * C::FM + 2 + 2 * C::FN; ++r)
-    fp4_read_item<BN, BM, DEPTH, NB>(st, base, kstep, wn, wm, lane, fr, r);
+  for (int r = 0; r < 3 * C::FM + 2 + 2 * FNE; ++r)
+    fp4_read_item<BN, BM, DEPTH, NB, FNE>(st, base, kstep, wn, wm, lane, fr, r);
   fp4_fix_scales<C::FM>(fr.sa, lane);
 }
 
@@ -1367,7 +1370,12 @@ hipError_t launch_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
 // workgroup per CU.  Tiles go to the 8 XCDs in contiguous chunks, each chunk
 // in the tile order of gemm_fp4_kernel (m fastest); within an XCD the 32
 // workgroups take its tiles round-robin, so each round of 32 concurrent
-// tiles shares activation rows and weight groups in that XCD's L2.
+// tiles shares activation rows and weight groups in that XCD's L2.  With
+// 96..128 tiles (fewer than the CUs), the items are the tiles' n halves of
+// 128 output features instead, two per tile: a half runs the same copy
+// stream as a whole tile (its weight copies for rows 128..255 read from an
+// empty buffer range, which moves nothing), so every wait count holds, and
+// half of the MFMAs.
 //
 // The tiles of a workgroup form one stream of K-steps, and the DEPTH-deep
 // copy ring runs over that stream: the next tile's first K-steps are in
@@ -1402,9 +1410,9 @@ static_assert(Fp4P::younger(1) + Fp4P::ITEM_OPS < 64 && Fp4P::younger(2) + Fp4P:
                   Fp4P::copies(1) + Fp4P::copies(2) + Fp4P::copies(3) + Fp4P::EPI_STORES < 64,
               "vmcnt range");
 
-// The tiles of workgroup b: its XCD x = b % 8 and index i = b / 8 within it
-// (workgroups are dealt to the XCDs round-robin) give tiles tb + i + 32 k of
-// the XCD's chunk [tb, te).
+// The items of workgroup b: its XCD x = b % 8 and index i = b / 8 within it
+// (workgroups are dealt to the XCDs round-robin) give items tb + i + 32 k of
+// the XCD's chunk [tb, te) of the launch's items (tiles, or n halves).
 struct Fp4PSched {
   int tiles_m, KS, tb, i, n_items;
 
@@ -1420,20 +1428,24 @@ struct Fp4PSched {
   __device__ __forceinline__ int tile(int k) const { return tb + i + Fp4P::PER_XCD * k; }
 };
 
-// Where item k (the k-th tile) of the stream reads: its tile origin and
-// K-steps [ks0, ks0 + len).  Past the last tile it repeats the last tile's
-// last quad, so copies beyond the end of the stream read valid sources.
+// Where item k of the stream reads: its tile origin and K-steps [ks0, ks0 +
+// len).  Past the last item it repeats the last item's last quad, so copies
+// beyond the end of the stream read valid sources.  With HALF, item h is n
+// half h % 2 of tile h / 2 (consecutive workgroups of an XCD take the two
+// halves of a tile, which share its activation rows).
 struct Fp4PDesc {
   int m0, g0;  // first activation row, first 32-row weight group
   int ks0, len;
 };
 
+template <bool HALF>
 __device__ __forceinline__ Fp4PDesc fp4p_desc(const Fp4PSched& S, int k) {
   const bool over = k >= S.n_items;
-  const int t = S.tile(over ? S.n_items - 1 : k);
+  const int it = S.tile(over ? S.n_items - 1 : k);
+  const int t = HALF ? it / 2 : it;
   Fp4PDesc d;
   d.m0 = (t % S.tiles_m) * Fp4P::BM;
-  d.g0 = (t / S.tiles_m) * (Fp4P::BN / 32);
+  d.g0 = (t / S.tiles_m) * (Fp4P::BN / 32) + (HALF ? 4 * (it & 1) : 0);
   d.ks0 = over ? S.KS - 4 : 0;
   d.len = over ? 4 : S.KS;
   return d;
@@ -1497,7 +1509,7 @@ struct Fp4PQuad {
 
 // Copy number k of a wave's share of K-step j of quad q (activation tiles,
 // weight tiles, weight scale words, then with j = 0 the scale quarters).
-template <int J>
+template <int J, bool HALF>
 __device__ __forceinline__ void fp4p_copy(const Fp4PSrc& b, const Fp4PQuad& q, const Fp4PLane& o,
                                           LDS uint8_t* smem, LDS uint8_t* dst, int wave, int k) {
   using C = Fp4P::C;
@@ -1506,7 +1518,9 @@ __device__ __forceinline__ void fp4p_copy(const Fp4PSrc& b, const Fp4PQuad& q, c
     llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.ac, q.m0 * b.K2 + ks * 64, b.ac_n),
                                     dst + (wave * C::A_DMA + k) * 1024, 16, o.a[k], 0, 0, 0);
   } else if (k < C::A_DMA + C::W_DMA) {
-    llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.wc, (q.g0 * b.KT + 2 * ks) * 1024, b.wc_n),
+    // (waves 2 and 3 copy weight tiles 8..15; for a half, from an empty range)
+    const int off = (q.g0 * b.KT + 2 * ks) * 1024;
+    llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.wc, off, HALF && wave >= 2 ? off : b.wc_n),
                                     dst + C::A_BYTES + (wave * C::W_DMA + k - C::A_DMA) * 1024, 16,
                                     o.w[k - C::A_DMA], 0, 0, 0);
   } else if (k == C::A_DMA + C::W_DMA) {
@@ -1539,35 +1553,36 @@ __device__ __forceinline__ void fp4p_copy_r(const Fp4PSrc& b, LDS uint8_t* smem,
                                   0, 0);
 }
 
-// One K-step of the stream, as Fp4Group: FN x 2 groups of FM MFMAs, each
-// followed by its share of the step's copies (K-step J of quad q) and of the
-// reads of stream K-step pr.
-template <int J, int G>
+// One K-step of the stream, as Fp4Group: FNE x 2 groups of FM MFMAs (FNE =
+// 2 for an n half), each followed by its share of the step's copies (K-step
+// J of quad q) and of the reads of stream K-step pr.
+template <int J, int G, int FNE>
 struct Fp4PGroup {
   using C = Fp4P::C;
-  static constexpr int FN = C::FN, FM = C::FM, NGRP = 2 * FN, NC = Fp4P::copies(J);
-  static constexpr int READS = 3 * FM + 2 + 2 * FN;
+  static constexpr int FN = C::FN, FM = C::FM, NGRP = 2 * FNE, NC = Fp4P::copies(J);
+  static constexpr int READS = 3 * FM + 2 + 2 * FNE;
   static __device__ __forceinline__ void run(v16f (&acc)[FN][FM], const Fp4Frags<FN, FM>& cur,
                                              Fp4Frags<FN, FM>& nxt, LDS uint8_t* smem,
                                              const Fp4PSrc& b, const Fp4PQuad& q, const Fp4PLane& o,
                                              LDS uint8_t* dst, const LDS uint8_t* __restrict__ st,
                                              int64_t pr, int wave, int wn, int wm, int lane) {
-    constexpr int H = G / FN, I = G % FN;
+    constexpr int H = G / FNE, I = G % FNE;
 #pragma unroll
     for (int j = 0; j < FM; ++j)
       acc[I][j] = mfma32_fp4_op<I, 2 * H>(cur.w[I][H], cur.a[j][H], acc[I][j], cur.sw[H], cur.sa[j]);
 #pragma unroll
-    for (int k = G * NC / NGRP; k < (G + 1) * NC / NGRP; ++k) fp4p_copy<J>(b, q, o, smem, dst, wave, k);
+    for (int k = G * NC / NGRP; k < (G + 1) * NC / NGRP; ++k)
+      fp4p_copy<J, FNE == 2>(b, q, o, smem, dst, wave, k);
     constexpr int RG = NGRP - 2;
     if constexpr (G < RG) {
 #pragma unroll
       for (int r = G * READS / RG; r < (G + 1) * READS / RG; ++r)
-        fp4_read_item<Fp4P::BN, Fp4P::BM, Fp4P::DEPTH, Fp4P::NSB>(st, smem, pr, wn, wm, lane, nxt, r);
+        fp4_read_item<Fp4P::BN, Fp4P::BM, Fp4P::DEPTH, Fp4P::NSB, FNE>(st, smem, pr, wn, wm, lane, nxt, r);
     }
     if constexpr (G + 1 == NGRP) fp4_fix_scales<FM>(nxt.sa, lane);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (G + 1 < NGRP)
-      Fp4PGroup<J, G + 1>::run(acc, cur, nxt, smem, b, q, o, dst, st, pr, wave, wn, wm, lane);
+      Fp4PGroup<J, G + 1, FNE>::run(acc, cur, nxt, smem, b, q, o, dst, st, pr, wave, wn, wm, lane);
   }
 };
 
@@ -1581,7 +1596,7 @@ struct Fp4PGroup {
 // copy); vector memory operations complete in issue order, so anything
 // else issued later only makes the wait stricter.  The stage indices are
 // compile-time, so the LDS reads use immediate offsets.
-template <int J, int X>
+template <int J, int X, int FNE>
 __device__ __forceinline__ void fp4p_step(v16f (&acc)[4][4], const Fp4Frags<4, 4>& cur,
                                           Fp4Frags<4, 4>& nxt, LDS uint8_t* smem, const Fp4PSrc& b,
                                           const Fp4PQuad& q, const Fp4PLane& o, int p4, int wave, int wn,
@@ -1590,8 +1605,8 @@ __device__ __forceinline__ void fp4p_step(v16f (&acc)[4][4], const Fp4Frags<4, 4
   __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(Fp4P::younger(J) + X));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  Fp4PGroup<J, 0>::run(acc, cur, nxt, smem, b, q, o, smem + J * C::STAGE, smem + ((J + 1) & 3) * C::STAGE,
-                       4 * int64_t(p4) + J + 1, wave, wn, wm, lane);
+  Fp4PGroup<J, 0, FNE>::run(acc, cur, nxt, smem, b, q, o, smem + J * C::STAGE,
+                            smem + ((J + 1) & 3) * C::STAGE, 4 * int64_t(p4) + J + 1, wave, wn, wm, lane);
 }
 
 // Y[m0.., n0..] = bf16(acc * r) for the wave's 128 x 128 block, straight
@@ -1607,7 +1622,10 @@ __device__ __forceinline__ void fp4p_step(v16f (&acc)[4][4], const Fp4Frags<4, 4
 // 16 rows x 64 bytes.  Blocks go out row band by row band (j outer), so a
 // band's rows are written as whole 256-byte segments back to back.  Exactly
 // EPI_STORES buffer stores per wave (the first K-steps of the next item
-// count them).
+// count them): an n half (FNE = 2) stores its 8 blocks and issues the
+// other 8 blocks' stores at an offset past the buffer, where they write
+// nothing.
+template <int FNE>
 __device__ __forceinline__ void fp4p_epilogue(const v16f (&acc)[4][4], LDS uint8_t* base, int rbuf,
                                               uint16_t* __restrict__ Y, int64_t M, int64_t N,
                                               int64_t m0, int64_t n0, int wn, int wm) {
@@ -1618,17 +1636,23 @@ __device__ __forceinline__ void fp4p_epilogue(const v16f (&acc)[4][4], LDS uint8
       __builtin_amdgcn_make_buffer_rsrc(Y + m0 * N, 0, int(rows * N * 2), 0x00020000);
   v4f rs[4][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FNE; ++i)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      rs[i][g] = *reinterpret_cast<const LDS v4f*>(rb + (wn * 128 + 32 * i + 8 * g + 4 * h) * 4);
+      rs[i][g] = *reinterpret_cast<const LDS v4f*>(rb + (wn * 32 * FNE + 32 * i + 8 * g + 4 * h) * 4);
   // 32-bit offsets: the host checks 256 N * 2 < 2^31
   const int N32 = int(N), row = wm * 128 + (lane & 15);
-  const int n32 = int(n0) + wn * 128 + 8 * (2 * ((lane >> 4) & 1) + h);
+  const int n32 = int(n0) + wn * 32 * FNE + 8 * (2 * ((lane >> 4) & 1) + h);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      if (i >= FNE) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, ys, -1, 0, 0);
+        continue;
+      }
       // read this block's accumulators here, not all of them up front
       v16f av = acc[i][j];
       asm volatile("" : "+a"(av));
@@ -1664,19 +1688,20 @@ __device__ __forceinline__ void fp4p_epilogue(const v16f (&acc)[4][4], LDS uint8
 // first quad, then EPI_STORES stores that write nothing (offsets beyond an
 // empty buffer), so that the first item's first quad finds as many
 // operations after its copies as every later item does (an epilogue's).
+template <bool HALF>
 __device__ __forceinline__ void fp4p_prologue(const Fp4PSrc& b, const Fp4PLane& o, LDS uint8_t* base,
                                               const Fp4PDesc& d0, uint16_t* Y, int wave) {
   using C = Fp4P::C;
   fp4p_copy_r(b, base, d0.g0, 0, wave);
   const Fp4PQuad q{d0.m0, d0.g0, d0.ks0, 0};
 #pragma unroll
-  for (int k = 0; k < Fp4P::copies(0); ++k) fp4p_copy<0>(b, q, o, base, base, wave, k);
+  for (int k = 0; k < Fp4P::copies(0); ++k) fp4p_copy<0, HALF>(b, q, o, base, base, wave, k);
 #pragma unroll
-  for (int k = 0; k < Fp4P::copies(1); ++k) fp4p_copy<1>(b, q, o, base, base + C::STAGE, wave, k);
+  for (int k = 0; k < Fp4P::copies(1); ++k) fp4p_copy<1, HALF>(b, q, o, base, base + C::STAGE, wave, k);
 #pragma unroll
-  for (int k = 0; k < Fp4P::copies(2); ++k) fp4p_copy<2>(b, q, o, base, base + 2 * C::STAGE, wave, k);
+  for (int k = 0; k < Fp4P::copies(2); ++k) fp4p_copy<2, HALF>(b, q, o, base, base + 2 * C::STAGE, wave, k);
 #pragma unroll
-  for (int k = 0; k < Fp4P::copies(3); ++k) fp4p_copy<3>(b, q, o, base, base + 3 * C::STAGE, wave, k);
+  for (int k = 0; k < Fp4P::copies(3); ++k) fp4p_copy<3, HALF>(b, q, o, base, base + 3 * C::STAGE, wave, k);
   const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(Y, 0, 0, 0x00020000);
   // (16-byte stores 32 bytes apart: nothing for the compiler to merge)
 #pragma unroll
@@ -1706,7 +1731,8 @@ __device__ __forceinline__ Fp4PQuad fp4p_quad(const Fp4PDesc& d0, const Fp4PDesc
 // The K-steps of item d0 (stream K-steps p..p + d0.len - 1, p a multiple
 // of 4), one quad at a time.  The first quad's waits for stages copied
 // before the previous epilogue also leave that epilogue's stores and the r
-// copy (ITEM_OPS) in flight.
+// copy (ITEM_OPS) in flight.  FNE = 2 for an n half.
+template <int FNE>
 __device__ __forceinline__ void fp4p_item(v16f (&acc)[4][4], Fp4Frags<4, 4>& fa, Fp4Frags<4, 4>& fb,
                                           LDS uint8_t* base, const Fp4PSrc& b, const Fp4PLane& o,
                                           const Fp4PDesc& d0, const Fp4PDesc& d1, int64_t p, int wave,
@@ -1715,21 +1741,23 @@ __device__ __forceinline__ void fp4p_item(v16f (&acc)[4][4], Fp4Frags<4, 4>& fa,
   {
     const Fp4PQuad q = fp4p_quad(d0, d1, p, 0);
     const int p4 = int(p >> 2);
-    fp4p_step<0, X>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<1, X>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<2, X>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<3, 0>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<0, X, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<1, X, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<2, X, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<3, 0, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
   }
   for (int u = 4; u < d0.len; u += 4) {
     const Fp4PQuad q = fp4p_quad(d0, d1, p, u);
     const int p4 = int((p + u) >> 2);
-    fp4p_step<0, 0>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<1, 0>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<2, 0>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<3, 0>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<0, 0, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<1, 0, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<2, 0, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<3, 0, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
   }
 }
 
+// HALF: every item is an n half (the launch's 2 T items); otherwise whole tiles.
+template <bool HALF>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
@@ -1742,7 +1770,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
   constexpr int FN = C::FN, FM = C::FM, DEPTH = Fp4P::DEPTH;
   const BlobLayout L = blob_layout(MXFP4, N, K);
   Fp4PSched S;
-  S.init(tiles_total, tiles_m, int(L.KS), int(blockIdx.x));
+  S.init(HALF ? 2 * tiles_total : tiles_total, tiles_m, int(L.KS), int(blockIdx.x));
   if (S.n_items == 0) return;
 
   Fp4PSrc b;
@@ -1766,11 +1794,11 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
   const int wn = wave % C::WN, wm = wave / C::WN;
   const Fp4PLane o = fp4p_lane(b, wave, lane);
 
-  fp4p_prologue(b, o, base, fp4p_desc(S, 0), Y, wave);
+  fp4p_prologue<HALF>(b, o, base, fp4p_desc<HALF>(S, 0), Y, wave);
 
   int64_t p = 0;  // stream K-step whose MFMAs run next
   for (int k = 0; k < S.n_items; ++k) {
-    const Fp4PDesc d0 = fp4p_desc(S, k), d1 = fp4p_desc(S, k + 1);
+    const Fp4PDesc d0 = fp4p_desc<HALF>(S, k), d1 = fp4p_desc<HALF>(S, k + 1);
     v16f acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
@@ -1786,27 +1814,43 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
     // the item's first fragments (read here rather than carried from the
     // previous item's last step, so that none are live in its epilogue)
     Fp4Frags<FN, FM> fa, fb;
-    fp4_read_all<Fp4P::BN, Fp4P::BM, DEPTH, Fp4P::NSB>(base, base, 4 * int64_t(p >> 2), wn, wm,
-                                                       fp4p_lane_id(), fa);
-    fp4p_item(acc, fa, fb, base, b, o, d0, d1, p, wave, wn, wm, lane);
+    constexpr int FNE = HALF ? 2 : 4;
+    fp4_read_all<Fp4P::BN, Fp4P::BM, DEPTH, Fp4P::NSB, FNE>(base, base, 4 * int64_t(p >> 2), wn, wm,
+                                                            fp4p_lane_id(), fa);
+    fp4p_item<FNE>(acc, fa, fb, base, b, o, d0, d1, p, wave, wn, wm, lane);
     p += d0.len;
 
     const int64_t n0 = int64_t(d0.g0) * 32;
-    fp4p_epilogue(acc, base, k & 1, Y, M, N, d0.m0, n0, wn, wm);
+    fp4p_epilogue<FNE>(acc, base, k & 1, Y, M, N, d0.m0, n0, wn, wm);
   }
   // every copy (the last ones repeat valid sources) lands before the end
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-// The persistent kernel's conditions: at least 192 tiles of 256 x 256 (below
-// that the one-tile-per-workgroup kernel does as well), K in whole quads of
-// 128-wide K-steps, operands and Y's tile rows addressable by 32-bit buffer
-// offsets.
-bool fp4_persistent_fits(int64_t M, int64_t N, int64_t K) {
-  const int64_t T = ((N + 255) / 256) * ((M + 255) / 256);
-  return M > 32 && K % 512 == 0 && T >= 192 && T < (int64_t(1) << 24) &&
+// The persistent kernel's conditions: K in whole quads of 128-wide K-steps,
+// operands and Y's tile rows addressable by 32-bit buffer offsets, and
+// either at least 192 tiles of 256 x 256 (below that the one-tile-per-
+// workgroup kernels do as well), or (halves) 96..128 tiles with M >= 1024
+// (so that the 256-row tiles are mostly full): 192..256 halves of 256 (m) x
+// 128 (n), at most one per CU, run faster there than the 256 (n) x 128 (m)
+// tile kernel (the 4096 x 4096 projection at M = 2048: 33.8 -> 30.3 us).
+// (Halves after whole rounds, for a last round of few tiles, gained nothing
+// on the 28672 x 4096 projection: the CUs a short last round leaves idle
+// give the busy ones power headroom.)
+static bool fp4_persistent_limits(int64_t M, int64_t N, int64_t K) {
+  return M > 32 && K % 512 == 0 && ((N + 255) / 256) * ((M + 255) / 256) < (int64_t(1) << 23) &&
          int64_t(Fp4P::BM) * N * 2 < (int64_t(1) << 31) && M * (K / 2) < (int64_t(1) << 31) &&
          ((N + 31) / 32) * 32 * (K / 2) < (int64_t(1) << 31);
+}
+
+bool fp4_persistent_halves(int64_t M, int64_t N, int64_t K) {
+  const int64_t T = ((N + 255) / 256) * ((M + 255) / 256);
+  return fp4_persistent_limits(M, N, K) && M >= 1024 && T >= 96 && T <= 128;
+}
+
+bool fp4_persistent_fits(int64_t M, int64_t N, int64_t K) {
+  const int64_t T = ((N + 255) / 256) * ((M + 255) / 256);
+  return fp4_persistent_limits(M, N, K) && (T >= 192 || fp4_persistent_halves(M, N, K));
 }
 
 hipError_t launch_fp4_persistent(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
@@ -1814,8 +1858,12 @@ hipError_t launch_fp4_persistent(int64_t M, int64_t N, int64_t K, const uint8_t*
                                  hipStream_t stream) {
   const int tiles_m = int((M + 255) / 256);
   const int total = int((N + 255) / 256) * tiles_m;
-  hipLaunchKernelGGL(gemm_fp4_persistent_kernel, dim3(Fp4P::XCDS * Fp4P::PER_XCD), dim3(256), 0,
-                     stream, ac, as, blob, Y, M, N, K, tiles_m, total);
+  if (fp4_persistent_halves(M, N, K))
+    hipLaunchKernelGGL(gemm_fp4_persistent_kernel<true>, dim3(Fp4P::XCDS * Fp4P::PER_XCD), dim3(256), 0,
+                       stream, ac, as, blob, Y, M, N, K, tiles_m, total);
+  else
+    hipLaunchKernelGGL(gemm_fp4_persistent_kernel<false>, dim3(Fp4P::XCDS * Fp4P::PER_XCD), dim3(256), 0,
+                       stream, ac, as, blob, Y, M, N, K, tiles_m, total);
   return hipGetLastError();
 }
 
@@ -1998,7 +2046,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_splitk_kernel(
   const int wn = wave % C::WN, wm = wave / C::WN;
   const Fp4PLane o = fp4p_lane(b, wave, lane);
 
-  fp4p_prologue(b, o, base, d0, Y, wave);
+  fp4p_prologue<false>(b, o, base, d0, Y, wave);
   v16f acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
@@ -2012,7 +2060,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_splitk_kernel(
   fp4p_copy_r(b, base, d0.g0, 1, wave);
   Fp4Frags<FN, FM> fa, fb;
   fp4_read_all<Fp4P::BN, Fp4P::BM, DEPTH, Fp4P::NSB>(base, base, 0, wn, wm, fp4p_lane_id(), fa);
-  fp4p_item(acc, fa, fb, base, b, o, d0, d1, 0, wave, wn, wm, lane);
+  fp4p_item<4>(acc, fa, fb, base, b, o, d0, d1, 0, wave, wn, wm, lane);
 
   // the meeting of the two halves at this wave's slot
   const int slot = t * Fp4S::SLOTS + wm * 2 + wn;
@@ -3070,11 +3118,12 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
       if ((N + 31) / 32 >= 512) return launch_fp4_decode<4, 8>(M, N, K, ac, as, blob, Y, stream);
       return launch_fp4_decode<8, 4>(M, N, K, ac, as, blob, Y, stream);
     }
-    // large problems: the persistent kernel (256 x 256 tiles); otherwise
-    // 256 x 256 tiles (4 waves of 128 x 128) unless that leaves more than
-    // ~30% of the 256 CUs idle, then 256 (n) x 128 (m) tiles.
-    if (fp4_persistent_fits(M, N, K)) return launch_fp4_persistent(M, N, K, ac, as, blob, Y, stream);
+    // few tiles and a long K: split-K; large problems: the persistent
+    // kernel (256 x 256 tiles and halves); otherwise 256 x 256 tiles (4
+    // waves of 128 x 128) unless that leaves more than ~30% of the 256 CUs
+    // idle, then 256 (n) x 128 (m) tiles.
     if (fp4_splitk_fits(M, N, K)) return launch_fp4_splitk(M, N, K, ac, as, blob, Y, workspace, stream);
+    if (fp4_persistent_fits(M, N, K)) return launch_fp4_persistent(M, N, K, ac, as, blob, Y, stream);
     const int64_t big = ((N + 255) / 256) * ((M + 255) / 256);
     if (big >= 180) return launch_fp4<256, 256, 4>(M, N, K, ac, as, blob, Y, stream);
     return launch_fp4<256, 128, 5>(M, N, K, ac, as, blob, Y, stream);
