@@ -217,18 +217,21 @@ __device__ inline void store4(uint16_t* y, const float* acc, const float* rn) {
                                             uint32_t(o[2]) | (uint32_t(o[3]) << 16));
 }
 
-// acc[v] += sum[v] * Delta_a * Delta_w[v] * 2^-8 with sw8 = Delta_w * 2^-8
-// (exact: BF16 values keep at most 8 significant bits above 2^-141).
-__device__ inline void scale_add4(float* acc, v4i s, float sa, const float* sw8) {
+// acc[v] += sum[v] * Delta_a * Delta_w[v]: the accumulators hold 2^8 times
+// the output (every block sum is 256 x the code dot product); the epilogue's
+// row scale carries the 2^-8 (power-of-two scalings, so the products and
+// sums round exactly as with the factor applied per block).  The product
+// Delta_a * Delta_w is exact (BF16 values keep at most 8 significant bits).
+__device__ inline void scale_add4(float* acc, v4i s, float sa, const float* sw) {
 #pragma unroll
-  for (int v = 0; v < 4; ++v) acc[v] = fmaf(float(s[v]), sa * sw8[v], acc[v]);
+  for (int v = 0; v < 4; ++v) acc[v] = fmaf(float(s[v]), sa * sw[v], acc[v]);
 }
 
-__device__ inline void unpack_sw8(uint2 w, float* sw8) {
-  sw8[0] = bf16_bits_to_f32(w.x & 0xFFFFu) * 0.00390625f;
-  sw8[1] = bf16_bits_to_f32(w.x >> 16) * 0.00390625f;
-  sw8[2] = bf16_bits_to_f32(w.y & 0xFFFFu) * 0.00390625f;
-  sw8[3] = bf16_bits_to_f32(w.y >> 16) * 0.00390625f;
+__device__ inline void unpack_sw(uint2 w, float* sw) {
+  sw[0] = bf16_bits_to_f32(w.x & 0xFFFFu);
+  sw[1] = bf16_bits_to_f32(w.x >> 16);
+  sw[2] = bf16_bits_to_f32(w.y & 0xFFFFu);
+  sw[3] = bf16_bits_to_f32(w.y >> 16);
 }
 
 // Tile kernel: 4 waves as 2 (M) x 2 (N); a wave owns FM x FN fragments of
@@ -300,6 +303,10 @@ gemm_int4g64_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __
       o.sw[j] = *reinterpret_cast<const uint2*>(wscales + tile * 16);
     }
   };
+  // Per pair of weight fragments: their 2 FM integer MFMAs back to back,
+  // then the scaling of the block sums, so that no sum is read right after
+  // the MFMA that writes it (each would stall the wave for the MFMA's
+  // latency).
   auto compute = [&](const Ops& o) {
     v4i A[FM];
     float sa[FM];
@@ -309,12 +316,21 @@ gemm_int4g64_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __
       sa[i] = bf16_bits_to_f32(o.sa[i]);
     }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const v4i W = widen(o.w[j]);
-      float sw8[4];
-      unpack_sw8(o.sw[j], sw8);
+    for (int j0 = 0; j0 < FN; j0 += 2) {
+      v4i S[2][FM];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) scale_add4(acc[i][j], mfma_block(W, A[i]), sa[i], sw8);
+      for (int jj = 0; jj < 2; ++jj) {
+        const v4i W = widen(o.w[j0 + jj]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) S[jj][i] = mfma_block(W, A[i]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        float sw[4];
+        unpack_sw(o.sw[j0 + jj], sw);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) scale_add4(acc[i][j0 + jj], S[jj][i], sa[i], sw);
+      }
     }
   };
   const int64_t last = L.KB - 1;
@@ -340,7 +356,7 @@ gemm_int4g64_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __
     if (g0 + j >= L.NG) continue;
     const int64_t n = (g0 + j) * 16 + 4 * (lane >> 4);
     const float4 r4 = *reinterpret_cast<const float4*>(r + n);
-    const float rn[4] = {r4.x, r4.y, r4.z, r4.w};
+    const float rn[4] = {r4.x * 0.00390625f, r4.y * 0.00390625f, r4.z * 0.00390625f, r4.w * 0.00390625f};
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int64_t m = m0 + i * 16 + (lane & 15);
@@ -387,18 +403,18 @@ gemm_int4g64_decode_kernel(const uint8_t* __restrict__ a_codes,
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float sw8[4];
-      unpack_sw8(ws[u], sw8);
-      scale_add4(acc, mfma_block(widen(wa[u]), widen(aa[u])), bf16_bits_to_f32(as[u]), sw8);
+      float sw[4];
+      unpack_sw(ws[u], sw);
+      scale_add4(acc, mfma_block(widen(wa[u]), widen(aa[u])), bf16_bits_to_f32(as[u]), sw);
     }
   }
   for (; b < L.KB; b += WAVES) {
-    float sw8[4];
-    unpack_sw8(*reinterpret_cast<const uint2*>(wsc + b * 16), sw8);
+    float sw[4];
+    unpack_sw(*reinterpret_cast<const uint2*>(wsc + b * 16), sw);
     scale_add4(acc,
                mfma_block(widen(*reinterpret_cast<const uint2*>(wtile + b * 512)),
                           widen(*reinterpret_cast<const uint2*>(arow + b * 32))),
-               bf16_bits_to_f32(srow[b]), sw8);
+               bf16_bits_to_f32(srow[b]), sw);
   }
 
   __shared__ float part[WAVES - 1][64][4];
@@ -414,7 +430,7 @@ gemm_int4g64_decode_kernel(const uint8_t* __restrict__ a_codes,
       for (int v = 0; v < 4; ++v) acc[v] += part[w][lane][v];
     const int64_t n = g * 16 + 4 * (lane >> 4);
     const float4 r4 = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(blob + L.r_off) + n);
-    const float rn[4] = {r4.x, r4.y, r4.z, r4.w};
+    const float rn[4] = {r4.x * 0.00390625f, r4.y * 0.00390625f, r4.z * 0.00390625f, r4.w * 0.00390625f};
     if ((lane & 15) < M) store4(Y + int64_t(lane & 15) * N + n, acc, rn);
   }
 }
