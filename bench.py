@@ -455,9 +455,9 @@ def gemm_kernel_label(fmt, M):
             return "gemm_fp4_decode16_kernel"
         if M <= 32:
             return "gemm_fp4_decode_kernel"
-        return ("gemm_fp4_persistent_kernel (linears of 128+ tiles of 256x256, a last round of at "
-                "most 16 tiles per XCD in n halves), gemm_fp4_splitk_kernel (64..128 tiles, K >= 8192) "
-                "and gemm_fp4_kernel (the others)")
+        return ("gemm_fp4_persistent_kernel (256x256 tiles; 256x192 tiles where those fill one "
+                "round; n halves of 96..128-tile shapes), gemm_fp4_splitk_kernel (64..128 tiles, "
+                "K >= 8192) and gemm_fp4_kernel (the others)")
     if fmt == "mxint4":
         if M <= 16:
             return "gemm_decode_kernel<mxint4>"

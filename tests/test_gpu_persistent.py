@@ -1,14 +1,17 @@
 """GPU parity of the MXFP4 persistent GEMM against the oracle.
 
-MXFP4 shapes with at least 192 tiles of 256 x 256 and K a multiple of 512 run
-one workgroup per CU that walks its tiles as one stream of K-steps (the copy
-ring crosses tile boundaries); with 96..128 tiles and M >= 1024 the items
-are the tiles' n halves of 128 features (two per tile).  Covered here, all
-outputs compared: several tiles per workgroup, tile counts that are not a
-multiple of the 8 XCDs, ragged M and N, one-quad tiles (K = 512: every
-tile's only quad also copies the next tile's first), halves (one per
-workgroup, and fewer halves than workgroups, with ragged M and N and a half
-past N), bit-exactness where accumulation is exact, and repeated calls."""
+MXFP4 shapes with enough 256 x 256 tiles and K a multiple of 512 run one
+workgroup per CU that walks its items as one stream of K-steps (the copy
+ring crosses item boundaries).  The items are whole tiles, 256 x 192 tiles
+(3 of the 4 weight groups of a wave) where those fill one round, or n halves
+of 128 features with 96..128 tiles.  Covered here, all outputs compared:
+several tiles per workgroup, tile counts that are not a multiple of the 8
+XCDs, ragged M and N, one-quad tiles (K = 512: every tile's only quad also
+copies the next tile's first), 192-wide tiles (their first weight group at
+either position of its scale word, and a last tile partly past N), halves
+(one per workgroup, and fewer halves than workgroups, with ragged M and N
+and a half past N), bit-exactness where accumulation is exact, and repeated
+calls."""
 import numpy as np
 import pytest
 import torch
@@ -22,18 +25,25 @@ import w4a4_block_scaled_amd as w4
 pytestmark = pytest.mark.gpu
 
 
+def fne(M, N, K):
+    """Item width the host picks for the persistent kernel (0: not taken);
+    mirrors the library's rule."""
+    if not (M > 32 and K % 512 == 0):
+        return 0
+    tm = (M + 255) // 256
+    T, T3 = (N + 255) // 256 * tm, (N + 191) // 192 * tm
+    if M >= 1024 and 128 < T <= 256 and T3 <= 256:
+        return 3
+    if T >= 192:
+        return 4
+    if M >= 1024 and 96 <= T <= 128:
+        return 2
+    return 0
+
+
 def persistent(M, N, K):
     """The host-side condition for the persistent kernel (MXFP4)."""
-    return M > 32 and K % 512 == 0 and (tiles(M, N) >= 192 or halves(M, N, K))
-
-
-def tiles(M, N):
-    return ((M + 255) // 256) * ((N + 255) // 256)
-
-
-def halves(M, N, K):
-    """The persistent kernel runs n halves of 128 features as its items."""
-    return M > 32 and K % 512 == 0 and M >= 1024 and 96 <= tiles(M, N) <= 128
+    return fne(M, N, K) != 0
 
 
 # (M, N, K): what the tile walk does with it (256 workgroups, 32 per XCD)
@@ -45,13 +55,14 @@ PERSIST = [
     (1024, 8192, 1024),    # 128 tiles: 256 halves, one per workgroup
     (2000, 4000, 1024),    # 128 tiles: halves, ragged M and N (the last half past N)
     (1100, 6000, 512),     # 120 tiles: 240 halves, ragged M and N, one quad each
+    (2048, 6144, 1024),    # 192 tiles: 256 tiles of 256 x 192
+    (1100, 7024, 512),     # 185 tiles of 256 x 192, ragged M, the last tile 112 features wide
 ]
 
 
 def test_shapes_take_the_intended_path():
-    assert not any(halves(*s) for s in PERSIST[:4])
-    assert all(halves(*s) for s in PERSIST[4:])
-    assert tiles(2048, 4096) == 128 and halves(2048, 4096, 4096)       # Llama o_proj, M = 2048
+    assert [fne(*s) for s in PERSIST] == [4, 4, 4, 4, 2, 2, 2, 3, 3]
+    assert fne(2048, 4096, 4096) == 2 and fne(2048, 6144, 4096) == 3 and fne(2048, 28672, 4096) == 4
 
 
 @pytest.mark.parametrize("M,N,K", PERSIST)

@@ -1117,11 +1117,14 @@ __device__ __forceinline__ void fp4_fix_scales(int (&sa)[FM], int lane) {
 // of 32-row weight groups the wave uses: a tile whose waves cover only the
 // first FNE groups each (the first 64 FNE of its BN rows) reads the same
 // stage layout.
+// With FNE = 3 the wave's 3 groups start at group goff + 3 wn of the two
+// scale words copied for the tile (goff = first group's position in its
+// scale word), so its scale word is cut from both.
 template <int BN, int BM, int DEPTH, int NB = 3, int FNE = BN / 64>
 __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st,
                                               const LDS uint8_t* __restrict__ base, int64_t kstep,
                                               int wn, int wm, int lane, Fp4Frags<BN / 64, BM / 64>& fr,
-                                              int r) {
+                                              int r, int goff = 0) {
   using C = Fp4Cfg<BN, BM, DEPTH>;
   if (r < C::FM) {
     const int j = r;
@@ -1129,11 +1132,18 @@ __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st
     fr.sa[j] = *reinterpret_cast<const LDS int*>(base + fp4_scale_offset<BN, BM, DEPTH, NB>(R, kstep));
   } else if (r < C::FM + 2) {
     const int hh = r - C::FM;
-    const int e = ((wn * FNE / 4) * 2 + hh) * 64 + lane;
-    const uint32_t wsw = *reinterpret_cast<const LDS uint32_t*>(st + C::A_BYTES + C::W_BYTES +
-                                                                (e / C::WS_DW) * 256 + (e % C::WS_DW) * 4);
-    // byte i of the shifted word is the scale of the wave's weight group i
-    fr.sw[hh] = int(FNE == 4 ? wsw : wsw >> (8 * ((wn * FNE) & 3)));
+    if constexpr (FNE == 3) {
+      static_assert(C::WS_DW == 64, "one scale word per lane and wave slot");
+      const LDS uint32_t* ws = reinterpret_cast<const LDS uint32_t*>(st + C::A_BYTES + C::W_BYTES);
+      const uint64_t w2 = uint64_t(ws[hh * 64 + lane]) | (uint64_t(ws[(2 + hh) * 64 + lane]) << 32);
+      fr.sw[hh] = int(uint32_t(w2 >> (8 * (goff + 3 * wn))));
+    } else {
+      const int e = ((wn * FNE / 4) * 2 + hh) * 64 + lane;
+      const uint32_t wsw = *reinterpret_cast<const LDS uint32_t*>(st + C::A_BYTES + C::W_BYTES +
+                                                                  (e / C::WS_DW) * 256 + (e % C::WS_DW) * 4);
+      // byte i of the shifted word is the scale of the wave's weight group i
+      fr.sw[hh] = int(FNE == 4 ? wsw : wsw >> (8 * ((wn * FNE) & 3)));
+    }
   } else if (r < 3 * C::FM + 2) {
     const int q = r - C::FM - 2, j = q >> 1, hh = q & 1;
     // fragment lane l: row 32 g + l%32 (16-row tile 2 g + (l%32)/16, row
@@ -1150,11 +1160,12 @@ __device__ __forceinline__ void fp4_read_item(const LDS uint8_t* __restrict__ st
 template <int BN, int BM, int DEPTH, int NB = 3, int FNE = BN / 64>
 __device__ __forceinline__ void fp4_read_all(const LDS uint8_t* __restrict__ st,
                                              const LDS uint8_t* __restrict__ base, int64_t kstep,
-                                             int wn, int wm, int lane, Fp4Frags<BN / 64, BM / 64>& fr) {
+                                             int wn, int wm, int lane, Fp4Frags<BN / 64, BM / 64>& fr,
+                                             int goff = 0) {
   using C = Fp4Cfg<BN, BM, DEPTH>;
 #pragma unroll
   for (int r = 0; r < 3 * C::FM + 2 + 2 * FNE; ++r)
-    fp4_read_item<BN, BM, DEPTH, NB, FNE>(st, base, kstep, wn, wm, lane, fr, r);
+    fp4_read_item<BN, BM, DEPTH, NB, FNE>(st, base, kstep, wn, wm, lane, fr, r, goff);
   fp4_fix_scales<C::FM>(fr.sa, lane);
 }
 
@@ -1370,12 +1381,13 @@ hipError_t launch_fp4(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
 // workgroup per CU.  Tiles go to the 8 XCDs in contiguous chunks, each chunk
 // in the tile order of gemm_fp4_kernel (m fastest); within an XCD the 32
 // workgroups take its tiles round-robin, so each round of 32 concurrent
-// tiles shares activation rows and weight groups in that XCD's L2.  With
-// 96..128 tiles (fewer than the CUs), the items are the tiles' n halves of
-// 128 output features instead, two per tile: a half runs the same copy
-// stream as a whole tile (its weight copies for rows 128..255 read from an
-// empty buffer range, which moves nothing), so every wait count holds, and
-// half of the MFMAs.
+// tiles shares activation rows and weight groups in that XCD's L2.  Where
+// whole tiles would leave CUs idle, the items are narrower: 256 x 192 tiles
+// (3 of the 4 weight groups per wave) when those fill at most one round,
+// and with 96..128 tiles, the tiles' n halves of 128 output features.  A
+// narrow item runs the same copy stream as a whole tile (the weight copies
+// of rows it does not have read from an empty buffer range, which moves
+// nothing), so every wait count holds, and fewer MFMAs.
 //
 // The tiles of a workgroup form one stream of K-steps, and the DEPTH-deep
 // copy ring runs over that stream: the next tile's first K-steps are in
@@ -1430,22 +1442,24 @@ struct Fp4PSched {
 
 // Where item k of the stream reads: its tile origin and K-steps [ks0, ks0 +
 // len).  Past the last item it repeats the last item's last quad, so copies
-// beyond the end of the stream read valid sources.  With HALF, item h is n
-// half h % 2 of tile h / 2 (consecutive workgroups of an XCD take the two
-// halves of a tile, which share its activation rows).
+// beyond the end of the stream read valid sources.  FNE is the item width
+// in 64-feature units per wave: 4, a 256 x 256 tile; 3, a 256 x 192 tile
+// (tiles of 192 features, 6 weight groups); 2, item h is n half h % 2 of
+// 256 x 256 tile h / 2 (consecutive workgroups of an XCD take the two halves
+// of a tile, which share its activation rows).
 struct Fp4PDesc {
   int m0, g0;  // first activation row, first 32-row weight group
   int ks0, len;
 };
 
-template <bool HALF>
+template <int FNE>
 __device__ __forceinline__ Fp4PDesc fp4p_desc(const Fp4PSched& S, int k) {
   const bool over = k >= S.n_items;
   const int it = S.tile(over ? S.n_items - 1 : k);
-  const int t = HALF ? it / 2 : it;
+  const int t = FNE == 2 ? it / 2 : it;
   Fp4PDesc d;
   d.m0 = (t % S.tiles_m) * Fp4P::BM;
-  d.g0 = (t / S.tiles_m) * (Fp4P::BN / 32) + (HALF ? 4 * (it & 1) : 0);
+  d.g0 = FNE == 3 ? (t / S.tiles_m) * 6 : (t / S.tiles_m) * (Fp4P::BN / 32) + (FNE == 2 ? 4 * (it & 1) : 0);
   d.ks0 = over ? S.KS - 4 : 0;
   d.len = over ? 4 : S.KS;
   return d;
@@ -1509,7 +1523,7 @@ struct Fp4PQuad {
 
 // Copy number k of a wave's share of K-step j of quad q (activation tiles,
 // weight tiles, weight scale words, then with j = 0 the scale quarters).
-template <int J, bool HALF>
+template <int J, int FNE>
 __device__ __forceinline__ void fp4p_copy(const Fp4PSrc& b, const Fp4PQuad& q, const Fp4PLane& o,
                                           LDS uint8_t* smem, LDS uint8_t* dst, int wave, int k) {
   using C = Fp4P::C;
@@ -1518,9 +1532,10 @@ __device__ __forceinline__ void fp4p_copy(const Fp4PSrc& b, const Fp4PQuad& q, c
     llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.ac, q.m0 * b.K2 + ks * 64, b.ac_n),
                                     dst + (wave * C::A_DMA + k) * 1024, 16, o.a[k], 0, 0, 0);
   } else if (k < C::A_DMA + C::W_DMA) {
-    // (waves 2 and 3 copy weight tiles 8..15; for a half, from an empty range)
+    // (wave w copies weight tiles 4 w .. 4 w + 3, groups 2 w and 2 w + 1;
+    // groups an item does not have come from an empty range)
     const int off = (q.g0 * b.KT + 2 * ks) * 1024;
-    llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.wc, off, HALF && wave >= 2 ? off : b.wc_n),
+    llvm_amdgcn_raw_buffer_load_lds(buf_rsrc(b.wc, off, FNE < 4 && wave >= FNE ? off : b.wc_n),
                                     dst + C::A_BYTES + (wave * C::W_DMA + k - C::A_DMA) * 1024, 16,
                                     o.w[k - C::A_DMA], 0, 0, 0);
   } else if (k == C::A_DMA + C::W_DMA) {
@@ -1565,24 +1580,25 @@ struct Fp4PGroup {
                                              Fp4Frags<FN, FM>& nxt, LDS uint8_t* smem,
                                              const Fp4PSrc& b, const Fp4PQuad& q, const Fp4PLane& o,
                                              LDS uint8_t* dst, const LDS uint8_t* __restrict__ st,
-                                             int64_t pr, int wave, int wn, int wm, int lane) {
+                                             int64_t pr, int wave, int wn, int wm, int lane, int goff) {
     constexpr int H = G / FNE, I = G % FNE;
 #pragma unroll
     for (int j = 0; j < FM; ++j)
       acc[I][j] = mfma32_fp4_op<I, 2 * H>(cur.w[I][H], cur.a[j][H], acc[I][j], cur.sw[H], cur.sa[j]);
 #pragma unroll
     for (int k = G * NC / NGRP; k < (G + 1) * NC / NGRP; ++k)
-      fp4p_copy<J, FNE == 2>(b, q, o, smem, dst, wave, k);
+      fp4p_copy<J, FNE>(b, q, o, smem, dst, wave, k);
     constexpr int RG = NGRP - 2;
     if constexpr (G < RG) {
 #pragma unroll
       for (int r = G * READS / RG; r < (G + 1) * READS / RG; ++r)
-        fp4_read_item<Fp4P::BN, Fp4P::BM, Fp4P::DEPTH, Fp4P::NSB, FNE>(st, smem, pr, wn, wm, lane, nxt, r);
+        fp4_read_item<Fp4P::BN, Fp4P::BM, Fp4P::DEPTH, Fp4P::NSB, FNE>(st, smem, pr, wn, wm, lane, nxt, r,
+                                                                       goff);
     }
     if constexpr (G + 1 == NGRP) fp4_fix_scales<FM>(nxt.sa, lane);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (G + 1 < NGRP)
-      Fp4PGroup<J, G + 1, FNE>::run(acc, cur, nxt, smem, b, q, o, dst, st, pr, wave, wn, wm, lane);
+      Fp4PGroup<J, G + 1, FNE>::run(acc, cur, nxt, smem, b, q, o, dst, st, pr, wave, wn, wm, lane, goff);
   }
 };
 
@@ -1600,13 +1616,14 @@ template <int J, int X, int FNE>
 __device__ __forceinline__ void fp4p_step(v16f (&acc)[4][4], const Fp4Frags<4, 4>& cur,
                                           Fp4Frags<4, 4>& nxt, LDS uint8_t* smem, const Fp4PSrc& b,
                                           const Fp4PQuad& q, const Fp4PLane& o, int p4, int wave, int wn,
-                                          int wm, int lane) {
+                                          int wm, int lane, int goff) {
   using C = Fp4P::C;
   __builtin_amdgcn_s_waitcnt(vm_lgkm0_encoding(Fp4P::younger(J) + X));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   Fp4PGroup<J, 0, FNE>::run(acc, cur, nxt, smem, b, q, o, smem + J * C::STAGE,
-                            smem + ((J + 1) & 3) * C::STAGE, 4 * int64_t(p4) + J + 1, wave, wn, wm, lane);
+                            smem + ((J + 1) & 3) * C::STAGE, 4 * int64_t(p4) + J + 1, wave, wn, wm, lane,
+                            goff);
 }
 
 // Y[m0.., n0..] = bf16(acc * r) for the wave's 128 x 128 block, straight
@@ -1688,20 +1705,20 @@ __device__ __forceinline__ void fp4p_epilogue(const v16f (&acc)[4][4], LDS uint8
 // first quad, then EPI_STORES stores that write nothing (offsets beyond an
 // empty buffer), so that the first item's first quad finds as many
 // operations after its copies as every later item does (an epilogue's).
-template <bool HALF>
+template <int FNE>
 __device__ __forceinline__ void fp4p_prologue(const Fp4PSrc& b, const Fp4PLane& o, LDS uint8_t* base,
                                               const Fp4PDesc& d0, uint16_t* Y, int wave) {
   using C = Fp4P::C;
   fp4p_copy_r(b, base, d0.g0, 0, wave);
   const Fp4PQuad q{d0.m0, d0.g0, d0.ks0, 0};
 #pragma unroll
-  for (int k = 0; k < Fp4P::copies(0); ++k) fp4p_copy<0, HALF>(b, q, o, base, base, wave, k);
+  for (int k = 0; k < Fp4P::copies(0); ++k) fp4p_copy<0, FNE>(b, q, o, base, base, wave, k);
 #pragma unroll
-  for (int k = 0; k < Fp4P::copies(1); ++k) fp4p_copy<1, HALF>(b, q, o, base, base + C::STAGE, wave, k);
+  for (int k = 0; k < Fp4P::copies(1); ++k) fp4p_copy<1, FNE>(b, q, o, base, base + C::STAGE, wave, k);
 #pragma unroll
-  for (int k = 0; k < Fp4P::copies(2); ++k) fp4p_copy<2, HALF>(b, q, o, base, base + 2 * C::STAGE, wave, k);
+  for (int k = 0; k < Fp4P::copies(2); ++k) fp4p_copy<2, FNE>(b, q, o, base, base + 2 * C::STAGE, wave, k);
 #pragma unroll
-  for (int k = 0; k < Fp4P::copies(3); ++k) fp4p_copy<3, HALF>(b, q, o, base, base + 3 * C::STAGE, wave, k);
+  for (int k = 0; k < Fp4P::copies(3); ++k) fp4p_copy<3, FNE>(b, q, o, base, base + 3 * C::STAGE, wave, k);
   const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(Y, 0, 0, 0x00020000);
   // (16-byte stores 32 bytes apart: nothing for the compiler to merge)
 #pragma unroll
@@ -1738,30 +1755,31 @@ __device__ __forceinline__ void fp4p_item(v16f (&acc)[4][4], Fp4Frags<4, 4>& fa,
                                           const Fp4PDesc& d0, const Fp4PDesc& d1, int64_t p, int wave,
                                           int wn, int wm, int lane) {
   constexpr int X = Fp4P::ITEM_OPS;
+  const int goff = FNE == 3 ? d0.g0 & 3 : 0;
   {
     const Fp4PQuad q = fp4p_quad(d0, d1, p, 0);
     const int p4 = int(p >> 2);
-    fp4p_step<0, X, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<1, X, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<2, X, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<3, 0, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<0, X, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane, goff);
+    fp4p_step<1, X, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane, goff);
+    fp4p_step<2, X, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane, goff);
+    fp4p_step<3, 0, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane, goff);
   }
   for (int u = 4; u < d0.len; u += 4) {
     const Fp4PQuad q = fp4p_quad(d0, d1, p, u);
     const int p4 = int((p + u) >> 2);
-    fp4p_step<0, 0, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<1, 0, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<2, 0, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane);
-    fp4p_step<3, 0, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane);
+    fp4p_step<0, 0, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane, goff);
+    fp4p_step<1, 0, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane, goff);
+    fp4p_step<2, 0, FNE>(acc, fa, fb, base, b, q, o, p4, wave, wn, wm, lane, goff);
+    fp4p_step<3, 0, FNE>(acc, fb, fa, base, b, q, o, p4, wave, wn, wm, lane, goff);
   }
 }
 
-// HALF: every item is an n half (the launch's 2 T items); otherwise whole tiles.
-template <bool HALF>
+// FNE: the items' width (see fp4p_desc); `items` of them in the launch.
+template <int FNE>
 __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
-    int tiles_m, int tiles_total) {
+    int tiles_m, int items) {
   if (!blob_header_ok(blob, MXFP4, N, K)) {
     fill_y_nan(Y, M, N);
     return;
@@ -1770,7 +1788,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
   constexpr int FN = C::FN, FM = C::FM, DEPTH = Fp4P::DEPTH;
   const BlobLayout L = blob_layout(MXFP4, N, K);
   Fp4PSched S;
-  S.init(HALF ? 2 * tiles_total : tiles_total, tiles_m, int(L.KS), int(blockIdx.x));
+  S.init(items, tiles_m, int(L.KS), int(blockIdx.x));
   if (S.n_items == 0) return;
 
   Fp4PSrc b;
@@ -1794,11 +1812,11 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
   const int wn = wave % C::WN, wm = wave / C::WN;
   const Fp4PLane o = fp4p_lane(b, wave, lane);
 
-  fp4p_prologue<HALF>(b, o, base, fp4p_desc<HALF>(S, 0), Y, wave);
+  fp4p_prologue<FNE>(b, o, base, fp4p_desc<FNE>(S, 0), Y, wave);
 
   int64_t p = 0;  // stream K-step whose MFMAs run next
   for (int k = 0; k < S.n_items; ++k) {
-    const Fp4PDesc d0 = fp4p_desc<HALF>(S, k), d1 = fp4p_desc<HALF>(S, k + 1);
+    const Fp4PDesc d0 = fp4p_desc<FNE>(S, k), d1 = fp4p_desc<FNE>(S, k + 1);
     v16f acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
@@ -1814,9 +1832,8 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
     // the item's first fragments (read here rather than carried from the
     // previous item's last step, so that none are live in its epilogue)
     Fp4Frags<FN, FM> fa, fb;
-    constexpr int FNE = HALF ? 2 : 4;
     fp4_read_all<Fp4P::BN, Fp4P::BM, DEPTH, Fp4P::NSB, FNE>(base, base, 4 * int64_t(p >> 2), wn, wm,
-                                                            fp4p_lane_id(), fa);
+                                                            fp4p_lane_id(), fa, FNE == 3 ? d0.g0 & 3 : 0);
     fp4p_item<FNE>(acc, fa, fb, base, b, o, d0, d1, p, wave, wn, wm, lane);
     p += d0.len;
 
@@ -1828,42 +1845,56 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_persistent_kernel(
 }
 
 // The persistent kernel's conditions: K in whole quads of 128-wide K-steps,
-// operands and Y's tile rows addressable by 32-bit buffer offsets, and
-// either at least 192 tiles of 256 x 256 (below that the one-tile-per-
-// workgroup kernels do as well), or (halves) 96..128 tiles with M >= 1024
-// (so that the 256-row tiles are mostly full): 192..256 halves of 256 (m) x
-// 128 (n), at most one per CU, run faster there than the 256 (n) x 128 (m)
-// tile kernel (the 4096 x 4096 projection at M = 2048: 33.8 -> 30.3 us).
-// (Halves after whole rounds, for a last round of few tiles, gained nothing
-// on the 28672 x 4096 projection: the CUs a short last round leaves idle
-// give the busy ones power headroom.)
+// operands and Y's tile rows addressable by 32-bit buffer offsets, and one of
+//   * at least 256 tiles of 256 x 256 (whole tiles, FNE = 4), or 192..256
+//     tiles when 256 x 192 tiles would need more than one round;
+//   * 129..256 tiles with M >= 1024 (256-row tiles mostly full) whose 256 x
+//     192 tiles fit one round (FNE = 3: the 6144 x 4096 projection at M =
+//     2048, 192 tiles, runs as 256 tiles of 3/4 the work);
+//   * 96..128 tiles with M >= 1024: n halves (FNE = 2), at most one per CU,
+//     faster there than the 256 (n) x 128 (m) tile kernel (the 4096 x 4096
+//     projection at M = 2048: 33.8 -> 30.3 us).
+// Below that the one-tile-per-workgroup kernels do as well.  (Halves after
+// whole rounds, for a last round of few tiles, gained nothing on the 28672 x
+// 4096 projection: the CUs a short last round leaves idle give the busy ones
+// power headroom.)
 static bool fp4_persistent_limits(int64_t M, int64_t N, int64_t K) {
   return M > 32 && K % 512 == 0 && ((N + 255) / 256) * ((M + 255) / 256) < (int64_t(1) << 23) &&
          int64_t(Fp4P::BM) * N * 2 < (int64_t(1) << 31) && M * (K / 2) < (int64_t(1) << 31) &&
          ((N + 31) / 32) * 32 * (K / 2) < (int64_t(1) << 31);
 }
 
-bool fp4_persistent_halves(int64_t M, int64_t N, int64_t K) {
-  const int64_t T = ((N + 255) / 256) * ((M + 255) / 256);
-  return fp4_persistent_limits(M, N, K) && M >= 1024 && T >= 96 && T <= 128;
+// item width of the persistent kernel for the shape (0: not taken)
+static int fp4_persistent_fne(int64_t M, int64_t N, int64_t K) {
+  if (!fp4_persistent_limits(M, N, K)) return 0;
+  const int64_t tm = (M + 255) / 256;
+  const int64_t T = ((N + 255) / 256) * tm, T3 = ((N + 191) / 192) * tm;
+  if (M >= 1024 && T > 128 && T <= 256 && T3 <= 256) return 3;
+  if (T >= 192) return 4;
+  if (M >= 1024 && T >= 96 && T <= 128) return 2;
+  return 0;
 }
 
-bool fp4_persistent_fits(int64_t M, int64_t N, int64_t K) {
-  const int64_t T = ((N + 255) / 256) * ((M + 255) / 256);
-  return fp4_persistent_limits(M, N, K) && (T >= 192 || fp4_persistent_halves(M, N, K));
-}
+bool fp4_persistent_fits(int64_t M, int64_t N, int64_t K) { return fp4_persistent_fne(M, N, K) != 0; }
 
 hipError_t launch_fp4_persistent(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
                                  const uint8_t* as, const uint8_t* blob, uint16_t* Y,
                                  hipStream_t stream) {
   const int tiles_m = int((M + 255) / 256);
-  const int total = int((N + 255) / 256) * tiles_m;
-  if (fp4_persistent_halves(M, N, K))
-    hipLaunchKernelGGL(gemm_fp4_persistent_kernel<true>, dim3(Fp4P::XCDS * Fp4P::PER_XCD), dim3(256), 0,
-                       stream, ac, as, blob, Y, M, N, K, tiles_m, total);
-  else
-    hipLaunchKernelGGL(gemm_fp4_persistent_kernel<false>, dim3(Fp4P::XCDS * Fp4P::PER_XCD), dim3(256), 0,
-                       stream, ac, as, blob, Y, M, N, K, tiles_m, total);
+  const dim3 grid(Fp4P::XCDS * Fp4P::PER_XCD);
+  switch (fp4_persistent_fne(M, N, K)) {
+    case 3:
+      hipLaunchKernelGGL(gemm_fp4_persistent_kernel<3>, grid, dim3(256), 0, stream, ac, as, blob, Y, M, N, K,
+                         tiles_m, int((N + 191) / 192) * tiles_m);
+      break;
+    case 2:
+      hipLaunchKernelGGL(gemm_fp4_persistent_kernel<2>, grid, dim3(256), 0, stream, ac, as, blob, Y, M, N, K,
+                         tiles_m, 2 * int((N + 255) / 256) * tiles_m);
+      break;
+    default:
+      hipLaunchKernelGGL(gemm_fp4_persistent_kernel<4>, grid, dim3(256), 0, stream, ac, as, blob, Y, M, N, K,
+                         tiles_m, int((N + 255) / 256) * tiles_m);
+  }
   return hipGetLastError();
 }
 
@@ -2046,7 +2077,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp4_splitk_kernel(
   const int wn = wave % C::WN, wm = wave / C::WN;
   const Fp4PLane o = fp4p_lane(b, wave, lane);
 
-  fp4p_prologue<false>(b, o, base, d0, Y, wave);
+  fp4p_prologue<4>(b, o, base, d0, Y, wave);
   v16f acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
