@@ -240,26 +240,29 @@ __device__ inline void unpack_sw(uint2 w, float* sw) {
 // multiplied (activation rows clamped to M - 1, weight row groups to NG - 1,
 // so every load is in bounds); outputs outside M x N are not stored.
 // Workgroups are dealt to the 8 XCDs round-robin; workgroup b takes tile
-// (b % 8) per_xcd + b / 8, so each XCD works through a contiguous range of
-// tiles in m-fastest order: the workgroups an XCD runs at once share their
-// weight row groups (read from HBM once into that XCD's L2) and cycle over
-// the activation rows, instead of every weight row group being fetched
-// again by each row block on whichever XCD it lands.
+// number (b % 8) per_xcd + b / 8 of an order that runs through blocks of 8
+// x 8 tiles (8 column tiles wide, then down the rows): each XCD works
+// through a contiguous range of that order, so the 64 workgroups it runs at
+// once (two per CU) cover 8 row tiles x 8 column tiles and fetch each of
+// their activation rows and weight groups into its L2 once.
 template <int FM, int FN>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_int4g64_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
                          const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M,
-                         int64_t N, int64_t K, int tiles_m, int tiles, int per_xcd) {
+                         int64_t N, int64_t K, int tiles_m, int tiles_n, int per_xcd) {
   if (!blob_header_ok(blob, 3, N, K)) {
     fill_y_nan(Y, M, N);
     return;
   }
-  const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
-  if (tile >= tiles) return;
+  const int o = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (o >= tiles_m * tiles_n) return;
+  const int nb = o / (8 * tiles_m), ob = o - nb * 8 * tiles_m;
+  const int nw = tiles_n - 8 * nb < 8 ? tiles_n - 8 * nb : 8;  // width of this column block
+  const int tm = ob / nw, tn = 8 * nb + ob % nw;
   const I4Layout L = i4_layout(N, K);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = int64_t(tile % tiles_m) * (2 * FM * 16) + (wave >> 1) * (FM * 16);
-  const int64_t g0 = int64_t(tile / tiles_m) * (2 * FN) + (wave & 1) * FN;
+  const int64_t m0 = int64_t(tm) * (2 * FM * 16) + (wave >> 1) * (FM * 16);
+  const int64_t g0 = int64_t(tn) * (2 * FN) + (wave & 1) * FN;
   const uint8_t* wcodes = blob + L.code_off + lane * 8;
   const uint16_t* wscales = reinterpret_cast<const uint16_t*>(blob + L.scale_off) + 4 * (lane >> 4);
 
@@ -493,7 +496,7 @@ hipError_t launch_linear_int4g64(int64_t M, int64_t N, int64_t K, const void* a_
     if (tiles_n * tiles_m >= (int64_t(1) << 30)) return hipErrorInvalidValue;
     const int tiles = int(tiles_n * tiles_m), per_xcd = (tiles + 7) / 8;
     hipLaunchKernelGGL((gemm_int4g64_tile_kernel<FM, FN>), dim3(unsigned(8 * per_xcd)), dim3(256), 0,
-                       stream, ac, as, bl, y, M, N, K, int(tiles_m), tiles, per_xcd);
+                       stream, ac, as, bl, y, M, N, K, int(tiles_m), int(tiles_n), per_xcd);
   }
   return hipGetLastError();
 }
