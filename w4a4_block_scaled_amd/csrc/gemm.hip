@@ -2295,44 +2295,56 @@ hipError_t launch_fp4_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
   return hipGetLastError();
 }
 
-// MXFP4 weight streaming for M <= 16: one workgroup per 16 output features
-// (one half of a 32-row weight group), on the 16x16x128 scaled MFMA with the
-// activation rows as its 16 columns (columns >= M are zero).  Twice as many
-// workgroups as with 32-feature groups, so every CU streams even when N is
-// only 4096.  Workgroup b takes slice (b % 8) S + b / 8 (S slices per XCD):
-// consecutive slices, which share 1 KiB weight tiles and scale words, run on
-// one XCD at about the same time.  The WAVES waves split the 128-wide
-// K-steps into contiguous ranges; each wave issues the loads of up to U
-// K-steps at once, then their MFMAs.  Weight fragment lane l holds row
-// l % 16 and 32-wide K chunk l / 16 of a K-step: the tile of 64-K half
-// (l / 16) / 2 and, in it, tile lane 32 ((l / 16) % 2) + 16 h + l % 16 for
-// slice half h, so each 16-lane group reads 256 contiguous bytes; the weight
-// stream is read once, with non-temporal loads.  Activation codes are loaded
-// with lane l taking row l / 4, 16-byte chunk l % 4 (a row's 64 bytes per
-// lane quad), then moved to the fragment lane (chunk l / 16 of row l % 16)
-// with a lane permutation.  Partial sums of the waves are added through LDS
-// and wave 0 runs the epilogue.
-template <int WAVES, int U>
+// MXFP4 weight streaming for M <= 16: one workgroup per FS x 16 output
+// features (FS = 1: one half of a 32-row weight group; FS = 2: the whole
+// group, for large N), on the 16x16x128 scaled MFMA with the activation rows
+// as its 16 columns (columns >= M are zero).  With FS = 1 there are twice as
+// many workgroups as 32-row groups, so every CU streams even when N is only
+// 4096; with FS = 2 each activation fragment (and its scale) serves two
+// weight fragments, halving the activation loads per weight byte, which at
+// M = 16 cost the texture unit as much as the weights.  Workgroup b takes
+// slice (b % 8) S + b / 8 (S slices per XCD): consecutive slices, which
+// share 1 KiB weight tiles and scale words, run on one XCD at about the same
+// time.  The WAVES waves split the 128-wide K-steps into contiguous ranges;
+// each wave issues the loads of up to U K-steps at once, then their MFMAs.
+// Weight fragment lane l holds row l % 16 and 32-wide K chunk l / 16 of a
+// K-step: the tile of 64-K half (l / 16) / 2 and, in it, tile lane 32 ((l /
+// 16) % 2) + 16 h + l % 16 for group half h, so each 16-lane group reads
+// 256 contiguous bytes; the weight stream is read once, with non-temporal
+// loads.  Activation codes are loaded with lane l taking row l / 4, 16-byte
+// chunk l % 4 (a row's 64 bytes per lane quad), then moved to the fragment
+// lane (chunk l / 16 of row l % 16) with a lane permutation.  Partial sums
+// of the waves are added through LDS and wave 0 runs the epilogue.
+template <int WAVES, int U, int FS = 1>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode16_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  static_assert(FS == 1 || FS == 2 || FS == 4, "one half, one or two 32-row groups");
   if (!blob_header_ok(blob, MXFP4, N, K)) {
     fill_y_nan(Y, M, N);
     return;
   }
   const BlobLayout L = blob_layout(MXFP4, N, K);
-  const int64_t F = N / 16, per_x = (F + 7) / 8;
-  const int64_t f = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8, g = f >> 1;
+  // slices of FS x 16 features (N % (16 FS) == 0 for FS > 1); slice h of
+  // the workgroup is half h % 2 of 32-row group g0 + h / 2
+  const int64_t F = N / (16 * FS), per_x = (F + 7) / 8;
+  const int64_t f = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8;
   if (f >= F) return;
-  const int hf = int(f & 1);
+  const int64_t g0 = FS == 1 ? f >> 1 : f * (FS / 2);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, c = lane >> 4;
-  const int tl = 32 * (c & 1) + 16 * hf + r;
   const int64_t KT = L.KT, KS = L.KS, K2 = K / 2, KB = K / 32;
-  const u32x4* __restrict__ W = reinterpret_cast<const u32x4*>(blob + L.code_off) + (g * KT + (c >> 1)) * 64 + tl;
-  const uint32_t* __restrict__ S =
-      reinterpret_cast<const uint32_t*>(blob + L.scale_off) + ((g >> 2) * KT + (c >> 1)) * 64 + tl;
-  const int sw_shift = 8 * int(g & 3);
+  const u32x4* __restrict__ W[FS];
+  const uint32_t* __restrict__ S[FS];
+  int sw_shift[FS];
+#pragma unroll
+  for (int h = 0; h < FS; ++h) {
+    const int64_t g = g0 + h / 2;
+    const int tl = 32 * (c & 1) + 16 * (FS == 1 ? int(f & 1) : h % 2) + r;
+    W[h] = reinterpret_cast<const u32x4*>(blob + L.code_off) + (g * KT + (c >> 1)) * 64 + tl;
+    S[h] = reinterpret_cast<const uint32_t*>(blob + L.scale_off) + ((g >> 2) * KT + (c >> 1)) * 64 + tl;
+    sw_shift[h] = 8 * int(g & 3);
+  }
   const bool mvalid = r < M;
   // activation loads: lane l takes row l / 4, chunk l % 4 (only the lanes of
   // rows < M load); fragment lane l then reads it from lane 4 (l % 16) + l / 16
@@ -2345,18 +2357,23 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode16_kernel(
   const int64_t s_begin = wave * per;
   const int64_t s_end = s_begin + per < KS ? s_begin + per : KS;
 
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  v4f acc[FS];
+#pragma unroll
+  for (int h = 0; h < FS; ++h) acc[h] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int64_t s0 = s_begin; s0 < s_end; s0 += U) {
-    u32x4 wf[U], af[U];
-    uint32_t swd[U];
+    u32x4 wf[U][FS], af[U];
+    uint32_t swd[U][FS];
     int sab[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t s = s0 + u;
       const bool ok = s < s_end;
       const int64_t sc = ok ? s : s_end - 1;  // clamped: loads stay in range
-      wf[u] = __builtin_nontemporal_load(&W[sc * 128]);
-      swd[u] = __builtin_nontemporal_load(&S[sc * 128]);
+#pragma unroll
+      for (int h = 0; h < FS; ++h) {
+        wf[u][h] = __builtin_nontemporal_load(&W[h][sc * 128]);
+        swd[u][h] = __builtin_nontemporal_load(&S[h][sc * 128]);
+      }
       u32x4 a = {0u, 0u, 0u, 0u};
       if (lvalid) a = *reinterpret_cast<const u32x4*>(arow + sc * 64);
       af[u] = ok ? a : u32x4{0u, 0u, 0u, 0u};
@@ -2369,33 +2386,42 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode16_kernel(
       a.y = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].y)));
       a.z = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].z)));
       a.w = uint32_t(__builtin_amdgcn_ds_bpermute(perm, int(af[u].w)));
-      acc = mfma_fp4_op<0>(wf[u], a, acc, int(swd[u] >> sw_shift), sab[u]);
+#pragma unroll
+      for (int h = 0; h < FS; ++h)
+        acc[h] = mfma_fp4_op<0>(wf[u][h], a, acc[h], int(swd[u][h] >> sw_shift[h]), sab[u]);
     }
   }
 
-  __shared__ v4f red[WAVES > 1 ? WAVES - 1 : 1][64];
-  if (wave != 0) red[wave - 1][lane] = acc;
+  __shared__ v4f red[WAVES > 1 ? WAVES - 1 : 1][FS][64];
+  if (wave != 0) {
+#pragma unroll
+    for (int h = 0; h < FS; ++h) red[wave - 1][h][lane] = acc[h];
+  }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int w = 0; w < WAVES - 1; ++w) {
-    const v4f o = red[w][lane];
+  for (int w = 0; w < WAVES - 1; ++w)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += o[e];
-  }
-  // lane l: activation row l % 16, features 4 (l / 16) + 0..3 of the slice
+    for (int h = 0; h < FS; ++h) {
+      const v4f o = red[w][h][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[h][e] += o[e];
+    }
+  // lane l: activation row l % 16, features 4 (l / 16) + 0..3 of a 16-slice
   if (!mvalid) return;
-  const int64_t n = f * 16 + 4 * c;
-  const float4 rv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(blob + L.r_off) + n);
-  store4(Y, N, r, n, acc, v4f{rv.x, rv.y, rv.z, rv.w});
+#pragma unroll
+  for (int h = 0; h < FS; ++h) {
+    const int64_t n = (FS * f + h) * 16 + 4 * c;
+    const float4 rv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(blob + L.r_off) + n);
+    store4(Y, N, r, n, acc[h], v4f{rv.x, rv.y, rv.z, rv.w});
+  }
 }
 
-template <int WAVES, int U = 8>
+template <int WAVES, int U = 8, int FS = 1>
 hipError_t launch_fp4_decode16(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                                const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_fp4_decode16_kernel<WAVES, U>), dim3(unsigned((N / 16 + 7) / 8 * 8)), dim3(64 * WAVES), 0,
-                     stream,
-                     ac, as, blob, Y, M, N, K);
+  hipLaunchKernelGGL((gemm_fp4_decode16_kernel<WAVES, U, FS>), dim3(unsigned((N / (16 * FS) + 7) / 8 * 8)),
+                     dim3(64 * WAVES), 0, stream, ac, as, blob, Y, M, N, K);
   return hipGetLastError();
 }
 
@@ -3135,6 +3161,12 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
     if (M <= 16) {
       // 16-feature workgroups; waves enough for at most 8 K-steps each
       const int64_t ks = K / 128;
+      // two whole 32-row groups per workgroup when there are enough of them
+      // to fill the CUs twice over, and more than 4 activation rows to
+      // share (Llama gate+up at M = 16: 20.5 -> 15.6 us; batches of 4
+      // K-steps keep the 16 fragments in flight that 8 of one slice had)
+      if (M > 4 && N % 64 == 0 && N / 64 >= 256 && ks <= 32)
+        return launch_fp4_decode16<4, 4, 4>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 32) return launch_fp4_decode16<4>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 64) return launch_fp4_decode16<8>(M, N, K, ac, as, blob, Y, stream);
       // one load batch per wave sized to its K-steps when they are <= 7
