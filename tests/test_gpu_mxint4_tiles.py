@@ -1,10 +1,11 @@
-"""GPU parity of the two MXINT4 tiled kernels against the oracle.
+"""GPU parity of the MXINT4 tiled kernels against the oracle.
 
 M > 16 runs either 256 x 128 tiles with one wave per SIMD or 256 x 256
 tiles with two waves per SIMD (8 waves of 128 x 64), whichever takes fewer
-estimated rounds over the 256 CUs.  Both are covered here on ragged and
-exact tile grids, with the oracle computing sampled outputs, and bit for bit
-where the accumulation is exact."""
+estimated rounds over the 256 CUs; with fewer than 128 tiles of 256 x 128,
+128 x 64 or 128 x 128 tiles (the most that fit one round).  All four are
+covered here on ragged and exact tile grids, with the oracle computing
+sampled outputs, and bit for bit where the accumulation is exact."""
 import numpy as np
 import pytest
 
@@ -17,28 +18,43 @@ import w4a4_block_scaled_amd as w4
 pytestmark = pytest.mark.gpu
 
 
-def two_waves_per_simd(M, N):
-    """The host-side choice between the two MXINT4 tiled kernels (M > 16)."""
+def tile_config(M, N):
+    """The host-side choice among the MXINT4 tiled kernels (M > 16)."""
     tn = (N + 255) // 256
     rounds_lean = (tn * ((M + 255) // 256) + 255) // 256
     rounds_one = (tn * ((M + 127) // 128) + 255) // 256
-    return 100 * rounds_lean <= 54 * rounds_one
+    if 100 * rounds_lean <= 54 * rounds_one:
+        return "256x256 lean"
+    if tn * ((M + 127) // 128) < 128:
+        tn2 = (N + 127) // 128
+        if tn2 * ((M + 63) // 64) <= 256:
+            return "128x64"
+        if tn2 * ((M + 127) // 128) <= 256:
+            return "128x128"
+    return "256x128"
+
+
+def two_waves_per_simd(M, N):
+    return tile_config(M, N) == "256x256 lean"
 
 
 # (M, N, K, kernel): ragged M and N, exact grids, one K-step and several
 SHAPES = [
-    (4000, 3504, 1024, True),
-    (4096, 3584, 512, True),
-    (4096, 4608, 384, False),
-    (1000, 2000, 640, False),
+    (4000, 3504, 1024, "256x256 lean"),
+    (4096, 3584, 512, "256x256 lean"),
+    (4096, 4608, 384, "256x128"),
+    (1000, 2000, 640, "128x64"),
+    (300, 3536, 640, "128x64"),
+    (512, 4608, 1024, "128x128"),
+    (520, 4560, 384, "128x128"),
 ]
 
 
-@pytest.mark.parametrize("M,N,K,lean", SHAPES)
-def test_mxint4_tiled_kernels_match_oracle(M, N, K, lean):
+@pytest.mark.parametrize("M,N,K,config", SHAPES)
+def test_mxint4_tiled_kernels_match_oracle(M, N, K, config):
     dev = device()
-    assert two_waves_per_simd(M, N) == lean
-    say(f"[mxint4 tiles] M={M} N={N} K={K} two waves per SIMD: {lean}")
+    assert tile_config(M, N) == config
+    say(f"[mxint4 tiles] M={M} N={N} K={K} tiles: {config}")
     rng = np.random.default_rng(M + N + K)
     case = inputs.adhoc_case("mxint4", M, N, K, seed=M + 3 * N + K)
     Y, *_ = gpu_layer(case, dev)
@@ -49,13 +65,14 @@ def test_mxint4_tiled_kernels_match_oracle(M, N, K, lean):
     say(f"    max elementwise rel err {elem:.2e}, max row rel-L2 {row:.2e}")
 
 
-def test_mxint4_two_waves_per_simd_bit_exact():
+@pytest.mark.parametrize("M,N,K,config", [(4096, 3584, 1024, "256x256 lean"), (512, 4608, 512, "128x128"),
+                                           (300, 3536, 512, "128x64")])
+def test_mxint4_tiled_bit_exact(M, N, K, config):
     """Equal block scales per operand: every fp32 partial sum is exact, so
     the output equals the oracle's BF16 rounding bit for bit."""
     dev = device()
-    M, N, K = 4096, 3584, 1024
-    assert two_waves_per_simd(M, N)
-    say(f"[mxint4 tiles bit-exact] M={M} N={N} K={K}")
+    assert tile_config(M, N) == config
+    say(f"[mxint4 tiles bit-exact] M={M} N={N} K={K} tiles: {config}")
     rng = np.random.default_rng(17)
     w_codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
     w_scales = np.full((N, K // 32), 124, np.uint8)

@@ -2315,11 +2315,17 @@ hipError_t launch_fp4_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
 // chunk l % 4 (a row's 64 bytes per lane quad), then moved to the fragment
 // lane (chunk l / 16 of row l % 16) with a lane permutation.  Partial sums
 // of the waves are added through LDS and wave 0 runs the epilogue.
-template <int WAVES, int U, int FS = 1>
+//
+// SD (M > 4): the activation scale bytes come as dwords, lane (r, c) loading
+// the four block scales of row r for K-step s + c, and reach the fragment
+// lanes through a lane permutation: one scale load per 4 K-steps instead of
+// one per K-step, each touching the same 16 rows.
+template <int WAVES, int U, int FS = 1, bool SD = false>
 __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode16_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
   static_assert(FS == 1 || FS == 2 || FS == 4, "one half, one or two 32-row groups");
+  static_assert(!SD || U % 4 == 0, "scale dwords cover whole groups of 4 K-steps");
   if (!blob_header_ok(blob, MXFP4, N, K)) {
     fill_y_nan(Y, M, N);
     return;
@@ -2364,6 +2370,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode16_kernel(
     u32x4 wf[U][FS], af[U];
     uint32_t swd[U][FS];
     int sab[U];
+    int sdw[SD ? U / 4 : 1];
+    if constexpr (SD) {
+#pragma unroll
+      for (int j = 0; j < U / 4; ++j) {
+        const int64_t s = s0 + 4 * j + c;
+        const int64_t sc = s < s_end ? s : s_end - 1;  // clamped: loads stay in range
+        sdw[j] = *reinterpret_cast<const int*>(srow - c + sc * 4);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t s = s0 + u;
@@ -2377,7 +2392,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode16_kernel(
       u32x4 a = {0u, 0u, 0u, 0u};
       if (lvalid) a = *reinterpret_cast<const u32x4*>(arow + sc * 64);
       af[u] = ok ? a : u32x4{0u, 0u, 0u, 0u};
-      sab[u] = mvalid ? int(srow[sc * 4]) : 127;
+      if constexpr (!SD) sab[u] = mvalid ? int(srow[sc * 4]) : 127;
+    }
+    if constexpr (SD) {
+      // byte c of the dword lane (r, u % 4) loaded for K-step s0 + u
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int d = __builtin_amdgcn_ds_bpermute(4 * (r + 16 * (u & 3)), sdw[u >> 2]);
+        sab[u] = mvalid ? int((uint32_t(d) >> (8 * c)) & 0xffu) : 127;
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -2417,10 +2440,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_fp4_decode16_kernel(
   }
 }
 
-template <int WAVES, int U = 8, int FS = 1>
+template <int WAVES, int U = 8, int FS = 1, bool SD = false>
 hipError_t launch_fp4_decode16(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
                                const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_fp4_decode16_kernel<WAVES, U, FS>), dim3(unsigned((N / (16 * FS) + 7) / 8 * 8)),
+  hipLaunchKernelGGL((gemm_fp4_decode16_kernel<WAVES, U, FS, SD>), dim3(unsigned((N / (16 * FS) + 7) / 8 * 8)),
                      dim3(64 * WAVES), 0, stream, ac, as, blob, Y, M, N, K);
   return hipGetLastError();
 }
@@ -3165,8 +3188,10 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
       // to fill the CUs twice over, and more than 4 activation rows to
       // share (Llama gate+up at M = 16: 20.5 -> 15.6 us; batches of 4
       // K-steps keep the 16 fragments in flight that 8 of one slice had)
+      // (activation scales as dwords there: -4%; on the 16-feature
+      // workgroups of the smaller linears they gained nothing)
       if (M > 4 && N % 64 == 0 && N / 64 >= 256 && ks <= 32)
-        return launch_fp4_decode16<4, 4, 4>(M, N, K, ac, as, blob, Y, stream);
+        return launch_fp4_decode16<4, 4, 4, true>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 32) return launch_fp4_decode16<4>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 64) return launch_fp4_decode16<8>(M, N, K, ac, as, blob, Y, stream);
       // one load batch per wave sized to its K-steps when they are <= 7
@@ -3217,6 +3242,18 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
     const int64_t rounds_one = (tn * ((M + 127) / 128) + 255) / 256;
     if (100 * rounds_lean <= 54 * rounds_one)
       return launch_mx_lean<FMT, 256, 256, 2, 4, 4>(M, N, K, ac, as, blob, Y, stream);
+    // Fewer than 128 tiles of 256 x 128 would leave half the CUs idle: then
+    // the most tiles that still fit one round, 128 x 64 (wave tiles 64 x 32)
+    // or 128 x 128 (64 x 64), which gain more from the CUs they add than
+    // they lose per tile (Qwen at M = 512: QKV 51.6 -> 36.3 us with 128 x
+    // 128, O 50.6 -> 26.9 and down 241 -> 114 us with 128 x 64).
+    const int64_t t1 = tn * ((M + 127) / 128);
+    if (t1 < 128) {
+      const int64_t tn2 = (N + 127) / 128;
+      if (tn2 * ((M + 63) / 64) <= 256) return launch_mx<FMT, 128, 64, 2, 2, 4>(M, N, K, ac, as, blob, Y, stream);
+      if (tn2 * ((M + 127) / 128) <= 256)
+        return launch_mx<FMT, 128, 128, 2, 2, 4>(M, N, K, ac, as, blob, Y, stream);
+    }
     return launch_mx<FMT, 256, 128, 2, 2, 4>(M, N, K, ac, as, blob, Y, stream);
   }
 }

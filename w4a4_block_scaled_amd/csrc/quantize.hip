@@ -161,6 +161,54 @@ __global__ __launch_bounds__(kThreads) void quantize_nv_kernel(
   if ((col8 & 1) == 0) scales[row * (K8 / 2) + (col8 >> 1)] = uint8_t(s);
 }
 
+// Small NVFP4 tensors (decode: a few rows) in one launch: every workgroup
+// takes the tensor amax over all of X itself (a few tens of KB, read from
+// L2 after the first), forms t, and quantizes its own kThreads groups; the
+// first writes t.  Same reduction result (a maximum does not depend on
+// order), same t rounding and the same block quantizer as the three-kernel
+// path, so codes, scales and t are identical, without the two extra
+// launches and without one workgroup doing all the fp64 block decisions.
+constexpr int64_t kNvSmallGroups = 8192;  // groups of 8 elements (<= 32 workgroups)
+
+__global__ __launch_bounds__(kThreads) void quantize_nv_small_kernel(
+    const uint4* __restrict__ X, const float* __restrict__ c, float* __restrict__ t_out,
+    uint32_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t n_groups, int64_t K8) {
+  float m = 0.0f;
+  for (int64_t g = threadIdx.x; g < n_groups; g += kThreads) {
+    float x[8];
+    load8(X, c, g, g % K8, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  float a = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) a = fmaxf(a, red[i]);
+  float t = __fdiv_rn(a, 2688.0f);
+  if (a == 0.0f || t == 0.0f) t = 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *t_out = t;
+  // this workgroup's groups (a 16-block is an even group and the next one,
+  // in adjacent lanes); lanes past the end quantize a clamped copy and
+  // store nothing
+  const int64_t g_raw = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const bool live = g_raw < n_groups;
+  const int64_t g = live ? g_raw : n_groups - 1;
+  const int64_t row = g / K8, col8 = g - row * K8;
+  float x[8];
+  load8(X, c, g, col8, x);
+  uint32_t word;
+  int sc;
+  quant8_nv(x, t, word, sc);
+  if (live) {
+    codes[g] = word;
+    if ((col8 & 1) == 0) scales[row * (K8 / 2) + (col8 >> 1)] = uint8_t(sc);
+  }
+}
+
 // ------------------------------------------------ several column scales --
 //
 // One X, P column-scale vectors (per-projection c on a fused input, e.g. the
@@ -414,6 +462,9 @@ hipError_t launch_quantize_act(int fmt, int64_t M, int64_t K, const void* X, con
       else
         hipLaunchKernelGGL((quantize_mx_kernel<MXINT4, 1>), g1, dim3(kThreads), 0, stream, Xv, c, cw, sb, M, K8);
     }
+  } else if (n_groups <= kNvSmallGroups) {
+    hipLaunchKernelGGL(quantize_nv_small_kernel, grid, dim3(kThreads), 0, stream, Xv, c, t_act, cw, sb,
+                       n_groups, K8);
   } else {
     float* partial = static_cast<float*>(workspace);
     const int nparts = int(std::min<int64_t>(kNvAmaxBlocks, (n_groups + kThreads - 1) / kThreads));
