@@ -16,17 +16,28 @@ import w4a4_block_scaled_amd as w4
 
 pytestmark = pytest.mark.gpu
 
-# (format, M, N, K): the persistent MXFP4 GEMM, the split-K GEMM (with its
-# workspace), the tile GEMM, the decode kernels, and the NVFP4 path (tensor
-# amax pre-pass with its workspace; tile and decode GEMMs)
+# (format, M, N, K): the persistent MXFP4 GEMM (256 x 256 tiles, 256 x 192
+# tiles, n halves), the split-K GEMM (with its workspace), the tile GEMM,
+# the decode kernels (16-feature, one-group and two-group workgroups), the
+# MXINT4 tile and small-tile GEMMs, the NVFP4 path (tensor amax pre-pass with
+# its workspace, or the one-launch quantizer; tile and decode GEMMs) and the
+# 8-bit MX formats
 CASES = [
     ("mxfp4", 512, 49152, 512),
+    ("mxfp4", 2048, 6144, 512),
+    ("mxfp4", 1024, 8192, 1024),
     ("mxfp4", 300, 8208, 8192),
     ("mxfp4", 300, 1024, 1024),
     ("mxfp4", 4, 4096, 4096),
+    ("mxfp4", 8, 6144, 1024),
+    ("mxfp4", 16, 16384, 1024),
     ("mxint4", 16, 2048, 1024),
+    ("mxint4", 300, 3536, 640),
     ("nvfp4", 260, 1024, 1024),
     ("nvfp4", 3, 1024, 1024),
+    ("nvfp4", 16, 4096, 4096),
+    ("mxfp8", 300, 1024, 512),
+    ("mxint8", 8, 1024, 512),
 ]
 
 
@@ -39,7 +50,7 @@ def build(case, dev):
     blob = w4.pack_weight(wc, ws, tw, to_dev(case.r, dev), case.fmt)
     x, c = to_dev(case.x, dev), to_dev(case.c, dev)
     G = w4.block_size(case.fmt)
-    codes = torch.empty((case.M, case.K // 2), dtype=torch.uint8, device=dev)
+    codes = torch.empty((case.M, w4.code_cols(case.fmt, case.K)), dtype=torch.uint8, device=dev)
     scales = torch.empty((case.M, case.K // G), dtype=torch.uint8, device=dev)
     t = torch.ones(1, dtype=torch.float32, device=dev)
     qws = torch.zeros(max(16, w4.lib().w4a4_quantize_workspace_bytes(w4.FORMATS[case.fmt], case.M, case.K)),
