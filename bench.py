@@ -50,13 +50,13 @@ PEAK = {  # MI355X published dense peaks
     "mxfp4": (10.1e15, "TFLOP/s", "mfma"),   # FP4 / FP6 MFMA
     "mxint4": (5.0e15, "TFLOP/s", "mfma"),   # runs on the FP8 scaled MFMA
     "nvfp4": (2.5e15, "TFLOP/s", "mfma"),    # runs on the fp16 MFMA
-    "int4g64": (5.0e15, "TOP/s", "mfma"),    # int8 MFMA (5.0 POP/s dense)
+    "int4g64": (2.5e15, "TFLOP/s", "mfma"),  # exact fp16 expansion of code x BF16 scale, fp16 MFMA
     "mxfp8": (2.5e15, "TFLOP/s", "mfma"),    # exact bf16 expansion on the bf16 MFMA
     "mxint8": (5.0e15, "TOP/s", "mfma"),     # FP8 scaled MFMA, four per int8 product
 }
 HBM_PEAK = 8.0e12
 DTYPE = {"mxfp4": "fp4", "nvfp4": "fp4xe4m3->fp16", "mxint4": "int4->fp8",
-         "int4g64": "int4->int8 (bf16 block scales)", "mxfp8": "fp8->bf16", "mxint8": "int8->2xfp8"}
+         "int4g64": "int4xbf16->fp16", "mxfp8": "fp8->bf16", "mxint8": "int8->2xfp8"}
 CODE_BYTES = {"mxfp8": 1.0, "mxint8": 1.0}   # bytes per code (0.5 for the 4-bit formats)
 SCALE_BYTES = {"int4g64": 2}   # bytes per block scale (1 for E8M0 / UE4M3)
 
@@ -464,7 +464,8 @@ def gemm_kernel_label(fmt, M):
         return ("gemm_mx_lean_kernel<mxint4> (256x256 tiles, where their rounds over the CUs are not "
                 "coarser) and gemm_mx_kernel<mxint4> (256x128 tiles)")
     if fmt == "int4g64":
-        return "gemm_int4g64_decode_kernel" if M <= 16 else "gemm_int4g64_tile_kernel<4, 4>"
+        return ("gemm_int4g64_decode_kernel" if M <= 16 else
+                "gemm_int4g64_f16_kernel (256x256 tiles for qkv and gate+up, 256x128 for o and down)")
     if fmt in ("mxfp8", "mxint8"):
         return (f"gemm_mx8_decode_kernel<{fmt}>" if M <= 16 else
                 f"gemm_mx8_tile_kernel<{fmt}, 256, 128, 2, 2, 3>")

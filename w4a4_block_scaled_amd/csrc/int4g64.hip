@@ -438,9 +438,525 @@ gemm_int4g64_decode_kernel(const uint8_t* __restrict__ a_codes,
   }
 }
 
+// ------------------------------------------------------ fp16 GEMM (M > 16) --
+// The block scaling moves into the operands: every code times its block's
+// scale becomes one exact fp16 value, and the fp16 MFMA (32 x 32 x 16,
+// fp32 accumulation) adds the products of both operands with no per-block
+// work on the accumulators.  An INT4 code q times a BF16 scale needs at most
+// 3 + 8 significant bits, which fp16 holds, so the expansion is exact while
+// the value stays in fp16's normal range.  That range is kept by a power of
+// two per activation row and per weight column, taken from the largest scale
+// of the row (column) over all of K and removed again in the epilogue:
+//
+//   g = Delta * 2^sh, sh = 147 - (largest biased exponent field of the row's
+//   scales), so the largest scale becomes 2^(E+9) m with E = 11 (m in [1, 2),
+//   8 significant bits) and the others E = 11 - (exponent distance).  A byte
+//   u = q + 8 (0..15) is the E4M3 encoding of u * 2^-9, so the hardware
+//   conversion with the power-of-two scale 2^(E+9) gives u * 2^E exactly,
+//   and one fp16 fma, u 2^E * m - 8 * 2^E * m, gives q * 2^E * m in a single
+//   rounding of an exact result (8 * 2^E * m has 8 significant bits).  For
+//   E in [-14, 11] every intermediate and result is an fp16 normal number
+//   (|q 2^E m| < 2^15), so blocks whose scales lie within 25 binades of the
+//   row's (column's) largest are exact; smaller ones are rounded to fp16,
+//   an error below 2^-36 of the largest block's values.
+//   Y = (sum of products) * 2^(ea + ew - 276) * r, with ea, ew the exponent
+//   fields of the row's and the column's largest scales.
+//
+// Workgroup: 4 waves as 2 (n) x 2 (m), wave tile 32 FN (n) x 32 FM (m) of
+// 32 x 32 fragments; the weight fragment is the MFMA's row operand, so lane
+// l holds outputs n = 32 i + 8 (e / 4) + 4 (l / 32) + e % 4 and m = 32 j + l % 32.
+// Each 128-wide K-step (two blocks) is one stage of a DEPTH-deep LDS ring,
+// filled by direct global -> LDS copies (equal counts per wave, so the load
+// counter tells when a stage has landed):
+//   A codes  per 32-row fragment, 2 KiB: block b, 16-byte half c of the
+//            block's 32 bytes, row R at b 1024 + c 512 + 16 R (lane (R, c)
+//            reads its 16 bytes of a block with one 16-byte read)
+//   W codes  per pair of 16-row groups, 2 KiB: block b, 8-byte chunk c of
+//            the blob's tile (K 16 c .. +16), row R of the pair at
+//            b 1024 + c 256 + 8 R
+//   A scales one dword per row (the two blocks' BF16 scales)
+//   W scales the blob's 64 bytes per group (two blocks x 16 columns)
+// Lane l takes, per block, the codes of K 32 (l / 32) .. +32 of its row
+// (chunks 2 (l / 32) and 2 (l / 32) + 1); MFMA t of the block uses their
+// dword t, in the same order for both operands.
+
+typedef _Float16 i4h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 i4v8h __attribute__((ext_vector_type(8)));
+typedef float i4v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t i4u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t i4u32x2 __attribute__((ext_vector_type(2)));
+#define I4_LDS __attribute__((address_space(3)))
+
+struct F16Scale {
+  float p2;       // 2^(E+9): the scale operand of the fp8 -> fp16 conversion
+  i4h2 mm, cc;    // (m, m) and (-8 2^E m, -8 2^E m)
+};
+
+// BF16 scale bits and the row's (column's) shift -> the expansion constants.
+// A zero scale gives zeros; a NaN scale gives NaN (cc is NaN).  The sign of
+// a scale stays with m, so a negative scale expands correctly as well.
+__device__ __forceinline__ F16Scale f16_scale(uint32_t bits, int sh) {
+  const float g = ldexpf(bf16_bits_to_f32(bits), sh);
+  const uint32_t gb = __float_as_uint(g);
+  F16Scale s;
+  s.p2 = __uint_as_float(gb & 0x7F800000u);
+  const float m = __uint_as_float((gb & 0x807FFFFFu) | 0x3F800000u);
+  const float c = g * -0.015625f;
+  s.mm = __builtin_bit_cast(i4h2, __builtin_amdgcn_cvt_pkrtz(m, m));
+  s.cc = __builtin_bit_cast(i4h2, __builtin_amdgcn_cvt_pkrtz(c, c));
+  return s;
+}
+
+// 8 INT4 codes (one dword, code j in bits 4j..4j+3) -> 8 fp16 values of
+// code x scale, in the order (0, 2, 4, 6, 1, 3, 5, 7).
+__device__ __forceinline__ i4v8h expand8(uint32_t x, const F16Scale& s) {
+  const uint32_t e = x ^ 0x88888888u;
+  const uint32_t lo = e & 0x0F0F0F0Fu;
+  const uint32_t hi = (e >> 4) & 0x0F0F0F0Fu;
+#define I4_CVT(d, w) __builtin_bit_cast(i4h2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d, s.p2, w))
+  const i4h2 v0 = __builtin_elementwise_fma(I4_CVT(lo, false), s.mm, s.cc);
+  const i4h2 v1 = __builtin_elementwise_fma(I4_CVT(lo, true), s.mm, s.cc);
+  const i4h2 v2 = __builtin_elementwise_fma(I4_CVT(hi, false), s.mm, s.cc);
+  const i4h2 v3 = __builtin_elementwise_fma(I4_CVT(hi, true), s.mm, s.cc);
+#undef I4_CVT
+  return i4v8h{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
+template <int FN, int FM, int DEPTH>
+struct F16Cfg {
+  static constexpr int BN = 64 * FN, BM = 64 * FM;
+  static constexpr int A_BYTES = BM * 64;
+  static constexpr int W_BYTES = BN * 64;
+  static constexpr int AS_BYTES = BM * 4;
+  static constexpr int WS_BYTES = BN * 4;
+  static constexpr int STAGE = A_BYTES + W_BYTES + AS_BYTES + WS_BYTES;
+  static constexpr int COPIES = FM + FN + 2;  // per wave per stage
+  static constexpr int EPI_WAVE = (32 * FM) * (64 * FN);  // bf16 outputs of a wave tile
+  static_assert(FN >= 2 && FN <= 4 && FM >= 2 && FM <= 4, "one scale copy per wave");
+  static_assert((DEPTH - 2) * COPIES < 64 && DEPTH >= 2, "load counter range");
+  static_assert(DEPTH * STAGE + 4 * (BM + BN) <= 160 * 1024, "LDS");
+  static_assert(4 * EPI_WAVE <= DEPTH * STAGE, "epilogue staging");
+};
+
+struct F16Args {
+  const uint8_t* a_codes;
+  const uint16_t* a_scales;
+  const uint8_t* wcodes;
+  const uint16_t* wscales;
+  int64_t M, K2, KB, NG, m0, g0;
+};
+
+// Copy K-step ks (blocks 2 ks, 2 ks + 1) into stage buffer dst: FM + FN
+// 16-byte copies and one 4-byte copy of each scale kind per wave.  Rows
+// beyond M and groups beyond N/16 read clamped valid addresses; they feed
+// only outputs that are not stored.
+template <int FN, int FM, int DEPTH>
+__device__ __forceinline__ void f16_issue(const F16Args& t, int64_t ks, I4_LDS uint8_t* dst, int wave,
+                                          int lane) {
+  using C = F16Cfg<FN, FM, DEPTH>;
+#pragma unroll
+  for (int x = 0; x < FM; ++x) {
+    const int k = wave * FM + x, f = k >> 1, b = k & 1;
+    int64_t row = t.m0 + 32 * f + (lane & 31);
+    row = row < t.M ? row : t.M - 1;
+    __builtin_amdgcn_global_load_lds(t.a_codes + row * t.K2 + (2 * ks + b) * 32 + 16 * (lane >> 5),
+                                     dst + f * 2048 + b * 1024, 16, 0, 0);
+  }
+  I4_LDS uint8_t* wdst = dst + C::A_BYTES;
+#pragma unroll
+  for (int x = 0; x < FN; ++x) {
+    const int k = wave * FN + x, p = k >> 1, b = k & 1;
+    int64_t g = t.g0 + 2 * p + ((lane >> 3) & 1);
+    g = g < t.NG ? g : t.NG - 1;
+    __builtin_amdgcn_global_load_lds(t.wcodes + (g * t.KB + 2 * ks + b) * 512 + 16 * (lane & 7) + 128 * (lane >> 4),
+                                     wdst + p * 2048 + b * 1024, 16, 0, 0);
+  }
+  I4_LDS uint8_t* asdst = wdst + C::W_BYTES;
+  if (lane < C::BM / 4) {
+    int64_t row = t.m0 + wave * (C::BM / 4) + lane;
+    row = row < t.M ? row : t.M - 1;
+    __builtin_amdgcn_global_load_lds(t.a_scales + row * t.KB + 2 * ks, asdst + wave * C::BM, 4, 0, 0);
+  }
+  I4_LDS uint8_t* wsdst = asdst + C::AS_BYTES;
+  if (lane < C::BN / 4) {
+    const int d = wave * (C::BN / 4) + lane;
+    int64_t g = t.g0 + d / 16;
+    g = g < t.NG ? g : t.NG - 1;
+    __builtin_amdgcn_global_load_lds(t.wscales + (g * t.KB + 2 * ks) * 16 + 2 * (d & 15), wsdst + wave * C::BN, 4,
+                                     0, 0);
+  }
+}
+
+__device__ __forceinline__ constexpr int f16_wait_encoding(int v) {
+  // s_waitcnt: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8] = 0, vmcnt[5:4] at [15:14]
+  return (v & 15) | (7 << 4) | (((v >> 4) & 3) << 14);
+}
+
+// Wait until at most `after` stages of C copies are in flight for this wave
+// and its LDS reads have completed, then barrier: the stage is in LDS for
+// every wave, and the buffer read in the previous step is free.
+template <int C, int DEPTH>
+__device__ __forceinline__ void f16_stage_ready(int after) {
+  switch (after) {
+    case 0: __builtin_amdgcn_s_waitcnt(f16_wait_encoding(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(f16_wait_encoding(C)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(f16_wait_encoding(2 * C)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(f16_wait_encoding(3 * C)); break;
+    default: __builtin_amdgcn_s_waitcnt(f16_wait_encoding(4 * C)); break;
+  }
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int FN, int FM, int DEPTH>
+__device__ __forceinline__ void f16_step(const I4_LDS uint8_t* __restrict__ st, int wn, int wm, int lane,
+                                         const int (&sha)[FM], const int (&shw)[FN],
+                                         i4v16f (&acc)[FN][FM]) {
+  using C = F16Cfg<FN, FM, DEPTH>;
+  const int R = lane & 31, h = lane >> 5;
+  const I4_LDS uint8_t* A = st;
+  const I4_LDS uint8_t* W = st + C::A_BYTES;
+  const I4_LDS uint8_t* AS = W + C::W_BYTES;
+  const I4_LDS uint8_t* WS = AS + C::AS_BYTES;
+  uint32_t asw[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j)
+    asw[j] = *reinterpret_cast<const I4_LDS uint32_t*>(AS + 4 * (32 * (wm * FM + j) + R));
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    i4u32x4 af[FM], wf[FN];
+    F16Scale sa[FM], sw[FN];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      af[j] = *reinterpret_cast<const I4_LDS i4u32x4*>(A + (wm * FM + j) * 2048 + b * 1024 + h * 512 + 16 * R);
+      sa[j] = f16_scale((asw[j] >> (16 * b)) & 0xFFFFu, sha[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int p = wn * FN + i;
+      const I4_LDS uint8_t* wp = W + p * 2048 + b * 1024 + h * 512 + 8 * R;
+      const i4u32x2 lo = *reinterpret_cast<const I4_LDS i4u32x2*>(wp);
+      const i4u32x2 hi = *reinterpret_cast<const I4_LDS i4u32x2*>(wp + 256);
+      wf[i] = i4u32x4{lo.x, lo.y, hi.x, hi.y};
+      const uint32_t bits =
+          *reinterpret_cast<const I4_LDS uint16_t*>(WS + (2 * p + (R >> 4)) * 64 + b * 32 + 2 * (R & 15));
+      sw[i] = f16_scale(bits, shw[i]);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      i4v8h ah[FM];
+#pragma unroll
+      for (int j = 0; j < FM; ++j) ah[j] = expand8(af[j][t], sa[j]);
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        const i4v8h wh = expand8(wf[i][t], sw[i]);
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wh, ah[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// The same K-step for a tile whose rows or columns hold scales more than 25
+// binades apart (or subnormal or non-finite ones), where one power of two
+// per row and column cannot keep every expanded value in fp16's normal
+// range: the operands are code x scale in fp32 (exact for any scale, 11
+// significant bits) and the fp32 MFMA (32 x 32 x 2) multiplies them, each
+// product exact (22 bits), into the same accumulators.  Sixteen times the
+// MFMA time of the fp16 path; it serves only such tiles.  MFMA c of a block
+// takes code c of each lane's 32 (K 32 (l / 32) + c), both operands alike.
+template <int FN, int FM, int DEPTH>
+__device__ __forceinline__ void f16_step_wide(const I4_LDS uint8_t* __restrict__ st, int wn, int wm, int lane,
+                                              i4v16f (&acc)[FN][FM]) {
+  using C = F16Cfg<FN, FM, DEPTH>;
+  const int R = lane & 31, h = lane >> 5;
+  const I4_LDS uint8_t* A = st;
+  const I4_LDS uint8_t* W = st + C::A_BYTES;
+  const I4_LDS uint8_t* AS = W + C::W_BYTES;
+  const I4_LDS uint8_t* WS = AS + C::AS_BYTES;
+  for (int b = 0; b < 2; ++b) {
+    i4u32x4 af[FM], wf[FN];
+    float sa[FM], sw[FN];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      af[j] = *reinterpret_cast<const I4_LDS i4u32x4*>(A + (wm * FM + j) * 2048 + b * 1024 + h * 512 + 16 * R);
+      const uint32_t asw = *reinterpret_cast<const I4_LDS uint32_t*>(AS + 4 * (32 * (wm * FM + j) + R));
+      sa[j] = bf16_bits_to_f32((asw >> (16 * b)) & 0xFFFFu);
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int p = wn * FN + i;
+      const I4_LDS uint8_t* wp = W + p * 2048 + b * 1024 + h * 512 + 8 * R;
+      const i4u32x2 lo = *reinterpret_cast<const I4_LDS i4u32x2*>(wp);
+      const i4u32x2 hi = *reinterpret_cast<const I4_LDS i4u32x2*>(wp + 256);
+      wf[i] = i4u32x4{lo.x, lo.y, hi.x, hi.y};
+      sw[i] = bf16_bits_to_f32(
+          *reinterpret_cast<const I4_LDS uint16_t*>(WS + (2 * p + (R >> 4)) * 64 + b * 32 + 2 * (R & 15)));
+    }
+    for (int c = 0; c < 32; ++c) {
+      const int d = c >> 3, sh = 28 - 4 * (c & 7);
+      float av[FM], wv[FN];
+#pragma unroll
+      for (int j = 0; j < FM; ++j) av[j] = float(int(af[j][d] << sh) >> 28) * sa[j];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) wv[i] = float(int(wf[i][d] << sh) >> 28) * sw[i];
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(wv[i], av[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+// Running range of the exponent fields (bits 7..14, kept in place) of BF16
+// scales: the largest over all, the smallest over the nonzero ones.  A
+// nonzero scale with a zero field (subnormal) enters the minimum as 0.
+__device__ __forceinline__ void exp_range1(uint32_t& mx, uint32_t& mn, uint32_t bits) {
+  const uint32_t e = bits & 0x7F80u;
+  mx = mx > e ? mx : e;
+  const uint32_t f = (bits & 0x7FFFu) ? e : 0xFFFFu;
+  mn = mn < f ? mn : f;
+}
+
+__device__ __forceinline__ void exp_range2(uint32_t& mx, uint32_t& mn, uint32_t w) {
+  exp_range1(mx, mn, w & 0xFFFFu);
+  exp_range1(mx, mn, w >> 16);
+}
+
+// Whether one power of two cannot hold the row's (column's) scales in the
+// exact window: nonzero scales more than 25 binades apart, a subnormal one,
+// or a non-finite one.
+__device__ __forceinline__ bool exp_wide(uint32_t mx, uint32_t mn) {
+  if (mn == 0xFFFFu) return false;  // all scales zero
+  return mx == 0x7F80u || mn == 0u || (mx >> 7) - (mn >> 7) > 25;
+}
+
+template <int FN, int FM, int DEPTH>
+__global__ void __launch_bounds__(256, 1)
+gemm_int4g64_f16_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
+                        const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N,
+                        int64_t K, int tiles_m, int tiles_n, int per_xcd) {
+  if (!blob_header_ok(blob, 3, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
+  using C = F16Cfg<FN, FM, DEPTH>;
+  // tile order as in the integer tile kernel: each XCD walks a contiguous
+  // range of an order through blocks of 8 column tiles
+  const int o = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (o >= tiles_m * tiles_n) return;
+  const int nb = o / (8 * tiles_m), ob = o - nb * 8 * tiles_m;
+  const int nw = tiles_n - 8 * nb < 8 ? tiles_n - 8 * nb : 8;
+  const int tm = ob / nw, tn = 8 * nb + ob % nw;
+  const I4Layout L = i4_layout(N, K);
+  F16Args t;
+  t.a_codes = a_codes;
+  t.a_scales = a_scales;
+  t.wcodes = blob + L.code_off;
+  t.wscales = reinterpret_cast<const uint16_t*>(blob + L.scale_off);
+  t.M = M;
+  t.K2 = K / 2;
+  t.KB = L.KB;
+  t.NG = L.NG;
+  t.m0 = int64_t(tm) * C::BM;
+  t.g0 = int64_t(tn) * (C::BN / 16);
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * C::STAGE];
+  __shared__ __attribute__((aligned(16))) int ea_s[C::BM];
+  __shared__ __attribute__((aligned(16))) int ew_s[C::BN];
+  __shared__ int wide_s;
+  I4_LDS uint8_t* ring = (I4_LDS uint8_t*)smem;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t KS = K / 128;
+
+#pragma unroll
+  for (int s = 0; s < DEPTH - 1; ++s)
+    if (s < KS) f16_issue<FN, FM, DEPTH>(t, s, ring + s * C::STAGE, wave, lane);
+
+  // largest exponent field of each row's and column's scales (over all of K),
+  // and whether any row or column needs the per-block scaling
+  if (tid == 0) wide_s = 0;
+  __syncthreads();
+  {
+    constexpr int TPR = 256 / C::BM;
+    const int rl = tid / TPR, sub = tid % TPR;
+    int64_t row = t.m0 + rl;
+    row = row < M ? row : M - 1;
+    const uint16_t* s = a_scales + row * t.KB;
+    uint32_t mx = 0, mn = 0xFFFFu;
+    if (t.KB % 8 == 0 && (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0) {
+      for (int64_t c = sub; c < t.KB / 8; c += TPR) {
+        const uint4 v = reinterpret_cast<const uint4*>(s)[c];
+        exp_range2(mx, mn, v.x);
+        exp_range2(mx, mn, v.y);
+        exp_range2(mx, mn, v.z);
+        exp_range2(mx, mn, v.w);
+      }
+    } else {
+      for (int64_t b = sub; b < t.KB; b += TPR) exp_range1(mx, mn, s[b]);
+    }
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) {
+      const uint32_t y = uint32_t(__shfl_xor(int(mx), off));
+      const uint32_t z = uint32_t(__shfl_xor(int(mn), off));
+      mx = mx > y ? mx : y;
+      mn = mn < z ? mn : z;
+    }
+    if (sub == 0) {
+      ea_s[rl] = int(mx >> 7);
+      if (exp_wide(mx, mn)) wide_s = 1;
+    }
+  }
+  {
+    constexpr int TPO = 2048 / C::BN;  // threads per 8 columns
+    const int oc = tid / TPO, sub = tid % TPO;
+    int64_t g = t.g0 + (oc >> 1);
+    g = g < t.NG ? g : t.NG - 1;
+    const uint4* s = reinterpret_cast<const uint4*>(t.wscales) + g * t.KB * 2 + (oc & 1);
+    uint32_t mx[8], mn[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      mx[c] = 0u;
+      mn[c] = 0xFFFFu;
+    }
+    for (int64_t b = sub; b < t.KB; b += TPO) {
+      const uint4 v = s[2 * b];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        exp_range1(mx[2 * d], mn[2 * d], w[d] & 0xFFFFu);
+        exp_range1(mx[2 * d + 1], mn[2 * d + 1], w[d] >> 16);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < TPO; off <<= 1)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t y = uint32_t(__shfl_xor(int(mx[c]), off));
+        const uint32_t z = uint32_t(__shfl_xor(int(mn[c]), off));
+        mx[c] = mx[c] > y ? mx[c] : y;
+        mn[c] = mn[c] < z ? mn[c] : z;
+      }
+    if (sub == 0) {
+      bool wide = false;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        ew_s[8 * oc + c] = int(mx[c] >> 7);
+        wide = wide || exp_wide(mx[c], mn[c]);
+      }
+      if (wide) wide_s = 1;
+    }
+  }
+  __syncthreads();
+  const bool wide_tile = wide_s != 0;
+
+  const int wn = wave & 1, wm = wave >> 1, R = lane & 31, h = lane >> 5;
+  int sha[FM], shw[FN];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) sha[j] = 147 - ea_s[32 * (wm * FM + j) + R];
+#pragma unroll
+  for (int i = 0; i < FN; ++i) shw[i] = 147 - ew_s[32 * (wn * FN + i) + R];
+
+  i4v16f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  if (!wide_tile) {
+    for (int64_t s = 0; s < KS; ++s) {
+      const int64_t after = KS - 1 - s < DEPTH - 2 ? KS - 1 - s : DEPTH - 2;
+      f16_stage_ready<C::COPIES, DEPTH>(int(after));
+      const int64_t nx = s + DEPTH - 1;
+      if (nx < KS) f16_issue<FN, FM, DEPTH>(t, nx, ring + (nx % DEPTH) * C::STAGE, wave, lane);
+      f16_step<FN, FM, DEPTH>(ring + (s % DEPTH) * C::STAGE, wn, wm, lane, sha, shw, acc);
+    }
+  } else {
+    for (int64_t s = 0; s < KS; ++s) {
+      const int64_t after = KS - 1 - s < DEPTH - 2 ? KS - 1 - s : DEPTH - 2;
+      f16_stage_ready<C::COPIES, DEPTH>(int(after));
+      const int64_t nx = s + DEPTH - 1;
+      if (nx < KS) f16_issue<FN, FM, DEPTH>(t, nx, ring + (nx % DEPTH) * C::STAGE, wave, lane);
+      f16_step_wide<FN, FM, DEPTH>(ring + (s % DEPTH) * C::STAGE, wn, wm, lane, acc);
+    }
+  }
+
+  // epilogue: y = acc * 2^(ea + ew - 276) * r, rounded to BF16, staged
+  // through LDS per wave (rows of 32 FN outputs in 16-byte chunks, chunk
+  // position XOR-swizzled by row) and stored as whole 16-byte chunks
+  __builtin_amdgcn_s_waitcnt(f16_wait_encoding(0));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const float* __restrict__ r = reinterpret_cast<const float*>(blob + L.r_off);
+  constexpr int CH = 4 * FN, ROWB = 64 * FN;
+  I4_LDS uint8_t* ep = ring + wave * C::EPI_WAVE;
+  const int64_t nbase = t.g0 * 16 + wn * 32 * FN, mbase = t.m0 + wm * 32 * FM;
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int nl = 32 * i + 8 * q + 4 * h;  // within the wave tile
+      int64_t n = nbase + nl;
+      n = n < N ? n : N - 4;
+      const float4 r4 = *reinterpret_cast<const float4*>(r + n);
+      const v4i ew4 = *reinterpret_cast<const v4i*>(&ew_s[32 * wn * FN + nl]);
+      const float rr[4] = {r4.x, r4.y, r4.z, r4.w};
+      const int ew[4] = {ew4[0], ew4[1], ew4[2], ew4[3]};
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int ml = 32 * j + R;
+        const int ea = ea_s[32 * wm * FM + ml] - 276;
+        uint16_t o4[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          bf16_round_f32((wide_tile ? acc[i][j][4 * q + v] : ldexpf(acc[i][j][4 * q + v], ea + ew[v])) * rr[v],
+                         &o4[v]);
+        const int chunk = 4 * i + q;
+        *reinterpret_cast<I4_LDS i4u32x2*>(ep + ml * ROWB + ((chunk ^ (ml % CH)) * 16) + 8 * h) =
+            i4u32x2{uint32_t(o4[0]) | (uint32_t(o4[1]) << 16), uint32_t(o4[2]) | (uint32_t(o4[3]) << 16)};
+      }
+    }
+  __builtin_amdgcn_s_waitcnt(f16_wait_encoding(0));
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int qq = 0; qq < 32 * FM * CH / 64; ++qq) {
+    const int idx = qq * 64 + lane;
+    const int row = idx / CH, chunk = idx % CH;
+    const i4u32x4 v = *reinterpret_cast<const I4_LDS i4u32x4*>(ep + row * ROWB + ((chunk ^ (row % CH)) * 16));
+    const int64_t m = mbase + row, n = nbase + 8 * chunk;
+    if (m < M && n < N) *reinterpret_cast<i4u32x4*>(Y + m * N + n) = v;
+  }
+}
+
 unsigned grid_for(int64_t work) {
   const int64_t blocks = (work + 255) / 256;
   return unsigned(blocks < (int64_t(1) << 20) ? blocks : (int64_t(1) << 20));
+}
+
+
+// The fp16 kernel takes whole 128-wide K-steps; other K run the integer tile
+// kernel.  (Its 16-byte copies and stores need the operand alignment the C
+// ABI already requires: 16 bytes for codes, scales and Y, 256 for the blob.)
+bool f16_eligible(int64_t K) { return K % 128 == 0; }
+
+int64_t f16_rounds(int64_t M, int64_t N, int64_t bn, int64_t bm) {
+  const int64_t tiles = (N + bn - 1) / bn * ((M + bm - 1) / bm);
+  return (tiles + 255) / 256;
+}
+
+template <int FN, int FM, int DEPTH>
+hipError_t launch_int4g64_f16(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint16_t* as,
+                              const uint8_t* bl, uint16_t* y, hipStream_t stream) {
+  using C = F16Cfg<FN, FM, DEPTH>;
+  const int64_t tiles_n = (N + C::BN - 1) / C::BN, tiles_m = (M + C::BM - 1) / C::BM;
+  if (tiles_n * tiles_m >= (int64_t(1) << 30)) return hipErrorInvalidValue;
+  const int tiles = int(tiles_n * tiles_m), per_xcd = (tiles + 7) / 8;
+  hipLaunchKernelGGL((gemm_int4g64_f16_kernel<FN, FM, DEPTH>), dim3(unsigned(8 * per_xcd)), dim3(256), 0,
+                     stream, ac, as, bl, y, M, N, K, int(tiles_m), int(tiles_n), per_xcd);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -489,6 +1005,15 @@ hipError_t launch_linear_int4g64(int64_t M, int64_t N, int64_t K, const void* a_
     constexpr int WAVES = 8, U = 8;
     hipLaunchKernelGGL((gemm_int4g64_decode_kernel<WAVES, U>), dim3(unsigned(N / 16)),
                        dim3(64 * WAVES), 0, stream, ac, as, bl, y, M, N, K);
+  } else if (f16_eligible(K)) {
+    // the tile with the least estimated time: rounds of 256 workgroups times
+    // a K-step's cost (MFMA-bound for 256 x 256, expansion-bound below)
+    const int64_t r44 = f16_rounds(M, N, 256, 256), r42 = f16_rounds(M, N, 256, 128),
+                  r22 = f16_rounds(M, N, 128, 128);
+    const int64_t c44 = r44 * 2048, c42 = r42 * 1320, c22 = r22 * 880;
+    if (c44 <= c42 && c44 <= c22) return launch_int4g64_f16<4, 4, 4>(M, N, K, ac, as, bl, y, stream);
+    if (c42 <= c22) return launch_int4g64_f16<4, 2, 5>(M, N, K, ac, as, bl, y, stream);
+    return launch_int4g64_f16<2, 2, 6>(M, N, K, ac, as, bl, y, stream);
   } else {
     constexpr int FM = 4, FN = 4;
     const int64_t tiles_n = (N / 16 + 2 * FN - 1) / (2 * FN);
