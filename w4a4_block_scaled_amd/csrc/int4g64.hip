@@ -742,13 +742,17 @@ gemm_int4g64_f16_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __r
     return;
   }
   using C = F16Cfg<FN, FM, DEPTH>;
-  // tile order as in the integer tile kernel: each XCD walks a contiguous
-  // range of an order through blocks of 8 column tiles
+  // tile order: each XCD walks a contiguous range of an order through
+  // blocks of CW column tiles (down the rows of a block, CW wide), so the 32
+  // workgroups an XCD runs at once cover CW column tiles x 32 / CW row tiles;
+  // CW = 4 for the 256 (n) x 128 (m) tile makes that 1024 x 1024 outputs,
+  // whose weight and activation rows are fetched in equal shares
+  constexpr int CW = C::BN > C::BM ? 4 : 8;
   const int o = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
   if (o >= tiles_m * tiles_n) return;
-  const int nb = o / (8 * tiles_m), ob = o - nb * 8 * tiles_m;
-  const int nw = tiles_n - 8 * nb < 8 ? tiles_n - 8 * nb : 8;
-  const int tm = ob / nw, tn = 8 * nb + ob % nw;
+  const int nb = o / (CW * tiles_m), ob = o - nb * CW * tiles_m;
+  const int nw = tiles_n - CW * nb < CW ? tiles_n - CW * nb : CW;
+  const int tm = ob / nw, tn = CW * nb + ob % nw;
   const I4Layout L = i4_layout(N, K);
   F16Args t;
   t.a_codes = a_codes;
