@@ -464,8 +464,9 @@ def gemm_kernel_label(fmt, M):
         return ("gemm_mx_lean_kernel<mxint4> (256x256 tiles, where their rounds over the CUs are not "
                 "coarser) and gemm_mx_kernel<mxint4> (256x128 tiles)")
     if fmt == "int4g64":
-        return ("gemm_int4g64_decode_kernel" if M <= 16 else
-                "gemm_int4g64_f16_kernel (256x256 tiles for qkv and gate+up, 256x128 for o and down)")
+        if M <= 16:
+            return "gemm_int4g64_dot_kernel (VALU int4 dot products)" if M <= 3 else "gemm_int4g64_decode_kernel"
+        return "gemm_int4g64_f16_kernel (256x256 tiles for qkv and gate+up, 256x128 for o and down)"
     if fmt in ("mxfp8", "mxint8"):
         return (f"gemm_mx8_decode_kernel<{fmt}>" if M <= 16 else
                 f"gemm_mx8_tile_kernel<{fmt}, 256, 128, 2, 2, 3>")

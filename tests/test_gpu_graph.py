@@ -19,9 +19,10 @@ pytestmark = pytest.mark.gpu
 # (format, M, N, K): the persistent MXFP4 GEMM (256 x 256 tiles, 256 x 192
 # tiles, n halves), the split-K GEMM (with its workspace), the tile GEMM,
 # the decode kernels (16-feature, one-group and two-group workgroups), the
-# MXINT4 tile and small-tile GEMMs, the NVFP4 path (tensor amax pre-pass with
-# its workspace, or the one-launch quantizer; tile and decode GEMMs) and the
-# 8-bit MX formats
+# MXINT4 decode (M = 1 and 16), tile and small-tile GEMMs, the NVFP4 path (tensor amax pre-pass with
+# its workspace, or the one-launch quantizer; tile and decode GEMMs), the
+# 8-bit MX formats and INT4 G=64 (dot-product and MFMA decode kernels, the
+# fp16-expansion GEMM's 128x128 and 256x256 tiles)
 CASES = [
     ("mxfp4", 512, 49152, 512),
     ("mxfp4", 2048, 6144, 512),
@@ -32,12 +33,17 @@ CASES = [
     ("mxfp4", 8, 6144, 1024),
     ("mxfp4", 16, 16384, 1024),
     ("mxint4", 16, 2048, 1024),
+    ("mxint4", 1, 4608, 3584),
     ("mxint4", 300, 3536, 640),
     ("nvfp4", 260, 1024, 1024),
     ("nvfp4", 3, 1024, 1024),
     ("nvfp4", 16, 4096, 4096),
     ("mxfp8", 300, 1024, 512),
     ("mxint8", 8, 1024, 512),
+    ("int4g64", 1, 2048, 1024),
+    ("int4g64", 8, 1024, 1024),
+    ("int4g64", 300, 1040, 1024),
+    ("int4g64", 1100, 8000, 256),
 ]
 
 
@@ -51,7 +57,7 @@ def build(case, dev):
     x, c = to_dev(case.x, dev), to_dev(case.c, dev)
     G = w4.block_size(case.fmt)
     codes = torch.empty((case.M, w4.code_cols(case.fmt, case.K)), dtype=torch.uint8, device=dev)
-    scales = torch.empty((case.M, case.K // G), dtype=torch.uint8, device=dev)
+    scales = torch.empty((case.M, case.K // G), dtype=w4.scale_dtype(case.fmt), device=dev)
     t = torch.ones(1, dtype=torch.float32, device=dev)
     qws = torch.zeros(max(16, w4.lib().w4a4_quantize_workspace_bytes(w4.FORMATS[case.fmt], case.M, case.K)),
                       dtype=torch.uint8, device=dev)

@@ -4,8 +4,9 @@ packed deployment format, Appendix I), through the C ABI.
 Codes and scale bit patterns are compared with the oracle bit for bit; GEMM
 outputs pass gates G1 (every element within the fp32-accumulation bound) and
 G2 (row relative L2 error <= 1e-3), and are bit-exact where every partial
-sum is exact (power-of-two scales).  Shapes reach both GEMM kernels (M <= 16
-decode, M > 16 tiles) with ragged M, N and K-block counts."""
+sum is exact (power-of-two scales).  Shapes reach every GEMM kernel (M <= 3
+and K a multiple of 128 the dot-product decode kernel, M <= 16 the MFMA
+decode kernel, M > 16 the tile kernels) with ragged M, N and K-block counts."""
 import numpy as np
 import pytest
 import torch
@@ -114,7 +115,7 @@ def run_case(case, dev, label):
     return check_linear(bf16_bits(Y), y, S, case.K, label), bf16_bits(Y), bits
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 64, 130, 300])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 17, 64, 130, 300])
 @pytest.mark.parametrize("N,K", [(48, 192), (272, 1088), (528, 4096)])
 def test_linear_matches_oracle(M, N, K):
     dev = device()
@@ -124,7 +125,7 @@ def test_linear_matches_oracle(M, N, K):
     run_case(case, dev, label)
 
 
-@pytest.mark.parametrize("M,N,K", [(8, 96, 1024), (40, 160, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 96, 1024), (2, 160, 1088), (8, 96, 1024), (40, 160, 1024)])
 def test_linear_bit_exact_with_power_of_two_scales(M, N, K):
     """Activation blocks whose amax is 7 * 2^e (Delta = 2^e exactly), weight
     scales and r powers of two in a narrow range: every fp32 step is exact,
@@ -167,6 +168,23 @@ def test_full_size_llama_sampled(M, name):
     bits, y = oracle.linear_bf16(a_o, as_o, None, wc, ws, 1.0, r, FMT)
     S = oracle.linear.linear_abs_sum(a_o, as_o, None, wc, ws, 1.0, r, FMT)
     check_linear(bf16_bits(Y)[np.ix_(rows, cols)], y, S, case.K, f"full {name} M={M}")
+
+
+def test_dot_and_mfma_decode_kernels_agree():
+    """M = 3 runs the dot-product kernel and M = 4 the MFMA decode kernel;
+    on the same first three rows both meet the bound against each other and
+    repeated calls are identical."""
+    dev = device()
+    case = inputs.adhoc_case(FMT, 4, 528, 4096, seed=8)
+    (_, y4, _) = run_case(case, dev, "mfma decode")
+    case3 = inputs.adhoc_case(FMT, 4, 528, 4096, seed=8)
+    case3.M = 3
+    case3.x = case3.x[:3]
+    (_, y3, _) = run_case(case3, dev, "dot decode")
+    (_, y3b, _) = run_case(case3, dev, "dot decode again")
+    assert np.array_equal(y3, y3b)
+    diff = np.abs(F.bf16_value(y3) - F.bf16_value(y4[:3]))
+    assert diff.max() <= 2.0 ** -6 * np.abs(F.bf16_value(y4[:3])).max()
 
 
 def test_decode_and_tile_kernels_agree():

@@ -57,7 +57,7 @@ def oracle_layer(case, rows=None, cols=None):
 
 SMALL = [(1, 16, 128), (5, 272, 640), (16, 512, 1152), (17, 144, 384), (129, 272, 640),
          (300, 400, 1152), (64, 1024, 4096), (3, 528, 6144), (9, 1040, 7168), (12, 528, 14336),
-         (9, 16448, 640), (16, 16384, 4096), (7, 6176, 512)]
+         (9, 16448, 640), (16, 16384, 4096), (7, 6176, 512), (2, 1040, 1152), (2, 16448, 640)]
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -438,6 +438,134 @@ gemm_int4g64_decode_kernel(const uint8_t* __restrict__ a_codes,
   }
 }
 
+typedef _Float16 i4h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 i4v8h __attribute__((ext_vector_type(8)));
+typedef float i4v16f __attribute__((ext_vector_type(16)));
+typedef uint32_t i4u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t i4u32x2 __attribute__((ext_vector_type(2)));
+#define I4_LDS __attribute__((address_space(3)))
+
+// Decode kernel for one to three activation rows (MD = M), K a multiple of
+// 128: the MFMA's 16 activation columns would be 15/16 empty, so the block
+// dot products run on the VALU instead (v_dot8_i32_i4: 8 signed int4
+// products per lane per instruction).  A workgroup owns one 16-column group
+// g and reads its blob tiles two blocks (1 KiB, contiguous) at a time with
+// one 16-byte load per lane: lane l takes tile b + l / 32 at byte 16 (l %
+// 32), which is the fragment chunk of columns n = 2 (l % 8) and n + 1 at
+// K 64 b' + 16 c .. +16 with c = (l % 32) / 8, and the same 16 activation
+// codes of each row.  Two dot instructions per column give the exact
+// integer block sum, which joins the lane's fp32 sum once multiplied by the
+// block's Delta_a * Delta_w (exact: two BF16 values).  The WAVES waves take
+// the block pairs wave, wave + WAVES, ... with U pairs' loads in flight;
+// the eight lanes of a column pair are added by three lane exchanges and
+// the waves in wave order through LDS, so results do not depend on timing.
+template <int WAVES, int U, int MD>
+__global__ void __launch_bounds__(64 * WAVES)
+gemm_int4g64_dot_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
+                        const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N,
+                        int64_t K) {
+  if (!blob_header_ok(blob, 3, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
+  const I4Layout L = i4_layout(N, K);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = lane >> 5, c = (lane & 31) >> 3, n0 = 2 * (lane & 7);
+  const int64_t g = blockIdx.x, KP = L.KB / 2;
+  // pair p: block 2 p + t of this lane
+  const uint8_t* wtile = blob + L.code_off + (g * L.KB + t) * 512 + 16 * (lane & 31);
+  const uint16_t* wsc = reinterpret_cast<const uint16_t*>(blob + L.scale_off) + (g * L.KB + t) * 16 + n0;
+  const uint8_t* arow[MD];
+  const uint16_t* srow[MD];
+#pragma unroll
+  for (int m = 0; m < MD; ++m) {
+    arow[m] = a_codes + m * (K / 2) + t * 32 + 8 * c;
+    srow[m] = a_scales + m * L.KB + t;
+  }
+
+  float acc[MD][2];
+#pragma unroll
+  for (int m = 0; m < MD; ++m) acc[m][0] = acc[m][1] = 0.f;
+  auto pair = [&](const i4u32x4& w, uint32_t wsb, const uint2 (&a)[MD], const uint32_t (&asb)[MD]) {
+    const float sw0 = bf16_bits_to_f32(wsb & 0xFFFFu), sw1 = bf16_bits_to_f32(wsb >> 16);
+#pragma unroll
+    for (int m = 0; m < MD; ++m) {
+      const float sa = bf16_bits_to_f32(asb[m]);
+      int d0 = __builtin_amdgcn_sdot8(int(w.x), int(a[m].x), 0, false);
+      d0 = __builtin_amdgcn_sdot8(int(w.y), int(a[m].y), d0, false);
+      int d1 = __builtin_amdgcn_sdot8(int(w.z), int(a[m].x), 0, false);
+      d1 = __builtin_amdgcn_sdot8(int(w.w), int(a[m].y), d1, false);
+      acc[m][0] = fmaf(float(d0), sa * sw0, acc[m][0]);
+      acc[m][1] = fmaf(float(d1), sa * sw1, acc[m][1]);
+    }
+  };
+  int64_t p = wave;
+  for (; p + WAVES * (U - 1) < KP; p += WAVES * U) {
+    i4u32x4 w[U];
+    uint2 a[U][MD];
+    uint32_t ws[U], as[U][MD];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t pp = p + WAVES * u;
+      w[u] = __builtin_nontemporal_load(reinterpret_cast<const i4u32x4*>(wtile + pp * 1024));
+      ws[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wsc + pp * 32));
+#pragma unroll
+      for (int m = 0; m < MD; ++m) {
+        a[u][m] = *reinterpret_cast<const uint2*>(arow[m] + pp * 64);
+        as[u][m] = srow[m][2 * pp];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) pair(w[u], ws[u], a[u], as[u]);
+  }
+  for (; p < KP; p += WAVES) {
+    uint2 a[MD];
+    uint32_t as[MD];
+#pragma unroll
+    for (int m = 0; m < MD; ++m) {
+      a[m] = *reinterpret_cast<const uint2*>(arow[m] + p * 64);
+      as[m] = srow[m][2 * p];
+    }
+    pair(*reinterpret_cast<const i4u32x4*>(wtile + p * 1024), *reinterpret_cast<const uint32_t*>(wsc + p * 32), a,
+         as);
+  }
+
+  // the column pair's eight lanes (c = 0..3, t = 0, 1), in every lane
+#pragma unroll
+  for (int m = 0; m < MD; ++m)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      acc[m][e] += __shfl_xor(acc[m][e], 8);
+      acc[m][e] += __shfl_xor(acc[m][e], 16);
+      acc[m][e] += __shfl_xor(acc[m][e], 32);
+    }
+  __shared__ float part[WAVES > 1 ? WAVES - 1 : 1][MD][16];
+  if (wave > 0 && lane < 8) {
+#pragma unroll
+    for (int m = 0; m < MD; ++m) {
+      part[wave - 1][m][n0] = acc[m][0];
+      part[wave - 1][m][n0 + 1] = acc[m][1];
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && lane < 8) {
+    const float* r = reinterpret_cast<const float*>(blob + L.r_off) + g * 16 + n0;
+#pragma unroll
+    for (int m = 0; m < MD; ++m) {
+      float y0 = acc[m][0], y1 = acc[m][1];
+#pragma unroll
+      for (int w = 0; w < WAVES - 1; ++w) {
+        y0 += part[w][m][n0];
+        y1 += part[w][m][n0 + 1];
+      }
+      uint16_t o0, o1;
+      bf16_round_f32(y0 * r[0], &o0);
+      bf16_round_f32(y1 * r[1], &o1);
+      *reinterpret_cast<uint32_t*>(Y + int64_t(m) * N + g * 16 + n0) = uint32_t(o0) | (uint32_t(o1) << 16);
+    }
+  }
+}
+
 // ------------------------------------------------------ fp16 GEMM (M > 16) --
 // The block scaling moves into the operands: every code times its block's
 // scale becomes one exact fp16 value, and the fp16 MFMA (32 x 32 x 16,
@@ -480,12 +608,6 @@ gemm_int4g64_decode_kernel(const uint8_t* __restrict__ a_codes,
 // (chunks 2 (l / 32) and 2 (l / 32) + 1); MFMA t of the block uses their
 // dword t, in the same order for both operands.
 
-typedef _Float16 i4h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 i4v8h __attribute__((ext_vector_type(8)));
-typedef float i4v16f __attribute__((ext_vector_type(16)));
-typedef uint32_t i4u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t i4u32x2 __attribute__((ext_vector_type(2)));
-#define I4_LDS __attribute__((address_space(3)))
 
 struct F16Scale {
   float p2;       // 2^(E+9): the scale operand of the fp8 -> fp16 conversion
@@ -1005,7 +1127,17 @@ hipError_t launch_linear_int4g64(int64_t M, int64_t N, int64_t K, const void* a_
   const auto* as = static_cast<const uint16_t*>(a_scales);
   const auto* bl = static_cast<const uint8_t*>(blob);
   auto* y = static_cast<uint16_t*>(Y);
-  if (M <= 16) {
+  if (M <= 3 && K % 128 == 0) {
+    // up to three rows: the dot-product kernel (one 16-column group per
+    // workgroup); from four rows on the MFMA decode kernel is faster
+    const dim3 grid(unsigned(N / 16)), block(512);
+    if (M == 1)
+      hipLaunchKernelGGL((gemm_int4g64_dot_kernel<8, 8, 1>), grid, block, 0, stream, ac, as, bl, y, M, N, K);
+    else if (M == 2)
+      hipLaunchKernelGGL((gemm_int4g64_dot_kernel<8, 8, 2>), grid, block, 0, stream, ac, as, bl, y, M, N, K);
+    else
+      hipLaunchKernelGGL((gemm_int4g64_dot_kernel<8, 8, 3>), grid, block, 0, stream, ac, as, bl, y, M, N, K);
+  } else if (M <= 16) {
     constexpr int WAVES = 8, U = 8;
     hipLaunchKernelGGL((gemm_int4g64_decode_kernel<WAVES, U>), dim3(unsigned(N / 16)),
                        dim3(64 * WAVES), 0, stream, ac, as, bl, y, M, N, K);
