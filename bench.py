@@ -383,6 +383,54 @@ def decode_bandwidth(dev, steps, workload="llama_decode", Ms=(1, 4, 16), copies=
     return out
 
 
+def decode_ceiling(dev, steps, copies=32):
+    """The ceiling the decode GEMMs are compared with: at the byte count of
+    each Llama decode linear (MXFP4, M = 1), the rate of one launch that only
+    reads that many bytes once (w4a4_probe_stream_read: 16-byte non-temporal
+    loads, four in flight per lane), measured like decode_bandwidth (a HIP
+    graph over 32 distinct buffers, so none is served from the 256 MB
+    last-level cache), beside the decode GEMM of the same linear alone,
+    measured the same way; and the cost of one launch (an empty kernel)."""
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, (steps + copies - 1) // copies)
+
+    def timed(fn):
+        g = capture(fn)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / (reps * copies)
+
+    out = {"read_probe": {}, "decode_mxfp4_M1": {}}
+    for case in inputs.workload_cases("llama_decode", M=1):
+        L = Layer(case, dev)
+        L.quantize()
+        nbytes = gemm_bytes("mxfp4", 1, L.N, L.K)
+        size = int(nbytes) // 16 * 16
+        bufs = [torch.empty(size, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        us_r = timed(lambda: [w4.probe_stream_read(b, sink) for b in bufs])
+        del bufs
+        blobs = [L.blob.clone() for _ in range(copies)]
+        us_g = timed(lambda: [L.gemm(b) for b in blobs])
+        del blobs
+        rate_r, rate_g = size / (us_r * 1e-6), nbytes / (us_g * 1e-6)
+        out["read_probe"][case.name] = {"MB": round(size / 1e6, 2), "us": round(us_r, 2),
+                                        "GB/s": round(rate_r / 1e9, 1),
+                                        "frac_of_8TBps": round(rate_r / HBM_PEAK, 3)}
+        out["decode_mxfp4_M1"][case.name] = {"us": round(us_g, 2), "GB/s": round(rate_g / 1e9, 1),
+                                             "of_read_probe": round(rate_g / rate_r, 3)}
+        del L
+        torch.cuda.empty_cache()
+    out["empty_kernel_us_per_launch"] = round(timed(lambda: [w4.probe_empty(dev) for _ in range(copies)]), 2)
+    return out
+
+
 def host_cpu():
     """(cores this process may run on, CPU model string)."""
     try:
@@ -522,6 +570,8 @@ def main():
                     help="skip the other formats' prefill and decode figures")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB calibration copy and one pass of the kernels, print nothing")
+    ap.add_argument("--ceiling-probe", action="store_true",
+                    help="only the decode ceiling leg (read probe, single-linear decode GEMMs, launch cost)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path "
@@ -529,6 +579,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if a.ceiling_probe:
+        print(json.dumps({"decode_ceiling": decode_ceiling(dev, a.steps)}), flush=True)
+        return
     seed, fmt, Ms, lins = inputs.WORKLOADS[a.workload]
     M = a.M or Ms[-1]
     log(f"[bench] building {a.workload} M={M} ({fmt})")
@@ -578,6 +631,8 @@ def main():
         log("[bench] decode: MXINT4 Qwen, NVFP4 Llama at M = 1")
         out["decode_hbm_qwen_mxint4"] = decode_bandwidth(dev, a.steps, "qwen_mxint4", (1,))
         out["decode_hbm_llama_nvfp4"] = decode_bandwidth(dev, a.steps, "llama_nvfp4", (1,))
+        log("[bench] decode ceiling: read probe and single-linear decode GEMMs")
+        out["decode_ceiling"] = decode_ceiling(dev, a.steps)
     if not a.no_formats:
         # the other formats' prefill configurations, each against the peak of
         # the MFMA it runs on

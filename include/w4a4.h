@@ -362,6 +362,26 @@ w4a4_status w4a4_dualquant_solve(w4a4_format fmt, int64_t N, int64_t K,
                                  void* codes, void* scales, float* t_w,
                                  void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Measurement aids for the decode roofline (not part of the quantized
+ * linear).  w4a4_probe_stream_read reads `bytes` of device memory once, in
+ * one launch, with 16-byte non-temporal loads four in flight per lane (the
+ * decode GEMMs' access): its duration is what any kernel reading that many
+ * bytes once can reach, the ceiling the weight-streaming decode GEMMs are
+ * compared with at their own sizes.  w4a4_probe_empty launches an empty
+ * kernel (the cost of one launch).
+ *
+ *   src      device, 16-byte aligned, `bytes` readable.
+ *   bytes    a positive multiple of 16.
+ *   sink     device, 256 x 4 bytes, 4-byte aligned; written only in the
+ *            (practically impossible) case that a workgroup's XOR of its
+ *            data equals a fixed constant, which keeps the loads live.
+ * Returns W4A4_ERR_NULL, W4A4_ERR_SHAPE or W4A4_ERR_ALIGN for bad arguments;
+ * enqueued on `stream`.
+ */
+w4a4_status w4a4_probe_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+w4a4_status w4a4_probe_empty(void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* w4a4_last_error(void);
 

@@ -312,3 +312,15 @@ def test_mx8_size_queries_and_unsupported_calls():
         # 8-byte code alignment for the 8-bit quantizer
         assert L.w4a4_quantize_act(f, 4, 256, FAKE, None, ctypes.c_void_p((1 << 20) + 4), FAKE, None,
                                    None, 0, None) == 3
+
+
+def test_probe_rejects_bad_arguments():
+    """The measurement probe validates its arguments on the host."""
+    L = w4.lib()
+    fake = ctypes.c_void_p(4096)
+    assert L.w4a4_probe_stream_read(None, 1024, fake, None) == 1           # NULL src
+    assert L.w4a4_probe_stream_read(fake, 1024, None, None) == 1           # NULL sink
+    assert L.w4a4_probe_stream_read(fake, 1000, fake, None) == 2           # bytes % 16
+    assert L.w4a4_probe_stream_read(fake, 0, fake, None) == 2
+    assert L.w4a4_probe_stream_read(ctypes.c_void_p(4100), 1024, fake, None) == 3  # alignment
+

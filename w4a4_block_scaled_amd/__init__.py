@@ -80,6 +80,10 @@ def lib() -> ctypes.CDLL:
     L.w4a4_dualquant_workspace_bytes.restype = sz
     L.w4a4_dualquant_solve.argtypes = [i32, i64, i64, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.w4a4_dualquant_solve.restype = i32
+    L.w4a4_probe_stream_read.argtypes = [vp, sz, vp, vp]
+    L.w4a4_probe_stream_read.restype = i32
+    L.w4a4_probe_empty.argtypes = [vp]
+    L.w4a4_probe_empty.restype = i32
     L.w4a4_last_error.argtypes = []
     L.w4a4_last_error.restype = ctypes.c_char_p
     L.w4a4_version.argtypes = []
@@ -310,3 +314,16 @@ def linear_grouped(problems, fmt, K: int, outs=None):
                                  arr(*[_ptr(pr[3]) for pr in problems]), arr(*[_ptr(o) for o in outs]),
                                  _stream(dev)))
     return outs
+
+
+def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """w4a4_probe_stream_read: read all of `buf` (contiguous, its byte size a
+    multiple of 16) once; `sink` a device buffer of at least 1 KiB."""
+    _check(lib().w4a4_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                        _stream(buf.device)))
+
+
+def probe_empty(device) -> None:
+    """w4a4_probe_empty: one empty kernel on the current stream of `device`."""
+    _check(lib().w4a4_probe_empty(_stream(torch.device(device))))
+

@@ -361,6 +361,18 @@ w4a4_status w4a4_dualquant_solve(w4a4_format fmt, int64_t N, int64_t K, const fl
                     "dualquant_solve launch");
 }
 
+w4a4_status w4a4_probe_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return fail(W4A4_ERR_NULL, "probe_stream_read: src and sink must be non-NULL");
+  if (bytes == 0 || bytes % 16) return fail(W4A4_ERR_SHAPE, "probe_stream_read: bytes must be a positive multiple of 16");
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(W4A4_ERR_ALIGN, "probe_stream_read: src 16-byte, sink 4-byte alignment");
+  return hip_status(w4a4::launch_stream_read(src, int64_t(bytes), sink, static_cast<hipStream_t>(stream)),
+                    "probe_stream_read launch");
+}
+
+w4a4_status w4a4_probe_empty(void* stream) {
+  return hip_status(w4a4::launch_empty(static_cast<hipStream_t>(stream)), "probe_empty launch");
+}
+
 const char* w4a4_last_error(void) { return g_err; }
 
 const char* w4a4_version(void) { return "w4a4 1.0 gfx950"; }

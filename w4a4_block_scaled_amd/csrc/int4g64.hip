@@ -5,10 +5,9 @@
 // 4.2 the BF16 admissible set for INT4 scales.
 //
 // gfx950's block-scaled MFMAs take only E8M0 scales, so BF16 scales cannot
-// ride on the matrix core.  A 64-block is exactly the K of
-// V_MFMA_I32_16X16X64_I8: each block's codes go through one integer MFMA
-// (exact) and the block's scale product is applied to that partial sum in
-// fp32 before it joins the accumulator.
+// ride on the matrix core: the kernels below either fold them into exact
+// fp16 operands or apply each block's scale product to its exact integer
+// partial sum in fp32.
 //
 //   quantize  x~ = fp32(X) * c (one rounded fp32 multiply); per 64-block
 //             Delta = BF16(amax / 7) rounded once from the fp64 quotient;
@@ -17,9 +16,13 @@
 //             = rows 16 g .. +16, K 64 b .. +64, lane l owning the 8 canonical
 //             bytes of row 16 g + l % 16 at K 64 b + 16 (l / 16) .. +16,
 //             g-major; scales [N/16][K/64][16] BF16; r [N] fp32.
-//   GEMM      int4 nibbles widened to int8 as (nibble << 4), which is 16 x the
-//             signed code, so each MFMA block sum is 256 x the code dot
-//             product; the 2^-8 goes into the weight scale (exact).
+//   GEMM      M > 16 and K a multiple of 128: code x scale expanded exactly
+//             into fp16 for the fp16 MFMA (gemm_int4g64_f16_kernel below);
+//             M <= 3 (same K): block dot products on the VALU
+//             (gemm_int4g64_dot_kernel); otherwise one integer MFMA per block,
+//             int4 nibbles widened to int8 as (nibble << 4), which is 16 x
+//             the signed code, so each block sum is 256 x the code dot
+//             product (the 2^-8 goes into the epilogue, exact).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

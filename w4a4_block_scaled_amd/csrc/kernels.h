@@ -81,4 +81,9 @@ hipError_t launch_linear_int4g64(int64_t M, int64_t N, int64_t K, const void* a_
                                  const void* a_scales, const void* blob, void* Y,
                                  hipStream_t stream);
 
+// Measurement aids (probe.hip): a streaming read of `bytes` (a multiple of
+// 16) and an empty kernel.
+hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t stream);
+hipError_t launch_empty(hipStream_t stream);
+
 }  // namespace w4a4
