@@ -383,14 +383,16 @@ def decode_bandwidth(dev, steps, workload="llama_decode", Ms=(1, 4, 16), copies=
     return out
 
 
-def decode_ceiling(dev, steps, copies=32):
+def decode_ceiling(dev, steps, copies=32,
+                   workloads=(("llama_decode", "llama_mxfp4"), ("qwen_mxint4", "qwen_mxint4"),
+                              ("llama_nvfp4", "llama_nvfp4"))):
     """The ceiling the decode GEMMs are compared with: at the byte count of
-    each Llama decode linear (MXFP4, M = 1), the rate of one launch that only
-    reads that many bytes once (w4a4_probe_stream_read: 16-byte non-temporal
-    loads, four in flight per lane), measured like decode_bandwidth (a HIP
-    graph over 32 distinct buffers, so none is served from the 256 MB
-    last-level cache), beside the decode GEMM of the same linear alone,
-    measured the same way; and the cost of one launch (an empty kernel)."""
+    each decode linear (M = 1), the rate of one launch that only reads that
+    many bytes once (w4a4_probe_stream_read: 16-byte non-temporal loads, four
+    in flight per lane), measured like decode_bandwidth (a HIP graph over 32
+    distinct buffers, so none is served from the 256 MB last-level cache),
+    beside the decode GEMM of the same linear alone, measured the same way;
+    and the cost of one launch (an empty kernel)."""
     sink = torch.zeros(256, dtype=torch.int32, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = max(1, (steps + copies - 1) // copies)
@@ -407,26 +409,34 @@ def decode_ceiling(dev, steps, copies=32):
         del g
         return e0.elapsed_time(e1) * 1e3 / (reps * copies)
 
-    out = {"read_probe": {}, "decode_mxfp4_M1": {}}
-    for case in inputs.workload_cases("llama_decode", M=1):
-        L = Layer(case, dev)
-        L.quantize()
-        nbytes = gemm_bytes("mxfp4", 1, L.N, L.K)
-        size = int(nbytes) // 16 * 16
-        bufs = [torch.empty(size, dtype=torch.uint8, device=dev) for _ in range(copies)]
-        us_r = timed(lambda: [w4.probe_stream_read(b, sink) for b in bufs])
-        del bufs
-        blobs = [L.blob.clone() for _ in range(copies)]
-        us_g = timed(lambda: [L.gemm(b) for b in blobs])
-        del blobs
-        rate_r, rate_g = size / (us_r * 1e-6), nbytes / (us_g * 1e-6)
-        out["read_probe"][case.name] = {"MB": round(size / 1e6, 2), "us": round(us_r, 2),
-                                        "GB/s": round(rate_r / 1e9, 1),
-                                        "frac_of_8TBps": round(rate_r / HBM_PEAK, 3)}
-        out["decode_mxfp4_M1"][case.name] = {"us": round(us_g, 2), "GB/s": round(rate_g / 1e9, 1),
-                                             "of_read_probe": round(rate_g / rate_r, 3)}
-        del L
-        torch.cuda.empty_cache()
+    out = {}
+    for workload, key in workloads:
+        fmt = inputs.WORKLOADS[workload][1]
+        res = {"read_probe": {}, "decode_gemm_M1": {}}
+        tr = tg = total = 0.0
+        for case in inputs.workload_cases(workload, M=1):
+            L = Layer(case, dev)
+            L.quantize()
+            nbytes = gemm_bytes(fmt, 1, L.N, L.K)
+            size = int(nbytes) // 16 * 16
+            bufs = [torch.empty(size, dtype=torch.uint8, device=dev) for _ in range(copies)]
+            us_r = timed(lambda: [w4.probe_stream_read(b, sink) for b in bufs])
+            del bufs
+            blobs = [L.blob.clone() for _ in range(copies)]
+            us_g = timed(lambda: [L.gemm(b) for b in blobs])
+            del blobs
+            rate_r, rate_g = size / (us_r * 1e-6), nbytes / (us_g * 1e-6)
+            res["read_probe"][case.name] = {"MB": round(size / 1e6, 2), "us": round(us_r, 2),
+                                            "GB/s": round(rate_r / 1e9, 1),
+                                            "frac_of_8TBps": round(rate_r / HBM_PEAK, 3)}
+            res["decode_gemm_M1"][case.name] = {"us": round(us_g, 2), "GB/s": round(rate_g / 1e9, 1),
+                                                "of_read_probe": round(rate_g / rate_r, 3)}
+            tr, tg, total = tr + us_r, tg + us_g, total + nbytes
+            del L
+            torch.cuda.empty_cache()
+        res["four_linears"] = {"read_probe_us": round(tr, 2), "read_probe_frac_of_8TBps": round(total / (tr * 1e-6) / HBM_PEAK, 3),
+                               "decode_gemm_us": round(tg, 2), "gemm_of_read_probe": round(tr / tg, 3)}
+        out[key] = res
     out["empty_kernel_us_per_launch"] = round(timed(lambda: [w4.probe_empty(dev) for _ in range(copies)]), 2)
     return out
 
