@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 # tiles, n halves), the split-K GEMM (with its workspace), the tile GEMM,
 # the decode kernels (16-feature, one-group and two-group workgroups), the
 # MXINT4 decode (M = 1 and 16), tile and small-tile GEMMs, the NVFP4 path (tensor amax pre-pass with
-# its workspace, or the one-launch quantizer; tile and decode GEMMs), the
+# its workspace, or the one-launch quantizer; tile, MFMA decode and dot-product
+# decode GEMMs), the
 # 8-bit MX formats and INT4 G=64 (dot-product and MFMA decode kernels, the
 # fp16-expansion GEMM's 128x128 and 256x256 tiles)
 CASES = [
@@ -37,6 +38,7 @@ CASES = [
     ("mxint4", 300, 3536, 640),
     ("nvfp4", 260, 1024, 1024),
     ("nvfp4", 3, 1024, 1024),
+    ("nvfp4", 1, 4096, 4096),
     ("nvfp4", 16, 4096, 4096),
     ("mxfp8", 300, 1024, 512),
     ("mxint8", 8, 1024, 512),

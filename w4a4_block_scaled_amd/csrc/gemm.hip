@@ -2678,6 +2678,150 @@ hipError_t launch_nv_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, 
   return hipGetLastError();
 }
 
+// =============================================== NVFP4 dot decode kernel ==
+//
+// M = 1, NVFP4: the workgroups, waves and K-step batches of the decode
+// kernel above, but with one activation row 15 of the MFMA's 16 columns
+// would be empty while every lane still expands its activation fragment.
+// Here the workgroup first expands its activation row(s) (MD) once into
+// LDS as exact fp16 (code times E4M3 scale, as e2m1x8_scaled_f16 does), and
+// the products run on the VALU as fp16 dot products (v_dot2_f32_f16) with the
+// weight codes converted under the power of two of their block scale alone
+// (v_cvt_scalef32_pk_f16_fp4, exact); each 16-code block's fp32 partial sum
+// is then multiplied by the scale's remaining mantissa factor (1 + f/8).
+// Lane (n = l % 16, c = l / 16) holds the weight tile's 32 codes of K-chunk c
+// (blocks 2c, 2c + 1) of feature 16 g + n; the activation pairs of the same
+// codes come from LDS in the conversion's own order (both sides use the same
+// instruction on canonical bytes), so every product pairs equal K.  The four
+// lanes of a feature are added by two lane exchanges and the waves in wave
+// order through LDS.
+template <int WAVES, int U, int MD>
+__global__ __launch_bounds__(64 * WAVES) void gemm_nv_dot_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ t_act, const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y,
+    int64_t M, int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, NVFP4, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
+  const BlobLayout L = blob_layout(NVFP4, N, K);
+  const u32x4* __restrict__ Wc = reinterpret_cast<const u32x4*>(blob + L.code_off);
+  const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+  const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
+
+  const int64_t F = N / 16, per_x = (F + 7) / 8;
+  const int64_t ng = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8;
+  if (ng >= F) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane >> 4, n = lane & 15;
+  const int64_t KS = L.KS, K2 = K / 2, KB = K / 16;
+  const int64_t per = (KS + WAVES - 1) / WAVES;
+  const int64_t k_begin = wave * per;
+  const int64_t k_end = k_begin + per < KS ? k_begin + per : KS;
+  const int sw_shift = 16 * int(ng & 1);
+  const uint32_t* __restrict__ Wsg = Ws + (ng >> 1) * KS * 64 + lane;
+  const u32x4* __restrict__ Wg = Wc + ng * KS * 64 + lane;
+
+  // the first batch of weight loads goes out before the activation rows are
+  // staged, so the staging's latency overlaps them
+  u32x4 wf[U];
+  uint32_t swd[U];
+  auto load_batch = [&](int64_t kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      wf[u] = __builtin_nontemporal_load(&Wg[(kb + u) * 64]);
+      swd[u] = __builtin_nontemporal_load(&Wsg[(kb + u) * 64]) >> sw_shift;
+    }
+  };
+  if (k_begin + U <= k_end) load_batch(k_begin);
+
+  // activation rows, expanded: pair p of row m = the two codes of byte p
+  extern __shared__ __attribute__((aligned(16))) uint8_t nv_dyn[];
+  h2* act = reinterpret_cast<h2*>(nv_dyn);
+  const int64_t rowd = K / 8;  // code dwords per row
+  for (int64_t d = tid; d < MD * rowd; d += 64 * WAVES) {
+    const int64_t m = d / rowd, kd = d - m * rowd;
+    const uint32_t code = reinterpret_cast<const uint32_t*>(a_codes + m * K2)[kd];
+    const v8h v = e2m1x8_scaled_f16(code, a_scales[m * KB + kd / 2]);
+    *reinterpret_cast<v8h*>(act + m * K2 + 4 * kd) = v;
+  }
+  __syncthreads();
+
+  float acc[MD];
+#pragma unroll
+  for (int m = 0; m < MD; ++m) acc[m] = 0.f;
+  auto step = [&](const u32x4& w, uint32_t swd, int64_t ks) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float sv = __builtin_amdgcn_cvt_f32_fp8(int((swd >> (8 * b)) & 0xffu), 0);
+      const float p2 = __uint_as_float(__float_as_uint(sv) & 0xff800000u);
+      const float fr = __uint_as_float((__float_as_uint(sv) & 0x007fffffu) | 0x3f800000u);
+      h2 wv[8];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t d = w[2 * b + q];
+        wv[4 * q + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 0);
+        wv[4 * q + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 1);
+        wv[4 * q + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 2);
+        wv[4 * q + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 3);
+      }
+#pragma unroll
+      for (int m = 0; m < MD; ++m) {
+        // the 16 codes of block 2c + b: bytes 8b .. 8b + 7 of the lane's 16
+        const h2* ap = act + m * K2 + ks * 64 + 16 * c + 8 * b;
+        const v8h a0 = *reinterpret_cast<const v8h*>(ap);
+        const v8h a1 = *reinterpret_cast<const v8h*>(ap + 4);
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part = __builtin_amdgcn_fdot2(wv[i], h2{a0[2 * i], a0[2 * i + 1]}, part, false);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          part = __builtin_amdgcn_fdot2(wv[4 + i], h2{a1[2 * i], a1[2 * i + 1]}, part, false);
+        acc[m] = fmaf(part, fr, acc[m]);
+      }
+    }
+  };
+  int64_t k0 = k_begin;
+  for (; k0 + U <= k_end; k0 += U) {
+    if (k0 != k_begin) load_batch(k0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) step(wf[u], swd[u], k0 + u);
+  }
+  for (; k0 < k_end; ++k0) step(Wg[k0 * 64], Wsg[k0 * 64] >> sw_shift, k0);
+
+  // the feature's four lanes (c = 0..3): (c0 + c1) + (c2 + c3) in every lane
+#pragma unroll
+  for (int m = 0; m < MD; ++m) {
+    acc[m] += __shfl_xor(acc[m], 16);
+    acc[m] += __shfl_xor(acc[m], 32);
+  }
+  __shared__ float red[WAVES > 1 ? WAVES - 1 : 1][MD][16];
+  if (wave != 0 && c == 0) {
+#pragma unroll
+    for (int m = 0; m < MD; ++m) red[wave - 1][m][n] = acc[m];
+  }
+  __syncthreads();
+  if (wave != 0 || c != 0) return;
+  const float rf = R[ng * 16 + n] * epilogue_factor(NVFP4, t_act, blob);
+#pragma unroll
+  for (int m = 0; m < MD; ++m) {
+    float y = acc[m];
+#pragma unroll
+    for (int w = 0; w < WAVES - 1; ++w) y += red[w][m][n];
+    const uint32_t u = __float_as_uint(y * rf);
+    Y[int64_t(m) * N + ng * 16 + n] = uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  }
+}
+
+template <int WAVES, int U>
+hipError_t launch_nv_dot(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                         const float* t_act, const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  const dim3 grid(unsigned((N / 16 + 7) / 8 * 8)), block(64 * WAVES);
+  const size_t lds = size_t(M) * size_t(K) * 2;  // M = 1: at most 64 KiB
+  hipLaunchKernelGGL((gemm_nv_dot_kernel<WAVES, U, 1>), grid, block, lds, stream, ac, as, t_act, blob, Y, M, N, K);
+  return hipGetLastError();
+}
+
 // ================================================ 8-bit MX (MXFP8, MXINT8) ==
 //
 // Codes are one byte each.  A fragment lane l (row r = l % 16, group c =
@@ -3170,6 +3314,11 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
       // weight streaming; waves enough for at most 8 K-steps each, more
       // waves when there are few groups
       const int64_t ks = K / 128, groups = N / 16;
+      // one row: the dot-product kernel, its activation row expanded once
+      // per workgroup into LDS (2 K bytes); 8 waves in batches of 4 K-steps
+      // were the fastest at every Llama shape (four linears 38.4 us against
+      // 41.9 on the MFMA decode kernel); from two rows the MFMA kernel wins
+      if (M == 1 && K <= 32768) return launch_nv_dot<8, 4>(M, N, K, ac, as, t_act, blob, Y, stream);
       if (ks <= 32 && groups < 256) return launch_nv_decode<16, 2>(M, N, K, ac, as, t_act, blob, Y, stream);
       if (ks <= 32 && groups < 1024) return launch_nv_decode<8, 4>(M, N, K, ac, as, t_act, blob, Y, stream);
       if (ks <= 32) return launch_nv_decode<4, 8>(M, N, K, ac, as, t_act, blob, Y, stream);
