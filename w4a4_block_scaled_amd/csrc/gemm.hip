@@ -2579,6 +2579,122 @@ hipError_t launch_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, con
   return hipGetLastError();
 }
 
+// ============================================= MXINT4 dot decode kernel ==
+//
+// M = 1, MXINT4: the workgroups, waves and K-step batches of the decode
+// kernel above, but with one activation row the MFMA's 16 columns would be
+// 15/16 empty; the block sums are integer dot products on the VALU
+// (v_dot8_i32_i4: 8 signed int4 products per lane per instruction) and
+// nothing is widened.  The workgroup first copies the activation row's codes
+// and scale bytes into LDS (K/2 + K/32 bytes; the first batch of weight loads
+// is issued before).  Lane (n = l % 16, c = l / 16) holds the weight tile's
+// 16 bytes: half (c & 1) of block c >> 1 in bytes 0..7 and the same half of
+// block 2 + (c >> 1) in bytes 8..15, canonical nibble order (see pack.hip);
+// it reads the same two 8-byte pieces of the activation row from LDS, and
+// those two blocks' weight scales from the scale words of lanes n + 16 (c >>
+// 1) and n + 16 (2 + (c >> 1)) by lane permutation.  Each half's integer
+// sum (16 products) is exact and joins the lane's fp32 sum times
+// 2^(e_w + e_a - 254), exact; a 0xFF (NaN) scale gives NaN.  The four lanes
+// of a feature are added by two lane exchanges and the waves in wave order
+// through LDS.
+__device__ __forceinline__ float mx_pair_factor(uint32_t ew, uint32_t ea) {
+  return (ew == 0xFFu || ea == 0xFFu) ? __builtin_nanf("") : ldexpf(1.0f, int(ew + ea) - 254);
+}
+
+template <int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void gemm_mxint4_dot_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, MXINT4, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
+  const BlobLayout L = blob_layout(MXINT4, N, K);
+  const u32x4* __restrict__ Wc = reinterpret_cast<const u32x4*>(blob + L.code_off);
+  const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+  const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
+
+  const int64_t F = N / 16, per_x = (F + 7) / 8;
+  const int64_t ng = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8;
+  if (ng >= F) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane >> 4, n = lane & 15, half = c >> 1;
+  const int64_t KS = L.KS, K2 = K / 2;
+  const int64_t per = (KS + WAVES - 1) / WAVES;
+  const int64_t k_begin = wave * per;
+  const int64_t k_end = k_begin + per < KS ? k_begin + per : KS;
+  const int sw_shift = 8 * int(ng & 3);
+  const u32x4* __restrict__ Wg = Wc + ng * KS * 64 + lane;
+  const uint32_t* __restrict__ Wsg = Ws + (ng >> 2) * KS * 64 + lane;
+  const int src_lo = 4 * (n + 16 * half), src_hi = src_lo + 128;
+  const int off = 16 * half + 8 * (c & 1);
+
+  u32x4 wf[U];
+  uint32_t wsw[U];
+  auto load_batch = [&](int64_t kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      wf[u] = __builtin_nontemporal_load(&Wg[(kb + u) * 64]);
+      wsw[u] = __builtin_nontemporal_load(&Wsg[(kb + u) * 64]);
+    }
+  };
+  if (k_begin + U <= k_end) load_batch(k_begin);
+
+  // the activation row: codes (K/2 bytes) then scale bytes (K/32), copied
+  extern __shared__ __attribute__((aligned(16))) uint8_t mx_dyn[];
+  for (int64_t d = tid; d < K2 / 16; d += 64 * WAVES)
+    reinterpret_cast<u32x4*>(mx_dyn)[d] = reinterpret_cast<const u32x4*>(a_codes)[d];
+  for (int64_t d = tid; d < K / 128; d += 64 * WAVES)
+    reinterpret_cast<uint32_t*>(mx_dyn + K2)[d] = reinterpret_cast<const uint32_t*>(a_scales)[d];
+  __syncthreads();
+  const uint8_t* act = mx_dyn;
+  const uint32_t* asc = reinterpret_cast<const uint32_t*>(mx_dyn + K2);
+
+  float acc = 0.f;
+  auto step = [&](const u32x4& w, uint32_t sw_own, int64_t ks) {
+    const uint32_t wl = uint32_t(__builtin_amdgcn_ds_bpermute(src_lo, int(sw_own)));
+    const uint32_t wh = uint32_t(__builtin_amdgcn_ds_bpermute(src_hi, int(sw_own)));
+    const u32x2 alo = *reinterpret_cast<const u32x2*>(act + ks * 64 + off);
+    const u32x2 ahi = *reinterpret_cast<const u32x2*>(act + ks * 64 + 32 + off);
+    const uint32_t asw = asc[ks];
+    int dl = __builtin_amdgcn_sdot8(int(w.x), int(alo.x), 0, false);
+    dl = __builtin_amdgcn_sdot8(int(w.y), int(alo.y), dl, false);
+    int dh = __builtin_amdgcn_sdot8(int(w.z), int(ahi.x), 0, false);
+    dh = __builtin_amdgcn_sdot8(int(w.w), int(ahi.y), dh, false);
+    acc = fmaf(float(dl), mx_pair_factor((wl >> sw_shift) & 0xFFu, (asw >> (8 * half)) & 0xFFu), acc);
+    acc = fmaf(float(dh), mx_pair_factor((wh >> sw_shift) & 0xFFu, (asw >> (8 * (2 + half))) & 0xFFu), acc);
+  };
+  int64_t k0 = k_begin;
+  for (; k0 + U <= k_end; k0 += U) {
+    if (k0 != k_begin) load_batch(k0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) step(wf[u], wsw[u], k0 + u);
+  }
+  for (; k0 < k_end; ++k0) step(Wg[k0 * 64], Wsg[k0 * 64], k0);
+
+  // the feature's four lanes (c = 0..3): (c0 + c1) + (c2 + c3) in every lane
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  __shared__ float red[WAVES > 1 ? WAVES - 1 : 1][16];
+  if (wave != 0 && c == 0) red[wave - 1][n] = acc;
+  __syncthreads();
+  if (wave != 0 || c != 0) return;
+  float y = acc;
+#pragma unroll
+  for (int w = 0; w < WAVES - 1; ++w) y += red[w][n];
+  const uint32_t u = __float_as_uint(y * R[ng * 16 + n]);
+  Y[ng * 16 + n] = uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int WAVES, int U>
+hipError_t launch_mxint4_dot(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                             const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  const size_t lds = size_t(K) / 2 + size_t(K) / 32;
+  hipLaunchKernelGGL((gemm_mxint4_dot_kernel<WAVES, U>), dim3(unsigned((N / 16 + 7) / 8 * 8)), dim3(64 * WAVES),
+                     lds, stream, ac, as, blob, Y, M, N, K);
+  return hipGetLastError();
+}
+
 // ================================================= NVFP4 decode kernel ==
 //
 // M <= 16, NVFP4: weight streaming like the MXINT4 decode kernel (one
@@ -3315,10 +3431,15 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
       // waves when there are few groups
       const int64_t ks = K / 128, groups = N / 16;
       // one row: the dot-product kernel, its activation row expanded once
-      // per workgroup into LDS (2 K bytes); 8 waves in batches of 4 K-steps
-      // were the fastest at every Llama shape (four linears 38.4 us against
-      // 41.9 on the MFMA decode kernel); from two rows the MFMA kernel wins
-      if (M == 1 && K <= 32768) return launch_nv_dot<8, 4>(M, N, K, ac, as, t_act, blob, Y, stream);
+      // per workgroup into LDS (2 K bytes); 16 waves in batches of 2 K-steps
+      // when there are few groups (Llama QKV, O, down), 8 waves in batches
+      // of 4 with many (gate+up): the fastest of the seven configurations
+      // measured at each shape (four linears 37.3 us against 41.9 on the
+      // MFMA decode kernel); from two rows the MFMA kernel wins
+      if (M == 1 && K <= 32768) {
+        if (groups < 1024) return launch_nv_dot<16, 2>(M, N, K, ac, as, t_act, blob, Y, stream);
+        return launch_nv_dot<8, 4>(M, N, K, ac, as, t_act, blob, Y, stream);
+      }
       if (ks <= 32 && groups < 256) return launch_nv_decode<16, 2>(M, N, K, ac, as, t_act, blob, Y, stream);
       if (ks <= 32 && groups < 1024) return launch_nv_decode<8, 4>(M, N, K, ac, as, t_act, blob, Y, stream);
       if (ks <= 32) return launch_nv_decode<4, 8>(M, N, K, ac, as, t_act, blob, Y, stream);
@@ -3376,6 +3497,14 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
       // one batch overlap the loads of the next (Qwen down, K = 18944: 12.5
       // -> 9.8 us against one batch of 10)
       const int64_t ks = K / 128, groups = N / 16;
+      // one row: the dot-product kernel, K-steps in batches of 2; 16 waves
+      // when there are few groups (Qwen QKV, O, down: 4.9, 4.3, 9.2 us), 8
+      // with many (gate+up: 14.8 us); the six configurations measured put
+      // these first at each shape
+      if (M == 1 && K <= 65536) {
+        if (groups < 1024) return launch_mxint4_dot<16, 2>(M, N, K, ac, as, blob, Y, stream);
+        return launch_mxint4_dot<8, 2>(M, N, K, ac, as, blob, Y, stream);
+      }
       if (ks <= 32 && groups < 256) return launch_decode<FMT, 16, 2>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 32 && groups < 1024) return launch_decode<FMT, 8, 4>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 28) return launch_decode<FMT, 4, 7>(M, N, K, ac, as, blob, Y, stream);
