@@ -42,6 +42,8 @@ CASES = [
     ("nvfp4", 16, 4096, 4096),
     ("mxfp8", 300, 1024, 512),
     ("mxint8", 8, 1024, 512),
+    ("mxint8", 1, 4096, 4096),
+    ("mxfp8", 3, 4096, 4096),
     ("int4g64", 1, 2048, 1024),
     ("int4g64", 8, 1024, 1024),
     ("int4g64", 300, 1040, 1024),

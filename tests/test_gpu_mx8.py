@@ -121,7 +121,24 @@ def test_mx8_pack_fragment_order():
 
 
 SMALL = [(1, 16, 128), (5, 272, 640), (16, 512, 1152), (17, 144, 384), (129, 272, 640),
-         (300, 400, 1152), (64, 1024, 4096), (3, 528, 6144), (2, 64, 14336)]
+         (300, 400, 1152), (64, 1024, 4096), (3, 528, 6144), (2, 64, 14336),
+         (1, 1040, 1152), (2, 528, 1152), (3, 1040, 1152)]
+
+# one to three rows take the dot-product kernel while the rows (MXINT8: K
+# bytes, MXFP8: 2K) and their K/32 scale bytes fit 64 KiB of LDS, the MFMA
+# decode kernel beyond: the K on either side of that bound
+LDS_BOUND = {"mxfp8": [(1, 32, 32256), (1, 32, 32384), (3, 32, 10752), (3, 32, 10880)],
+             "mxint8": [(1, 16, 63488), (1, 16, 63616), (3, 16, 21120), (3, 16, 21248)]}
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [(f,) + s for f in FMTS for s in LDS_BOUND[f]])
+def test_mx8_dot_kernel_lds_bound(fmt, M, N, K):
+    dev = device()
+    say(f"[mx8 lds bound] {fmt} M={M} N={N} K={K}")
+    case = inputs.adhoc_case(fmt, M, N, K, seed=M + N + K)
+    Y, *_ = gpu_layer(case, dev)
+    y, S, _, _ = oracle_layer(case)
+    check_linear(bf16_bits(Y), y, S, K, f"{fmt} {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -142,7 +159,7 @@ def test_mx8_linear_random_codes(fmt):
     subnormals and +-448; every int8 incl. -128) and widely spread block
     scales, through both kernels."""
     dev = device()
-    for M in (7, 150):
+    for M in (1, 3, 7, 150):
         say(f"[mx8 random codes] {fmt} M={M}")
         case = inputs.adhoc_case(fmt, M, 272, 1024, seed=40 + M, weights="codes")
         Y, *_ = gpu_layer(case, dev)
@@ -155,7 +172,9 @@ E4M3_INTS = [0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50, 0x51, 0x52, 0
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [("mxfp8", 16, 256, 4096), ("mxfp8", 200, 272, 4096),
-                                       ("mxint8", 5, 64, 512), ("mxint8", 130, 272, 512)])
+                                       ("mxint8", 5, 64, 512), ("mxint8", 130, 272, 512),
+                                       ("mxfp8", 1, 1040, 4096), ("mxfp8", 3, 16400, 1152),
+                                       ("mxint8", 1, 1040, 512), ("mxint8", 3, 16400, 640)])
 def test_mx8_bit_exact_when_accumulation_is_exact(fmt, M, N, K):
     """Equal block scales per operand and element values that keep every
     partial sum an integer below 2^24 (MXFP8: the integers -16..16, so
@@ -195,8 +214,24 @@ def test_mx8_decode_and_tile_kernels_agree(fmt):
     check_linear(bf16_bits(Y40[:16]), y, S, case.K, "tile")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mx8_dot_and_decode_kernels_agree(fmt):
+    """Three activation rows go through the VALU dot-product kernel, four
+    through the MFMA decode kernel: the first three rows' outputs of both
+    pass G1/G2 against the oracle."""
+    dev = device()
+    case = inputs.adhoc_case(fmt, 4, 4096, 4096, seed=12)
+    Y4, blob, (ac, as_, ta), _ = gpu_layer(case, dev)
+    Y3 = w4.linear(ac[:3].contiguous(), as_[:3].contiguous(), ta, blob, fmt, case.N, case.K)
+    torch.cuda.synchronize()
+    y, S, _, _ = oracle_layer(case, rows=np.arange(3))
+    check_linear(bf16_bits(Y3), y, S, case.K, "dot")
+    check_linear(bf16_bits(Y4[:3]), y, S, case.K, "decode")
+
+
 @pytest.mark.parametrize("workload,M", [("llama_mxfp8", 2048), ("llama_mxfp8", 1),
-                                        ("llama_mxint8", 2048), ("llama_mxint8", 1)])
+                                        ("llama_mxint8", 2048), ("llama_mxint8", 1),
+                                        ("llama_mxfp8", 3), ("llama_mxint8", 3)])
 def test_mx8_workload_full_size(workload, M):
     """Every Llama linear at full size in the launch configuration the
     benchmark times: the weight codes and scales the GPU quantizer made from

@@ -3172,6 +3172,193 @@ hipError_t launch_mx8_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac,
   return hipGetLastError();
 }
 
+// M <= 3: the weight tile streamed as by gemm_mx8_decode_kernel, the sums on
+// the VALU instead of the MFMA.  Lane (n = l % 16, c = l / 16) holds the
+// tile's 32 bytes: K 16c .. +16 (in block c >> 1) and 64 + 16c .. +16 (in
+// block 2 + (c >> 1)); the two blocks' weight scales come from the scale
+// words of lanes n + 16 (c >> 1) and n + 16 (2 + (c >> 1)) by lane
+// permutation.  The MD activation rows are copied once per workgroup into
+// LDS, then their block scales:
+//   MXINT8: the code bytes as they are; v_dot4_i32_i8 adds four products, so
+//           each half's sum (16 products, |sum| < 2^19) is an exact integer;
+//   MXFP8 : the codes expanded to fp16 (every E4M3 value is an fp16 value,
+//           subnormals included); the weight codes expanded the same way and
+//           v_dot2_f32_f16 adds two exact products into the fp32 sum.
+// Each half's sum joins the fp32 sum of its row times 2^(e_w + e_a - 254)
+// (NaN for a 0xFF scale).  The four lanes of a feature are added by two lane
+// exchanges and the waves in wave order through LDS.
+template <int FMT>
+__host__ __device__ constexpr int64_t mx8_dot_row_bytes(int64_t K) {
+  return (FMT == MXFP8 ? 2 * K : K) + K / 32;
+}
+
+template <int FMT, int WAVES, int U, int MD>
+__global__ __launch_bounds__(64 * WAVES) void gemm_mx8_dot_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  static_assert(FMT == MXFP8 || FMT == MXINT8, "8-bit MX formats");
+  if (!blob_header_ok(blob, FMT, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
+  const BlobLayout L = blob_layout(FMT, N, K);
+  const u32x4* __restrict__ Wc = reinterpret_cast<const u32x4*>(blob + L.code_off);
+  const uint32_t* __restrict__ Ws = reinterpret_cast<const uint32_t*>(blob + L.scale_off);
+  const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
+
+  const int64_t F = N / 16, per_x = (F + 7) / 8;
+  const int64_t ng = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8;
+  if (ng >= F) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane >> 4, n = lane & 15, half = c >> 1;
+  const int64_t KS = L.KS;
+  const int64_t per = (KS + WAVES - 1) / WAVES;
+  const int64_t k_begin = wave * per;
+  const int64_t k_end = k_begin + per < KS ? k_begin + per : KS;
+  const int sw_shift = 8 * int(ng & 3);
+  const u32x4* __restrict__ Wg = Wc + (ng * KS * 64 + lane) * 2;   // the lane's two 16-byte halves
+  const uint32_t* __restrict__ Wsg = Ws + (ng >> 2) * KS * 64 + lane;
+  const int src_lo = 4 * (n + 16 * half), src_hi = src_lo + 128;
+
+  // the first batch of weight loads goes out before the activation rows are
+  // staged, so the staging's latency overlaps them
+  u32x4 w0[U], w1[U];
+  uint32_t wsw[U];
+  auto load_batch = [&](int64_t kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      w0[u] = __builtin_nontemporal_load(&Wg[(kb + u) * 128]);
+      w1[u] = __builtin_nontemporal_load(&Wg[(kb + u) * 128 + 1]);
+      wsw[u] = __builtin_nontemporal_load(&Wsg[(kb + u) * 64]);
+    }
+  };
+  if (k_begin + U <= k_end) load_batch(k_begin);
+
+  // LDS: MD rows of codes (MXINT8: K bytes each; MXFP8: K fp16 values), then
+  // MD rows of K/32 scale bytes
+  extern __shared__ __attribute__((aligned(16))) uint8_t mx8_dyn[];
+  const int64_t code_row = FMT == MXFP8 ? 2 * K : K;
+  for (int64_t d = tid; d < MD * (K / 16); d += 64 * WAVES) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(a_codes)[d];
+    if constexpr (FMT == MXINT8) {
+      reinterpret_cast<u32x4*>(mx8_dyn)[d] = v;
+    } else {
+      h2* dst = reinterpret_cast<h2*>(mx8_dyn) + 8 * d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dst[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[i], 1.0f, false);
+        dst[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[i], 1.0f, true);
+      }
+    }
+  }
+  for (int64_t d = tid; d < MD * (K / 128); d += 64 * WAVES)
+    reinterpret_cast<uint32_t*>(mx8_dyn + MD * code_row)[d] = reinterpret_cast<const uint32_t*>(a_scales)[d];
+  __syncthreads();
+  const uint32_t* asc = reinterpret_cast<const uint32_t*>(mx8_dyn + MD * code_row);
+
+  float acc[MD];
+#pragma unroll
+  for (int m = 0; m < MD; ++m) acc[m] = 0.f;
+  auto step = [&](const u32x4& a_w, const u32x4& b_w, uint32_t sw_own, int64_t ks) {
+    const uint32_t wl = uint32_t(__builtin_amdgcn_ds_bpermute(src_lo, int(sw_own)));
+    const uint32_t wh = uint32_t(__builtin_amdgcn_ds_bpermute(src_hi, int(sw_own)));
+    const uint32_t ewl = (wl >> sw_shift) & 0xFFu, ewh = (wh >> sw_shift) & 0xFFu;
+    if constexpr (FMT == MXINT8) {
+#pragma unroll
+      for (int m = 0; m < MD; ++m) {
+        const uint8_t* row = mx8_dyn + m * K + ks * 128 + 16 * c;
+        const u32x4 alo = *reinterpret_cast<const u32x4*>(row);
+        const u32x4 ahi = *reinterpret_cast<const u32x4*>(row + 64);
+        const uint32_t asw = asc[m * (K / 128) + ks];
+        int dl = 0, dh = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dl = __builtin_amdgcn_sdot4(int(a_w[i]), int(alo[i]), dl, false);
+          dh = __builtin_amdgcn_sdot4(int(b_w[i]), int(ahi[i]), dh, false);
+        }
+        acc[m] = fmaf(float(dl), mx_pair_factor(ewl, (asw >> (8 * half)) & 0xFFu), acc[m]);
+        acc[m] = fmaf(float(dh), mx_pair_factor(ewh, (asw >> (8 * (2 + half))) & 0xFFu), acc[m]);
+      }
+    } else {
+      h2 wv[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wv[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a_w[i], 1.0f, false);
+        wv[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a_w[i], 1.0f, true);
+        wv[8 + 2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b_w[i], 1.0f, false);
+        wv[8 + 2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b_w[i], 1.0f, true);
+      }
+#pragma unroll
+      for (int m = 0; m < MD; ++m) {
+        const h2* row = reinterpret_cast<const h2*>(mx8_dyn + m * code_row) + ks * 64 + 8 * c;
+        const uint32_t asw = asc[m * (K / 128) + ks];
+        float pl = 0.f, ph = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const v8h lo = *reinterpret_cast<const v8h*>(row + 4 * j);
+          const v8h hi = *reinterpret_cast<const v8h*>(row + 32 + 4 * j);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pl = __builtin_amdgcn_fdot2(wv[4 * j + i], h2{lo[2 * i], lo[2 * i + 1]}, pl, false);
+            ph = __builtin_amdgcn_fdot2(wv[8 + 4 * j + i], h2{hi[2 * i], hi[2 * i + 1]}, ph, false);
+          }
+        }
+        acc[m] = fmaf(pl, mx_pair_factor(ewl, (asw >> (8 * half)) & 0xFFu), acc[m]);
+        acc[m] = fmaf(ph, mx_pair_factor(ewh, (asw >> (8 * (2 + half))) & 0xFFu), acc[m]);
+      }
+    }
+  };
+  int64_t k0 = k_begin;
+  for (; k0 + U <= k_end; k0 += U) {
+    if (k0 != k_begin) load_batch(k0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) step(w0[u], w1[u], wsw[u], k0 + u);
+  }
+  for (; k0 < k_end; ++k0) step(Wg[k0 * 128], Wg[k0 * 128 + 1], Wsg[k0 * 64], k0);
+
+#pragma unroll
+  for (int m = 0; m < MD; ++m) {
+    acc[m] += __shfl_xor(acc[m], 16);
+    acc[m] += __shfl_xor(acc[m], 32);
+  }
+  __shared__ float red[WAVES > 1 ? WAVES - 1 : 1][MD][16];
+  if (wave != 0 && c == 0) {
+#pragma unroll
+    for (int m = 0; m < MD; ++m) red[wave - 1][m][n] = acc[m];
+  }
+  __syncthreads();
+  if (wave != 0 || c != 0) return;
+  const float rn = R[ng * 16 + n];
+#pragma unroll
+  for (int m = 0; m < MD; ++m) {
+    float y = acc[m];
+#pragma unroll
+    for (int w = 0; w < WAVES - 1; ++w) y += red[w][m][n];
+    const uint32_t u = __float_as_uint(y * rn);
+    Y[int64_t(m) * N + ng * 16 + n] = uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  }
+}
+
+// dynamic LDS the dot kernels may take (activation rows and their scales)
+constexpr int64_t kMx8DotLds = 64 * 1024;
+
+template <int FMT, int WAVES, int U, int MD>
+hipError_t launch_mx8_dot_md(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                             const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  const size_t lds = size_t(MD * mx8_dot_row_bytes<FMT>(K));
+  hipLaunchKernelGGL((gemm_mx8_dot_kernel<FMT, WAVES, U, MD>), dim3(unsigned((N / 16 + 7) / 8 * 8)),
+                     dim3(64 * WAVES), lds, stream, ac, as, blob, Y, M, N, K);
+  return hipGetLastError();
+}
+
+template <int FMT, int WAVES, int U>
+hipError_t launch_mx8_dot(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint8_t* as,
+                          const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  if (M == 1) return launch_mx8_dot_md<FMT, WAVES, U, 1>(M, N, K, ac, as, blob, Y, stream);
+  if (M == 2) return launch_mx8_dot_md<FMT, WAVES, U, 2>(M, N, K, ac, as, blob, Y, stream);
+  return launch_mx8_dot_md<FMT, WAVES, U, 3>(M, N, K, ac, as, blob, Y, stream);
+}
+
 // ------------------------------------------------------ 8-bit tiled (M > 16)
 //
 // Workgroup tile BN (n) x BM (m) with WN x WM waves; one 128-wide K-step per
@@ -3417,6 +3604,11 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
       // weight streaming; waves enough for at most 8 K-steps each, more
       // waves when there are few groups
       const int64_t ks = K / 128, groups = N / 16;
+      // up to three rows: dot products on the VALU (the rows in LDS)
+      if (M <= 3 && M * mx8_dot_row_bytes<FMT>(K) <= kMx8DotLds) {
+        if (groups < 1024) return launch_mx8_dot<FMT, 16, 2>(M, N, K, ac, as, blob, Y, stream);
+        return launch_mx8_dot<FMT, 8, 2>(M, N, K, ac, as, blob, Y, stream);
+      }
       if (ks <= 32 && groups < 256) return launch_mx8_decode<FMT, 16, 2>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 32 && groups < 1024) return launch_mx8_decode<FMT, 8, 4>(M, N, K, ac, as, blob, Y, stream);
       if (ks <= 32) return launch_mx8_decode<FMT, 4, 8>(M, N, K, ac, as, blob, Y, stream);
