@@ -518,7 +518,8 @@ def gemm_kernel_label(fmt, M):
                 "K >= 8192) and gemm_fp4_kernel (the others)")
     if fmt == "mxint4":
         if M <= 16:
-            return "gemm_decode_kernel<mxint4>"
+            return ("gemm_mxint4_dot_kernel (VALU int4 dot products)" if M == 1 else
+                    "gemm_decode_kernel<mxint4>")
         return ("gemm_mx_lean_kernel<mxint4> (256x256 tiles, where their rounds over the CUs are not "
                 "coarser) and gemm_mx_kernel<mxint4> (256x128 tiles)")
     if fmt == "int4g64":
@@ -526,8 +527,13 @@ def gemm_kernel_label(fmt, M):
             return "gemm_int4g64_dot_kernel (VALU int4 dot products)" if M <= 3 else "gemm_int4g64_decode_kernel"
         return "gemm_int4g64_f16_kernel (256x256 tiles for qkv and gate+up, 256x128 for o and down)"
     if fmt in ("mxfp8", "mxint8"):
+        if M <= 3:
+            return (f"gemm_mx8_dot_kernel<{fmt}> (VALU dot products; gemm_mx8_decode_kernel where the "
+                    "rows exceed 64 KiB of LDS)")
         return (f"gemm_mx8_decode_kernel<{fmt}>" if M <= 16 else
                 f"gemm_mx8_tile_kernel<{fmt}, 256, 128, 2, 2, 3>")
+    if M == 1:
+        return "gemm_nv_dot_kernel (VALU fp16 dot products)"
     return "gemm_nv_decode_kernel" if M <= 16 else "gemm_tile_kernel<nvfp4>"
 
 
