@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY.  A plain, slow, fp64 restatement of DualQuant's
 inference-time computation (Section 4.4 with the formats of Section 3):
 rescale the activations by the column scales, quantize them to MXFP4 /
 NVFP4 / MXINT4 blocks (or INT4 blocks of 64 with BF16 scales, or the 8-bit
-MXFP8 / MXINT8 blocks), multiply with the quantized weights and apply the row
-scales, rounding the result once to BF16.
+MXFP8 / MXINT8 blocks and INT8 blocks of 128 with BF16 scales), multiply
+with the quantized weights and apply the row scales, rounding the result
+once to BF16.
 
 Only tests/, the smoke check in __graft_entry__.py and the CPU-baseline leg
 of bench.py may import this package.  It shares no code with the HIP path

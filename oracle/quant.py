@@ -35,6 +35,15 @@ What is computed (DualQuant):
   quotient; code = clip(RNE(x~ / Delta), -8, 7) decided exactly (ties to
   the even integer); an all-zero block (or one whose Delta rounds to 0)
   gets Delta = 0 and zero codes.
+* INT8 with G = 128 and BF16 block scales (Appendix G.2, Table 9's 8-bit
+  integer W+A variant, G = 128 on both operands): Section 3's symmetric scale
+  with q_max = 127, Delta = BF16(amax / 127) rounded once to nearest even
+  from the exact quotient (BF16 scales read as for INT4 G=64: the pages give
+  no other scale format for the integer grid); code = clip(RNE(x~ / Delta),
+  -128, 127), the whole two's-complement grid (only a subnormal Delta, which
+  rounds far from amax / 127, can take a code past +-127); zero blocks and
+  non-finite blocks as for INT4 G=64.  Codes are stored one byte per
+  element, [rows, K].
 * 8-bit MX formats (Appendix G.2, Table 9: MXFP8 and MXINT8 with G = 32 and
   E8M0 scales), with the same OCP shared-exponent rule: MXFP8 elements are
   E4M3 (emax_elem = 8, 448 = 1.75 * 2^8), code = RNE_E4M3(x~ * 2^-e)
@@ -43,13 +52,13 @@ What is computed (DualQuant):
   code = clip(RNE(x~ * 2^-e), -128, 127) (the OCP fixed-point convention
   with 6 fraction bits gives the same values with the scale byte 6 higher).
   Codes are stored one byte per element, [rows, K].
-* MX and INT4 G=64 blocks holding a non-finite value get scale byte 0xFF
-  (BF16 0x7FC0) and zero codes (inputs are expected finite; this only fixes
-  what happens otherwise).
+* MX and INT4 G=64 / INT8 G=128 blocks holding a non-finite value get scale
+  byte 0xFF (BF16 0x7FC0) and zero codes (inputs are expected finite; this
+  only fixes what happens otherwise).
 
 Canonical storage: codes [rows, K/2] bytes, element 2j in the low nibble of
 byte j and 2j+1 in the high nibble; scales [rows, K/G] bytes, row-major
-(uint16 BF16 bit patterns for INT4 G=64).
+(uint16 BF16 bit patterns for INT4 G=64 and INT8 G=128).
 """
 from __future__ import annotations
 
@@ -57,10 +66,14 @@ import numpy as np
 
 from . import formats as F
 
-BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32, "int4g64": 64, "mxfp8": 32, "mxint8": 32}
+BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32, "int4g64": 64, "mxfp8": 32, "mxint8": 32,
+         "int8g128": 128}
 MX_FORMATS = ("mxfp4", "mxint4", "mxfp8", "mxint8")
-CODE_BITS = {"mxfp4": 4, "nvfp4": 4, "mxint4": 4, "int4g64": 4, "mxfp8": 8, "mxint8": 8}
+CODE_BITS = {"mxfp4": 4, "nvfp4": 4, "mxint4": 4, "int4g64": 4, "mxfp8": 8, "mxint8": 8,
+             "int8g128": 8}
+BF16_SCALED = ("int4g64", "int8g128")   # integer grids with BF16 block scales
 INT4_QMAX = 7                      # symmetric INT4 grid maximum
+INT8_QMAX = 127                    # symmetric INT8 grid maximum
 # floor(log2) of the largest element magnitude of each MX element grid:
 # E2M1 6 = 1.5 * 2^2; int4 7 < 2^3; E4M3 448 = 1.75 * 2^8; int8 127 < 2^7
 EMAX_ELEM = {"mxfp4": 2, "mxint4": 2, "mxfp8": 8, "mxint8": 6}
@@ -113,13 +126,14 @@ def _quantize_chunk(xt, fmt, t):
             codes = F.int4_encode(np.clip(np.rint(v), -8, 7))
         scales = np.where(nonfinite, np.uint8(255), scales)
         codes = np.where(nonfinite[..., None], np.uint8(0), codes)
-    elif fmt == "int4g64":
+    elif fmt in BF16_SCALED:
+        qmax = INT4_QMAX if fmt == "int4g64" else INT8_QMAX
         nonfinite = ~np.isfinite(blocks).all(axis=-1)
         amax = np.where(nonfinite, 0.0, amax)
-        # amax / 7 in fp64 then one rounding to BF16: the fp64 quotient can only
-        # land on a BF16 midpoint when the exact quotient is that midpoint, so
-        # this is the single correct rounding of amax / 7
-        bits = F.bf16_from_f64(amax / INT4_QMAX)
+        # amax / q_max in fp64 then one rounding to BF16: the fp64 quotient can
+        # only land on a BF16 midpoint when the exact quotient is that
+        # midpoint, so this is the single correct rounding of amax / q_max
+        bits = F.bf16_from_f64(amax / qmax)
         delta = F.bf16_value(bits)
         live = delta > 0
         # x~ (24 bits) / Delta (8 bits) in fp64: a quotient that is not a
@@ -128,7 +142,10 @@ def _quantize_chunk(xt, fmt, t):
         with np.errstate(invalid="ignore", over="ignore"):
             v = np.where(live[..., None] & np.isfinite(blocks),
                          blocks / np.where(live, delta, 1.0)[..., None], 0.0)
-        codes = F.int4_encode(np.clip(np.rint(v), -8, 7))
+        if fmt == "int4g64":
+            codes = F.int4_encode(np.clip(np.rint(v), -8, 7))
+        else:
+            codes = F.int8_encode(np.clip(np.rint(v), -128, 127))
         scales = np.where(nonfinite, np.uint16(0x7FC0), np.where(live, bits, np.uint16(0)))
         codes = np.where(nonfinite[..., None], np.uint8(0), codes)
         return codes.reshape(R, K).astype(np.uint8), scales.astype(np.uint16)
@@ -161,7 +178,7 @@ def quantize_rows(xt, fmt, t=None):
     if fmt == "nvfp4" and t is None:
         t = nv_tensor_scale(xt)
     codes = np.empty((R, K), np.uint8)
-    scales = np.empty((R, K // G), np.uint16 if fmt == "int4g64" else np.uint8)
+    scales = np.empty((R, K // G), np.uint16 if fmt in BF16_SCALED else np.uint8)
     for r0 in range(0, R, ROW_CHUNK):
         codes[r0:r0 + ROW_CHUNK], scales[r0:r0 + ROW_CHUNK] = \
             _quantize_chunk(xt[r0:r0 + ROW_CHUNK], fmt, t)
@@ -223,11 +240,11 @@ def dequantize(packed, scales, fmt):
         elem = F.int4_value(codes)
     elif fmt == "mxfp8":
         elem = F.e4m3_value(codes)
-    elif fmt == "mxint8":
+    elif fmt in ("mxint8", "int8g128"):
         elem = F.int8_value(codes)
     else:
         elem = F.e2m1_value(codes)
-    if fmt == "int4g64":
+    if fmt in BF16_SCALED:
         svals = F.bf16_value(scales)
     elif fmt in MX_FORMATS:
         svals = F.e8m0_value(scales)
