@@ -17,11 +17,12 @@ the GEMM kernel's roofline position (algorithmic flops per launch over its
 HIP-event-timed average duration, against the MI355X dense MXFP4 peak),
 decode weight-streaming bandwidth and linear-layer tokens/s with the
 activation quantization included (MXFP4 Llama linears at M = 1, 4, 16;
-MXINT4 Qwen, NVFP4, MXFP8, MXINT8 and INT4 G=64 Llama linears at M = 1;
+MXINT4 Qwen, NVFP4, MXFP8, MXINT8, INT4 G=64 and INT8 G=128 Llama linears
+at M = 1;
 32 layer copies cycled so that the 256 MB last-level cache cannot hold the
 weights), the other formats' prefill configurations (NVFP4 Llama at
-M = 4096, MXINT4 Qwen at M = 512 and 4096, MXFP8, MXINT8 and INT4 G=64 Llama
-at M = 2048), each against the peak of the MFMA it runs on, the offline
+M = 4096, MXINT4 Qwen at M = 512 and 4096, MXFP8, MXINT8, INT4 G=64 and
+INT8 G=128 Llama at M = 2048), each against the peak of the MFMA it runs on, the offline
 dual-scale solver on fp32 weights of the Llama linears' shapes, the q, k, v
 projections with their own column scales (one multi-output quantize and one
 grouped GEMM against three separate pairs), and the CPU oracle timed on a
@@ -53,12 +54,14 @@ PEAK = {  # MI355X published dense peaks
     "int4g64": (2.5e15, "TFLOP/s", "mfma"),  # exact fp16 expansion of code x BF16 scale, fp16 MFMA
     "mxfp8": (2.5e15, "TFLOP/s", "mfma"),    # exact bf16 expansion on the bf16 MFMA
     "mxint8": (5.0e15, "TOP/s", "mfma"),     # FP8 scaled MFMA, four per int8 product
+    "int8g128": (5.0e15, "TOP/s", "mfma"),   # int8 MFMA, BF16 block scales on the VALU
 }
 HBM_PEAK = 8.0e12
 DTYPE = {"mxfp4": "fp4", "nvfp4": "fp4xe4m3->fp16", "mxint4": "int4->fp8",
-         "int4g64": "int4xbf16->fp16", "mxfp8": "fp8->bf16", "mxint8": "int8->2xfp8"}
-CODE_BYTES = {"mxfp8": 1.0, "mxint8": 1.0}   # bytes per code (0.5 for the 4-bit formats)
-SCALE_BYTES = {"int4g64": 2}   # bytes per block scale (1 for E8M0 / UE4M3)
+         "int4g64": "int4xbf16->fp16", "mxfp8": "fp8->bf16", "mxint8": "int8->2xfp8",
+         "int8g128": "int8"}
+CODE_BYTES = {"mxfp8": 1.0, "mxint8": 1.0, "int8g128": 1.0}   # bytes per code (0.5 for the 4-bit formats)
+SCALE_BYTES = {"int4g64": 2, "int8g128": 2}   # bytes per block scale (1 for E8M0 / UE4M3)
 
 
 def log(*a):
@@ -74,7 +77,7 @@ class Layer:
         if case.w_codes is not None:
             wc = torch.from_numpy(case.w_codes).to(dev)
             ws = torch.from_numpy(case.w_scales).to(dev)
-            if case.fmt == "int4g64":                       # BF16 bit patterns
+            if case.fmt in ("int4g64", "int8g128"):        # BF16 bit patterns
                 ws = torch.from_numpy(case.w_scales.view(np.int16)).to(dev).view(torch.bfloat16)
             tw = torch.tensor([case.t_w], dtype=torch.float32, device=dev)
         else:
@@ -526,6 +529,11 @@ def gemm_kernel_label(fmt, M):
         if M <= 16:
             return "gemm_int4g64_dot_kernel (VALU int4 dot products)" if M <= 3 else "gemm_int4g64_decode_kernel"
         return "gemm_int4g64_f16_kernel (256x256 tiles for qkv and gate+up, 256x128 for o and down)"
+    if fmt == "int8g128":
+        if M <= 3:
+            return ("gemm_int8g128_dot_kernel (VALU int8 dot products; the tile kernel where the rows "
+                    "exceed 64 KiB of LDS)")
+        return "gemm_int8g128_tile_kernel (64x128 tiles, 32x128 for M <= 32)"
     if fmt in ("mxfp8", "mxint8"):
         if M <= 3:
             return (f"gemm_mx8_dot_kernel<{fmt}> (VALU dot products; gemm_mx8_decode_kernel where the "
@@ -655,11 +663,12 @@ def main():
         steps = max(5, a.steps // 4)
         out["prefill_formats"] = {}
         for wl, Mp in (("llama_nvfp4", 4096), ("qwen_mxint4", 512), ("qwen_mxint4", 4096),
-                       ("llama_mxfp8", 2048), ("llama_mxint8", 2048), ("llama_int4g64", 2048)):
+                       ("llama_mxfp8", 2048), ("llama_mxint8", 2048), ("llama_int4g64", 2048),
+                       ("llama_int8g128", 2048)):
             log(f"[bench] prefill {wl} M={Mp}")
             out["prefill_formats"][f"{wl}_M{Mp}"] = prefill_rates(dev, wl, Mp, steps, min(a.warmup, 5))
         if not a.no_decode:
-            for wl in ("llama_mxfp8", "llama_mxint8", "llama_int4g64"):
+            for wl in ("llama_mxfp8", "llama_mxint8", "llama_int4g64", "llama_int8g128"):
                 log(f"[bench] decode {wl} M=1")
                 out[f"decode_hbm_{wl}"] = decode_bandwidth(dev, a.steps, wl, (1,))
     if not a.no_solver:

@@ -53,7 +53,8 @@ typedef enum {
   W4A4_MXINT4 = 2,  /* int4 elements, G = 32, E8M0 block scale             */
   W4A4_INT4G64 = 3, /* int4 elements, G = 64, BF16 block scale (see below)  */
   W4A4_MXFP8 = 4,   /* E4M3 elements, G = 32, E8M0 block scale (8-bit)     */
-  W4A4_MXINT8 = 5   /* int8 elements, G = 32, E8M0 block scale (8-bit)     */
+  W4A4_MXINT8 = 5,  /* int8 elements, G = 32, E8M0 block scale (8-bit)     */
+  W4A4_INT8G128 = 6 /* int8 elements, G = 128, BF16 block scale (8-bit)    */
 } w4a4_format;
 
 /*
@@ -89,9 +90,33 @@ typedef enum {
  * requirement); there is no tensor scale (t_act and t_w are ignored; unpack
  * writes t_w = 1).  Supported by the size queries, w4a4_quantize_act,
  * w4a4_pack_weight, w4a4_unpack_weight and w4a4_linear (no workspace); the
- * multi-output quantizer, the grouped linear and the solver return
- * W4A4_ERR_FORMAT for it.  The GEMM runs one int8 MFMA (16x16x64) per 64-block
- * and applies Delta_a * Delta_w to each block sum in fp32.
+ * multi-output quantizer, w4a4_linear_noalloc, the grouped linear and the
+ * solver return W4A4_ERR_FORMAT for it.  The GEMM expands code x scale
+ * exactly into fp16 for the fp16 MFMA (M > 16, K % 128 == 0), takes int4 dot
+ * products on the VALU for up to three rows, and otherwise runs one int8
+ * MFMA (16x16x64) per 64-block and applies Delta_a * Delta_w to each block
+ * sum in fp32.
+ */
+
+/*
+ * W4A4_INT8G128 - the 8-bit integer W+A variant of Appendix G.2 (Table 9: INT8
+ * weights and activations in groups of 128), with Section 3's symmetric
+ * quantizer (q_max = 127) and BF16 block scales as for W4A4_INT4G64.  A
+ * block's scale is Delta = BF16(amax / 127), rounded once to nearest even;
+ * codes are RNE(x~ / Delta) on the INT8 grid, clip(., -128, 127) (only a
+ * subnormal Delta can take a code past +-127); a zero block has Delta = 0
+ * and zero codes; a block with a non-finite value gets Delta = 0x7FC0 and
+ * zero codes.  Canonical codes are [rows x K] two's-complement bytes,
+ * scales [rows x K/128] BF16 bit patterns (two bytes per block).  K % 128 ==
+ * 0 and N % 16 == 0; no tensor scale (t_act and t_w are ignored; unpack
+ * writes t_w = 1).  w4a4_quantize_act needs codes 8-byte aligned.  Supported
+ * by the size queries, w4a4_quantize_act, w4a4_pack_weight,
+ * w4a4_unpack_weight and w4a4_linear (no workspace); the multi-output
+ * quantizer, w4a4_linear_noalloc, the grouped linear and the solver return
+ * W4A4_ERR_FORMAT for it.  The GEMM takes each 128-block's exact integer sum
+ * (int8 dot products on the VALU for up to three rows, two int8 MFMAs
+ * (16x16x64) per block otherwise) and applies Delta_a * Delta_w to it in
+ * fp32.
  */
 
 typedef enum {
@@ -287,7 +312,7 @@ w4a4_status w4a4_linear(w4a4_format fmt, int64_t M, int64_t N, int64_t K,
  * library.  Shapes whose workspace would exceed the array return
  * W4A4_ERR_WORKSPACE (none does: split-K shapes have at most 128 tiles).
  * Nothing is allocated, freed or synchronized.  Not available for
- * W4A4_INT4G64 (W4A4_ERR_FORMAT).
+ * W4A4_INT4G64 and W4A4_INT8G128 (W4A4_ERR_FORMAT).
  */
 #define W4A4_NOALLOC_SCRATCH_BYTES (4352 + 128 * 4 * 65536)
 w4a4_status w4a4_linear_noalloc(w4a4_format fmt, int64_t M, int64_t N, int64_t K,

@@ -324,3 +324,53 @@ def test_probe_rejects_bad_arguments():
     assert L.w4a4_probe_stream_read(fake, 0, fake, None) == 2
     assert L.w4a4_probe_stream_read(ctypes.c_void_p(4100), 1024, fake, None) == 3  # alignment
 
+
+
+def test_int8g128_size_queries():
+    """INT8 G=128 with BF16 scales (6): one byte per code, two scale bytes per
+    128-block, K % 128 and N % 16, a blob of N*K code bytes + N*K/64 scale
+    bytes + r, no workspaces."""
+    L = w4.lib()
+    assert L.w4a4_block_size(6) == 128
+    assert L.w4a4_act_codes_bytes(6, 5, 384) == 5 * 384
+    assert L.w4a4_act_scales_bytes(6, 5, 384) == 5 * 3 * 2
+    assert L.w4a4_act_scales_bytes(6, 5, 192) == 0                  # K % 128
+    assert L.w4a4_act_codes_bytes(6, 5, 64) == 0
+    assert L.w4a4_quantize_workspace_bytes(6, 5, 384) == 0
+    assert L.w4a4_linear_workspace_bytes(6, 2048, 4096, 4096) == 0
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    for N, K in [(16, 128), (48, 384), (4096, 14336)]:
+        assert L.w4a4_packed_weight_bytes(6, N, K) == a256(a256(256 + N * K) + N * (K // 128) * 2) + a256(4 * N)
+    assert L.w4a4_packed_weight_bytes(6, 24, 256) == 0              # N % 16
+    assert L.w4a4_packed_weight_bytes(6, 16, 192) == 0              # K % 128
+    assert L.w4a4_dualquant_workspace_bytes(6, 64, 256) == 0        # no solver for this format
+
+
+def test_int8g128_rejects():
+    L = w4.lib()
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    n = (ctypes.c_int64 * 4)(64, 64, 64, 64)
+    # quantize_act: K % 128, NULL X, misaligned X, codes not 8-byte aligned
+    assert L.w4a4_quantize_act(6, 4, 192, FAKE, None, FAKE, FAKE, None, None, 0, None) == 2
+    assert L.w4a4_quantize_act(6, 4, 256, None, None, FAKE, FAKE, None, None, 0, None) == 1
+    assert L.w4a4_quantize_act(6, 4, 256, FAKE_MIS, None, FAKE, FAKE, None, None, 0, None) == 3
+    assert L.w4a4_quantize_act(6, 4, 256, FAKE, None, ctypes.c_void_p((1 << 20) + 4), FAKE, None,
+                               None, 0, None) == 3
+    # pack / unpack / linear: N % 16, K % 128, NULL r, misaligned blob
+    assert L.w4a4_pack_weight(6, 24, 128, FAKE, FAKE, None, FAKE, FAKE, None) == 2
+    assert L.w4a4_pack_weight(6, 16, 192, FAKE, FAKE, None, FAKE, FAKE, None) == 2
+    assert L.w4a4_pack_weight(6, 16, 128, FAKE, FAKE, None, None, FAKE, None) == 1
+    assert L.w4a4_unpack_weight(6, 16, 128, None, FAKE, FAKE, None, None, None) == 1
+    assert L.w4a4_linear(6, 4, 16, 192, FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == 2
+    assert L.w4a4_linear(6, 4, 16, 128, FAKE, FAKE, None, FAKE_MIS, FAKE, None, 0, None) == 3
+    assert L.w4a4_linear(6, 0, 16, 128, None, None, None, None, None, None, 0, None) == 0
+    # the multi-output quantizer, noalloc and grouped linear and the solver do not take it
+    assert L.w4a4_quantize_act_multi(6, 4, 128, FAKE, 1, arr, arr, arr, None, None, 0, None) == 4
+    assert L.w4a4_linear_noalloc(6, 4, 128, 256, FAKE, FAKE, None, FAKE, FAKE, None) == 4
+    assert L.w4a4_linear_grouped(6, 1, 4, 128, n, arr, arr, None, arr, arr, None) == 4
+    assert L.w4a4_dualquant_solve(6, 64, 256, FAKE, 15, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                  1 << 30, None) == 4
+    assert "INT8 G=128" in L.w4a4_last_error().decode()

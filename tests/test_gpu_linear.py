@@ -248,6 +248,8 @@ MISMATCH = [
     (("mxfp8", 256, 512), ("mxint8", 5, 256, 512)),
     (("mxfp8", 256, 512), ("mxint8", 1, 256, 512)),
     (("mxint8", 256, 512), ("mxfp8", 3, 256, 512)),
+    (("mxint8", 256, 512), ("int8g128", 1, 256, 512)),
+    (("mxfp8", 256, 512), ("int8g128", 40, 256, 1024)),
     (("mxint4", 256, 512), ("mxint4", 1, 256, 1024)),
     (("mxint4", 256, 512), ("nvfp4", 1, 256, 512)),
     (("mxint4", 256, 512), ("int4g64", 33, 256, 512)),

@@ -24,7 +24,7 @@ import torch
 __all__ = ["FORMATS", "lib", "library_path", "block_size", "scale_dtype", "quantize_act", "pack_weight",
            "unpack_weight", "linear", "linear_noalloc", "linear_workspace", "packed_weight_bytes", "W4A4Error"]
 
-FORMATS = {"mxfp4": 0, "nvfp4": 1, "mxint4": 2, "int4g64": 3, "mxfp8": 4, "mxint8": 5}
+FORMATS = {"mxfp4": 0, "nvfp4": 1, "mxint4": 2, "int4g64": 3, "mxfp8": 4, "mxint8": 5, "int8g128": 6}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
@@ -112,13 +112,13 @@ def _stream(device: torch.device):
 
 
 def scale_dtype(fmt) -> torch.dtype:
-    """Element type of block scales: bytes (E8M0 / UE4M3), BF16 for INT4 G=64."""
-    return torch.bfloat16 if _fmt(fmt) == FORMATS["int4g64"] else torch.uint8
+    """Element type of block scales: bytes (E8M0 / UE4M3), BF16 for INT4 G=64 and INT8 G=128."""
+    return torch.bfloat16 if _fmt(fmt) in (FORMATS["int4g64"], FORMATS["int8g128"]) else torch.uint8
 
 
 def code_cols(fmt, K: int) -> int:
     """Bytes of canonical codes per row of K elements (K/2; K for the 8-bit formats)."""
-    return K if _fmt(fmt) in (FORMATS["mxfp8"], FORMATS["mxint8"]) else K // 2
+    return K if _fmt(fmt) in (FORMATS["mxfp8"], FORMATS["mxint8"], FORMATS["int8g128"]) else K // 2
 
 
 def block_size(fmt) -> int:
@@ -191,10 +191,14 @@ def pack_weight(codes: torch.Tensor, scales: torch.Tensor, t_w: Optional[torch.T
     f = _fmt(fmt)
     L = lib()
     N = codes.shape[0]
-    K = codes.shape[1] if f in (FORMATS["mxfp8"], FORMATS["mxint8"]) else codes.shape[1] * 2
+    K = codes.shape[1] * (1 if code_cols(fmt, 2) == 2 else 2)     # one byte or one nibble per code
     nbytes = L.w4a4_packed_weight_bytes(f, N, K)
     if nbytes == 0:
         raise W4A4Error(2, f"invalid packed weight shape N={N} K={K}")
+    G = L.w4a4_block_size(f)
+    if codes.dim() != 2 or tuple(scales.shape) != (N, K // G) or r.numel() != N:
+        raise W4A4Error(2, f"pack_weight: codes {tuple(codes.shape)}, scales {tuple(scales.shape)} and "
+                           f"r {tuple(r.shape)} do not describe one N={N} x K={K} weight")
     blob = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
     _check(L.w4a4_pack_weight(f, N, K, _ptr(codes), _ptr(scales), _ptr(t_w), _ptr(r), _ptr(blob),
                               _stream(codes.device)))

@@ -1,0 +1,560 @@
+// INT8 with blocks of 128 and BF16 block scales: the 8-bit integer W+A
+// variant of DualQuant's Appendix G.2 (Table 9: INT8 weights and activations,
+// groups of 128).  Section 3 gives the symmetric block quantizer (Delta =
+// max|x| / q_max, q_max = 127 on the INT8 grid); the scales are BF16 as in
+// the packed INT4 deployment of Appendix I.
+//
+// gfx950's block-scaled MFMAs take only E8M0 scales, so the BF16 scales are
+// applied on the VALU, once per 128-block: each block's integer sum is exact
+// (|sum| <= 128 * 128 * 128 = 2^21) and joins the fp32 accumulator times
+// Delta_a * Delta_w (an exact product of two BF16 values).
+//
+//   quantize  x~ = fp32(X) * c (one rounded fp32 multiply); per 128-block
+//             Delta = BF16(amax / 127) rounded once from the fp64 quotient;
+//             code = clip(RNE(x~ / Delta), -128, 127) from the fp64 quotient.
+//   blob      256-byte header; codes in 2 KiB tiles of 16 rows x 128 K, tile
+//             (g, s) = rows 16 g .. +16, K 128 s .. +128, g-major; lane l owns
+//             32 bytes of row 16 g + l % 16: K 128 s + 16 c .. +16 and
+//             128 s + 64 + 16 c .. +16 with c = l / 16 (each half one operand
+//             of v_mfma_i32_16x16x64_i8); scales [N/16][K/128][16] BF16;
+//             r [N] fp32.
+//   GEMM      M <= 3 while the rows fit 64 KiB of LDS: block dot products on
+//             the VALU (v_dot4_i32_i8), the activation rows copied once per
+//             workgroup into LDS; otherwise two integer MFMAs per block and
+//             16 x 16 fragment pair, then the block's scale product.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace w4a4 {
+namespace {
+
+constexpr int kFmt = 6;   // W4A4_INT8G128
+constexpr int kG = 128;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Nearest BF16 (ties to even) to a non-negative finite double: 8 significant
+// bits, spacing fixed at 2^-133 below 2^-126.  The result is a BF16 value, so
+// its conversion to fp32 is exact and the top 16 bits are the pattern.
+__device__ inline uint32_t bf16_rne_bits(double v) {
+  if (v == 0.0) return 0;
+  const int e = ilogb(v);                      // 2^e <= v < 2^(e+1)
+  const int qe = e - 7 > -133 ? e - 7 : -133;  // exponent of one unit in the last place
+  const double n = rint(ldexp(v, -qe));
+  return __float_as_uint(float(ldexp(n, qe))) >> 16;
+}
+
+__device__ inline uint16_t bf16_rne_f32(float y) {
+  const uint32_t u = __float_as_uint(y);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------- quantize --
+// One thread per 8 consecutive elements (one 16-byte load, one 8-byte store);
+// the 16 threads of a 128-block are 16 consecutive lanes and exchange the
+// block maximum and the non-finite flag through lane shuffles.  Total threads
+// M*K/8 is a multiple of 16, so a block's lanes are all inside or all
+// outside the range.
+__global__ void __launch_bounds__(256)
+quantize_int8g128_kernel(const uint16_t* __restrict__ X, const float* __restrict__ c, int64_t K,
+                         int64_t total8, uint2* __restrict__ codes, uint16_t* __restrict__ scales) {
+  const int64_t k8 = K / 8;
+  for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < total8;
+       t += int64_t(gridDim.x) * 256) {
+    const int64_t row = t / k8;
+    const int64_t kc = (t - row * k8) * 8;
+    const uint4 raw = *reinterpret_cast<const uint4*>(X + row * K + kc);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
+      x[2 * j + 1] = bf16_to_f32(w[j] >> 16);
+    }
+    if (c) {
+      const float4 c0 = *reinterpret_cast<const float4*>(c + kc);
+      const float4 c1 = *reinterpret_cast<const float4*>(c + kc + 4);
+      const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = x[j] * cc[j];
+    }
+    float amax = 0.f;
+    int bad = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bad |= !isfinite(x[j]);
+      amax = fmaxf(amax, fabsf(x[j]));
+    }
+#pragma unroll
+    for (int s = 1; s < 16; s <<= 1) {
+      amax = fmaxf(amax, __shfl_xor(amax, s));
+      bad |= __shfl_xor(bad, s);
+    }
+    // amax / 127 in fp64, then one rounding to BF16: the fp64 quotient lands
+    // on a BF16 midpoint only when the exact quotient is that midpoint
+    uint32_t bits = bad ? 0u : bf16_rne_bits(double(amax) / 127.0);
+    const double delta = double(bf16_to_f32(bits));
+    uint32_t lo = 0, hi = 0;
+    if (!bad && bits) {
+      // x~ (24 bits) / Delta (8 bits) in fp64: a quotient that is not a
+      // half-integer is much farther from one than the fp64 rounding, so
+      // rint of it is the exact nearest-even decision
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        double q = rint(double(x[j]) / delta);
+        q = q > 127.0 ? 127.0 : (q < -128.0 ? -128.0 : q);
+        const uint32_t b = uint32_t(int(q)) & 0xFFu;
+        if (j < 4) lo |= b << (8 * j);
+        else hi |= b << (8 * (j - 4));
+      }
+    }
+    if (bad) bits = 0x7FC0u;
+    codes[t] = make_uint2(lo, hi);
+    if ((threadIdx.x & 15) == 0) scales[t / 16] = uint16_t(bits);
+  }
+}
+
+// -------------------------------------------------------------------- pack --
+struct I8Layout {
+  int64_t NG, KS, code_off, scale_off, r_off, total;
+};
+
+__host__ __device__ inline I8Layout i8_layout(int64_t N, int64_t K) {
+  I8Layout L;
+  L.NG = N / 16;
+  L.KS = K / kG;
+  L.code_off = 256;
+  L.scale_off = align256(L.code_off + N * K);
+  L.r_off = align256(L.scale_off + N * L.KS * 2);
+  L.total = align256(L.r_off + N * 4);
+  return L;
+}
+
+// One thread per 16-byte chunk of a tile: chunk t = tile * 128 + 2 * lane +
+// half, tile = g * KS + s; also one per scale and per row scale.  unpack = 1
+// copies the other way (canonical outputs that are NULL are skipped).
+__global__ void __launch_bounds__(256)
+pack_int8g128_kernel(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+                     const float* __restrict__ r, int64_t N, int64_t K, uint8_t* __restrict__ blob,
+                     int unpack, float* __restrict__ t_w) {
+  const I8Layout L = i8_layout(N, K);
+  const int64_t chunks = N * K / 16;
+  const int64_t nscales = N * L.KS;
+  const int64_t work = chunks > nscales ? chunks : nscales;
+  for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < work;
+       t += int64_t(gridDim.x) * 256) {
+    if (t < chunks) {
+      const int64_t tile = t >> 7;
+      const int lane = int((t >> 1) & 63), half = int(t & 1);
+      const int64_t g = tile / L.KS, s = tile - g * L.KS;
+      const int64_t src = (16 * g + (lane & 15)) * K + s * kG + 64 * half + 16 * (lane >> 4);
+      uint4* packed = reinterpret_cast<uint4*>(blob + L.code_off) + t;
+      uint4* canon = reinterpret_cast<uint4*>(const_cast<uint8_t*>(codes) + src);
+      if (!unpack) *packed = *canon;
+      else if (codes) *canon = *packed;
+    }
+    if (t < nscales) {
+      const int64_t n = t / L.KS, s = t - n * L.KS;
+      uint16_t* ps = reinterpret_cast<uint16_t*>(blob + L.scale_off) + ((n >> 4) * L.KS + s) * 16 + (n & 15);
+      uint16_t* cs = const_cast<uint16_t*>(scales) + t;
+      if (!unpack) *ps = *cs;
+      else if (scales) *cs = *ps;
+    }
+    if (t < N) {
+      float* pr = reinterpret_cast<float*>(blob + L.r_off) + t;
+      if (!unpack) *pr = r[t];
+      else if (r) const_cast<float*>(r)[t] = *pr;
+    }
+    if (unpack && t_w && t == 0) *t_w = 1.0f;   // no tensor scale in this format
+  }
+}
+
+// The header is written field by field into the blob (the GEMM kernels check
+// its magic, format, N and K before reading the blob).
+__global__ void pack_int8g128_header_kernel(int64_t N, int64_t K, uint8_t* blob) {
+  if (threadIdx.x != 0) return;
+  const I8Layout L = i8_layout(N, K);
+  BlobHeader* h = reinterpret_cast<BlobHeader*>(blob);
+  const char m[8] = {'W', '4', 'A', '4', 'P', 'K', '0', '1'};
+  for (int i = 0; i < 8; ++i) h->magic[i] = m[i];
+  h->version = 1;
+  h->format = kFmt;
+  h->N = N;
+  h->K = K;
+  h->layout = 5;
+  h->t_w = 1.0f;
+  h->code_off = uint64_t(L.code_off);
+  h->scale_off = uint64_t(L.scale_off);
+  h->r_off = uint64_t(L.r_off);
+  h->total = uint64_t(L.total);
+  for (int i = 0; i < int(sizeof(h->pad)); ++i) h->pad[i] = 0;
+}
+
+// ------------------------------------------------------- dot-product GEMM --
+// M = MD <= 3.  One workgroup per 16 output features (group ng = (b % 8) S +
+// b / 8 for workgroup b, S groups per XCD); WAVES waves split the K-steps
+// into contiguous ranges, each with the loads of U K-steps in flight (two
+// 16-byte non-temporal loads of the lane's tile bytes and its row's BF16
+// scale).  The MD activation rows (K bytes each) and their scales (K/128
+// BF16 each) are copied once per workgroup into LDS.  Lane (n = l % 16, c =
+// l / 16) takes v_dot4_i32_i8 products of its 32 bytes with the same K of
+// each row (the block's integer part sum is exact), and adds it to the row's
+// fp32 sum times Delta_w * Delta_a.  The four lanes of a feature are added by
+// two lane exchanges, the waves in wave order through LDS.
+template <int MD>
+__host__ __device__ constexpr int64_t i8_dot_lds(int64_t K) {
+  return MD * (K + 2 * (K / kG));
+}
+
+template <int WAVES, int U, int MD>
+__global__ __launch_bounds__(64 * WAVES) void gemm_int8g128_dot_kernel(
+    const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, kFmt, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
+  const I8Layout L = i8_layout(N, K);
+  const int64_t F = L.NG, per_x = (F + 7) / 8;
+  const int64_t ng = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8;
+  if (ng >= F) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane >> 4, n = lane & 15;
+  const int64_t KS = L.KS;
+  const int64_t per = (KS + WAVES - 1) / WAVES;
+  const int64_t k_begin = wave * per;
+  const int64_t k_end = k_begin + per < KS ? k_begin + per : KS;
+  const u4* __restrict__ Wg = reinterpret_cast<const u4*>(blob + L.code_off) + (ng * KS * 64 + lane) * 2;
+  const uint16_t* __restrict__ Sg = reinterpret_cast<const uint16_t*>(blob + L.scale_off) + ng * KS * 16 + n;
+  const float* __restrict__ R = reinterpret_cast<const float*>(blob + L.r_off);
+
+  // the first batch of weight loads goes out before the activation rows are
+  // staged, so the staging's latency overlaps them
+  u4 w0[U], w1[U];
+  uint16_t ws[U];
+  auto load_batch = [&](int64_t kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      w0[u] = __builtin_nontemporal_load(&Wg[(kb + u) * 128]);
+      w1[u] = __builtin_nontemporal_load(&Wg[(kb + u) * 128 + 1]);
+      ws[u] = Sg[(kb + u) * 16];
+    }
+  };
+  if (k_begin + U <= k_end) load_batch(k_begin);
+
+  // LDS: MD rows of K code bytes, then MD rows of K/128 BF16 scales
+  extern __shared__ __attribute__((aligned(16))) uint8_t i8_dyn[];
+  for (int64_t d = tid; d < MD * (K / 16); d += 64 * WAVES)
+    reinterpret_cast<u4*>(i8_dyn)[d] = reinterpret_cast<const u4*>(a_codes)[d];
+  uint16_t* asc = reinterpret_cast<uint16_t*>(i8_dyn + MD * K);
+  for (int64_t d = tid; d < MD * KS; d += 64 * WAVES) asc[d] = a_scales[d];
+  __syncthreads();
+
+  float acc[MD];
+#pragma unroll
+  for (int m = 0; m < MD; ++m) acc[m] = 0.f;
+  auto step = [&](const u4& a_w, const u4& b_w, uint16_t sw, int64_t ks) {
+    const float dw = bf16_to_f32(sw);
+#pragma unroll
+    for (int m = 0; m < MD; ++m) {
+      const uint8_t* row = i8_dyn + m * K + ks * kG + 16 * c;
+      const u4 alo = *reinterpret_cast<const u4*>(row);
+      const u4 ahi = *reinterpret_cast<const u4*>(row + 64);
+      int dl = 0, dh = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dl = __builtin_amdgcn_sdot4(int(a_w[i]), int(alo[i]), dl, false);
+        dh = __builtin_amdgcn_sdot4(int(b_w[i]), int(ahi[i]), dh, false);
+      }
+      acc[m] = fmaf(float(dl + dh), dw * bf16_to_f32(asc[m * KS + ks]), acc[m]);
+    }
+  };
+  int64_t k0 = k_begin;
+  for (; k0 + U <= k_end; k0 += U) {
+    if (k0 != k_begin) load_batch(k0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) step(w0[u], w1[u], ws[u], k0 + u);
+  }
+  for (; k0 < k_end; ++k0) step(Wg[k0 * 128], Wg[k0 * 128 + 1], Sg[k0 * 16], k0);
+
+#pragma unroll
+  for (int m = 0; m < MD; ++m) {
+    acc[m] += __shfl_xor(acc[m], 16);
+    acc[m] += __shfl_xor(acc[m], 32);
+  }
+  __shared__ float red[WAVES > 1 ? WAVES - 1 : 1][MD][16];
+  if (wave != 0 && c == 0) {
+#pragma unroll
+    for (int m = 0; m < MD; ++m) red[wave - 1][m][n] = acc[m];
+  }
+  __syncthreads();
+  if (wave != 0 || c != 0) return;
+  const float rn = R[ng * 16 + n];
+#pragma unroll
+  for (int m = 0; m < MD; ++m) {
+    float y = acc[m];
+#pragma unroll
+    for (int w = 0; w < WAVES - 1; ++w) y += red[w][m][n];
+    Y[int64_t(m) * N + ng * 16 + n] = bf16_rne_f32(y * rn);
+  }
+}
+
+template <int WAVES, int U, int MD>
+hipError_t launch_i8_dot_md(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint16_t* as,
+                            const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_int8g128_dot_kernel<WAVES, U, MD>), dim3(unsigned((N / 16 + 7) / 8 * 8)),
+                     dim3(64 * WAVES), size_t(i8_dot_lds<MD>(K)), stream, ac, as, blob, Y, M, N, K);
+  return hipGetLastError();
+}
+
+template <int WAVES, int U>
+hipError_t launch_i8_dot(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint16_t* as,
+                         const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  if (M == 1) return launch_i8_dot_md<WAVES, U, 1>(M, N, K, ac, as, blob, Y, stream);
+  if (M == 2) return launch_i8_dot_md<WAVES, U, 2>(M, N, K, ac, as, blob, Y, stream);
+  return launch_i8_dot_md<WAVES, U, 3>(M, N, K, ac, as, blob, Y, stream);
+}
+
+// -------------------------------------------------------------- tile GEMM --
+// The weight fragment is the MFMA's row operand and the activation fragment
+// its column operand, so lane l holds the outputs (activation row l % 16,
+// weight columns 4 (l / 16) .. +4): one activation scale per fragment, the
+// four weight scales in one 8-byte load and the four outputs in one 8-byte
+// store.  Per 128-block and fragment pair, two v_mfma_i32_16x16x64_i8 (the
+// lane's two 16-byte halves, the same K on both operands) give the block's
+// exact integer sums; acc[v] += sum[v] * Delta_a * Delta_w[v].
+__device__ inline v4i mfma_i8(u4 w, u4 a, v4i acc) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, w), __builtin_bit_cast(v4i, a),
+                                               acc, 0, 0, 0);
+}
+
+__device__ inline void store4(uint16_t* y, const float* acc, const float* rn) {
+  uint16_t o[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) o[v] = bf16_rne_f32(acc[v] * rn[v]);
+  *reinterpret_cast<uint2*>(y) = make_uint2(uint32_t(o[0]) | (uint32_t(o[1]) << 16),
+                                            uint32_t(o[2]) | (uint32_t(o[3]) << 16));
+}
+
+// 4 waves as 2 (M) x 2 (N); a wave owns FM x FN fragments of 16 x 16
+// outputs, the workgroup (2 FM 16) x (2 FN 16).  Operands come straight from
+// global memory, two blocks ahead of the one being multiplied (activation
+// rows clamped to M - 1, weight row groups to NG - 1, so every load is in
+// bounds); outputs outside M x N are not stored.  Workgroups are dealt to the
+// 8 XCDs round-robin; workgroup b takes tile number (b % 8) per_xcd + b / 8
+// of an order that runs through blocks of 8 x 8 tiles (8 column tiles wide,
+// then down the rows), so the workgroups an XCD runs at once share their
+// activation rows and weight groups in its L2.
+template <int FM, int FN>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+gemm_int8g128_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
+                          const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M,
+                          int64_t N, int64_t K, int tiles_m, int tiles_n, int per_xcd) {
+  if (!blob_header_ok(blob, kFmt, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
+  const int o = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
+  if (o >= tiles_m * tiles_n) return;
+  const int nb = o / (8 * tiles_m), ob = o - nb * 8 * tiles_m;
+  const int nw = tiles_n - 8 * nb < 8 ? tiles_n - 8 * nb : 8;  // width of this column block
+  const int tm = ob / nw, tn = 8 * nb + ob % nw;
+  const I8Layout L = i8_layout(N, K);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m0 = int64_t(tm) * (2 * FM * 16) + (wave >> 1) * (FM * 16);
+  const int64_t g0 = int64_t(tn) * (2 * FN) + (wave & 1) * FN;
+  const u4* wcodes = reinterpret_cast<const u4*>(blob + L.code_off) + 2 * lane;
+  const uint16_t* wscales = reinterpret_cast<const uint16_t*>(blob + L.scale_off) + 4 * (lane >> 4);
+
+  const uint8_t* arow[FM];
+  const uint16_t* srow[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t m = m0 + i * 16 + (lane & 15);
+    const int64_t mc = m < M ? m : M - 1;
+    arow[i] = a_codes + mc * K + 16 * (lane >> 4);
+    srow[i] = a_scales + mc * L.KS;
+  }
+  int64_t gbase[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) gbase[j] = (g0 + j < L.NG ? g0 + j : L.NG - 1) * L.KS;
+
+  float acc[FM][FN][4];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.f;
+
+  // two register sets: block b + 2's loads go out while block b + 1's are
+  // still in flight, so the in-order load counter only waits for the older set
+  struct Ops {
+    u4 a0[FM], a1[FM], w0[FN], w1[FN];
+    uint2 sw[FN];
+    uint16_t sa[FM];
+  };
+  auto load = [&](int64_t b, Ops& p) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      p.a0[i] = *reinterpret_cast<const u4*>(arow[i] + b * kG);
+      p.a1[i] = *reinterpret_cast<const u4*>(arow[i] + b * kG + 64);
+      p.sa[i] = srow[i][b];
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t tile = gbase[j] + b;
+      p.w0[j] = wcodes[tile * 128];
+      p.w1[j] = wcodes[tile * 128 + 1];
+      p.sw[j] = *reinterpret_cast<const uint2*>(wscales + tile * 16);
+    }
+  };
+  // Per pair of weight fragments: the first halves' MFMAs for every
+  // activation fragment, then the second halves' (each adding to the sum of
+  // its first), then the scaling, so that no sum is read right after the
+  // MFMA that writes it.
+  auto compute = [&](const Ops& p) {
+    float sa[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sa[i] = bf16_to_f32(p.sa[i]);
+#pragma unroll
+    for (int j0 = 0; j0 < FN; j0 += 2) {
+      v4i S[2][FM];
+      const v4i zero = {0, 0, 0, 0};
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) S[jj][i] = mfma_i8(p.w0[j0 + jj], p.a0[i], zero);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) S[jj][i] = mfma_i8(p.w1[j0 + jj], p.a1[i], S[jj][i]);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const uint2 w = p.sw[j0 + jj];
+        const float sw[4] = {bf16_to_f32(w.x & 0xFFFFu), bf16_to_f32(w.x >> 16),
+                             bf16_to_f32(w.y & 0xFFFFu), bf16_to_f32(w.y >> 16)};
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            acc[i][j0 + jj][v] = fmaf(float(S[jj][i][v]), sa[i] * sw[v], acc[i][j0 + jj][v]);
+      }
+    }
+  };
+  const int64_t last = L.KS - 1;
+  Ops p0, p1;
+  load(0, p0);
+  load(last < 1 ? last : 1, p1);
+  // the scheduling barriers keep each set's use (and so its load wait) after
+  // the other set's loads have been issued
+  for (int64_t b = 0; b < L.KS; b += 2) {
+    compute(p0);
+    load(b + 2 < last ? b + 2 : last, p0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (b + 1 < L.KS) {
+      compute(p1);
+      load(b + 3 < last ? b + 3 : last, p1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  const float* r = reinterpret_cast<const float*>(blob + L.r_off);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if (g0 + j >= L.NG) continue;
+    const int64_t n = (g0 + j) * 16 + 4 * (lane >> 4);
+    const float4 r4 = *reinterpret_cast<const float4*>(r + n);
+    const float rn[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + i * 16 + (lane & 15);
+      if (m < M) store4(Y + m * N + n, acc[i][j], rn);
+    }
+  }
+}
+
+template <int FM, int FN>
+hipError_t launch_i8_tile(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint16_t* as,
+                          const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  const int64_t tiles_n = (N / 16 + 2 * FN - 1) / (2 * FN);
+  const int64_t tiles_m = (M + 2 * FM * 16 - 1) / (2 * FM * 16);
+  if (tiles_n * tiles_m >= (int64_t(1) << 30)) return hipErrorInvalidValue;
+  const int tiles = int(tiles_n * tiles_m), per_xcd = (tiles + 7) / 8;
+  hipLaunchKernelGGL((gemm_int8g128_tile_kernel<FM, FN>), dim3(unsigned(8 * per_xcd)), dim3(256), 0,
+                     stream, ac, as, blob, Y, M, N, K, int(tiles_m), int(tiles_n), per_xcd);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t int8g128_packed_weight_bytes(int64_t N, int64_t K) { return size_t(i8_layout(N, K).total); }
+
+hipError_t launch_quantize_int8g128(int64_t M, int64_t K, const void* X, const float* c, void* codes,
+                                    void* scales, hipStream_t stream) {
+  const int64_t total8 = M * K / 8;
+  if (total8 == 0) return hipSuccess;
+  int64_t blocks = (total8 + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(quantize_int8g128_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(X), c, K, total8, static_cast<uint2*>(codes),
+                     static_cast<uint16_t*>(scales));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_int8g128(int64_t N, int64_t K, const void* codes, const void* scales,
+                                const float* r, void* blob, hipStream_t stream) {
+  auto* b = static_cast<uint8_t*>(blob);
+  hipLaunchKernelGGL(pack_int8g128_header_kernel, dim3(1), dim3(64), 0, stream, N, K, b);
+  const int64_t work = N * K / 16;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_int8g128_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(codes), static_cast<const uint16_t*>(scales), r, N, K,
+                     b, 0, static_cast<float*>(nullptr));
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_int8g128(int64_t N, int64_t K, const void* blob, void* codes, void* scales,
+                                  float* r, float* t_w, hipStream_t stream) {
+  const int64_t work = N * K / 16;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_int8g128_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(codes), static_cast<const uint16_t*>(scales), r, N, K,
+                     const_cast<uint8_t*>(static_cast<const uint8_t*>(blob)), 1, t_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_int8g128(int64_t M, int64_t N, int64_t K, const void* a_codes,
+                                  const void* a_scales, const void* blob, void* Y,
+                                  hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const auto* ac = static_cast<const uint8_t*>(a_codes);
+  const auto* as = static_cast<const uint16_t*>(a_scales);
+  const auto* bl = static_cast<const uint8_t*>(blob);
+  auto* y = static_cast<uint16_t*>(Y);
+  const int64_t groups = N / 16;
+  if (M == 1 && i8_dot_lds<1>(K) <= 65536) {
+    if (groups < 1024) return launch_i8_dot<16, 2>(M, N, K, ac, as, bl, y, stream);
+    return launch_i8_dot<8, 2>(M, N, K, ac, as, bl, y, stream);
+  }
+  if (M == 2 && i8_dot_lds<2>(K) <= 65536) {
+    if (groups < 1024) return launch_i8_dot<16, 2>(M, N, K, ac, as, bl, y, stream);
+    return launch_i8_dot<8, 2>(M, N, K, ac, as, bl, y, stream);
+  }
+  if (M == 3 && i8_dot_lds<3>(K) <= 65536) {
+    if (groups < 1024) return launch_i8_dot<16, 2>(M, N, K, ac, as, bl, y, stream);
+    return launch_i8_dot<8, 2>(M, N, K, ac, as, bl, y, stream);
+  }
+  if (M <= 32) return launch_i8_tile<1, 4>(M, N, K, ac, as, bl, y, stream);
+  return launch_i8_tile<2, 4>(M, N, K, ac, as, bl, y, stream);
+}
+
+}  // namespace w4a4

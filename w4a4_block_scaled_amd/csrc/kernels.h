@@ -81,6 +81,23 @@ hipError_t launch_linear_int4g64(int64_t M, int64_t N, int64_t K, const void* a_
                                  const void* a_scales, const void* blob, void* Y,
                                  hipStream_t stream);
 
+// INT8 with G = 128 and BF16 block scales (int8g128.hip): canonical codes
+// [rows x K] int8, scales [rows x K/128] BF16 bit patterns.
+size_t int8g128_packed_weight_bytes(int64_t N, int64_t K);
+
+hipError_t launch_quantize_int8g128(int64_t M, int64_t K, const void* X, const float* c,
+                                    void* codes, void* scales, hipStream_t stream);
+
+hipError_t launch_pack_int8g128(int64_t N, int64_t K, const void* codes, const void* scales,
+                                const float* r, void* blob, hipStream_t stream);
+
+hipError_t launch_unpack_int8g128(int64_t N, int64_t K, const void* blob, void* codes, void* scales,
+                                  float* r, float* t_w, hipStream_t stream);
+
+hipError_t launch_linear_int8g128(int64_t M, int64_t N, int64_t K, const void* a_codes,
+                                  const void* a_scales, const void* blob, void* Y,
+                                  hipStream_t stream);
+
 // Measurement aids (probe.hip): a streaming read of `bytes` (a multiple of
 // 16) and an empty kernel.
 hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t stream);

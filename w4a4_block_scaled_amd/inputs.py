@@ -23,6 +23,9 @@ Qwen-7B-class linears; formats MXFP4 / NVFP4 / MXINT4 from Section 3):
   Student-t with 3 degrees of freedom.
 * ``llama_mxfp8`` / ``llama_mxint8`` : the 8-bit MX variants (Appendix G.2),
   M in {2048, 1}, Llama shapes and laws as ``llama_prefill``.
+* ``llama_int8g128`` : INT8 with G = 128 and BF16 block scales (Appendix
+  G.2's 8-bit integer variant), M in {2048, 1}, as ``llama_mxfp8``; r and c
+  lognormal(0, 0.5) rounded to BF16.
 * ``qwen_mxint4`` : MXINT4, M in {1,512,4096}, Qwen-7B-class shapes (QKV
   3584->4608, O 3584->3584, gate+up 3584->37888, down 18944->3584).
   Weight codes drawn directly (uniform int4) with E8M0 exponents uniform in
@@ -45,9 +48,10 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-FORMATS = ("mxfp4", "nvfp4", "mxint4", "int4g64", "mxfp8", "mxint8")
-BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32, "int4g64": 64, "mxfp8": 32, "mxint8": 32}
-EIGHT_BIT = ("mxfp8", "mxint8")
+FORMATS = ("mxfp4", "nvfp4", "mxint4", "int4g64", "mxfp8", "mxint8", "int8g128")
+BLOCK = {"mxfp4": 32, "nvfp4": 16, "mxint4": 32, "int4g64": 64, "mxfp8": 32, "mxint8": 32,
+         "int8g128": 128}
+EIGHT_BIT = ("mxfp8", "mxint8", "int8g128")
 
 LLAMA_LINEARS = (("qkv", 6144, 4096), ("o", 4096, 4096),
                  ("gate_up", 28672, 4096), ("down", 4096, 14336))
@@ -66,6 +70,8 @@ WORKLOADS = {
     # the 8-bit MX variants (Appendix G.2, Table 9): Llama shapes, prefill and decode
     "llama_mxfp8": (7, "mxfp8", (2048, 1), LLAMA_LINEARS),
     "llama_mxint8": (8, "mxint8", (2048, 1), LLAMA_LINEARS),
+    # INT8 with G = 128 and BF16 scales (Table 9's 8-bit integer variant)
+    "llama_int8g128": (9, "int8g128", (2048, 1), LLAMA_LINEARS),
 }
 
 
@@ -81,7 +87,7 @@ class LinearCase:
     w_codes     : uint8 [N, K/2] canonical packed codes ([N, K] for 8-bit
                   formats) (or None)
     w_scales    : uint8 [N, K/G] block scale bytes (uint16 BF16 patterns for
-                  int4g64) (or None)
+                  int4g64 and int8g128) (or None)
     t_w         : float tensor scale of the weights when codes are drawn
     """
     workload: str
@@ -132,7 +138,7 @@ def lognormal_scales(rng: np.random.Generator, n: int) -> np.ndarray:
 
 
 def scale_family(fmt: str) -> str:
-    return {"nvfp4": "ue4m3", "int4g64": "bf16"}.get(fmt, "e8m0")
+    return {"nvfp4": "ue4m3", "int4g64": "bf16", "int8g128": "bf16"}.get(fmt, "e8m0")
 
 
 def random_codes_bf16(rng: np.random.Generator, N: int, K: int, exp_lo: int, exp_hi: int):
@@ -170,7 +176,13 @@ def random_codes(rng: np.random.Generator, N: int, K: int, G: int,
                  exp_lo: int, exp_hi: int, fmt: str = "mxfp4"):
     """Canonical codes and E8M0 bytes 127+U{lo..hi}: packed nibbles uniform over
     all 16 values, or for the 8-bit formats one byte per element, uniform over
-    all 256 bytes except the E4M3 NaN codes 0x7F / 0xFF (MXFP8)."""
+    all 256 bytes except the E4M3 NaN codes 0x7F / 0xFF (MXFP8).  INT8 G=128
+    takes BF16 block scales 2^e (1 + m/128), e in U{lo..hi}, m in U{0..127}."""
+    if fmt == "int8g128":
+        codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+        e = rng.integers(exp_lo, exp_hi + 1, size=(N, K // G))
+        m = rng.integers(0, 128, size=(N, K // G))
+        return codes, (((127 + e) << 7) | m).astype(np.uint16)
     if fmt in EIGHT_BIT:
         codes = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
         if fmt == "mxfp8":
@@ -198,7 +210,8 @@ def make_case(workload: str, name: str, fmt: str, M: int, N: int, K: int,
         r = admissible_scales(rr, N, family)
     if workload == "llama_nvfp4":
         x = student_t_activations(rx, M, K)
-    elif workload in ("llama_decode", "llama_prefill", "llama_int4g64", "llama_mxfp8", "llama_mxint8"):
+    elif workload in ("llama_decode", "llama_prefill", "llama_int4g64", "llama_mxfp8", "llama_mxint8",
+                      "llama_int8g128"):
         x = outlier_activations(rx, M, K, int(round(0.01 * K)), 30.0)
     else:  # single, qwen_mxint4 and ad-hoc cases: the single-linear distributions
         x = outlier_activations(rx, M, K, int(round(2 * K / 256)), 50.0)
@@ -235,8 +248,8 @@ def adhoc_case(fmt: str, M: int, N: int, K: int, seed: int,
     """A case of any shape with the single-linear activation law.
 
     weights = "prescaled" (N(0,0.02)/(r c), quantized by the method),
-    "codes" (random codes with E8M0 exponents in {-6..1}; MX formats only)
-    or "none".
+    "codes" (random codes with block exponents in {-6..1}; MX formats and
+    INT8 G=128) or "none".
     """
     rx, rc, rr, rw = _rngs(seed, 4)
     family = scale_family(fmt)
