@@ -531,8 +531,10 @@ def gemm_kernel_label(fmt, M):
         return "gemm_int4g64_f16_kernel (256x256 tiles for qkv and gate+up, 256x128 for o and down)"
     if fmt == "int8g128":
         if M <= 3:
-            return ("gemm_int8g128_dot_kernel (VALU int8 dot products; the tile kernel where the rows "
+            return ("gemm_int8g128_dot_kernel (VALU int8 dot products; the decode kernel where the rows "
                     "exceed 64 KiB of LDS)")
+        if M <= 16:
+            return "gemm_int8g128_decode_kernel (int8 MFMA, 16 features per workgroup)"
         return "gemm_int8g128_tile_kernel (64x128 tiles, 32x128 for M <= 32)"
     if fmt in ("mxfp8", "mxint8"):
         if M <= 3:

@@ -49,6 +49,7 @@ CASES = [
     ("int4g64", 300, 1040, 1024),
     ("int4g64", 1100, 8000, 256),
     ("int8g128", 1, 4096, 4096),
+    ("int8g128", 8, 1024, 1024),
     ("int8g128", 300, 1040, 1024),
 ]
 

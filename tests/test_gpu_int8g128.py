@@ -6,9 +6,9 @@ outputs pass gates G1 (every element within the fp32-accumulation bound) and
 G2 (row relative L2 error <= 1e-3), and are bit-exact where every partial
 sum is exact (equal scales per operand).  Shapes reach every GEMM kernel:
 M <= 3 the dot-product kernel while the rows fit 64 KiB of LDS (and the K on
-either side of that bound), 3 < M <= 32 the tile kernel with 32-row
-workgroup tiles, larger M the 64-row tiles, with ragged M, N and K-block
-counts."""
+either side of that bound, beyond it the MFMA decode kernel), M <= 16 the
+MFMA decode kernel, 16 < M <= 32 the tile kernel with 32-row workgroup
+tiles, larger M the 64-row tiles, with ragged M, N and K-block counts."""
 import numpy as np
 import pytest
 import torch
@@ -183,7 +183,7 @@ def run_case(case, dev, label):
     return check_linear(bf16_bits(Y), y, S, case.K, label), bf16_bits(Y), bits
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 32, 33, 64, 130, 300])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9, 16, 17, 32, 33, 64, 130, 300])
 @pytest.mark.parametrize("N,K", [(48, 384), (272, 1152), (528, 4096)])
 def test_linear_matches_oracle(M, N, K):
     dev = device()
@@ -195,7 +195,8 @@ def test_linear_matches_oracle(M, N, K):
 
 # many 16-feature groups (the dot kernel's 8-wave workgroups), a long K, and
 # the K on either side of the dot kernel's 64 KiB LDS bound for 1, 2, 3 rows
-@pytest.mark.parametrize("M,N,K", [(1, 16400, 640), (3, 16384, 512), (2, 64, 14336), (1, 16, 64512),
+@pytest.mark.parametrize("M,N,K", [(1, 16400, 640), (3, 16384, 512), (2, 64, 14336), (8, 16400, 640),
+                                   (12, 64, 14336), (16, 4096, 4096), (1, 16, 64512),
                                    (1, 16, 64640), (2, 16, 32256), (2, 16, 32384), (3, 16, 21504),
                                    (3, 16, 21632), (40, 16400, 256)])
 def test_linear_kernel_bounds(M, N, K):
@@ -215,7 +216,8 @@ def test_linear_random_codes(M):
     run_case(case, dev, f"int8g128 random codes M={M}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1040, 1024), (3, 16400, 512), (5, 272, 1024), (70, 528, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 1040, 1024), (3, 16400, 512), (5, 272, 1024), (16, 16400, 512),
+                                   (20, 272, 1024), (70, 528, 1024)])
 def test_linear_bit_exact_with_equal_scales(M, N, K):
     """All activation scales equal and all weight scales equal (powers of
     two), r a power of two: every block sum is an integer below 2^21 and every
@@ -238,13 +240,13 @@ def test_linear_bit_exact_with_equal_scales(M, N, K):
     assert np.array_equal(got, bits), f"{(got != bits).sum()} of {bits.size} outputs differ"
 
 
-def test_dot_and_tile_kernels_agree():
-    """M = 3 runs the dot-product kernel and M = 4 the tile kernel: on the
-    same first three rows both pass the gates and repeated calls are
+def test_dot_and_decode_kernels_agree():
+    """M = 3 runs the dot-product kernel and M = 4 the MFMA decode kernel: on
+    the same first three rows both pass the gates and repeated calls are
     identical."""
     dev = device()
     case = inputs.adhoc_case(FMT, 4, 528, 4096, seed=8)
-    (_, y4, _) = run_case(case, dev, "tile")
+    (_, y4, _) = run_case(case, dev, "decode")
     case3 = inputs.adhoc_case(FMT, 4, 528, 4096, seed=8)
     case3.M = 3
     case3.x = case3.x[:3]
@@ -255,7 +257,24 @@ def test_dot_and_tile_kernels_agree():
     assert diff.max() <= 2.0 ** -6 * np.abs(F.bf16_value(y4[:3])).max()
 
 
-@pytest.mark.parametrize("M", [1, 3, 2048])
+def test_decode_and_tile_kernels_agree():
+    """M = 16 runs the MFMA decode kernel and M = 17 the tile kernel: on the
+    same first 16 rows both pass the gates and repeated calls are
+    identical."""
+    dev = device()
+    case = inputs.adhoc_case(FMT, 17, 272, 1152, seed=5)
+    (_, y17, _) = run_case(case, dev, "tile")
+    case16 = inputs.adhoc_case(FMT, 17, 272, 1152, seed=5)
+    case16.M = 16
+    case16.x = case16.x[:16]
+    (_, y16, _) = run_case(case16, dev, "decode")
+    (_, y16b, _) = run_case(case16, dev, "decode again")
+    assert np.array_equal(y16, y16b)
+    diff = np.abs(F.bf16_value(y16) - F.bf16_value(y17[:16]))
+    assert diff.max() <= 2.0 ** -6 * np.abs(F.bf16_value(y17[:16])).max()
+
+
+@pytest.mark.parametrize("M", [1, 3, 16, 2048])
 @pytest.mark.parametrize("name", ["qkv", "gate_up", "down"])
 def test_full_size_llama_sampled(M, name):
     """Llama shapes at their full size, in the launch configuration the

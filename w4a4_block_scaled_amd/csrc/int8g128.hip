@@ -21,7 +21,9 @@
 //   GEMM      M <= 3 while the rows fit 64 KiB of LDS: block dot products on
 //             the VALU (v_dot4_i32_i8), the activation rows copied once per
 //             workgroup into LDS; otherwise two integer MFMAs per block and
-//             16 x 16 fragment pair, then the block's scale product.
+//             16 x 16 fragment pair, then the block's scale product: weight
+//             streaming with one 16-feature group per workgroup for M <= 16,
+//             tiles of 32 or 64 rows x 128 features above.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -342,6 +344,108 @@ __device__ inline void store4(uint16_t* y, const float* acc, const float* rn) {
                                             uint32_t(o[2]) | (uint32_t(o[3]) << 16));
 }
 
+// ------------------------------------------------------------ decode GEMM --
+// M <= 16: one workgroup per 16 output features (as the dot kernel), WAVES
+// waves splitting the K-steps into contiguous ranges, each issuing the loads
+// of up to U K-steps at once: the lane's 32 weight bytes (the MFMA's row
+// operand, feature l % 16), the four weight scales of its outputs, and the 32
+// bytes of activation row l % 16 at the same K (the column operand; lanes of
+// rows >= M load nothing and hold zeros).  Per K-step two
+// v_mfma_i32_16x16x64_i8 give the block's exact integer sums for (feature
+// 4 (l / 16) + v, row l % 16), which join the fp32 sums times Delta_a *
+// Delta_w[v].  Partial sums meet in LDS in wave order; wave 0 applies r and
+// stores four features per lane.
+template <int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void gemm_int8g128_decode_kernel(
+    const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
+    const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K) {
+  if (!blob_header_ok(blob, kFmt, N, K)) {
+    fill_y_nan(Y, M, N);
+    return;
+  }
+  static_assert(U <= 8, "load batch");
+  const I8Layout L = i8_layout(N, K);
+  const int64_t F = L.NG, per_x = (F + 7) / 8;
+  const int64_t ng = int64_t(blockIdx.x % 8) * per_x + blockIdx.x / 8;
+  if (ng >= F) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane >> 4;
+  const int64_t m = lane & 15;
+  const bool mvalid = m < M;
+  const int64_t KS = L.KS;
+  const int64_t per = (KS + WAVES - 1) / WAVES;
+  const int64_t k_begin = wave * per;
+  const int64_t k_end = k_begin + per < KS ? k_begin + per : KS;
+  const u4* __restrict__ Wg = reinterpret_cast<const u4*>(blob + L.code_off) + (ng * KS * 64 + lane) * 2;
+  const uint16_t* __restrict__ Sg =
+      reinterpret_cast<const uint16_t*>(blob + L.scale_off) + ng * KS * 16 + 4 * c;
+  const uint8_t* __restrict__ arow = a_codes + (mvalid ? m : 0) * K + 16 * c;
+  const uint16_t* __restrict__ srow = a_scales + (mvalid ? m : 0) * KS;
+
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += U) {
+    u4 w0[U], w1[U], a0[U], a1[U];
+    uint2 sw[U];
+    uint16_t sa[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t ks = k0 + u;
+      const bool ok = ks < k_end;
+      const int64_t kc = ok ? ks : k_end - 1;  // clamped: loads stay in range
+      const u4 x0 = __builtin_nontemporal_load(&Wg[kc * 128]);
+      const u4 x1 = __builtin_nontemporal_load(&Wg[kc * 128 + 1]);
+      u4 y0 = {0u, 0u, 0u, 0u}, y1 = {0u, 0u, 0u, 0u};
+      if (mvalid) {
+        y0 = *reinterpret_cast<const u4*>(arow + kc * kG);
+        y1 = *reinterpret_cast<const u4*>(arow + kc * kG + 64);
+      }
+      const u4 z = {0u, 0u, 0u, 0u};
+      w0[u] = ok ? x0 : z;
+      w1[u] = ok ? x1 : z;
+      a0[u] = ok ? y0 : z;
+      a1[u] = ok ? y1 : z;
+      sw[u] = *reinterpret_cast<const uint2*>(Sg + kc * 16);
+      sa[u] = mvalid ? srow[kc] : uint16_t(0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const v4i zero = {0, 0, 0, 0};
+      v4i S = mfma_i8(w0[u], a0[u], zero);
+      S = mfma_i8(w1[u], a1[u], S);
+      const float da = bf16_to_f32(sa[u]);
+      const float dw[4] = {bf16_to_f32(sw[u].x & 0xFFFFu), bf16_to_f32(sw[u].x >> 16),
+                           bf16_to_f32(sw[u].y & 0xFFFFu), bf16_to_f32(sw[u].y >> 16)};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = fmaf(float(S[v]), da * dw[v], acc[v]);
+    }
+  }
+
+  __shared__ float red[WAVES > 1 ? WAVES - 1 : 1][4][64];
+  if (wave != 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave - 1][v][lane] = acc[v];
+  }
+  __syncthreads();
+  if (wave != 0 || !mvalid) return;
+#pragma unroll
+  for (int w = 0; w < WAVES - 1; ++w)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] += red[w][v][lane];
+  const int64_t n = ng * 16 + 4 * c;
+  const float* R = reinterpret_cast<const float*>(blob + L.r_off);
+  const float4 r4 = *reinterpret_cast<const float4*>(R + n);
+  const float rn[4] = {r4.x, r4.y, r4.z, r4.w};
+  store4(Y + m * N + n, acc, rn);
+}
+
+template <int WAVES, int U>
+hipError_t launch_i8_decode(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint16_t* as,
+                            const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_int8g128_decode_kernel<WAVES, U>), dim3(unsigned((N / 16 + 7) / 8 * 8)),
+                     dim3(64 * WAVES), 0, stream, ac, as, blob, Y, M, N, K);
+  return hipGetLastError();
+}
+
 // 4 waves as 2 (M) x 2 (N); a wave owns FM x FN fragments of 16 x 16
 // outputs, the workgroup (2 FM 16) x (2 FN 16).  Operands come straight from
 // global memory, two blocks ahead of the one being multiplied (activation
@@ -552,6 +656,14 @@ hipError_t launch_linear_int8g128(int64_t M, int64_t N, int64_t K, const void* a
   if (M == 3 && i8_dot_lds<3>(K) <= 65536) {
     if (groups < 1024) return launch_i8_dot<16, 2>(M, N, K, ac, as, bl, y, stream);
     return launch_i8_dot<8, 2>(M, N, K, ac, as, bl, y, stream);
+  }
+  if (M <= 16) {
+    // weight streaming with the MFMA taking up to 16 activation rows
+    const int64_t KS = K / kG;
+    if (KS > 32) return launch_i8_decode<8, 8>(M, N, K, ac, as, bl, y, stream);
+    if (groups < 256) return launch_i8_decode<16, 2>(M, N, K, ac, as, bl, y, stream);
+    if (groups < 1024) return launch_i8_decode<8, 4>(M, N, K, ac, as, bl, y, stream);
+    return launch_i8_decode<4, 8>(M, N, K, ac, as, bl, y, stream);
   }
   if (M <= 32) return launch_i8_tile<1, 4>(M, N, K, ac, as, bl, y, stream);
   return launch_i8_tile<2, 4>(M, N, K, ac, as, bl, y, stream);
