@@ -535,7 +535,9 @@ def gemm_kernel_label(fmt, M):
                     "exceed 64 KiB of LDS)")
         if M <= 16:
             return "gemm_int8g128_decode_kernel (int8 MFMA, 16 features per workgroup)"
-        return "gemm_int8g128_tile_kernel (64x128 tiles, 32x128 for M <= 32)"
+        if M <= 64:
+            return "gemm_int8g128_tile_kernel (64x128 tiles, 32x128 for M <= 32)"
+        return "gemm_int8g128_lds_kernel (128x128 tiles staged through a 4-deep LDS ring)"
     if fmt in ("mxfp8", "mxint8"):
         if M <= 3:
             return (f"gemm_mx8_dot_kernel<{fmt}> (VALU dot products; gemm_mx8_decode_kernel where the "
@@ -556,7 +558,7 @@ def traffic_record(kernel, fmt="mxfp4"):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    name = "int4g64.hip" if fmt == "int4g64" else "gemm.hip"
+    name = {"int4g64": "int4g64.hip", "int8g128": "int8g128.hip"}.get(fmt, "gemm.hip")
     src = open(os.path.join(ROOT, "w4a4_block_scaled_amd", "csrc", name), "rb").read()
     if kernel not in rec:
         return None
