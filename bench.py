@@ -14,7 +14,9 @@ durations.
 
 Printed: one JSON line with the workload's throughput (TFLOP/s, whole step),
 the GEMM kernel's roofline position (algorithmic flops per launch over its
-HIP-event-timed average duration, against the MI355X dense MXFP4 peak),
+HIP-event-timed average duration, against the MI355X dense MXFP4 peak, and
+beside it the rate of the FP4 MFMAs alone on register operands, the ceiling
+the chip holds under that load),
 decode weight-streaming bandwidth and linear-layer tokens/s with the
 activation quantization included (MXFP4 Llama linears at M = 1, 4, 16;
 MXINT4 Qwen, NVFP4, MXFP8, MXINT8, INT4 G=64 and INT8 G=128 Llama linears
@@ -444,6 +446,30 @@ def decode_ceiling(dev, steps, copies=32,
     return out
 
 
+def mfma_ceiling(dev, iters=400, reps=10, bursts=5):
+    """The FP4 matrix-core rate without the GEMM around it
+    (w4a4_probe_mfma_fp4: each wave holds a persistent-GEMM wave's 128 x 128
+    fp32 tile and runs `iters` rounds of its 16 scaled 32 x 32 x 64 FP4 MFMAs
+    on register operands): with random codes on all 256 CUs (the operand
+    bits of a real GEMM), with zero codes (less power drawn), and with random
+    codes on half the CUs (the power of the idle half goes to the clock of
+    the busy one).  TFLOP/s from HIP-graph bursts of back-to-back launches."""
+    g = torch.Generator(device="cpu").manual_seed(20261204)
+    rnd = torch.randint(0, 256, (16384,), dtype=torch.uint8, generator=g).to(dev)
+    zero = torch.zeros(16384, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    out = {}
+    for key, ops, wgs in (("random_256_workgroups", rnd, 256), ("zeros_256_workgroups", zero, 256),
+                          ("random_128_workgroups", rnd, 128)):
+        ms = time_launches(lambda: w4.probe_mfma_fp4(ops, iters, wgs, sink), reps=reps, bursts=bursts)
+        flops = 2 * 128 * 128 * 64 * iters * 4 * wgs
+        rate = flops / (ms * 1e-3)
+        out[key] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(rate / 1e12, 1),
+                    "frac_of_peak": round(rate / PEAK["mxfp4"][0], 4),
+                    "per_CU_TFLOP/s": round(rate / wgs / 1e12, 2)}
+    return out
+
+
 def host_cpu():
     """(cores this process may run on, CPU model string)."""
     try:
@@ -598,6 +624,8 @@ def main():
                     help="skip the other formats' prefill and decode figures")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB calibration copy and one pass of the kernels, print nothing")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only the FP4 MFMA ceiling leg (scaled FP4 MFMAs on register operands)")
     ap.add_argument("--ceiling-probe", action="store_true",
                     help="only the decode ceiling leg (read probe, single-linear decode GEMMs, launch cost)")
     a = ap.parse_args()
@@ -609,6 +637,9 @@ def main():
     dev = torch.device("cuda:0")
     if a.ceiling_probe:
         print(json.dumps({"decode_ceiling": decode_ceiling(dev, a.steps)}), flush=True)
+        return
+    if a.mfma_probe:
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(dev)}), flush=True)
         return
     seed, fmt, Ms, lins = inputs.WORKLOADS[a.workload]
     M = a.M or Ms[-1]
@@ -653,6 +684,11 @@ def main():
            "roofline": roof}
     del layers
     torch.cuda.empty_cache()
+    if fmt == "mxfp4":
+        log("[bench] FP4 MFMA ceiling: the MFMAs alone on register operands")
+        out["mfma_ceiling"] = mfma_ceiling(dev)
+        rc = out["mfma_ceiling"]["random_256_workgroups"]["TFLOP/s"]
+        out["mfma_ceiling"]["gemm_achieved_of_random_256"] = round(roof["achieved"] / rc, 3)
     if not a.no_decode:
         log("[bench] decode: MXFP4 Llama linears at M = 1, 4, 16")
         out["decode_hbm"] = decode_bandwidth(dev, a.steps)

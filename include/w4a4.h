@@ -407,6 +407,31 @@ w4a4_status w4a4_dualquant_solve(w4a4_format fmt, int64_t N, int64_t K,
 w4a4_status w4a4_probe_stream_read(const void* src, size_t bytes, void* sink, void* stream);
 w4a4_status w4a4_probe_empty(void* stream);
 
+/*
+ * Measurement aid for the prefill roofline (not part of the quantized
+ * linear): the scaled FP4 MFMA of the MXFP4 GEMMs (32 x 32 x 64, E8M0
+ * scales) alone, on register operands.  Each of the 4 waves of each of
+ * `workgroups` workgroups holds a 128 x 128 tile of fp32 accumulators (4 x 4
+ * blocks of 32 x 32, as a wave of the persistent MXFP4 GEMM) and runs `iters`
+ * rounds of its 16 MFMAs, alternating two operand sets, with no memory
+ * traffic in the loop: 2 * 128 * 128 * 64 * iters * 4 * workgroups FP4
+ * operations per launch.  Its rate is what the matrix cores sustain at the
+ * clock the chip holds under that load, for the operand bits given (random
+ * codes draw more power than zeros).
+ *
+ *   ops         device, 16-byte aligned, 16 KiB: 16 fragments of 64 lanes x
+ *               16 bytes (32 FP4 codes a lane): weight fragments 0..3 and
+ *               activation fragments 4..7 of set 0, then 8..15 of set 1.
+ *   iters       even, 2 .. 2^20.
+ *   workgroups  1 .. 4096 (one workgroup per CU at most: 256 fill the chip).
+ *   sink        device, 256 x 4 bytes, 4-byte aligned; written only if a
+ *               workgroup's sum of accumulators equals a fixed constant that
+ *               the sums never reach, which keeps the MFMAs live.
+ * Returns W4A4_ERR_NULL, W4A4_ERR_SHAPE or W4A4_ERR_ALIGN for bad arguments;
+ * enqueued on `stream`.
+ */
+w4a4_status w4a4_probe_mfma_fp4(const void* ops, int iters, int workgroups, void* sink, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* w4a4_last_error(void);
 

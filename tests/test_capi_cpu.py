@@ -323,6 +323,14 @@ def test_probe_rejects_bad_arguments():
     assert L.w4a4_probe_stream_read(fake, 1000, fake, None) == 2           # bytes % 16
     assert L.w4a4_probe_stream_read(fake, 0, fake, None) == 2
     assert L.w4a4_probe_stream_read(ctypes.c_void_p(4100), 1024, fake, None) == 3  # alignment
+    assert L.w4a4_probe_mfma_fp4(None, 2, 1, fake, None) == 1              # NULL ops
+    assert L.w4a4_probe_mfma_fp4(fake, 2, 1, None, None) == 1              # NULL sink
+    assert L.w4a4_probe_mfma_fp4(fake, 3, 1, fake, None) == 2              # odd iters
+    assert L.w4a4_probe_mfma_fp4(fake, 0, 1, fake, None) == 2
+    assert L.w4a4_probe_mfma_fp4(fake, (1 << 20) + 2, 1, fake, None) == 2
+    assert L.w4a4_probe_mfma_fp4(fake, 2, 0, fake, None) == 2              # workgroups
+    assert L.w4a4_probe_mfma_fp4(fake, 2, 4097, fake, None) == 2
+    assert L.w4a4_probe_mfma_fp4(ctypes.c_void_p(4104), 2, 1, fake, None) == 3  # alignment
 
 
 

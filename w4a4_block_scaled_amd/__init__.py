@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.w4a4_probe_stream_read.restype = i32
     L.w4a4_probe_empty.argtypes = [vp]
     L.w4a4_probe_empty.restype = i32
+    L.w4a4_probe_mfma_fp4.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp]
+    L.w4a4_probe_mfma_fp4.restype = i32
     L.w4a4_last_error.argtypes = []
     L.w4a4_last_error.restype = ctypes.c_char_p
     L.w4a4_version.argtypes = []
@@ -325,6 +327,15 @@ def probe_stream_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
     multiple of 16) once; `sink` a device buffer of at least 1 KiB."""
     _check(lib().w4a4_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                         _stream(buf.device)))
+
+
+def probe_mfma_fp4(ops: torch.Tensor, iters: int, workgroups: int, sink: torch.Tensor) -> None:
+    """w4a4_probe_mfma_fp4: `iters` rounds of 16 scaled FP4 MFMAs per wave on
+    the 16 KiB of operand fragments in `ops`, over `workgroups` workgroups of
+    4 waves; `sink` a device buffer of at least 1 KiB."""
+    if ops.numel() * ops.element_size() < 16384:
+        raise ValueError("probe_mfma_fp4: ops must hold 16 KiB")
+    _check(lib().w4a4_probe_mfma_fp4(_ptr(ops), int(iters), int(workgroups), _ptr(sink), _stream(ops.device)))
 
 
 def probe_empty(device) -> None:

@@ -392,6 +392,15 @@ w4a4_status w4a4_probe_stream_read(const void* src, size_t bytes, void* sink, vo
                     "probe_stream_read launch");
 }
 
+w4a4_status w4a4_probe_mfma_fp4(const void* ops, int iters, int workgroups, void* sink, void* stream) {
+  if (!ops || !sink) return fail(W4A4_ERR_NULL, "probe_mfma_fp4: ops and sink must be non-NULL");
+  if (iters < 2 || iters > (1 << 20) || iters % 2) return fail(W4A4_ERR_SHAPE, "probe_mfma_fp4: iters must be even, 2 .. 2^20");
+  if (workgroups < 1 || workgroups > 4096) return fail(W4A4_ERR_SHAPE, "probe_mfma_fp4: workgroups must be 1 .. 4096");
+  if (!aligned(ops, 16) || !aligned(sink, 4)) return fail(W4A4_ERR_ALIGN, "probe_mfma_fp4: ops 16-byte, sink 4-byte alignment");
+  return hip_status(w4a4::launch_mfma_fp4(ops, iters, workgroups, sink, static_cast<hipStream_t>(stream)),
+                    "probe_mfma_fp4 launch");
+}
+
 w4a4_status w4a4_probe_empty(void* stream) {
   return hip_status(w4a4::launch_empty(static_cast<hipStream_t>(stream)), "probe_empty launch");
 }

@@ -99,8 +99,11 @@ hipError_t launch_linear_int8g128(int64_t M, int64_t N, int64_t K, const void* a
                                   hipStream_t stream);
 
 // Measurement aids (probe.hip): a streaming read of `bytes` (a multiple of
-// 16) and an empty kernel.
+// 16), an empty kernel, and `iters` (even) rounds of 16 scaled FP4 MFMAs per
+// wave on register operands from `ops` (16 KiB) over `workgroups` workgroups
+// of 4 waves.
 hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t stream);
 hipError_t launch_empty(hipStream_t stream);
+hipError_t launch_mfma_fp4(const void* ops, int iters, int workgroups, void* sink, hipStream_t stream);
 
 }  // namespace w4a4
