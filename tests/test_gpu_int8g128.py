@@ -183,7 +183,7 @@ def run_case(case, dev, label):
     return check_linear(bf16_bits(Y), y, S, case.K, label), bf16_bits(Y), bits
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9, 16, 17, 32, 33, 64, 130, 300])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 9, 16, 17, 32, 33, 64, 100, 130, 300])
 @pytest.mark.parametrize("N,K", [(48, 384), (272, 1152), (528, 4096)])
 def test_linear_matches_oracle(M, N, K):
     dev = device()
@@ -272,6 +272,21 @@ def test_decode_and_tile_kernels_agree():
     assert np.array_equal(y16, y16b)
     diff = np.abs(F.bf16_value(y16) - F.bf16_value(y17[:16]))
     assert diff.max() <= 2.0 ** -6 * np.abs(F.bf16_value(y17[:16])).max()
+
+
+def test_lds_kernels_agree():
+    """M = 128 runs the 128-row LDS-staged kernel (one wave per SIMD) and
+    M = 200 the 256-row one (two waves per SIMD): both add every output's
+    block sums in the same order with the same operations, so the first 128
+    rows are bit-identical, and both pass the gates."""
+    dev = device()
+    case = inputs.adhoc_case(FMT, 200, 528, 4096, seed=11)
+    (_, y200, _) = run_case(case, dev, "lds 256-row tiles")
+    case128 = inputs.adhoc_case(FMT, 200, 528, 4096, seed=11)
+    case128.M = 128
+    case128.x = case128.x[:128]
+    (_, y128, _) = run_case(case128, dev, "lds 128-row tiles")
+    assert np.array_equal(y128, y200[:128])
 
 
 @pytest.mark.parametrize("M", [1, 3, 16, 2048])

@@ -42,8 +42,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-source code generation options: the INT8 G=128 kernels apply each
+# integer MFMA result on the VALU, so they take the MFMA results in ordinary
+# vector registers (no copy out of the accumulation registers per result).
+SOURCE_FLAGS = {"int8g128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
@@ -95,7 +101,8 @@ def build_asan(jobs: int = 4, verbose: bool = False) -> str:
     objs = [os.path.join(ASAN_DIR, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
 
     def comp(src, obj):
-        cmd = [hipcc(), *FLAGS, *host_flags, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *host_flags, "-x", "hip", "-c", os.path.join(CSRC, src),
+               "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

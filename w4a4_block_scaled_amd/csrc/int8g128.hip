@@ -588,47 +588,60 @@ gemm_int8g128_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* _
 }
 
 // ------------------------------------------------------- LDS-staged tile --
-// 128 (rows) x 128 (features) workgroup tiles, 4 waves as 2 x 2 of 64 x 64
-// (4 x 4 fragments); one 128-wide K-step (one block) per stage, DEPTH stages
-// in a ring, copied global -> LDS with direct-to-LDS loads, so each operand
-// byte crosses the L2 once per workgroup instead of once per wave.
-//   A codes   128 rows x 128 B; 16-byte chunk j of row r at chunk position
+// (64 WM) (rows) x 128 (features) workgroup tiles, 2 WM waves as WM (rows)
+// x 2 (features) of 64 x 64 (4 x 4 fragments); one 128-wide K-step (one
+// block) per stage, DEPTH stages in a ring, copied global -> LDS with
+// direct-to-LDS loads, so each operand byte crosses the L2 once per
+// workgroup instead of once per wave.  WM = 2: 128-row tiles, one wave per
+// SIMD; WM = 4: 256-row tiles, two waves per SIMD, so that one wave's VALU
+// work (the scale products) runs while the other's MFMAs do.
+//   A codes   64 WM rows x 128 B; 16-byte chunk j of row r at chunk position
 //             8 r + (j ^ (r & 7)), so a fragment read (16 rows, one chunk
 //             each) spreads over the banks;
 //   W codes   8 tiles of 2 KiB, as in the blob;
-//   A scales  128 dwords, the low half of dword r the K-step's BF16 scale of
-//             row r (a two-byte direct-to-LDS copy fills one dword per lane);
+//   A scales  64 WM dwords, the low half of dword r the K-step's BF16 scale
+//             of row r (a two-byte direct-to-LDS copy fills one dword per
+//             lane);
 //   W scales  8 x 16 BF16 (the K-step's scales of each 16-feature group).
-// Every wave issues the same number of copies per stage (4 + 4 + 1) and one
-// stage per K-step (past the last K-step a copy of the last stage, into a
-// slot that is not read again), so a stage is complete for a wave when its
-// vmcnt has dropped to 9 x (DEPTH - 2); a barrier then makes it complete for
-// the workgroup, and also orders the reads of the slot a new stage
-// overwrites before its copy.  All copies have landed before the epilogue.
-// Rows beyond M and groups beyond N/16 are read from clamped valid
-// addresses; they only feed outputs that are never stored.
-constexpr int kLdsA = 128 * 128, kLdsW = 8 * 2048, kLdsAS = 128 * 4, kLdsWS = 8 * 32;
-constexpr int kLdsStage = kLdsA + kLdsW + kLdsAS + kLdsWS;
-constexpr int kLdsCopies = 9;
+// Every wave issues the same number of copies per stage (4 activation, 8 /
+// WM weight, 1 scale) and one stage per K-step (past the last K-step a copy
+// of the last stage, into a slot that is not read again), so a stage is
+// complete for a wave when its vmcnt has dropped to copies x (DEPTH - 2); a
+// barrier then makes it complete for the workgroup, and also orders the
+// reads of the slot a new stage overwrites before its copy.  All copies have
+// landed before the epilogue.  Rows beyond M and groups beyond N/16 are read
+// from clamped valid addresses; they only feed outputs that are never
+// stored.
+template <int WM>
+struct I8Lds {
+  static constexpr int ROWS = 64 * WM, WAVES = 2 * WM;
+  static constexpr int A = ROWS * 128, W = 8 * 2048, AS = ROWS * 4, WS = 8 * 32;
+  static constexpr int STAGE = A + W + AS + WS;
+  static constexpr int W_COPIES = 16 / WAVES;
+  static constexpr int COPIES = 4 + W_COPIES + 1;
+  static_assert(ROWS / 8 == 4 * WAVES && W_COPIES * WAVES == 16, "copy split");
+};
 
 __device__ __forceinline__ constexpr int i8_vmcnt(int v) {
   // s_waitcnt simm16 on gfx9: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] at [15:14]
   return (v & 15) | (7 << 4) | (15 << 8) | (((v >> 4) & 3) << 14);
 }
 
-template <int DEPTH>
+template <int WM, int DEPTH>
 __device__ __forceinline__ void i8_stage_ready() {
-  static_assert(DEPTH >= 2 && (DEPTH - 2) * kLdsCopies < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(i8_vmcnt((DEPTH - 2) * kLdsCopies));
+  static_assert(DEPTH >= 2 && (DEPTH - 2) * I8Lds<WM>::COPIES < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(i8_vmcnt((DEPTH - 2) * I8Lds<WM>::COPIES));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
+template <int WM>
 __device__ __forceinline__ void i8_issue(const uint8_t* __restrict__ a_codes,
                                          const uint16_t* __restrict__ a_scales,
                                          const uint8_t* __restrict__ wc, const uint16_t* __restrict__ wsc,
                                          int64_t M, int64_t K, int64_t KS, int64_t NG, int64_t m0,
                                          int64_t g0, int64_t ks, LDS uint8_t* dst, int wave, int lane) {
+  using C = I8Lds<WM>;
   // activation rows: copy f covers rows 8 f .. 8 f + 7; lane L fills chunk
   // position L % 8 of row L / 8 with the chunk that belongs there
 #pragma unroll
@@ -640,35 +653,36 @@ __device__ __forceinline__ void i8_issue(const uint8_t* __restrict__ a_codes,
     const int j = (lane & 7) ^ (rr & 7);
     __builtin_amdgcn_global_load_lds(a_codes + row * K + ks * kG + 16 * j, dst + f * 1024, 16, 0, 0);
   }
-  LDS uint8_t* wdst = dst + kLdsA;
+  LDS uint8_t* wdst = dst + C::A;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int f = wave * 4 + i;  // half (f % 2) of tile f / 2
+  for (int i = 0; i < C::W_COPIES; ++i) {
+    const int f = wave * C::W_COPIES + i;  // half (f % 2) of tile f / 2
     int64_t g = g0 + f / 2;
     g = g < NG ? g : NG - 1;
     __builtin_amdgcn_global_load_lds(wc + (g * KS + ks) * 2048 + (f & 1) * 1024 + 16 * lane,
                                      wdst + f * 1024, 16, 0, 0);
   }
-  if (wave < 2) {
+  if (wave < WM) {
     // rows 64 wave + lane: one scale per lane, one dword per lane in LDS
     int64_t row = m0 + 64 * wave + lane;
     row = row < M ? row : M - 1;
-    __builtin_amdgcn_global_load_lds(a_scales + row * KS + ks, dst + kLdsA + kLdsW + wave * 256, 2, 0, 0);
+    __builtin_amdgcn_global_load_lds(a_scales + row * KS + ks, dst + C::A + C::W + wave * 256, 2, 0, 0);
   } else {
-    // waves 2 and 3 copy the same 256 bytes of weight scales (same copy
+    // the other waves copy the same 256 bytes of weight scales (same copy
     // count on every wave); lane L: two scales of group L / 8
     int64_t g = g0 + (lane >> 3);
     g = g < NG ? g : NG - 1;
-    __builtin_amdgcn_global_load_lds(wsc + (g * KS + ks) * 16 + 2 * (lane & 7),
-                                     dst + kLdsA + kLdsW + kLdsAS, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(wsc + (g * KS + ks) * 16 + 2 * (lane & 7), dst + C::A + C::W + C::AS, 4,
+                                     0, 0);
   }
 }
 
-template <int DEPTH>
-__global__ __launch_bounds__(256, 1) void gemm_int8g128_lds_kernel(
+template <int WM, int DEPTH>
+__global__ __launch_bounds__(128 * WM, 1) void gemm_int8g128_lds_kernel(
     const uint8_t* __restrict__ a_codes, const uint16_t* __restrict__ a_scales,
     const uint8_t* __restrict__ blob, uint16_t* __restrict__ Y, int64_t M, int64_t N, int64_t K,
     int tiles_m, int tiles_n, int per_xcd) {
+  using C = I8Lds<WM>;
   if (!blob_header_ok(blob, kFmt, N, K)) {
     fill_y_nan(Y, M, N);
     return;
@@ -679,11 +693,11 @@ __global__ __launch_bounds__(256, 1) void gemm_int8g128_lds_kernel(
   const int nw = tiles_n - 8 * nb < 8 ? tiles_n - 8 * nb : 8;  // width of this column block
   const int tm = ob / nw, tn = 8 * nb + ob % nw;
   const I8Layout L = i8_layout(N, K);
-  const int64_t m0 = int64_t(tm) * 128, g0 = int64_t(tn) * 8;
+  const int64_t m0 = int64_t(tm) * C::ROWS, g0 = int64_t(tn) * 8;
   const uint8_t* wc = blob + L.code_off;
   const uint16_t* wsc = reinterpret_cast<const uint16_t*>(blob + L.scale_off);
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * kLdsStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DEPTH * C::STAGE];
   LDS uint8_t* base = (LDS uint8_t*)smem;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -700,17 +714,17 @@ __global__ __launch_bounds__(256, 1) void gemm_int8g128_lds_kernel(
   const int64_t KS = L.KS;
 #pragma unroll
   for (int s = 0; s < DEPTH - 1; ++s)
-    i8_issue(a_codes, a_scales, wc, wsc, M, K, KS, L.NG, m0, g0, s < KS ? s : KS - 1, base + s * kLdsStage,
-             wave, lane);
+    i8_issue<WM>(a_codes, a_scales, wc, wsc, M, K, KS, L.NG, m0, g0, s < KS ? s : KS - 1, base + s * C::STAGE,
+                 wave, lane);
   for (int64_t s = 0; s < KS; ++s) {
-    i8_stage_ready<DEPTH>();
-    i8_issue(a_codes, a_scales, wc, wsc, M, K, KS, L.NG, m0, g0, s + DEPTH - 1 < KS ? s + DEPTH - 1 : KS - 1,
-             base + ((s + DEPTH - 1) % DEPTH) * kLdsStage, wave, lane);
-    const LDS uint8_t* st = base + (s % DEPTH) * kLdsStage;
+    i8_stage_ready<WM, DEPTH>();
+    i8_issue<WM>(a_codes, a_scales, wc, wsc, M, K, KS, L.NG, m0, g0, s + DEPTH - 1 < KS ? s + DEPTH - 1 : KS - 1,
+                 base + ((s + DEPTH - 1) % DEPTH) * C::STAGE, wave, lane);
+    const LDS uint8_t* st = base + (s % DEPTH) * C::STAGE;
     const LDS uint8_t* A = st;
-    const LDS uint8_t* W = st + kLdsA;
-    const LDS uint32_t* AS = reinterpret_cast<const LDS uint32_t*>(st + kLdsA + kLdsW);
-    const LDS uint16_t* WS = reinterpret_cast<const LDS uint16_t*>(st + kLdsA + kLdsW + kLdsAS);
+    const LDS uint8_t* W = st + C::A;
+    const LDS uint32_t* AS = reinterpret_cast<const LDS uint32_t*>(st + C::A + C::W);
+    const LDS uint16_t* WS = reinterpret_cast<const LDS uint16_t*>(st + C::A + C::W + C::AS);
     u4 a0[4], a1[4];
     float sa[4];
 #pragma unroll
@@ -773,15 +787,17 @@ __global__ __launch_bounds__(256, 1) void gemm_int8g128_lds_kernel(
   }
 }
 
-template <int DEPTH>
+template <int WM, int DEPTH>
 hipError_t launch_i8_lds(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const uint16_t* as,
                          const uint8_t* blob, uint16_t* Y, hipStream_t stream) {
+  using C = I8Lds<WM>;
+  static_assert(DEPTH * C::STAGE <= 160 * 1024, "LDS");
   const int64_t tiles_n = (N / 16 + 7) / 8;
-  const int64_t tiles_m = (M + 127) / 128;
+  const int64_t tiles_m = (M + C::ROWS - 1) / C::ROWS;
   if (tiles_n * tiles_m >= (int64_t(1) << 30)) return hipErrorInvalidValue;
   const int tiles = int(tiles_n * tiles_m), per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL((gemm_int8g128_lds_kernel<DEPTH>), dim3(unsigned(8 * per_xcd)), dim3(256), 0, stream,
-                     ac, as, blob, Y, M, N, K, int(tiles_m), int(tiles_n), per_xcd);
+  hipLaunchKernelGGL((gemm_int8g128_lds_kernel<WM, DEPTH>), dim3(unsigned(8 * per_xcd)), dim3(128 * WM), 0,
+                     stream, ac, as, blob, Y, M, N, K, int(tiles_m), int(tiles_n), per_xcd);
   return hipGetLastError();
 }
 
@@ -868,7 +884,8 @@ hipError_t launch_linear_int8g128(int64_t M, int64_t N, int64_t K, const void* a
   }
   if (M <= 32) return launch_i8_tile<1, 4>(M, N, K, ac, as, bl, y, stream);
   if (M <= 64) return launch_i8_tile<2, 4>(M, N, K, ac, as, bl, y, stream);
-  return launch_i8_lds<4>(M, N, K, ac, as, bl, y, stream);
+  if (M <= 128) return launch_i8_lds<2, 4>(M, N, K, ac, as, bl, y, stream);
+  return launch_i8_lds<4, 3>(M, N, K, ac, as, bl, y, stream);
 }
 
 }  // namespace w4a4
