@@ -257,6 +257,28 @@ def test_mx8_workload_full_size(workload, M):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_mx8_large_tiles_ragged(fmt):
+    """A shape with at least 160 tiles of 256 x 256 takes the 8-wave
+    256 x 256 tile kernel: M and N end inside a tile (the last row tile has
+    20 rows, the last column tile 16 features); sampled outputs including the
+    first and last 40 rows and 272 columns pass G1/G2, and the activation
+    codes of the sampled rows equal the oracle's."""
+    dev = device()
+    M, N, K = 1300, 6928, 384
+    assert ((N + 255) // 256) * ((M + 255) // 256) >= 160
+    case = inputs.adhoc_case(fmt, M, N, K, seed=77)
+    Y, blob, (ac, as_, ta), _ = gpu_layer(case, dev)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(40), _sample(M, 24, rng), np.arange(M - 40, M)]))
+    cols = np.unique(np.concatenate([np.arange(272), _sample(N, 64, rng), np.arange(N - 272, N)]))
+    y, S, (oa, osc, _), _ = oracle_layer(case, rows, cols)
+    assert np.array_equal(ac.cpu().numpy()[rows], oa)
+    assert np.array_equal(as_.cpu().numpy()[rows], osc)
+    elem, row = check_linear(bf16_bits(Y)[np.ix_(rows, cols)], y, S, K, f"{fmt} {M}x{N}x{K}")
+    say(f"    max elementwise rel err {elem:.2e}, max row rel-L2 {row:.2e}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_mx8_empty_and_noalloc(fmt):
     dev = device()
     case = inputs.adhoc_case(fmt, 9, 256, 512, seed=2)

@@ -3616,6 +3616,11 @@ hipError_t launch_fmt(int64_t M, int64_t N, int64_t K, const uint8_t* ac, const 
       // fit their loads in the 128 registers a wave of 1024 threads has)
       return launch_mx8_decode<FMT, 8, 8>(M, N, K, ac, as, blob, Y, stream);
     }
+    // 256 x 256 tiles with 8 waves (two per SIMD: one wave's operand
+    // expansion runs beside the other's MFMAs) where they nearly fill the
+    // CUs; otherwise 256 (n) x 128 (m) tiles with 4 waves, twice as many
+    if (((N + 255) / 256) * ((M + 255) / 256) >= 160)
+      return launch_mx8_tile<FMT, 256, 256, 2, 4, 2>(M, N, K, ac, as, blob, Y, stream);
     return launch_mx8_tile<FMT, 256, 128, 2, 2, 3>(M, N, K, ac, as, blob, Y, stream);
   } else if constexpr (FMT == NVFP4) {
     if (M <= 16) {
