@@ -596,9 +596,11 @@ gemm_int8g128_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* _
 // SIMD; WM = 4: 256-row tiles, two waves per SIMD, so that one wave's VALU
 // work (the scale products) runs while the other's MFMAs do.
 //   A codes   64 WM rows x 128 B; 16-byte chunk j of row r at chunk position
-//             8 r + (j ^ (r & 7)), so a fragment read (16 rows, one chunk
-//             each) spreads over the banks;
-//   W codes   8 tiles of 2 KiB, as in the blob;
+//             8 r + (j ^ i8_swz(r)), so a fragment read (16 rows, one chunk
+//             each) touches 16 different 16-byte bank groups;
+//   W codes   8 tiles of 2 KiB: the first 16 bytes of every lane's 32 (the
+//             operand of the block's first MFMA), then the second 16, so
+//             that a fragment read is 64 consecutive 16-byte chunks;
 //   A scales  64 WM dwords, the low half of dword r the K-step's BF16 scale
 //             of row r (a two-byte direct-to-LDS copy fills one dword per
 //             lane);
@@ -612,6 +614,10 @@ gemm_int8g128_tile_kernel(const uint8_t* __restrict__ a_codes, const uint16_t* _
 // landed before the epilogue.  Rows beyond M and groups beyond N/16 are read
 // from clamped valid addresses; they only feed outputs that are never
 // stored.
+// chunk swizzle of the staged activation rows: the rows r and r + 8 of a
+// 16-row fragment read land in different bank groups
+__device__ __forceinline__ int i8_swz(int r) { return ((r & 7) + ((r >> 3) & 1)) & 7; }
+
 template <int WM>
 struct I8Lds {
   static constexpr int ROWS = 64 * WM, WAVES = 2 * WM;
@@ -650,17 +656,17 @@ __device__ __forceinline__ void i8_issue(const uint8_t* __restrict__ a_codes,
     const int rr = 8 * f + (lane >> 3);
     int64_t row = m0 + rr;
     row = row < M ? row : M - 1;
-    const int j = (lane & 7) ^ (rr & 7);
+    const int j = (lane & 7) ^ i8_swz(rr);
     __builtin_amdgcn_global_load_lds(a_codes + row * K + ks * kG + 16 * j, dst + f * 1024, 16, 0, 0);
   }
   LDS uint8_t* wdst = dst + C::A;
 #pragma unroll
   for (int i = 0; i < C::W_COPIES; ++i) {
-    const int f = wave * C::W_COPIES + i;  // half (f % 2) of tile f / 2
+    const int f = wave * C::W_COPIES + i;  // 16-byte half (f % 2) of every lane's 32 bytes of tile f / 2
     int64_t g = g0 + f / 2;
     g = g < NG ? g : NG - 1;
-    __builtin_amdgcn_global_load_lds(wc + (g * KS + ks) * 2048 + (f & 1) * 1024 + 16 * lane,
-                                     wdst + f * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wc + (g * KS + ks) * 2048 + 32 * lane + 16 * (f & 1), wdst + f * 1024,
+                                     16, 0, 0);
   }
   if (wave < WM) {
     // rows 64 wave + lane: one scale per lane, one dword per lane in LDS
@@ -730,8 +736,8 @@ __global__ __launch_bounds__(128 * WM, 1) void gemm_int8g128_lds_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int R = 64 * wm + 16 * i + (lane & 15);
-      a0[i] = *reinterpret_cast<const LDS u4*>(A + R * 128 + 16 * (c ^ (R & 7)));
-      a1[i] = *reinterpret_cast<const LDS u4*>(A + R * 128 + 16 * ((4 + c) ^ (R & 7)));
+      a0[i] = *reinterpret_cast<const LDS u4*>(A + R * 128 + 16 * (c ^ i8_swz(R)));
+      a1[i] = *reinterpret_cast<const LDS u4*>(A + R * 128 + 16 * ((4 + c) ^ i8_swz(R)));
       sa[i] = bf16_to_f32(AS[R] & 0xFFFFu);
     }
 #pragma unroll
@@ -741,8 +747,8 @@ __global__ __launch_bounds__(128 * WM, 1) void gemm_int8g128_lds_kernel(
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int T = 4 * wn + j0 + jj;
-        w0[jj] = *reinterpret_cast<const LDS u4*>(W + T * 2048 + 32 * lane);
-        w1[jj] = *reinterpret_cast<const LDS u4*>(W + T * 2048 + 32 * lane + 16);
+        w0[jj] = *reinterpret_cast<const LDS u4*>(W + T * 2048 + 16 * lane);
+        w1[jj] = *reinterpret_cast<const LDS u4*>(W + T * 2048 + 1024 + 16 * lane);
         swb[jj] = *reinterpret_cast<const LDS u2*>(WS + T * 16 + 4 * c);
       }
       v4i S[2][4];
