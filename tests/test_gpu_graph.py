@@ -22,8 +22,10 @@ pytestmark = pytest.mark.gpu
 # MXINT4 decode (M = 1 and 16), tile and small-tile GEMMs, the NVFP4 path (tensor amax pre-pass with
 # its workspace, or the one-launch quantizer; tile, MFMA decode and dot-product
 # decode GEMMs), the
-# 8-bit MX formats and INT4 G=64 (dot-product and MFMA decode kernels, the
-# fp16-expansion GEMM's 128x128 and 256x256 tiles)
+# 8-bit MX formats (with the 8-wave 256x256 tiles of the large shapes),
+# INT4 G=64 (dot-product and MFMA decode kernels, the fp16-expansion GEMM's
+# 128x128 and 256x256 tiles) and INT8 G=128 (the LDS-staged 128-row and
+# 256-row tiles)
 CASES = [
     ("mxfp4", 512, 49152, 512),
     ("mxfp4", 2048, 6144, 512),
@@ -51,6 +53,9 @@ CASES = [
     ("int8g128", 1, 4096, 4096),
     ("int8g128", 8, 1024, 1024),
     ("int8g128", 300, 1040, 1024),
+    ("int8g128", 100, 1040, 1024),
+    ("mxfp8", 1024, 10240, 256),
+    ("mxint8", 1300, 6928, 256),
 ]
 
 
