@@ -304,6 +304,21 @@ __device__ __forceinline__ void tile_epilogue(const v4f (&acc)[FN][FM], LDS uint
   }
 }
 
+// Tile order of the one-tile-per-workgroup kernels: the hardware deals
+// workgroups round-robin to the 8 XCDs, and workgroup b takes number
+// (b % 8) per_xcd + b / 8 of an order that walks blocks of (up to) 4 column
+// tiles row by row, so each XCD runs through a contiguous range of it: the
+// workgroups sharing an L2 at once cover 8 row tiles x 4 column tiles, and
+// the activation rows are swept once per 4 column tiles rather than once per
+// column tile.  A bijection onto the tiles_m x (tiles_total / tiles_m) grid.
+__device__ __forceinline__ void col_block_tile(int tile, int tiles_m, int tiles_total, int& tm, int& tn) {
+  const int tiles_n = tiles_total / tiles_m;
+  const int nb = tile / (4 * tiles_m), ob = tile - nb * 4 * tiles_m;
+  const int nw = tiles_n - 4 * nb < 4 ? tiles_n - 4 * nb : 4;  // width of this column block
+  tm = ob / nw;
+  tn = 4 * nb + ob % nw;
+}
+
 // ======================================================== tiled kernel ==
 //
 // NVFP4, all M.  Workgroup tile BN (n) x BM (m), WN x WM waves (n x m), wave tile
@@ -490,12 +505,13 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_tile_kernel(
   }
   using C = TileCfg<FMT, BN, BM, WN, WM, DEPTH>;
   constexpr int FN = C::FN, FM = C::FM;
-  // XCD-aware order: the hardware deals workgroups round-robin to the 8 XCDs;
-  // give each XCD a contiguous run of tiles (m fastest), so the workgroups
-  // sharing an L2 share weight tiles and sweep the activations.
+  // XCD-aware order (col_block_tile): 8 row tiles x 4 column tiles share an
+  // XCD's L2 at once (2 MiB of activation rows and 2 MiB of weights at K =
+  // 4096)
   const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
   if (tile >= tiles_total) return;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  int tm, tn;
+  col_block_tile(tile, tiles_m, tiles_total, tm, tn);
 
   const BlobLayout L = blob_layout(FMT, N, K);
   const TileArgs t = tile_args(FMT, a_codes, a_scales, blob, L, M, K, int64_t(tm) * BM,
@@ -768,7 +784,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx_kernel(
   constexpr int FN = C::FN, FM = C::FM;
   const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
   if (tile >= tiles_total) return;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  int tm, tn;
+  col_block_tile(tile, tiles_m, tiles_total, tm, tn);
 
   const BlobLayout L = blob_layout(FMT, N, K);
   const TileArgs t = tile_args(FMT, a_codes, a_scales, blob, L, M, K, int64_t(tm) * BM,
@@ -870,7 +887,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx_lean_kernel(
   constexpr int FN = C::FN, FM = C::FM;
   const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
   if (tile >= tiles_total) return;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  int tm, tn;
+  col_block_tile(tile, tiles_m, tiles_total, tm, tn);
 
   const BlobLayout L = blob_layout(FMT, N, K);
   const TileArgs t = tile_args(FMT, a_codes, a_scales, blob, L, M, K, int64_t(tm) * BM,
@@ -3528,7 +3546,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_mx8_tile_kernel(
   constexpr int FN = C::FN, FM = C::FM;
   const int tile = int(blockIdx.x % 8) * per_xcd + int(blockIdx.x / 8);
   if (tile >= tiles_total) return;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  int tm, tn;
+  col_block_tile(tile, tiles_m, tiles_total, tm, tn);
 
   const BlobLayout L = blob_layout(FMT, N, K);
   const int64_t m0 = int64_t(tm) * BM, ng0 = int64_t(tn) * (BN / 16);
