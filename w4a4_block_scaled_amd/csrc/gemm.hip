@@ -3388,13 +3388,19 @@ hipError_t launch_mx8_dot(int64_t M, int64_t N, int64_t K, const uint8_t* ac, co
 //
 // Stage layout:
 //   A codes   BM rows x 128 B; 16-byte chunk j of row r at chunk position
-//             8 r + (j ^ (r & 7)), so the fragment reads (16 rows, one chunk
-//             each) fall on distinct banks;
-//   W codes   BN/16 tiles of 2 KiB, copied from the blob as they are;
+//             8 r + (j ^ mx8_swz(r)), so the fragment reads (16 rows, one
+//             chunk each) touch 16 different 16-byte bank groups;
+//   W codes   BN/16 tiles of 2 KiB: the first 16 bytes of every lane's 32
+//             in the blob's tile, then the second 16, so that a fragment
+//             read is 64 consecutive 16-byte chunks;
 //   A scales  BM rows x 4 B (the K-step's four block scales of a row);
 //   W scales  BN/64 scale-word sets x 64 lanes x 4 B.
 // Rows beyond M and row groups beyond N/16 are read from clamped valid
 // addresses; they only feed outputs that are never stored.
+// chunk swizzle of the staged 8-bit activation rows: the rows r and r + 8
+// of a 16-row fragment read land in different bank groups
+__device__ __forceinline__ int mx8_swz(int r) { return ((r & 7) + ((r >> 3) & 1)) & 7; }
+
 template <int BN, int BM, int WN, int WM, int DEPTH>
 struct Mx8Cfg {
   static constexpr int WAVES = WN * WM;
@@ -3430,17 +3436,17 @@ __device__ __forceinline__ void mx8_issue(const uint8_t* __restrict__ a_codes,
     const int rr = 8 * f + (lane >> 3);
     int64_t row = m0 + rr;
     row = row < M ? row : M - 1;
-    const int j = (lane & 7) ^ (rr & 7);
+    const int j = (lane & 7) ^ mx8_swz(rr);
     __builtin_amdgcn_global_load_lds(a_codes + row * K + ks * 128 + 16 * j, dst + f * 1024, 16, 0, 0);
   }
   LDS uint8_t* wdst = dst + C::A_BYTES;
 #pragma unroll
   for (int i = 0; i < C::W_DMA; ++i) {
-    const int f = wave * C::W_DMA + i;  // half (f % 2) of tile f / 2
+    const int f = wave * C::W_DMA + i;  // 16-byte half (f % 2) of every lane's 32 bytes of tile f / 2
     int64_t ng = ng0 + f / 2;
     ng = ng < NG ? ng : NG - 1;
-    __builtin_amdgcn_global_load_lds(wc + (ng * KS + ks) * 2048 + (f & 1) * 1024 + 16 * lane,
-                                     wdst + f * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wc + (ng * KS + ks) * 2048 + 32 * lane + 16 * (f & 1), wdst + f * 1024, 16,
+                                     0, 0);
   }
   LDS uint8_t* asdst = wdst + C::W_BYTES;
   if (lane < C::AS_DW) {
@@ -3481,8 +3487,8 @@ __device__ __forceinline__ void mx8_step(const LDS uint8_t* __restrict__ st, int
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int R = wm * (16 * FM) + 16 * j + r;
-      const u32x4 lo = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * (c ^ (R & 7)));
-      const u32x4 hi = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * ((4 + c) ^ (R & 7)));
+      const u32x4 lo = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * (c ^ mx8_swz(R)));
+      const u32x4 hi = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * ((4 + c) ^ mx8_swz(R)));
       ab[j] = e4m3_frag_bf16(v8i_of(lo, hi), e8m0_scale(AS[R * 4 + b0]), e8m0_scale(AS[R * 4 + 2 + b0]));
     }
     uint32_t sw0[FN / 4], sw1[FN / 4];
@@ -3493,9 +3499,9 @@ __device__ __forceinline__ void mx8_step(const LDS uint8_t* __restrict__ st, int
     }
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const LDS uint8_t* wt = W + (wn * FN + i) * 2048 + 32 * lane;
+      const LDS uint8_t* wt = W + (wn * FN + i) * 2048 + 16 * lane;
       const u32x4 wlo = *reinterpret_cast<const LDS u32x4*>(wt);
-      const u32x4 whi = *reinterpret_cast<const LDS u32x4*>(wt + 16);
+      const u32x4 whi = *reinterpret_cast<const LDS u32x4*>(wt + 1024);
       const int sh = 8 * (i % 4);
       const Bf16Frag wb = e4m3_frag_bf16(v8i_of(wlo, whi), e8m0_scale(sw0[i / 4] >> sh),
                                          e8m0_scale(sw1[i / 4] >> sh));
@@ -3509,8 +3515,8 @@ __device__ __forceinline__ void mx8_step(const LDS uint8_t* __restrict__ st, int
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int R = wm * (16 * FM) + 16 * j + r;
-      const u32x4 lo = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * (c ^ (R & 7)));
-      const u32x4 hi = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * ((4 + c) ^ (R & 7)));
+      const u32x4 lo = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * (c ^ mx8_swz(R)));
+      const u32x4 hi = *reinterpret_cast<const LDS u32x4*>(A + R * 128 + 16 * ((4 + c) ^ mx8_swz(R)));
       af[j] = v8i_of(lo, hi);
       sa[j] = AS[R * 4 + c];
       as[j] = int8_frag_split(af[j]);
@@ -3520,9 +3526,9 @@ __device__ __forceinline__ void mx8_step(const LDS uint8_t* __restrict__ st, int
     for (int q = 0; q < FN / 4; ++q) sw[q] = WS[(wn * (FN / 4) + q) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const LDS uint8_t* wt = W + (wn * FN + i) * 2048 + 32 * lane;
+      const LDS uint8_t* wt = W + (wn * FN + i) * 2048 + 16 * lane;
       const u32x4 wlo = *reinterpret_cast<const LDS u32x4*>(wt);
-      const u32x4 whi = *reinterpret_cast<const LDS u32x4*>(wt + 16);
+      const u32x4 whi = *reinterpret_cast<const LDS u32x4*>(wt + 1024);
       const v8i w = v8i_of(wlo, whi);
       const Mx8Split ws = int8_frag_split(w);
 #pragma unroll
