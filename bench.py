@@ -689,6 +689,10 @@ def main():
         out["mfma_ceiling"] = mfma_ceiling(dev)
         rc = out["mfma_ceiling"]["random_256_workgroups"]["TFLOP/s"]
         out["mfma_ceiling"]["gemm_achieved_of_random_256"] = round(roof["achieved"] / rc, 3)
+        # beside the nominal peak: the same GEMM rate against what the FP4
+        # MFMAs alone sustain on random operands on this chip (power-limited)
+        roof["measured_mfma_ceiling"] = rc
+        roof["frac_of_measured_mfma_ceiling"] = round(roof["achieved"] / rc, 4)
     if not a.no_decode:
         log("[bench] decode: MXFP4 Llama linears at M = 1, 4, 16")
         out["decode_hbm"] = decode_bandwidth(dev, a.steps)
